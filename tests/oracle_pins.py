@@ -1,0 +1,276 @@
+"""Pins of the fp64 oracle against facts fixed outside it.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with the fact it checks.  ``test_oracle_pins.py`` runs them
+on the real oracle; ``test_oracle_mutants.py`` runs them on copies of the
+oracle with planted mistakes and requires that some pin fails for each.
+
+The pages print no worked example for this path, so the pins are closed
+forms, invariants, special cases that reduce to a library routine, and brute
+force against an independent numpy reference on tiny shapes.
+"""
+from __future__ import annotations
+
+import copy
+
+import numpy as np
+
+import synth
+import np_reference as npr
+
+TINY = synth.Dims(d_model=128, n_experts=16, top_k=4, d_ff=64, d_ff_shared=64, group_size=64)
+
+_cache = {}
+
+
+def tiny_layer(seed=11, **kw) -> synth.Layer:
+    key = (seed, tuple(sorted(kw.items())))
+    if key not in _cache:
+        _cache[key] = synth.make_layer(seed, TINY, w_sd=0.05, nthreads=1, **kw)
+    return copy.deepcopy(_cache[key])
+
+
+def tiny_x(seed=3, T=6):
+    return synth.x_rows(seed, T, TINY.d_model, nthreads=1)
+
+
+def rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# ----------------------------------------------------------------- bf16
+def pin_bf16_exhaustive(O):
+    """bf16 -> fp32 is the 16-bit left shift of the bit pattern, for all
+    65,536 patterns (NaNs compared by bits)."""
+    bits = np.arange(65536, dtype=np.uint32)
+    want = (bits << 16).view(np.float32)
+    # through the oracle's dequant with s=1 would lose NaN payloads; call directly
+    got = np.array([O.bf16_to_f32(int(b)) for b in bits[::1]], dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32)[~np.isnan(want)], want.view(np.uint32)[~np.isnan(want)])
+    assert np.isnan(got[np.isnan(want)]).all()
+
+
+# ----------------------------------------------------------------- dequant
+def _q4_one_row(words, scales, biases):
+    return synth.Q4(np.asarray(words, dtype=np.uint32).reshape(1, 1, -1),
+                    np.asarray(scales, dtype=np.uint16).reshape(1, 1, -1),
+                    np.asarray(biases, dtype=np.uint16).reshape(1, 1, -1))
+
+
+def pin_dequant_handpacked(O):
+    """Nibble k of word j is element 8j+k ("low first"); one bf16 scale and
+    bias per group of 64.  Words 0x76543210, 0xFEDCBA98 give q = 0..15."""
+    one, zero, half, m1, two, three = 0x3F80, 0x0000, 0x3F00, 0xBF80, 0x4000, 0x4040
+    words = [0x76543210, 0xFEDCBA98] + [0] * 6 + [0x76543210, 0xFEDCBA98] + [0] * 6
+    q = np.array(list(range(16)) + [0] * 48, dtype=np.float32)
+    # group 0: (s, b) = (1, 0); group 1: (0.5, -1)
+    got = O.dequant_row(_q4_one_row(words, [one, half], [zero, m1]), 0, 1, 128, 64, 0)
+    assert np.array_equal(got[:64], q)
+    assert np.array_equal(got[64:], 0.5 * q - 1.0)
+    # group 0: (2, 3): W = 2q + 3
+    got = O.dequant_row(_q4_one_row(words[:8], [two], [three]), 0, 1, 64, 64, 0)
+    assert np.array_equal(got, 2.0 * q + 3.0)
+
+
+def pin_dequant_quantizer_bound(O):
+    """The generator's encoding decodes to within s/2 (plus the bf16 rounding
+    of s and b) of the fp32 weights it encoded."""
+    rows, cols, g = 4, 256, 64
+    qw, sc, bi = synth.q4_matrix(5, 99, 1, rows, cols, g, 0.02, nthreads=1)
+    w = synth.normal_f32(5, 99, rows * cols, 0.02, nthreads=1).reshape(rows, cols)
+    q4 = synth.Q4(qw, sc, bi)
+    s = np.repeat(synth.bf16_to_f32(sc[0]), g, axis=1)
+    b = np.repeat(synth.bf16_to_f32(bi[0]), g, axis=1)
+    mn = np.repeat(w.reshape(rows, -1, g).min(axis=2), g, axis=1)
+    for r in range(rows):
+        got = O.dequant_row(q4, 0, rows, cols, g, r)
+        slack = 0.5 * s[r] + np.abs(b[r] - mn[r]) + 1e-7
+        assert np.all(np.abs(got - w[r]) <= slack + 0.01 * s[r])
+
+
+# ----------------------------------------------------------------- router
+def pin_router_onehot(O):
+    """x = e_j gives logits = Wr[:, j] (+ bias) exactly."""
+    lay = tiny_layer(zipf_s=1.0)
+    for j in (0, 5, 127):
+        x = np.zeros(TINY.d_model, dtype=np.uint16)
+        x[j] = 0x3F80  # 1.0
+        got = O.router_logits(lay, x)
+        want = lay.router_w[:, j].astype(np.float64) + lay.router_b.astype(np.float64)
+        assert np.array_equal(got, want)
+
+
+def pin_router_bruteforce(O):
+    lay = tiny_layer(zipf_s=1.0)
+    x = tiny_x()
+    want = npr.bf16(x).astype(np.float64) @ lay.router_w.astype(np.float64).T + lay.router_b.astype(np.float64)
+    for t in range(x.shape[0]):
+        got = O.router_logits(lay, x[t])
+        assert np.max(np.abs(got - want[t])) <= 1e-12 * np.max(np.abs(want[t]))
+
+
+# ----------------------------------------------------------------- select
+def pin_select_random(O):
+    """Selected set and order equal a stable argsort of -logits; weights are
+    the renormalised softmax; they sum to 1; margin is l(k) - l(k+1)."""
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        E, k = 32, 8
+        lg = rng.standard_normal(E)
+        sel, w, m = O.select(lg, k)
+        order = np.argsort(-lg, kind="stable")
+        assert np.array_equal(sel, order[:k])
+        p = np.exp(lg - lg.max())
+        p /= p.sum()
+        assert np.allclose(w, p[order[:k]] / p[order[:k]].sum(), rtol=1e-13, atol=0)
+        assert abs(w.sum() - 1.0) <= 1e-15 * 4
+        assert abs(m - (lg[order[k - 1]] - lg[order[k]])) <= 1e-15
+        assert np.all(np.diff(w) <= 0)
+
+
+def pin_select_ties(O):
+    """Equal logits: lower index first, for membership and order; all-equal
+    logits select 0..k-1 with weight exactly 1/k."""
+    sel, w, m = O.select(np.zeros(256), 8)
+    assert list(sel) == list(range(8)) and np.all(w == 0.125) and m == 0.0
+    lg = np.array([0.0, 3.0, 1.0, 3.0, 2.0, 1.0, 2.0, -1.0])
+    sel, w, m = O.select(lg, 4)
+    assert list(sel) == [1, 3, 4, 6]
+    sel, w, m = O.select(lg, 5)
+    assert list(sel) == [1, 3, 4, 6, 2] and m == 0.0  # 2 beats 5 at logit 1.0
+
+
+# ----------------------------------------------------------------- experts
+def pin_identical_experts_dense(O):
+    """When every expert holds the same bytes the routed sum is one dense
+    SwiGLU (the weights sum to 1), computed here by numpy matmuls on the
+    dequantised matrices."""
+    lay = tiny_layer(shared=False)
+    for q in (lay.gate, lay.up, lay.down):
+        for a in (q.qweight, q.scales, q.biases):
+            a[:] = a[2][None]
+    x = tiny_x()
+    r = O.forward(lay, x, nthreads=1)
+    mats = [npr.dequant(q, 0, TINY.group_size).astype(np.float64) for q in (lay.gate, lay.up, lay.down)]
+    for t in range(x.shape[0]):
+        want = npr.swiglu(*mats, npr.bf16(x[t]).astype(np.float64))
+        assert rel(r["y"][t], want) <= 1e-13
+
+
+def pin_dominant_expert(O):
+    """A router offset of +100 on expert e gives it weight 1 - O(e^-90), so
+    the output is that expert's dense SwiGLU."""
+    lay = tiny_layer(shared=False)
+    lay.router_b = np.zeros(TINY.n_experts, dtype=np.float32)
+    e = 9
+    lay.router_b[e] = 100.0
+    x = tiny_x()
+    r = O.forward(lay, x, nthreads=1)
+    mats = [npr.dequant(q, e, TINY.group_size).astype(np.float64) for q in (lay.gate, lay.up, lay.down)]
+    assert np.all(r["idx"][:, 0] == e) and np.all(r["w"][:, 0] >= 1.0 - 1e-15)
+    for t in range(x.shape[0]):
+        want = npr.swiglu(*mats, npr.bf16(x[t]).astype(np.float64))
+        assert rel(r["y"][t], want) <= 1e-13
+
+
+def pin_expert_direct(O):
+    """moe_oracle_expert equals the dense numpy SwiGLU of that expert."""
+    lay = tiny_layer()
+    xd = npr.bf16(tiny_x()[0]).astype(np.float64)
+    for e in (0, 7, 15):
+        mats = [npr.dequant(q, e, TINY.group_size).astype(np.float64) for q in (lay.gate, lay.up, lay.down)]
+        assert rel(O.expert(lay, e, xd), npr.swiglu(*mats, xd)) <= 1e-13
+
+
+# ----------------------------------------------------------------- shared / combine
+def pin_shared_terms(O):
+    """No shared expert => y = routed.  No gate vector => sgate = 1.  The
+    shared expert equals the dense numpy SwiGLU of its bf16 matrices and
+    sgate = sigmoid(w . x)."""
+    lay = tiny_layer()
+    x = tiny_x()
+    full = O.forward(lay, x, nthreads=1)["y"]
+    no_sh = copy.deepcopy(lay)
+    no_sh.sh_gate = no_sh.sh_up = no_sh.sh_down = no_sh.sh_gate_inp = None
+    routed = O.forward(no_sh, x, nthreads=1)["y"]
+    no_gate = copy.deepcopy(lay)
+    no_gate.sh_gate_inp = None
+    ungated = O.forward(no_gate, x, nthreads=1)["y"]
+    wg, wu, wd = (npr.bf16(m).astype(np.float64) for m in (lay.sh_gate, lay.sh_up, lay.sh_down))
+    for t in range(x.shape[0]):
+        xd = npr.bf16(x[t]).astype(np.float64)
+        ys = npr.swiglu(wg, wu, wd, xd)
+        sg = 1.0 / (1.0 + np.exp(-(npr.bf16(lay.sh_gate_inp).astype(np.float64) @ xd)))
+        assert rel(ungated[t] - routed[t], ys) <= 1e-12
+        assert rel(full[t] - routed[t], sg * ys) <= 1e-12
+        out, s = O.shared(lay, xd)
+        assert rel(out, ys) <= 1e-13 and abs(s - sg) <= 1e-15
+
+
+def pin_zero_input(O):
+    """x = 0 gives y = 0 exactly (silu(0) = 0), and uniform routing."""
+    lay = tiny_layer()
+    x = np.zeros((3, TINY.d_model), dtype=np.uint16)
+    r = O.forward(lay, x, nthreads=1)
+    assert np.all(r["y"] == 0.0)
+    assert np.all(r["idx"] == np.arange(TINY.top_k)[None, :]) and np.all(r["w"] == 1.0 / TINY.top_k)
+
+
+# ----------------------------------------------------------------- invariants
+def pin_permutation_invariance(O):
+    lay = tiny_layer(zipf_s=1.5)
+    x = tiny_x(T=9)
+    perm = np.array([4, 0, 8, 2, 7, 1, 3, 6, 5])
+    a = O.forward(lay, x, nthreads=3)
+    b = O.forward(lay, x[perm], nthreads=2)
+    for key in ("y", "idx", "w", "margin"):
+        assert np.array_equal(b[key], a[key][perm])
+    c = O.forward(lay, x, tokens=perm, nthreads=1)
+    for key in ("y", "idx", "w", "margin"):
+        assert np.array_equal(c[key], a[key][perm])
+
+
+def pin_down_halving(O):
+    """Halving every down scale and bias (exact in bf16) halves the routed
+    output exactly."""
+    lay = tiny_layer(shared=False)
+    x = tiny_x()
+    a = O.forward(lay, x, nthreads=1)["y"]
+    half = copy.deepcopy(lay)
+    for arr in (half.down.scales, half.down.biases):
+        f = synth.bf16_to_f32(arr) * np.float32(0.5)
+        arr[:] = synth.f32_to_bf16(f)
+        assert np.array_equal(synth.bf16_to_f32(arr), f)
+    b = O.forward(half, x, nthreads=1)["y"]
+    assert np.array_equal(b, 0.5 * a)
+
+
+def pin_bruteforce_tiny(O):
+    """Whole forward equals the independent numpy reference on tiny shapes,
+    with and without router offsets, shared expert and shared gate."""
+    x = tiny_x(T=7)
+    for kw in (dict(), dict(zipf_s=1.0), dict(shared=False), dict(gate_inp=False)):
+        lay = tiny_layer(**kw)
+        got = O.forward(lay, x, nthreads=2)
+        want = npr.forward(lay, x)
+        assert np.array_equal(got["idx"], want["idx"])
+        assert np.allclose(got["w"], want["w"], rtol=1e-13, atol=0)
+        for t in range(x.shape[0]):
+            assert rel(got["y"][t], want["y"][t]) <= 1e-12
+
+
+def pin_gate_up_order(O):
+    """Swapping gate and up changes the output completely (the math contract
+    is silu(gate) * up, not silu(up) * gate)."""
+    lay = tiny_layer()
+    x = tiny_x()
+    a = O.forward(lay, x, nthreads=1)["y"]
+    sw = copy.deepcopy(lay)
+    sw.gate, sw.up = sw.up, sw.gate
+    b = O.forward(sw, x, nthreads=1)["y"]
+    want = npr.forward(lay, x)["y"]
+    assert all(rel(a[t], want[t]) <= 1e-12 for t in range(x.shape[0]))
+    assert all(rel(b[t], a[t]) > 0.2 for t in range(x.shape[0]))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
