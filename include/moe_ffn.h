@@ -1,0 +1,137 @@
+/*
+ * moe_ffn -- sparse shared-expert MoE FFN for AMD Instinct MI355X (gfx950).
+ *
+ * One layer of the FFN described in "qwen35moe - Forward-Pass Design
+ * (Pantheon port)", section "Shared-expert MoE FFN (every layer)":
+ *
+ *   moe_out = MoE(x; softmax router over 256 experts, top-8 used,
+ *                 norm_topk_prob = true, SwiGLU experts)
+ *   shexp   = SwiGLU(x; ffn_gate_shexp, ffn_up_shexp, ffn_down_shexp)
+ *   sgate   = sigmoid(ffn_gate_inp_shexp . x)           (one scalar per token)
+ *   y       = moe_out + sgate * shexp
+ *
+ * with expert(x) = down(silu(gate(x)) * up(x)) ("SSD Streaming Expert Layers
+ * (streaming)", section "Math Contract") and routed expert weights in the
+ * 4-bit affine layout of the same page, section "Quantized Layout".  Shapes are
+ * those of the "Config" table of the qwen35moe page: n_embd 2048, 256 experts,
+ * 8 used, expert FF 512, shared FF 512; quantisation group 64.
+ *
+ * Conventions of every entry point:
+ *   - Plain C ABI; no exception crosses it.  Return 0 (MOE_FFN_OK) or a
+ *     negative MOE_FFN_E* status; moe_ffn_status_string names it.
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, row-major and contiguous.  bf16 values are passed as their
+ *     uint16_t bit patterns.  The library never writes an input and never
+ *     keeps a pointer after the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  A call only
+ *     enqueues work on it: no host synchronisation, no device allocation.
+ *     Faults inside kernels surface as HIP errors at the caller's next
+ *     synchronisation, as for any HIP launch.
+ *   - Inputs must be finite.  x, the shared-expert weights, and every
+ *     dequantised routed weight s*q + b (and s, b themselves) must lie within
+ *     the fp16 range |v| <= 65504: the expert GEMMs run on fp16 MFMA operands.
+ *     Values below 2^-14 in magnitude lose relative precision (fp16
+ *     subnormals); they contribute at most 2^-24 absolute error each.
+ *   - Calls that share a workspace must not overlap in time (same stream, or
+ *     ordered by events).
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_FFN_OK 0
+#define MOE_FFN_EINVAL (-1)       /* NULL required pointer, T < 0, bad path id, dims NULL */
+#define MOE_FFN_EUNSUPPORTED (-2) /* dims differ from the compiled shape, or T too large */
+#define MOE_FFN_EALIGN (-3)       /* a pointer is not 16-byte aligned */
+#define MOE_FFN_EWORKSPACE (-4)   /* workspace NULL or smaller than moe_ffn_workspace_size */
+#define MOE_FFN_EHIP (-5)         /* a kernel launch failed (hipGetLastError) */
+
+/* execution paths (moe_ffn_forward_path) */
+#define MOE_FFN_PATH_AUTO 0    /* decode for T <= MOE_FFN_DECODE_MAX_T, else prefill */
+#define MOE_FFN_PATH_DECODE 1  /* small-T path: weight-streaming GEMV kernels */
+#define MOE_FFN_PATH_PREFILL 2 /* large-T path: routing sort + grouped MFMA GEMMs */
+
+#define MOE_FFN_DECODE_MAX_T 64
+#define MOE_FFN_MAX_T (1 << 20)
+
+/* Layer shape.  The library is compiled for {2048, 256, 8, 512, 512, 64}
+ * (d_model, n_experts, top_k, d_ff, d_ff_shared, group_size) and returns
+ * MOE_FFN_EUNSUPPORTED for anything else. */
+typedef struct {
+    int32_t d_model, n_experts, top_k, d_ff, d_ff_shared, group_size;
+} moe_ffn_dims;
+
+/* A 4-bit affine tensor of E stacked matrices [out, in] ("Quantized Layout"):
+ *   qweight u32  [E, out, in/8]: element 8j+k of a row is bits 4k..4k+3 of
+ *                word j ("low first");
+ *   scales  bf16 [E, out, in/64], biases bf16 [E, out, in/64];
+ *   W[e, o, i] = scales[e, o, i/64] * q + biases[e, o, i/64]. */
+typedef struct {
+    const uint32_t *qweight;
+    const uint16_t *scales;
+    const uint16_t *biases;
+} moe_q4_tensor;
+
+/* ffn_{gate,up,down}_exps: gate and up are [E, d_ff, d_model] (out = d_ff),
+ * down is [E, d_model, d_ff]. */
+typedef struct {
+    moe_q4_tensor gate, up, down;
+} moe_ffn_experts;
+
+/* ffn_gate_inp: weight fp32 [E, d_model]; bias fp32 [E] or NULL, added to the
+ * logits before the softmax (it moves both the selection and the weights). */
+typedef struct {
+    const float *weight;
+    const float *bias;
+} moe_ffn_router;
+
+/* Shared expert, bf16: gate, up [d_ff_shared, d_model]; down [d_model,
+ * d_ff_shared]; gate_inp (ffn_gate_inp_shexp) [d_model] or NULL, in which case
+ * sgate = 1. */
+typedef struct {
+    const uint16_t *gate_inp;
+    const uint16_t *gate;
+    const uint16_t *up;
+    const uint16_t *down;
+} moe_ffn_shared;
+
+/* Bytes of device workspace a call with T tokens needs (0 for T == 0; 0 for
+ * invalid dims or T).  The workspace needs no initialisation and holds no
+ * state between calls. */
+size_t moe_ffn_workspace_size(const moe_ffn_dims *dims, int64_t T);
+
+/* y[T, d_model] bf16 = the FFN above applied to x[T, d_model] bf16.
+ *
+ * router, experts: required.  shared: NULL means no shared expert (y =
+ * moe_out).  topk_idx int32 [T, top_k] and topk_weight fp32 [T, top_k]:
+ * optional outputs (NULL to skip): the selected experts in descending logit
+ * order (ties to the lower index) and their renormalised softmax weights.
+ * Routing uses fp32 logits.  y is rounded once, to nearest even.
+ * T == 0 returns MOE_FFN_OK without launching anything. */
+int moe_ffn_forward(const moe_ffn_dims *dims, int64_t T, const uint16_t *x, const moe_ffn_router *router,
+                    const moe_ffn_experts *experts, const moe_ffn_shared *shared, uint16_t *y,
+                    int32_t *topk_idx, float *topk_weight, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* moe_ffn_forward with the execution path forced (MOE_FFN_PATH_*).  Both
+ * paths compute the same function; they differ in kernels and rounding
+ * order.  The decode path accepts T <= MOE_FFN_DECODE_MAX_T only. */
+int moe_ffn_forward_path(const moe_ffn_dims *dims, int64_t T, const uint16_t *x, const moe_ffn_router *router,
+                         const moe_ffn_experts *experts, const moe_ffn_shared *shared, uint16_t *y,
+                         int32_t *topk_idx, float *topk_weight, void *workspace, size_t workspace_bytes,
+                         void *stream, int path);
+
+/* Static string for a status code. */
+const char *moe_ffn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

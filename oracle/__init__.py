@@ -78,6 +78,8 @@ class Oracle:
         L.moe_oracle_forward.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Layer), i64, vp, vp, i64,
                                          vp, vp, vp, vp, vp, ctypes.c_int]
         L.moe_oracle_forward.restype = ctypes.c_int
+        L.moe_oracle_route.argtypes = L.moe_oracle_forward.argtypes[:6] + [vp, vp, vp, vp, ctypes.c_int]
+        L.moe_oracle_route.restype = ctypes.c_int
         self.L = L
         self.path = lib_path
 
@@ -159,6 +161,29 @@ class Oracle:
         if st != 0:
             raise ValueError(f"moe_oracle_forward failed: {st}")
         out = dict(y=y, idx=idx, w=w, margin=margin)
+        if want_logits:
+            out["logits"] = logits
+        return out
+
+
+    def route(self, lay, x: np.ndarray, tokens=None, nthreads=None, want_logits=False) -> dict:
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        T, D = x.shape
+        tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
+        n = T if tok is None else tok.size
+        k, E = lay.dims.top_k, lay.dims.n_experts
+        idx = np.empty((n, k), dtype=np.int32)
+        w = np.empty((n, k), dtype=np.float64)
+        margin = np.empty(n, dtype=np.float64)
+        logits = np.empty((n, E), dtype=np.float64) if want_logits else None
+        d, l = self._dims(lay.dims), self._layer(lay)
+        st = self.L.moe_oracle_route(ctypes.byref(d), ctypes.byref(l), T, x.ctypes.data,
+                                     None if tok is None else tok.ctypes.data, n, idx.ctypes.data, w.ctypes.data,
+                                     margin.ctypes.data, None if logits is None else logits.ctypes.data,
+                                     nthreads or default_threads())
+        if st != 0:
+            raise ValueError(f"moe_oracle_route failed: {st}")
+        out = dict(idx=idx, w=w, margin=margin)
         if want_logits:
             out["logits"] = logits
         return out

@@ -241,3 +241,68 @@ int moe_oracle_forward(const moe_oracle_dims *d, const moe_oracle_layer *L, int6
     }
     return st;
 }
+
+/* ------------------------------------------------------------- routing only */
+typedef struct {
+    const moe_oracle_dims *d;
+    const moe_oracle_layer *L;
+    const uint16_t *x;
+    const int64_t *tokens;
+    int32_t *idx;
+    double *w, *margin, *logits;
+    int64_t lo, hi;
+    int status;
+} route_job;
+
+static void *route_range(void *p) {
+    route_job *j = (route_job *)p;
+    const int64_t D = j->d->d_model, E = j->d->n_experts, k = j->d->top_k;
+    double *lg = (double *)malloc(sizeof(double) * (size_t)E);
+    double *ww = (double *)malloc(sizeof(double) * (size_t)k);
+    int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    if (!lg || !ww || !sel) j->status = MOE_ORACLE_ENOMEM;
+    for (int64_t n = j->lo; n < j->hi && j->status == MOE_ORACLE_OK; n++) {
+        const int64_t t = j->tokens ? j->tokens[n] : n;
+        double mg = 0.0;
+        moe_oracle_router_logits(j->d, j->L, j->x + t * D, lg);
+        j->status = moe_oracle_select(lg, E, k, sel, ww, &mg);
+        if (j->idx) for (int64_t r = 0; r < k; r++) j->idx[n * k + r] = sel[r];
+        if (j->w) for (int64_t r = 0; r < k; r++) j->w[n * k + r] = ww[r];
+        if (j->margin) j->margin[n] = mg;
+        if (j->logits) for (int64_t e = 0; e < E; e++) j->logits[n * E + e] = lg[e];
+    }
+    free(lg); free(ww); free(sel);
+    return NULL;
+}
+
+int moe_oracle_route(const moe_oracle_dims *d, const moe_oracle_layer *L, int64_t T, const uint16_t *x,
+                     const int64_t *tokens, int64_t n_tok, int32_t *idx, double *w, double *margin, double *logits,
+                     int nthreads) {
+    if (!d || !L || !L->router_w || (!x && n_tok > 0) || T < 0 || n_tok < 0) return MOE_ORACLE_EINVAL;
+    if (d->n_experts <= 0 || d->top_k <= 0 || d->top_k > d->n_experts || d->d_model <= 0) return MOE_ORACLE_EINVAL;
+    if (!tokens && n_tok != T) return MOE_ORACLE_EINVAL;
+    if (tokens)
+        for (int64_t n = 0; n < n_tok; n++)
+            if (tokens[n] < 0 || tokens[n] >= T) return MOE_ORACLE_EINVAL;
+    if (n_tok == 0) return MOE_ORACLE_OK;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > n_tok) nthreads = (int)n_tok;
+    route_job jobs[256];
+    pthread_t th[256];
+    int joinable[256];
+    int64_t chunk = (n_tok + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; t++) {
+        int64_t lo = t * chunk, hi = lo + chunk < n_tok ? lo + chunk : n_tok;
+        jobs[t] = (route_job){d, L, x, tokens, idx, w, margin, logits, lo, hi < lo ? lo : hi, MOE_ORACLE_OK};
+        joinable[t] = 0;
+        if (nthreads > 1 && pthread_create(&th[t], NULL, route_range, &jobs[t]) == 0) joinable[t] = 1;
+        else route_range(&jobs[t]);
+    }
+    int st = MOE_ORACLE_OK;
+    for (int t = 0; t < nthreads; t++) {
+        if (joinable[t]) pthread_join(th[t], NULL);
+        if (jobs[t].status != MOE_ORACLE_OK) st = jobs[t].status;
+    }
+    return st;
+}

@@ -105,6 +105,12 @@ int moe_oracle_forward(const moe_oracle_dims *d, const moe_oracle_layer *L, int6
                        const int64_t *tokens, int64_t n_tok, double *y, int32_t *idx, double *w, double *margin,
                        double *logits, int nthreads);
 
+/* Routing only (logits, selection, weights, margin) for the listed tokens;
+ * same conventions as moe_oracle_forward. */
+int moe_oracle_route(const moe_oracle_dims *d, const moe_oracle_layer *L, int64_t T, const uint16_t *x,
+                     const int64_t *tokens, int64_t n_tok, int32_t *idx, double *w, double *margin, double *logits,
+                     int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,174 @@
+"""Python binding of libmoe_ffn.so, the MI355X (gfx950) sparse shared-expert
+MoE FFN.
+
+Marshalling only: every step of the FFN runs in the library's HIP kernels.
+PyTorch provides device memory and streams.  The functions carry the C
+entry points' names; see include/moe_ffn.h for the contract.  There is no
+CPU fallback: if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
+
+MOE_FFN_OK = 0
+MOE_FFN_EINVAL = -1
+MOE_FFN_EUNSUPPORTED = -2
+MOE_FFN_EALIGN = -3
+MOE_FFN_EWORKSPACE = -4
+MOE_FFN_EHIP = -5
+PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+DECODE_MAX_T = 64
+
+EXPORTED = ("moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_path", "moe_ffn_status_string")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("d_model", "n_experts", "top_k", "d_ff", "d_ff_shared", "group_size")]
+
+
+DIMS = Dims(2048, 256, 8, 512, 512, 64)
+
+
+class Q4Tensor(ctypes.Structure):
+    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class Experts(ctypes.Structure):
+    _fields_ = [("gate", Q4Tensor), ("up", Q4Tensor), ("down", Q4Tensor)]
+
+
+class Router(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+class Shared(ctypes.Structure):
+    _fields_ = [("gate_inp", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p),
+                ("down", ctypes.c_void_p)]
+
+
+class MoeFfnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m sparse_moe_ffn_fp32_amd.build` "
+                               "(or __graft_entry__.build())")
+        L = ctypes.CDLL(path)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.moe_ffn_workspace_size.argtypes = [ctypes.POINTER(Dims), i64]
+        L.moe_ffn_workspace_size.restype = ctypes.c_size_t
+        fwd = [ctypes.POINTER(Dims), i64, vp, ctypes.POINTER(Router), ctypes.POINTER(Experts),
+               ctypes.POINTER(Shared), vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.moe_ffn_forward.argtypes = fwd
+        L.moe_ffn_forward.restype = ctypes.c_int
+        L.moe_ffn_forward_path.argtypes = fwd + [ctypes.c_int]
+        L.moe_ffn_forward_path.restype = ctypes.c_int
+        L.moe_ffn_status_string.argtypes = [ctypes.c_int]
+        L.moe_ffn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+@dataclass
+class DeviceLayer:
+    """Device-resident weights of one layer (torch tensors; bf16 as int16 bits)."""
+    router_w: object
+    router_b: object
+    gate: tuple
+    up: tuple
+    down: tuple
+    sh_gate_inp: object
+    sh_gate: object
+    sh_up: object
+    sh_down: object
+
+    @staticmethod
+    def from_host(layer, device="cuda") -> "DeviceLayer":
+        import numpy as np
+        import torch
+
+        def t(a, dt):
+            if a is None:
+                return None
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+
+        def q(q4):
+            return (t(q4.qweight, np.int32), t(q4.scales, np.int16), t(q4.biases, np.int16))
+
+        return DeviceLayer(t(layer.router_w, np.float32), t(layer.router_b, np.float32), q(layer.gate),
+                           q(layer.up), q(layer.down), t(layer.sh_gate_inp, np.int16), t(layer.sh_gate, np.int16),
+                           t(layer.sh_up, np.int16), t(layer.sh_down, np.int16))
+
+    def structs(self):
+        r = Router(_ptr(self.router_w), _ptr(self.router_b))
+        ex = Experts(*(Q4Tensor(*(_ptr(a) for a in m)) for m in (self.gate, self.up, self.down)))
+        sh = None
+        if self.sh_gate is not None:
+            sh = Shared(_ptr(self.sh_gate_inp), _ptr(self.sh_gate), _ptr(self.sh_up), _ptr(self.sh_down))
+        return r, ex, sh
+
+
+def moe_ffn_status_string(status: int) -> str:
+    return lib().moe_ffn_status_string(status).decode()
+
+
+def moe_ffn_workspace_size(T: int, dims: Dims = DIMS) -> int:
+    return int(lib().moe_ffn_workspace_size(ctypes.byref(dims), T))
+
+
+def _stream_ptr(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def moe_ffn_forward_path(x, layer: DeviceLayer, y, workspace, topk_idx=None, topk_weight=None, stream=None,
+                         path: int = PATH_AUTO, dims: Dims = DIMS, T: Optional[int] = None,
+                         workspace_bytes: Optional[int] = None, check: bool = True) -> int:
+    """Enqueue one FFN call on `stream` (default: torch's current stream).
+    x, y: int16 tensors [T, d_model] holding bf16 bits.  Returns the status;
+    raises MoeFfnError on a non-zero status when check is True."""
+    r, ex, sh = layer.structs()
+    T = x.shape[0] if T is None else T
+    wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    if workspace_bytes is not None:
+        wsb = workspace_bytes
+    st = lib().moe_ffn_forward_path(ctypes.byref(dims), T, _ptr(x), ctypes.byref(r), ctypes.byref(ex),
+                                    ctypes.byref(sh) if sh is not None else None, _ptr(y), _ptr(topk_idx),
+                                    _ptr(topk_weight), _ptr(workspace), wsb, _stream_ptr(stream), path)
+    if check and st != MOE_FFN_OK:
+        raise MoeFfnError(st, moe_ffn_status_string(st))
+    return st
+
+
+def moe_ffn_forward(x, layer: DeviceLayer, y, workspace, topk_idx=None, topk_weight=None, stream=None,
+                    **kw) -> int:
+    return moe_ffn_forward_path(x, layer, y, workspace, topk_idx, topk_weight, stream, PATH_AUTO, **kw)
+
+
+def alloc_workspace(T: int, device="cuda"):
+    import torch
+    n = moe_ffn_workspace_size(T)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

@@ -1,0 +1,165 @@
+// C-ABI entry points: argument validation, workspace carve-up, path choice,
+// launches on the caller's stream.  See include/moe_ffn.h for the contract.
+#include "../../include/moe_ffn.h"
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Byte offsets of every workspace region for T tokens.
+struct Layout {
+    size_t wr3, logits, idx, w, sgate, xh, cnt, offs, tiles, tile_count, perm, pos_of, h, hs, partial, total;
+};
+
+Layout layout(int64_t T) {
+    const size_t N = (size_t)T * K;
+    const int nblk = sort_blocks((int)N);
+    const size_t max_tiles = (N + gemm_bm() - 1) / gemm_bm() + E;
+    Layout L{};
+    size_t o = 0;
+    L.wr3 = o;        o += up((size_t)3 * E * D * 2);
+    L.logits = o;     o += up((size_t)T * E * 4);
+    L.idx = o;        o += up(N * 4);
+    L.w = o;          o += up(N * 4);
+    L.sgate = o;      o += up((size_t)T * 4);
+    L.xh = o;         o += up((size_t)T * D * 2);
+    L.cnt = o;        o += up((size_t)nblk * E * 4);
+    L.offs = o;       o += up((E + 1) * 4);
+    L.tiles = o;      o += up(max_tiles * 2 * 4);
+    L.tile_count = o; o += up(4);
+    L.perm = o;       o += up(N * 4);
+    L.pos_of = o;     o += up(N * 4);
+    L.h = o;          o += up(N * F * 2);
+    L.hs = o;         o += up((size_t)T * FS * 2);
+    L.partial = o;    o += up(N * D * 4);
+    L.total = o;
+    return L;
+}
+
+bool dims_ok(const moe_ffn_dims* d) {
+    return d->d_model == D && d->n_experts == E && d->top_k == K && d->d_ff == F && d->d_ff_shared == FS &&
+           d->group_size == G;
+}
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
+             const moe_ffn_experts* ex, const moe_ffn_shared* sh, uint16_t* y, int32_t* topk_idx,
+             float* topk_weight, void* ws, size_t ws_bytes, int path) {
+    if (!dims || T < 0 || path < MOE_FFN_PATH_AUTO || path > MOE_FFN_PATH_PREFILL) return MOE_FFN_EINVAL;
+    if (!dims_ok(dims)) return MOE_FFN_EUNSUPPORTED;
+    if (T > MOE_FFN_MAX_T) return MOE_FFN_EUNSUPPORTED;
+    if (T == 0) return MOE_FFN_OK;
+    if (!x || !y || !router || !router->weight || !ex) return MOE_FFN_EINVAL;
+    const void* req[] = {ex->gate.qweight, ex->gate.scales, ex->gate.biases, ex->up.qweight, ex->up.scales,
+                         ex->up.biases, ex->down.qweight, ex->down.scales, ex->down.biases};
+    for (const void* p : req)
+        if (!p) return MOE_FFN_EINVAL;
+    if (sh && (!sh->gate || !sh->up || !sh->down)) return MOE_FFN_EINVAL;
+    for (const void* p : req)
+        if (!al16(p)) return MOE_FFN_EALIGN;
+    const void* opt[] = {x, y, router->weight, router->bias, topk_idx, topk_weight,
+                         sh ? sh->gate : nullptr, sh ? sh->up : nullptr, sh ? sh->down : nullptr,
+                         sh ? sh->gate_inp : nullptr, ws};
+    for (const void* p : opt)
+        if (p && !al16(p)) return MOE_FFN_EALIGN;
+    if (path == MOE_FFN_PATH_DECODE) return MOE_FFN_EUNSUPPORTED;
+    if (!ws || ws_bytes < layout(T).total) return MOE_FFN_EWORKSPACE;
+    return MOE_FFN_OK;
+}
+
+int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const moe_ffn_experts* ex,
+                const moe_ffn_shared* sh, uint16_t* y, int32_t* idx_user, float* w_user, char* ws,
+                hipStream_t s) {
+    const Layout L = layout(T);
+    const int N = T * K;
+    auto at = [&](size_t off) { return (void*)(ws + off); };
+    uint16_t* wr3 = (uint16_t*)at(L.wr3);
+    float* logits = (float*)at(L.logits);
+    int32_t* idx = idx_user ? idx_user : (int32_t*)at(L.idx);
+    float* w = w_user ? w_user : (float*)at(L.w);
+    float* sgate = (float*)at(L.sgate);
+    uint16_t* xh = (uint16_t*)at(L.xh);
+    int32_t* cnt = (int32_t*)at(L.cnt);
+    int32_t* offs = (int32_t*)at(L.offs);
+    int32_t* tiles = (int32_t*)at(L.tiles);
+    int32_t* tile_count = (int32_t*)at(L.tile_count);
+    int32_t* perm = (int32_t*)at(L.perm);
+    int32_t* pos_of = (int32_t*)at(L.pos_of);
+
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    chk(launch_split_router(router->weight, wr3, s));
+    chk(launch_prep_x(x, xh, T, s));
+    chk(launch_router_logits(x, wr3, router->bias, logits, T, s));
+    chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, T, s));
+    chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(), s));
+    PrefillGemmParams p{};
+    p.xh = xh;
+    p.h = (uint16_t*)at(L.h);
+    p.hs = (uint16_t*)at(L.hs);
+    p.perm = perm;
+    p.pos_of = pos_of;
+    p.offs = offs;
+    p.tiles = tiles;
+    p.tile_count = tile_count;
+    p.wflat = w;
+    p.sgate = sgate;
+    p.gate_q = ex->gate.qweight; p.gate_s = ex->gate.scales; p.gate_b = ex->gate.biases;
+    p.up_q = ex->up.qweight;     p.up_s = ex->up.scales;     p.up_b = ex->up.biases;
+    p.down_q = ex->down.qweight; p.down_s = ex->down.scales; p.down_b = ex->down.biases;
+    p.sh_gate = sh ? sh->gate : nullptr;
+    p.sh_up = sh ? sh->up : nullptr;
+    p.sh_down = sh ? sh->down : nullptr;
+    p.partial = (float*)at(L.partial);
+    p.y = y;
+    p.T = T;
+    chk(launch_prefill_gemms(p, s));
+    return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_ffn_workspace_size(const moe_ffn_dims* dims, int64_t T) {
+    if (!dims || !dims_ok(dims) || T <= 0 || T > MOE_FFN_MAX_T) return 0;
+    return layout(T).total;
+}
+
+int moe_ffn_forward_path(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
+                         const moe_ffn_experts* experts, const moe_ffn_shared* shared, uint16_t* y,
+                         int32_t* topk_idx, float* topk_weight, void* workspace, size_t workspace_bytes,
+                         void* stream, int path) {
+    int st = validate(dims, T, x, router, experts, shared, y, topk_idx, topk_weight, workspace, workspace_bytes,
+                      path);
+    if (st != MOE_FFN_OK || T == 0) return st;
+    return run_prefill((int)T, x, router, experts, shared, y, topk_idx, topk_weight, (char*)workspace,
+                       (hipStream_t)stream);
+}
+
+int moe_ffn_forward(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
+                    const moe_ffn_experts* experts, const moe_ffn_shared* shared, uint16_t* y, int32_t* topk_idx,
+                    float* topk_weight, void* workspace, size_t workspace_bytes, void* stream) {
+    return moe_ffn_forward_path(dims, T, x, router, experts, shared, y, topk_idx, topk_weight, workspace,
+                                workspace_bytes, stream, MOE_FFN_PATH_AUTO);
+}
+
+const char* moe_ffn_status_string(int status) {
+    switch (status) {
+        case MOE_FFN_OK: return "ok";
+        case MOE_FFN_EINVAL: return "invalid argument";
+        case MOE_FFN_EUNSUPPORTED: return "unsupported shape, size or path";
+        case MOE_FFN_EALIGN: return "pointer not 16-byte aligned";
+        case MOE_FFN_EWORKSPACE: return "workspace missing or too small";
+        case MOE_FFN_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router (k_router.hip)
+hipError_t launch_split_router(const float* wr, uint16_t* wr3, hipStream_t s);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr3, const float* bias, float* logits, int T,
+                                hipStream_t s);
+hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
+                       float* sgate, int T, hipStream_t s);
+
+// ---- routing sort (k_sort.hip)
+int sort_blocks(int N);
+hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tile_count,
+                       int32_t* perm, int32_t* pos_of, int bm, hipStream_t s);
+
+// ---- grouped GEMMs (k_gemm.hip)
+struct PrefillGemmParams {
+    const uint16_t* xh;
+    uint16_t* h;
+    uint16_t* hs;
+    const int32_t* perm;
+    const int32_t* pos_of;
+    const int32_t* offs;
+    const int32_t* tiles;
+    const int32_t* tile_count;
+    const float* wflat;
+    const float* sgate;
+    const uint32_t *gate_q, *up_q, *down_q;
+    const uint16_t *gate_s, *up_s, *down_s;
+    const uint16_t *gate_b, *up_b, *down_b;
+    const uint16_t *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
+    float* partial;
+    uint16_t* y;
+    int T;
+};
+int gemm_bm();
+hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s);
+hipError_t launch_prefill_gemms(const PrefillGemmParams& p, hipStream_t s);
+
+}  // namespace moe

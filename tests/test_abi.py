@@ -1,0 +1,100 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+header declares, sizes workspaces, and rejects bad arguments before any
+launch (no GPU needed: every call here returns from validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_ffn_fp32_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_ffn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from sparse_moe_ffn_fp32_amd import build
+        build.build()
+    return moe.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_ffn_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert moe.moe_ffn_status_string(st)
+    assert moe.moe_ffn_status_string(-99) == "unknown status"
+
+
+def test_workspace_size(L):
+    assert moe.moe_ffn_workspace_size(0) == 0
+    assert moe.moe_ffn_workspace_size(-1) == 0
+    a, b = moe.moe_ffn_workspace_size(1), moe.moe_ffn_workspace_size(4096)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+    bad = moe.Dims(2048, 128, 8, 512, 512, 64)
+    assert L.moe_ffn_workspace_size(ctypes.byref(bad), 4) == 0
+
+
+class _Fake:
+    """Device pointers that are never dereferenced (validation fails first)."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+    numel = staticmethod(lambda: 1 << 40)
+    element_size = staticmethod(lambda: 1)
+
+
+def _layer(base=0x10000000):
+    f = lambda i: _Fake(base + 0x1000 * i)
+    return moe.DeviceLayer(f(1), None, (f(2), f(3), f(4)), (f(5), f(6), f(7)), (f(8), f(9), f(10)), f(11),
+                           f(12), f(13), f(14))
+
+
+def _call(L, T=4, x=0x20000000, y=0x30000000, ws=0x40000000, wsb=None, layer=None, dims=moe.DIMS, path=0,
+          idx=None, w=None):
+    layer = layer or _layer()
+    r, ex, sh = layer.structs()
+    wsb = moe.moe_ffn_workspace_size(max(T, 1)) if wsb is None else wsb
+    return L.moe_ffn_forward_path(ctypes.byref(dims), T, x, ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh),
+                                  y, idx, w, ws, wsb, None, path)
+
+
+def test_rejects_bad_arguments(L):
+    assert _call(L, T=0) == moe.MOE_FFN_OK  # no launch for T == 0
+    assert _call(L, T=-1) == moe.MOE_FFN_EINVAL
+    assert _call(L, x=None) == moe.MOE_FFN_EINVAL
+    assert _call(L, y=None) == moe.MOE_FFN_EINVAL
+    assert _call(L, path=7) == moe.MOE_FFN_EINVAL
+    assert _call(L, dims=moe.Dims(2048, 256, 8, 512, 512, 32)) == moe.MOE_FFN_EUNSUPPORTED
+    assert _call(L, T=(1 << 20) + 1) == moe.MOE_FFN_EUNSUPPORTED
+    assert _call(L, x=0x20000008) == moe.MOE_FFN_EALIGN
+    assert _call(L, idx=0x50000004) == moe.MOE_FFN_EALIGN
+    assert _call(L, ws=None) == moe.MOE_FFN_EWORKSPACE
+    assert _call(L, wsb=1024) == moe.MOE_FFN_EWORKSPACE
+    lay = _layer()
+    lay.up = (lay.up[0], None, lay.up[2])
+    assert _call(L, layer=lay) == moe.MOE_FFN_EINVAL
+    lay = _layer()
+    lay.sh_down = None
+    assert _call(L, layer=lay) == moe.MOE_FFN_EINVAL
+    lay = _layer()
+    lay.down = (_Fake(0x60000002), lay.down[1], lay.down[2])
+    assert _call(L, layer=lay) == moe.MOE_FFN_EALIGN
+    assert L.moe_ffn_forward_path(None, 4, 1, None, None, None, 1, None, None, 1, 1, None, 0) == moe.MOE_FFN_EINVAL

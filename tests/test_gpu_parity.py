@@ -1,0 +1,157 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+seeded inputs, at sizes the oracle finishes in seconds and at the measured
+configurations' full sizes (routing on every token, outputs on samples)."""
+from __future__ import annotations
+
+import copy
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import workloads
+from gpu_common import GpuRunner, output_check, routing_check, bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_moe_ffn_fp32_amd as moe
+    moe.lib()
+    return GpuRunner(torch)
+
+
+@pytest.fixture(scope="module")
+def layer0():
+    return workloads.layer_for(0)
+
+
+PATHS = {"auto": 0, "prefill": 2}
+
+
+def test_config0_T4(gpu, layer0):
+    x, _, _ = workloads.enforce_margin(layer0, 4, 0)
+    _say("config0 T=4")
+    y, idx, w = gpu.run(layer0, x)
+    _say(routing_check(layer0, x, idx, w), output_check(layer0, x, y))
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 17, 63, 64, 65, 100, 257])
+@pytest.mark.parametrize("path", ["auto", "prefill"])
+def test_ragged_T(gpu, layer0, T, path):
+    x, _, _ = workloads.enforce_margin(layer0, T, 100 + T)
+    _say(f"ragged T={T} path={path}")
+    y, idx, w = gpu.run(layer0, x, path=PATHS[path])
+    routing_check(layer0, x, idx, w)
+    _say(output_check(layer0, x, y))
+
+
+def test_config2_T64(gpu):
+    layer, x, meta = workloads.config(2)
+    _say("config2 T=64")
+    y, idx, w = gpu.run(layer, x)
+    _say(routing_check(layer, x, idx, w), output_check(layer, x, y))
+
+
+def test_config3_T4096_skewed(gpu):
+    layer, x, meta = workloads.config(3)
+    _say("config3 T=4096")
+    y, idx, w = gpu.run(layer, x)
+    _say(routing_check(layer, x, idx, w))
+    sample = np.unique(np.concatenate([np.arange(0, 4096, 16), np.arange(4089, 4096)]))
+    _say(output_check(layer, x, y, tokens=sample))
+
+
+def test_config4_T32768_skewed_ties(gpu):
+    layer, x, meta = workloads.config(4)
+    ties = meta["ties"]
+    _say(f"config4 T=32768, {ties.size} near-tie tokens")
+    y, idx, w = gpu.run(layer, x)
+    _say(routing_check(layer, x, idx, w))
+    sample = np.unique(np.concatenate([np.arange(0, 32768, 256), ties[::16], np.arange(32760, 32768)]))
+    _say(output_check(layer, x, y, tokens=sample))
+
+
+@pytest.mark.parametrize("variant", ["no_shared", "no_gate_inp", "router_bias"])
+def test_layer_variants(gpu, variant):
+    kw = dict(no_shared=dict(shared=False), no_gate_inp=dict(gate_inp=False), router_bias=dict(zipf_s=1.0))[variant]
+    layer = synth.make_layer(7, **kw)
+    x, _, _ = workloads.enforce_margin(layer, 37, 7)
+    _say(f"variant {variant}")
+    y, idx, w = gpu.run(layer, x)
+    routing_check(layer, x, idx, w)
+    _say(output_check(layer, x, y))
+
+
+def test_zero_tokens(gpu, layer0):
+    import sparse_moe_ffn_fp32_amd as moe
+    torch = gpu.torch
+    x = torch.zeros((1, 2048), dtype=torch.int16, device="cuda")
+    y = torch.full((1, 2048), 7, dtype=torch.int16, device="cuda")
+    st = moe.moe_ffn_forward(x, gpu.device_layer(layer0), y, None, T=0)
+    torch.cuda.synchronize()
+    assert st == 0 and bool((y == 7).all())
+
+
+def test_zero_input_gives_zero(gpu, layer0):
+    x = np.zeros((9, 2048), dtype=np.uint16)
+    y, idx, w = gpu.run(layer0, x)
+    assert np.all(bf16_to_f64(y) == 0.0)
+    assert np.all(idx == np.arange(8)[None, :]) and np.all(w == np.float32(0.125))
+
+
+def test_deterministic_and_no_unwritten_reads(gpu, layer0):
+    """Run-to-run bitwise identical, also with the workspace filled with 0xFF
+    (NaN in every float slot) beforehand: nothing reads unwritten scratch."""
+    x, _, _ = workloads.enforce_margin(layer0, 300, 5)
+    a = gpu.run(layer0, x)
+    b = gpu.run(layer0, x, poison=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    assert not np.isnan(bf16_to_f64(b[0])).any()
+
+
+def test_token_permutation_invariance(gpu, layer0):
+    """Permuting tokens permutes the outputs bit for bit."""
+    x, _, _ = workloads.enforce_margin(layer0, 300, 6)
+    perm = np.random.default_rng(0).permutation(300)
+    a = gpu.run(layer0, x)
+    b = gpu.run(layer0, x[perm])
+    for u, v in zip(a, b):
+        assert np.array_equal(u[perm], v)
+
+
+def test_down_scale_halving(gpu):
+    """Halving every down scale and bias halves y exactly (no shared
+    expert; all values stay normal)."""
+    layer = workloads.layer_for(8, shared=False)
+    half = copy.deepcopy(layer)
+    for arr in (half.down.scales, half.down.biases):
+        arr[:] = synth.f32_to_bf16(synth.bf16_to_f32(arr) * np.float32(0.5))
+    x, _, _ = workloads.enforce_margin(layer, 70, 8)
+    ya = gpu.run(layer, x)[0]
+    yb = gpu.run(half, x)[0]
+    assert np.array_equal(bf16_to_f64(yb), 0.5 * bf16_to_f64(ya))
+
+
+def test_gate_up_swap_is_detected(gpu, layer0):
+    """Swapping gate and up pointers breaks parity by far (negative test of
+    the comparison itself)."""
+    sw = copy.deepcopy(layer0)
+    sw.gate, sw.up = sw.up, sw.gate
+    x, _, _ = workloads.enforce_margin(layer0, 8, 9)
+    y = gpu.run(sw, x)[0]
+    ref = oracle.get().forward(layer0, x)["y"]
+    rel = np.linalg.norm(bf16_to_f64(y) - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert rel.min() > 0.2
