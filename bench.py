@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""MoE-FFN throughput on one MI355X, with the dominant kernel's roofline and
+the fp64 CPU oracle timed beside it.
+
+Default workload: 40 independent MoE FFN layers (seeds 0..39) at decode T=1,
+the whole ~18 GB of 4-bit expert weights resident in HBM; one step = one
+token through all 40 layers (40 library calls on one stream).  Other
+workloads (single layers, flushed between repetitions) are available with
+--workload for measurement.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0
+EXPERT_BYTES = 3 * (512 * 2048 // 2 + 2 * 512 * 32 * 2)  # gate+up+down packed + scales + biases = 1,769,472
+GU_BYTES = 2 * (512 * 2048 // 2 + 2 * 512 * 32 * 2)      # gate+up of one expert = 1,179,648
+SHARED_BYTES = 3 * 512 * 2048 * 2
+ROUTER_BYTES = 256 * 2048 * 4
+GATE_INP_BYTES = 2048 * 2
+
+WORKLOADS = {
+    "decode_T1_40layers": dict(T=1, layers=40, zipf=None, flush=False),
+    "decode_T4": dict(T=4, layers=1, zipf=None, flush=True),
+    "decode_T64": dict(T=64, layers=1, zipf=None, flush=True),
+    "prefill_T4096_zipf1.0": dict(T=4096, layers=1, zipf=1.0, flush=True),
+    "prefill_T32768_zipf1.5": dict(T=32768, layers=1, zipf=1.5, flush=True),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """hipEvent_t handles through the HIP runtime's C API."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, e, stream):
+        assert self.L.hipEventRecord(e, ctypes.c_void_p(stream.cuda_stream)) == 0
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        assert self.L.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(e)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_T1_40layers", choices=sorted(WORKLOADS))
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 decode, 2 prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every traced kernel (stderr)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import sparse_moe_ffn_fp32_amd as moe
+
+    wl = WORKLOADS[args.workload]
+    T, nlayers = wl["T"], wl["layers"]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    moe.lib()
+    hip = Hip()
+
+    # ---------------------------------------------------------------- inputs
+    n_cpu_layers = min(nlayers, 8)
+    host_layers, dev_layers, xs = [], [], []
+    t0 = time.time()
+    for l in range(nlayers):
+        layer = synth.make_layer(l, zipf_s=wl["zipf"])
+        x = synth.x_rows(l, T, 2048)
+        dev_layers.append(moe.DeviceLayer.from_host(layer, dev))
+        xs.append(torch.from_numpy(x.view(np.int16)).to(dev))
+        if l < n_cpu_layers:
+            host_layers.append((layer, x))
+        del layer
+        if nlayers > 1 and (l % 8 == 7 or l == nlayers - 1):
+            log(f"generated and uploaded layer {l + 1}/{nlayers} ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    ys = [torch.empty((T, 2048), dtype=torch.int16, device=dev) for _ in range(nlayers)]
+    idxs = [torch.empty((T, 8), dtype=torch.int32, device=dev) for _ in range(nlayers)]
+    ws_ = [torch.empty((T, 8), dtype=torch.float32, device=dev) for _ in range(nlayers)]
+    wspace = moe.alloc_workspace(T, dev)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if wl["flush"] else None
+    stream = torch.cuda.current_stream()
+
+    def call(l, trace=None):
+        moe.moe_ffn_forward_traced(xs[l], dev_layers[l], ys[l], wspace, idxs[l], ws_[l], stream=stream,
+                                   path=args.path, trace=trace)
+
+    dom_kernel = moe.KERNEL_EXPERT_GU
+
+    def run_steps(nsteps, kernel=None):
+        """nsteps steps; returns (wall seconds, per-launch ms of `kernel`)."""
+        ev = []
+        if kernel is not None:
+            ev = [(hip.event(), hip.event()) for _ in range(nsteps * nlayers)]
+        if flush_buf is None:
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for s in range(nsteps):
+                for l in range(nlayers):
+                    tr = moe.Trace(kernel, *ev[s * nlayers + l]) if kernel is not None else None
+                    call(l, tr)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t
+            step_ms = None
+        else:
+            # single layer: write 1 GiB between repetitions (outside the timed
+            # call) so no weights stay in the caches; time each call with events
+            step_ms = []
+            se, ee = hip.event(), hip.event()
+            for s in range(nsteps):
+                flush_buf.fill_(s & 0xFF)
+                torch.cuda.synchronize()
+                hip.record(se, stream)
+                tr = moe.Trace(kernel, *ev[s]) if kernel is not None else None
+                call(0, tr)
+                hip.record(ee, stream)
+                step_ms.append(hip.elapsed_ms(se, ee))
+            hip.destroy(se)
+            hip.destroy(ee)
+            wall = float(np.median(step_ms)) * 1e-3 * nsteps
+        kms = [hip.elapsed_ms(a, b) for a, b in ev]
+        for a, b in ev:
+            hip.destroy(a)
+            hip.destroy(b)
+        return wall, kms
+
+    log(f"warmup {args.warmup} steps")
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    distinct = [np.unique(i.cpu().numpy()).size for i in idxs]
+
+    log(f"timing {args.steps} steps")
+    wall, kms = run_steps(args.steps, dom_kernel)
+    ms_per_step = 1000.0 * wall / args.steps
+    tokens_per_step = T  # one step pushes T tokens through all `nlayers` layers
+    value = tokens_per_step / (wall / args.steps)
+
+    # dominant kernel: algorithmic bytes / flops per launch
+    kernel_ms = float(np.mean(kms))
+    if T <= 64:
+        gu_bytes = [d * GU_BYTES + T * 2048 * 2 + T * 8 * 512 * 4 for d in distinct]
+        per_launch = float(np.mean(gu_bytes))
+        achieved = per_launch / (kernel_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
+                    kernel="expert_gate_up", alg_bytes_per_launch=int(per_launch),
+                    avg_launch_us=round(kernel_ms * 1e3, 2))
+    else:
+        flops = 2.0 * T * 8 * 1024 * 2048
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_F16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_F16_TFLOPS, 4), traffic=None,
+                    kernel="expert_gate_up", alg_flops_per_launch=flops,
+                    avg_launch_us=round(kernel_ms * 1e3, 2))
+    step_bytes = sum(d * EXPERT_BYTES + SHARED_BYTES + ROUTER_BYTES + GATE_INP_BYTES + T * 2048 * 4
+                     for d in distinct)
+    log(f"step {ms_per_step * 1e3:.1f} us, {value:.1f} tok/s, step bytes {step_bytes / 1e6:.1f} MB "
+        f"-> {step_bytes / (wall / args.steps) / 1e9:.0f} GB/s; dominant kernel {kernel_ms * 1e3:.2f} us/launch")
+
+    if args.breakdown:
+        for kid, name in ((moe.KERNEL_ROUTER, "router"), (moe.KERNEL_EXPERT_GU, "expert_gu"),
+                          (moe.KERNEL_EXPERT_DOWN, "expert_down"), (moe.KERNEL_COMBINE, "combine")):
+            _, km = run_steps(max(2, args.steps // 4), kid)
+            log(f"  kernel {name}: {np.mean(km) * 1e3:.2f} us/launch")
+
+    # ---------------------------------------------------------------- oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import concurrent.futures as cf
+
+        import oracle
+        O = oracle.get()
+        cores = max(1, min(16, os.cpu_count() or 1))
+        if nlayers > 1:
+            threads = min(cores, len(host_layers))
+            done, t = 0, time.perf_counter()
+            with cf.ThreadPoolExecutor(threads) as ex:
+                while time.perf_counter() - t < 10.0:
+                    list(ex.map(lambda hx: O.forward(hx[0], hx[1], nthreads=1), host_layers))
+                    done += len(host_layers)
+            el = time.perf_counter() - t
+            cpu = dict(value=round((done / nlayers) * T / el, 3), unit="tokens/s", cores=threads, kind="oracle",
+                       sample=f"{len(host_layers)} of the {nlayers} layers at T={T}, {done} layer calls in "
+                              f"{el:.1f}s, one layer per thread; tokens/s scaled to the {nlayers}-layer step")
+        else:
+            layer, x = host_layers[0]
+            stride = max(1, T // 256)
+            tok = np.arange(0, T, stride)
+            t = time.perf_counter()
+            O.forward(layer, x, tokens=tok, nthreads=cores)
+            el = time.perf_counter() - t
+            cpu = dict(value=round(tok.size / el, 2), unit="tokens/s", cores=min(cores, tok.size), kind="oracle",
+                       sample=f"{tok.size} of {T} tokens (every {stride}th), {el:.1f}s")
+        log(f"oracle: {cpu}")
+
+    out = {
+        "metric": "MoE-FFN tokens/s (decode T=1..64; prefill T=4K) + % HBM / MFMA roofline",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "layers": nlayers,
+                   "router_bias_zipf_s": wl["zipf"], "distinct_experts_per_layer": float(np.mean(distinct)),
+                   "alg_bytes_per_step": int(step_bytes)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

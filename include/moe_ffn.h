@@ -128,6 +128,28 @@ int moe_ffn_forward_path(const moe_ffn_dims *dims, int64_t T, const uint16_t *x,
                          int32_t *topk_idx, float *topk_weight, void *workspace, size_t workspace_bytes,
                          void *stream, int path);
 
+/* Kernels a measurement tool can bracket with moe_ffn_forward_traced. */
+#define MOE_FFN_KERNEL_ROUTER 1      /* router logits (+ top-8 where fused) */
+#define MOE_FFN_KERNEL_EXPERT_GU 2   /* routed expert gate/up projections + SwiGLU */
+#define MOE_FFN_KERNEL_EXPERT_DOWN 3 /* routed expert down projection */
+#define MOE_FFN_KERNEL_COMBINE 4     /* shared-expert down + combine into y */
+
+typedef struct {
+    int32_t kernel; /* MOE_FFN_KERNEL_* */
+    void *start;    /* hipEvent_t recorded on `stream` right before that kernel's launch */
+    void *stop;     /* hipEvent_t recorded on `stream` right after it */
+} moe_ffn_trace;
+
+/* moe_ffn_forward_path that also records trace->start / trace->stop around
+ * one kernel of the call, for timing it with hipEventElapsedTime.  The events
+ * are caller-owned and created by the caller; trace may be NULL.  Measurement
+ * use only: the two event records are the only difference from
+ * moe_ffn_forward_path. */
+int moe_ffn_forward_traced(const moe_ffn_dims *dims, int64_t T, const uint16_t *x, const moe_ffn_router *router,
+                           const moe_ffn_experts *experts, const moe_ffn_shared *shared, uint16_t *y,
+                           int32_t *topk_idx, float *topk_weight, void *workspace, size_t workspace_bytes,
+                           void *stream, int path, const moe_ffn_trace *trace);
+
 /* Static string for a status code. */
 const char *moe_ffn_status_string(int status);
 

@@ -25,7 +25,9 @@ MOE_FFN_EHIP = -5
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 DECODE_MAX_T = 64
 
-EXPORTED = ("moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_path", "moe_ffn_status_string")
+EXPORTED = ("moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_path", "moe_ffn_forward_traced",
+            "moe_ffn_status_string")
+KERNEL_ROUTER, KERNEL_EXPERT_GU, KERNEL_EXPERT_DOWN, KERNEL_COMBINE = 1, 2, 3, 4
 
 
 class Dims(ctypes.Structure):
@@ -51,6 +53,10 @@ class Router(ctypes.Structure):
 class Shared(ctypes.Structure):
     _fields_ = [("gate_inp", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p),
                 ("down", ctypes.c_void_p)]
+
+
+class Trace(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("start", ctypes.c_void_p), ("stop", ctypes.c_void_p)]
 
 
 class MoeFfnError(RuntimeError):
@@ -79,6 +85,8 @@ def lib(path: str = LIB_PATH):
         L.moe_ffn_forward.restype = ctypes.c_int
         L.moe_ffn_forward_path.argtypes = fwd + [ctypes.c_int]
         L.moe_ffn_forward_path.restype = ctypes.c_int
+        L.moe_ffn_forward_traced.argtypes = fwd + [ctypes.c_int, ctypes.POINTER(Trace)]
+        L.moe_ffn_forward_traced.restype = ctypes.c_int
         L.moe_ffn_status_string.argtypes = [ctypes.c_int]
         L.moe_ffn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -158,6 +166,23 @@ def moe_ffn_forward_path(x, layer: DeviceLayer, y, workspace, topk_idx=None, top
     st = lib().moe_ffn_forward_path(ctypes.byref(dims), T, _ptr(x), ctypes.byref(r), ctypes.byref(ex),
                                     ctypes.byref(sh) if sh is not None else None, _ptr(y), _ptr(topk_idx),
                                     _ptr(topk_weight), _ptr(workspace), wsb, _stream_ptr(stream), path)
+    if check and st != MOE_FFN_OK:
+        raise MoeFfnError(st, moe_ffn_status_string(st))
+    return st
+
+
+def moe_ffn_forward_traced(x, layer: DeviceLayer, y, workspace, topk_idx=None, topk_weight=None, stream=None,
+                           path: int = PATH_AUTO, trace: Optional[Trace] = None, dims: Dims = DIMS,
+                           T: Optional[int] = None, check: bool = True) -> int:
+    """moe_ffn_forward_path plus an optional Trace (kernel id and two
+    hipEvent_t handles as integers) bracketing one kernel of the call."""
+    r, ex, sh = layer.structs()
+    T = x.shape[0] if T is None else T
+    wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    st = lib().moe_ffn_forward_traced(ctypes.byref(dims), T, _ptr(x), ctypes.byref(r), ctypes.byref(ex),
+                                      ctypes.byref(sh) if sh is not None else None, _ptr(y), _ptr(topk_idx),
+                                      _ptr(topk_weight), _ptr(workspace), wsb, _stream_ptr(stream), path,
+                                      ctypes.byref(trace) if trace is not None else None)
     if check and st != MOE_FFN_OK:
         raise MoeFfnError(st, moe_ffn_status_string(st))
     return st

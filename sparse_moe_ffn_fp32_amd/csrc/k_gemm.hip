@@ -25,6 +25,7 @@
 //          (fused chain (ii)).
 #include "moe_common.h"
 #include "moe_kernels.h"
+#include "../../include/moe_ffn.h"
 
 namespace moe {
 
@@ -261,7 +262,7 @@ hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s) 
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_gemms(const PrefillGemmParams& p, hipStream_t s) {
+hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hipStream_t s) {
     GemmArgs g = {};
     g.xh = p.xh; g.h = p.h; g.hs = p.hs;
     g.perm = p.perm; g.pos_of = p.pos_of; g.offs = p.offs; g.tiles = p.tiles; g.tile_count = p.tile_count;
@@ -273,7 +274,9 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, hipStream_t s) {
     g.q[0] = p.gate_q; g.sc[0] = p.gate_s; g.bi[0] = p.gate_b;
     g.q[1] = p.up_q; g.sc[1] = p.up_s; g.bi[1] = p.up_b;
     g.h_out = p.h;
+    tr.before(MOE_FFN_KERNEL_EXPERT_GU, s);
     hipLaunchKernelGGL((k_gemm<MODE_GU, GEMM_BM>), dim3(max_tiles, F / 64), dim3(256), 0, s, g);
+    tr.after(MOE_FFN_KERNEL_EXPERT_GU, s);
     // shared gate/up
     if (p.sh_gate) {
         g.sw[0] = p.sh_gate; g.sw[1] = p.sh_up; g.hs_out = p.hs;
@@ -282,8 +285,11 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, hipStream_t s) {
     // routed down
     g.q[0] = p.down_q; g.sc[0] = p.down_s; g.bi[0] = p.down_b;
     g.p_out = p.partial;
+    tr.before(MOE_FFN_KERNEL_EXPERT_DOWN, s);
     hipLaunchKernelGGL((k_gemm<MODE_DOWN, GEMM_BM>), dim3(max_tiles, D / 128), dim3(256), 0, s, g);
+    tr.after(MOE_FFN_KERNEL_EXPERT_DOWN, s);
     // combine
+    tr.before(MOE_FFN_KERNEL_COMBINE, s);
     if (p.sh_gate) {
         g.sw[0] = p.sh_down; g.p_in = p.partial; g.y = p.y;
         hipLaunchKernelGGL((k_gemm<MODE_SDOWN, GEMM_BM>), dim3(mt, D / 128), dim3(256), 0, s, g);
@@ -291,6 +297,7 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, hipStream_t s) {
         hipLaunchKernelGGL(k_combine_routed, dim3((p.T * D + 255) / 256), dim3(256), 0, s, p.partial, p.pos_of, p.y,
                            p.T);
     }
+    tr.after(MOE_FFN_KERNEL_COMBINE, s);
     return hipGetLastError();
 }
 

@@ -75,7 +75,7 @@ int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_f
 
 int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const moe_ffn_experts* ex,
                 const moe_ffn_shared* sh, uint16_t* y, int32_t* idx_user, float* w_user, char* ws,
-                hipStream_t s) {
+                const Tracer& tr, hipStream_t s) {
     const Layout L = layout(T);
     const int N = T * K;
     auto at = [&](size_t off) { return (void*)(ws + off); };
@@ -96,7 +96,9 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
     chk(launch_split_router(router->weight, wr3, s));
     chk(launch_prep_x(x, xh, T, s));
+    tr.before(MOE_FFN_KERNEL_ROUTER, s);
     chk(launch_router_logits(x, wr3, router->bias, logits, T, s));
+    tr.after(MOE_FFN_KERNEL_ROUTER, s);
     chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, T, s));
     chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(), s));
     PrefillGemmParams p{};
@@ -119,7 +121,7 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     p.partial = (float*)at(L.partial);
     p.y = y;
     p.T = T;
-    chk(launch_prefill_gemms(p, s));
+    chk(launch_prefill_gemms(p, tr, s));
     return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
 }
 
@@ -132,15 +134,29 @@ size_t moe_ffn_workspace_size(const moe_ffn_dims* dims, int64_t T) {
     return layout(T).total;
 }
 
+int moe_ffn_forward_traced(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
+                           const moe_ffn_experts* experts, const moe_ffn_shared* shared, uint16_t* y,
+                           int32_t* topk_idx, float* topk_weight, void* workspace, size_t workspace_bytes,
+                           void* stream, int path, const moe_ffn_trace* trace) {
+    int st = validate(dims, T, x, router, experts, shared, y, topk_idx, topk_weight, workspace, workspace_bytes,
+                      path);
+    if (st != MOE_FFN_OK || T == 0) return st;
+    Tracer tr;
+    if (trace) {
+        tr.kernel = trace->kernel;
+        tr.start = (hipEvent_t)trace->start;
+        tr.stop = (hipEvent_t)trace->stop;
+    }
+    return run_prefill((int)T, x, router, experts, shared, y, topk_idx, topk_weight, (char*)workspace, tr,
+                       (hipStream_t)stream);
+}
+
 int moe_ffn_forward_path(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
                          const moe_ffn_experts* experts, const moe_ffn_shared* shared, uint16_t* y,
                          int32_t* topk_idx, float* topk_weight, void* workspace, size_t workspace_bytes,
                          void* stream, int path) {
-    int st = validate(dims, T, x, router, experts, shared, y, topk_idx, topk_weight, workspace, workspace_bytes,
-                      path);
-    if (st != MOE_FFN_OK || T == 0) return st;
-    return run_prefill((int)T, x, router, experts, shared, y, topk_idx, topk_weight, (char*)workspace,
-                       (hipStream_t)stream);
+    return moe_ffn_forward_traced(dims, T, x, router, experts, shared, y, topk_idx, topk_weight, workspace,
+                                  workspace_bytes, stream, path, nullptr);
 }
 
 int moe_ffn_forward(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,

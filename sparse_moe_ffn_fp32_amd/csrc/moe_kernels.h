@@ -6,6 +6,18 @@
 
 namespace moe {
 
+// Optional pair of events around one kernel id (MOE_FFN_KERNEL_*).
+struct Tracer {
+    int kernel = 0;
+    hipEvent_t start = nullptr, stop = nullptr;
+    void before(int k, hipStream_t s) const {
+        if (k == kernel && start) (void)hipEventRecord(start, s);
+    }
+    void after(int k, hipStream_t s) const {
+        if (k == kernel && stop) (void)hipEventRecord(stop, s);
+    }
+};
+
 // ---- router (k_router.hip)
 hipError_t launch_split_router(const float* wr, uint16_t* wr3, hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr3, const float* bias, float* logits, int T,
@@ -40,6 +52,6 @@ struct PrefillGemmParams {
 };
 int gemm_bm();
 hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s);
-hipError_t launch_prefill_gemms(const PrefillGemmParams& p, hipStream_t s);
+hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hipStream_t s);
 
 }  // namespace moe
