@@ -83,6 +83,7 @@ def main():
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 decode, 2 prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every traced kernel (stderr)")
+    ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of a HIP graph")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -130,21 +131,17 @@ def main():
 
     dom_kernel = moe.KERNEL_EXPERT_GU
 
-    def run_steps(nsteps, kernel=None):
-        """nsteps steps; returns (wall seconds, per-launch ms of `kernel`)."""
-        ev = []
-        if kernel is not None:
-            ev = [(hip.event(), hip.event()) for _ in range(nsteps * nlayers)]
+    def run_steps_eager(nsteps, kernel=None):
+        """nsteps steps launched directly; returns (wall seconds, per-launch ms of `kernel`)."""
+        ev = [(hip.event(), hip.event()) for _ in range(nsteps * nlayers)] if kernel is not None else []
         if flush_buf is None:
             torch.cuda.synchronize()
             t = time.perf_counter()
             for s in range(nsteps):
                 for l in range(nlayers):
-                    tr = moe.Trace(kernel, *ev[s * nlayers + l]) if kernel is not None else None
-                    call(l, tr)
+                    call(l, moe.Trace(kernel, *ev[s * nlayers + l]) if kernel is not None else None)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t
-            step_ms = None
         else:
             # single layer: write 1 GiB between repetitions (outside the timed
             # call) so no weights stay in the caches; time each call with events
@@ -154,8 +151,7 @@ def main():
                 flush_buf.fill_(s & 0xFF)
                 torch.cuda.synchronize()
                 hip.record(se, stream)
-                tr = moe.Trace(kernel, *ev[s]) if kernel is not None else None
-                call(0, tr)
+                call(0, moe.Trace(kernel, *ev[s]) if kernel is not None else None)
                 hip.record(ee, stream)
                 step_ms.append(hip.elapsed_ms(se, ee))
             hip.destroy(se)
@@ -167,13 +163,60 @@ def main():
             hip.destroy(b)
         return wall, kms
 
+    def run_steps_graph(nsteps):
+        """Multi-layer steps: the nsteps steps are captured into one HIP graph
+        (launching 40 x several kernels per step from Python would otherwise
+        leave the GPU idle between kernels), replayed once in the timed region."""
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=cap):
+            for s in range(nsteps):
+                for l in range(nlayers):
+                    moe.moe_ffn_forward_path(xs[l], dev_layers[l], ys[l], wspace, idxs[l], ws_[l], stream=cap,
+                                             path=args.path)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t
+        del g
+        return wall
+
+    def kernel_times(nsteps, kernel):
+        """Per-launch ms of `kernel` over nsteps steps, from HIP events that the
+        library records around it on the call's stream.  A bounded device-side
+        sleep queued first keeps the GPU busy while Python enqueues the steps,
+        so the intervals hold GPU execution only (events recorded inside a
+        captured graph cannot be timed)."""
+        if flush_buf is not None:
+            return run_steps_eager(nsteps, kernel)[1]
+        ev = [(hip.event(), hip.event()) for _ in range(nsteps * nlayers)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.004 * nsteps))  # ~4 ms of GPU time per step at 2.4 GHz
+        for s in range(nsteps):
+            for l in range(nlayers):
+                call(l, moe.Trace(kernel, *ev[s * nlayers + l]))
+        torch.cuda.synchronize()
+        kms = [hip.elapsed_ms(a, b) for a, b in ev]
+        for a, b in ev:
+            hip.destroy(a)
+            hip.destroy(b)
+        return kms
+
+    def run_steps(nsteps):
+        if flush_buf is None and not args.eager:
+            return run_steps_graph(nsteps)
+        return run_steps_eager(nsteps)[0]
+
     log(f"warmup {args.warmup} steps")
-    run_steps(args.warmup)
+    run_steps(max(1, args.warmup))
     torch.cuda.synchronize()
     distinct = [np.unique(i.cpu().numpy()).size for i in idxs]
 
     log(f"timing {args.steps} steps")
-    wall, kms = run_steps(args.steps, dom_kernel)
+    wall = run_steps(args.steps)
+    kms = kernel_times(args.steps, dom_kernel)
     ms_per_step = 1000.0 * wall / args.steps
     tokens_per_step = T  # one step pushes T tokens through all `nlayers` layers
     value = tokens_per_step / (wall / args.steps)
@@ -203,7 +246,7 @@ def main():
     if args.breakdown:
         for kid, name in ((moe.KERNEL_ROUTER, "router"), (moe.KERNEL_EXPERT_GU, "expert_gu"),
                           (moe.KERNEL_EXPERT_DOWN, "expert_down"), (moe.KERNEL_COMBINE, "combine")):
-            _, km = run_steps(max(2, args.steps // 4), kid)
+            km = kernel_times(max(2, args.steps // 4), kid)
             log(f"  kernel {name}: {np.mean(km) * 1e3:.2f} us/launch")
 
     # ---------------------------------------------------------------- oracle

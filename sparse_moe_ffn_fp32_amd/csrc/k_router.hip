@@ -88,11 +88,6 @@ __global__ void __launch_bounds__(256) k_router_logits(const uint16_t* __restric
     }
 }
 
-// (value desc, index asc) ordering: does (va, ia) rank before (vb, ib)?
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
-}
-
 // One wave per token: top-8 of the 256 logits, renormalised softmax weights,
 // and sgate.  Lane l holds experts l, l+64, l+128, l+192.
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, const uint16_t* __restrict__ x,
@@ -104,32 +99,9 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
     float v[4];
 #pragma unroll
     for (int c = 0; c < 4; c++) v[c] = logits[(size_t)t * E + lane + 64 * c];
-    unsigned taken = 0;
     float sel_v[K];
     int sel_i[K];
-#pragma unroll
-    for (int r = 0; r < K; r++) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int c = 0; c < 4; c++)
-            if (!(taken & (1u << c)) && ranks_before(v[c], lane + 64 * c, bv, bi)) {
-                bv = v[c];
-                bi = lane + 64 * c;
-            }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            float ov = __shfl_xor(bv, off);
-            int oi = __shfl_xor(bi, off);
-            if (ranks_before(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        sel_v[r] = bv;
-        sel_i[r] = bi;
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    }
+    wave_top8(v, lane, sel_v, sel_i);
     // norm_topk_prob: the full-softmax normaliser cancels, so the weights are
     // the softmax over the eight selected logits.
     float p[K], s = 0.0f;

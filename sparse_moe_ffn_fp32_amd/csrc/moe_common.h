@@ -77,4 +77,70 @@ __device__ __forceinline__ u32x4 q4_word_to_f16x8(uint32_t w, f16x2 s2, f16x2 b2
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// (value desc, index asc): does (va, ia) rank before (vb, ib)?
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+    return (va > vb) | ((va == vb) & (ia < ib));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_argmax_step(float& v, int& i) {
+    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+    const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xf, 0xf, false);
+    const bool take = ranks_before(ov, oi, v, i);
+    v = take ? ov : v;
+    i = take ? oi : i;
+}
+
+// Top-8 of 256 scores held by one wave (lane l holds experts l, l+64,
+// l+128, l+192 in v[0..3]), ordered by (score desc, index asc).  Each round
+// is an arg-max: DPP exchanges inside 16-lane rows (xor 1, xor 2, half-row
+// mirror, row mirror), then the four row winners are read as scalars.  The
+// results are wave-uniform.
+__device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v, int* sel_i) {
+    float a[4];
+    int ai[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        a[c] = v[c];
+        ai[c] = lane + 64 * c;
+    }
+    // sort the lane's four candidates (compare-exchange network)
+    const int net[5][2] = {{0, 1}, {2, 3}, {0, 2}, {1, 3}, {1, 2}};
+#pragma unroll
+    for (int s = 0; s < 5; s++) {
+        const int p = net[s][0], q = net[s][1];
+        const bool sw = ranks_before(a[q], ai[q], a[p], ai[p]);
+        const float tv = a[p];
+        const int ti = ai[p];
+        a[p] = sw ? a[q] : a[p];
+        ai[p] = sw ? ai[q] : ai[p];
+        a[q] = sw ? tv : a[q];
+        ai[q] = sw ? ti : ai[q];
+    }
+    int head = 0;
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        float cv = head == 0 ? a[0] : head == 1 ? a[1] : head == 2 ? a[2] : head == 3 ? a[3] : -INFINITY;
+        int ci = head == 0 ? ai[0] : head == 1 ? ai[1] : head == 2 ? ai[2] : head == 3 ? ai[3] : 0x7fffffff;
+        dpp_argmax_step<0xB1>(cv, ci);   // quad_perm [1,0,3,2]
+        dpp_argmax_step<0x4E>(cv, ci);   // quad_perm [2,3,0,1]
+        dpp_argmax_step<0x141>(cv, ci);  // row_half_mirror
+        dpp_argmax_step<0x140>(cv, ci);  // row_mirror
+        float bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cv), 15));
+        int bi = __builtin_amdgcn_readlane(ci, 15);
+#pragma unroll
+        for (int row = 1; row < 4; row++) {
+            const float rv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cv), 16 * row + 15));
+            const int ri = __builtin_amdgcn_readlane(ci, 16 * row + 15);
+            if (ranks_before(rv, ri, bv, bi)) {
+                bv = rv;
+                bi = ri;
+            }
+        }
+        sel_v[r] = bv;
+        sel_i[r] = bi;
+        head += (bi & 63) == lane;
+    }
+}
+
 }  // namespace moe

@@ -21,7 +21,7 @@ Layout layout(int64_t T) {
     const int nblk = sort_blocks((int)N);
     const size_t max_tiles = (N + gemm_bm() - 1) / gemm_bm() + E;
     Layout L{};
-    size_t o = 0;
+    size_t o = WS_COUNTER_BYTES;
     L.wr3 = o;        o += up((size_t)3 * E * D * 2);
     L.logits = o;     o += up((size_t)T * E * 4);
     L.idx = o;        o += up(N * 4);
@@ -39,6 +39,16 @@ Layout layout(int64_t T) {
     L.partial = o;    o += up(N * D * 4);
     L.total = o;
     return L;
+}
+
+// Both paths' regions, so any path can run in a workspace sized for T.
+size_t workspace_bytes(int64_t T) {
+    size_t b = layout(T).total;
+    if (T <= MOE_FFN_DECODE_MAX_T) {
+        const size_t d = decode_workspace_bytes((int)T, nullptr);
+        if (d > b) b = d;
+    }
+    return b;
 }
 
 bool dims_ok(const moe_ffn_dims* d) {
@@ -68,8 +78,8 @@ int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_f
                          sh ? sh->gate_inp : nullptr, ws};
     for (const void* p : opt)
         if (p && !al16(p)) return MOE_FFN_EALIGN;
-    if (path == MOE_FFN_PATH_DECODE) return MOE_FFN_EUNSUPPORTED;
-    if (!ws || ws_bytes < layout(T).total) return MOE_FFN_EWORKSPACE;
+    if (path == MOE_FFN_PATH_DECODE && T > MOE_FFN_DECODE_MAX_T) return MOE_FFN_EUNSUPPORTED;
+    if (!ws || ws_bytes < workspace_bytes(T)) return MOE_FFN_EWORKSPACE;
     return MOE_FFN_OK;
 }
 
@@ -127,11 +137,27 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
 
 }  // namespace
 
+namespace moe {
+__global__ void k_zero_counters(int32_t* p) { p[threadIdx.x] = 0; }
+
+hipError_t launch_workspace_init(void* ws, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(WS_COUNTER_BYTES / 4), 0, s, (int32_t*)ws);
+    return hipGetLastError();
+}
+}  // namespace moe
+
 extern "C" {
+
+int moe_ffn_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) return MOE_FFN_EINVAL;
+    if (((uintptr_t)workspace & 15u) != 0) return MOE_FFN_EALIGN;
+    if (workspace_bytes < WS_COUNTER_BYTES) return MOE_FFN_EWORKSPACE;
+    return launch_workspace_init(workspace, (hipStream_t)stream) == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
+}
 
 size_t moe_ffn_workspace_size(const moe_ffn_dims* dims, int64_t T) {
     if (!dims || !dims_ok(dims) || T <= 0 || T > MOE_FFN_MAX_T) return 0;
-    return layout(T).total;
+    return workspace_bytes(T);
 }
 
 int moe_ffn_forward_traced(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
@@ -147,8 +173,26 @@ int moe_ffn_forward_traced(const moe_ffn_dims* dims, int64_t T, const uint16_t* 
         tr.start = (hipEvent_t)trace->start;
         tr.stop = (hipEvent_t)trace->stop;
     }
-    return run_prefill((int)T, x, router, experts, shared, y, topk_idx, topk_weight, (char*)workspace, tr,
-                       (hipStream_t)stream);
+    const bool decode = path == MOE_FFN_PATH_DECODE || (path == MOE_FFN_PATH_AUTO && T <= MOE_FFN_DECODE_MAX_T);
+    if (!decode)
+        return run_prefill((int)T, x, router, experts, shared, y, topk_idx, topk_weight, (char*)workspace, tr,
+                           (hipStream_t)stream);
+    DecodeParams p{};
+    p.x = x;
+    p.T = (int)T;
+    p.router_w = router->weight;
+    p.router_b = router->bias;
+    p.sh_gate_inp = shared ? shared->gate_inp : nullptr;
+    p.sh_gate = shared ? shared->gate : nullptr;
+    p.sh_up = shared ? shared->up : nullptr;
+    p.sh_down = shared ? shared->down : nullptr;
+    p.gate_q = experts->gate.qweight; p.gate_s = experts->gate.scales; p.gate_b = experts->gate.biases;
+    p.up_q = experts->up.qweight;     p.up_s = experts->up.scales;     p.up_b = experts->up.biases;
+    p.down_q = experts->down.qweight; p.down_s = experts->down.scales; p.down_b = experts->down.biases;
+    p.idx = topk_idx;
+    p.w = topk_weight;
+    p.y = y;
+    return launch_decode(p, (char*)workspace, tr, (hipStream_t)stream) == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
 }
 
 int moe_ffn_forward_path(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,

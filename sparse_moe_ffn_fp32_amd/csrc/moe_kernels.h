@@ -54,4 +54,29 @@ int gemm_bm();
 hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s);
 hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hipStream_t s);
 
+// ---- workspace head: arrival counters, zero before the first call and
+// returned to zero by every call
+constexpr size_t WS_COUNTER_BYTES = 1024;
+constexpr size_t WS_ARRIVE_A = 0;    // int32 [1]
+constexpr size_t WS_ARRIVE_D = 256;  // int32 [D/16]
+hipError_t launch_workspace_init(void* ws, hipStream_t s);
+
+// ---- decode path (k_decode.hip), T <= 64
+struct DecodeLayout {
+    size_t logits, xp, hs, ys, h, part, idx, w, sgate, nuniq, uexp, ucnt, uoff, pairs, total;
+};
+struct DecodeParams {
+    const uint16_t* x;
+    int T;
+    const float *router_w, *router_b;
+    const uint16_t *sh_gate_inp, *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
+    const uint32_t *gate_q, *up_q, *down_q;
+    const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
+    int32_t* idx;  // user outputs or nullptr
+    float* w;
+    uint16_t* y;
+};
+size_t decode_workspace_bytes(int T, DecodeLayout* L);
+hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipStream_t s);
+
 }  // namespace moe

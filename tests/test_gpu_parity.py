@@ -37,7 +37,7 @@ def layer0():
     return workloads.layer_for(0)
 
 
-PATHS = {"auto": 0, "prefill": 2}
+PATHS = {"auto": 0, "decode": 1, "prefill": 2}
 
 
 def test_config0_T4(gpu, layer0):
@@ -47,9 +47,11 @@ def test_config0_T4(gpu, layer0):
     _say(routing_check(layer0, x, idx, w), output_check(layer0, x, y))
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 5, 17, 63, 64, 65, 100, 257])
-@pytest.mark.parametrize("path", ["auto", "prefill"])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 17, 33, 63, 64, 65, 100, 257])
+@pytest.mark.parametrize("path", ["auto", "decode", "prefill"])
 def test_ragged_T(gpu, layer0, T, path):
+    if path == "decode" and T > 64:
+        pytest.skip("the decode path takes T <= 64")
     x, _, _ = workloads.enforce_margin(layer0, T, 100 + T)
     _say(f"ragged T={T} path={path}")
     y, idx, w = gpu.run(layer0, x, path=PATHS[path])
@@ -111,10 +113,11 @@ def test_zero_input_gives_zero(gpu, layer0):
     assert np.all(idx == np.arange(8)[None, :]) and np.all(w == np.float32(0.125))
 
 
-def test_deterministic_and_no_unwritten_reads(gpu, layer0):
+@pytest.mark.parametrize("T", [37, 300])
+def test_deterministic_and_no_unwritten_reads(gpu, layer0, T):
     """Run-to-run bitwise identical, also with the workspace filled with 0xFF
     (NaN in every float slot) beforehand: nothing reads unwritten scratch."""
-    x, _, _ = workloads.enforce_margin(layer0, 300, 5)
+    x, _, _ = workloads.enforce_margin(layer0, T, 5)
     a = gpu.run(layer0, x)
     b = gpu.run(layer0, x, poison=True)
     for u, v in zip(a, b):
@@ -122,24 +125,26 @@ def test_deterministic_and_no_unwritten_reads(gpu, layer0):
     assert not np.isnan(bf16_to_f64(b[0])).any()
 
 
-def test_token_permutation_invariance(gpu, layer0):
+@pytest.mark.parametrize("T", [50, 300])
+def test_token_permutation_invariance(gpu, layer0, T):
     """Permuting tokens permutes the outputs bit for bit."""
-    x, _, _ = workloads.enforce_margin(layer0, 300, 6)
-    perm = np.random.default_rng(0).permutation(300)
+    x, _, _ = workloads.enforce_margin(layer0, T, 6)
+    perm = np.random.default_rng(0).permutation(T)
     a = gpu.run(layer0, x)
     b = gpu.run(layer0, x[perm])
     for u, v in zip(a, b):
         assert np.array_equal(u[perm], v)
 
 
-def test_down_scale_halving(gpu):
+@pytest.mark.parametrize("T", [20, 70])
+def test_down_scale_halving(gpu, T):
     """Halving every down scale and bias halves y exactly (no shared
     expert; all values stay normal)."""
     layer = workloads.layer_for(8, shared=False)
     half = copy.deepcopy(layer)
     for arr in (half.down.scales, half.down.biases):
         arr[:] = synth.f32_to_bf16(synth.bf16_to_f32(arr) * np.float32(0.5))
-    x, _, _ = workloads.enforce_margin(layer, 70, 8)
+    x, _, _ = workloads.enforce_margin(layer, T, 8)
     ya = gpu.run(layer, x)[0]
     yb = gpu.run(half, x)[0]
     assert np.array_equal(bf16_to_f64(yb), 0.5 * bf16_to_f64(ya))
@@ -155,3 +160,41 @@ def test_gate_up_swap_is_detected(gpu, layer0):
     ref = oracle.get().forward(layer0, x)["y"]
     rel = np.linalg.norm(bf16_to_f64(y) - ref, axis=1) / np.linalg.norm(ref, axis=1)
     assert rel.min() > 0.2
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_decode_and_prefill_paths_agree(gpu, layer0, T):
+    """Both paths compute the same function: identical routing where the
+    order is unique, weights within 1e-5, outputs within the parity bar of
+    each other."""
+    x, _, _ = workloads.enforce_margin(layer0, T, 200 + T)
+    yd, idd, wd = gpu.run(layer0, x, path=PATHS["decode"])
+    yp, ip, wp = gpu.run(layer0, x, path=PATHS["prefill"])
+    assert np.array_equal(np.sort(idd, axis=1), np.sort(ip, axis=1))
+    assert np.abs(wd[idd == ip] - wp[idd == ip]).max() <= 1e-5
+    a, b = bf16_to_f64(yd), bf16_to_f64(yp)
+    rel = np.linalg.norm(a - b, axis=1) / np.linalg.norm(b, axis=1)
+    assert rel.max() <= 3e-3
+
+
+def test_workspace_reuse_across_calls(gpu, layer0):
+    """One workspace serves a sequence of calls of both paths and several T;
+    every result equals the result with a fresh workspace (the counters in
+    the workspace head come back to zero after each call)."""
+    import sparse_moe_ffn_fp32_amd as moe
+    torch = gpu.torch
+    dl = gpu.device_layer(layer0)
+    ws = moe.alloc_workspace(300)
+    for T in (37, 1, 300, 64, 2, 37):
+        x, _, _ = workloads.enforce_margin(layer0, T, 300 + T)
+        ref = gpu.run(layer0, x)
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        y = torch.empty_like(xd)
+        idx = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
+        moe.moe_ffn_forward(xd, dl, y, ws, idx, w)
+        torch.cuda.synchronize()
+        got = (y.cpu().numpy().view(np.uint16), idx.cpu().numpy(), w.cpu().numpy())
+        for u, v in zip(got, ref):
+            assert np.array_equal(u, v), f"T={T}"
+    assert int(ws[:1024].count_nonzero()) == 0
