@@ -65,9 +65,12 @@ class Hip:
         return e.value
 
     def elapsed_ms(self, a, b):
-        assert self.L.hipEventSynchronize(b) == 0
+        """Elapsed ms between two events, NaN if they were never recorded."""
+        if self.L.hipEventSynchronize(b) != 0:
+            return float("nan")
         ms = ctypes.c_float()
-        assert self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        if self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            return float("nan")
         return ms.value
 
     def destroy(self, e):
@@ -222,7 +225,7 @@ def main():
     value = tokens_per_step / (wall / args.steps)
 
     # dominant kernel: algorithmic bytes / flops per launch
-    kernel_ms = float(np.mean(kms))
+    kernel_ms = float(np.nanmean(kms))
     if T <= 64:
         gu_bytes = [d * GU_BYTES + T * 2048 * 2 + T * 8 * 512 * 4 for d in distinct]
         per_launch = float(np.mean(gu_bytes))
@@ -246,8 +249,11 @@ def main():
     if args.breakdown:
         for kid, name in ((moe.KERNEL_ROUTER, "router"), (moe.KERNEL_EXPERT_GU, "expert_gu"),
                           (moe.KERNEL_EXPERT_DOWN, "expert_down"), (moe.KERNEL_COMBINE, "combine")):
-            km = kernel_times(max(2, args.steps // 4), kid)
-            log(f"  kernel {name}: {np.mean(km) * 1e3:.2f} us/launch")
+            km = np.array(kernel_times(max(2, args.steps // 4), kid))
+            if np.isfinite(km).any():
+                log(f"  kernel {name}: {np.nanmean(km) * 1e3:.2f} us/launch")
+            else:
+                log(f"  kernel {name}: not launched on this path")
 
     # ---------------------------------------------------------------- oracle
     cpu = None

@@ -103,18 +103,9 @@ typedef struct {
 } moe_ffn_shared;
 
 /* Bytes of device workspace a call with T tokens needs (0 for T == 0; 0 for
- * invalid dims or T).  Its first 1024 bytes hold arrival counters that must
- * be zero when a call starts: zero them once with moe_ffn_workspace_init (or
- * allocate the workspace zero-filled).  Every call that completes returns
- * them to zero, so a workspace needs initialising only after allocation or
- * after a failed call.  Nothing else in it carries state between calls. */
+ * invalid dims or T).  The workspace needs no initialisation and carries no
+ * state from one call to the next. */
 size_t moe_ffn_workspace_size(const moe_ffn_dims *dims, int64_t T);
-
-/* Zero the counter head of a workspace on `stream` (a kernel launch, no
- * memset, so it may be captured in a graph).  Returns MOE_FFN_EINVAL for a
- * NULL workspace, MOE_FFN_EALIGN if it is not 16-byte aligned,
- * MOE_FFN_EWORKSPACE if workspace_bytes < 1024. */
-int moe_ffn_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /* y[T, d_model] bf16 = the FFN above applied to x[T, d_model] bf16.
  *

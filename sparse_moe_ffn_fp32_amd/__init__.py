@@ -25,8 +25,8 @@ MOE_FFN_EHIP = -5
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 DECODE_MAX_T = 64
 
-EXPORTED = ("moe_ffn_workspace_size", "moe_ffn_workspace_init", "moe_ffn_forward", "moe_ffn_forward_path",
-            "moe_ffn_forward_traced", "moe_ffn_status_string")
+EXPORTED = ("moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_path", "moe_ffn_forward_traced",
+            "moe_ffn_status_string")
 KERNEL_ROUTER, KERNEL_EXPERT_GU, KERNEL_EXPERT_DOWN, KERNEL_COMBINE = 1, 2, 3, 4
 
 
@@ -87,8 +87,6 @@ def lib(path: str = LIB_PATH):
         L.moe_ffn_forward_path.restype = ctypes.c_int
         L.moe_ffn_forward_traced.argtypes = fwd + [ctypes.c_int, ctypes.POINTER(Trace)]
         L.moe_ffn_forward_traced.restype = ctypes.c_int
-        L.moe_ffn_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
-        L.moe_ffn_workspace_init.restype = ctypes.c_int
         L.moe_ffn_status_string.argtypes = [ctypes.c_int]
         L.moe_ffn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -195,18 +193,8 @@ def moe_ffn_forward(x, layer: DeviceLayer, y, workspace, topk_idx=None, topk_wei
     return moe_ffn_forward_path(x, layer, y, workspace, topk_idx, topk_weight, stream, PATH_AUTO, **kw)
 
 
-def moe_ffn_workspace_init(workspace, stream=None, check: bool = True) -> int:
-    """Zero the counter head of a workspace tensor (needed once after
-    allocation unless it was allocated zero-filled)."""
-    st = lib().moe_ffn_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
-                                      _stream_ptr(stream))
-    if check and st != MOE_FFN_OK:
-        raise MoeFfnError(st, moe_ffn_status_string(st))
-    return st
-
-
 def alloc_workspace(T: int, device="cuda"):
-    """A zero-filled workspace for calls with up to T tokens."""
+    """A workspace for calls with up to T tokens (uninitialised memory)."""
     import torch
     n = moe_ffn_workspace_size(T)
-    return torch.zeros(max(n, 1024), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

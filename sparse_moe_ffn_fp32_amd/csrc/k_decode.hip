@@ -15,27 +15,33 @@
 // operand.  "Rows on N": the 16 weight rows are the MFMA's N columns, so each
 // lane holds one weight row and needs one scale and one bias per group.
 //
-// Every wave issues all of its global loads up front, in the order it
-// consumes them, from addresses that are always valid (token slots past the
-// end reuse slot 0's row and their results are dropped), so the loads overlap
-// one another instead of waiting one by one.
+// Every wave issues its global loads up front, in the order it consumes
+// them, from addresses that are always valid (token slots past the end reuse
+// slot 0's row and their results are dropped), so the loads overlap one
+// another instead of waiting one by one.
+//
+// No block waits on another block inside a kernel: on gfx950 a device-scope
+// release/acquire writes back and invalidates a whole XCD's L2 and costs as
+// much as a kernel boundary, so the only global synchronisation is the
+// stream order between launches.
 //
 // Launches (all on the caller's stream):
-//   A  router logits (fp32 weights split exactly into three bf16 terms) and
-//      the shared expert's gate/up + SwiGLU, K split over the 16 waves of a
-//      block and reduced in LDS in fixed order; x in the K order of the codes.
-//      The last router block to finish does the routing: softmax/top-8/
-//      renormalise per token, sgate, and the distinct experts with their
-//      (token, rank) pairs.
-//   C  routed gate/up + SwiGLU per (distinct expert, 32 features), K split in
-//      four; and the shared expert's down projection.
-//   D  routed down projection per (16 output rows, 8 distinct experts); the
-//      last block to finish a row tile does the combine
-//      y = sum_{r=0..7} w_r * down_r + sgate * shexp  in fixed order with one
-//      bf16 rounding (no float atomics).
-// The arrival counters live in the zero-initialised head of the workspace;
-// each is returned to zero by the block that sees the last arrival, so every
-// call leaves them ready for the next.
+//   A      router logits (fp32 weights split exactly into three bf16 terms)
+//          and the shared expert's gate/up + SwiGLU, K split over the 16
+//          waves of a block and reduced in LDS in fixed order; x copied into
+//          the K order of the codes.
+//   route  (T > 4 only) one block: softmax/top-8/renormalise per token,
+//          sgate, the distinct experts with their (token, rank) pairs.
+//   C      routed gate/up + SwiGLU, 32 features x one expert per block with K
+//          split in four; for T <= 4 a block serves one (token, rank) pair
+//          and every wave derives the pair's expert from the token's logits
+//          (top-8 by DPP arg-max) instead of waiting for a routing launch.
+//          Extra blocks: the shared expert's down projection.
+//   D      routed down projection of 16 output rows per block; for T <= 4
+//          over every (token, rank) pair and then the combine
+//          y = sum_{r=0..7} w_r * down_r + sgate * shexp  in fixed order with
+//          one bf16 rounding (no float atomics); for T > 4 over 8 distinct
+//          experts per block, fp32 partials per pair, and a combine launch.
 //
 // Indices read back from the workspace are clamped to their ranges before
 // they address memory.
@@ -123,9 +129,7 @@ struct DecodeArgs {
     float* hs;       // [T, FS] shared SwiGLU output
     float* ys;       // [T, D] shared down output
     uint16_t* h;     // fp16 [8T, F] (pair-major), perm8
-    float* part;     // [8T, D] routed down outputs (when a row tile spans blocks)
-    int32_t* arrive_a; // [1] arrival counter of the router blocks of stage A
-    int32_t* arrive; // [N_ROW_TILES] arrival counters of stage D
+    float* part;     // [8T, D] routed down outputs per pair (T > 4)
     int32_t* idx;
     float* w;
     float* sgate;
@@ -137,95 +141,8 @@ struct DecodeArgs {
     uint16_t* y;
 };
 
-// ------------------------------------------------------------------ routing
-// Run by the last router block of stage A (1024 threads) once every logit is
-// in memory: softmax/top-8/renormalise and sgate per token (one wave per
-// token), then the distinct experts in increasing id order, each with its
-// (token, rank) pairs in token order.
-__device__ void route_block(const DecodeArgs& a, int* sidx, int* scan_a, int* scan_b) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int T = a.T;
-    for (int t = wave; t < T; t += 16) {
-        float v[4];
-#pragma unroll
-        for (int c = 0; c < 4; c++) v[c] = a.logits[(size_t)t * E + lane + 64 * c];
-        float sel_v[K];
-        int sel_i[K];
-        wave_top8(v, lane, sel_v, sel_i);
-        // norm_topk_prob: the softmax normaliser cancels, so the weights are
-        // the softmax of the eight selected logits
-        float p[K], s = 0.0f;
-#pragma unroll
-        for (int r = 0; r < K; r++) {
-            p[r] = __expf(sel_v[r] - sel_v[0]);
-            s += p[r];
-        }
-        const float inv = 1.0f / s;
-        if (lane < K) {
-            float wv = 0.f;
-            int iv = 0;
-#pragma unroll
-            for (int r = 0; r < K; r++)
-                if (r == lane) {
-                    wv = p[r] * inv;
-                    iv = sel_i[r];
-                }
-            a.idx[t * K + lane] = iv;
-            a.w[t * K + lane] = wv;
-            sidx[t * K + lane] = iv;
-        }
-        float z = 0.0f;
-        if (a.sgi) {
-            const u32x4* xp = (const u32x4*)(a.x + (size_t)t * D + 32 * lane);
-            const u32x4* gp = (const u32x4*)(a.sgi + 32 * lane);
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const u32x4 xv = xp[q], gv = gp[q];
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    z += __uint_as_float(xv[j] << 16) * __uint_as_float(gv[j] << 16);
-                    z += __uint_as_float(xv[j] & 0xffff0000u) * __uint_as_float(gv[j] & 0xffff0000u);
-                }
-            }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-        }
-        if (lane == 0) a.sgate[t] = a.sgi ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
-    }
-    __syncthreads();
-    int cnt = 0;
-    const int e = tid;
-    if (e < E)
-        for (int i = 0; i < T * K; i++) cnt += sidx[i] == e;
-    if (e < E) {
-        scan_a[e] = cnt > 0;
-        scan_b[e] = cnt;
-    }
-    __syncthreads();
-    for (int off = 1; off < E; off <<= 1) {  // inclusive scans
-        int va = 0, vb = 0;
-        if (e < E && e >= off) {
-            va = scan_a[e - off];
-            vb = scan_b[e - off];
-        }
-        __syncthreads();
-        if (e < E) {
-            scan_a[e] += va;
-            scan_b[e] += vb;
-        }
-        __syncthreads();
-    }
-    if (e < E && cnt > 0) {
-        const int u = scan_a[e] - 1;
-        int j = scan_b[e] - cnt;
-        a.uexp[u] = e;
-        a.ucnt[u] = cnt;
-        a.uoff[u] = j;
-        for (int i = 0; i < T * K; i++)
-            if (sidx[i] == e) a.pairs[j++] = i;
-    }
-    if (tid == 0) a.nuniq[0] = scan_a[E - 1];
-}
+
+constexpr int TINY_T = 4;  // up to this many tokens: no distinct-expert lists
 
 // ------------------------------------------------------------------ stage A
 // Router blocks: 16 experts; shared blocks: 16 gate + 16 up rows.  Wave w
@@ -233,8 +150,6 @@ __device__ void route_block(const DecodeArgs& a, int* sidx, int* scan_a, int* sc
 template <int NMT>
 __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a) {
     __shared__ float red[16][NMT * 16][17];
-    __shared__ int sidx[64 * K], scan_a[E], scan_b[E];
-    __shared__ int last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
@@ -337,26 +252,139 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a) {
         if (router) a.logits[(size_t)t * E + row0 + c] = s0[0] + (a.rbias ? a.rbias[row0 + c] : 0.0f);
         else a.hs[(size_t)t * FS + row0 + c] = silu_f32(s0[0]) * s0[1];
     }
-    if (!router) return;
-    // the last router block to finish routes every token
-    __threadfence();
+}
+
+// ------------------------------------------------------------------ routing
+// Top-8 of token t's logits (one wave, result wave-uniform).
+__device__ __forceinline__ void token_top8(const DecodeArgs& a, int t, int lane, float* sel_v, int* sel_i) {
+    float v[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) v[c] = a.logits[(size_t)t * E + lane + 64 * c];
+    wave_top8(v, lane, sel_v, sel_i);
+}
+
+// One wave: write token t's routing (expert ids, renormalised weights; the
+// softmax normaliser cancels under norm_topk_prob, so the weights are the
+// softmax of the eight selected logits) and sgate = sigmoid(gate_inp . x).
+__device__ void write_token_route(const DecodeArgs& a, int t, int lane, const float* sel_v, const int* sel_i,
+                                  int* sidx) {
+    float p[K], s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < K; r++) {
+        p[r] = __expf(sel_v[r] - sel_v[0]);
+        s += p[r];
+    }
+    const float inv = 1.0f / s;
+    if (lane < K) {
+        float wv = 0.f;
+        int iv = 0;
+#pragma unroll
+        for (int r = 0; r < K; r++)
+            if (r == lane) {
+                wv = p[r] * inv;
+                iv = sel_i[r];
+            }
+        a.idx[t * K + lane] = iv;
+        a.w[t * K + lane] = wv;
+        if (sidx) sidx[t * K + lane] = iv;
+    }
+    float z = 0.0f;
+    if (a.sgi) {
+        const u32x4* xq = (const u32x4*)(a.x + (size_t)t * D + 32 * lane);
+        const u32x4* gp = (const u32x4*)(a.sgi + 32 * lane);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const u32x4 xv = xq[q], gv = gp[q];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                z += __uint_as_float(xv[j] << 16) * __uint_as_float(gv[j] << 16);
+                z += __uint_as_float(xv[j] & 0xffff0000u) * __uint_as_float(gv[j] & 0xffff0000u);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    }
+    if (lane == 0) a.sgate[t] = a.sgi ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
+}
+
+// T > TINY_T: one block routes every token and lists the distinct experts in
+// increasing id order, each with its (token, rank) pairs in token order.  An
+// assignment's place among equal experts comes from ballots over the 8 bits
+// of the expert id (within a wave) plus per-wave counts (across waves).
+__global__ void __launch_bounds__(1024) k_dec_route(DecodeArgs a) {
+    __shared__ int sidx[64 * K];
+    __shared__ int wcnt[8][E];
+    __shared__ int scan_a[E], scan_b[E];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = a.T, N = T * K;
+    for (int t = wave; t < T; t += 16) {
+        float sel_v[K];
+        int sel_i[K];
+        token_top8(a, t, lane, sel_v, sel_i);
+        write_token_route(a, t, lane, sel_v, sel_i, sidx);
+    }
+    for (int i = tid; i < 8 * E; i += 1024) (&wcnt[0][0])[i] = 0;
     __syncthreads();
-    if (tid == 0) {
-        const int prev = __hip_atomic_fetch_add(a.arrive_a, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        last = prev == N_ROUTER_BLK - 1;
+    int e = 0, rank = 0;
+    const bool valid = tid < N;
+    if (tid < 64 * K) {  // waves 0..7 hold assignments 0..511
+        e = valid ? sidx[tid] & (E - 1) : 0;
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; bit++) {
+            const uint64_t bb = __ballot((e >> bit) & 1);
+            peers &= ((e >> bit) & 1) ? bb : ~bb;
+        }
+        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        rank = __popcll(peers & lt);
+        if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);
     }
     __syncthreads();
-    if (!last) return;
-    __threadfence();
-    if (tid == 0) *a.arrive_a = 0;  // every router block has arrived: ready for the next call
-    route_block(a, sidx, scan_a, scan_b);
+    int cnt = 0;
+    if (tid < E) {  // per-wave counts -> per-wave prefixes, total per expert
+#pragma unroll
+        for (int w = 0; w < 8; w++) {
+            const int v = wcnt[w][tid];
+            wcnt[w][tid] = cnt;
+            cnt += v;
+        }
+        scan_a[tid] = cnt > 0;
+        scan_b[tid] = cnt;
+    }
+    __syncthreads();
+    for (int off = 1; off < E; off <<= 1) {  // inclusive scans over experts
+        int va = 0, vb = 0;
+        if (tid < E && tid >= off) {
+            va = scan_a[tid - off];
+            vb = scan_b[tid - off];
+        }
+        __syncthreads();
+        if (tid < E) {
+            scan_a[tid] += va;
+            scan_b[tid] += vb;
+        }
+        __syncthreads();
+    }
+    if (tid < E && cnt > 0) {
+        const int u = scan_a[tid] - 1;
+        a.uexp[u] = tid;
+        a.ucnt[u] = cnt;
+        a.uoff[u] = scan_b[tid] - cnt;
+    }
+    if (valid) {
+        const int start = e > 0 ? scan_b[e - 1] : 0;
+        a.pairs[start + wcnt[wave][e] + rank] = tid;
+    }
+    if (tid == 0) a.nuniq[0] = scan_a[E - 1];
 }
 
 // ------------------------------------------------------------------ stage C
-// One wave: 16 features of one distinct expert, gate and up, 8 quantisation
-// groups (512 inputs), for the token tiles of the expert one at a time.  The
-// partial sums of token slot 16m + 4kq + v and feature n go to red_g/red_u.
-__device__ __forceinline__ void gu_wave(const DecodeArgs& a, size_t row, int gq8, int cnt, int off, int lane,
+// One wave, one token tile: 16 features (rows `row`) of gate and up over 8
+// quantisation groups starting at gq8, for the token slots whose pair ids are
+// pair_of(slot) (slot < cnt <= 16).  Partial sums of token slot 4kq + v and
+// feature n go to red_g / red_u.
+template <class PairOf>
+__device__ __forceinline__ void gu_tile(const DecodeArgs& a, size_t row, int gq8, int cnt, PairOf pair_of, int lane,
                                         float (*red_g)[16], float (*red_u)[16]) {
     const int n = lane & 15, kq = lane >> 4;
     const size_t sbase = row * (D / G) + gq8;
@@ -364,10 +392,10 @@ __device__ __forceinline__ void gu_wave(const DecodeArgs& a, size_t row, int gq8
     const u32x4 usv = *(const u32x4*)(a.us + sbase), ubv = *(const u32x4*)(a.ub + sbase);
     const uint32_t* gw_p = a.gq + row * (D / 8) + 8 * gq8 + 2 * kq;
     const uint32_t* uw_p = a.uq + row * (D / 8) + 8 * gq8 + 2 * kq;
+    const int tk = a.T * K - 1;
+    const uint16_t* xrow = a.xp + (size_t)(min(max(pair_of(n < cnt ? n : 0), 0), tk) >> 3) * D;
     u32x2 gw[8], uw[8];
     u32x4 xa[8][2];
-    const int tk = a.T * K - 1;
-    const uint16_t* xrow = a.xp + (size_t)(min(max(a.pairs[off + (n < cnt ? n : 0)], 0), tk) >> 3) * D;
 #pragma unroll
     for (int g = 0; g < 8; g++) {  // loads in the order they are consumed
         gw[g] = *(const u32x2*)(gw_p + 8 * g);
@@ -377,63 +405,71 @@ __device__ __forceinline__ void gu_wave(const DecodeArgs& a, size_t row, int gq8
         xa[g][1] = *(const u32x4*)(xrow + 8 * wd + 8);
     }
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
-    const int nm = (cnt + 15) >> 4;
-#pragma unroll 1
-    for (int m = 0; m < nm; m++) {
-        if (m > 0) {  // later token tiles (more than 16 tokens on this expert)
-            const int slot = 16 * m + n;
-            xrow = a.xp + (size_t)(min(max(a.pairs[off + (slot < cnt ? slot : 0)], 0), tk) >> 3) * D;
+    f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int g = 0; g < 8; g++) {
-                const int wd = 8 * (gq8 + g) + 2 * kq;
-                xa[g][0] = *(const u32x4*)(xrow + 8 * wd);
-                xa[g][1] = *(const u32x4*)(xrow + 8 * wd + 8);
-            }
-        }
-        f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int g = 0; g < 8; g++) {
-            const float s_g = bf16_at(gsv, g), s_u = bf16_at(usv, g);
-            const float c_g = bf16_at(gbv, g) - 128.0f * s_g, c_u = bf16_at(ubv, g) - 128.0f * s_u;
-            const bf16x8 a0 = as_bf16x8(xa[g][0]), a1 = as_bf16x8(xa[g][1]);
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4 ag = mfma16_bf16(a0, as_bf16x8(nibbles_to_codes(gw[g][0], 0x43004300u)), z);
-            ag = mfma16_bf16(a1, as_bf16x8(nibbles_to_codes(gw[g][1], 0x43004300u)), ag);
-            f32x4 au = mfma16_bf16(a0, as_bf16x8(nibbles_to_codes(uw[g][0], 0x43004300u)), z);
-            au = mfma16_bf16(a1, as_bf16x8(nibbles_to_codes(uw[g][1], 0x43004300u)), au);
-            f32x4 xs = mfma16_bf16(a0, as_bf16x8(ones), z);
-            xs = mfma16_bf16(a1, as_bf16x8(ones), xs);
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-                og[v] += s_g * ag[v] + c_g * xs[v];
-                ou[v] += s_u * au[v] + c_u * xs[v];
-            }
-        }
+    for (int g = 0; g < 8; g++) {
+        const float s_g = bf16_at(gsv, g), s_u = bf16_at(usv, g);
+        const float c_g = bf16_at(gbv, g) - 128.0f * s_g, c_u = bf16_at(ubv, g) - 128.0f * s_u;
+        const bf16x8 a0 = as_bf16x8(xa[g][0]), a1 = as_bf16x8(xa[g][1]);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 ag = mfma16_bf16(a0, as_bf16x8(nibbles_to_codes(gw[g][0], 0x43004300u)), z);
+        ag = mfma16_bf16(a1, as_bf16x8(nibbles_to_codes(gw[g][1], 0x43004300u)), ag);
+        f32x4 au = mfma16_bf16(a0, as_bf16x8(nibbles_to_codes(uw[g][0], 0x43004300u)), z);
+        au = mfma16_bf16(a1, as_bf16x8(nibbles_to_codes(uw[g][1], 0x43004300u)), au);
+        f32x4 xs = mfma16_bf16(a0, as_bf16x8(ones), z);
+        xs = mfma16_bf16(a1, as_bf16x8(ones), xs);
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            red_g[16 * m + 4 * kq + v][n] = og[v];
-            red_u[16 * m + 4 * kq + v][n] = ou[v];
+            og[v] += s_g * ag[v] + c_g * xs[v];
+            ou[v] += s_u * au[v] + c_u * xs[v];
         }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        red_g[4 * kq + v][n] = og[v];
+        red_u[4 * kq + v][n] = ou[v];
     }
 }
 
-__global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int max_u) {
-    __shared__ float red[2][4][2][64][16];  // [gate/up][K quarter][feature group][token slot][feature]
+// Sum the four K quarters (in order), SwiGLU, store h (perm8 order) for the
+// tile's token slots; 32 features starting at f0.
+template <class PairOf>
+__device__ __forceinline__ void gu_finish(const DecodeArgs& a, float (*red)[4][2][16][16], int f0, int cnt,
+                                          PairOf pair_of) {
+    const int tid = threadIdx.x;
+    if (tid < cnt * 32) {
+        const int slot = tid >> 5, fl = tid & 31;
+        const int g2 = fl >> 4, c = fl & 15;
+        float gg = 0.f, uu = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            gg += red[0][q][g2][slot][c];
+            uu += red[1][q][g2][slot][c];
+        }
+        const int f = f0 + fl;
+        const int pc = (f & ~7) | perm8_pos(f & 7);
+        const f16 hv = (f16)(silu_f32(gg) * uu);
+        a.h[(size_t)min(max(pair_of(slot), 0), a.T * K - 1) * F + pc] = __builtin_bit_cast(uint16_t, hv);
+    }
+}
+
+__global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_gu_blocks) {
+    __shared__ float red[2][4][2][16][16];  // [gate/up][K quarter][feature group][token slot][feature]
+    __shared__ int tile_pairs[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
-    if ((int)blockIdx.x >= max_u * (F / 32)) {
+    if ((int)blockIdx.x >= n_gu_blocks) {
         // ---- shared expert down: ys[t, o0+n] = sum_j Wsd[o0+n, j] hs[t, j],
         // hs split into bf16 hi + lo; wave w takes K in [64w, 64w+64)
         if (!a.sg) return;
-        const int o0 = 16 * (blockIdx.x - max_u * (F / 32));
+        float(*sred)[16][16] = (float(*)[16][16])red;  // [8][16][16]
+        const int o0 = 16 * (blockIdx.x - n_gu_blocks);
         const int k0 = 64 * wave + 8 * kq;
         const uint16_t* wrow = a.sd + (size_t)(o0 + n) * FS + k0;
         const u32x4 b0 = *(const u32x4*)(wrow), b1 = *(const u32x4*)(wrow + 32);
-        const int nm = (T + 15) / 16;
-        float(*sred)[64][16] = (float(*)[64][16])red;  // [8][64][16]
 #pragma unroll 1
-        for (int m = 0; m < nm; m++) {
+        for (int m = 0; m < (T + 15) / 16; m++) {
             const int t = 16 * m + n;
             const float* hrow = a.hs + (size_t)(t < T ? t : 0) * FS + k0;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -452,160 +488,175 @@ __global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int max_u) {
                 acc = mfma16_bf16(as_bf16x8(lo), bv, acc);
                 acc = mfma16_bf16(as_bf16x8(hi), bv, acc);
             }
+            if (m > 0) __syncthreads();
 #pragma unroll
-            for (int v = 0; v < 4; v++) sred[wave][16 * m + 4 * kq + v][n] = acc[v];
-        }
-        __syncthreads();
-        for (int i = tid; i < T * 16; i += 512) {
-            const int t = i >> 4, c = i & 15;
-            float s = 0.f;
+            for (int v = 0; v < 4; v++) sred[wave][4 * kq + v][n] = acc[v];
+            __syncthreads();
+            if (tid < 256) {
+                const int tl = tid >> 4, c = tid & 15;
+                const int t2 = 16 * m + tl;
+                float s = 0.f;
 #pragma unroll
-            for (int w = 0; w < 8; w++) s += sred[w][t][c];
-            a.ys[(size_t)t * D + o0 + c] = s;
+                for (int w = 0; w < 8; w++) s += sred[w][tl][c];
+                if (t2 < T) a.ys[(size_t)t2 * D + o0 + c] = s;
+            }
         }
         return;
     }
     // ---- routed gate/up: 32 features (2 groups of 16) x 4 K quarters
-    const int u = blockIdx.x / (F / 32), chunk = blockIdx.x % (F / 32);
-    if (u >= min(a.nuniq[0], max_u)) return;
+    const int fg = wave & 1, kq4 = wave >> 1;
+    const int chunk = blockIdx.x % (F / 32);
+    const int f0 = 32 * chunk;
+    const size_t frow = f0 + 16 * fg + n;
+    if (T <= TINY_T) {
+        // one (token, rank) pair per block; every wave routes the token itself
+        const int p = blockIdx.x / (F / 32), t = p >> 3, r = p & 7;
+        float sel_v[K];
+        int sel_i[K];
+        token_top8(a, t, lane, sel_v, sel_i);
+        const int e = sel_i[r] & (E - 1);
+        if (r == 0 && chunk == 0 && wave == 0) write_token_route(a, t, lane, sel_v, sel_i, nullptr);
+        auto pair_of = [p](int) { return p; };
+        gu_tile(a, (size_t)e * F + frow, 8 * kq4, 1, pair_of, lane, red[0][kq4][fg], red[1][kq4][fg]);
+        __syncthreads();
+        gu_finish(a, red, f0, 1, pair_of);
+        return;
+    }
+    const int u = blockIdx.x / (F / 32);
+    if (u >= min(a.nuniq[0], E)) return;
     const int e = a.uexp[u] & (E - 1), cnt = min(max(a.ucnt[u], 1), T);
     const int off = min(max(a.uoff[u], 0), T * K - cnt);
-    const int fg = wave & 1, kq4 = wave >> 1;
-    gu_wave(a, (size_t)e * F + 32 * chunk + 16 * fg + n, 8 * kq4, cnt, off, lane, red[0][kq4][fg], red[1][kq4][fg]);
-    __syncthreads();
-    // quarters summed in order 0..3, then SwiGLU; h stored in perm8 order
-    for (int i = tid; i < cnt * 32; i += 512) {
-        const int slot = i >> 5, fl = i & 31;
-        const int g2 = fl >> 4, c = fl & 15;
-        float gg = 0.f, uu = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            gg += red[0][q][g2][slot][c];
-            uu += red[1][q][g2][slot][c];
-        }
-        const int f = 32 * chunk + fl;
-        const int pc = (f & ~7) | perm8_pos(f & 7);
-        const f16 hv = (f16)(silu_f32(gg) * uu);
-        a.h[(size_t)min(max(a.pairs[off + slot], 0), T * K - 1) * F + pc] = __builtin_bit_cast(uint16_t, hv);
+#pragma unroll 1
+    for (int m0 = 0; m0 < cnt; m0 += 16) {
+        const int tc = min(16, cnt - m0);
+        if (tid < 16) tile_pairs[tid] = a.pairs[off + m0 + min(tid, tc - 1)];
+        __syncthreads();
+        auto pair_of = [&](int slot) { return tile_pairs[slot]; };
+        gu_tile(a, (size_t)e * F + frow, 8 * kq4, tc, pair_of, lane, red[0][kq4][fg], red[1][kq4][fg]);
+        __syncthreads();
+        gu_finish(a, red, f0, tc, pair_of);
+        __syncthreads();
     }
 }
 
 // ------------------------------------------------------------------ stage D
-// One wave: the routed down projection of 16 output rows for one distinct
-// expert, its token tiles one at a time; results land in P[pair][row] (LDS)
-// or in the global partials.
-__device__ __forceinline__ void down_wave(const DecodeArgs& a, int e, int cnt, int off, int o0, int lane,
-                                          float (*P)[17], bool to_lds) {
-    const int n = lane & 15, kq = lane >> 4;
-    const size_t row = (size_t)e * D + o0 + n;
-    const u32x4 sv = *(const u32x4*)(a.ds + row * (F / G));
-    const u32x4 bv = *(const u32x4*)(a.db + row * (F / G));
+// Loads of one (expert, token tile) for 16 output rows: scales, biases,
+// codes, and h rows of the tile's tokens.
+struct DownLoads {
+    u32x4 sv, bv;
     u32x2 wv[8];
     u32x4 ha[8][2];
-    const int tk = a.T * K - 1;
-    const uint16_t* hrow = a.h + (size_t)min(max(a.pairs[off + (n < cnt ? n : 0)], 0), tk) * F;
+};
+
+__device__ __forceinline__ void down_load(const DecodeArgs& a, size_t row, int pair, int lane, DownLoads& L) {
+    const int kq = lane >> 4;
+    L.sv = *(const u32x4*)(a.ds + row * (F / G));
+    L.bv = *(const u32x4*)(a.db + row * (F / G));
+    const uint16_t* hrow = a.h + (size_t)min(max(pair, 0), a.T * K - 1) * F;
 #pragma unroll
-    for (int g = 0; g < 8; g++) {  // loads in the order they are consumed
-        wv[g] = *(const u32x2*)(a.dq + row * (F / 8) + 8 * g + 2 * kq);
+    for (int g = 0; g < 8; g++) {
+        L.wv[g] = *(const u32x2*)(a.dq + row * (F / 8) + 8 * g + 2 * kq);
         const int wd = 8 * g + 2 * kq;
-        ha[g][0] = *(const u32x4*)(hrow + 8 * wd);
-        ha[g][1] = *(const u32x4*)(hrow + 8 * wd + 8);
+        L.ha[g][0] = *(const u32x4*)(hrow + 8 * wd);
+        L.ha[g][1] = *(const u32x4*)(hrow + 8 * wd + 8);
     }
+}
+
+// Down projection of the loaded tile: row n of the lane, token slots 4kq+v.
+__device__ __forceinline__ f32x4 down_compute(const DownLoads& L) {
     const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
-    const int nm = (cnt + 15) >> 4;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 8; g++) {
+        const float s = bf16_at(L.sv, g);
+        const float c = bf16_at(L.bv, g) - 1024.0f * s;
+        const f16x8 a0 = as_f16x8(L.ha[g][0]), a1 = as_f16x8(L.ha[g][1]);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = mfma16_f16(a0, as_f16x8(nibbles_to_codes(L.wv[g][0], 0x64006400u)), z);
+        acc = mfma16_f16(a1, as_f16x8(nibbles_to_codes(L.wv[g][1], 0x64006400u)), acc);
+        f32x4 hsum = mfma16_f16(a0, as_f16x8(ones), z);
+        hsum = mfma16_f16(a1, as_f16x8(ones), hsum);
+#pragma unroll
+        for (int v = 0; v < 4; v++) o[v] += s * acc[v] + c * hsum[v];
+    }
+    return o;
+}
+
+// 16 output rows per block.  T <= 4: the 8T (token, rank) pairs are the
+// work items, taken by the 8 waves in turn, results kept in LDS, then the
+// combine.  T > 4: block (row tile, chunk) takes distinct experts 8*chunk..+7,
+// one per wave, and writes fp32 partials per pair; k_dec_combine finishes.
+__global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
+    __shared__ float P[TINY_T * K][17];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, kq = lane >> 4;
+    const int T = a.T;
+    const bool tiny = T <= TINY_T;
+    const int rt = blockIdx.x % N_ROW_TILES, ch = blockIdx.x / N_ROW_TILES;
+    const int o0 = 16 * rt;
+    const int tk = T * K - 1;
+    if (tiny) {
+        for (int p = wave; p < T * K; p += 8) {
+            const int e = a.idx[p] & (E - 1);
+            DownLoads L;
+            down_load(a, (size_t)e * D + o0 + n, p, lane, L);
+            const f32x4 o = down_compute(L);
+            if (kq == 0) P[p][n] = o[0];  // token slot 0 is the pair
+        }
+        __syncthreads();
+        if (tid < T * 16) {
+            const int t = tid >> 4, c = tid & 15;
+            float sum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < K; r++) sum += a.w[t * K + r] * P[t * K + r][c];
+            if (a.sg) sum += a.sgate[t] * a.ys[(size_t)t * D + o0 + c];
+            a.y[(size_t)t * D + o0 + c] = f32_to_bf16_rne(sum);
+        }
+        return;
+    }
+    const int nu = min(max(a.nuniq[0], 0), min(T * K, E));
+    const int u = 8 * ch + wave;
+    if (u >= nu) return;
+    const int e = a.uexp[u] & (E - 1), cnt = min(max(a.ucnt[u], 1), T);
+    const int off = min(max(a.uoff[u], 0), T * K - cnt);
 #pragma unroll 1
-    for (int m = 0; m < nm; m++) {
-        if (m > 0) {
-            const int slot = 16 * m + n;
-            hrow = a.h + (size_t)min(max(a.pairs[off + (slot < cnt ? slot : 0)], 0), tk) * F;
-#pragma unroll
-            for (int g = 0; g < 8; g++) {
-                const int wd = 8 * g + 2 * kq;
-                ha[g][0] = *(const u32x4*)(hrow + 8 * wd);
-                ha[g][1] = *(const u32x4*)(hrow + 8 * wd + 8);
-            }
-        }
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int g = 0; g < 8; g++) {
-            const float s = bf16_at(sv, g);
-            const float c = bf16_at(bv, g) - 1024.0f * s;
-            const f16x8 a0 = as_f16x8(ha[g][0]), a1 = as_f16x8(ha[g][1]);
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4 acc = mfma16_f16(a0, as_f16x8(nibbles_to_codes(wv[g][0], 0x64006400u)), z);
-            acc = mfma16_f16(a1, as_f16x8(nibbles_to_codes(wv[g][1], 0x64006400u)), acc);
-            f32x4 hsum = mfma16_f16(a0, as_f16x8(ones), z);
-            hsum = mfma16_f16(a1, as_f16x8(ones), hsum);
-#pragma unroll
-            for (int v = 0; v < 4; v++) o[v] += s * acc[v] + c * hsum[v];
-        }
+    for (int m0 = 0; m0 < cnt; m0 += 16) {
+        const int slot0 = m0 + n;
+        DownLoads L;
+        down_load(a, (size_t)e * D + o0 + n, a.pairs[off + (slot0 < cnt ? slot0 : m0)], lane, L);
+        const f32x4 o = down_compute(L);
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const int slot = 16 * m + 4 * kq + v;
-            if (slot < cnt) {
-                const int p = min(max(a.pairs[off + slot], 0), tk);
-                if (to_lds) P[p][n] = o[v];
-                else a.part[(size_t)p * D + o0 + n] = o[v];
-            }
+            const int slot = m0 + 4 * kq + v;
+            if (slot < cnt) a.part[(size_t)min(max(a.pairs[off + slot], 0), tk) * D + o0 + n] = o[v];
         }
     }
 }
 
-__global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
-    __shared__ float P[64 * K][17];
-    __shared__ int last;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int T = a.T;
-    const int rt = blockIdx.x % N_ROW_TILES, ch = blockIdx.x / N_ROW_TILES;
-    const int o0 = 16 * rt;
-    const int nu = min(max(a.nuniq[0], 0), min(T * K, E));
-    const int nch = (nu + 7) >> 3;
-    if (ch >= nch) return;
-    const bool single = nch == 1;  // the whole row tile in this block: keep partials in LDS
-    const int u = 8 * ch + wave;
-    if (u < nu) {
-        const int cnt = min(max(a.ucnt[u], 1), T);
-        down_wave(a, a.uexp[u] & (E - 1), cnt, min(max(a.uoff[u], 0), T * K - cnt), o0, lane, P, single);
-    }
-    if (!single) {
-        // publish this block's partials; the last block of the row tile combines
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const int prev = __hip_atomic_fetch_add(&a.arrive[rt], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            last = prev == nch - 1;
-        }
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-        if (tid == 0) a.arrive[rt] = 0;  // all blocks of this row tile have arrived
-    } else {
-        __syncthreads();
-    }
-    for (int i = tid; i < T * 16; i += 512) {
-        const int t = i >> 4, c = i & 15;
-        float sum = 0.0f;
+// y = sum_{r=0..7} w_r * partial_r + sgate * shexp, fixed order, one bf16
+// rounding (T > 4).
+__global__ void __launch_bounds__(256) k_dec_combine(DecodeArgs a) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.T * D) return;
+    const int t = i / D, o = i % D;
+    float sum = 0.0f;
 #pragma unroll
-        for (int r = 0; r < K; r++) {
-            const float pv = single ? P[t * K + r][c] : a.part[(size_t)(t * K + r) * D + o0 + c];
-            sum += a.w[t * K + r] * pv;
-        }
-        if (a.sg) sum += a.sgate[t] * a.ys[(size_t)t * D + o0 + c];
-        a.y[(size_t)t * D + o0 + c] = f32_to_bf16_rne(sum);
-    }
+    for (int r = 0; r < K; r++) sum += a.w[t * K + r] * a.part[(size_t)(t * K + r) * D + o];
+    if (a.sg) sum += a.sgate[t] * a.ys[i];
+    a.y[i] = f32_to_bf16_rne(sum);
 }
 
 // ------------------------------------------------------------------ host
 size_t decode_workspace_bytes(int T, DecodeLayout* L) {
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     DecodeLayout l{};
-    size_t o = WS_COUNTER_BYTES;
+    size_t o = 0;
     l.logits = o; o += up((size_t)T * E * 4);
     l.xp = o;     o += up((size_t)T * D * 2);
     l.hs = o;     o += up((size_t)T * FS * 4);
     l.ys = o;     o += up((size_t)T * D * 4);
     l.h = o;      o += up((size_t)T * K * F * 2);
-    l.part = o;   o += up((size_t)T * K * D * 4);
+    l.part = o;   o += up(T > TINY_T ? (size_t)T * K * D * 4 : 0);
     l.idx = o;    o += up((size_t)T * K * 4);
     l.w = o;      o += up((size_t)T * K * 4);
     l.sgate = o;  o += up((size_t)T * 4);
@@ -621,18 +672,17 @@ size_t decode_workspace_bytes(int T, DecodeLayout* L) {
 
 template <int NMT>
 static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
-    const int max_u = a.T * K < E ? a.T * K : E;
-    tr.before(MOE_FFN_KERNEL_ROUTER, s);
-    hipLaunchKernelGGL(k_dec_stage_a<NMT>, dim3(N_ROUTER_BLK + N_SGU_BLK + 1), dim3(1024), 0, s, a);
-    tr.after(MOE_FFN_KERNEL_ROUTER, s);
-    tr.before(MOE_FFN_KERNEL_EXPERT_GU, s);
-    hipLaunchKernelGGL(k_dec_stage_c, dim3(max_u * (F / 32) + (a.sg ? N_SDOWN_BLK : 0)), dim3(512), 0, s, a, max_u);
-    tr.after(MOE_FFN_KERNEL_EXPERT_GU, s);
-    tr.before(MOE_FFN_KERNEL_EXPERT_DOWN, s);
-    tr.before(MOE_FFN_KERNEL_COMBINE, s);
-    hipLaunchKernelGGL(k_dec_stage_d, dim3(N_ROW_TILES * ((max_u + 7) / 8)), dim3(512), 0, s, a);
-    tr.after(MOE_FFN_KERNEL_EXPERT_DOWN, s);
-    tr.after(MOE_FFN_KERNEL_COMBINE, s);
+    const bool tiny = a.T <= TINY_T;
+    const int n_items = tiny ? a.T * K : (a.T * K < E ? a.T * K : E);
+    const int n_gu = n_items * (F / 32);
+    tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<NMT>, dim3(N_ROUTER_BLK + N_SGU_BLK + 1), dim3(1024), 0, s, a);
+    if (!tiny) hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_gu + (a.sg ? N_SDOWN_BLK : 0)), dim3(512), 0, s, a,
+              n_gu);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(N_ROW_TILES * (tiny ? 1 : (n_items + 7) / 8)),
+              dim3(512), 0, s, a);
+    if (!tiny)
+        tr.launch(MOE_FFN_KERNEL_COMBINE, k_dec_combine, dim3((a.T * D + 255) / 256), dim3(256), 0, s, a);
 }
 
 hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipStream_t s) {
@@ -650,8 +700,6 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     a.ys = (float*)(ws + L.ys);
     a.h = (uint16_t*)(ws + L.h);
     a.part = (float*)(ws + L.part);
-    a.arrive_a = (int32_t*)(ws + WS_ARRIVE_A);
-    a.arrive = (int32_t*)(ws + WS_ARRIVE_D);
     a.idx = p.idx ? p.idx : (int32_t*)(ws + L.idx);
     a.w = p.w ? p.w : (float*)(ws + L.w);
     a.sgate = (float*)(ws + L.sgate);

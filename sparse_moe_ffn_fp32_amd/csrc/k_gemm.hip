@@ -274,9 +274,7 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.q[0] = p.gate_q; g.sc[0] = p.gate_s; g.bi[0] = p.gate_b;
     g.q[1] = p.up_q; g.sc[1] = p.up_s; g.bi[1] = p.up_b;
     g.h_out = p.h;
-    tr.before(MOE_FFN_KERNEL_EXPERT_GU, s);
-    hipLaunchKernelGGL((k_gemm<MODE_GU, GEMM_BM>), dim3(max_tiles, F / 64), dim3(256), 0, s, g);
-    tr.after(MOE_FFN_KERNEL_EXPERT_GU, s);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm<MODE_GU, GEMM_BM>, dim3(max_tiles, F / 64), dim3(256), 0, s, g);
     // shared gate/up
     if (p.sh_gate) {
         g.sw[0] = p.sh_gate; g.sw[1] = p.sh_up; g.hs_out = p.hs;
@@ -285,19 +283,15 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     // routed down
     g.q[0] = p.down_q; g.sc[0] = p.down_s; g.bi[0] = p.down_b;
     g.p_out = p.partial;
-    tr.before(MOE_FFN_KERNEL_EXPERT_DOWN, s);
-    hipLaunchKernelGGL((k_gemm<MODE_DOWN, GEMM_BM>), dim3(max_tiles, D / 128), dim3(256), 0, s, g);
-    tr.after(MOE_FFN_KERNEL_EXPERT_DOWN, s);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm<MODE_DOWN, GEMM_BM>, dim3(max_tiles, D / 128), dim3(256), 0, s, g);
     // combine
-    tr.before(MOE_FFN_KERNEL_COMBINE, s);
     if (p.sh_gate) {
         g.sw[0] = p.sh_down; g.p_in = p.partial; g.y = p.y;
-        hipLaunchKernelGGL((k_gemm<MODE_SDOWN, GEMM_BM>), dim3(mt, D / 128), dim3(256), 0, s, g);
+        tr.launch(MOE_FFN_KERNEL_COMBINE, k_gemm<MODE_SDOWN, GEMM_BM>, dim3(mt, D / 128), dim3(256), 0, s, g);
     } else {
-        hipLaunchKernelGGL(k_combine_routed, dim3((p.T * D + 255) / 256), dim3(256), 0, s, p.partial, p.pos_of, p.y,
-                           p.T);
+        tr.launch(MOE_FFN_KERNEL_COMBINE, k_combine_routed, dim3((p.T * D + 255) / 256), dim3(256), 0, s,
+                  (const float*)p.partial, (const int32_t*)p.pos_of, p.y, p.T);
     }
-    tr.after(MOE_FFN_KERNEL_COMBINE, s);
     return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@
 // exact and the logits carry fp32 accumulation error only.
 #include "moe_common.h"
 #include "moe_kernels.h"
+#include "../../include/moe_ffn.h"
 
 namespace moe {
 
@@ -151,8 +152,8 @@ hipError_t launch_split_router(const float* wr, uint16_t* wr3, hipStream_t s) {
 }
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr3, const float* bias, float* logits, int T,
-                                hipStream_t s) {
-    hipLaunchKernelGGL(k_router_logits, dim3((T + 31) / 32), dim3(256), 0, s, x, wr3, bias, logits, T);
+                                const Tracer& tr, hipStream_t s) {
+    tr.launch(MOE_FFN_KERNEL_ROUTER, k_router_logits, dim3((T + 31) / 32), dim3(256), 0, s, x, wr3, bias, logits, T);
     return hipGetLastError();
 }
 

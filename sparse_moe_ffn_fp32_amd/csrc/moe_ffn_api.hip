@@ -21,7 +21,7 @@ Layout layout(int64_t T) {
     const int nblk = sort_blocks((int)N);
     const size_t max_tiles = (N + gemm_bm() - 1) / gemm_bm() + E;
     Layout L{};
-    size_t o = WS_COUNTER_BYTES;
+    size_t o = 0;
     L.wr3 = o;        o += up((size_t)3 * E * D * 2);
     L.logits = o;     o += up((size_t)T * E * 4);
     L.idx = o;        o += up(N * 4);
@@ -106,9 +106,7 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
     chk(launch_split_router(router->weight, wr3, s));
     chk(launch_prep_x(x, xh, T, s));
-    tr.before(MOE_FFN_KERNEL_ROUTER, s);
-    chk(launch_router_logits(x, wr3, router->bias, logits, T, s));
-    tr.after(MOE_FFN_KERNEL_ROUTER, s);
+    chk(launch_router_logits(x, wr3, router->bias, logits, T, tr, s));
     chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, T, s));
     chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(), s));
     PrefillGemmParams p{};
@@ -137,23 +135,7 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
 
 }  // namespace
 
-namespace moe {
-__global__ void k_zero_counters(int32_t* p) { p[threadIdx.x] = 0; }
-
-hipError_t launch_workspace_init(void* ws, hipStream_t s) {
-    hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(WS_COUNTER_BYTES / 4), 0, s, (int32_t*)ws);
-    return hipGetLastError();
-}
-}  // namespace moe
-
 extern "C" {
-
-int moe_ffn_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
-    if (!workspace) return MOE_FFN_EINVAL;
-    if (((uintptr_t)workspace & 15u) != 0) return MOE_FFN_EALIGN;
-    if (workspace_bytes < WS_COUNTER_BYTES) return MOE_FFN_EWORKSPACE;
-    return launch_workspace_init(workspace, (hipStream_t)stream) == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
-}
 
 size_t moe_ffn_workspace_size(const moe_ffn_dims* dims, int64_t T) {
     if (!dims || !dims_ok(dims) || T <= 0 || T > MOE_FFN_MAX_T) return 0;

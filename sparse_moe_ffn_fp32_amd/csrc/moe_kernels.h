@@ -1,27 +1,32 @@
 // Host-side launchers of the gfx950 kernels (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
 
-// Optional pair of events around one kernel id (MOE_FFN_KERNEL_*).
+// Optional pair of events for one kernel id (MOE_FFN_KERNEL_*): the launch
+// of that kernel goes through hipExtLaunchKernelGGL, which stamps the events
+// with the kernel's own start and end.
 struct Tracer {
     int kernel = 0;
     hipEvent_t start = nullptr, stop = nullptr;
-    void before(int k, hipStream_t s) const {
-        if (k == kernel && start) (void)hipEventRecord(start, s);
-    }
-    void after(int k, hipStream_t s) const {
-        if (k == kernel && stop) (void)hipEventRecord(stop, s);
+    template <typename... KArgs, typename... Args>
+    void launch(int id, void (*k)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStream_t s, Args... args) const {
+        if (id == kernel && start && stop)
+            hipExtLaunchKernelGGL(k, grid, block, shm, s, start, stop, 0, args...);
+        else
+            hipLaunchKernelGGL(k, grid, block, shm, s, args...);
     }
 };
+
 
 // ---- router (k_router.hip)
 hipError_t launch_split_router(const float* wr, uint16_t* wr3, hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr3, const float* bias, float* logits, int T,
-                                hipStream_t s);
+                                const Tracer& tr, hipStream_t s);
 hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
                        float* sgate, int T, hipStream_t s);
 
@@ -53,13 +58,6 @@ struct PrefillGemmParams {
 int gemm_bm();
 hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s);
 hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hipStream_t s);
-
-// ---- workspace head: arrival counters, zero before the first call and
-// returned to zero by every call
-constexpr size_t WS_COUNTER_BYTES = 1024;
-constexpr size_t WS_ARRIVE_A = 0;    // int32 [1]
-constexpr size_t WS_ARRIVE_D = 256;  // int32 [D/16]
-hipError_t launch_workspace_init(void* ws, hipStream_t s);
 
 // ---- decode path (k_decode.hip), T <= 64
 struct DecodeLayout {

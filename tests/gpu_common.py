@@ -44,7 +44,6 @@ class GpuRunner:
         ws = moe.alloc_workspace(max(T, 1))
         if poison:
             ws.fill_(0xFF)
-            moe.moe_ffn_workspace_init(ws)
         moe.moe_ffn_forward_path(xd, dl, y, ws, idx, w, path=path, T=T)
         torch.cuda.synchronize()
         return (y.cpu().numpy().view(np.uint16)[:T], idx.cpu().numpy()[:T], w.cpu().numpy()[:T])

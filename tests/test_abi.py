@@ -99,8 +99,3 @@ def test_rejects_bad_arguments(L):
     assert _call(L, layer=lay) == moe.MOE_FFN_EALIGN
     assert L.moe_ffn_forward_path(None, 4, 1, None, None, None, 1, None, None, 1, 1, None, 0) == moe.MOE_FFN_EINVAL
 
-
-def test_workspace_init_rejects_bad_arguments(L):
-    assert L.moe_ffn_workspace_init(None, 4096, None) == moe.MOE_FFN_EINVAL
-    assert L.moe_ffn_workspace_init(0x10000008, 4096, None) == moe.MOE_FFN_EALIGN
-    assert L.moe_ffn_workspace_init(0x10000000, 512, None) == moe.MOE_FFN_EWORKSPACE

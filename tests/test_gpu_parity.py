@@ -179,8 +179,7 @@ def test_decode_and_prefill_paths_agree(gpu, layer0, T):
 
 def test_workspace_reuse_across_calls(gpu, layer0):
     """One workspace serves a sequence of calls of both paths and several T;
-    every result equals the result with a fresh workspace (the counters in
-    the workspace head come back to zero after each call)."""
+    every result equals the result with a fresh workspace."""
     import sparse_moe_ffn_fp32_amd as moe
     torch = gpu.torch
     dl = gpu.device_layer(layer0)
@@ -197,4 +196,3 @@ def test_workspace_reuse_across_calls(gpu, layer0):
         got = (y.cpu().numpy().view(np.uint16), idx.cpu().numpy(), w.cpu().numpy())
         for u, v in zip(got, ref):
             assert np.array_equal(u, v), f"T={T}"
-    assert int(ws[:1024].count_nonzero()) == 0
