@@ -32,6 +32,10 @@
  *     the fp16 range |v| <= 65504: the expert GEMMs run on fp16 MFMA operands.
  *     Values below 2^-14 in magnitude lose relative precision (fp16
  *     subnormals); they contribute at most 2^-24 absolute error each.
+ *     On the prefill path (MOE_FFN_PATH_PREFILL, which AUTO takes for
+ *     T > MOE_FFN_DECODE_MAX_T) the intermediates are held in fp16 too:
+ *     every h = silu(gate) * up must stay below 65504 in magnitude and every
+ *     weighted routed-expert output w * down(h) below 1023.
  *   - Calls that share a workspace must not overlap in time (same stream, or
  *     ordered by events).
  */

@@ -6,19 +6,34 @@
 // a time into on-chip memory, used at once by the MFMAs, and the full
 // dequantised matrix never exists; accumulation is fp32.
 //
-// Operands.  A = activation rows (tokens), B = weight rows (output features),
-// both fp16 in LDS with K inside every 8-block in the perm8 order (see
-// moe_common.h).  A dequantised weight is fp16(s*q + b) rounded once; x is
-// converted from bf16 exactly (within the fp16 range); h is rounded once to
-// fp16.  MFMA v_mfma_f32_32x32x16_f16: lane l holds A[l%32][8*(l/32) .. +8]
+// Block tile: 128 activation rows (tokens) x 256 weight rows (output
+// features); 4 waves as 2 x 2, each 64 x 128 = 2 x 4 tiles of
+// v_mfma_f32_32x32x16_f16.  MFMA layout: lane l holds A[l%32][8*(l/32) .. +8]
 // and B[8*(l/32) .. +8][l%32]; accumulator lane l holds C[i][l%32] for
-// i = 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
+// i = 8*(v/4) + 4*(l/32) + v%4, v = 0..15.  K advances in steps of 64, one
+// quantisation group.  Both operands are fp16 with K inside every 8-block in
+// the perm8 order (see moe_common.h); a dequantised weight is fp16(s*q + b)
+// rounded once, x is converted from bf16 exactly (within the fp16 range), h is
+// rounded once to fp16.
+//
+//   A (activations) goes from global memory straight into registers in MFMA
+//     layout.  Inside a K step the lane half kq = l/32 owns K in
+//     [32kq, 32kq + 32) and MFMA sub-step kk uses [32kq + 8kk, +8), so a
+//     lane's slice of one row is one contiguous 64-byte load.  The same K
+//     mapping is applied to B, so every product pairs equal K.
+//   B (weights), one row per thread: the row's codes (or bf16 values) and the
+//     group's scale and bias are loaded two steps ahead, expanded in registers
+//     and written to a double-buffered LDS tile [256][64 + 8]; the MFMAs read
+//     their B fragments from there.
+//   One barrier per K step: step k multiplies from LDS buffer k%2 while the
+//     threads expand step k+1 into the other buffer.
 //
 // Modes:
 //   GU     routed gate/up over the expert-sorted rows; epilogue SwiGLU
 //          h = silu(gate) * up -> fp16 (fused chain (i) of the Lily page,
 //          "Sumazinti tarpini ir busenos srauta");
-//   DOWN   routed down over h; epilogue * routing weight -> fp32 partials;
+//   DOWN   routed down over h; epilogue * routing weight -> fp16 partials
+//          (one per assignment, scaled by 2^6, summed in fp32 by the combine);
 //   SGU    shared gate/up over all tokens (bf16 weights converted to fp16);
 //   SDOWN  shared down; epilogue = the combine: y = sum_{r=0..7} partial_r
 //          + sgate * shexp, fixed order, one bf16 rounding, no atomics
@@ -31,18 +46,22 @@ namespace moe {
 
 enum { MODE_GU = 0, MODE_DOWN = 1, MODE_SGU = 2, MODE_SDOWN = 3 };
 
+constexpr int GEMM_BM = 128;          // activation rows per block
+constexpr int GEMM_BN = 256;          // weight rows per block
 constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // fp16 elements per LDS row (16 B pad)
+constexpr int LDSB = BK + 8;          // fp16 per LDS row (16-byte pad)
+// Partials are stored as fp16(2^6 * w * out): the power of two moves the
+// typical magnitudes (1e-6 .. 1) clear of the fp16 subnormal range and is
+// removed exactly in the combine; |w * out| must stay below 1023.
+constexpr float PARTIAL_SCALE = 64.0f;
 
-template <int MODE, int BM>
+template <int MODE>
 struct GemmCfg {
-    static constexpr int BN = 128;
     static constexpr bool GATED = (MODE == MODE_GU || MODE == MODE_SGU);
     static constexpr bool Q4 = (MODE == MODE_GU || MODE == MODE_DOWN);
     static constexpr int KTOT = GATED ? D : (MODE == MODE_DOWN ? F : FS);
-    static constexpr int MT = BM / 64;   // 32-row MFMA tiles per wave (2x2 waves)
-    static constexpr int NT = 2;         // 32-col MFMA tiles per wave
-    static constexpr int A_CHUNKS = BM * (BK / 8) / 256;  // 16-byte chunks per thread
+    static constexpr int NK = KTOT / BK;  // even for every mode
+    static constexpr int BW = Q4 ? 2 : 8; // 16-byte words of B source per row per step
 };
 
 struct GemmArgs {
@@ -65,22 +84,28 @@ struct GemmArgs {
     const uint16_t* sw[2];   // SGU: shared gate, up; SDOWN: shared down
     // outputs
     uint16_t* h_out;         // GU
-    float* p_out;            // DOWN: fp32 partials [N_assign, D]
+    uint16_t* p_out;         // DOWN: fp16 partials [N_assign, D]
     uint16_t* hs_out;        // SGU
     uint16_t* y;             // SDOWN: bf16 [T, D]
-    const float* p_in;       // SDOWN: partials
+    const uint16_t* p_in;    // SDOWN: fp16 partials
     int T;
 };
 
-template <int MODE, int BM>
+// One step of one thread's B row, as loaded from global memory.
+template <int BW>
+struct BStage {
+    u32x4 c[BW];
+    uint16_t s, b;  // Q4: the group's bf16 scale and bias
+};
+
+template <int MODE>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
-    using C = GemmCfg<MODE, BM>;
-    constexpr int BN = C::BN;
-    __shared__ __attribute__((aligned(16))) f16 sA[BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) f16 sB[BN * LDS_STRIDE];
+    using C = GemmCfg<MODE>;
+    __shared__ __attribute__((aligned(16))) f16 sB[2][GEMM_BN * LDSB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, kq = lane >> 5;
 
     // ---- which rows this block owns
     int e = 0, m0 = 0, rows = 0, seg = 0;
@@ -90,142 +115,177 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
         e = g.tiles[2 * tile];
         m0 = g.tiles[2 * tile + 1];
         seg = g.offs[e];
-        rows = min(BM, g.offs[e + 1] - seg - m0);
+        rows = min(GEMM_BM, g.offs[e + 1] - seg - m0);  // >= 1 for a listed tile
     } else {
-        m0 = blockIdx.x * BM;
-        rows = min(BM, g.T - m0);
+        m0 = blockIdx.x * GEMM_BM;
+        rows = min(GEMM_BM, g.T - m0);                  // >= 1 inside the grid
     }
 
-    // ---- A row pointers of this thread's chunks (fixed over K)
-    const uint16_t* arow[C::A_CHUNKS];
-    const int acol = (tid & 7) * 8;
+    // ---- this lane's two A rows; rows past the end repeat the last valid row
+    // (their products are computed and dropped)
+    const uint16_t* arow[2];
 #pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; i++) {
-        const int r = (tid >> 3) + 32 * i;
-        const uint16_t* p = nullptr;
-        if (r < rows) {
-            if constexpr (MODE == MODE_GU) p = g.xh + (size_t)(g.perm[seg + m0 + r] / K) * D;
-            else if constexpr (MODE == MODE_DOWN) p = g.h + (size_t)(seg + m0 + r) * F;
-            else if constexpr (MODE == MODE_SGU) p = g.xh + (size_t)(m0 + r) * D;
-            else p = g.hs + (size_t)(m0 + r) * FS;
-        }
-        arow[i] = p;
+    for (int mt = 0; mt < 2; mt++) {
+        const int r = min(wm * 64 + mt * 32 + l32, rows - 1);
+        const uint16_t* p;
+        if constexpr (MODE == MODE_GU) p = g.xh + (size_t)(g.perm[seg + m0 + r] / K) * D;
+        else if constexpr (MODE == MODE_DOWN) p = g.h + (size_t)(seg + m0 + r) * F;
+        else if constexpr (MODE == MODE_SGU) p = g.xh + (size_t)(m0 + r) * D;
+        else p = g.hs + (size_t)(m0 + r) * FS;
+        arow[mt] = p + 32 * kq;
     }
 
-    // ---- B row of this thread: row n = tid/2, half = tid%2 (32 K each)
-    const int bn = tid >> 1, bhalf = tid & 1;
-    const uint32_t* bq = nullptr;
-    const uint16_t *bsc = nullptr, *bbi = nullptr, *bw = nullptr;
+    // ---- this thread's B row: LDS row tid.  Gated modes: inside each wave
+    // column's 128 rows, 32-row tile nt holds gate (nt even) or up (nt odd)
+    // rows of features fbase + (nt/2)*32 + 0..31, so one lane's accumulators
+    // for tiles 2h and 2h+1 hold the gate and up value of the same feature.
+    const u32x4* bsrc;
+    const uint16_t *bsc = nullptr, *bbi = nullptr;
     if constexpr (C::GATED) {
-        const int blk = bn >> 5, mat = blk & 1;
-        const int feat = blockIdx.y * 64 + (blk >> 1) * 32 + (bn & 31);
+        const int j = tid & 127, nt = j >> 5, mat = nt & 1;
+        const int feat = blockIdx.y * 128 + (tid >> 7) * 64 + (nt >> 1) * 32 + (j & 31);
         if constexpr (C::Q4) {
             const size_t row = (size_t)e * F + feat;
-            bq = g.q[mat] + row * (D / 8) + 4 * bhalf;
+            bsrc = (const u32x4*)(g.q[mat] + row * (D / 8));
             bsc = g.sc[mat] + row * (D / G);
             bbi = g.bi[mat] + row * (D / G);
         } else {
-            bw = g.sw[mat] + (size_t)feat * D + 32 * bhalf;
+            bsrc = (const u32x4*)(g.sw[mat] + (size_t)feat * D);
         }
     } else {
-        const int o = blockIdx.y * BN + bn;
+        const int o = blockIdx.y * GEMM_BN + tid;
         if constexpr (C::Q4) {
             const size_t row = (size_t)e * D + o;
-            bq = g.q[0] + row * (F / 8) + 4 * bhalf;
+            bsrc = (const u32x4*)(g.q[0] + row * (F / 8));
             bsc = g.sc[0] + row * (F / G);
             bbi = g.bi[0] + row * (F / G);
         } else {
-            bw = g.sw[0] + (size_t)o * FS + 32 * bhalf;
+            bsrc = (const u32x4*)(g.sw[0] + (size_t)o * FS);
         }
     }
 
-    f32x16 acc[C::MT][C::NT];
+    auto load_a = [&](int k, u32x4 (&a)[2][4]) {
 #pragma unroll
-    for (int m = 0; m < C::MT; m++)
+        for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-        for (int n = 0; n < C::NT; n++)
+            for (int i = 0; i < 4; i++) a[mt][i] = *(const u32x4*)(arow[mt] + k * BK + 8 * i);
+    };
+    auto load_b = [&](int k, BStage<C::BW>& b) {
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[m][n][v] = 0.0f;
-
-    for (int k0 = 0; k0 < C::KTOT; k0 += BK) {
-        // global -> registers
-        u32x4 av[C::A_CHUNKS];
-#pragma unroll
-        for (int i = 0; i < C::A_CHUNKS; i++)
-            av[i] = arow[i] ? *(const u32x4*)(arow[i] + k0 + acol) : u32x4{0u, 0u, 0u, 0u};
-        u32x4 bv[4];
+        for (int i = 0; i < C::BW; i++) b.c[i] = bsrc[k * C::BW + i];
         if constexpr (C::Q4) {
-            const u32x4 wq = *(const u32x4*)(bq + k0 / 8);
-            const float s = bf16_to_f32(bsc[k0 / G]);
-            const float b = bf16_to_f32(bbi[k0 / G]);
-            const f16x2 s2 = {(f16)s, (f16)s}, b2 = {(f16)b, (f16)b};
+            b.s = bsc[k];
+            b.b = bbi[k];
+        }
+    };
+    // expand one step of this thread's row into LDS buffer `buf`
+    auto store_b = [&](const BStage<C::BW>& b, int buf) {
+        f16* dst = &sB[buf][tid * LDSB];
+        if constexpr (C::Q4) {
+            const f16 s = (f16)bf16_to_f32(b.s), bb = (f16)bf16_to_f32(b.b);
+            const f16x2 s2 = {s, s}, b2 = {bb, bb};
 #pragma unroll
-            for (int j = 0; j < 4; j++) bv[j] = q4_word_to_f16x8(wq[j], s2, b2);
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * (4 * i + w)) = q4_word_to_f16x8(b.c[i][w], s2, b2);
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; j++) bv[j] = bf16x8_to_f16x8_perm(*(const u32x4*)(bw + k0 + 8 * j));
+            for (int i = 0; i < 8; i++) *(u32x4*)(dst + 8 * i) = bf16x8_to_f16x8_perm(b.c[i]);
         }
-        __syncthreads();  // previous step's MFMAs are done with LDS
+    };
+
+    f32x16 acc[2][4];
 #pragma unroll
-        for (int i = 0; i < C::A_CHUNKS; i++)
-            *(u32x4*)(sA + ((tid >> 3) + 32 * i) * LDS_STRIDE + acol) = av[i];
+    for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) *(u32x4*)(sB + bn * LDS_STRIDE + 32 * bhalf + 8 * j) = bv[j];
-        __syncthreads();
+        for (int nt = 0; nt < 4; nt++)
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; kk++) {
-            f16x8 a[C::MT], b[C::NT];
+            for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
+
+    auto mfma_step = [&](int buf, const u32x4 (&a)[2][4]) {
+        const f16* bb = &sB[buf][(wn * 128 + l32) * LDSB + 32 * kq];
 #pragma unroll
-            for (int m = 0; m < C::MT; m++)
-                a[m] = *(const f16x8*)(sA + (wm * (BM / 2) + m * 32 + (lane & 31)) * LDS_STRIDE + kk * 16 +
-                                       8 * (lane >> 5));
+        for (int kk = 0; kk < 4; kk++) {
+            f16x8 bf[4];
 #pragma unroll
-            for (int n = 0; n < C::NT; n++)
-                b[n] = *(const f16x8*)(sB + (wn * (BN / 2) + n * 32 + (lane & 31)) * LDS_STRIDE + kk * 16 +
-                                       8 * (lane >> 5));
+            for (int nt = 0; nt < 4; nt++) bf[nt] = *(const f16x8*)(bb + nt * 32 * LDSB + 8 * kk);
 #pragma unroll
-            for (int m = 0; m < C::MT; m++)
+            for (int mt = 0; mt < 2; mt++) {
+                const f16x8 af = __builtin_bit_cast(f16x8, a[mt][kk]);
 #pragma unroll
-                for (int n = 0; n < C::NT; n++)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[n], acc[m][n], 0, 0, 0);
+                for (int nt = 0; nt < 4; nt++)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nt], acc[mt][nt], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- pipeline.  Global loads run three steps ahead of the MFMAs (A into
+    // a ring of four register sets, B codes into a ring of four stages); the
+    // B tile of step k+1 is expanded into LDS while step k multiplies.  The
+    // loop body covers four steps so every ring index and LDS buffer is a
+    // compile-time constant; loads past the last step re-read the last step
+    // (in bounds, unused) so the body has no branches.
+    u32x4 ar[4][2][4];
+    BStage<C::BW> br[4];
+#pragma unroll
+    for (int j = 0; j < 3; j++) {
+        load_a(j, ar[j]);
+        load_b(j, br[j]);
+    }
+    store_b(br[0], 0);
+    __syncthreads();
+    static_assert(C::NK % 4 == 0, "K steps must be a multiple of four");
+#pragma unroll 1
+    for (int k = 0; k < C::NK; k += 4) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int kn = min(k + j + 3, C::NK - 1);
+            load_a(kn, ar[(j + 3) & 3]);
+            load_b(kn, br[(j + 3) & 3]);
+            // keep the loads here: the scheduler would otherwise sink them
+            // towards their first use and undo the prefetch
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step(j & 1, ar[j]);
+            store_b(br[(j + 1) & 3], (j + 1) & 1);  // past the end: rewrites an unused buffer
+            __syncthreads();
         }
     }
 
     // ---- epilogues
-    const int col = lane & 31;
 #pragma unroll
-    for (int m = 0; m < C::MT; m++) {
+    for (int mt = 0; mt < 2; mt++) {
 #pragma unroll
         for (int v = 0; v < 16; v++) {
-            const int r = wm * (BM / 2) + m * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
             if (r >= rows) continue;
             if constexpr (C::GATED) {
-                const int feat = blockIdx.y * 64 + wn * 32 + col;
-                const float hv = silu_f32(acc[m][0][v]) * acc[m][1][v];
-                const int pc = (feat & ~7) | perm8_pos(feat & 7);
-                const f16 hh = (f16)hv;
-                if constexpr (MODE == MODE_GU)
-                    g.h_out[(size_t)(seg + m0 + r) * F + pc] = __builtin_bit_cast(uint16_t, hh);
-                else
-                    g.hs_out[(size_t)(m0 + r) * FS + pc] = __builtin_bit_cast(uint16_t, hh);
+#pragma unroll
+                for (int hf = 0; hf < 2; hf++) {
+                    const int feat = blockIdx.y * 128 + wn * 64 + hf * 32 + l32;
+                    const float hv = silu_f32(acc[mt][2 * hf][v]) * acc[mt][2 * hf + 1][v];
+                    const int pc = (feat & ~7) | perm8_pos(feat & 7);
+                    const uint16_t hb = __builtin_bit_cast(uint16_t, (f16)hv);
+                    if constexpr (MODE == MODE_GU) g.h_out[(size_t)(seg + m0 + r) * F + pc] = hb;
+                    else g.hs_out[(size_t)(m0 + r) * FS + pc] = hb;
+                }
             } else if constexpr (MODE == MODE_DOWN) {
                 const int s = seg + m0 + r;
-                const float wt = g.wflat[g.perm[s]];
+                const float wt = g.wflat[g.perm[s]] * PARTIAL_SCALE;
 #pragma unroll
-                for (int n = 0; n < C::NT; n++) {
-                    const int o = blockIdx.y * BN + wn * 64 + n * 32 + col;
-                    g.p_out[(size_t)s * D + o] = wt * acc[m][n][v];
+                for (int nt = 0; nt < 4; nt++) {
+                    const int o = blockIdx.y * GEMM_BN + wn * 128 + nt * 32 + l32;
+                    g.p_out[(size_t)s * D + o] = __builtin_bit_cast(uint16_t, (f16)(wt * acc[mt][nt][v]));  // wt carries 2^6
                 }
             } else {
                 const int t = m0 + r;
                 const float sg = g.sgate[t];
 #pragma unroll
-                for (int n = 0; n < C::NT; n++) {
-                    const int o = blockIdx.y * BN + wn * 64 + n * 32 + col;
+                for (int nt = 0; nt < 4; nt++) {
+                    const int o = blockIdx.y * GEMM_BN + wn * 128 + nt * 32 + l32;
                     float sum = 0.0f;
 #pragma unroll
-                    for (int rr = 0; rr < K; rr++) sum += g.p_in[(size_t)g.pos_of[t * K + rr] * D + o];
-                    sum += sg * acc[m][n][v];
+                    for (int rr = 0; rr < K; rr++) sum += (float)__builtin_bit_cast(f16, g.p_in[(size_t)g.pos_of[t * K + rr] * D + o]);
+                    sum = sum * (1.0f / PARTIAL_SCALE) + sg * acc[mt][nt][v];
                     g.y[(size_t)t * D + o] = f32_to_bf16_rne(sum);
                 }
             }
@@ -234,15 +294,15 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
 }
 
 // y = sum_r partial_r, for layers without a shared expert.
-__global__ void __launch_bounds__(256) k_combine_routed(const float* __restrict__ p, const int32_t* __restrict__ pos_of,
+__global__ void __launch_bounds__(256) k_combine_routed(const uint16_t* __restrict__ p, const int32_t* __restrict__ pos_of,
                                                         uint16_t* __restrict__ y, int T) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= T * D) return;
     const int t = i / D, o = i % D;
     float sum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < K; r++) sum += p[(size_t)pos_of[t * K + r] * D + o];
-    y[i] = f32_to_bf16_rne(sum);
+    for (int r = 0; r < K; r++) sum += (float)__builtin_bit_cast(f16, p[(size_t)pos_of[t * K + r] * D + o]);
+    y[i] = f32_to_bf16_rne(sum * (1.0f / PARTIAL_SCALE));
 }
 
 // x bf16 [T, D] -> fp16 [T, D] in perm8 order.
@@ -251,8 +311,6 @@ __global__ void __launch_bounds__(256) k_prep_x(const uint16_t* __restrict__ x, 
     if (i >= n8) return;
     ((u32x4*)xh)[i] = bf16x8_to_f16x8_perm(((const u32x4*)x)[i]);
 }
-
-constexpr int GEMM_BM = 64;
 
 int gemm_bm() { return GEMM_BM; }
 
@@ -270,27 +328,27 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.T = p.T;
     const int max_tiles = (p.T * K + GEMM_BM - 1) / GEMM_BM + E;
     const int mt = (p.T + GEMM_BM - 1) / GEMM_BM;
-    // routed gate/up
+    // routed gate/up: 128 features (256 gate + up rows) per block
     g.q[0] = p.gate_q; g.sc[0] = p.gate_s; g.bi[0] = p.gate_b;
     g.q[1] = p.up_q; g.sc[1] = p.up_s; g.bi[1] = p.up_b;
     g.h_out = p.h;
-    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm<MODE_GU, GEMM_BM>, dim3(max_tiles, F / 64), dim3(256), 0, s, g);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm<MODE_GU>, dim3(max_tiles, F / 128), dim3(256), 0, s, g);
     // shared gate/up
     if (p.sh_gate) {
         g.sw[0] = p.sh_gate; g.sw[1] = p.sh_up; g.hs_out = p.hs;
-        hipLaunchKernelGGL((k_gemm<MODE_SGU, GEMM_BM>), dim3(mt, FS / 64), dim3(256), 0, s, g);
+        hipLaunchKernelGGL(k_gemm<MODE_SGU>, dim3(mt, FS / 128), dim3(256), 0, s, g);
     }
     // routed down
     g.q[0] = p.down_q; g.sc[0] = p.down_s; g.bi[0] = p.down_b;
     g.p_out = p.partial;
-    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm<MODE_DOWN, GEMM_BM>, dim3(max_tiles, D / 128), dim3(256), 0, s, g);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm<MODE_DOWN>, dim3(max_tiles, D / GEMM_BN), dim3(256), 0, s, g);
     // combine
     if (p.sh_gate) {
         g.sw[0] = p.sh_down; g.p_in = p.partial; g.y = p.y;
-        tr.launch(MOE_FFN_KERNEL_COMBINE, k_gemm<MODE_SDOWN, GEMM_BM>, dim3(mt, D / 128), dim3(256), 0, s, g);
+        tr.launch(MOE_FFN_KERNEL_COMBINE, k_gemm<MODE_SDOWN>, dim3(mt, D / GEMM_BN), dim3(256), 0, s, g);
     } else {
         tr.launch(MOE_FFN_KERNEL_COMBINE, k_combine_routed, dim3((p.T * D + 255) / 256), dim3(256), 0, s,
-                  (const float*)p.partial, (const int32_t*)p.pos_of, p.y, p.T);
+                  (const uint16_t*)p.partial, (const int32_t*)p.pos_of, p.y, p.T);
     }
     return hipGetLastError();
 }

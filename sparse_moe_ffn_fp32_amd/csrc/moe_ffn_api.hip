@@ -36,7 +36,7 @@ Layout layout(int64_t T) {
     L.pos_of = o;     o += up(N * 4);
     L.h = o;          o += up(N * F * 2);
     L.hs = o;         o += up((size_t)T * FS * 2);
-    L.partial = o;    o += up(N * D * 4);
+    L.partial = o;    o += up(N * D * 2);
     L.total = o;
     return L;
 }
@@ -126,7 +126,7 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     p.sh_gate = sh ? sh->gate : nullptr;
     p.sh_up = sh ? sh->up : nullptr;
     p.sh_down = sh ? sh->down : nullptr;
-    p.partial = (float*)at(L.partial);
+    p.partial = (uint16_t*)at(L.partial);
     p.y = y;
     p.T = T;
     chk(launch_prefill_gemms(p, tr, s));

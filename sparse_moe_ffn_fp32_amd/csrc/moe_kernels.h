@@ -51,7 +51,7 @@ struct PrefillGemmParams {
     const uint16_t *gate_s, *up_s, *down_s;
     const uint16_t *gate_b, *up_b, *down_b;
     const uint16_t *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
-    float* partial;
+    uint16_t* partial;  // fp16 [N_assign, D]
     uint16_t* y;
     int T;
 };

@@ -139,7 +139,9 @@ def test_token_permutation_invariance(gpu, layer0, T):
 @pytest.mark.parametrize("T", [20, 70])
 def test_down_scale_halving(gpu, T):
     """Halving every down scale and bias halves y exactly (no shared
-    expert; all values stay normal)."""
+    expert).  Power-of-two scaling commutes with every rounding while values
+    stay normal; the prefill path's fp16 partials carry a 2^6 factor that
+    keeps all but negligible ones (< 1e-6) normal."""
     layer = workloads.layer_for(8, shared=False)
     half = copy.deepcopy(layer)
     for arr in (half.down.scales, half.down.biases):
