@@ -29,6 +29,7 @@ PEAK_F16_TFLOPS = 2500.0
 EXPERT_BYTES = 3 * (512 * 2048 // 2 + 2 * 512 * 32 * 2)  # gate+up+down packed + scales + biases = 1,769,472
 GU_BYTES = 2 * (512 * 2048 // 2 + 2 * 512 * 32 * 2)      # gate+up of one expert = 1,179,648
 SHARED_BYTES = 3 * 512 * 2048 * 2
+SHARED_DOWN_BYTES = 2048 * 512 * 2
 ROUTER_BYTES = 256 * 2048 * 4
 GATE_INP_BYTES = 2048 * 2
 
@@ -39,6 +40,36 @@ WORKLOADS = {
     "prefill_T4096_zipf1.0": dict(T=4096, layers=1, zipf=1.0, flush=True),
     "prefill_T32768_zipf1.5": dict(T=32768, layers=1, zipf=1.5, flush=True),
 }
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed PMC
+    measurement (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain
+    copy of known size gives the same counter), or None when there is none
+    or the kernel's sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        recs = json.load(fh)
+    for r in recs:
+        if r["workload"] == workload and r["kernel"] == kernel:
+            if kernel_source_digest(r["sources"]) != r["sources_sha256"]:
+                return None
+            return int(round(1024 * (r["fetch_kib_per_dispatch"] * r["copy_factor_fetch"]
+                                     + r["write_kib_per_dispatch"] * r["copy_factor_write"])))
+    return None
 
 
 def log(*a):
@@ -87,6 +118,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every traced kernel (stderr)")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of a HIP graph")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (calibrates PMC byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -105,6 +138,15 @@ def main():
     dev = torch.device("cuda:0")
     moe.lib()
     hip = Hip()
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read, {n} bytes written")
+        del src, dst
 
     # ---------------------------------------------------------------- inputs
     n_cpu_layers = min(nlayers, 8)
@@ -227,18 +269,22 @@ def main():
     # dominant kernel: algorithmic bytes / flops per launch
     kernel_ms = float(np.nanmean(kms))
     if T <= 64:
-        gu_bytes = [d * GU_BYTES + T * 2048 * 2 + T * 8 * 512 * 4 for d in distinct]
+        # the gate/up launch also runs the shared expert's down projection:
+        # routed gate/up weights of the distinct experts, the shared down
+        # weights, x and the shared h in; routed h and the shared output out
+        gu_bytes = [d * GU_BYTES + SHARED_DOWN_BYTES + T * 2048 * 2 + T * 512 * 4 + T * 8 * 512 * 2 + T * 2048 * 4
+                    for d in distinct]
         per_launch = float(np.mean(gu_bytes))
         achieved = per_launch / (kernel_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
+                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=measured_traffic(args.workload, "expert_gate_up"),
                     kernel="expert_gate_up", alg_bytes_per_launch=int(per_launch),
                     avg_launch_us=round(kernel_ms * 1e3, 2))
     else:
         flops = 2.0 * T * 8 * 1024 * 2048
         achieved = flops / (kernel_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_F16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / PEAK_F16_TFLOPS, 4), traffic=None,
+                    frac=round(achieved / PEAK_F16_TFLOPS, 4), traffic=measured_traffic(args.workload, "expert_gate_up"),
                     kernel="expert_gate_up", alg_flops_per_launch=flops,
                     avg_launch_us=round(kernel_ms * 1e3, 2))
     step_bytes = sum(d * EXPERT_BYTES + SHARED_BYTES + ROUTER_BYTES + GATE_INP_BYTES + T * 2048 * 4
