@@ -14,19 +14,19 @@
 // quantisation group.  Both operands are fp16 with K inside every 8-block in
 // the perm8 order (see moe_common.h); a dequantised weight is fp16(s*q + b)
 // rounded once, x is converted from bf16 exactly (within the fp16 range), h is
-// rounded once to fp16.
+// rounded once to fp16.  Inside a K step, MFMA sub-step kk and lane half
+// kq = l/32 use K in [32kq + 8kk, +8) for both operands.
 //
-//   A (activations) goes from global memory straight into registers in MFMA
-//     layout.  Inside a K step the lane half kq = l/32 owns K in
-//     [32kq, 32kq + 32) and MFMA sub-step kk uses [32kq + 8kk, +8), so a
-//     lane's slice of one row is one contiguous 64-byte load.  The same K
-//     mapping is applied to B, so every product pairs equal K.
-//   B (weights), one row per thread: the row's codes (or bf16 values) and the
-//     group's scale and bias are loaded two steps ahead, expanded in registers
-//     and written to a double-buffered LDS tile [256][64 + 8]; the MFMAs read
-//     their B fragments from there.
-//   One barrier per K step: step k multiplies from LDS buffer k%2 while the
-//     threads expand step k+1 into the other buffer.
+// Per K step every operand goes global -> registers -> LDS in coalesced
+// pieces, and the MFMAs read their fragments from LDS:
+//   A (activations): eight lanes per row, 16 bytes each, so one load
+//     instruction covers eight whole 128-byte rows of the step;
+//   B (weights): two lanes per weight row, 16 bytes of codes (32 weights)
+//     each; the lane expands them to fp16 s*q + b with the group's scale and
+//     bias, which the block stages in LDS once at its start.
+// Global loads run three steps ahead in a ring of four register stages; LDS
+// tiles are double-buffered; one barrier per step.  Epilogues stage the
+// output tile in LDS so global stores are 16-byte row pieces.
 //
 // Modes:
 //   GU     routed gate/up over the expert-sorted rows; epilogue SwiGLU
@@ -49,7 +49,7 @@ enum { MODE_GU = 0, MODE_DOWN = 1, MODE_SGU = 2, MODE_SDOWN = 3 };
 constexpr int GEMM_BM = 128;          // activation rows per block
 constexpr int GEMM_BN = 256;          // weight rows per block
 constexpr int BK = 64;
-constexpr int LDSB = BK + 8;          // fp16 per LDS row (16-byte pad)
+constexpr int LDSB = BK + 8;          // fp16 per LDS operand row (16-byte pad)
 // Partials are stored as fp16(2^6 * w * out): the power of two moves the
 // typical magnitudes (1e-6 .. 1) clear of the fp16 subnormal range and is
 // removed exactly in the combine; |w * out| must stay below 1023.
@@ -59,9 +59,14 @@ template <int MODE>
 struct GemmCfg {
     static constexpr bool GATED = (MODE == MODE_GU || MODE == MODE_SGU);
     static constexpr bool Q4 = (MODE == MODE_GU || MODE == MODE_DOWN);
+    static constexpr bool ROUTED = (MODE == MODE_GU || MODE == MODE_DOWN);
     static constexpr int KTOT = GATED ? D : (MODE == MODE_DOWN ? F : FS);
-    static constexpr int NK = KTOT / BK;  // even for every mode
-    static constexpr int BW = Q4 ? 2 : 8; // 16-byte words of B source per row per step
+    static constexpr int NK = KTOT / BK;
+    static constexpr int NG = KTOT / G;      // quantisation groups per weight row
+    static constexpr int SROW = NG + 4;      // u32 per staged scale row (pad)
+    static constexpr int BW = Q4 ? 1 : 4;    // 16-byte B words per (row, lane half) per step
+    static constexpr int R = Q4 ? 4 : 2;     // register ring stages (loads run R-1 steps ahead)
+    static constexpr int NB = GATED ? (MODE == MODE_GU ? F : FS) / 128 : D / GEMM_BN;  // column blocks
 };
 
 struct GemmArgs {
@@ -91,106 +96,141 @@ struct GemmArgs {
     int T;
 };
 
-// One step of one thread's B row, as loaded from global memory.
-template <int BW>
-struct BStage {
-    u32x4 c[BW];
-    uint16_t s, b;  // Q4: the group's bf16 scale and bias
+// LDS of one block: double-buffered operand tiles; Q4 modes add the staged
+// scales and biases.  The epilogues reuse the operand tiles.
+template <int MODE>
+struct GemmSmem {
+    using C = GemmCfg<MODE>;
+    f16 a[2][GEMM_BM * LDSB];
+    f16 b[2][GEMM_BN * LDSB];
+    uint32_t sb[C::Q4 ? GEMM_BN * C::SROW : 1];  // (bias << 16) | scale, bf16 bits
 };
 
 template <int MODE>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
     using C = GemmCfg<MODE>;
-    __shared__ __attribute__((aligned(16))) f16 sB[2][GEMM_BN * LDSB];
+    __shared__ __attribute__((aligned(16))) GemmSmem<MODE> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, kq = lane >> 5;
 
-    // ---- which rows this block owns
+    // ---- which (row tile, column block) this block owns.  Workgroups are
+    // dealt to the 8 XCDs round-robin by id; id p is remapped so that XCD
+    // p%8 takes one contiguous run of the live (tile, column block) items,
+    // column block fastest: the blocks sharing a tile's activations, and the
+    // tiles sharing an expert's weights, then meet in the same L2.
+    constexpr int NB = C::NB;
+    const int n_tiles = C::ROUTED ? g.tile_count[0] : (g.T + GEMM_BM - 1) / GEMM_BM;
+    const int live = n_tiles * NB, per_xcd = (live + 7) >> 3;
+    const int slot = blockIdx.x >> 3, item = (blockIdx.x & 7) * per_xcd + slot;
+    if (slot >= per_xcd || item >= live) return;
+    const int tile = item / NB, nblk = item % NB;
     int e = 0, m0 = 0, rows = 0, seg = 0;
-    if constexpr (MODE == MODE_GU || MODE == MODE_DOWN) {
-        const int tile = blockIdx.x;
-        if (tile >= g.tile_count[0]) return;
+    if constexpr (C::ROUTED) {
         e = g.tiles[2 * tile];
         m0 = g.tiles[2 * tile + 1];
         seg = g.offs[e];
         rows = min(GEMM_BM, g.offs[e + 1] - seg - m0);  // >= 1 for a listed tile
     } else {
-        m0 = blockIdx.x * GEMM_BM;
-        rows = min(GEMM_BM, g.T - m0);                  // >= 1 inside the grid
+        m0 = tile * GEMM_BM;
+        rows = min(GEMM_BM, g.T - m0);                  // >= 1 for tile < n_tiles
     }
 
-    // ---- this lane's two A rows; rows past the end repeat the last valid row
-    // (their products are computed and dropped)
-    const uint16_t* arow[2];
+    // ---- A: this thread loads 16 bytes (chunk ac) of rows ar0 + 32i, i < 4;
+    // rows past the end repeat the last valid row (their results are dropped)
+    const int ac = tid & 7, ar0 = tid >> 3;
+    const uint16_t* apt[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-        const int r = min(wm * 64 + mt * 32 + l32, rows - 1);
+    for (int i = 0; i < 4; i++) {
+        const int r = min(ar0 + 32 * i, rows - 1);
         const uint16_t* p;
         if constexpr (MODE == MODE_GU) p = g.xh + (size_t)(g.perm[seg + m0 + r] / K) * D;
         else if constexpr (MODE == MODE_DOWN) p = g.h + (size_t)(seg + m0 + r) * F;
         else if constexpr (MODE == MODE_SGU) p = g.xh + (size_t)(m0 + r) * D;
         else p = g.hs + (size_t)(m0 + r) * FS;
-        arow[mt] = p + 32 * kq;
+        apt[i] = p + 8 * ac;
     }
 
-    // ---- this thread's B row: LDS row tid.  Gated modes: inside each wave
+    // ---- B: this thread covers lane half bh (K [32bh, 32bh+32) of a step) of
+    // LDS weight rows br0 and br0 + 128.  Gated modes: inside each wave
     // column's 128 rows, 32-row tile nt holds gate (nt even) or up (nt odd)
     // rows of features fbase + (nt/2)*32 + 0..31, so one lane's accumulators
     // for tiles 2h and 2h+1 hold the gate and up value of the same feature.
-    const u32x4* bsrc;
-    const uint16_t *bsc = nullptr, *bbi = nullptr;
-    if constexpr (C::GATED) {
-        const int j = tid & 127, nt = j >> 5, mat = nt & 1;
-        const int feat = blockIdx.y * 128 + (tid >> 7) * 64 + (nt >> 1) * 32 + (j & 31);
-        if constexpr (C::Q4) {
-            const size_t row = (size_t)e * F + feat;
-            bsrc = (const u32x4*)(g.q[mat] + row * (D / 8));
-            bsc = g.sc[mat] + row * (D / G);
-            bbi = g.bi[mat] + row * (D / G);
+    const int bh = tid & 1, br0 = tid >> 1;
+    auto wrow = [&](int n, int& mat) -> size_t {  // global weight row of LDS row n
+        if constexpr (C::GATED) {
+            const int j = n & 127, nt = j >> 5;
+            mat = nt & 1;
+            const int feat = nblk * 128 + (n >> 7) * 64 + (nt >> 1) * 32 + (j & 31);
+            return C::Q4 ? (size_t)e * F + feat : (size_t)feat;
         } else {
-            bsrc = (const u32x4*)(g.sw[mat] + (size_t)feat * D);
+            mat = 0;
+            const int o = nblk * GEMM_BN + n;
+            return C::Q4 ? (size_t)e * D + o : (size_t)o;
         }
-    } else {
-        const int o = blockIdx.y * GEMM_BN + tid;
-        if constexpr (C::Q4) {
-            const size_t row = (size_t)e * D + o;
-            bsrc = (const u32x4*)(g.q[0] + row * (F / 8));
-            bsc = g.sc[0] + row * (F / G);
-            bbi = g.bi[0] + row * (F / G);
-        } else {
-            bsrc = (const u32x4*)(g.sw[0] + (size_t)o * FS);
+    };
+    const u32x4* bpt[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        int mat;
+        const size_t row = wrow(br0 + 128 * i, mat);
+        if constexpr (C::Q4) bpt[i] = (const u32x4*)(g.q[mat] + row * (C::KTOT / 8)) + bh;
+        else bpt[i] = (const u32x4*)(g.sw[mat] + row * C::KTOT) + 4 * bh;
+    }
+
+    // ---- stage the block's scales and biases: LDS row n = tid
+    if constexpr (C::Q4) {
+        int mat;
+        const size_t row = wrow(tid, mat);
+        const uint16_t* sp = g.sc[mat] + row * C::NG;
+        const uint16_t* bp = g.bi[mat] + row * C::NG;
+        uint32_t* dst = &sm.sb[tid * C::SROW];
+#pragma unroll
+        for (int i = 0; i < C::NG / 8; i++) {
+            const u32x4 sv = *(const u32x4*)(sp + 8 * i), bv = *(const u32x4*)(bp + 8 * i);
+            u32x4 lo, hi;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                lo[j] = (sv[j] & 0xffffu) | (bv[j] << 16);
+                hi[j] = (sv[j] >> 16) | (bv[j] & 0xffff0000u);
+            }
+            // groups 8i + 2j (lo) and 8i + 2j + 1 (hi)
+            *(u32x4*)(dst + 8 * i) = u32x4{lo[0], hi[0], lo[1], hi[1]};
+            *(u32x4*)(dst + 8 * i + 4) = u32x4{lo[2], hi[2], lo[3], hi[3]};
         }
     }
 
-    auto load_a = [&](int k, u32x4 (&a)[2][4]) {
-#pragma unroll
-        for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) a[mt][i] = *(const u32x4*)(arow[mt] + k * BK + 8 * i);
+    struct Stage {
+        u32x4 a[4];
+        u32x4 b[2][C::BW];
     };
-    auto load_b = [&](int k, BStage<C::BW>& b) {
+    auto load = [&](int k, Stage& st) {
 #pragma unroll
-        for (int i = 0; i < C::BW; i++) b.c[i] = bsrc[k * C::BW + i];
-        if constexpr (C::Q4) {
-            b.s = bsc[k];
-            b.b = bbi[k];
-        }
+        for (int i = 0; i < 4; i++) st.a[i] = *(const u32x4*)(apt[i] + k * BK);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int w = 0; w < C::BW; w++) st.b[i][w] = bpt[i][k * (C::Q4 ? 2 : 8) + w];
     };
-    // expand one step of this thread's row into LDS buffer `buf`
-    auto store_b = [&](const BStage<C::BW>& b, int buf) {
-        f16* dst = &sB[buf][tid * LDSB];
-        if constexpr (C::Q4) {
-            const f16 s = (f16)bf16_to_f32(b.s), bb = (f16)bf16_to_f32(b.b);
-            const f16x2 s2 = {s, s}, b2 = {bb, bb};
+    // write step k's staged data into LDS buffer `buf`
+    auto store = [&](int k, const Stage& st, int buf) {
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 4; i++) *(u32x4*)&sm.a[buf][(ar0 + 32 * i) * LDSB + 8 * ac] = st.a[i];
 #pragma unroll
-                for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * (4 * i + w)) = q4_word_to_f16x8(b.c[i][w], s2, b2);
-        } else {
+        for (int i = 0; i < 2; i++) {
+            const int n = br0 + 128 * i;
+            f16* dst = &sm.b[buf][n * LDSB + 32 * bh];
+            if constexpr (C::Q4) {
+                const uint32_t sbw = sm.sb[n * C::SROW + k];
+                const f16 sv = (f16)bf16_to_f32(sbw & 0xffffu), bv = (f16)bf16_to_f32(sbw >> 16);
+                const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
 #pragma unroll
-            for (int i = 0; i < 8; i++) *(u32x4*)(dst + 8 * i) = bf16x8_to_f16x8_perm(b.c[i]);
+                for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = q4_word_to_f16x8(st.b[i][0][w], s2, b2);
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = bf16x8_to_f16x8_perm(st.b[i][w]);
+            }
         }
     };
 
@@ -202,93 +242,151 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
 
-    auto mfma_step = [&](int buf, const u32x4 (&a)[2][4]) {
-        const f16* bb = &sB[buf][(wn * 128 + l32) * LDSB + 32 * kq];
+    auto mfma_step = [&](int buf) {
+        const f16* ab = &sm.a[buf][(wm * 64 + l32) * LDSB + 32 * kq];
+        const f16* bb = &sm.b[buf][(wn * 128 + l32) * LDSB + 32 * kq];
 #pragma unroll
         for (int kk = 0; kk < 4; kk++) {
-            f16x8 bf[4];
+            f16x8 af[2], bf[4];
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
 #pragma unroll
             for (int nt = 0; nt < 4; nt++) bf[nt] = *(const f16x8*)(bb + nt * 32 * LDSB + 8 * kk);
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++) {
-                const f16x8 af = __builtin_bit_cast(f16x8, a[mt][kk]);
+            for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                 for (int nt = 0; nt < 4; nt++)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nt], acc[mt][nt], 0, 0, 0);
-            }
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
         }
     };
 
-    // ---- pipeline.  Global loads run three steps ahead of the MFMAs (A into
-    // a ring of four register sets, B codes into a ring of four stages); the
-    // B tile of step k+1 is expanded into LDS while step k multiplies.  The
-    // loop body covers four steps so every ring index and LDS buffer is a
-    // compile-time constant; loads past the last step re-read the last step
-    // (in bounds, unused) so the body has no branches.
-    u32x4 ar[4][2][4];
-    BStage<C::BW> br[4];
+    // ---- pipeline.  Step k's loads sit in ring stage k % R; they are issued
+    // R-1 steps ahead and written to LDS one step ahead of their MFMAs.  The
+    // body covers R steps so ring stages and LDS buffers are compile-time
+    // constants; loads past the last step re-read the last step and the final
+    // store fills an unused buffer, so the body has no branches.
+    static_assert(C::NK % C::R == 0, "K steps must be a multiple of the ring size");
+    Stage ring[C::R];
 #pragma unroll
-    for (int j = 0; j < 3; j++) {
-        load_a(j, ar[j]);
-        load_b(j, br[j]);
-    }
-    store_b(br[0], 0);
+    for (int j = 0; j < C::R - 1; j++) load(j, ring[j]);
+    __syncthreads();  // staged scales and biases visible
+    store(0, ring[0], 0);
     __syncthreads();
-    static_assert(C::NK % 4 == 0, "K steps must be a multiple of four");
 #pragma unroll 1
-    for (int k = 0; k < C::NK; k += 4) {
+    for (int k0 = 0; k0 < C::NK; k0 += C::R) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int kn = min(k + j + 3, C::NK - 1);
-            load_a(kn, ar[(j + 3) & 3]);
-            load_b(kn, br[(j + 3) & 3]);
+        for (int j = 0; j < C::R; j++) {
+            const int k = k0 + j;
+            load(min(k + C::R - 1, C::NK - 1), ring[(j + C::R - 1) % C::R]);
             // keep the loads here: the scheduler would otherwise sink them
             // towards their first use and undo the prefetch
             __builtin_amdgcn_sched_barrier(0);
-            mfma_step(j & 1, ar[j]);
-            store_b(br[(j + 1) & 3], (j + 1) & 1);  // past the end: rewrites an unused buffer
+            mfma_step(j & 1);
+            store(min(k + 1, C::NK - 1), ring[(j + 1) % C::R], (j + 1) & 1);
             __syncthreads();
         }
     }
 
-    // ---- epilogues
+    // ---- epilogues (the loop ended with a barrier: the operand tiles are free)
+    if constexpr (C::GATED) {
+        // h tile [128 rows][128 features] fp16 in LDS, then 16-byte row pieces
+        constexpr int HS = 128 + 8;
+        f16* hb = &sm.b[0][0];
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
+        for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-        for (int v = 0; v < 16; v++) {
-            const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
-            if (r >= rows) continue;
-            if constexpr (C::GATED) {
+            for (int v = 0; v < 16; v++) {
+                const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
 #pragma unroll
                 for (int hf = 0; hf < 2; hf++) {
-                    const int feat = blockIdx.y * 128 + wn * 64 + hf * 32 + l32;
+                    const int f = wn * 64 + hf * 32 + l32;  // feature inside the block
                     const float hv = silu_f32(acc[mt][2 * hf][v]) * acc[mt][2 * hf + 1][v];
-                    const int pc = (feat & ~7) | perm8_pos(feat & 7);
-                    const uint16_t hb = __builtin_bit_cast(uint16_t, (f16)hv);
-                    if constexpr (MODE == MODE_GU) g.h_out[(size_t)(seg + m0 + r) * F + pc] = hb;
-                    else g.hs_out[(size_t)(m0 + r) * FS + pc] = hb;
-                }
-            } else if constexpr (MODE == MODE_DOWN) {
-                const int s = seg + m0 + r;
-                const float wt = g.wflat[g.perm[s]] * PARTIAL_SCALE;
-#pragma unroll
-                for (int nt = 0; nt < 4; nt++) {
-                    const int o = blockIdx.y * GEMM_BN + wn * 128 + nt * 32 + l32;
-                    g.p_out[(size_t)s * D + o] = __builtin_bit_cast(uint16_t, (f16)(wt * acc[mt][nt][v]));  // wt carries 2^6
-                }
-            } else {
-                const int t = m0 + r;
-                const float sg = g.sgate[t];
-#pragma unroll
-                for (int nt = 0; nt < 4; nt++) {
-                    const int o = blockIdx.y * GEMM_BN + wn * 128 + nt * 32 + l32;
-                    float sum = 0.0f;
-#pragma unroll
-                    for (int rr = 0; rr < K; rr++) sum += (float)__builtin_bit_cast(f16, g.p_in[(size_t)g.pos_of[t * K + rr] * D + o]);
-                    sum = sum * (1.0f / PARTIAL_SCALE) + sg * acc[mt][nt][v];
-                    g.y[(size_t)t * D + o] = f32_to_bf16_rne(sum);
+                    hb[r * HS + ((f & ~7) | perm8_pos(f & 7))] = (f16)hv;
                 }
             }
+        __syncthreads();
+        // 128 rows x 16 pieces of 8 features
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int pc = tid + 256 * i, r = pc >> 4, c = pc & 15;
+            if (r < rows) {
+                const u32x4 v = *(const u32x4*)&hb[r * HS + 8 * c];
+                const int f = nblk * 128 + 8 * c;
+                if constexpr (MODE == MODE_GU) *(u32x4*)&g.h_out[(size_t)(seg + m0 + r) * F + f] = v;
+                else *(u32x4*)&g.hs_out[(size_t)(m0 + r) * FS + f] = v;
+            }
+        }
+    } else if constexpr (MODE == MODE_DOWN) {
+        // partial tile [128 rows][256 outputs] fp16 (x 2^6 x routing weight)
+        constexpr int PS = GEMM_BN + 8;
+        f16* pb = &sm.a[0][0];  // spans the A and B tiles (67.6 KB)
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
+                const float wt = g.wflat[g.perm[seg + m0 + min(r, rows - 1)]] * PARTIAL_SCALE;
+#pragma unroll
+                for (int nt = 0; nt < 4; nt++) pb[r * PS + wn * 128 + nt * 32 + l32] = (f16)(wt * acc[mt][nt][v]);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int pc = tid + 256 * i, r = pc >> 5, c = pc & 31;
+            if (r < rows)
+                *(u32x4*)&g.p_out[(size_t)(seg + m0 + r) * D + nblk * GEMM_BN + 8 * c] = *(const u32x4*)&pb[r * PS + 8 * c];
+        }
+    } else {
+        // combine: y = 2^-6 * sum_r partial_r + sgate * shexp, in two passes
+        // of 128 columns (the fp32 shared tile of one wave column per pass)
+        constexpr int YS = 128 + 4;
+        float* yb = (float*)&sm.a[0][0];  // 128 x 132 fp32 = 67.6 KB
+#pragma unroll
+        for (int pass = 0; pass < 2; pass++) {
+            if (wn == pass) {
+#pragma unroll
+                for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) {
+                        const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
+#pragma unroll
+                        for (int nt = 0; nt < 4; nt++) yb[r * YS + nt * 32 + l32] = acc[mt][nt][v];
+                    }
+            }
+            __syncthreads();
+            // 128 rows x 16 pieces of 8 outputs
+#pragma unroll 1
+            for (int i = 0; i < 8; i++) {
+                const int pc = tid + 256 * i, r = pc >> 4, c = pc & 15;
+                if (r < rows) {
+                    const int t = m0 + r, o = nblk * GEMM_BN + pass * 128 + 8 * c;
+                    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int rr = 0; rr < K; rr++) {
+                        const u32x4 pv = *(const u32x4*)&g.p_in[(size_t)g.pos_of[t * K + rr] * D + o];
+#pragma unroll
+                        for (int j = 0; j < 4; j++) {
+                            // copy the element to a scalar first: a bit cast of the
+                            // vector-element expression itself is miscompiled by
+                            // clang 22 (it reads element 0 for every j)
+                            const uint32_t pw = pv[j];
+                            const f16x2 h2 = __builtin_bit_cast(f16x2, pw);
+                            sum[2 * j] += (float)h2[0];
+                            sum[2 * j + 1] += (float)h2[1];
+                        }
+                    }
+                    const float sg = g.sgate[t];
+                    u32x4 out;
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const float y0 = sum[2 * j] * (1.0f / PARTIAL_SCALE) + sg * yb[r * YS + 8 * c + 2 * j];
+                        const float y1 = sum[2 * j + 1] * (1.0f / PARTIAL_SCALE) + sg * yb[r * YS + 8 * c + 2 * j + 1];
+                        out[j] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+                    }
+                    *(u32x4*)&g.y[(size_t)t * D + o] = out;
+                }
+            }
+            __syncthreads();
         }
     }
 }
@@ -326,26 +424,27 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.perm = p.perm; g.pos_of = p.pos_of; g.offs = p.offs; g.tiles = p.tiles; g.tile_count = p.tile_count;
     g.wflat = p.wflat; g.sgate = p.sgate;
     g.T = p.T;
-    const int max_tiles = (p.T * K + GEMM_BM - 1) / GEMM_BM + E;
+    const int max_tiles = (p.T * K + GEMM_BM - 1) / GEMM_BM + E;  // bound on the sort's tile count
     const int mt = (p.T + GEMM_BM - 1) / GEMM_BM;
+    auto grid = [](int items) { return dim3(8 * ((items + 7) / 8)); };
     // routed gate/up: 128 features (256 gate + up rows) per block
     g.q[0] = p.gate_q; g.sc[0] = p.gate_s; g.bi[0] = p.gate_b;
     g.q[1] = p.up_q; g.sc[1] = p.up_s; g.bi[1] = p.up_b;
     g.h_out = p.h;
-    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm<MODE_GU>, dim3(max_tiles, F / 128), dim3(256), 0, s, g);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm<MODE_GU>, grid(max_tiles * (F / 128)), dim3(256), 0, s, g);
     // shared gate/up
     if (p.sh_gate) {
         g.sw[0] = p.sh_gate; g.sw[1] = p.sh_up; g.hs_out = p.hs;
-        hipLaunchKernelGGL(k_gemm<MODE_SGU>, dim3(mt, FS / 128), dim3(256), 0, s, g);
+        hipLaunchKernelGGL(k_gemm<MODE_SGU>, grid(mt * (FS / 128)), dim3(256), 0, s, g);
     }
     // routed down
     g.q[0] = p.down_q; g.sc[0] = p.down_s; g.bi[0] = p.down_b;
     g.p_out = p.partial;
-    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm<MODE_DOWN>, dim3(max_tiles, D / GEMM_BN), dim3(256), 0, s, g);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm<MODE_DOWN>, grid(max_tiles * (D / GEMM_BN)), dim3(256), 0, s, g);
     // combine
     if (p.sh_gate) {
         g.sw[0] = p.sh_down; g.p_in = p.partial; g.y = p.y;
-        tr.launch(MOE_FFN_KERNEL_COMBINE, k_gemm<MODE_SDOWN>, dim3(mt, D / GEMM_BN), dim3(256), 0, s, g);
+        tr.launch(MOE_FFN_KERNEL_COMBINE, k_gemm<MODE_SDOWN>, grid(mt * (D / GEMM_BN)), dim3(256), 0, s, g);
     } else {
         tr.launch(MOE_FFN_KERNEL_COMBINE, k_combine_routed, dim3((p.T * D + 255) / 256), dim3(256), 0, s,
                   (const uint16_t*)p.partial, (const int32_t*)p.pos_of, p.y, p.T);
