@@ -27,9 +27,9 @@
  *     enqueues work on it: no host synchronisation, no device allocation.
  *     Faults inside kernels surface as HIP errors at the caller's next
  *     synchronisation, as for any HIP launch.
- *   - Inputs must be finite.  x, the shared-expert weights, and every
- *     dequantised routed weight s*q + b (and s, b themselves) must lie within
- *     the fp16 range |v| <= 65504: the expert GEMMs run on fp16 MFMA operands.
+ *   - Inputs must be finite.  x, the router and shared-expert weights, and
+ *     every dequantised routed weight s*q + b (and s, b themselves) must lie
+ *     within the fp16 range |v| <= 65504: the GEMMs run on fp16 MFMA operands.
  *     Values below 2^-14 in magnitude lose relative precision (fp16
  *     subnormals); they contribute at most 2^-24 absolute error each.
  *     On the prefill path (MOE_FFN_PATH_PREFILL, which AUTO takes for

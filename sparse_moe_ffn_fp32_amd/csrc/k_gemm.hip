@@ -37,14 +37,18 @@
 //   SGU    shared gate/up over all tokens (bf16 weights converted to fp16);
 //   SDOWN  shared down; epilogue = the combine: y = sum_{r=0..7} partial_r
 //          + sgate * shexp, fixed order, one bf16 rounding, no atomics
-//          (fused chain (ii)).
+//          (fused chain (ii));
+//   ROUTER router logits over all tokens: B = the fp32 router weights as two
+//          fp16 planes hi + lo (|w - hi - lo| <= 2^-22 |w|), paired like gate
+//          and up so one lane adds the two planes of an expert; epilogue
+//          + router bias -> fp32 logits.
 #include "moe_common.h"
 #include "moe_kernels.h"
 #include "../../include/moe_ffn.h"
 
 namespace moe {
 
-enum { MODE_GU = 0, MODE_DOWN = 1, MODE_SGU = 2, MODE_SDOWN = 3 };
+enum { MODE_GU = 0, MODE_DOWN = 1, MODE_SGU = 2, MODE_SDOWN = 3, MODE_ROUTER = 4 };
 
 constexpr int GEMM_BM = 128;          // activation rows per block
 constexpr int GEMM_BN = 256;          // weight rows per block
@@ -58,15 +62,18 @@ constexpr float PARTIAL_SCALE = 64.0f;
 template <int MODE>
 struct GemmCfg {
     static constexpr bool GATED = (MODE == MODE_GU || MODE == MODE_SGU);
+    static constexpr bool PAIRED = GATED || MODE == MODE_ROUTER;  // B rows in pairs of 32-row tiles
     static constexpr bool Q4 = (MODE == MODE_GU || MODE == MODE_DOWN);
+    static constexpr bool F16SRC = (MODE == MODE_ROUTER);          // B already fp16 in perm8 order
     static constexpr bool ROUTED = (MODE == MODE_GU || MODE == MODE_DOWN);
-    static constexpr int KTOT = GATED ? D : (MODE == MODE_DOWN ? F : FS);
+    static constexpr int KTOT = (GATED || MODE == MODE_ROUTER) ? D : (MODE == MODE_DOWN ? F : FS);
     static constexpr int NK = KTOT / BK;
     static constexpr int NG = KTOT / G;      // quantisation groups per weight row
     static constexpr int SROW = NG + 4;      // u32 per staged scale row (pad)
     static constexpr int BW = Q4 ? 1 : 4;    // 16-byte B words per (row, lane half) per step
     static constexpr int R = Q4 ? 4 : 2;     // register ring stages (loads run R-1 steps ahead)
-    static constexpr int NB = GATED ? (MODE == MODE_GU ? F : FS) / 128 : D / GEMM_BN;  // column blocks
+    static constexpr int NB = MODE == MODE_ROUTER ? E / 128
+                            : GATED ? (MODE == MODE_GU ? F : FS) / 128 : D / GEMM_BN;  // column blocks
 };
 
 struct GemmArgs {
@@ -93,6 +100,9 @@ struct GemmArgs {
     uint16_t* hs_out;        // SGU
     uint16_t* y;             // SDOWN: bf16 [T, D]
     const uint16_t* p_in;    // SDOWN: fp16 partials
+    const uint16_t* wr2;     // ROUTER: fp16 [2, E, D] (hi, lo planes; perm8)
+    const float* rbias;      // ROUTER: fp32 [E] or null
+    float* logits;           // ROUTER: fp32 [T, E]
     int T;
 };
 
@@ -147,7 +157,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
         const uint16_t* p;
         if constexpr (MODE == MODE_GU) p = g.xh + (size_t)(g.perm[seg + m0 + r] / K) * D;
         else if constexpr (MODE == MODE_DOWN) p = g.h + (size_t)(seg + m0 + r) * F;
-        else if constexpr (MODE == MODE_SGU) p = g.xh + (size_t)(m0 + r) * D;
+        else if constexpr (MODE == MODE_SGU || MODE == MODE_ROUTER) p = g.xh + (size_t)(m0 + r) * D;
         else p = g.hs + (size_t)(m0 + r) * FS;
         apt[i] = p + 8 * ac;
     }
@@ -159,10 +169,11 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
     // for tiles 2h and 2h+1 hold the gate and up value of the same feature.
     const int bh = tid & 1, br0 = tid >> 1;
     auto wrow = [&](int n, int& mat) -> size_t {  // global weight row of LDS row n
-        if constexpr (C::GATED) {
+        if constexpr (C::PAIRED) {
             const int j = n & 127, nt = j >> 5;
             mat = nt & 1;
             const int feat = nblk * 128 + (n >> 7) * 64 + (nt >> 1) * 32 + (j & 31);
+            if constexpr (MODE == MODE_ROUTER) return (size_t)mat * E + feat;  // plane, expert
             return C::Q4 ? (size_t)e * F + feat : (size_t)feat;
         } else {
             mat = 0;
@@ -176,6 +187,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
         int mat;
         const size_t row = wrow(br0 + 128 * i, mat);
         if constexpr (C::Q4) bpt[i] = (const u32x4*)(g.q[mat] + row * (C::KTOT / 8)) + bh;
+        else if constexpr (C::F16SRC) bpt[i] = (const u32x4*)(g.wr2 + row * C::KTOT) + 4 * bh;
         else bpt[i] = (const u32x4*)(g.sw[mat] + row * C::KTOT) + 4 * bh;
     }
 
@@ -227,6 +239,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
                 const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
 #pragma unroll
                 for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = q4_word_to_f16x8(st.b[i][0][w], s2, b2);
+            } else if constexpr (C::F16SRC) {
+#pragma unroll
+                for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = st.b[i][w];
             } else {
 #pragma unroll
                 for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = bf16x8_to_f16x8_perm(st.b[i][w]);
@@ -288,7 +303,20 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
     }
 
     // ---- epilogues (the loop ended with a barrier: the operand tiles are free)
-    if constexpr (C::GATED) {
+    if constexpr (MODE == MODE_ROUTER) {
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+            const int ex = nblk * 128 + wn * 64 + hf * 32 + l32;
+            const float b = g.rbias ? g.rbias[ex] : 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
+                    if (r < rows) g.logits[(size_t)(m0 + r) * E + ex] = (acc[mt][2 * hf][v] + acc[mt][2 * hf + 1][v]) + b;
+                }
+        }
+    } else if constexpr (C::GATED) {
         // h tile [128 rows][128 features] fp16 in LDS, then 16-byte row pieces
         constexpr int HS = 128 + 8;
         f16* hb = &sm.b[0][0];
@@ -411,6 +439,15 @@ __global__ void __launch_bounds__(256) k_prep_x(const uint16_t* __restrict__ x, 
 }
 
 int gemm_bm() { return GEMM_BM; }
+
+hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits, int T,
+                              const Tracer& tr, hipStream_t s) {
+    GemmArgs g = {};
+    g.xh = xh; g.wr2 = wr2; g.rbias = bias; g.logits = logits; g.T = T;
+    const int mt = (T + GEMM_BM - 1) / GEMM_BM;
+    tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm<MODE_ROUTER>, dim3(8 * ((mt * (E / 128) + 7) / 8)), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
 
 hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s) {
     const int n8 = T * D / 8;

@@ -6,87 +6,36 @@
 // watch-list": renormalise the top-8 weights); sgate = sigmoid(
 // ffn_gate_inp_shexp . x).
 //
-// Large T: the logits are a [T, 2048] x [2048, 256] GEMM on bf16 MFMA.  x is
-// bf16 already; each fp32 router weight is split exactly into three bf16
-// terms hi + mid + lo (8 significant bits each), so every MFMA product is
-// exact and the logits carry fp32 accumulation error only.
+// Large T: the logits are a [T, 2048] x [2048, 256] GEMM on fp16 MFMA (the
+// grouped-GEMM kernel's router mode).  x is exact in fp16 within the fp16
+// range; each fp32 router weight is split into two fp16 planes hi + lo with
+// |w - hi - lo| <= max(2^-22 |w|, 2^-25) (hi = fp16(w), lo = fp16(w - hi),
+// w - hi exact in fp32; the absolute term is fp16's subnormal spacing), so a
+// logit over 2048 inputs of unit size is off by ~1e-6 at most: far below the
+// 1e-4 top-8/top-9 margin the index-exactness bar is stated for.
 #include "moe_common.h"
 #include "moe_kernels.h"
 #include "../../include/moe_ffn.h"
 
 namespace moe {
 
-// Wr fp32 [E, D] -> Wr3 bf16 [3, E, D] with Wr = hi + mid + lo exactly.
-__global__ void __launch_bounds__(256) k_split_router(const float* __restrict__ wr, uint16_t* __restrict__ wr3) {
-    const int i = blockIdx.x * 256 + threadIdx.x;  // one element per thread
-    if (i >= E * D) return;
-    const uint32_t u = __float_as_uint(wr[i]);
-    const uint32_t hi = u & 0xffff0000u;                       // truncate to 8 significant bits
-    const float r1 = __uint_as_float(u) - __uint_as_float(hi);  // exact, <= 16 significant bits
-    const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
-    const float r2 = r1 - __uint_as_float(mid);                 // exact, <= 8 significant bits
-    wr3[i] = (uint16_t)(hi >> 16);
-    wr3[E * D + i] = (uint16_t)(mid >> 16);
-    wr3[2 * E * D + i] = (uint16_t)(__float_as_uint(r2) >> 16);  // exact in bf16
-}
-
-// logits[T, E] = x . Wr^T (+ bias).  Block: 32 tokens x 256 experts, 4 waves;
-// wave w owns experts [64w, 64w+64) as four 16-wide tiles; two 16-token
-// tiles.  v_mfma_f32_16x16x32_bf16 operand layout: lane l holds
-// A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16]; the accumulator lane l
-// holds C[4*(l/16) + v][l%16], v = 0..3.
-__global__ void __launch_bounds__(256) k_router_logits(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr3,
-                                                       const float* __restrict__ bias, float* __restrict__ logits,
-                                                       int T) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * 32;
-    const int li = lane & 15, lk = lane >> 4;
-    f32x4 acc[2][4];
+// Wr fp32 [E, D] -> Wr2 fp16 [2, E, D] (hi, lo), K in the perm8 order.  One
+// thread per 8-element block.
+__global__ void __launch_bounds__(256) k_split_router(const float* __restrict__ wr, uint16_t* __restrict__ wr2) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= E * D / 8) return;
+    const f32x4 a = ((const f32x4*)wr)[2 * i], b = ((const f32x4*)wr)[2 * i + 1];
+    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    u32x4 hi, lo;
 #pragma unroll
-    for (int m = 0; m < 2; m++)
-#pragma unroll
-        for (int n = 0; n < 4; n++) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const uint16_t* xa[2];
-    bool va[2];
-#pragma unroll
-    for (int m = 0; m < 2; m++) {
-        int t = t0 + m * 16 + li;
-        va[m] = t < T;
-        xa[m] = x + (size_t)(va[m] ? t : 0) * D + 8 * lk;
+    for (int j = 0; j < 4; j++) {  // perm8: pair j holds elements j and j + 4
+        const f16 h0 = (f16)v[j], h1 = (f16)v[j + 4];
+        const f16 l0 = (f16)(v[j] - (float)h0), l1 = (f16)(v[j + 4] - (float)h1);
+        hi[j] = __builtin_bit_cast(uint32_t, f16x2{h0, h1});
+        lo[j] = __builtin_bit_cast(uint32_t, f16x2{l0, l1});
     }
-    const uint16_t* wb = wr3 + (size_t)(wave * 64 + li) * D + 8 * lk;
-
-    for (int k0 = 0; k0 < D; k0 += 32) {
-        bf16x8 a[2];
-#pragma unroll
-        for (int m = 0; m < 2; m++) {
-            u32x4 v = va[m] ? *(const u32x4*)(xa[m] + k0) : u32x4{0u, 0u, 0u, 0u};
-            a[m] = __builtin_bit_cast(bf16x8, v);
-        }
-#pragma unroll
-        for (int n = 0; n < 4; n++) {
-#pragma unroll
-            for (int s = 2; s >= 0; s--) {
-                u32x4 v = *(const u32x4*)(wb + (size_t)s * E * D + (size_t)n * 16 * D + k0);
-                bf16x8 b = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-                for (int m = 0; m < 2; m++) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b, acc[m][n], 0, 0, 0);
-            }
-        }
-    }
-#pragma unroll
-    for (int n = 0; n < 4; n++) {
-        const int e = wave * 64 + n * 16 + li;
-        const float b = bias ? bias[e] : 0.0f;
-#pragma unroll
-        for (int m = 0; m < 2; m++)
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-                int t = t0 + m * 16 + 4 * lk + v;
-                if (t < T) logits[(size_t)t * E + e] = acc[m][n][v] + b;
-            }
-    }
+    ((u32x4*)wr2)[i] = hi;
+    ((u32x4*)wr2)[E * D / 8 + i] = lo;
 }
 
 // One wave per token: top-8 of the 256 logits, renormalised softmax weights,
@@ -146,14 +95,8 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
     }
 }
 
-hipError_t launch_split_router(const float* wr, uint16_t* wr3, hipStream_t s) {
-    hipLaunchKernelGGL(k_split_router, dim3((E * D + 255) / 256), dim3(256), 0, s, wr, wr3);
-    return hipGetLastError();
-}
-
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr3, const float* bias, float* logits, int T,
-                                const Tracer& tr, hipStream_t s) {
-    tr.launch(MOE_FFN_KERNEL_ROUTER, k_router_logits, dim3((T + 31) / 32), dim3(256), 0, s, x, wr3, bias, logits, T);
+hipError_t launch_split_router(const float* wr, uint16_t* wr2, hipStream_t s) {
+    hipLaunchKernelGGL(k_split_router, dim3((E * D / 8 + 255) / 256), dim3(256), 0, s, wr, wr2);
     return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 // Byte offsets of every workspace region for T tokens.
 struct Layout {
-    size_t wr3, logits, idx, w, sgate, xh, cnt, offs, tiles, tile_count, perm, pos_of, h, hs, partial, total;
+    size_t wr2, logits, idx, w, sgate, xh, cnt, offs, tiles, tile_count, perm, pos_of, h, hs, partial, total;
 };
 
 Layout layout(int64_t T) {
@@ -22,7 +22,7 @@ Layout layout(int64_t T) {
     const size_t max_tiles = (N + gemm_bm() - 1) / gemm_bm() + E;
     Layout L{};
     size_t o = 0;
-    L.wr3 = o;        o += up((size_t)3 * E * D * 2);
+    L.wr2 = o;        o += up((size_t)2 * E * D * 2);
     L.logits = o;     o += up((size_t)T * E * 4);
     L.idx = o;        o += up(N * 4);
     L.w = o;          o += up(N * 4);
@@ -89,7 +89,7 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     const Layout L = layout(T);
     const int N = T * K;
     auto at = [&](size_t off) { return (void*)(ws + off); };
-    uint16_t* wr3 = (uint16_t*)at(L.wr3);
+    uint16_t* wr2 = (uint16_t*)at(L.wr2);
     float* logits = (float*)at(L.logits);
     int32_t* idx = idx_user ? idx_user : (int32_t*)at(L.idx);
     float* w = w_user ? w_user : (float*)at(L.w);
@@ -104,9 +104,9 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
 
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-    chk(launch_split_router(router->weight, wr3, s));
+    chk(launch_split_router(router->weight, wr2, s));
     chk(launch_prep_x(x, xh, T, s));
-    chk(launch_router_logits(x, wr3, router->bias, logits, T, tr, s));
+    chk(launch_router_gemm(xh, wr2, router->bias, logits, T, tr, s));
     chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, T, s));
     chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(), s));
     PrefillGemmParams p{};

@@ -24,9 +24,7 @@ struct Tracer {
 
 
 // ---- router (k_router.hip)
-hipError_t launch_split_router(const float* wr, uint16_t* wr3, hipStream_t s);
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr3, const float* bias, float* logits, int T,
-                                const Tracer& tr, hipStream_t s);
+hipError_t launch_split_router(const float* wr, uint16_t* wr2, hipStream_t s);
 hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
                        float* sgate, int T, hipStream_t s);
 
@@ -57,6 +55,8 @@ struct PrefillGemmParams {
 };
 int gemm_bm();
 hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s);
+hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits, int T,
+                              const Tracer& tr, hipStream_t s);
 hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hipStream_t s);
 
 // ---- decode path (k_decode.hip), T <= 64
