@@ -1,0 +1,93 @@
+// Decode-path kernel arguments and the per-token routing helpers shared by
+// the decode kernels (k_decode.hip: T > 4 tokens; k_decode_tiny.hip: T <= 4).
+#pragma once
+
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+constexpr int TINY_T = 4;  // up to this many tokens: no distinct-expert lists
+
+struct DecodeArgs {
+    const uint16_t* x;
+    int T;
+    const float* wr;
+    const float* rbias;
+    const uint16_t *sgi, *sg, *su, *sd;  // shared expert (sg == nullptr: none)
+    const uint32_t *gq, *uq, *dq;
+    const uint16_t *gs, *gb, *us, *ub, *ds, *db;
+    float* logits;   // [T, E]
+    uint16_t* xp;    // bf16 [T, D], perm8
+    float* xsum;     // [T, D/32] sums of x over 32-element chunks (T <= TINY_T)
+    float* hs;       // [T, FS] shared SwiGLU output
+    float* ys;       // [T, D] shared down output
+    uint16_t* h;     // fp16 [8T, F] (pair-major), perm8
+    float* part;     // [8T, D] routed down outputs per pair (T > 4)
+    int32_t* idx;
+    float* w;
+    float* sgate;
+    int32_t* nuniq;  // [1]
+    int32_t* uexp;   // [E]
+    int32_t* ucnt;   // [E]
+    int32_t* uoff;   // [E]
+    int32_t* pairs;  // [8T] (t*8 + r), grouped by distinct expert, t ascending
+    uint16_t* y;
+};
+
+// Top-8 of token t's logits (one wave, result wave-uniform).
+__device__ __forceinline__ void token_top8(const DecodeArgs& a, int t, int lane, float* sel_v, int* sel_i) {
+    float v[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) v[c] = a.logits[(size_t)t * E + lane + 64 * c];
+    wave_top8(v, lane, sel_v, sel_i);
+}
+
+// One wave: write token t's routing (expert ids, renormalised weights; the
+// softmax normaliser cancels under norm_topk_prob, so the weights are the
+// softmax of the eight selected logits) and sgate = sigmoid(gate_inp . x).
+__device__ inline void write_token_route(const DecodeArgs& a, int t, int lane, const float* sel_v, const int* sel_i,
+                                  int* sidx) {
+    float p[K], s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < K; r++) {
+        p[r] = __expf(sel_v[r] - sel_v[0]);
+        s += p[r];
+    }
+    const float inv = 1.0f / s;
+    if (lane < K) {
+        float wv = 0.f;
+        int iv = 0;
+#pragma unroll
+        for (int r = 0; r < K; r++)
+            if (r == lane) {
+                wv = p[r] * inv;
+                iv = sel_i[r];
+            }
+        a.idx[t * K + lane] = iv;
+        a.w[t * K + lane] = wv;
+        if (sidx) sidx[t * K + lane] = iv;
+    }
+    float z = 0.0f;
+    if (a.sgi) {
+        const u32x4* xq = (const u32x4*)(a.x + (size_t)t * D + 32 * lane);
+        const u32x4* gp = (const u32x4*)(a.sgi + 32 * lane);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const u32x4 xv = xq[q], gv = gp[q];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                z += __uint_as_float(xv[j] << 16) * __uint_as_float(gv[j] << 16);
+                z += __uint_as_float(xv[j] & 0xffff0000u) * __uint_as_float(gv[j] & 0xffff0000u);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    }
+    if (lane == 0) a.sgate[t] = a.sgi ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
+}
+
+
+hipError_t launch_decode_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s);
+
+}  // namespace moe

@@ -46,8 +46,7 @@
 // Indices read back from the workspace are clamped to their ranges before
 // they address memory.
 #include "../../include/moe_ffn.h"
-#include "moe_common.h"
-#include "moe_kernels.h"
+#include "decode_common.h"
 
 namespace moe {
 
@@ -116,33 +115,9 @@ __device__ __forceinline__ void split2(const float* v, u32x4& hi, u32x4& lo) {
     }
 }
 
-struct DecodeArgs {
-    const uint16_t* x;
-    int T;
-    const float* wr;
-    const float* rbias;
-    const uint16_t *sgi, *sg, *su, *sd;  // shared expert (sg == nullptr: none)
-    const uint32_t *gq, *uq, *dq;
-    const uint16_t *gs, *gb, *us, *ub, *ds, *db;
-    float* logits;   // [T, E]
-    uint16_t* xp;    // bf16 [T, D], perm8
-    float* hs;       // [T, FS] shared SwiGLU output
-    float* ys;       // [T, D] shared down output
-    uint16_t* h;     // fp16 [8T, F] (pair-major), perm8
-    float* part;     // [8T, D] routed down outputs per pair (T > 4)
-    int32_t* idx;
-    float* w;
-    float* sgate;
-    int32_t* nuniq;  // [1]
-    int32_t* uexp;   // [E]
-    int32_t* ucnt;   // [E]
-    int32_t* uoff;   // [E]
-    int32_t* pairs;  // [8T] (t*8 + r), grouped by distinct expert, t ascending
-    uint16_t* y;
-};
 
 
-constexpr int TINY_T = 4;  // up to this many tokens: no distinct-expert lists
+
 
 // ------------------------------------------------------------------ stage A
 // Router blocks: 16 experts; shared blocks: 16 gate + 16 up rows.  Wave w
@@ -192,6 +167,7 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a) {
 #pragma unroll
             for (int m = 0; m < NMT; m++) xv[ks][m] = *(const u32x4*)(xrow[m] + 32 * ks);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) {
             float v[8];
@@ -221,6 +197,7 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a) {
 #pragma unroll
             for (int m = 0; m < NMT; m++) xv[ks][m] = *(const u32x4*)(xrow[m] + 32 * ks);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
 #pragma unroll
@@ -255,58 +232,6 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ routing
-// Top-8 of token t's logits (one wave, result wave-uniform).
-__device__ __forceinline__ void token_top8(const DecodeArgs& a, int t, int lane, float* sel_v, int* sel_i) {
-    float v[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) v[c] = a.logits[(size_t)t * E + lane + 64 * c];
-    wave_top8(v, lane, sel_v, sel_i);
-}
-
-// One wave: write token t's routing (expert ids, renormalised weights; the
-// softmax normaliser cancels under norm_topk_prob, so the weights are the
-// softmax of the eight selected logits) and sgate = sigmoid(gate_inp . x).
-__device__ void write_token_route(const DecodeArgs& a, int t, int lane, const float* sel_v, const int* sel_i,
-                                  int* sidx) {
-    float p[K], s = 0.0f;
-#pragma unroll
-    for (int r = 0; r < K; r++) {
-        p[r] = __expf(sel_v[r] - sel_v[0]);
-        s += p[r];
-    }
-    const float inv = 1.0f / s;
-    if (lane < K) {
-        float wv = 0.f;
-        int iv = 0;
-#pragma unroll
-        for (int r = 0; r < K; r++)
-            if (r == lane) {
-                wv = p[r] * inv;
-                iv = sel_i[r];
-            }
-        a.idx[t * K + lane] = iv;
-        a.w[t * K + lane] = wv;
-        if (sidx) sidx[t * K + lane] = iv;
-    }
-    float z = 0.0f;
-    if (a.sgi) {
-        const u32x4* xq = (const u32x4*)(a.x + (size_t)t * D + 32 * lane);
-        const u32x4* gp = (const u32x4*)(a.sgi + 32 * lane);
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const u32x4 xv = xq[q], gv = gp[q];
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                z += __uint_as_float(xv[j] << 16) * __uint_as_float(gv[j] << 16);
-                z += __uint_as_float(xv[j] & 0xffff0000u) * __uint_as_float(gv[j] & 0xffff0000u);
-            }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-    }
-    if (lane == 0) a.sgate[t] = a.sgi ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
-}
-
 // T > TINY_T: one block routes every token and lists the distinct experts in
 // increasing id order, each with its (token, rank) pairs in token order.  An
 // assignment's place among equal experts comes from ballots over the 8 bits
@@ -404,6 +329,7 @@ __device__ __forceinline__ void gu_tile(const DecodeArgs& a, size_t row, int gq8
         xa[g][0] = *(const u32x4*)(xrow + 8 * wd);
         xa[g][1] = *(const u32x4*)(xrow + 8 * wd + 8);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
     f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -508,20 +434,6 @@ __global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_gu_bloc
     const int chunk = blockIdx.x % (F / 32);
     const int f0 = 32 * chunk;
     const size_t frow = f0 + 16 * fg + n;
-    if (T <= TINY_T) {
-        // one (token, rank) pair per block; every wave routes the token itself
-        const int p = blockIdx.x / (F / 32), t = p >> 3, r = p & 7;
-        float sel_v[K];
-        int sel_i[K];
-        token_top8(a, t, lane, sel_v, sel_i);
-        const int e = sel_i[r] & (E - 1);
-        if (r == 0 && chunk == 0 && wave == 0) write_token_route(a, t, lane, sel_v, sel_i, nullptr);
-        auto pair_of = [p](int) { return p; };
-        gu_tile(a, (size_t)e * F + frow, 8 * kq4, 1, pair_of, lane, red[0][kq4][fg], red[1][kq4][fg]);
-        __syncthreads();
-        gu_finish(a, red, f0, 1, pair_of);
-        return;
-    }
     const int u = blockIdx.x / (F / 32);
     if (u >= min(a.nuniq[0], E)) return;
     const int e = a.uexp[u] & (E - 1), cnt = min(max(a.ucnt[u], 1), T);
@@ -560,6 +472,7 @@ __device__ __forceinline__ void down_load(const DecodeArgs& a, size_t row, int p
         L.ha[g][0] = *(const u32x4*)(hrow + 8 * wd);
         L.ha[g][1] = *(const u32x4*)(hrow + 8 * wd + 8);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
 }
 
 // Down projection of the loaded tile: row n of the lane, token slots 4kq+v.
@@ -587,33 +500,12 @@ __device__ __forceinline__ f32x4 down_compute(const DownLoads& L) {
 // combine.  T > 4: block (row tile, chunk) takes distinct experts 8*chunk..+7,
 // one per wave, and writes fp32 partials per pair; k_dec_combine finishes.
 __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
-    __shared__ float P[TINY_T * K][17];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
-    const bool tiny = T <= TINY_T;
     const int rt = blockIdx.x % N_ROW_TILES, ch = blockIdx.x / N_ROW_TILES;
     const int o0 = 16 * rt;
     const int tk = T * K - 1;
-    if (tiny) {
-        for (int p = wave; p < T * K; p += 8) {
-            const int e = a.idx[p] & (E - 1);
-            DownLoads L;
-            down_load(a, (size_t)e * D + o0 + n, p, lane, L);
-            const f32x4 o = down_compute(L);
-            if (kq == 0) P[p][n] = o[0];  // token slot 0 is the pair
-        }
-        __syncthreads();
-        if (tid < T * 16) {
-            const int t = tid >> 4, c = tid & 15;
-            float sum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < K; r++) sum += a.w[t * K + r] * P[t * K + r][c];
-            if (a.sg) sum += a.sgate[t] * a.ys[(size_t)t * D + o0 + c];
-            a.y[(size_t)t * D + o0 + c] = f32_to_bf16_rne(sum);
-        }
-        return;
-    }
     const int nu = min(max(a.nuniq[0], 0), min(T * K, E));
     const int u = 8 * ch + wave;
     if (u >= nu) return;
@@ -665,6 +557,7 @@ size_t decode_workspace_bytes(int T, DecodeLayout* L) {
     l.ucnt = o;   o += up(E * 4);
     l.uoff = o;   o += up(E * 4);
     l.pairs = o;  o += up((size_t)T * K * 4);
+    l.xsum = o;   o += up(T <= TINY_T ? (size_t)T * (D / 32) * 4 : 0);
     l.total = o;
     if (L) *L = l;
     return o;
@@ -672,17 +565,14 @@ size_t decode_workspace_bytes(int T, DecodeLayout* L) {
 
 template <int NMT>
 static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
-    const bool tiny = a.T <= TINY_T;
-    const int n_items = tiny ? a.T * K : (a.T * K < E ? a.T * K : E);
+    const int n_items = a.T * K < E ? a.T * K : E;
     const int n_gu = n_items * (F / 32);
     tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<NMT>, dim3(N_ROUTER_BLK + N_SGU_BLK + 1), dim3(1024), 0, s, a);
-    if (!tiny) hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_gu + (a.sg ? N_SDOWN_BLK : 0)), dim3(512), 0, s, a,
               n_gu);
-    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(N_ROW_TILES * (tiny ? 1 : (n_items + 7) / 8)),
-              dim3(512), 0, s, a);
-    if (!tiny)
-        tr.launch(MOE_FFN_KERNEL_COMBINE, k_dec_combine, dim3((a.T * D + 255) / 256), dim3(256), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(N_ROW_TILES * ((n_items + 7) / 8)), dim3(512), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_COMBINE, k_dec_combine, dim3((a.T * D + 255) / 256), dim3(256), 0, s, a);
 }
 
 hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipStream_t s) {
@@ -708,7 +598,9 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     a.ucnt = (int32_t*)(ws + L.ucnt);
     a.uoff = (int32_t*)(ws + L.uoff);
     a.pairs = (int32_t*)(ws + L.pairs);
+    a.xsum = (float*)(ws + L.xsum);
     a.y = p.y;
+    if (p.T <= TINY_T) return launch_decode_tiny(a, tr, s);
     const int nmt = (p.T + 15) / 16;
     switch (nmt) {
         case 1: launch_decode_t<1>(a, tr, s); break;

@@ -1,0 +1,360 @@
+// Decode path for T <= 4 tokens: weight streaming on the vector ALUs.
+//
+// Lily engine page, "Dekodavimas: sumazinti perkeliamu baitu kieki vienam
+// tokenui": batch-1 decode is a GEMV bound by the bytes moved per token, and
+// a group of lanes cooperates on one output while reading different parts of
+// its weight row.  With at most four tokens a matrix-core tile would be 3/4
+// or more padding, so here every weight row is read by one wave: lane l takes
+// the l-th 16-byte piece of the row (64 lanes = 1 KB, whole cache lines per
+// load instruction), forms dot products with v_dot2 on pairs, and the wave
+// sums the 64 partials in a fixed butterfly order.  Each launch is spread
+// over at least 256 blocks and each wave issues all of its loads before it
+// consumes any, so a launch costs one memory round trip.
+//
+// Weights stay exact: 4-bit codes become 128 + q (bf16, gate/up against bf16
+// x) or 1024 + q (fp16, down against fp16 h), and each 32-element piece is
+// finished in fp32 as  s * dot(code, x) + (b - c*s) * sum(x over the piece)
+// (c = 128 or 1024).  The piece sums of x come from the first launch, those
+// of h from the down launch's own staging.
+//
+// Launches:
+//   A  router logits (fp32 weights, 2 experts per block, K halves over wave
+//      pairs) and shared gate/up + SwiGLU (2 features per block, one row per
+//      wave); one block copies x into the codes' K order and sums its pieces.
+//   C  routed gate/up + SwiGLU: block = one (token, rank) pair x 8 features;
+//      every wave derives the pair's expert from the token's logits (DPP
+//      top-8) so no routing launch is needed; shared down (8 rows / block).
+//   D  routed down: block = 8 output rows x every pair; h staged in LDS;
+//      then the combine  y = sum_{r=0..7} w_r * down_r + sgate * shexp  in
+//      fixed order with one bf16 rounding.
+#include "../../include/moe_ffn.h"
+#include "decode_common.h"
+
+namespace moe {
+
+constexpr int TA_ROUTER_BLK = E / 2;  // 2 experts per block
+constexpr int TA_SHARED_BLK = FS / 2; // 2 features (4 rows) per block
+constexpr int TC_FEAT = 8;            // features per routed gate/up block
+constexpr int TC_SDOWN_BLK = D / 8;   // shared-down blocks, 8 rows each
+constexpr int TD_ROWS = 8;            // output rows per down block
+constexpr int XPIECES = D / 32;       // 32-element pieces of an x row
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 16-bit pairs from a u32 passed by value.  (Bit-casting a vector-element
+// expression directly is miscompiled by clang 22: it reads element 0.)
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
+// Sum over the 64 lanes of a wave; butterfly, so every lane ends with the
+// same, order-fixed value.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// Sum over the 16 lanes of a lane row (lanes 16j .. 16j+15).
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Dot product of one u32 of eight 4-bit codes, as (magic + q) pairs in the
+// perm8 order, with four 16-bit activation pairs (one u32x4, perm8).
+__device__ __forceinline__ float dot_codes_bf16(uint32_t w, const u32x4& x, float acc) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint32_t c = ((w >> (4 * j)) & 0x000f000fu) | 0x43004300u;  // bf16 128 + q
+        const uint32_t xj = x[j];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(c), as_bf16x2(xj), acc, false);
+    }
+    return acc;
+}
+__device__ __forceinline__ float dot_codes_f16(uint32_t w, const u32x4& h, float acc) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint32_t c = ((w >> (4 * j)) & 0x000f000fu) | 0x64006400u;  // fp16 1024 + q
+        const uint32_t hj = h[j];
+        acc = __builtin_amdgcn_fdot2(as_f16x2(c), as_f16x2(hj), acc, false);
+    }
+    return acc;
+}
+
+// bf16 scale or bias of quantisation group g from a row's [groups] array:
+// one u32 load covers groups g & ~1 and g | 1.
+__device__ __forceinline__ float group_param(uint32_t pairw, int g) {
+    return (g & 1) ? hi_bf16(pairw) : lo_bf16(pairw);
+}
+
+// ------------------------------------------------------------------ A
+__global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
+    __shared__ float red[4][2 * TINY_T];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = a.T;
+    const int b = blockIdx.x;
+    if (b == TA_ROUTER_BLK + TA_SHARED_BLK) {
+        // x -> perm8 copy (pairs j, j+4 of every 8-block) and piece sums
+        for (int i = tid; i < T * (D / 8); i += 256) {
+            const u32x4 d = ((const u32x4*)a.x)[i];
+            u32x4 o;
+            o[0] = (d[0] & 0xffffu) | (d[2] << 16);
+            o[1] = (d[0] >> 16) | (d[2] & 0xffff0000u);
+            o[2] = (d[1] & 0xffffu) | (d[3] << 16);
+            o[3] = (d[1] >> 16) | (d[3] & 0xffff0000u);
+            ((u32x4*)a.xp)[i] = o;
+        }
+        for (int i = tid; i < T * XPIECES; i += 256) {
+            const u32x4* src = (const u32x4*)(a.x + (size_t)i * 32);
+            float s = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const u32x4 v = src[q];
+#pragma unroll
+                for (int j = 0; j < 4; j++) s += lo_bf16(v[j]) + hi_bf16(v[j]);
+            }
+            a.xsum[i] = s;
+        }
+        return;
+    }
+    if (b < TA_ROUTER_BLK) {
+        // experts 2b + (wave >> 1); the wave pair splits the row's 512 pieces
+        // of 4 fp32 weights (K = 4c) into alternating 64-piece runs
+        const int e = 2 * b + (wave >> 1), kh = wave & 1;
+        const float* wrow = a.wr + (size_t)e * D;
+        f32x4 wv[4];
+        u32x2 xv[TINY_T][4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int c = lane + 64 * (2 * i + kh);
+            wv[i] = *(const f32x4*)(wrow + 4 * c);
+#pragma unroll
+            for (int t = 0; t < TINY_T; t++) xv[t][i] = *(const u32x2*)(a.x + (size_t)min(t, T - 1) * D + 4 * c);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
+        float acc[TINY_T];
+#pragma unroll
+        for (int t = 0; t < TINY_T; t++) {
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                s += wv[i][0] * lo_bf16(xv[t][i][0]);
+                s += wv[i][1] * hi_bf16(xv[t][i][0]);
+                s += wv[i][2] * lo_bf16(xv[t][i][1]);
+                s += wv[i][3] * hi_bf16(xv[t][i][1]);
+            }
+            acc[t] = wave_sum(s);
+        }
+        if (lane == 0)
+#pragma unroll
+            for (int t = 0; t < TINY_T; t++) red[wave][t] = acc[t];
+        __syncthreads();
+        if (tid < 2 * T) {
+            const int r = tid / T, t = tid % T;
+            const float s = red[2 * r][t] + red[2 * r + 1][t];
+            a.logits[(size_t)t * E + 2 * b + r] = s + (a.rbias ? a.rbias[2 * b + r] : 0.0f);
+        }
+        return;
+    }
+    // shared gate/up: features f0, f0 + 1; wave w: row (gate f0, gate f0+1,
+    // up f0, up f0+1)[w]; lane piece c = lane + 64 i holds 8 bf16 at K = 8c
+    if (!a.sg) return;
+    const int f0 = 2 * (b - TA_ROUTER_BLK);
+    const uint16_t* wrow = (wave < 2 ? a.sg : a.su) + (size_t)(f0 + (wave & 1)) * D;
+    u32x4 wv[4], xv[TINY_T][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int c = lane + 64 * i;
+        wv[i] = *(const u32x4*)(wrow + 8 * c);
+#pragma unroll
+        for (int t = 0; t < TINY_T; t++) xv[t][i] = *(const u32x4*)(a.x + (size_t)min(t, T - 1) * D + 8 * c);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
+#pragma unroll
+    for (int t = 0; t < TINY_T; t++) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                {
+                    const uint32_t wj = wv[i][j], xj = xv[t][i][j];
+                    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wj), as_bf16x2(xj), s, false);
+                }
+        s = wave_sum(s);
+        if (lane == 0) red[wave][t] = s;
+    }
+    __syncthreads();
+    if (tid < 2 * T) {
+        const int i = tid / T, t = tid % T;
+        a.hs[(size_t)t * FS + f0 + i] = silu_f32(red[i][t]) * red[2 + i][t];
+    }
+}
+
+// ------------------------------------------------------------------ C
+__global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = a.T;
+    if ((int)blockIdx.x >= n_gu_blocks) {
+        // shared down: rows o0 + 2w, o0 + 2w + 1; lane piece = 8 bf16 at K = 8 lane
+        if (!a.sd) return;
+        const int o = TD_ROWS * (blockIdx.x - n_gu_blocks) + 2 * wave;
+        u32x4 wv[2];
+        f32x4 hv[TINY_T][2];
+#pragma unroll
+        for (int r = 0; r < 2; r++) wv[r] = *(const u32x4*)(a.sd + (size_t)(o + r) * FS + 8 * lane);
+#pragma unroll
+        for (int t = 0; t < TINY_T; t++) {
+            const float* hrow = a.hs + (size_t)min(t, T - 1) * FS + 8 * lane;
+            hv[t][0] = *(const f32x4*)hrow;
+            hv[t][1] = *(const f32x4*)(hrow + 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
+#pragma unroll
+        for (int r = 0; r < 2; r++)
+#pragma unroll
+            for (int t = 0; t < TINY_T; t++) {
+                float s = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    s += lo_bf16(wv[r][j]) * hv[t][j >> 1][2 * (j & 1)];
+                    s += hi_bf16(wv[r][j]) * hv[t][j >> 1][2 * (j & 1) + 1];
+                }
+                s = wave_sum(s);
+                if (lane == 0 && t < T) a.ys[(size_t)t * D + o + r] = s;
+            }
+        return;
+    }
+    // routed gate/up: pair p = (token t, rank r), features f0 .. f0 + 7
+    const int p = blockIdx.x / (F / TC_FEAT), fc = blockIdx.x % (F / TC_FEAT);
+    const int t = p >> 3, r = p & 7;
+    const int f0 = TC_FEAT * fc;
+    float sel_v[K];
+    int sel_i[K];
+    token_top8(a, t, lane, sel_v, sel_i);
+    if (r == 0 && fc == 0 && wave == 0) write_token_route(a, t, lane, sel_v, sel_i, nullptr);
+    const int e = sel_i[r] & (E - 1);
+    // wave w: features f0 + 2w, f0 + 2w + 1; rows gate f, gate f+1, up f, up f+1
+    const size_t row0 = (size_t)e * F + f0 + 2 * wave;
+    const uint32_t* rows[4] = {a.gq + row0 * (D / 8), a.gq + (row0 + 1) * (D / 8), a.uq + row0 * (D / 8),
+                               a.uq + (row0 + 1) * (D / 8)};
+    const uint16_t* srow[4] = {a.gs + row0 * (D / G), a.gs + (row0 + 1) * (D / G), a.us + row0 * (D / G),
+                               a.us + (row0 + 1) * (D / G)};
+    const uint16_t* brow[4] = {a.gb + row0 * (D / G), a.gb + (row0 + 1) * (D / G), a.ub + row0 * (D / G),
+                               a.ub + (row0 + 1) * (D / G)};
+    // lane piece: 32 codes at K = 32 lane (4 u32), group lane / 2
+    u32x4 cv[4];
+    uint32_t sv[4], bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        cv[q] = *(const u32x4*)(rows[q] + 4 * lane);
+        sv[q] = *(const uint32_t*)(srow[q] + 2 * (lane >> 2));
+        bv[q] = *(const uint32_t*)(brow[q] + 2 * (lane >> 2));
+    }
+    u32x4 xv[4];
+    const uint16_t* xrow = a.xp + (size_t)t * D + 32 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; i++) xv[i] = *(const u32x4*)(xrow + 8 * i);
+    const float xs = a.xsum[t * XPIECES + lane];
+    __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
+    float out[4];
+    const int g = lane >> 1;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc = dot_codes_bf16(cv[q][i], xv[i], acc);
+        const float s = group_param(sv[q], g), bb = group_param(bv[q], g);
+        out[q] = wave_sum(s * acc + (bb - 128.0f * s) * xs);
+    }
+    if (lane < 2) {
+        const int f = f0 + 2 * wave + lane;
+        const float hv = silu_f32(lane ? out[1] : out[0]) * (lane ? out[3] : out[2]);
+        const int pc = (f & ~7) | perm8_pos(f & 7);
+        a.h[(size_t)p * F + pc] = __builtin_bit_cast(uint16_t, (f16)hv);
+    }
+}
+
+// ------------------------------------------------------------------ D
+__global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t hl[TINY_T * K][F];   // h of every pair, fp16 perm8
+    __shared__ float hsum[TINY_T * K][F / 32];                            // piece sums of h
+    __shared__ float dv[TINY_T * K][TD_ROWS];                             // down outputs
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = a.T, NP = T * K;
+    const int o0 = TD_ROWS * blockIdx.x;
+    // units u = (pair u >> 3, row u & 7); lanes 16j .. 16j+15 share a unit,
+    // lane piece c = lane & 15 holds 32 codes at K = 32c.  Wave w takes the
+    // units 16T*w .. 16T*w + 16T - 1, four per load instruction (1 KB).
+    const int c = lane & 15, sub = lane >> 4;
+    constexpr int MAXJ = TINY_T * 4;
+    u32x4 cv[MAXJ];
+    uint32_t sv[MAXJ], bv[MAXJ];
+    const int nj = 4 * T;
+#pragma unroll
+    for (int j = 0; j < MAXJ; j++) {
+        if (j < nj) {
+            const int u = (wave * nj + j) * 4 + sub;
+            const int pp = u >> 3, i = u & 7;
+            const size_t row = (size_t)(a.idx[pp] & (E - 1)) * D + o0 + i;
+            cv[j] = *(const u32x4*)(a.dq + row * (F / 8) + 4 * c);
+            sv[j] = *(const uint32_t*)(a.ds + row * (F / G) + 2 * (c >> 2));
+            bv[j] = *(const uint32_t*)(a.db + row * (F / G) + 2 * (c >> 2));
+        }
+    }
+    // stage h (8T rows x 1 KB) and its piece sums: thread takes 16 bytes
+    for (int q = tid; q < NP * (F / 8); q += 256) {
+        const int pp = q / (F / 8), k8 = q % (F / 8);
+        const u32x4 v = *(const u32x4*)(a.h + (size_t)pp * F + 8 * k8);
+        *(u32x4*)&hl[pp][8 * k8] = v;
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t vj = v[j];
+            const f16x2 h2 = as_f16x2(vj);
+            s += (float)h2[0] + (float)h2[1];
+        }
+        // four consecutive threads hold one 32-element piece (F/8 is a multiple of 4)
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if ((k8 & 3) == 0) hsum[pp][k8 >> 2] = s;
+    }
+    __syncthreads();
+    const int g = c >> 1;
+#pragma unroll
+    for (int j = 0; j < MAXJ; j++) {
+        if (j < nj) {
+            const int u = (wave * nj + j) * 4 + sub;
+            const int pp = u >> 3, i = u & 7;
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; w++) acc = dot_codes_f16(cv[j][w], *(const u32x4*)&hl[pp][32 * c + 8 * w], acc);
+            const float s = group_param(sv[j], g), bb = group_param(bv[j], g);
+            const float v = row16_sum(s * acc + (bb - 1024.0f * s) * hsum[pp][c]);
+            if (c == 0) dv[pp][i] = v;
+        }
+    }
+    __syncthreads();
+    if (tid < T * TD_ROWS) {
+        const int t = tid / TD_ROWS, i = tid % TD_ROWS;
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < K; r++) sum += a.w[t * K + r] * dv[t * K + r][i];
+        if (a.sg) sum += a.sgate[t] * a.ys[(size_t)t * D + o0 + i];
+        a.y[(size_t)t * D + o0 + i] = f32_to_bf16_rne(sum);
+    }
+}
+
+hipError_t launch_decode_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
+    const int n_gu = a.T * K * (F / TC_FEAT);
+    tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a, dim3(TA_ROUTER_BLK + TA_SHARED_BLK + 1), dim3(256), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_tiny_c, dim3(n_gu + (a.sd ? TC_SDOWN_BLK : 0)), dim3(256), 0, s, a, n_gu);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_tiny_d, dim3(D / TD_ROWS), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

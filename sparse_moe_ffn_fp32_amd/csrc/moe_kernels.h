@@ -61,7 +61,7 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
 
 // ---- decode path (k_decode.hip), T <= 64
 struct DecodeLayout {
-    size_t logits, xp, hs, ys, h, part, idx, w, sgate, nuniq, uexp, ucnt, uoff, pairs, total;
+    size_t logits, xp, hs, ys, h, part, idx, w, sgate, nuniq, uexp, ucnt, uoff, pairs, xsum, total;
 };
 struct DecodeParams {
     const uint16_t* x;
