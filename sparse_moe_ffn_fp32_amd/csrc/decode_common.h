@@ -43,11 +43,11 @@ __device__ __forceinline__ void token_top8(const DecodeArgs& a, int t, int lane,
     wave_top8(v, lane, sel_v, sel_i);
 }
 
-// One wave: write token t's routing (expert ids, renormalised weights; the
-// softmax normaliser cancels under norm_topk_prob, so the weights are the
-// softmax of the eight selected logits) and sgate = sigmoid(gate_inp . x).
+// One wave: write token t's routing, the expert ids and renormalised weights
+// (the softmax normaliser cancels under norm_topk_prob, so the weights are
+// the softmax of the eight selected logits).
 __device__ inline void write_token_route(const DecodeArgs& a, int t, int lane, const float* sel_v, const int* sel_i,
-                                  int* sidx) {
+                                         int* sidx) {
     float p[K], s = 0.0f;
 #pragma unroll
     for (int r = 0; r < K; r++) {
@@ -68,21 +68,30 @@ __device__ inline void write_token_route(const DecodeArgs& a, int t, int lane, c
         a.w[t * K + lane] = wv;
         if (sidx) sidx[t * K + lane] = iv;
     }
+}
+
+// One wave: the shared-expert gate of token t, sgate = sigmoid(gate_inp . x)
+// (1 when the layer has no gate vector).
+__device__ inline void write_token_sgate(const DecodeArgs& a, int t, int lane) {
     float z = 0.0f;
     if (a.sgi) {
         const u32x4* xq = (const u32x4*)(a.x + (size_t)t * D + 32 * lane);
         const u32x4* gp = (const u32x4*)(a.sgi + 32 * lane);
+        u32x4 xv[4], gv[4];
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            const u32x4 xv = xq[q], gv = gp[q];
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                z += __uint_as_float(xv[j] << 16) * __uint_as_float(gv[j] << 16);
-                z += __uint_as_float(xv[j] & 0xffff0000u) * __uint_as_float(gv[j] & 0xffff0000u);
-            }
+            xv[q] = xq[q];
+            gv[q] = gp[q];
         }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint32_t xw = xv[q][j], gw = gv[q][j];
+                z += __uint_as_float(xw << 16) * __uint_as_float(gw << 16);
+                z += __uint_as_float(xw & 0xffff0000u) * __uint_as_float(gw & 0xffff0000u);
+            }
+        z = wave_sum(z);
     }
     if (lane == 0) a.sgate[t] = a.sgi ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
 }

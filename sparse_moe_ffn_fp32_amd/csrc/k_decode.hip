@@ -247,6 +247,7 @@ __global__ void __launch_bounds__(1024) k_dec_route(DecodeArgs a) {
         int sel_i[K];
         token_top8(a, t, lane, sel_v, sel_i);
         write_token_route(a, t, lane, sel_v, sel_i, sidx);
+        write_token_sgate(a, t, lane);
     }
     for (int i = tid; i < 8 * E; i += 1024) (&wcnt[0][0])[i] = 0;
     __syncthreads();

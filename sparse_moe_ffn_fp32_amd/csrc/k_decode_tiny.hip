@@ -7,7 +7,7 @@
 // or more padding, so here every weight row is read by one wave: lane l takes
 // the l-th 16-byte piece of the row (64 lanes = 1 KB, whole cache lines per
 // load instruction), forms dot products with v_dot2 on pairs, and the wave
-// sums the 64 partials in a fixed butterfly order.  Each launch is spread
+// sums the 64 partials in a fixed order (DPP and lane swaps).  Each launch is spread
 // over at least 256 blocks and each wave issues all of its loads before it
 // consumes any, so a launch costs one memory round trip.
 //
@@ -22,8 +22,10 @@
 //      pairs) and shared gate/up + SwiGLU (2 features per block, one row per
 //      wave); one block copies x into the codes' K order and sums its pieces.
 //   C  routed gate/up + SwiGLU: block = one (token, rank) pair x 8 features;
-//      every wave derives the pair's expert from the token's logits (DPP
-//      top-8) so no routing launch is needed; shared down (8 rows / block).
+//      the block's first wave derives the pair's expert from the token's
+//      logits (DPP top-8) so no routing launch is needed; each block also
+//      pulls the down rows stage D will read into cache; shared down (8 rows
+//      per block).
 //   D  routed down: block = 8 output rows x every pair; h staged in LDS;
 //      then the combine  y = sum_{r=0..7} w_r * down_r + sgate * shexp  in
 //      fixed order with one bf16 rounding.
@@ -45,21 +47,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // expression directly is miscompiled by clang 22: it reads element 0.)
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
-
-// Sum over the 64 lanes of a wave; butterfly, so every lane ends with the
-// same, order-fixed value.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
-
-// Sum over the 16 lanes of a lane row (lanes 16j .. 16j+15).
-__device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -119,6 +106,7 @@ __global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
             }
             a.xsum[i] = s;
         }
+        if (wave < T) write_token_sgate(a, wave, lane);  // one wave per token
         return;
     }
     if (b < TA_ROUTER_BLK) {
@@ -233,11 +221,26 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
     const int p = blockIdx.x / (F / TC_FEAT), fc = blockIdx.x % (F / TC_FEAT);
     const int t = p >> 3, r = p & 7;
     const int f0 = TC_FEAT * fc;
-    float sel_v[K];
-    int sel_i[K];
-    token_top8(a, t, lane, sel_v, sel_i);
-    if (r == 0 && fc == 0 && wave == 0) write_token_route(a, t, lane, sel_v, sel_i, nullptr);
-    const int e = sel_i[r] & (E - 1);
+    // x in the codes' K order and its piece sums do not depend on the routing
+    u32x4 xv[4];
+    const uint16_t* xrow = a.xp + (size_t)t * D + 32 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; i++) xv[i] = *(const u32x4*)(xrow + 8 * i);
+    const float xs = a.xsum[t * XPIECES + lane];
+    // wave 0 ranks the token's experts once for the block
+    __shared__ int s_expert;
+    if (wave == 0) {
+        float sel_v[K];
+        int sel_i[K];
+        token_top8(a, t, lane, sel_v, sel_i);
+        if (r == 0 && fc == 0) write_token_route(a, t, lane, sel_v, sel_i, nullptr);  // sgate: stage A
+        int er = sel_i[0];
+#pragma unroll
+        for (int k = 1; k < K; k++) er = (k == r) ? sel_i[k] : er;
+        if (lane == 0) s_expert = er;
+    }
+    __syncthreads();
+    const int e = s_expert & (E - 1);
     // wave w: features f0 + 2w, f0 + 2w + 1; rows gate f, gate f+1, up f, up f+1
     const size_t row0 = (size_t)e * F + f0 + 2 * wave;
     const uint32_t* rows[4] = {a.gq + row0 * (D / 8), a.gq + (row0 + 1) * (D / 8), a.uq + row0 * (D / 8),
@@ -255,11 +258,17 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
         sv[q] = *(const uint32_t*)(srow[q] + 2 * (lane >> 2));
         bv[q] = *(const uint32_t*)(brow[q] + 2 * (lane >> 2));
     }
-    u32x4 xv[4];
-    const uint16_t* xrow = a.xp + (size_t)t * D + 32 * lane;
-#pragma unroll
-    for (int i = 0; i < 4; i++) xv[i] = *(const u32x4*)(xrow + 8 * i);
-    const float xs = a.xsum[t * XPIECES + lane];
+    // Down rows 32 fc .. 32 fc + 31 of this pair's expert, which stage D reads
+    // next: one dword per 64 bytes (8 KB of codes, 512 B each of scales and
+    // biases) pulls them into cache in this same round trip.  Stage D's
+    // blocks take these rows on this block's XCD (block id mod 8 = fc mod 8).
+    uint32_t pf = 0;
+    {
+        const size_t drow0 = (size_t)e * D + 32 * fc;
+        if (tid < 128) pf = a.dq[drow0 * (F / 8) + 16 * tid];
+        else if (tid < 136) pf = *(const uint32_t*)(a.ds + drow0 * (F / G) + 32 * (tid - 128));
+        else if (tid < 144) pf = *(const uint32_t*)(a.db + drow0 * (F / G) + 32 * (tid - 136));
+    }
     __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
     float out[4];
     const int g = lane >> 1;
@@ -277,6 +286,7 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
         const int pc = (f & ~7) | perm8_pos(f & 7);
         a.h[(size_t)p * F + pc] = __builtin_bit_cast(uint16_t, (f16)hv);
     }
+    asm volatile("" ::"v"(pf));  // the prefetch completes before the wave ends
 }
 
 // ------------------------------------------------------------------ D
@@ -286,7 +296,22 @@ __global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
     __shared__ float dv[TINY_T * K][TD_ROWS];                             // down outputs
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = a.T, NP = T * K;
-    const int o0 = TD_ROWS * blockIdx.x;
+    // Row tile: block id b runs on XCD b % 8; stage C's block for feature
+    // chunk fc (rows 32 fc .. +31, row tiles 4 fc .. 4 fc + 3) ran on XCD
+    // fc % 8, so b takes a row tile of a chunk with fc % 8 = b % 8.
+    const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
+    const int o0 = TD_ROWS * (32 * (jb >> 2) + 4 * xcd + (jb & 3));
+    // the combine's operands, loaded with the first round trip
+    float wr[K], sgv = 0.0f, ysv = 0.0f;
+    if (tid < T * TD_ROWS) {
+        const int t = tid / TD_ROWS, i = tid % TD_ROWS;
+#pragma unroll
+        for (int r = 0; r < K; r++) wr[r] = a.w[t * K + r];
+        if (a.sg) {
+            sgv = a.sgate[t];
+            ysv = a.ys[(size_t)t * D + o0 + i];
+        }
+    }
     // units u = (pair u >> 3, row u & 7); lanes 16j .. 16j+15 share a unit,
     // lane piece c = lane & 15 holds 32 codes at K = 32c.  Wave w takes the
     // units 16T*w .. 16T*w + 16T - 1, four per load instruction (1 KB).
@@ -318,9 +343,8 @@ __global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
             const f16x2 h2 = as_f16x2(vj);
             s += (float)h2[0] + (float)h2[1];
         }
-        // four consecutive threads hold one 32-element piece (F/8 is a multiple of 4)
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
+        // four consecutive threads (one lane quad) hold one 32-element piece
+        s = quad_sum(s);
         if ((k8 & 3) == 0) hsum[pp][k8 >> 2] = s;
     }
     __syncthreads();
@@ -343,8 +367,8 @@ __global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
         const int t = tid / TD_ROWS, i = tid % TD_ROWS;
         float sum = 0.0f;
 #pragma unroll
-        for (int r = 0; r < K; r++) sum += a.w[t * K + r] * dv[t * K + r][i];
-        if (a.sg) sum += a.sgate[t] * a.ys[(size_t)t * D + o0 + i];
+        for (int r = 0; r < K; r++) sum += wr[r] * dv[t * K + r][i];
+        if (a.sg) sum += sgv * ysv;
         a.y[(size_t)t * D + o0 + i] = f32_to_bf16_rne(sum);
     }
 }

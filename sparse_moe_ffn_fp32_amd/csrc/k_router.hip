@@ -88,8 +88,7 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
                     z += __uint_as_float(xv[j] & 0xffff0000u) * __uint_as_float(gv[j] & 0xffff0000u);
                 }
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+            z = wave_sum(z);
         }
         if (lane == 0) sgate_out[t] = gate_inp ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
     }

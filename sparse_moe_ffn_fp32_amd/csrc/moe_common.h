@@ -91,11 +91,38 @@ __device__ __forceinline__ void dpp_argmax_step(float& v, int& i) {
     i = take ? oi : i;
 }
 
+// Cross-row steps of a wave arg-max: rows 1 and 3 take the better of
+// themselves and lane 15 of the row below (row_bcast:15), then rows 2 and 3
+// take lane 31 (row_bcast:31); lane 63 ends with the wave's best.  Rows a
+// step does not write keep their own pair, which never ranks before itself.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void dpp_argmax_bcast(float& v, int& i) {
+    const float ov = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, false));
+    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false);
+    const bool take = ranks_before(ov, oi, v, i);
+    v = take ? ov : v;
+    i = take ? oi : i;
+}
+
+// Wave-wide best (score desc, index asc) of one candidate per lane; the
+// result is wave-uniform.
+__device__ __forceinline__ void wave_argmax(float cv, int ci, float& bv, int& bi) {
+    dpp_argmax_step<0xB1>(cv, ci);   // quad_perm [1,0,3,2]
+    dpp_argmax_step<0x4E>(cv, ci);   // quad_perm [2,3,0,1]
+    dpp_argmax_step<0x141>(cv, ci);  // row_half_mirror
+    dpp_argmax_step<0x140>(cv, ci);  // row_mirror: every lane holds its row's best
+    dpp_argmax_bcast<0x142, 0xa>(cv, ci);
+    dpp_argmax_bcast<0x143, 0xc>(cv, ci);
+    bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cv), 63));
+    bi = __builtin_amdgcn_readlane(ci, 63);
+}
+
 // Top-8 of 256 scores held by one wave (lane l holds experts l, l+64,
-// l+128, l+192 in v[0..3]), ordered by (score desc, index asc).  Each round
-// is an arg-max: DPP exchanges inside 16-lane rows (xor 1, xor 2, half-row
-// mirror, row mirror), then the four row winners are read as scalars.  The
-// results are wave-uniform.
+// l+128, l+192 in v[0..3]), ordered by (score desc, index asc).  Each lane
+// sorts its four candidates once; each of the eight rounds is then one wave
+// arg-max over the lanes' current heads, and the winning lane advances its
+// head.  The results are wave-uniform.
 __device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v, int* sel_i) {
     float a[4];
     int ai[4];
@@ -117,30 +144,57 @@ __device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v
         a[q] = sw ? tv : a[q];
         ai[q] = sw ? ti : ai[q];
     }
-    int head = 0;
+    // the lane's head candidate; a lane that has given all four holds -inf
+    float hv = a[0];
+    int hi = ai[0];
 #pragma unroll
     for (int r = 0; r < 8; r++) {
-        float cv = head == 0 ? a[0] : head == 1 ? a[1] : head == 2 ? a[2] : head == 3 ? a[3] : -INFINITY;
-        int ci = head == 0 ? ai[0] : head == 1 ? ai[1] : head == 2 ? ai[2] : head == 3 ? ai[3] : 0x7fffffff;
-        dpp_argmax_step<0xB1>(cv, ci);   // quad_perm [1,0,3,2]
-        dpp_argmax_step<0x4E>(cv, ci);   // quad_perm [2,3,0,1]
-        dpp_argmax_step<0x141>(cv, ci);  // row_half_mirror
-        dpp_argmax_step<0x140>(cv, ci);  // row_mirror
-        float bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cv), 15));
-        int bi = __builtin_amdgcn_readlane(ci, 15);
-#pragma unroll
-        for (int row = 1; row < 4; row++) {
-            const float rv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cv), 16 * row + 15));
-            const int ri = __builtin_amdgcn_readlane(ci, 16 * row + 15);
-            if (ranks_before(rv, ri, bv, bi)) {
-                bv = rv;
-                bi = ri;
-            }
-        }
+        float bv;
+        int bi;
+        wave_argmax(hv, hi, bv, bi);
         sel_v[r] = bv;
         sel_i[r] = bi;
-        head += (bi & 63) == lane;
+        if (bi == hi) {  // this lane gave the winner: shift its list
+            a[0] = a[1]; ai[0] = ai[1];
+            a[1] = a[2]; ai[1] = ai[2];
+            a[2] = a[3]; ai[2] = ai[3];
+            a[3] = -INFINITY; ai[3] = 0x7fffffff;
+            hv = a[0];
+            hi = ai[0];
+        }
     }
+}
+
+// Sum over each 16-lane row; every lane of the row ends with the same,
+// order-fixed value (each step adds a lane's partner, and the partner adds
+// the same two terms).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v = quad_sum(v);
+    v += dpp_mov<0x141>(v);  // row_half_mirror
+    v += dpp_mov<0x140>(v);  // row_mirror
+    return v;
+}
+
+// Sum over the 64 lanes of a wave, the same value in every lane: row sums,
+// then rows (0,1) and (2,3) through v_permlane16_swap, then the two halves
+// through v_permlane32_swap.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    v = __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+    const uint32_t c = __builtin_bit_cast(uint32_t, v);
+    const auto q = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+    return __builtin_bit_cast(float, (uint32_t)q[0]) + __builtin_bit_cast(float, (uint32_t)q[1]);
 }
 
 }  // namespace moe
