@@ -28,6 +28,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0
 EXPERT_BYTES = 3 * (512 * 2048 // 2 + 2 * 512 * 32 * 2)  # gate+up+down packed + scales + biases = 1,769,472
 GU_BYTES = 2 * (512 * 2048 // 2 + 2 * 512 * 32 * 2)      # gate+up of one expert = 1,179,648
+DOWN_BYTES = 512 * 2048 // 2 + 2 * 2048 * 8 * 2           # down of one expert = 589,824
 SHARED_BYTES = 3 * 512 * 2048 * 2
 SHARED_DOWN_BYTES = 2048 * 512 * 2
 ROUTER_BYTES = 256 * 2048 * 4
@@ -271,9 +272,12 @@ def main():
     if T <= 64:
         # the gate/up launch also runs the shared expert's down projection:
         # routed gate/up weights of the distinct experts, the shared down
-        # weights, x and the shared h in; routed h and the shared output out
-        gu_bytes = [d * GU_BYTES + SHARED_DOWN_BYTES + T * 2048 * 2 + T * 512 * 4 + T * 8 * 512 * 2 + T * 2048 * 4
-                    for d in distinct]
+        # weights, x and the shared h in; routed h and the shared output out.
+        # For T <= 4 it also streams the selected experts' down rows from HBM
+        # (the down launch then reads them from cache), so they count here.
+        down_here = DOWN_BYTES if T <= 4 else 0
+        gu_bytes = [d * (GU_BYTES + down_here) + SHARED_DOWN_BYTES + T * 2048 * 2 + T * 512 * 4 + T * 8 * 512 * 2
+                    + T * 2048 * 4 for d in distinct]
         per_launch = float(np.mean(gu_bytes))
         achieved = per_launch / (kernel_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
