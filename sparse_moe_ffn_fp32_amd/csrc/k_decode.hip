@@ -1,4 +1,5 @@
-// Decode path (T <= 64): bandwidth-bound expert GEMVs on skinny MFMA tiles.
+// Decode path for 4 < T <= 64 tokens: bandwidth-bound expert GEMVs on skinny
+// MFMA tiles (T <= 4 runs k_decode_tiny.hip).
 //
 // Lily engine page: batch-1 decode is a GEMV bound by the bytes moved per
 // token ("Dekodavimas: sumazinti perkeliamu baitu kieki vienam tokenui"), and
@@ -30,18 +31,15 @@
 //          and the shared expert's gate/up + SwiGLU, K split over the 16
 //          waves of a block and reduced in LDS in fixed order; x copied into
 //          the K order of the codes.
-//   route  (T > 4 only) one block: softmax/top-8/renormalise per token,
-//          sgate, the distinct experts with their (token, rank) pairs.
-//   C      routed gate/up + SwiGLU, 32 features x one expert per block with K
-//          split in four; for T <= 4 a block serves one (token, rank) pair
-//          and every wave derives the pair's expert from the token's logits
-//          (top-8 by DPP arg-max) instead of waiting for a routing launch.
-//          Extra blocks: the shared expert's down projection.
-//   D      routed down projection of 16 output rows per block; for T <= 4
-//          over every (token, rank) pair and then the combine
-//          y = sum_{r=0..7} w_r * down_r + sgate * shexp  in fixed order with
-//          one bf16 rounding (no float atomics); for T > 4 over 8 distinct
-//          experts per block, fp32 partials per pair, and a combine launch.
+//   route  one block: softmax/top-8/renormalise per token, sgate, the
+//          distinct experts with their (token, rank) pairs.
+//   C      routed gate/up + SwiGLU, 32 features x one distinct expert per
+//          block with K split in four; extra blocks: the shared expert's down
+//          projection.
+//   D      routed down projection of 16 output rows per block over 8 distinct
+//          experts (one per wave), fp32 partials per pair.
+//   combine  y = sum_{r=0..7} w_r * partial_r + sgate * shexp  in fixed order
+//          with one bf16 rounding (no float atomics).
 //
 // Indices read back from the workspace are clamped to their ranges before
 // they address memory.
