@@ -198,3 +198,62 @@ def test_workspace_reuse_across_calls(gpu, layer0):
         got = (y.cpu().numpy().view(np.uint16), idx.cpu().numpy(), w.cpu().numpy())
         for u, v in zip(got, ref):
             assert np.array_equal(u, v), f"T={T}"
+
+
+def test_config1_40_layers_graph_replays(gpu):
+    """The default measured workload in the launch configuration the bench
+    times: 40 independent layers (seed = layer) at T=1, every call captured
+    into one HIP graph.  The eager pass matches the oracle layer by layer
+    (routing exact, y within the per-token bar); three replays, with eager
+    device work and synchronisation between them, reproduce the eager
+    outputs bit for bit."""
+    import sparse_moe_ffn_fp32_amd as moe
+    torch = gpu.torch
+    n_layers, T = 40, 1
+    O = oracle.get()
+    layers, dls, xs = [], [], []
+    for l in range(n_layers):
+        layer = synth.make_layer(l)
+        x, _, _ = workloads.enforce_margin(layer, T, l, O=O)
+        dls.append(moe.DeviceLayer.from_host(layer))
+        layers.append((layer, x))
+        xs.append(torch.from_numpy(x.view(np.int16)).cuda())
+        if l % 10 == 9:
+            _say(f"config1: {l + 1} layers uploaded")
+    ws = moe.alloc_workspace(T)
+    ys = [torch.empty((T, 2048), dtype=torch.int16, device="cuda") for _ in range(n_layers)]
+    idx = [torch.empty((T, 8), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+    w = [torch.empty((T, 8), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+
+    def run(stream):
+        for l in range(n_layers):
+            moe.moe_ffn_forward_path(xs[l], dls[l], ys[l], ws, idx[l], w[l], stream=stream)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [(a.cpu().numpy().copy(), b.cpu().numpy().copy(), c.cpu().numpy().copy()) for a, b, c in zip(ys, idx, w)]
+
+    run(None)
+    eager = snapshot()
+    for l, (layer, x) in enumerate(layers):
+        y_l, i_l, w_l = eager[l]
+        routing_check(layer, x, i_l, w_l, O=O)
+        output_check(layer, x, y_l.view(np.uint16), O=O)
+    _say("config1: eager pass matches the oracle on all 40 layers")
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=cap):
+        run(cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (*ys, *idx, *w):
+            t.zero_()  # eager device work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for l in range(n_layers):
+            for u, v in zip(got[l], eager[l]):
+                assert np.array_equal(u, v), f"replay {rep} layer {l} differs from the eager pass"
+    _say("config1: 3 graph replays reproduce the eager pass bit for bit")
