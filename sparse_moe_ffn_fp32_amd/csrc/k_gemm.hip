@@ -116,10 +116,11 @@ struct GemmSmem {
     uint32_t sb[C::Q4 ? GEMM_BN * C::SROW : 1];  // (bias << 16) | scale, bf16 bits
 };
 
+// One block's work; `bid` is the block's index within its mode's grid
+// (a multiple-of-8 offset from blockIdx.x, so bid % 8 is still the XCD).
 template <int MODE>
-__global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
+__device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm, int bid) {
     using C = GemmCfg<MODE>;
-    __shared__ __attribute__((aligned(16))) GemmSmem<MODE> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -133,7 +134,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
     constexpr int NB = C::NB;
     const int n_tiles = C::ROUTED ? g.tile_count[0] : (g.T + GEMM_BM - 1) / GEMM_BM;
     const int live = n_tiles * NB, per_xcd = (live + 7) >> 3;
-    const int slot = blockIdx.x >> 3, item = (blockIdx.x & 7) * per_xcd + slot;
+    const int slot = bid >> 3, item = (bid & 7) * per_xcd + slot;
     if (slot >= per_xcd || item >= live) return;
     const int tile = item / NB, nblk = item % NB;
     int e = 0, m0 = 0, rows = 0, seg = 0;
@@ -419,6 +420,25 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
     }
 }
 
+template <int MODE>
+__global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) GemmSmem<MODE> sm;
+    gemm_block<MODE>(g, sm, blockIdx.x);
+}
+
+// The router logits and the shared expert's gate/up read only x, so they
+// share one launch: blocks [0, n_router) compute logits, the rest the shared
+// gate/up (either alone fills only part of the chip at a few thousand tokens).
+constexpr size_t ROUTER_SGU_SMEM = sizeof(GemmSmem<MODE_ROUTER>) > sizeof(GemmSmem<MODE_SGU>)
+                                       ? sizeof(GemmSmem<MODE_ROUTER>) : sizeof(GemmSmem<MODE_SGU>);
+__global__ void __launch_bounds__(256) k_gemm_router_sgu(GemmArgs g, int n_router) {
+    __shared__ __attribute__((aligned(16))) char sm[ROUTER_SGU_SMEM];
+    if ((int)blockIdx.x < n_router)
+        gemm_block<MODE_ROUTER>(g, *reinterpret_cast<GemmSmem<MODE_ROUTER>*>(sm), blockIdx.x);
+    else
+        gemm_block<MODE_SGU>(g, *reinterpret_cast<GemmSmem<MODE_SGU>*>(sm), blockIdx.x - n_router);
+}
+
 // y = sum_r partial_r, for layers without a shared expert.
 __global__ void __launch_bounds__(256) k_combine_routed(const uint16_t* __restrict__ p, const int32_t* __restrict__ pos_of,
                                                         uint16_t* __restrict__ y, int T) {
@@ -440,12 +460,20 @@ __global__ void __launch_bounds__(256) k_prep_x(const uint16_t* __restrict__ x, 
 
 int gemm_bm() { return GEMM_BM; }
 
-hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits, int T,
-                              const Tracer& tr, hipStream_t s) {
+hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits,
+                              const uint16_t* sh_gate, const uint16_t* sh_up, uint16_t* hs, int T, const Tracer& tr,
+                              hipStream_t s) {
     GemmArgs g = {};
     g.xh = xh; g.wr2 = wr2; g.rbias = bias; g.logits = logits; g.T = T;
     const int mt = (T + GEMM_BM - 1) / GEMM_BM;
-    tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm<MODE_ROUTER>, dim3(8 * ((mt * (E / 128) + 7) / 8)), dim3(256), 0, s, g);
+    const int n_router = 8 * ((mt * (E / 128) + 7) / 8);
+    if (sh_gate) {
+        g.sw[0] = sh_gate; g.sw[1] = sh_up; g.hs_out = hs;
+        const int n_sgu = 8 * ((mt * (FS / 128) + 7) / 8);
+        tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm_router_sgu, dim3(n_router + n_sgu), dim3(256), 0, s, g, n_router);
+    } else {
+        tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm<MODE_ROUTER>, dim3(n_router), dim3(256), 0, s, g);
+    }
     return hipGetLastError();
 }
 
@@ -469,11 +497,7 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.q[1] = p.up_q; g.sc[1] = p.up_s; g.bi[1] = p.up_b;
     g.h_out = p.h;
     tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm<MODE_GU>, grid(max_tiles * (F / 128)), dim3(256), 0, s, g);
-    // shared gate/up
-    if (p.sh_gate) {
-        g.sw[0] = p.sh_gate; g.sw[1] = p.sh_up; g.hs_out = p.hs;
-        hipLaunchKernelGGL(k_gemm<MODE_SGU>, grid(mt * (FS / 128)), dim3(256), 0, s, g);
-    }
+    // (the shared gate/up ran with the router logits)
     // routed down
     g.q[0] = p.down_q; g.sc[0] = p.down_s; g.bi[0] = p.down_b;
     g.p_out = p.partial;

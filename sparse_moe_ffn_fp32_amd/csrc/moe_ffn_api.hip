@@ -106,7 +106,8 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
     chk(launch_split_router(router->weight, wr2, s));
     chk(launch_prep_x(x, xh, T, s));
-    chk(launch_router_gemm(xh, wr2, router->bias, logits, T, tr, s));
+    chk(launch_router_gemm(xh, wr2, router->bias, logits, sh ? sh->gate : nullptr, sh ? sh->up : nullptr,
+                           (uint16_t*)at(L.hs), T, tr, s));
     chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, T, s));
     chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(), s));
     PrefillGemmParams p{};

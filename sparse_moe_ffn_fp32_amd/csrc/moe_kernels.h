@@ -55,8 +55,10 @@ struct PrefillGemmParams {
 };
 int gemm_bm();
 hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s);
-hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits, int T,
-                              const Tracer& tr, hipStream_t s);
+// router logits, and the shared expert's gate/up + SwiGLU into hs when sh_gate != nullptr
+hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits,
+                              const uint16_t* sh_gate, const uint16_t* sh_up, uint16_t* hs, int T, const Tracer& tr,
+                              hipStream_t s);
 hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hipStream_t s);
 
 // ---- decode path (k_decode.hip), T <= 64
