@@ -230,23 +230,33 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ routing
-// T > TINY_T: one block routes every token and lists the distinct experts in
-// increasing id order, each with its (token, rank) pairs in token order.  An
-// assignment's place among equal experts comes from ballots over the 8 bits
-// of the expert id (within a wave) plus per-wave counts (across waves).
+// One wave per token: DPP top-8 of the logits, renormalised weights and
+// sgate, with the token's logits, x and gate vector loaded together.  Many
+// small blocks, so the 8T arg-max rounds spread over the chip.
+__global__ void __launch_bounds__(256) k_dec_topk(DecodeArgs a) {
+    const int lane = threadIdx.x & 63, t = 4 * blockIdx.x + (threadIdx.x >> 6);
+    if (t >= a.T) return;
+    float v[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) v[c] = a.logits[(size_t)t * E + lane + 64 * c];
+    float sel_v[K];
+    int sel_i[K];
+    wave_top8(v, lane, sel_v, sel_i);
+    write_token_route(a, t, lane, sel_v, sel_i, nullptr);
+    write_token_sgate(a, t, lane);
+}
+
+// One block lists the distinct experts in increasing id order, each with its
+// (token, rank) pairs in token order.  An assignment's place among equal
+// experts comes from ballots over the 8 bits of the expert id (within a
+// wave) plus per-wave counts (across waves).
 __global__ void __launch_bounds__(1024) k_dec_route(DecodeArgs a) {
     __shared__ int sidx[64 * K];
     __shared__ int wcnt[8][E];
     __shared__ int scan_a[E], scan_b[E];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = a.T, N = T * K;
-    for (int t = wave; t < T; t += 16) {
-        float sel_v[K];
-        int sel_i[K];
-        token_top8(a, t, lane, sel_v, sel_i);
-        write_token_route(a, t, lane, sel_v, sel_i, sidx);
-        write_token_sgate(a, t, lane);
-    }
+    if (tid < N) sidx[tid] = a.idx[tid];
     for (int i = tid; i < 8 * E; i += 1024) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     int e = 0, rank = 0;
@@ -378,18 +388,20 @@ __device__ __forceinline__ void gu_finish(const DecodeArgs& a, float (*red)[4][2
     }
 }
 
-__global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_gu_blocks) {
+// Blocks [0, n_sd) are the shared expert's down projection (first, so they
+// start at once), the routed blocks follow.
+__global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_sd) {
     __shared__ float red[2][4][2][16][16];  // [gate/up][K quarter][feature group][token slot][feature]
     __shared__ int tile_pairs[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
-    if ((int)blockIdx.x >= n_gu_blocks) {
+    if ((int)blockIdx.x < n_sd) {
         // ---- shared expert down: ys[t, o0+n] = sum_j Wsd[o0+n, j] hs[t, j],
         // hs split into bf16 hi + lo; wave w takes K in [64w, 64w+64)
         if (!a.sg) return;
         float(*sred)[16][16] = (float(*)[16][16])red;  // [8][16][16]
-        const int o0 = 16 * (blockIdx.x - n_gu_blocks);
+        const int o0 = 16 * blockIdx.x;
         const int k0 = 64 * wave + 8 * kq;
         const uint16_t* wrow = a.sd + (size_t)(o0 + n) * FS + k0;
         const u32x4 b0 = *(const u32x4*)(wrow), b1 = *(const u32x4*)(wrow + 32);
@@ -430,10 +442,11 @@ __global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_gu_bloc
     }
     // ---- routed gate/up: 32 features (2 groups of 16) x 4 K quarters
     const int fg = wave & 1, kq4 = wave >> 1;
-    const int chunk = blockIdx.x % (F / 32);
+    const int bid = blockIdx.x - n_sd;
+    const int chunk = bid % (F / 32);
     const int f0 = 32 * chunk;
     const size_t frow = f0 + 16 * fg + n;
-    const int u = blockIdx.x / (F / 32);
+    const int u = bid / (F / 32);
     if (u >= min(a.nuniq[0], E)) return;
     const int e = a.uexp[u] & (E - 1), cnt = min(max(a.ucnt[u], 1), T);
     const int off = min(max(a.uoff[u], 0), T * K - cnt);
@@ -567,9 +580,10 @@ static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s
     const int n_items = a.T * K < E ? a.T * K : E;
     const int n_gu = n_items * (F / 32);
     tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<NMT>, dim3(N_ROUTER_BLK + N_SGU_BLK + 1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(k_dec_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
-    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_gu + (a.sg ? N_SDOWN_BLK : 0)), dim3(512), 0, s, a,
-              n_gu);
+    const int n_sd = a.sg ? N_SDOWN_BLK : 0;
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_sd + n_gu), dim3(512), 0, s, a, n_sd);
     tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(N_ROW_TILES * ((n_items + 7) / 8)), dim3(512), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_COMBINE, k_dec_combine, dim3((a.T * D + 255) / 256), dim3(256), 0, s, a);
 }
