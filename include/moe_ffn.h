@@ -64,6 +64,14 @@ extern "C" {
 
 #define MOE_FFN_DECODE_MAX_T 64
 #define MOE_FFN_MAX_T (1 << 20)
+/* The prefill path runs at most this many tokens per pass; a longer call runs
+ * consecutive passes over token slices in the same workspace, so the
+ * workspace stops growing at this size.  Tokens are independent and every
+ * output row is accumulated in the same order whatever rows share its tile,
+ * so the result is the one a single pass would give, bit for bit.  (The
+ * qwen35moe page's batched prefill and the Lily engine page both process
+ * long prompts in bounded slices.) */
+#define MOE_FFN_PREFILL_CHUNK_T 32768
 
 /* Layer shape.  The library is compiled for {2048, 256, 8, 512, 512, 64}
  * (d_model, n_experts, top_k, d_ff, d_ff_shared, group_size) and returns
@@ -107,8 +115,9 @@ typedef struct {
 } moe_ffn_shared;
 
 /* Bytes of device workspace a call with T tokens needs (0 for T == 0; 0 for
- * invalid dims or T).  The workspace needs no initialisation and carries no
- * state from one call to the next. */
+ * invalid dims or T); the same for every T >= MOE_FFN_PREFILL_CHUNK_T.  The
+ * workspace needs no initialisation and carries no state from one call to
+ * the next. */
 size_t moe_ffn_workspace_size(const moe_ffn_dims *dims, int64_t T);
 
 /* y[T, d_model] bf16 = the FFN above applied to x[T, d_model] bf16.

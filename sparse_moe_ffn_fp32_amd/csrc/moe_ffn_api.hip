@@ -41,9 +41,10 @@ Layout layout(int64_t T) {
     return L;
 }
 
-// Both paths' regions, so any path can run in a workspace sized for T.
+// Both paths' regions, so any path can run in a workspace sized for T; the
+// prefill regions are sized for one pass of at most MOE_FFN_PREFILL_CHUNK_T.
 size_t workspace_bytes(int64_t T) {
-    size_t b = layout(T).total;
+    size_t b = layout(T < MOE_FFN_PREFILL_CHUNK_T ? T : MOE_FFN_PREFILL_CHUNK_T).total;
     if (T <= MOE_FFN_DECODE_MAX_T) {
         const size_t d = decode_workspace_bytes((int)T, nullptr);
         if (d > b) b = d;
@@ -157,9 +158,18 @@ int moe_ffn_forward_traced(const moe_ffn_dims* dims, int64_t T, const uint16_t* 
         tr.stop = (hipEvent_t)trace->stop;
     }
     const bool decode = path == MOE_FFN_PATH_DECODE || (path == MOE_FFN_PATH_AUTO && T <= MOE_FFN_DECODE_MAX_T);
-    if (!decode)
-        return run_prefill((int)T, x, router, experts, shared, y, topk_idx, topk_weight, (char*)workspace, tr,
-                           (hipStream_t)stream);
+    if (!decode) {
+        // passes over token slices of at most MOE_FFN_PREFILL_CHUNK_T (a
+        // traced kernel is bracketed in every pass; the events keep the last)
+        for (int64_t c0 = 0; c0 < T; c0 += MOE_FFN_PREFILL_CHUNK_T) {
+            const int tc = (int)(T - c0 < MOE_FFN_PREFILL_CHUNK_T ? T - c0 : MOE_FFN_PREFILL_CHUNK_T);
+            const int r = run_prefill(tc, x + c0 * D, router, experts, shared, y + c0 * D,
+                                      topk_idx ? topk_idx + c0 * K : nullptr, topk_weight ? topk_weight + c0 * K : nullptr,
+                                      (char*)workspace, tr, (hipStream_t)stream);
+            if (r != MOE_FFN_OK) return r;
+        }
+        return MOE_FFN_OK;
+    }
     DecodeParams p{};
     p.x = x;
     p.T = (int)T;

@@ -99,3 +99,15 @@ def test_rejects_bad_arguments(L):
     assert _call(L, layer=lay) == moe.MOE_FFN_EALIGN
     assert L.moe_ffn_forward_path(None, 4, 1, None, None, None, 1, None, None, 1, 1, None, 0) == moe.MOE_FFN_EINVAL
 
+
+
+def test_workspace_is_bounded_by_the_prefill_slice(L):
+    """Prefill runs in passes of at most MOE_FFN_PREFILL_CHUNK_T tokens, so
+    the workspace stops growing there (and is never smaller than a pass
+    needs)."""
+    chunk = 32768
+    w = moe.moe_ffn_workspace_size(chunk)
+    assert moe.moe_ffn_workspace_size(chunk + 1) == w
+    assert moe.moe_ffn_workspace_size(1 << 20) == w
+    assert moe.moe_ffn_workspace_size(chunk - 1) < w
+    assert "#define MOE_FFN_PREFILL_CHUNK_T 32768" in open(HEADER).read()

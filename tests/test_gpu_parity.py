@@ -257,3 +257,35 @@ def test_config1_40_layers_graph_replays(gpu):
             for u, v in zip(got[l], eager[l]):
                 assert np.array_equal(u, v), f"replay {rep} layer {l} differs from the eager pass"
     _say("config1: 3 graph replays reproduce the eager pass bit for bit")
+
+
+def test_prefill_in_slices_matches_one_pass(gpu, layer0):
+    """A call longer than MOE_FFN_PREFILL_CHUNK_T runs in token slices inside
+    a workspace of one slice's size: 32768 + 7 tokens give, bit for bit, what
+    separate calls on the two slices give, and match the oracle on a sample
+    that includes the slice boundary and the ragged tail."""
+    import sparse_moe_ffn_fp32_amd as moe
+    torch = gpu.torch
+    chunk, tail = 32768, 7
+    T = chunk + tail
+    x, _, _ = workloads.enforce_margin(layer0, T, 777)
+    dl = gpu.device_layer(layer0)
+    ws = moe.alloc_workspace(T)
+    assert ws.numel() == moe.moe_ffn_workspace_size(chunk)
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+
+    def call(lo, hi):
+        y = torch.empty((hi - lo, 2048), dtype=torch.int16, device="cuda")
+        idx = torch.empty((hi - lo, 8), dtype=torch.int32, device="cuda")
+        w = torch.empty((hi - lo, 8), dtype=torch.float32, device="cuda")
+        moe.moe_ffn_forward_path(xd[lo:hi], dl, y, ws, idx, w, path=PATHS["prefill"])
+        torch.cuda.synchronize()
+        return y.cpu().numpy().view(np.uint16), idx.cpu().numpy(), w.cpu().numpy()
+
+    whole = call(0, T)
+    parts = [call(0, chunk), call(chunk, T)]
+    for u, a, b in zip(whole, parts[0], parts[1]):
+        assert np.array_equal(u, np.concatenate([a, b])), "sliced prefill differs from separate passes"
+    sample = np.unique(np.concatenate([np.arange(0, T, 512), np.arange(chunk - 4, T)]))
+    _say(routing_check(layer0, x, whole[1], whole[2], tokens=sample))
+    _say(output_check(layer0, x, whole[0], tokens=sample))
