@@ -7,26 +7,33 @@
 // dequantised matrix never exists; accumulation is fp32.
 //
 // Block tile: 128 activation rows (tokens) x 256 weight rows (output
-// features); 4 waves as 2 x 2, each 64 x 128 = 2 x 4 tiles of
-// v_mfma_f32_32x32x16_f16.  MFMA layout: lane l holds A[l%32][8*(l/32) .. +8]
-// and B[8*(l/32) .. +8][l%32]; accumulator lane l holds C[i][l%32] for
-// i = 8*(v/4) + 4*(l/32) + v%4, v = 0..15.  K advances in steps of 64, one
-// quantisation group.  Both operands are fp16 with K inside every 8-block in
-// the perm8 order (see moe_common.h); a dequantised weight is fp16(s*q + b)
-// rounded once, x is converted from bf16 exactly (within the fp16 range), h is
-// rounded once to fp16.  Inside a K step, MFMA sub-step kk and lane half
-// kq = l/32 use K in [32kq + 8kk, +8) for both operands.
+// features); 4 waves, wave w computing all 128 rows against weight rows
+// [64w, 64w + 64) as 4 x 2 tiles of v_mfma_f32_32x32x16_f16.  MFMA layout:
+// lane l holds A[l%32][8*(l/32) .. +8] and B[8*(l/32) .. +8][l%32];
+// accumulator lane l holds C[i][l%32] for i = 8*(v/4) + 4*(l/32) + v%4,
+// v = 0..15.  K advances in steps of 64, one quantisation group.  Both
+// operands are fp16 with K inside every 8-block in the perm8 order (see
+// moe_common.h); a dequantised weight is fp16(s*q + b) rounded once, x is
+// converted from bf16 exactly (within the fp16 range), h is rounded once to
+// fp16.  Inside a K step, MFMA sub-step kk and lane half kq = l/32 use K in
+// [32kq + 8kk, +8) for both operands.
 //
 // Per K step every operand goes global -> registers -> LDS in coalesced
-// pieces, and the MFMAs read their fragments from LDS:
+// pieces:
 //   A (activations): eight lanes per row, 16 bytes each, so one load
-//     instruction covers eight whole 128-byte rows of the step;
-//   B (weights): two lanes per weight row, 16 bytes of codes (32 weights)
-//     each; the lane expands them to fp16 s*q + b with the group's scale and
-//     bias, which the block stages in LDS once at its start.
-// Global loads run three steps ahead in a ring of four register stages; LDS
-// tiles are double-buffered; one barrier per step.  Epilogues stage the
-// output tile in LDS so global stores are 16-byte row pieces.
+//     instruction covers eight whole 128-byte rows of the step; the MFMAs
+//     read their fragments from LDS;
+//   4-bit weights: two lanes per weight row, 16 bytes of codes (32 weights)
+//     each, stored raw (a quarter of the fp16 bytes); each wave expands the
+//     codes of its own 64 rows straight into MFMA operand registers, fp16
+//     s*q + b with the group's scale and bias (staged in LDS once at the
+//     block's start), one step ahead of the MFMAs that use them;
+//   16-bit weights (shared expert, router planes): converted to fp16 on the
+//     way into LDS and read back as fragments.
+// Global loads run ahead in a ring of register stages (three steps for 4-bit
+// weights, one otherwise); activation tiles are double-buffered, code tiles
+// quadruple-buffered; one barrier per step.  Epilogues stage the output tile
+// in LDS so global stores are 16-byte row pieces.
 //
 // Modes:
 //   GU     routed gate/up over the expert-sorted rows; epilogue SwiGLU
@@ -106,24 +113,36 @@ struct GemmArgs {
     int T;
 };
 
-// LDS of one block: double-buffered operand tiles; Q4 modes add the staged
-// scales and biases.  The epilogues reuse the operand tiles.
+constexpr int BQS = 12;  // u32 per LDS raw-code row: 32 bytes of codes + 16 bytes pad
+constexpr int QBUF = 4;  // raw-code LDS buffers (codes are stored two steps ahead of their MFMAs)
+
+// LDS of one block: double-buffered activation tiles; the 4-bit modes keep the
+// raw codes of four steps plus the staged scales and biases (and DOWN the
+// rows' routing weights), the other modes a double-buffered fp16 weight
+// tile.  The epilogues reuse the operand tiles (a, then b or bq).
 template <int MODE>
 struct GemmSmem {
     using C = GemmCfg<MODE>;
     f16 a[2][GEMM_BM * LDSB];
-    f16 b[2][GEMM_BN * LDSB];
-    uint32_t sb[C::Q4 ? GEMM_BN * C::SROW : 1];  // (bias << 16) | scale, bf16 bits
+    f16 b[C::Q4 ? 1 : 2][C::Q4 ? 8 : GEMM_BN * LDSB];
+    uint32_t bq[C::Q4 ? QBUF : 1][C::Q4 ? GEMM_BN * BQS : 4];
+    uint32_t sb[C::Q4 ? GEMM_BN * C::SROW : 4];  // (bias << 16) | scale, bf16 bits
+    float rw[MODE == MODE_DOWN ? GEMM_BM : 4];   // DOWN: routing weight x 2^6 per row
 };
 
 // One block's work; `bid` is the block's index within its mode's grid
 // (a multiple-of-8 offset from blockIdx.x, so bid % 8 is still the XCD).
+//
+// Wave w computes all 128 activation rows against LDS weight rows
+// [64w, 64w + 64): two 32-row tiles nt, acc[mt][nt] for activation rows
+// [32mt, 32mt + 32).  Paired modes map LDS row 64w + 32nt + j to gate
+// (nt = 0) or up (nt = 1) of feature 32w + j of the block (ROUTER: the hi
+// or lo plane of expert 32w + j), so one lane holds both values of a feature.
 template <int MODE>
 __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm, int bid) {
     using C = GemmCfg<MODE>;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, kq = lane >> 5;
 
     // ---- which (row tile, column block) this block owns.  Workgroups are
@@ -164,16 +183,12 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     }
 
     // ---- B: this thread covers lane half bh (K [32bh, 32bh+32) of a step) of
-    // LDS weight rows br0 and br0 + 128.  Gated modes: inside each wave
-    // column's 128 rows, 32-row tile nt holds gate (nt even) or up (nt odd)
-    // rows of features fbase + (nt/2)*32 + 0..31, so one lane's accumulators
-    // for tiles 2h and 2h+1 hold the gate and up value of the same feature.
+    // LDS weight rows br0 and br0 + 128.
     const int bh = tid & 1, br0 = tid >> 1;
     auto wrow = [&](int n, int& mat) -> size_t {  // global weight row of LDS row n
         if constexpr (C::PAIRED) {
-            const int j = n & 127, nt = j >> 5;
-            mat = nt & 1;
-            const int feat = nblk * 128 + (n >> 7) * 64 + (nt >> 1) * 32 + (j & 31);
+            mat = (n >> 5) & 1;
+            const int feat = nblk * 128 + 32 * (n >> 6) + (n & 31);
             if constexpr (MODE == MODE_ROUTER) return (size_t)mat * E + feat;  // plane, expert
             return C::Q4 ? (size_t)e * F + feat : (size_t)feat;
         } else {
@@ -192,7 +207,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
         else bpt[i] = (const u32x4*)(g.sw[mat] + row * C::KTOT) + 4 * bh;
     }
 
-    // ---- stage the block's scales and biases: LDS row n = tid
+    // ---- stage the block's scales and biases (LDS row n = tid) and, for
+    // DOWN, the rows' routing weights
     if constexpr (C::Q4) {
         int mat;
         const size_t row = wrow(tid, mat);
@@ -213,125 +229,184 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
             *(u32x4*)(dst + 8 * i + 4) = u32x4{lo[2], hi[2], lo[3], hi[3]};
         }
     }
+    if constexpr (MODE == MODE_DOWN) {
+        if (tid < GEMM_BM) sm.rw[tid] = g.wflat[g.perm[seg + m0 + min(tid, rows - 1)]] * PARTIAL_SCALE;
+    }
 
-    struct Stage {
-        u32x4 a[4];
-        u32x4 b[2][C::BW];
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
+
+    // eight MFMAs per sub-step kk against the activation tile in LDS buffer abuf
+    auto mfma_step = [&](int abuf, const f16x8 (&bf)[2][4]) {
+        const f16* ab = &sm.a[abuf][l32 * LDSB + 32 * kq];
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            f16x8 af[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
+#pragma unroll
+            for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt][kk], acc[mt][nt], 0, 0, 0);
+        }
     };
-    auto load = [&](int k, Stage& st) {
+    auto store_a = [&](const u32x4 (&av)[4], int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) st.a[i] = *(const u32x4*)(apt[i] + k * BK);
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int w = 0; w < C::BW; w++) st.b[i][w] = bpt[i][k * (C::Q4 ? 2 : 8) + w];
+        for (int i = 0; i < 4; i++) *(u32x4*)&sm.a[buf][(ar0 + 32 * i) * LDSB + 8 * ac] = av[i];
     };
-    // write step k's staged data into LDS buffer `buf`
-    auto store = [&](int k, const Stage& st, int buf) {
+    auto load_a = [&](int k, u32x4 (&av)[4]) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) *(u32x4*)&sm.a[buf][(ar0 + 32 * i) * LDSB + 8 * ac] = st.a[i];
+        for (int i = 0; i < 4; i++) av[i] = *(const u32x4*)(apt[i] + k * BK);
+    };
+
+    if constexpr (C::Q4) {
+        // ---- 4-bit weights: the raw codes (32 bytes per row and step) go to
+        // LDS; each wave expands its own rows' codes into MFMA operands,
+        // fp16 s*q + b, one step ahead of the MFMAs that use them.  Ring
+        // stage j holds A(j) and the codes of step j + 1; the codes of step
+        // j sit in LDS buffer j % 4, A(j) in buffer j % 2.  Loads run three
+        // steps ahead.
+        constexpr int R = 4;
+        static_assert(C::NK % R == 0 && QBUF == R, "K steps must be a multiple of the ring size");
+        struct Stage { u32x4 a[4]; u32x4 b[2]; };
+        auto load_b = [&](int k, u32x4 (&bv)[2]) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int n = br0 + 128 * i;
-            f16* dst = &sm.b[buf][n * LDSB + 32 * bh];
-            if constexpr (C::Q4) {
+            for (int i = 0; i < 2; i++) bv[i] = bpt[i][2 * k];
+        };
+        auto store_b = [&](const u32x4 (&bv)[2], int buf) {
+#pragma unroll
+            for (int i = 0; i < 2; i++) *(u32x4*)&sm.bq[buf][(br0 + 128 * i) * BQS + 4 * bh] = bv[i];
+        };
+        auto dequant = [&](int k, int qbuf, f16x8 (&bf)[2][4]) {
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++) {
+                const int n = 64 * wave + 32 * nt + l32;
+                const u32x4 codes = *(const u32x4*)&sm.bq[qbuf][n * BQS + 4 * kq];
                 const uint32_t sbw = sm.sb[n * C::SROW + k];
                 const f16 sv = (f16)bf16_to_f32(sbw & 0xffffu), bv = (f16)bf16_to_f32(sbw >> 16);
                 const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
 #pragma unroll
-                for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = q4_word_to_f16x8(st.b[i][0][w], s2, b2);
-            } else if constexpr (C::F16SRC) {
+                for (int kk = 0; kk < 4; kk++) bf[nt][kk] = __builtin_bit_cast(f16x8, q4_word_to_f16x8(codes[kk], s2, b2));
+            }
+        };
+        Stage ring[R];
+        u32x4 c0[2];
+        load_b(0, c0);
 #pragma unroll
-                for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = st.b[i][w];
-            } else {
+        for (int j = 0; j < R - 1; j++) {
+            load_a(j, ring[j].a);
+            load_b(min(j + 1, C::NK - 1), ring[j].b);
+        }
+        store_b(c0, 0);
+        __syncthreads();  // staged scales, biases, routing weights; codes of step 0
+        store_a(ring[0].a, 0);
+        store_b(ring[0].b, 1);
+        f16x8 bfr[2][2][4];
+        dequant(0, 0, bfr[0]);
+        __syncthreads();
+#pragma unroll 1
+        for (int k0 = 0; k0 < C::NK; k0 += R) {
 #pragma unroll
-                for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = bf16x8_to_f16x8_perm(st.b[i][w]);
+            for (int j = 0; j < R; j++) {
+                const int k = k0 + j;
+                Stage& nx = ring[(j + R - 1) % R];
+                load_a(min(k + R - 1, C::NK - 1), nx.a);
+                load_b(min(k + R, C::NK - 1), nx.b);
+                // keep the loads here: the scheduler would otherwise sink them
+                // towards their first use and undo the prefetch
+                __builtin_amdgcn_sched_barrier(0);
+                dequant(min(k + 1, C::NK - 1), (j + 1) % QBUF, bfr[(j + 1) & 1]);
+                mfma_step(j & 1, bfr[j & 1]);
+                store_a(ring[(j + 1) % R].a, (j + 1) & 1);
+                store_b(ring[(j + 1) % R].b, (j + 2) % QBUF);
+                __syncthreads();
             }
         }
-    };
-
-    f32x16 acc[2][4];
+    } else {
+        // ---- 16-bit weights: converted to fp16 (perm8) on the way into LDS,
+        // read back as MFMA operands.  Loads run one step ahead.
+        constexpr int R = 2;
+        static_assert(C::NK % R == 0, "K steps must be a multiple of the ring size");
+        struct Stage { u32x4 a[4]; u32x4 b[2][4]; };
+        auto load = [&](int k, Stage& st) {
+            load_a(k, st.a);
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
+            for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int nt = 0; nt < 4; nt++)
+                for (int w = 0; w < 4; w++) st.b[i][w] = bpt[i][8 * k + w];
+        };
+        auto store = [&](const Stage& st, int buf) {
+            store_a(st.a, buf);
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
-
-    auto mfma_step = [&](int buf) {
-        const f16* ab = &sm.a[buf][(wm * 64 + l32) * LDSB + 32 * kq];
-        const f16* bb = &sm.b[buf][(wn * 128 + l32) * LDSB + 32 * kq];
+            for (int i = 0; i < 2; i++) {
+                f16* dst = &sm.b[buf][(br0 + 128 * i) * LDSB + 32 * bh];
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            f16x8 af[2], bf[4];
+                for (int w = 0; w < 4; w++) {
+                    if constexpr (C::F16SRC) *(u32x4*)(dst + 8 * w) = st.b[i][w];
+                    else *(u32x4*)(dst + 8 * w) = bf16x8_to_f16x8_perm(st.b[i][w]);
+                }
+            }
+        };
+        auto read_b = [&](int buf, f16x8 (&bf)[2][4]) {
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
+            for (int nt = 0; nt < 2; nt++) {
+                const f16* bb = &sm.b[buf][(64 * wave + 32 * nt + l32) * LDSB + 32 * kq];
 #pragma unroll
-            for (int nt = 0; nt < 4; nt++) bf[nt] = *(const f16x8*)(bb + nt * 32 * LDSB + 8 * kk);
-#pragma unroll
-            for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                for (int nt = 0; nt < 4; nt++)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
-        }
-    };
-
-    // ---- pipeline.  Step k's loads sit in ring stage k % R; they are issued
-    // R-1 steps ahead and written to LDS one step ahead of their MFMAs.  The
-    // body covers R steps so ring stages and LDS buffers are compile-time
-    // constants; loads past the last step re-read the last step and the final
-    // store fills an unused buffer, so the body has no branches.
-    static_assert(C::NK % C::R == 0, "K steps must be a multiple of the ring size");
-    Stage ring[C::R];
-#pragma unroll
-    for (int j = 0; j < C::R - 1; j++) load(j, ring[j]);
-    __syncthreads();  // staged scales and biases visible
-    store(0, ring[0], 0);
-    __syncthreads();
+                for (int kk = 0; kk < 4; kk++) bf[nt][kk] = *(const f16x8*)(bb + 8 * kk);
+            }
+        };
+        Stage ring[R];
+        load(0, ring[0]);
+        store(ring[0], 0);
+        __syncthreads();
 #pragma unroll 1
-    for (int k0 = 0; k0 < C::NK; k0 += C::R) {
+        for (int k0 = 0; k0 < C::NK; k0 += R) {
 #pragma unroll
-        for (int j = 0; j < C::R; j++) {
-            const int k = k0 + j;
-            load(min(k + C::R - 1, C::NK - 1), ring[(j + C::R - 1) % C::R]);
-            // keep the loads here: the scheduler would otherwise sink them
-            // towards their first use and undo the prefetch
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_step(j & 1);
-            store(min(k + 1, C::NK - 1), ring[(j + 1) % C::R], (j + 1) & 1);
-            __syncthreads();
+            for (int j = 0; j < R; j++) {
+                const int k = k0 + j;
+                load(min(k + 1, C::NK - 1), ring[(j + 1) % R]);
+                __builtin_amdgcn_sched_barrier(0);
+                f16x8 bf[2][4];
+                read_b(j & 1, bf);
+                mfma_step(j & 1, bf);
+                store(ring[(j + 1) % R], (j + 1) & 1);
+                __syncthreads();
+            }
         }
     }
 
-    // ---- epilogues (the loop ended with a barrier: the operand tiles are free)
+    // ---- epilogues (the loop ended with a barrier: the operand tiles are
+    // free).  Accumulator element v of acc[mt][nt] is activation row
+    // r = 32mt + 8(v/4) + 4kq + v%4 and LDS weight row 64w + 32nt + l32.
+    auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
     if constexpr (MODE == MODE_ROUTER) {
+        const int ex = nblk * 128 + 32 * wave + l32;
+        const float b = g.rbias ? g.rbias[ex] : 0.0f;
 #pragma unroll
-        for (int hf = 0; hf < 2; hf++) {
-            const int ex = nblk * 128 + wn * 64 + hf * 32 + l32;
-            const float b = g.rbias ? g.rbias[ex] : 0.0f;
+        for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
-                    if (r < rows) g.logits[(size_t)(m0 + r) * E + ex] = (acc[mt][2 * hf][v] + acc[mt][2 * hf + 1][v]) + b;
-                }
-        }
+            for (int v = 0; v < 16; v++) {
+                const int r = acc_row(mt, v);
+                if (r < rows) g.logits[(size_t)(m0 + r) * E + ex] = (acc[mt][0][v] + acc[mt][1][v]) + b;
+            }
     } else if constexpr (C::GATED) {
         // h tile [128 rows][128 features] fp16 in LDS, then 16-byte row pieces
         constexpr int HS = 128 + 8;
-        f16* hb = &sm.b[0][0];
+        static_assert(GEMM_BM * HS * sizeof(f16) <= sizeof(sm.a), "h tile must fit the activation tiles");
+        f16* hb = &sm.a[0][0];
+        const int f = 32 * wave + l32;  // feature inside the block
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++)
+        for (int mt = 0; mt < 4; mt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
-#pragma unroll
-                for (int hf = 0; hf < 2; hf++) {
-                    const int f = wn * 64 + hf * 32 + l32;  // feature inside the block
-                    const float hv = silu_f32(acc[mt][2 * hf][v]) * acc[mt][2 * hf + 1][v];
-                    hb[r * HS + ((f & ~7) | perm8_pos(f & 7))] = (f16)hv;
-                }
+                const float hv = silu_f32(acc[mt][0][v]) * acc[mt][1][v];
+                hb[acc_row(mt, v) * HS + ((f & ~7) | perm8_pos(f & 7))] = (f16)hv;
             }
         __syncthreads();
         // 128 rows x 16 pieces of 8 features
@@ -340,23 +415,24 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
             const int pc = tid + 256 * i, r = pc >> 4, c = pc & 15;
             if (r < rows) {
                 const u32x4 v = *(const u32x4*)&hb[r * HS + 8 * c];
-                const int f = nblk * 128 + 8 * c;
-                if constexpr (MODE == MODE_GU) *(u32x4*)&g.h_out[(size_t)(seg + m0 + r) * F + f] = v;
-                else *(u32x4*)&g.hs_out[(size_t)(m0 + r) * FS + f] = v;
+                const int fo = nblk * 128 + 8 * c;
+                if constexpr (MODE == MODE_GU) *(u32x4*)&g.h_out[(size_t)(seg + m0 + r) * F + fo] = v;
+                else *(u32x4*)&g.hs_out[(size_t)(m0 + r) * FS + fo] = v;
             }
         }
     } else if constexpr (MODE == MODE_DOWN) {
         // partial tile [128 rows][256 outputs] fp16 (x 2^6 x routing weight)
         constexpr int PS = GEMM_BN + 8;
-        f16* pb = &sm.a[0][0];  // spans the A and B tiles (67.6 KB)
+        static_assert(GEMM_BM * PS * sizeof(f16) <= offsetof(GemmSmem<MODE>, sb), "partial tile must fit a, b, bq");
+        f16* pb = &sm.a[0][0];  // spans the activation and code tiles (67.6 KB)
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++)
+        for (int mt = 0; mt < 4; mt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
-                const float wt = g.wflat[g.perm[seg + m0 + min(r, rows - 1)]] * PARTIAL_SCALE;
+                const int r = acc_row(mt, v);
+                const float wt = sm.rw[r];
 #pragma unroll
-                for (int nt = 0; nt < 4; nt++) pb[r * PS + wn * 128 + nt * 32 + l32] = (f16)(wt * acc[mt][nt][v]);
+                for (int nt = 0; nt < 2; nt++) pb[r * PS + 64 * wave + 32 * nt + l32] = (f16)(wt * acc[mt][nt][v]);
             }
         __syncthreads();
 #pragma unroll
@@ -367,20 +443,19 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
         }
     } else {
         // combine: y = 2^-6 * sum_r partial_r + sgate * shexp, in two passes
-        // of 128 columns (the fp32 shared tile of one wave column per pass)
+        // of 128 columns (the fp32 shared tile of waves 2p, 2p + 1 in pass p)
         constexpr int YS = 128 + 4;
+        static_assert(GEMM_BM * YS * sizeof(float) <= offsetof(GemmSmem<MODE>, bq), "shared tile must fit a, b");
         float* yb = (float*)&sm.a[0][0];  // 128 x 132 fp32 = 67.6 KB
 #pragma unroll
         for (int pass = 0; pass < 2; pass++) {
-            if (wn == pass) {
+            if ((wave >> 1) == pass) {
 #pragma unroll
-                for (int mt = 0; mt < 2; mt++)
+                for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-                    for (int v = 0; v < 16; v++) {
-                        const int r = wm * 64 + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3);
+                    for (int v = 0; v < 16; v++)
 #pragma unroll
-                        for (int nt = 0; nt < 4; nt++) yb[r * YS + nt * 32 + l32] = acc[mt][nt][v];
-                    }
+                        for (int nt = 0; nt < 2; nt++) yb[acc_row(mt, v) * YS + 64 * (wave & 1) + 32 * nt + l32] = acc[mt][nt][v];
             }
             __syncthreads();
             // 128 rows x 16 pieces of 8 outputs
