@@ -66,6 +66,15 @@ constexpr int LDSB = BK + 8;          // fp16 per LDS operand row (16-byte pad)
 // removed exactly in the combine; |w * out| must stay below 1023.
 constexpr float PARTIAL_SCALE = 64.0f;
 
+// A kernel-argument pointer pinned in scalar registers.  Without this the
+// compiler reloads the argument inside every predicated store of an epilogue
+// and waits for it there, serialising one scalar round trip per store.
+template <typename P>
+__device__ __forceinline__ P pinned(P p) {
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
 template <int MODE>
 struct GemmCfg {
     static constexpr bool GATED = (MODE == MODE_GU || MODE == MODE_SGU);
@@ -92,7 +101,7 @@ struct GemmArgs {
     const int32_t* perm;     // sorted position -> assignment
     const int32_t* pos_of;   // assignment -> sorted position
     const int32_t* offs;     // [E+1] expert segment starts
-    const int32_t* tiles;    // [2*i] expert, [2*i+1] first row
+    const int32_t* tiles;    // [4i..4i+3] expert, first row, segment start, rows
     const int32_t* tile_count;
     const float* wflat;      // [T*K] routing weights by assignment
     const float* sgate;      // [T]
@@ -158,10 +167,11 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     const int tile = item / NB, nblk = item % NB;
     int e = 0, m0 = 0, rows = 0, seg = 0;
     if constexpr (C::ROUTED) {
-        e = g.tiles[2 * tile];
-        m0 = g.tiles[2 * tile + 1];
-        seg = g.offs[e];
-        rows = min(GEMM_BM, g.offs[e + 1] - seg - m0);  // >= 1 for a listed tile
+        const int4 rec = *(const int4*)&g.tiles[4 * tile];  // one dependent load
+        e = rec.x;
+        m0 = rec.y;
+        seg = rec.z;
+        rows = rec.w;  // 1 .. GEMM_BM
     } else {
         m0 = tile * GEMM_BM;
         rows = min(GEMM_BM, g.T - m0);                  // >= 1 for tile < n_tiles
@@ -408,16 +418,22 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
                 const float hv = silu_f32(acc[mt][0][v]) * acc[mt][1][v];
                 hb[acc_row(mt, v) * HS + ((f & ~7) | perm8_pos(f & 7))] = (f16)hv;
             }
+        uint16_t* const h_out = pinned(g.h_out);
+        uint16_t* const hs_out = pinned(g.hs_out);
         __syncthreads();
-        // 128 rows x 16 pieces of 8 features
+        // 128 rows x 16 pieces of 8 features: thread tid takes rows
+        // tid/16 + 16i, piece tid%16; all LDS reads first, then the stores
+        const int c = tid & 15, rb = tid >> 4;
+        u32x4 hv[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) hv[i] = *(const u32x4*)&hb[(rb + 16 * i) * HS + 8 * c];
+        const int fo = nblk * 128 + 8 * c;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int pc = tid + 256 * i, r = pc >> 4, c = pc & 15;
+            const int r = rb + 16 * i;
             if (r < rows) {
-                const u32x4 v = *(const u32x4*)&hb[r * HS + 8 * c];
-                const int fo = nblk * 128 + 8 * c;
-                if constexpr (MODE == MODE_GU) *(u32x4*)&g.h_out[(size_t)(seg + m0 + r) * F + fo] = v;
-                else *(u32x4*)&g.hs_out[(size_t)(m0 + r) * FS + fo] = v;
+                if constexpr (MODE == MODE_GU) *(u32x4*)&h_out[(size_t)(seg + m0 + r) * F + fo] = hv[i];
+                else *(u32x4*)&hs_out[(size_t)(m0 + r) * FS + fo] = hv[i];
             }
         }
     } else if constexpr (MODE == MODE_DOWN) {
@@ -434,12 +450,18 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
 #pragma unroll
                 for (int nt = 0; nt < 2; nt++) pb[r * PS + 64 * wave + 32 * nt + l32] = (f16)(wt * acc[mt][nt][v]);
             }
+        uint16_t* const p_out = pinned(g.p_out);
         __syncthreads();
+        // 128 rows x 32 pieces of 8 outputs: thread tid takes rows tid/32 + 8i,
+        // piece tid%32; all LDS reads first, then the stores
+        const int c = tid & 31, rb = tid >> 5;
+        u32x4 pv[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) pv[i] = *(const u32x4*)&pb[(rb + 8 * i) * PS + 8 * c];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-            const int pc = tid + 256 * i, r = pc >> 5, c = pc & 31;
-            if (r < rows)
-                *(u32x4*)&g.p_out[(size_t)(seg + m0 + r) * D + nblk * GEMM_BN + 8 * c] = *(const u32x4*)&pb[r * PS + 8 * c];
+            const int r = rb + 8 * i;
+            if (r < rows) *(u32x4*)&p_out[(size_t)(seg + m0 + r) * D + nblk * GEMM_BN + 8 * c] = pv[i];
         }
     } else {
         // combine: y = 2^-6 * sum_r partial_r + sgate * shexp, in two passes

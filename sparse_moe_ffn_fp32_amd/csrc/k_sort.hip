@@ -49,8 +49,9 @@ __device__ int block_exclusive_scan_256(int v, int* smem, int& total) {
 }
 
 // One block: per-(block, expert) bases, expert offsets offs[0..E], and the
-// tile map tiles[2*i] = expert, tiles[2*i+1] = first row of the tile within
-// the expert's segment; tile_count[0] = number of tiles.
+// tile map: record i is tiles[4i .. 4i+3] = {expert, first row of the tile
+// within the expert's segment, segment start, rows in the tile (1..bm)};
+// tile_count[0] = number of tiles.
 __global__ void __launch_bounds__(256) k_sort_scan(int32_t* __restrict__ cnt, int nblk, int32_t* __restrict__ offs,
                                                    int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count,
                                                    int bm) {
@@ -70,10 +71,8 @@ __global__ void __launch_bounds__(256) k_sort_scan(int32_t* __restrict__ cnt, in
     const int nt = (run + bm - 1) / bm;
     int ntot;
     const int toff = block_exclusive_scan_256(nt, smem, ntot);
-    for (int j = 0; j < nt; j++) {
-        tiles[2 * (toff + j)] = e;
-        tiles[2 * (toff + j) + 1] = j * bm;
-    }
+    for (int j = 0; j < nt; j++)
+        *(int4*)&tiles[4 * (toff + j)] = make_int4(e, j * bm, off, min(bm, run - j * bm));
     if (e == 0) tile_count[0] = ntot;
 }
 

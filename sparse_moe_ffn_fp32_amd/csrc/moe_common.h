@@ -75,7 +75,11 @@ __device__ __forceinline__ u32x4 q4_word_to_f16x8(uint32_t w, f16x2 s2, f16x2 b2
     return o;
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (about
+// 1 ulp each): every caller rounds the result to fp16 or feeds an fp32 dot
+// product, far coarser than the few-ulp difference from an IEEE division.
+// z -> -inf: exp overflows to inf and the reciprocal to 0, giving -0.
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // (value desc, index asc): does (va, ia) rank before (vb, ib)?
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {

@@ -30,7 +30,7 @@ Layout layout(int64_t T) {
     L.xh = o;         o += up((size_t)T * D * 2);
     L.cnt = o;        o += up((size_t)nblk * E * 4);
     L.offs = o;       o += up((E + 1) * 4);
-    L.tiles = o;      o += up(max_tiles * 2 * 4);
+    L.tiles = o;      o += up(max_tiles * 4 * 4);
     L.tile_count = o; o += up(4);
     L.perm = o;       o += up(N * 4);
     L.pos_of = o;     o += up(N * 4);
