@@ -49,6 +49,8 @@
 //          fp16 planes hi + lo (|w - hi - lo| <= 2^-22 |w|), paired like gate
 //          and up so one lane adds the two planes of an expert; epilogue
 //          + router bias -> fp32 logits.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 #include "../../include/moe_ffn.h"
@@ -251,29 +253,34 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
 
-    // eight MFMAs per sub-step kk against the activation tile in LDS buffer abuf
-    auto mfma_step = [&](int abuf, const f16x8 (&bf)[2][4]) {
+    // The activation rows come in NMT groups of 32 (a compile-time count):
+    // a tile's row groups past its last row are neither loaded nor multiplied.
+    // Eight MFMAs per group and sub-step kk against the activation tile in
+    // LDS buffer abuf.
+    auto mfma_step = [&](auto nmt_c, int abuf, const f16x8 (&bf)[2][4]) {
+        constexpr int NMT = decltype(nmt_c)::value;
         const f16* ab = &sm.a[abuf][l32 * LDSB + 32 * kq];
 #pragma unroll
         for (int kk = 0; kk < 4; kk++) {
-            f16x8 af[4];
+            f16x8 af[NMT];
 #pragma unroll
-            for (int mt = 0; mt < 4; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
+            for (int mt = 0; mt < NMT; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
 #pragma unroll
-            for (int mt = 0; mt < 4; mt++)
+            for (int mt = 0; mt < NMT; mt++)
 #pragma unroll
                 for (int nt = 0; nt < 2; nt++)
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt][kk], acc[mt][nt], 0, 0, 0);
         }
     };
-    auto store_a = [&](const u32x4 (&av)[4], int buf) {
+    auto store_a = [&](auto nmt_c, const u32x4 (&av)[4], int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) *(u32x4*)&sm.a[buf][(ar0 + 32 * i) * LDSB + 8 * ac] = av[i];
+        for (int i = 0; i < decltype(nmt_c)::value; i++) *(u32x4*)&sm.a[buf][(ar0 + 32 * i) * LDSB + 8 * ac] = av[i];
     };
-    auto load_a = [&](int k, u32x4 (&av)[4]) {
+    auto load_a = [&](auto nmt_c, int k, u32x4 (&av)[4]) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) av[i] = *(const u32x4*)(apt[i] + k * BK);
+        for (int i = 0; i < decltype(nmt_c)::value; i++) av[i] = *(const u32x4*)(apt[i] + k * BK);
     };
+    using All = std::integral_constant<int, 4>;
 
     if constexpr (C::Q4) {
         // ---- 4-bit weights: the raw codes (32 bytes per row and step) go to
@@ -305,39 +312,47 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
                 for (int kk = 0; kk < 4; kk++) bf[nt][kk] = __builtin_bit_cast(f16x8, q4_word_to_f16x8(codes[kk], s2, b2));
             }
         };
-        Stage ring[R];
-        u32x4 c0[2];
-        load_b(0, c0);
+        auto main_loop = [&](auto nmt_c) {
+            Stage ring[R];
+            u32x4 c0[2];
+            load_b(0, c0);
 #pragma unroll
-        for (int j = 0; j < R - 1; j++) {
-            load_a(j, ring[j].a);
-            load_b(min(j + 1, C::NK - 1), ring[j].b);
-        }
-        store_b(c0, 0);
-        __syncthreads();  // staged scales, biases, routing weights; codes of step 0
-        store_a(ring[0].a, 0);
-        store_b(ring[0].b, 1);
-        f16x8 bfr[2][2][4];
-        dequant(0, 0, bfr[0]);
-        __syncthreads();
-#pragma unroll 1
-        for (int k0 = 0; k0 < C::NK; k0 += R) {
-#pragma unroll
-            for (int j = 0; j < R; j++) {
-                const int k = k0 + j;
-                Stage& nx = ring[(j + R - 1) % R];
-                load_a(min(k + R - 1, C::NK - 1), nx.a);
-                load_b(min(k + R, C::NK - 1), nx.b);
-                // keep the loads here: the scheduler would otherwise sink them
-                // towards their first use and undo the prefetch
-                __builtin_amdgcn_sched_barrier(0);
-                dequant(min(k + 1, C::NK - 1), (j + 1) % QBUF, bfr[(j + 1) & 1]);
-                mfma_step(j & 1, bfr[j & 1]);
-                store_a(ring[(j + 1) % R].a, (j + 1) & 1);
-                store_b(ring[(j + 1) % R].b, (j + 2) % QBUF);
-                __syncthreads();
+            for (int j = 0; j < R - 1; j++) {
+                load_a(nmt_c, j, ring[j].a);
+                load_b(min(j + 1, C::NK - 1), ring[j].b);
             }
-        }
+            store_b(c0, 0);
+            __syncthreads();  // staged scales, biases, routing weights; codes of step 0
+            store_a(nmt_c, ring[0].a, 0);
+            store_b(ring[0].b, 1);
+            f16x8 bfr[2][2][4];
+            dequant(0, 0, bfr[0]);
+            __syncthreads();
+#pragma unroll 1
+            for (int k0 = 0; k0 < C::NK; k0 += R) {
+#pragma unroll
+                for (int j = 0; j < R; j++) {
+                    const int k = k0 + j;
+                    Stage& nx = ring[(j + R - 1) % R];
+                    load_a(nmt_c, min(k + R - 1, C::NK - 1), nx.a);
+                    load_b(min(k + R, C::NK - 1), nx.b);
+                    // keep the loads here: the scheduler would otherwise sink them
+                    // towards their first use and undo the prefetch
+                    __builtin_amdgcn_sched_barrier(0);
+                    dequant(min(k + 1, C::NK - 1), (j + 1) % QBUF, bfr[(j + 1) & 1]);
+                    mfma_step(nmt_c, j & 1, bfr[j & 1]);
+                    store_a(nmt_c, ring[(j + 1) % R].a, (j + 1) & 1);
+                    store_b(ring[(j + 1) % R].b, (j + 2) % QBUF);
+                    __syncthreads();
+                }
+            }
+        };
+        // routed tiles hold 1 .. 128 rows
+        const int nmt = (rows + 31) >> 5;
+        if (nmt >= 4) main_loop(All{});
+        else if (nmt == 3) main_loop(std::integral_constant<int, 3>{});
+        else if (nmt == 2) main_loop(std::integral_constant<int, 2>{});
+        else main_loop(std::integral_constant<int, 1>{});
     } else {
         // ---- 16-bit weights: converted to fp16 (perm8) on the way into LDS,
         // read back as MFMA operands.  Loads run one step ahead.
@@ -345,14 +360,14 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
         static_assert(C::NK % R == 0, "K steps must be a multiple of the ring size");
         struct Stage { u32x4 a[4]; u32x4 b[2][4]; };
         auto load = [&](int k, Stage& st) {
-            load_a(k, st.a);
+            load_a(All{}, k, st.a);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
                 for (int w = 0; w < 4; w++) st.b[i][w] = bpt[i][8 * k + w];
         };
         auto store = [&](const Stage& st, int buf) {
-            store_a(st.a, buf);
+            store_a(All{}, st.a, buf);
 #pragma unroll
             for (int i = 0; i < 2; i++) {
                 f16* dst = &sm.b[buf][(br0 + 128 * i) * LDSB + 32 * bh];
@@ -384,7 +399,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
                 __builtin_amdgcn_sched_barrier(0);
                 f16x8 bf[2][4];
                 read_b(j & 1, bf);
-                mfma_step(j & 1, bf);
+                mfma_step(All{}, j & 1, bf);
                 store(ring[(j + 1) % R], (j + 1) & 1);
                 __syncthreads();
             }
