@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every traced kernel (stderr)")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of a HIP graph")
+    ap.add_argument("--flush", choices=["read", "write"], default="read",
+                    help="how single-layer workloads evict the caches between calls: read 1 GiB (leaves clean "
+                         "lines) or write 1 GiB (leaves the infinity cache full of dirty lines to write back)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (calibrates PMC byte counters)")
     args = ap.parse_args()
@@ -169,6 +172,10 @@ def main():
     ws_ = [torch.empty((T, 8), dtype=torch.float32, device=dev) for _ in range(nlayers)]
     wspace = moe.alloc_workspace(T, dev)
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if wl["flush"] else None
+    if flush_buf is not None:
+        flush_buf.fill_(1)
+        flush_words = flush_buf.view(torch.int64)
+        flush_sink = torch.empty((), dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
 
     def call(l, trace=None):
@@ -194,7 +201,10 @@ def main():
             step_ms = []
             se, ee = hip.event(), hip.event()
             for s in range(nsteps):
-                flush_buf.fill_(s & 0xFF)
+                if args.flush == "write":
+                    flush_buf.fill_(s & 0xFF)
+                else:
+                    flush_sink.copy_(flush_words.amax(), non_blocking=True)
                 torch.cuda.synchronize()
                 hip.record(se, stream)
                 call(0, moe.Trace(kernel, *ev[s]) if kernel is not None else None)

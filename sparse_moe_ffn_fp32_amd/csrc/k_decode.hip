@@ -33,9 +33,10 @@
 //          the K order of the codes.
 //   route  one block: softmax/top-8/renormalise per token, sgate, the
 //          distinct experts with their (token, rank) pairs.
-//   C      routed gate/up + SwiGLU, 32 features x one distinct expert per
-//          block with K split in four; extra blocks: the shared expert's down
-//          projection.
+//   C      routed gate/up + SwiGLU: 256 persistent workgroups stream the
+//          (distinct expert, 128 features) items, each wave a full K sweep
+//          of 16 gate and 16 up rows with a deep load ring; extra blocks:
+//          the shared expert's down projection.
 //   D      routed down projection of 16 output rows per block over 8 distinct
 //          experts (one per wave), fp32 partials per pair.
 //   combine  y = sum_{r=0..7} w_r * partial_r + sgate * shexp  in fixed order
@@ -61,6 +62,18 @@ __device__ __forceinline__ f32x4 mfma16_f16(const f16x8& a, const f16x8& b, f32x
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// Wave-uniform read of memory that no kernel of the launch writes, through
+// the constant address space so it becomes a scalar load.
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// Raw buffer resource over an array of at most 2 GiB (no stride, bounds
+// check at 2^31 - 1 bytes); offsets are bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
+}
 
 // One u32 of eight nibbles -> eight codes c + q in perm8 order; `magic`
 // holds the bit pattern of c in both 16-bit halves (0x4300 for bf16 128,
@@ -313,86 +326,206 @@ __global__ void __launch_bounds__(1024) k_dec_route(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ stage C
-// One wave, one token tile: 16 features (rows `row`) of gate and up over 8
-// quantisation groups starting at gq8, for the token slots whose pair ids are
-// pair_of(slot) (slot < cnt <= 16).  Partial sums of token slot 4kq + v and
-// feature n go to red_g / red_u.
-template <class PairOf>
-__device__ __forceinline__ void gu_tile(const DecodeArgs& a, size_t row, int gq8, int cnt, PairOf pair_of, int lane,
-                                        float (*red_g)[16], float (*red_u)[16]) {
-    const int n = lane & 15, kq = lane >> 4;
-    const size_t sbase = row * (D / G) + gq8;
-    const u32x4 gsv = *(const u32x4*)(a.gs + sbase), gbv = *(const u32x4*)(a.gb + sbase);
-    const u32x4 usv = *(const u32x4*)(a.us + sbase), ubv = *(const u32x4*)(a.ub + sbase);
-    const uint32_t* gw_p = a.gq + row * (D / 8) + 8 * gq8 + 2 * kq;
-    const uint32_t* uw_p = a.uq + row * (D / 8) + 8 * gq8 + 2 * kq;
-    const int tk = a.T * K - 1;
-    const uint16_t* xrow = a.xp + (size_t)(min(max(pair_of(n < cnt ? n : 0), 0), tk) >> 3) * D;
-    u32x2 gw[8], uw[8];
-    u32x4 xa[8][2];
-#pragma unroll
-    for (int g = 0; g < 8; g++) {  // loads in the order they are consumed
-        gw[g] = *(const u32x2*)(gw_p + 8 * g);
-        uw[g] = *(const u32x2*)(uw_p + 8 * g);
-        const int wd = 8 * (gq8 + g) + 2 * kq;
-        xa[g][0] = *(const u32x4*)(xrow + 8 * wd);
-        xa[g][1] = *(const u32x4*)(xrow + 8 * wd + 8);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
-    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
-    f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int g = 0; g < 8; g++) {
-        const float s_g = bf16_at(gsv, g), s_u = bf16_at(usv, g);
-        const float c_g = bf16_at(gbv, g) - 128.0f * s_g, c_u = bf16_at(ubv, g) - 128.0f * s_u;
-        const bf16x8 a0 = as_bf16x8(xa[g][0]), a1 = as_bf16x8(xa[g][1]);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 ag = mfma16_bf16(a0, as_bf16x8(nibbles_to_codes(gw[g][0], 0x43004300u)), z);
-        ag = mfma16_bf16(a1, as_bf16x8(nibbles_to_codes(gw[g][1], 0x43004300u)), ag);
-        f32x4 au = mfma16_bf16(a0, as_bf16x8(nibbles_to_codes(uw[g][0], 0x43004300u)), z);
-        au = mfma16_bf16(a1, as_bf16x8(nibbles_to_codes(uw[g][1], 0x43004300u)), au);
-        f32x4 xs = mfma16_bf16(a0, as_bf16x8(ones), z);
-        xs = mfma16_bf16(a1, as_bf16x8(ones), xs);
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-            og[v] += s_g * ag[v] + c_g * xs[v];
-            ou[v] += s_u * au[v] + c_u * xs[v];
-        }
-    }
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-        red_g[4 * kq + v][n] = og[v];
-        red_u[4 * kq + v][n] = ou[v];
-    }
-}
+// Routed gate/up, streamed.  The work items are (distinct expert, 128
+// features); GU_BLOCKS persistent workgroups (one per compute unit) take
+// items bid, bid + GU_BLOCKS, ... in turn.  Wave w owns the gate and up rows
+// of features 16w .. 16w + 15 of an item over the whole K, one quantisation
+// group (64 inputs) per step, so no partial sums cross waves.  An item's
+// token tile (up to 16 tokens) sits in LDS; each wave keeps the codes of the
+// next GU_RING groups in flight and loads the next item's token tile while
+// it streams the current one, so a workgroup never starts an item with an
+// empty pipeline (a fresh block would queue its first loads behind the
+// compute unit's outstanding ones).
+constexpr int GU_FEAT = 128;                 // features per item
+constexpr int GU_NCH = F / GU_FEAT;          // items per expert
+constexpr int GU_RING = 16;                  // groups of codes in flight per wave
+constexpr int GU_BLOCKS = 256;               // persistent routed workgroups
+constexpr int GU_ITEMS = E * GU_NCH / GU_BLOCKS;  // at most this many items each
+constexpr int XS_STRIDE = D + 8;             // bf16 per staged x row (16-byte pad)
+struct GuSmem {
+    uint16_t xs[16][XS_STRIDE];              // token tile of x, perm8 K order
+    int pairs[GU_ITEMS][16];                 // first-tile pair ids of the workgroup's items
+    int info[GU_ITEMS][4];                   // expert, token count, first pair of each item
+    int tile_pairs[16];                      // pair ids of a later tile (more than 16 tokens)
+};
 
-// Sum the four K quarters (in order), SwiGLU, store h (perm8 order) for the
-// tile's token slots; 32 features starting at f0.
-template <class PairOf>
-__device__ __forceinline__ void gu_finish(const DecodeArgs& a, float (*red)[4][2][16][16], int f0, int cnt,
-                                          PairOf pair_of) {
-    const int tid = threadIdx.x;
-    if (tid < cnt * 32) {
-        const int slot = tid >> 5, fl = tid & 31;
-        const int g2 = fl >> 4, c = fl & 15;
-        float gg = 0.f, uu = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            gg += red[0][q][g2][slot][c];
-            uu += red[1][q][g2][slot][c];
+__device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, kq = lane >> 4;
+    const int T = a.T;
+    const int tk = T * K - 1;
+    const int n_items = min(a.nuniq[0], E) * GU_NCH;
+    constexpr int NGRP = D / G;  // 32
+    static_assert(NGRP % GU_RING == 0 && GU_RING % 8 == 0, "ring period: whole scale vectors");
+
+    // ---- the workgroup's item descriptors and first-tile pair ids
+    if (tid < GU_ITEMS * 16) {
+        const int j = tid >> 4, s = tid & 15, it = bid + j * GU_BLOCKS;
+        if (it < n_items) {
+            const int u = it / GU_NCH;
+            const int cnt = min(max(a.ucnt[u], 1), T);
+            const int off = min(max(a.uoff[u], 0), T * K - cnt);
+            sm.pairs[j][s] = min(max(a.pairs[off + min(s, min(16, cnt) - 1)], 0), tk);
+            if (s == 0) {
+                sm.info[j][0] = a.uexp[u] & (E - 1);
+                sm.info[j][1] = cnt;
+                sm.info[j][2] = off;
+            }
         }
-        const int f = f0 + fl;
-        const int pc = (f & ~7) | perm8_pos(f & 7);
-        const f16 hv = (f16)(silu_f32(gg) * uu);
-        a.h[(size_t)min(max(pair_of(slot), 0), a.T * K - 1) * F + pc] = __builtin_bit_cast(uint16_t, hv);
+    }
+    __syncthreads();
+    if (bid >= n_items) return;
+
+    // x rows of a token tile: 16 rows x 256 pieces of 16 bytes; waves 4h ..
+    // 4h+3 take rows h + 2i (wave-uniform), piece tid % 256; rows >= tc unused
+    const int xc = tid & 255, xr0 = tid >> 8;
+    auto load_x = [&](const int* tp, int tc, u32x4 (&xv)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int r = xr0 + 2 * i;
+            if (r < tc) {
+                const int pr = __builtin_amdgcn_readfirstlane(tp[r]);
+                xv[i] = *(const u32x4*)(a.xp + (size_t)(pr >> 3) * D + 8 * xc);
+            }
+        }
+    };
+    auto store_x = [&](const u32x4 (&xv)[8], int tc) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int r = xr0 + 2 * i;
+            if (r < tc) *(u32x4*)&sm.xs[r][8 * xc] = xv[i];
+        }
+    };
+    u32x4 xn[8];
+    load_x(sm.pairs[0], min(16, sm.info[0][1]), xn);
+    store_x(xn, min(16, sm.info[0][1]));
+    __syncthreads();
+
+    const __amdgpu_buffer_rsrc_t rgq = buffer_rsrc(a.gq), ruq = buffer_rsrc(a.uq);
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+#pragma unroll 1
+    for (int j = 0; j < GU_ITEMS; j++) {
+        const int it = bid + j * GU_BLOCKS;
+        const int e = __builtin_amdgcn_readfirstlane(sm.info[j][0]);
+        const int cnt = __builtin_amdgcn_readfirstlane(sm.info[j][1]);
+        const int off = __builtin_amdgcn_readfirstlane(sm.info[j][2]);
+        const bool has_next = j + 1 < GU_ITEMS && it + GU_BLOCKS < n_items;
+        const int f = (it % GU_NCH) * GU_FEAT + 16 * wave + n;  // this lane's feature (B column n)
+        // lane (n, kq) takes K [64g + 16kq, +16) of group g: two words of
+        // codes.  Gate and up share one row layout: one byte offset serves
+        // both; buffer loads keep the base in scalar registers.
+        const uint32_t row = (uint32_t)(e * F + f);
+        const uint32_t qo = (row * (D / 8) + 2 * kq) * 4;
+        auto ld_codes = [&](__amdgpu_buffer_rsrc_t r, int g) {
+            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, qo, 32 * g, 0));
+        };
+        // the four lanes of row n (kq = 0..3, one per 16-lane row) each load
+        // one of the row's gate scales, gate biases, up scales, up biases
+        // (eight groups per load) and swap them across lane rows when used
+        const uint16_t* sarr = kq == 0 ? a.gs : kq == 1 ? a.gb : kq == 2 ? a.us : a.ub;
+        const uint16_t* sptr = sarr + row * (D / G);
+        auto ld_sc = [&](int b) { return *(const u32x4*)(sptr + 8 * b); };
+
+#pragma unroll 1
+        for (int m0 = 0; m0 < cnt; m0 += 16) {
+            const int tc = min(16, cnt - m0);
+            const int* tp = m0 == 0 ? sm.pairs[j] : sm.tile_pairs;
+            if (m0 > 0) {  // a later tile of an expert with more than 16 tokens
+                __syncthreads();
+                if (tid < 16) sm.tile_pairs[tid] = min(max(a.pairs[off + m0 + min(tid, tc - 1)], 0), tk);
+                __syncthreads();
+                u32x4 xv[8];
+                load_x(sm.tile_pairs, tc, xv);
+                store_x(xv, tc);
+                __syncthreads();
+            }
+            // ---- codes of groups 0 .. GU_RING-1 and the first scale vectors,
+            // then (last tile) the next item's token tile behind them
+            u32x4 sc0 = ld_sc(0), sc1 = ld_sc(1);
+            u32x2 gw[GU_RING], uw[GU_RING];
+#pragma unroll
+            for (int g = 0; g < GU_RING; g++) {
+                gw[g] = ld_codes(rgq, g);
+                uw[g] = ld_codes(ruq, g);
+            }
+            if (m0 + 16 >= cnt && has_next) load_x(sm.pairs[j + 1], min(16, sm.info[j + 1][1]), xn);
+
+            const uint16_t* xrow = &sm.xs[min(n, tc - 1)][16 * kq];  // A row: token slot n
+            f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
+            // bodies of GU_RING groups: ring slot g % GU_RING holds group g
+            // and is refilled with group g + GU_RING (the last body re-reads
+            // group 31); the scale vectors of the next body load at its start
+#pragma unroll 1
+            for (int gb = 0; gb < NGRP / GU_RING; gb++) {
+                const int nb = min(gb + 1, NGRP / GU_RING - 1);
+                const u32x4 scn0 = ld_sc(2 * nb), scn1 = ld_sc(2 * nb + 1);
+                uint32_t sgs = 0, sgb = 0, sus = 0, sub = 0;
+#pragma unroll
+                for (int gi = 0; gi < GU_RING; gi++) {
+                    const int g = GU_RING * gb + gi;
+                    // expand the slot's codes first, then refill the slot: the
+                    // refill can take the slot's own registers, so the loop
+                    // back-edge needs no copies (a copy would wait for its
+                    // load and drain the ring)
+                    const u32x4 bg0 = nibbles_to_codes(gw[gi][0], 0x43004300u), bg1 = nibbles_to_codes(gw[gi][1], 0x43004300u);
+                    const u32x4 bu0 = nibbles_to_codes(uw[gi][0], 0x43004300u), bu1 = nibbles_to_codes(uw[gi][1], 0x43004300u);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int gn = min(g + GU_RING, NGRP - 1);
+                    gw[gi] = ld_codes(rgq, gn);
+                    uw[gi] = ld_codes(ruq, gn);
+                    const bf16x8 a0 = as_bf16x8(*(const u32x4*)(xrow + 64 * g));
+                    const bf16x8 a1 = as_bf16x8(*(const u32x4*)(xrow + 64 * g + 8));
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    f32x4 ag = mfma16_bf16(a0, as_bf16x8(bg0), z);
+                    ag = mfma16_bf16(a1, as_bf16x8(bg1), ag);
+                    f32x4 au = mfma16_bf16(a0, as_bf16x8(bu0), z);
+                    au = mfma16_bf16(a1, as_bf16x8(bu1), au);
+                    f32x4 xsum = mfma16_bf16(a0, as_bf16x8(ones), z);
+                    xsum = mfma16_bf16(a1, as_bf16x8(ones), xsum);
+                    const int gs8 = gi & 7;
+                    if ((gs8 & 1) == 0) {
+                        // dword gs8/2 of the four arrays: after the 16-lane swap
+                        // p0 holds the even lane row's array (kq & ~1), p1 the
+                        // odd one's; the 32-lane swaps then give rows 0/1, 2/3
+                        const uint32_t d = (gi < 8 ? sc0 : sc1)[gs8 >> 1];
+                        const auto p = __builtin_amdgcn_permlane16_swap(d, d, false, false);
+                        const auto q0 = __builtin_amdgcn_permlane32_swap((uint32_t)p[0], (uint32_t)p[0], false, false);
+                        const auto q1 = __builtin_amdgcn_permlane32_swap((uint32_t)p[1], (uint32_t)p[1], false, false);
+                        sgs = q0[0]; sus = q0[1]; sgb = q1[0]; sub = q1[1];
+                    }
+                    const bool hi = gs8 & 1;
+                    const float s_g = __uint_as_float(hi ? (sgs & 0xffff0000u) : (sgs << 16));
+                    const float s_u = __uint_as_float(hi ? (sus & 0xffff0000u) : (sus << 16));
+                    const float c_g = __uint_as_float(hi ? (sgb & 0xffff0000u) : (sgb << 16)) - 128.0f * s_g;
+                    const float c_u = __uint_as_float(hi ? (sub & 0xffff0000u) : (sub << 16)) - 128.0f * s_u;
+#pragma unroll
+                    for (int v = 0; v < 4; v++) {
+                        og[v] += s_g * ag[v] + c_g * xsum[v];
+                        ou[v] += s_u * au[v] + c_u * xsum[v];
+                    }
+                }
+                sc0 = scn0;
+                sc1 = scn1;
+            }
+            // ---- SwiGLU for token slots 4kq + v, feature f (perm8 position)
+            const int pc = (f & ~7) | perm8_pos(f & 7);
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int slot = 4 * kq + v;
+                if (slot < tc) a.h[(size_t)tp[slot] * F + pc] = __builtin_bit_cast(uint16_t, (f16)(silu_f32(og[v]) * ou[v]));
+            }
+        }
+        if (!has_next) break;
+        __syncthreads();  // every wave is done reading this item's token tile
+        store_x(xn, min(16, sm.info[j + 1][1]));
+        __syncthreads();
     }
 }
 
 // Blocks [0, n_sd) are the shared expert's down projection (first, so they
 // start at once), the routed blocks follow.
 __global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_sd) {
-    __shared__ float red[2][4][2][16][16];  // [gate/up][K quarter][feature group][token slot][feature]
-    __shared__ int tile_pairs[16];
+    __shared__ __attribute__((aligned(16))) char smem[sizeof(GuSmem)];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
@@ -400,7 +533,7 @@ __global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_sd) {
         // ---- shared expert down: ys[t, o0+n] = sum_j Wsd[o0+n, j] hs[t, j],
         // hs split into bf16 hi + lo; wave w takes K in [64w, 64w+64)
         if (!a.sg) return;
-        float(*sred)[16][16] = (float(*)[16][16])red;  // [8][16][16]
+        float(*sred)[16][16] = (float(*)[16][16])smem;  // [8][16][16]
         const int o0 = 16 * blockIdx.x;
         const int k0 = 64 * wave + 8 * kq;
         const uint16_t* wrow = a.sd + (size_t)(o0 + n) * FS + k0;
@@ -440,27 +573,7 @@ __global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_sd) {
         }
         return;
     }
-    // ---- routed gate/up: 32 features (2 groups of 16) x 4 K quarters
-    const int fg = wave & 1, kq4 = wave >> 1;
-    const int bid = blockIdx.x - n_sd;
-    const int chunk = bid % (F / 32);
-    const int f0 = 32 * chunk;
-    const size_t frow = f0 + 16 * fg + n;
-    const int u = bid / (F / 32);
-    if (u >= min(a.nuniq[0], E)) return;
-    const int e = a.uexp[u] & (E - 1), cnt = min(max(a.ucnt[u], 1), T);
-    const int off = min(max(a.uoff[u], 0), T * K - cnt);
-#pragma unroll 1
-    for (int m0 = 0; m0 < cnt; m0 += 16) {
-        const int tc = min(16, cnt - m0);
-        if (tid < 16) tile_pairs[tid] = a.pairs[off + m0 + min(tid, tc - 1)];
-        __syncthreads();
-        auto pair_of = [&](int slot) { return tile_pairs[slot]; };
-        gu_tile(a, (size_t)e * F + frow, 8 * kq4, tc, pair_of, lane, red[0][kq4][fg], red[1][kq4][fg]);
-        __syncthreads();
-        gu_finish(a, red, f0, tc, pair_of);
-        __syncthreads();
-    }
+    gu_stream(a, (int)blockIdx.x - n_sd, *reinterpret_cast<GuSmem*>(smem));
 }
 
 // ------------------------------------------------------------------ stage D
@@ -578,7 +691,7 @@ size_t decode_workspace_bytes(int T, DecodeLayout* L) {
 template <int NMT>
 static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
     const int n_items = a.T * K < E ? a.T * K : E;
-    const int n_gu = n_items * (F / 32);
+    const int n_gu = GU_BLOCKS;
     tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<NMT>, dim3(N_ROUTER_BLK + N_SGU_BLK + 1), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(k_dec_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
