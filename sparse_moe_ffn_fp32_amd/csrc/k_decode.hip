@@ -69,11 +69,6 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
     return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
-// Raw buffer resource over an array of at most 2 GiB (no stride, bounds
-// check at 2^31 - 1 bytes); offsets are bytes.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
-}
 
 // One u32 of eight nibbles -> eight codes c + q in perm8 order; `magic`
 // holds the bit pattern of c in both 16-bit halves (0x4300 for bf16 128,

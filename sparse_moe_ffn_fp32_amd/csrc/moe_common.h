@@ -75,6 +75,12 @@ __device__ __forceinline__ u32x4 q4_word_to_f16x8(uint32_t w, f16x2 s2, f16x2 b2
     return o;
 }
 
+// Raw buffer resource over an array of at most 2 GiB (no stride, bounds
+// check at 2^31 - 1 bytes); offsets are bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+
 // silu(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (about
 // 1 ulp each): every caller rounds the result to fp16 or feeds an fp32 dot
 // product, far coarser than the few-ulp difference from an IEEE division.

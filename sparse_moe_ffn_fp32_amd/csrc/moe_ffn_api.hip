@@ -19,7 +19,7 @@ struct Layout {
 Layout layout(int64_t T) {
     const size_t N = (size_t)T * K;
     const int nblk = sort_blocks((int)N);
-    const size_t max_tiles = (N + gemm_bm() - 1) / gemm_bm() + E;
+    const size_t max_tiles = (N + 127) / 128 + E;  // tiles of at least 128 rows
     Layout L{};
     size_t o = 0;
     L.wr2 = o;        o += up((size_t)2 * E * D * 2);
@@ -110,7 +110,7 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     chk(launch_router_gemm(xh, wr2, router->bias, logits, sh ? sh->gate : nullptr, sh ? sh->up : nullptr,
                            (uint16_t*)at(L.hs), T, tr, s));
     chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, T, s));
-    chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(), s));
+    chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(T), s));
     PrefillGemmParams p{};
     p.xh = xh;
     p.h = (uint16_t*)at(L.h);

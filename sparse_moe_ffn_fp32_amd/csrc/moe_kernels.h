@@ -53,7 +53,7 @@ struct PrefillGemmParams {
     uint16_t* y;
     int T;
 };
-int gemm_bm();
+int gemm_bm(int T);  // rows per routed tile for a prefill pass of T tokens
 hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s);
 // router logits, and the shared expert's gate/up + SwiGLU into hs when sh_gate != nullptr
 hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits,
