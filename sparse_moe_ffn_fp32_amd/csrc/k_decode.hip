@@ -52,7 +52,6 @@ namespace moe {
 constexpr int N_ROUTER_BLK = E / 16;
 constexpr int N_SGU_BLK = FS / 16;
 constexpr int N_SDOWN_BLK = D / 16;
-constexpr int N_ROW_TILES = D / 16;
 
 __device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8& a, const bf16x8& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -372,24 +371,22 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     if (bid >= n_items) return;
 
     // x rows of a token tile: 16 rows x 256 pieces of 16 bytes; waves 4h ..
-    // 4h+3 take rows h + 2i (wave-uniform), piece tid % 256; rows >= tc unused
+    // 4h+3 take rows h + 2i (wave-uniform), piece tid % 256.  Every row is
+    // loaded and stored (rows >= tc repeat the last token; no lane reads
+    // them): a load under a lane-dependent branch makes the compiler wait
+    // for it at once.
     const int xc = tid & 255, xr0 = tid >> 8;
     auto load_x = [&](const int* tp, int tc, u32x4 (&xv)[8]) {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int r = xr0 + 2 * i;
-            if (r < tc) {
-                const int pr = __builtin_amdgcn_readfirstlane(tp[r]);
-                xv[i] = *(const u32x4*)(a.xp + (size_t)(pr >> 3) * D + 8 * xc);
-            }
+            const int pr = __builtin_amdgcn_readfirstlane(tp[min(xr0 + 2 * i, tc - 1)]);
+            xv[i] = *(const u32x4*)(a.xp + (size_t)(pr >> 3) * D + 8 * xc);
         }
     };
     auto store_x = [&](const u32x4 (&xv)[8], int tc) {
+        (void)tc;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int r = xr0 + 2 * i;
-            if (r < tc) *(u32x4*)&sm.xs[r][8 * xc] = xv[i];
-        }
+        for (int i = 0; i < 8; i++) *(u32x4*)&sm.xs[xr0 + 2 * i][8 * xc] = xv[i];
     };
     u32x4 xn[8];
     load_x(sm.pairs[0], min(16, sm.info[0][1]), xn);
@@ -572,75 +569,182 @@ __global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_sd) {
 }
 
 // ------------------------------------------------------------------ stage D
-// Loads of one (expert, token tile) for 16 output rows: scales, biases,
-// codes, and h rows of the tile's tokens.
-struct DownLoads {
-    u32x4 sv, bv;
-    u32x2 wv[8];
-    u32x4 ha[8][2];
+// Routed down, streamed like stage C.  The work units are (distinct expert,
+// 128 output rows, token tile of up to 16 tokens); DN_BLOCKS persistent
+// workgroups each take a contiguous run of (expert, 128 rows) items, so
+// consecutive units mostly share an expert and its token tile.  Wave w owns
+// output rows 16w .. 16w + 15 of a unit over K = F (eight quantisation
+// groups); the codes of the next DN_RING groups (two units) stay in flight
+// across unit boundaries, and the next unit's token tile loads while the
+// current one computes.  Partials per (pair, output) in fp32.
+constexpr int DN_ROWS = 128;                        // output rows per item
+constexpr int DN_NCH = D / DN_ROWS;                 // items per expert
+constexpr int DN_BLOCKS = 256;                      // persistent workgroups
+constexpr int DN_ITEMS = E * DN_NCH / DN_BLOCKS;    // at most this many items each
+constexpr int DN_UNITS = DN_ITEMS * 4;              // token tiles of 16: at most 64 tokens per expert
+constexpr int DN_RING = 16;                         // groups of codes in flight per wave
+constexpr int HS_STRIDE = F + 8;                    // fp16 per staged h row (16-byte pad)
+struct DnSmem {
+    uint16_t hs[2][16][HS_STRIDE];  // token tiles of h (fp16, perm8 order), two buffers
+    int info[DN_ITEMS][4];          // expert, token count, first pair of each item
+    int unit[DN_UNITS][8];          // expert, first output row, tokens in the tile, h buffer, first pair
+    int pairs[DN_UNITS][16];        // pair ids of each unit's token slots
+    int n_units;
 };
 
-__device__ __forceinline__ void down_load(const DecodeArgs& a, size_t row, int pair, int lane, DownLoads& L) {
-    const int kq = lane >> 4;
-    L.sv = *(const u32x4*)(a.ds + row * (F / G));
-    L.bv = *(const u32x4*)(a.db + row * (F / G));
-    const uint16_t* hrow = a.h + (size_t)min(max(pair, 0), a.T * K - 1) * F;
-#pragma unroll
-    for (int g = 0; g < 8; g++) {
-        L.wv[g] = *(const u32x2*)(a.dq + row * (F / 8) + 8 * g + 2 * kq);
-        const int wd = 8 * g + 2 * kq;
-        L.ha[g][0] = *(const u32x4*)(hrow + 8 * wd);
-        L.ha[g][1] = *(const u32x4*)(hrow + 8 * wd + 8);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
-}
-
-// Down projection of the loaded tile: row n of the lane, token slots 4kq+v.
-__device__ __forceinline__ f32x4 down_compute(const DownLoads& L) {
-    const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int g = 0; g < 8; g++) {
-        const float s = bf16_at(L.sv, g);
-        const float c = bf16_at(L.bv, g) - 1024.0f * s;
-        const f16x8 a0 = as_f16x8(L.ha[g][0]), a1 = as_f16x8(L.ha[g][1]);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 acc = mfma16_f16(a0, as_f16x8(nibbles_to_codes(L.wv[g][0], 0x64006400u)), z);
-        acc = mfma16_f16(a1, as_f16x8(nibbles_to_codes(L.wv[g][1], 0x64006400u)), acc);
-        f32x4 hsum = mfma16_f16(a0, as_f16x8(ones), z);
-        hsum = mfma16_f16(a1, as_f16x8(ones), hsum);
-#pragma unroll
-        for (int v = 0; v < 4; v++) o[v] += s * acc[v] + c * hsum[v];
-    }
-    return o;
-}
-
-// 16 output rows per block.  T <= 4: the 8T (token, rank) pairs are the
-// work items, taken by the 8 waves in turn, results kept in LDS, then the
-// combine.  T > 4: block (row tile, chunk) takes distinct experts 8*chunk..+7,
-// one per wave, and writes fp32 partials per pair; k_dec_combine finishes.
 __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) DnSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
-    const int rt = blockIdx.x % N_ROW_TILES, ch = blockIdx.x / N_ROW_TILES;
-    const int o0 = 16 * rt;
     const int tk = T * K - 1;
     const int nu = min(max(a.nuniq[0], 0), min(T * K, E));
-    const int u = 8 * ch + wave;
-    if (u >= nu) return;
-    const int e = a.uexp[u] & (E - 1), cnt = min(max(a.ucnt[u], 1), T);
-    const int off = min(max(a.uoff[u], 0), T * K - cnt);
-#pragma unroll 1
-    for (int m0 = 0; m0 < cnt; m0 += 16) {
-        const int slot0 = m0 + n;
-        DownLoads L;
-        down_load(a, (size_t)e * D + o0 + n, a.pairs[off + (slot0 < cnt ? slot0 : m0)], lane, L);
-        const f32x4 o = down_compute(L);
+    const int n_items = nu * DN_NCH;
+    const int q = (n_items + DN_BLOCKS - 1) / DN_BLOCKS;  // <= DN_ITEMS
+    const int i0 = blockIdx.x * q, i1 = min(i0 + q, n_items);
+    if (i0 >= i1) return;
+
+    // ---- unit table: item descriptors in parallel, then units in order
+    if (tid < i1 - i0) {
+        const int u = (i0 + tid) / DN_NCH;
+        const int cnt = min(max(a.ucnt[u], 1), T);
+        sm.info[tid][0] = a.uexp[u] & (E - 1);
+        sm.info[tid][1] = cnt;
+        sm.info[tid][2] = min(max(a.uoff[u], 0), T * K - cnt);
+    }
+    __syncthreads();
+    if (tid == 0) {  // at most 16 items x 4 tiles, from LDS
+        int nun = 0, buf = 0, prev_u = -1;
+        for (int j = 0; j < i1 - i0; j++) {
+            const int u = (i0 + j) / DN_NCH, chunk = (i0 + j) % DN_NCH;
+            const int cnt = sm.info[j][1];
+            for (int m0 = 0; m0 < cnt && nun < DN_UNITS; m0 += 16) {
+                // a new token tile goes to the other buffer (consecutive items
+                // of one expert with one tile share it)
+                if (nun > 0 && (u != prev_u || m0 > 0 || cnt > 16)) buf ^= 1;
+                prev_u = u;
+                sm.unit[nun][0] = sm.info[j][0];
+                sm.unit[nun][1] = chunk * DN_ROWS;
+                sm.unit[nun][2] = min(16, cnt - m0);
+                sm.unit[nun][3] = buf;
+                sm.unit[nun][4] = sm.info[j][2] + m0;
+                nun++;
+            }
+        }
+        sm.n_units = nun;
+    }
+    __syncthreads();
+    const int n_units = sm.n_units;
+    // pair ids of every unit's token slots (slots >= tc repeat the last)
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int slot = m0 + 4 * kq + v;
-            if (slot < cnt) a.part[(size_t)min(max(a.pairs[off + slot], 0), tk) * D + o0 + n] = o[v];
+    for (int i = 0; i < DN_UNITS * 16 / 512; i++) {
+        const int t = tid + 512 * i, k = t >> 4, sl = t & 15;
+        if (k < n_units) sm.pairs[k][sl] = min(max(a.pairs[sm.unit[k][4] + min(sl, sm.unit[k][2] - 1)], 0), tk);
+    }
+    __syncthreads();
+
+    // h rows of a unit's token tile: 16 rows x 64 pieces of 16 bytes; thread
+    // tid takes piece tid % 64 of rows tid / 64 + 8i.  Every row is loaded
+    // and stored (slots >= tc repeat the last token; no lane reads them):
+    // a load under a lane-dependent branch makes the compiler wait for it
+    // at once.
+    const int hc = tid & 63, hr0 = tid >> 6;
+    auto load_h = [&](int k, u32x4 (&hv)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) hv[i] = *(const u32x4*)(a.h + (size_t)sm.pairs[k][hr0 + 8 * i] * F + 8 * hc);
+    };
+    auto store_h = [&](int k, const u32x4 (&hv)[2]) {
+        const int buf = sm.unit[k][3];
+#pragma unroll
+        for (int i = 0; i < 2; i++) *(u32x4*)&sm.hs[buf][hr0 + 8 * i][8 * hc] = hv[i];
+    };
+    // code and scale offsets of this lane's output row in unit k
+    const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(a.dq);
+    auto row_of = [&](int k) {
+        const int kk = min(k, n_units - 1);
+        return (uint32_t)(__builtin_amdgcn_readfirstlane(sm.unit[kk][0]) * D + __builtin_amdgcn_readfirstlane(sm.unit[kk][1])) +
+               (uint32_t)(16 * wave + n);
+    };
+    auto ld_codes = [&](uint32_t row, int g) {
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rdq, (row * (F / 8) + 2 * kq) * 4, 32 * g, 0));
+    };
+    auto ld_sc = [&](uint32_t row, u32x4& sv, u32x4& bv) {
+        sv = *(const u32x4*)(a.ds + (size_t)row * (F / G));
+        bv = *(const u32x4*)(a.db + (size_t)row * (F / G));
+    };
+
+    // ---- prologue: codes of units 0 and 1, scales of unit 0, token tile of unit 0
+    u32x2 ring[DN_RING];
+    {
+        const uint32_t r0 = row_of(0), r1 = row_of(1);
+#pragma unroll
+        for (int g = 0; g < 8; g++) ring[g] = ld_codes(r0, g);
+#pragma unroll
+        for (int g = 0; g < 8; g++) ring[8 + g] = ld_codes(r1, g);
+    }
+    u32x4 sv, bv;
+    ld_sc(row_of(0), sv, bv);
+    {
+        u32x4 hv[2];
+        load_h(0, hv);
+        store_h(0, hv);
+    }
+    __syncthreads();
+
+    const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
+    static_assert(DN_RING == 2 * (F / G), "the ring holds two units");
+    // bodies of two units: ring slot 8(k % 2) + g holds group g of unit k and
+    // is refilled with group g of unit k + 2 (past the last unit: its copy)
+#pragma unroll 1
+    for (int k0 = 0; k0 < n_units; k0 += 2) {
+#pragma unroll
+        for (int uu = 0; uu < 2; uu++) {
+            const int k = k0 + uu;
+            const bool active = k < n_units;
+            const int kc = min(k, n_units - 1);
+            const bool next_tile = k + 1 < n_units && sm.unit[k + 1][3] != sm.unit[kc][3];
+            u32x4 hv[2];
+            if (next_tile) load_h(k + 1, hv);
+            u32x4 svn, bvn;
+            ld_sc(row_of(k + 1), svn, bvn);
+            const uint32_t rn = row_of(k + 2);
+            const uint16_t* hrow = &sm.hs[sm.unit[kc][3]][min(n, sm.unit[kc][2] - 1)][16 * kq];  // A row: token slot n
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int g = 0; g < 8; g++) {
+                const int rs = 8 * uu + g;
+                // expand the slot's codes first, then refill the slot (no
+                // register copy across the loop back-edge)
+                const u32x4 b0 = nibbles_to_codes(ring[rs][0], 0x64006400u), b1 = nibbles_to_codes(ring[rs][1], 0x64006400u);
+                __builtin_amdgcn_sched_barrier(0);
+                ring[rs] = ld_codes(rn, g);
+                const f16x8 a0 = as_f16x8(*(const u32x4*)(hrow + 64 * g));
+                const f16x8 a1 = as_f16x8(*(const u32x4*)(hrow + 64 * g + 8));
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                f32x4 acc = mfma16_f16(a0, as_f16x8(b0), z);
+                acc = mfma16_f16(a1, as_f16x8(b1), acc);
+                f32x4 hsum = mfma16_f16(a0, as_f16x8(ones), z);
+                hsum = mfma16_f16(a1, as_f16x8(ones), hsum);
+                const float sg = bf16_at(sv, g);
+                const float cg = bf16_at(bv, g) - 1024.0f * sg;
+#pragma unroll
+                for (int v = 0; v < 4; v++) o[v] += sg * acc[v] + cg * hsum[v];
+            }
+            if (active) {
+                const int tc = sm.unit[k][2];
+                const int orow = sm.unit[k][1] + 16 * wave + n;
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    const int slot = 4 * kq + v;
+                    if (slot < tc) a.part[(size_t)sm.pairs[k][slot] * D + orow] = o[v];
+                }
+            }
+            sv = svn;
+            bv = bvn;
+            // the other buffer's last reader finished before the barrier that
+            // ended the previous unit; the barrier below publishes the tile
+            if (next_tile) store_h(k + 1, hv);
+            __syncthreads();
         }
     }
 }
@@ -685,14 +789,13 @@ size_t decode_workspace_bytes(int T, DecodeLayout* L) {
 
 template <int NMT>
 static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
-    const int n_items = a.T * K < E ? a.T * K : E;
     const int n_gu = GU_BLOCKS;
     tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<NMT>, dim3(N_ROUTER_BLK + N_SGU_BLK + 1), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(k_dec_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
     const int n_sd = a.sg ? N_SDOWN_BLK : 0;
     tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_sd + n_gu), dim3(512), 0, s, a, n_sd);
-    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(N_ROW_TILES * ((n_items + 7) / 8)), dim3(512), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(DN_BLOCKS), dim3(512), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_COMBINE, k_dec_combine, dim3((a.T * D + 255) / 256), dim3(256), 0, s, a);
 }
 
