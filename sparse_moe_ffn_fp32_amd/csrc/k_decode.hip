@@ -320,27 +320,31 @@ __global__ void __launch_bounds__(1024) k_dec_route(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ stage C
-// Routed gate/up, streamed.  The work items are (distinct expert, 128
-// features); GU_BLOCKS persistent workgroups (one per compute unit) take
-// items bid, bid + GU_BLOCKS, ... in turn.  Wave w owns the gate and up rows
-// of features 16w .. 16w + 15 of an item over the whole K, one quantisation
-// group (64 inputs) per step, so no partial sums cross waves.  An item's
-// token tile (up to 16 tokens) sits in LDS; each wave keeps the codes of the
-// next GU_RING groups in flight and loads the next item's token tile while
-// it streams the current one, so a workgroup never starts an item with an
-// empty pipeline (a fresh block would queue its first loads behind the
-// compute unit's outstanding ones).
+// Routed gate/up, streamed.  The work units are (distinct expert, 128
+// features, token tile of up to 16 tokens); GU_BLOCKS persistent workgroups
+// (one per compute unit) each take a contiguous run of (expert, 128
+// features) items, so consecutive units mostly share an expert and its
+// token tile (at 64 tokens every workgroup takes the four items of one
+// expert).  Wave w owns the gate and up rows of features 16w .. 16w + 15 of
+// a unit over the whole K, one quantisation group (64 inputs) per step, so
+// no partial sums cross waves.  The codes of the next GU_RING groups stay
+// in flight across unit boundaries.  A unit's token tile sits in LDS; a new
+// tile loads into registers during the last body of the unit before it and
+// is stored between two barriers (one LDS buffer, so that a routed
+// workgroup and a shared-down workgroup fit on one compute unit).
 constexpr int GU_FEAT = 128;                 // features per item
 constexpr int GU_NCH = F / GU_FEAT;          // items per expert
 constexpr int GU_RING = 16;                  // groups of codes in flight per wave
 constexpr int GU_BLOCKS = 256;               // persistent routed workgroups
 constexpr int GU_ITEMS = E * GU_NCH / GU_BLOCKS;  // at most this many items each
+constexpr int GU_UNITS = GU_ITEMS * 4;       // token tiles of 16: at most 64 tokens per expert
 constexpr int XS_STRIDE = D + 8;             // bf16 per staged x row (16-byte pad)
 struct GuSmem {
-    uint16_t xs[16][XS_STRIDE];              // token tile of x, perm8 K order
-    int pairs[GU_ITEMS][16];                 // first-tile pair ids of the workgroup's items
+    uint16_t xs[16][XS_STRIDE];              // token tile of x (bf16, perm8 K order)
     int info[GU_ITEMS][4];                   // expert, token count, first pair of each item
-    int tile_pairs[16];                      // pair ids of a later tile (more than 16 tokens)
+    int unit[GU_UNITS][8];                   // expert, first feature, tokens in the tile, tile parity, first pair
+    int pairs[GU_UNITS][16];                 // pair ids of each unit's token slots
+    int n_units;
 };
 
 __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& sm) {
@@ -348,27 +352,50 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
     const int tk = T * K - 1;
-    const int n_items = min(a.nuniq[0], E) * GU_NCH;
+    const int nu = min(max(a.nuniq[0], 0), min(T * K, E));
+    const int n_items = nu * GU_NCH;
+    const int q = (n_items + GU_BLOCKS - 1) / GU_BLOCKS;  // <= GU_ITEMS
+    const int i0 = bid * q, i1 = min(i0 + q, n_items);
+    if (i0 >= i1) return;
     constexpr int NGRP = D / G;  // 32
-    static_assert(NGRP % GU_RING == 0 && GU_RING % 8 == 0, "ring period: whole scale vectors");
+    static_assert(NGRP == 2 * GU_RING && GU_RING % 8 == 0, "two ring bodies per unit, whole scale vectors");
 
-    // ---- the workgroup's item descriptors and first-tile pair ids
-    if (tid < GU_ITEMS * 16) {
-        const int j = tid >> 4, s = tid & 15, it = bid + j * GU_BLOCKS;
-        if (it < n_items) {
-            const int u = it / GU_NCH;
-            const int cnt = min(max(a.ucnt[u], 1), T);
-            const int off = min(max(a.uoff[u], 0), T * K - cnt);
-            sm.pairs[j][s] = min(max(a.pairs[off + min(s, min(16, cnt) - 1)], 0), tk);
-            if (s == 0) {
-                sm.info[j][0] = a.uexp[u] & (E - 1);
-                sm.info[j][1] = cnt;
-                sm.info[j][2] = off;
-            }
-        }
+    // ---- unit table: item descriptors in parallel, then units in order
+    if (tid < i1 - i0) {
+        const int u = (i0 + tid) / GU_NCH;
+        const int cnt = min(max(a.ucnt[u], 1), T);
+        sm.info[tid][0] = a.uexp[u] & (E - 1);
+        sm.info[tid][1] = cnt;
+        sm.info[tid][2] = min(max(a.uoff[u], 0), T * K - cnt);
     }
     __syncthreads();
-    if (bid >= n_items) return;
+    if (tid == 0) {  // at most 4 items x 4 tiles, from LDS
+        int nun = 0, buf = 0, prev_u = -1;
+        for (int j = 0; j < i1 - i0; j++) {
+            const int u = (i0 + j) / GU_NCH, chunk = (i0 + j) % GU_NCH;
+            const int cnt = sm.info[j][1];
+            for (int m0 = 0; m0 < cnt && nun < GU_UNITS; m0 += 16) {
+                // the tile parity flips with every new token tile (consecutive
+                // items of one expert with one tile share it)
+                if (nun > 0 && (u != prev_u || m0 > 0 || cnt > 16)) buf ^= 1;
+                prev_u = u;
+                sm.unit[nun][0] = sm.info[j][0];
+                sm.unit[nun][1] = chunk * GU_FEAT;
+                sm.unit[nun][2] = min(16, cnt - m0);
+                sm.unit[nun][3] = buf;
+                sm.unit[nun][4] = sm.info[j][2] + m0;
+                nun++;
+            }
+        }
+        sm.n_units = nun;
+    }
+    __syncthreads();
+    const int n_units = sm.n_units;
+    if (tid < n_units * 16) {  // pair ids of every unit's token slots (slots >= tc repeat the last)
+        const int k = tid >> 4, sl = tid & 15;
+        sm.pairs[k][sl] = min(max(a.pairs[sm.unit[k][4] + min(sl, sm.unit[k][2] - 1)], 0), tk);
+    }
+    __syncthreads();
 
     // x rows of a token tile: 16 rows x 256 pieces of 16 bytes; waves 4h ..
     // 4h+3 take rows h + 2i (wave-uniform), piece tid % 256.  Every row is
@@ -376,141 +403,132 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     // them): a load under a lane-dependent branch makes the compiler wait
     // for it at once.
     const int xc = tid & 255, xr0 = tid >> 8;
-    auto load_x = [&](const int* tp, int tc, u32x4 (&xv)[8]) {
+    auto load_x = [&](int k, u32x4 (&xv)[8]) {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int pr = __builtin_amdgcn_readfirstlane(tp[min(xr0 + 2 * i, tc - 1)]);
+            const int pr = __builtin_amdgcn_readfirstlane(sm.pairs[k][xr0 + 2 * i]);
             xv[i] = *(const u32x4*)(a.xp + (size_t)(pr >> 3) * D + 8 * xc);
         }
     };
-    auto store_x = [&](const u32x4 (&xv)[8], int tc) {
-        (void)tc;
+    auto store_x = [&](const u32x4 (&xv)[8]) {
 #pragma unroll
         for (int i = 0; i < 8; i++) *(u32x4*)&sm.xs[xr0 + 2 * i][8 * xc] = xv[i];
     };
-    u32x4 xn[8];
-    load_x(sm.pairs[0], min(16, sm.info[0][1]), xn);
-    store_x(xn, min(16, sm.info[0][1]));
+    // this lane's gate/up row in unit k (clamped to the last unit); gate and
+    // up share one row layout, so one byte offset serves both code arrays
+    auto row_of = [&](int k) {
+        const int kk = min(k, n_units - 1);
+        return (uint32_t)(__builtin_amdgcn_readfirstlane(sm.unit[kk][0]) * F + __builtin_amdgcn_readfirstlane(sm.unit[kk][1])) +
+               (uint32_t)(16 * wave + n);
+    };
+    const __amdgpu_buffer_rsrc_t rgq = buffer_rsrc(a.gq), ruq = buffer_rsrc(a.uq);
+    // lane (n, kq) takes K [64g + 16kq, +16) of group g: two words of codes
+    auto ld_codes = [&](__amdgpu_buffer_rsrc_t r, uint32_t row, int g) {
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (row * (D / 8) + 2 * kq) * 4, 32 * g, 0));
+    };
+    // the four lanes of row n (kq = 0..3, one per 16-lane row) each load one
+    // of the row's gate scales, gate biases, up scales, up biases (eight
+    // groups per load) and swap them across lane rows when used
+    const uint16_t* sarr = kq == 0 ? a.gs : kq == 1 ? a.gb : kq == 2 ? a.us : a.ub;
+    auto ld_sc = [&](uint32_t row, int b) { return *(const u32x4*)(sarr + (size_t)row * (D / G) + 8 * b); };
+
+    // ---- prologue: unit 0's scales and token tile, then the codes of its
+    // first body (issued last, so that neither the tile store below nor the
+    // first use of the scales in the loop waits for them)
+    u32x4 sc0 = ld_sc(row_of(0), 0), sc1 = ld_sc(row_of(0), 1);
+    u32x4 xv[8];
+    load_x(0, xv);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x2 gw[GU_RING], uw[GU_RING];
+    {
+        const uint32_t r0 = row_of(0);
+#pragma unroll
+        for (int g = 0; g < GU_RING; g++) {
+            gw[g] = ld_codes(rgq, r0, g);
+            uw[g] = ld_codes(ruq, r0, g);
+        }
+    }
+    store_x(xv);
     __syncthreads();
 
-    const __amdgpu_buffer_rsrc_t rgq = buffer_rsrc(a.gq), ruq = buffer_rsrc(a.uq);
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
+    f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
+    u32x4 xn[8];
+    // bodies of GU_RING groups, two per unit: ring slot gi holds group gi of
+    // the body and is refilled with group gi of the next body (past the last
+    // unit: its copy); the scale vectors of the next body load at its start
 #pragma unroll 1
-    for (int j = 0; j < GU_ITEMS; j++) {
-        const int it = bid + j * GU_BLOCKS;
-        const int e = __builtin_amdgcn_readfirstlane(sm.info[j][0]);
-        const int cnt = __builtin_amdgcn_readfirstlane(sm.info[j][1]);
-        const int off = __builtin_amdgcn_readfirstlane(sm.info[j][2]);
-        const bool has_next = j + 1 < GU_ITEMS && it + GU_BLOCKS < n_items;
-        const int f = (it % GU_NCH) * GU_FEAT + 16 * wave + n;  // this lane's feature (B column n)
-        // lane (n, kq) takes K [64g + 16kq, +16) of group g: two words of
-        // codes.  Gate and up share one row layout: one byte offset serves
-        // both; buffer loads keep the base in scalar registers.
-        const uint32_t row = (uint32_t)(e * F + f);
-        const uint32_t qo = (row * (D / 8) + 2 * kq) * 4;
-        auto ld_codes = [&](__amdgpu_buffer_rsrc_t r, int g) {
-            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, qo, 32 * g, 0));
-        };
-        // the four lanes of row n (kq = 0..3, one per 16-lane row) each load
-        // one of the row's gate scales, gate biases, up scales, up biases
-        // (eight groups per load) and swap them across lane rows when used
-        const uint16_t* sarr = kq == 0 ? a.gs : kq == 1 ? a.gb : kq == 2 ? a.us : a.ub;
-        const uint16_t* sptr = sarr + row * (D / G);
-        auto ld_sc = [&](int b) { return *(const u32x4*)(sptr + 8 * b); };
-
-#pragma unroll 1
-        for (int m0 = 0; m0 < cnt; m0 += 16) {
-            const int tc = min(16, cnt - m0);
-            const int* tp = m0 == 0 ? sm.pairs[j] : sm.tile_pairs;
-            if (m0 > 0) {  // a later tile of an expert with more than 16 tokens
-                __syncthreads();
-                if (tid < 16) sm.tile_pairs[tid] = min(max(a.pairs[off + m0 + min(tid, tc - 1)], 0), tk);
-                __syncthreads();
-                u32x4 xv[8];
-                load_x(sm.tile_pairs, tc, xv);
-                store_x(xv, tc);
-                __syncthreads();
-            }
-            // ---- codes of groups 0 .. GU_RING-1 and the first scale vectors,
-            // then (last tile) the next item's token tile behind them
-            u32x4 sc0 = ld_sc(0), sc1 = ld_sc(1);
-            u32x2 gw[GU_RING], uw[GU_RING];
+    for (int bb = 0; bb < 2 * n_units; bb++) {
+        const int k = bb >> 1, half = bb & 1;
+        const uint32_t rn = row_of((bb + 1) >> 1);
+        const int ghn = 16 * ((bb + 1) & 1);  // first group of the next body
+        const u32x4 scn0 = ld_sc(rn, ghn / 8), scn1 = ld_sc(rn, ghn / 8 + 1);
+        const bool next_tile = half == 1 && k + 1 < n_units && sm.unit[k + 1][3] != sm.unit[k][3];
+        if (next_tile) load_x(k + 1, xn);
+        const uint16_t* xrow = &sm.xs[min(n, sm.unit[k][2] - 1)][16 * kq];  // A row: token slot n
+        uint32_t sgs = 0, sgb = 0, sus = 0, sub = 0;
 #pragma unroll
-            for (int g = 0; g < GU_RING; g++) {
-                gw[g] = ld_codes(rgq, g);
-                uw[g] = ld_codes(ruq, g);
+        for (int gi = 0; gi < GU_RING; gi++) {
+            const int g = 16 * half + gi;
+            // expand the slot's codes first, then refill the slot: the refill
+            // can take the slot's own registers, so the loop back-edge needs no
+            // copies (a copy would wait for its load and drain the ring)
+            const u32x4 bg0 = nibbles_to_codes(gw[gi][0], 0x43004300u), bg1 = nibbles_to_codes(gw[gi][1], 0x43004300u);
+            const u32x4 bu0 = nibbles_to_codes(uw[gi][0], 0x43004300u), bu1 = nibbles_to_codes(uw[gi][1], 0x43004300u);
+            __builtin_amdgcn_sched_barrier(0);
+            gw[gi] = ld_codes(rgq, rn, ghn + gi);
+            uw[gi] = ld_codes(ruq, rn, ghn + gi);
+            const bf16x8 a0 = as_bf16x8(*(const u32x4*)(xrow + 64 * g));
+            const bf16x8 a1 = as_bf16x8(*(const u32x4*)(xrow + 64 * g + 8));
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 ag = mfma16_bf16(a0, as_bf16x8(bg0), z);
+            ag = mfma16_bf16(a1, as_bf16x8(bg1), ag);
+            f32x4 au = mfma16_bf16(a0, as_bf16x8(bu0), z);
+            au = mfma16_bf16(a1, as_bf16x8(bu1), au);
+            f32x4 xsum = mfma16_bf16(a0, as_bf16x8(ones), z);
+            xsum = mfma16_bf16(a1, as_bf16x8(ones), xsum);
+            const int gs8 = gi & 7;
+            if ((gs8 & 1) == 0) {
+                // dword gs8/2 of the four arrays: after the 16-lane swap p0
+                // holds the even lane row's array (kq & ~1), p1 the odd one's;
+                // the 32-lane swaps then give rows 0/1 and 2/3
+                const uint32_t d = (gi < 8 ? sc0 : sc1)[gs8 >> 1];
+                const auto p = __builtin_amdgcn_permlane16_swap(d, d, false, false);
+                const auto q0 = __builtin_amdgcn_permlane32_swap((uint32_t)p[0], (uint32_t)p[0], false, false);
+                const auto q1 = __builtin_amdgcn_permlane32_swap((uint32_t)p[1], (uint32_t)p[1], false, false);
+                sgs = q0[0]; sus = q0[1]; sgb = q1[0]; sub = q1[1];
             }
-            if (m0 + 16 >= cnt && has_next) load_x(sm.pairs[j + 1], min(16, sm.info[j + 1][1]), xn);
-
-            const uint16_t* xrow = &sm.xs[min(n, tc - 1)][16 * kq];  // A row: token slot n
-            f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
-            // bodies of GU_RING groups: ring slot g % GU_RING holds group g
-            // and is refilled with group g + GU_RING (the last body re-reads
-            // group 31); the scale vectors of the next body load at its start
-#pragma unroll 1
-            for (int gb = 0; gb < NGRP / GU_RING; gb++) {
-                const int nb = min(gb + 1, NGRP / GU_RING - 1);
-                const u32x4 scn0 = ld_sc(2 * nb), scn1 = ld_sc(2 * nb + 1);
-                uint32_t sgs = 0, sgb = 0, sus = 0, sub = 0;
+            const bool hi = gs8 & 1;
+            const float s_g = __uint_as_float(hi ? (sgs & 0xffff0000u) : (sgs << 16));
+            const float s_u = __uint_as_float(hi ? (sus & 0xffff0000u) : (sus << 16));
+            const float c_g = __uint_as_float(hi ? (sgb & 0xffff0000u) : (sgb << 16)) - 128.0f * s_g;
+            const float c_u = __uint_as_float(hi ? (sub & 0xffff0000u) : (sub << 16)) - 128.0f * s_u;
 #pragma unroll
-                for (int gi = 0; gi < GU_RING; gi++) {
-                    const int g = GU_RING * gb + gi;
-                    // expand the slot's codes first, then refill the slot: the
-                    // refill can take the slot's own registers, so the loop
-                    // back-edge needs no copies (a copy would wait for its
-                    // load and drain the ring)
-                    const u32x4 bg0 = nibbles_to_codes(gw[gi][0], 0x43004300u), bg1 = nibbles_to_codes(gw[gi][1], 0x43004300u);
-                    const u32x4 bu0 = nibbles_to_codes(uw[gi][0], 0x43004300u), bu1 = nibbles_to_codes(uw[gi][1], 0x43004300u);
-                    __builtin_amdgcn_sched_barrier(0);
-                    const int gn = min(g + GU_RING, NGRP - 1);
-                    gw[gi] = ld_codes(rgq, gn);
-                    uw[gi] = ld_codes(ruq, gn);
-                    const bf16x8 a0 = as_bf16x8(*(const u32x4*)(xrow + 64 * g));
-                    const bf16x8 a1 = as_bf16x8(*(const u32x4*)(xrow + 64 * g + 8));
-                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    f32x4 ag = mfma16_bf16(a0, as_bf16x8(bg0), z);
-                    ag = mfma16_bf16(a1, as_bf16x8(bg1), ag);
-                    f32x4 au = mfma16_bf16(a0, as_bf16x8(bu0), z);
-                    au = mfma16_bf16(a1, as_bf16x8(bu1), au);
-                    f32x4 xsum = mfma16_bf16(a0, as_bf16x8(ones), z);
-                    xsum = mfma16_bf16(a1, as_bf16x8(ones), xsum);
-                    const int gs8 = gi & 7;
-                    if ((gs8 & 1) == 0) {
-                        // dword gs8/2 of the four arrays: after the 16-lane swap
-                        // p0 holds the even lane row's array (kq & ~1), p1 the
-                        // odd one's; the 32-lane swaps then give rows 0/1, 2/3
-                        const uint32_t d = (gi < 8 ? sc0 : sc1)[gs8 >> 1];
-                        const auto p = __builtin_amdgcn_permlane16_swap(d, d, false, false);
-                        const auto q0 = __builtin_amdgcn_permlane32_swap((uint32_t)p[0], (uint32_t)p[0], false, false);
-                        const auto q1 = __builtin_amdgcn_permlane32_swap((uint32_t)p[1], (uint32_t)p[1], false, false);
-                        sgs = q0[0]; sus = q0[1]; sgb = q1[0]; sub = q1[1];
-                    }
-                    const bool hi = gs8 & 1;
-                    const float s_g = __uint_as_float(hi ? (sgs & 0xffff0000u) : (sgs << 16));
-                    const float s_u = __uint_as_float(hi ? (sus & 0xffff0000u) : (sus << 16));
-                    const float c_g = __uint_as_float(hi ? (sgb & 0xffff0000u) : (sgb << 16)) - 128.0f * s_g;
-                    const float c_u = __uint_as_float(hi ? (sub & 0xffff0000u) : (sub << 16)) - 128.0f * s_u;
-#pragma unroll
-                    for (int v = 0; v < 4; v++) {
-                        og[v] += s_g * ag[v] + c_g * xsum[v];
-                        ou[v] += s_u * au[v] + c_u * xsum[v];
-                    }
-                }
-                sc0 = scn0;
-                sc1 = scn1;
+            for (int v = 0; v < 4; v++) {
+                og[v] += s_g * ag[v] + c_g * xsum[v];
+                ou[v] += s_u * au[v] + c_u * xsum[v];
             }
+        }
+        sc0 = scn0;
+        sc1 = scn1;
+        if (half == 1) {
             // ---- SwiGLU for token slots 4kq + v, feature f (perm8 position)
+            const int tc = sm.unit[k][2];
+            const int f = sm.unit[k][1] + 16 * wave + n;
             const int pc = (f & ~7) | perm8_pos(f & 7);
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int slot = 4 * kq + v;
-                if (slot < tc) a.h[(size_t)tp[slot] * F + pc] = __builtin_bit_cast(uint16_t, (f16)(silu_f32(og[v]) * ou[v]));
+                if (slot < tc) a.h[(size_t)sm.pairs[k][slot] * F + pc] = __builtin_bit_cast(uint16_t, (f16)(silu_f32(og[v]) * ou[v]));
             }
+            og = f32x4{0.f, 0.f, 0.f, 0.f};
+            ou = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (!has_next) break;
-        __syncthreads();  // every wave is done reading this item's token tile
-        store_x(xn, min(16, sm.info[j + 1][1]));
-        __syncthreads();
+        if (half == 1) __syncthreads();
+        if (next_tile) {  // every wave has left the old tile: store and publish the new one
+            store_x(xn);
+            __syncthreads();
+        }
     }
 }
 
@@ -619,8 +637,8 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
             const int u = (i0 + j) / DN_NCH, chunk = (i0 + j) % DN_NCH;
             const int cnt = sm.info[j][1];
             for (int m0 = 0; m0 < cnt && nun < DN_UNITS; m0 += 16) {
-                // a new token tile goes to the other buffer (consecutive items
-                // of one expert with one tile share it)
+                // the tile parity flips with every new token tile (consecutive
+                // items of one expert with one tile share it)
                 if (nun > 0 && (u != prev_u || m0 > 0 || cnt > 16)) buf ^= 1;
                 prev_u = u;
                 sm.unit[nun][0] = sm.info[j][0];
