@@ -422,9 +422,12 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
                (uint32_t)(16 * wave + n);
     };
     const __amdgpu_buffer_rsrc_t rgq = buffer_rsrc(a.gq), ruq = buffer_rsrc(a.uq);
-    // lane (n, kq) takes K [64g + 16kq, +16) of group g: two words of codes
-    auto ld_codes = [&](__amdgpu_buffer_rsrc_t r, uint32_t row, int g) {
-        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (row * (D / 8) + 2 * kq) * 4, 32 * g, 0));
+    // codes move as group pairs: lane (n, kq) loads words 4kq .. 4kq+3 of
+    // the 16 words of pair p (groups 2p, 2p+1) of row n, so one instruction
+    // reads 64 contiguous bytes of each of 16 rows (twice the run of one
+    // group, which streams markedly faster)
+    auto ld_codes = [&](__amdgpu_buffer_rsrc_t r, uint32_t row, int p) {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (row * (D / 8) + 4 * kq) * 4, 64 * p, 0));
     };
     // the four lanes of row n (kq = 0..3, one per 16-lane row) each load one
     // of the row's gate scales, gate biases, up scales, up biases (eight
@@ -439,13 +442,14 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     u32x4 xv[8];
     load_x(0, xv);
     __builtin_amdgcn_sched_barrier(0);
-    u32x2 gw[GU_RING], uw[GU_RING];
+    constexpr int NPAIR = GU_RING / 2;  // ring slots: group pairs
+    u32x4 gw[NPAIR], uw[NPAIR];
     {
         const uint32_t r0 = row_of(0);
 #pragma unroll
-        for (int g = 0; g < GU_RING; g++) {
-            gw[g] = ld_codes(rgq, r0, g);
-            uw[g] = ld_codes(ruq, r0, g);
+        for (int q = 0; q < NPAIR; q++) {
+            gw[q] = ld_codes(rgq, r0, q);
+            uw[q] = ld_codes(ruq, r0, q);
         }
     }
     store_x(xv);
@@ -454,37 +458,55 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
     f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
     u32x4 xn[8];
-    // bodies of GU_RING groups, two per unit: ring slot gi holds group gi of
-    // the body and is refilled with group gi of the next body (past the last
-    // unit: its copy); the scale vectors of the next body load at its start
+    // bodies of GU_RING groups, two per unit: ring slot q holds pair q of the
+    // body and is refilled with pair q of the next body (past the last unit:
+    // its copy); the scale vectors of the next body load at its start
 #pragma unroll 1
     for (int bb = 0; bb < 2 * n_units; bb++) {
         const int k = bb >> 1, half = bb & 1;
         const uint32_t rn = row_of((bb + 1) >> 1);
-        const int ghn = 16 * ((bb + 1) & 1);  // first group of the next body
+        const int ghn = GU_RING * ((bb + 1) & 1);  // first group of the next body
         const u32x4 scn0 = ld_sc(rn, ghn / 8), scn1 = ld_sc(rn, ghn / 8 + 1);
         const bool next_tile = half == 1 && k + 1 < n_units && sm.unit[k + 1][3] != sm.unit[k][3];
         if (next_tile) load_x(k + 1, xn);
-        const uint16_t* xrow = &sm.xs[min(n, sm.unit[k][2] - 1)][16 * kq];  // A row: token slot n
+        // A row: token slot n.  After the regrouping below, lane kq holds
+        // words wq = 4(kq & 1) + 2(kq >> 1) and wq + 1 of each group, so its
+        // x slice starts at K offset 8 wq.
+        const uint16_t* xrow = &sm.xs[min(n, sm.unit[k][2] - 1)][32 * (kq & 1) + 16 * (kq >> 1)];
         uint32_t sgs = 0, sgb = 0, sus = 0, sub = 0;
+        u32x4 bg[4], bu[4];
 #pragma unroll
         for (int gi = 0; gi < GU_RING; gi++) {
-            const int g = 16 * half + gi;
-            // expand the slot's codes first, then refill the slot: the refill
-            // can take the slot's own registers, so the loop back-edge needs no
-            // copies (a copy would wait for its load and drain the ring)
-            const u32x4 bg0 = nibbles_to_codes(gw[gi][0], 0x43004300u), bg1 = nibbles_to_codes(gw[gi][1], 0x43004300u);
-            const u32x4 bu0 = nibbles_to_codes(uw[gi][0], 0x43004300u), bu1 = nibbles_to_codes(uw[gi][1], 0x43004300u);
-            __builtin_amdgcn_sched_barrier(0);
-            gw[gi] = ld_codes(rgq, rn, ghn + gi);
-            uw[gi] = ld_codes(ruq, rn, ghn + gi);
+            const int g = GU_RING * half + gi, q = gi >> 1;
+            if ((gi & 1) == 0) {
+                // regroup pair q so each MFMA sees a single group: swapping
+                // words 0/2 and 1/3 between lanes kq and kq + 2 leaves lanes
+                // kq = 0..3 holding words {0,4,2,6} (w0), {1,5,3,7} (w1) of
+                // the first group and {8,12,10,14}, {9,13,11,15} of the second
+                const auto g02 = __builtin_amdgcn_permlane32_swap(gw[q][0], gw[q][2], false, false);
+                const auto g13 = __builtin_amdgcn_permlane32_swap(gw[q][1], gw[q][3], false, false);
+                const auto u02 = __builtin_amdgcn_permlane32_swap(uw[q][0], uw[q][2], false, false);
+                const auto u13 = __builtin_amdgcn_permlane32_swap(uw[q][1], uw[q][3], false, false);
+                // expand the slot's codes first, then refill the slot: the
+                // refill can take the slot's own registers, so the loop
+                // back-edge needs no copies (a copy would wait for its load
+                // and drain the ring)
+                bg[0] = nibbles_to_codes(g02[0], 0x43004300u); bg[1] = nibbles_to_codes(g13[0], 0x43004300u);
+                bg[2] = nibbles_to_codes(g02[1], 0x43004300u); bg[3] = nibbles_to_codes(g13[1], 0x43004300u);
+                bu[0] = nibbles_to_codes(u02[0], 0x43004300u); bu[1] = nibbles_to_codes(u13[0], 0x43004300u);
+                bu[2] = nibbles_to_codes(u02[1], 0x43004300u); bu[3] = nibbles_to_codes(u13[1], 0x43004300u);
+                __builtin_amdgcn_sched_barrier(0);
+                gw[q] = ld_codes(rgq, rn, ghn / 2 + q);
+                uw[q] = ld_codes(ruq, rn, ghn / 2 + q);
+            }
+            const int h2 = 2 * (gi & 1);
             const bf16x8 a0 = as_bf16x8(*(const u32x4*)(xrow + 64 * g));
             const bf16x8 a1 = as_bf16x8(*(const u32x4*)(xrow + 64 * g + 8));
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4 ag = mfma16_bf16(a0, as_bf16x8(bg0), z);
-            ag = mfma16_bf16(a1, as_bf16x8(bg1), ag);
-            f32x4 au = mfma16_bf16(a0, as_bf16x8(bu0), z);
-            au = mfma16_bf16(a1, as_bf16x8(bu1), au);
+            f32x4 ag = mfma16_bf16(a0, as_bf16x8(bg[h2]), z);
+            ag = mfma16_bf16(a1, as_bf16x8(bg[h2 + 1]), ag);
+            f32x4 au = mfma16_bf16(a0, as_bf16x8(bu[h2]), z);
+            au = mfma16_bf16(a1, as_bf16x8(bu[h2 + 1]), au);
             f32x4 xsum = mfma16_bf16(a0, as_bf16x8(ones), z);
             xsum = mfma16_bf16(a1, as_bf16x8(ones), xsum);
             const int gs8 = gi & 7;
