@@ -614,9 +614,10 @@ __global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_sd) {
 // workgroups each take a contiguous run of (expert, 128 rows) items, so
 // consecutive units mostly share an expert and its token tile.  Wave w owns
 // output rows 16w .. 16w + 15 of a unit over K = F (eight quantisation
-// groups); the codes of the next DN_RING groups (two units) stay in flight
-// across unit boundaries, and the next unit's token tile loads while the
-// current one computes.  Partials per (pair, output) in fp32.
+// groups, moved as four group pairs like the gate/up codes); the codes of
+// the next DN_RING groups (two units) stay in flight across unit
+// boundaries, and the next unit's token tile loads while the current one
+// computes.  Partials per (pair, output) in fp32.
 constexpr int DN_ROWS = 128;                        // output rows per item
 constexpr int DN_NCH = D / DN_ROWS;                 // items per expert
 constexpr int DN_BLOCKS = 256;                      // persistent workgroups
@@ -705,36 +706,39 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
         return (uint32_t)(__builtin_amdgcn_readfirstlane(sm.unit[kk][0]) * D + __builtin_amdgcn_readfirstlane(sm.unit[kk][1])) +
                (uint32_t)(16 * wave + n);
     };
-    auto ld_codes = [&](uint32_t row, int g) {
-        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rdq, (row * (F / 8) + 2 * kq) * 4, 32 * g, 0));
+    // lane (n, kq) loads words 4kq .. 4kq+3 of group pair p of row n
+    auto ld_codes = [&](uint32_t row, int p) {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdq, (row * (F / 8) + 4 * kq) * 4, 64 * p, 0));
     };
     auto ld_sc = [&](uint32_t row, u32x4& sv, u32x4& bv) {
         sv = *(const u32x4*)(a.ds + (size_t)row * (F / G));
         bv = *(const u32x4*)(a.db + (size_t)row * (F / G));
     };
 
-    // ---- prologue: codes of units 0 and 1, scales of unit 0, token tile of unit 0
-    u32x2 ring[DN_RING];
+    // ---- prologue: scales and token tile of unit 0, then the codes of
+    // units 0 and 1 (issued last, so that neither the tile store below nor
+    // the first use of the scales in the loop waits for them)
+    u32x4 sv, bv;
+    ld_sc(row_of(0), sv, bv);
+    u32x4 hv0[2];
+    load_h(0, hv0);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NPAIR = F / G / 2;  // group pairs per unit
+    u32x4 ring[DN_RING / 2];
     {
         const uint32_t r0 = row_of(0), r1 = row_of(1);
 #pragma unroll
-        for (int g = 0; g < 8; g++) ring[g] = ld_codes(r0, g);
+        for (int q = 0; q < NPAIR; q++) ring[q] = ld_codes(r0, q);
 #pragma unroll
-        for (int g = 0; g < 8; g++) ring[8 + g] = ld_codes(r1, g);
+        for (int q = 0; q < NPAIR; q++) ring[NPAIR + q] = ld_codes(r1, q);
     }
-    u32x4 sv, bv;
-    ld_sc(row_of(0), sv, bv);
-    {
-        u32x4 hv[2];
-        load_h(0, hv);
-        store_h(0, hv);
-    }
+    store_h(0, hv0);
     __syncthreads();
 
     const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
     static_assert(DN_RING == 2 * (F / G), "the ring holds two units");
-    // bodies of two units: ring slot 8(k % 2) + g holds group g of unit k and
-    // is refilled with group g of unit k + 2 (past the last unit: its copy)
+    // bodies of two units: ring slot 4(k % 2) + q holds pair q of unit k and
+    // is refilled with pair q of unit k + 2 (past the last unit: its copy)
 #pragma unroll 1
     for (int k0 = 0; k0 < n_units; k0 += 2) {
 #pragma unroll
@@ -748,21 +752,31 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
             u32x4 svn, bvn;
             ld_sc(row_of(k + 1), svn, bvn);
             const uint32_t rn = row_of(k + 2);
-            const uint16_t* hrow = &sm.hs[sm.unit[kc][3]][min(n, sm.unit[kc][2] - 1)][16 * kq];  // A row: token slot n
+            // A row: token slot n, at the K offset of the words this lane
+            // holds after the regrouping (as in the gate/up stage)
+            const uint16_t* hrow = &sm.hs[sm.unit[kc][3]][min(n, sm.unit[kc][2] - 1)][32 * (kq & 1) + 16 * (kq >> 1)];
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            u32x4 b[4];
 #pragma unroll
             for (int g = 0; g < 8; g++) {
-                const int rs = 8 * uu + g;
-                // expand the slot's codes first, then refill the slot (no
-                // register copy across the loop back-edge)
-                const u32x4 b0 = nibbles_to_codes(ring[rs][0], 0x64006400u), b1 = nibbles_to_codes(ring[rs][1], 0x64006400u);
-                __builtin_amdgcn_sched_barrier(0);
-                ring[rs] = ld_codes(rn, g);
+                const int rs = NPAIR * uu + (g >> 1);
+                if ((g & 1) == 0) {
+                    // regroup the pair (one group per MFMA), expand the
+                    // slot's codes, then refill the slot (no register copy
+                    // across the loop back-edge)
+                    const auto w02 = __builtin_amdgcn_permlane32_swap(ring[rs][0], ring[rs][2], false, false);
+                    const auto w13 = __builtin_amdgcn_permlane32_swap(ring[rs][1], ring[rs][3], false, false);
+                    b[0] = nibbles_to_codes(w02[0], 0x64006400u); b[1] = nibbles_to_codes(w13[0], 0x64006400u);
+                    b[2] = nibbles_to_codes(w02[1], 0x64006400u); b[3] = nibbles_to_codes(w13[1], 0x64006400u);
+                    __builtin_amdgcn_sched_barrier(0);
+                    ring[rs] = ld_codes(rn, g >> 1);
+                }
+                const int h2 = 2 * (g & 1);
                 const f16x8 a0 = as_f16x8(*(const u32x4*)(hrow + 64 * g));
                 const f16x8 a1 = as_f16x8(*(const u32x4*)(hrow + 64 * g + 8));
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                f32x4 acc = mfma16_f16(a0, as_f16x8(b0), z);
-                acc = mfma16_f16(a1, as_f16x8(b1), acc);
+                f32x4 acc = mfma16_f16(a0, as_f16x8(b[h2]), z);
+                acc = mfma16_f16(a1, as_f16x8(b[h2 + 1]), acc);
                 f32x4 hsum = mfma16_f16(a0, as_f16x8(ones), z);
                 hsum = mfma16_f16(a1, as_f16x8(ones), hsum);
                 const float sg = bf16_at(sv, g);
