@@ -17,10 +17,15 @@
 // (c = 128 or 1024).  The piece sums of x come from the first launch, those
 // of h from the down launch's own staging.
 //
+// Every kernel is compiled per token count (T = 1 .. 4), so that all loop
+// bounds are constants: a load in a loop with a run-time trip count or under
+// a run-time guard makes the compiler copy registers and wait for it at once.
+//
 // Launches:
 //   A  router logits (fp32 weights, 2 experts per block, K halves over wave
 //      pairs) and shared gate/up + SwiGLU (2 features per block, one row per
-//      wave); one block copies x into the codes' K order and sums its pieces.
+//      wave); one block copies x into the codes' K order, sums its pieces
+//      and computes the shared-expert gate, from one round trip.
 //   C  routed gate/up + SwiGLU: block = one (token, rank) pair x 8 features;
 //      the block's first wave derives the pair's expert from the token's
 //      logits (DPP top-8) so no routing launch is needed; each block also
@@ -79,34 +84,46 @@ __device__ __forceinline__ float group_param(uint32_t pairw, int g) {
 }
 
 // ------------------------------------------------------------------ A
+// NT = T tokens (compiled per token count: every loop bound is a constant).
+template <int NT>
 __global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
-    __shared__ float red[4][2 * TINY_T];
+    __shared__ float red[4][2 * NT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int T = a.T;
     const int b = blockIdx.x;
     if (b == TA_ROUTER_BLK + TA_SHARED_BLK) {
-        // x -> perm8 copy (pairs j, j+4 of every 8-block) and piece sums
-        for (int i = tid; i < T * (D / 8); i += 256) {
-            const u32x4 d = ((const u32x4*)a.x)[i];
+        // x -> perm8 copy (pairs j, j+4 of every 8-block), its 32-element
+        // piece sums and the shared-expert gate, from one round trip: thread
+        // tid holds elements 8 tid .. 8 tid + 7 of every token
+        u32x4 d[NT];
+#pragma unroll
+        for (int t = 0; t < NT; t++) d[t] = ((const u32x4*)(a.x + (size_t)t * D))[tid];
+        const u32x4 gi = a.sgi ? ((const u32x4*)a.sgi)[tid] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
             u32x4 o;
-            o[0] = (d[0] & 0xffffu) | (d[2] << 16);
-            o[1] = (d[0] >> 16) | (d[2] & 0xffff0000u);
-            o[2] = (d[1] & 0xffffu) | (d[3] << 16);
-            o[3] = (d[1] >> 16) | (d[3] & 0xffff0000u);
-            ((u32x4*)a.xp)[i] = o;
-        }
-        for (int i = tid; i < T * XPIECES; i += 256) {
-            const u32x4* src = (const u32x4*)(a.x + (size_t)i * 32);
-            float s = 0.0f;
+            o[0] = (d[t][0] & 0xffffu) | (d[t][2] << 16);
+            o[1] = (d[t][0] >> 16) | (d[t][2] & 0xffff0000u);
+            o[2] = (d[t][1] & 0xffffu) | (d[t][3] << 16);
+            o[3] = (d[t][1] >> 16) | (d[t][3] & 0xffff0000u);
+            ((u32x4*)(a.xp + (size_t)t * D))[tid] = o;
+            float s = 0.0f, z = 0.0f;
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const u32x4 v = src[q];
-#pragma unroll
-                for (int j = 0; j < 4; j++) s += lo_bf16(v[j]) + hi_bf16(v[j]);
+            for (int j = 0; j < 4; j++) {
+                const uint32_t xj = d[t][j], gj = gi[j];
+                s += lo_bf16(xj) + hi_bf16(xj);
+                z += lo_bf16(xj) * lo_bf16(gj) + hi_bf16(xj) * hi_bf16(gj);
             }
-            a.xsum[i] = s;
+            // one lane quad holds one 32-element piece
+            s = quad_sum(s);
+            if ((lane & 3) == 0) a.xsum[t * XPIECES + (tid >> 2)] = s;
+            z = wave_sum(z);
+            if (lane == 0) red[wave][t] = z;
         }
-        if (wave < T) write_token_sgate(a, wave, lane);  // one wave per token
+        __syncthreads();
+        if (tid < NT) {
+            const float z = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+            a.sgate[tid] = a.sgi ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
+        }
         return;
     }
     if (b < TA_ROUTER_BLK) {
@@ -115,18 +132,18 @@ __global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
         const int e = 2 * b + (wave >> 1), kh = wave & 1;
         const float* wrow = a.wr + (size_t)e * D;
         f32x4 wv[4];
-        u32x2 xv[TINY_T][4];
+        u32x2 xv[NT][4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int c = lane + 64 * (2 * i + kh);
             wv[i] = *(const f32x4*)(wrow + 4 * c);
 #pragma unroll
-            for (int t = 0; t < TINY_T; t++) xv[t][i] = *(const u32x2*)(a.x + (size_t)min(t, T - 1) * D + 4 * c);
+            for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x2*)(a.x + (size_t)t * D + 4 * c);
         }
         __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
-        float acc[TINY_T];
+        float acc[NT];
 #pragma unroll
-        for (int t = 0; t < TINY_T; t++) {
+        for (int t = 0; t < NT; t++) {
             float s = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
@@ -139,10 +156,10 @@ __global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
         }
         if (lane == 0)
 #pragma unroll
-            for (int t = 0; t < TINY_T; t++) red[wave][t] = acc[t];
+            for (int t = 0; t < NT; t++) red[wave][t] = acc[t];
         __syncthreads();
-        if (tid < 2 * T) {
-            const int r = tid / T, t = tid % T;
+        if (tid < 2 * NT) {
+            const int r = tid / NT, t = tid % NT;
             const float s = red[2 * r][t] + red[2 * r + 1][t];
             a.logits[(size_t)t * E + 2 * b + r] = s + (a.rbias ? a.rbias[2 * b + r] : 0.0f);
         }
@@ -153,17 +170,17 @@ __global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
     if (!a.sg) return;
     const int f0 = 2 * (b - TA_ROUTER_BLK);
     const uint16_t* wrow = (wave < 2 ? a.sg : a.su) + (size_t)(f0 + (wave & 1)) * D;
-    u32x4 wv[4], xv[TINY_T][4];
+    u32x4 wv[4], xv[NT][4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int c = lane + 64 * i;
         wv[i] = *(const u32x4*)(wrow + 8 * c);
 #pragma unroll
-        for (int t = 0; t < TINY_T; t++) xv[t][i] = *(const u32x4*)(a.x + (size_t)min(t, T - 1) * D + 8 * c);
+        for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x4*)(a.x + (size_t)t * D + 8 * c);
     }
     __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
 #pragma unroll
-    for (int t = 0; t < TINY_T; t++) {
+    for (int t = 0; t < NT; t++) {
         float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++)
@@ -177,27 +194,27 @@ __global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
         if (lane == 0) red[wave][t] = s;
     }
     __syncthreads();
-    if (tid < 2 * T) {
-        const int i = tid / T, t = tid % T;
+    if (tid < 2 * NT) {
+        const int i = tid / NT, t = tid % NT;
         a.hs[(size_t)t * FS + f0 + i] = silu_f32(red[i][t]) * red[2 + i][t];
     }
 }
 
 // ------------------------------------------------------------------ C
+template <int NT>
 __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int T = a.T;
     if ((int)blockIdx.x >= n_gu_blocks) {
         // shared down: rows o0 + 2w, o0 + 2w + 1; lane piece = 8 bf16 at K = 8 lane
         if (!a.sd) return;
         const int o = TD_ROWS * (blockIdx.x - n_gu_blocks) + 2 * wave;
         u32x4 wv[2];
-        f32x4 hv[TINY_T][2];
+        f32x4 hv[NT][2];
 #pragma unroll
         for (int r = 0; r < 2; r++) wv[r] = *(const u32x4*)(a.sd + (size_t)(o + r) * FS + 8 * lane);
 #pragma unroll
-        for (int t = 0; t < TINY_T; t++) {
-            const float* hrow = a.hs + (size_t)min(t, T - 1) * FS + 8 * lane;
+        for (int t = 0; t < NT; t++) {
+            const float* hrow = a.hs + (size_t)t * FS + 8 * lane;
             hv[t][0] = *(const f32x4*)hrow;
             hv[t][1] = *(const f32x4*)(hrow + 4);
         }
@@ -205,7 +222,7 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
 #pragma unroll
         for (int r = 0; r < 2; r++)
 #pragma unroll
-            for (int t = 0; t < TINY_T; t++) {
+            for (int t = 0; t < NT; t++) {
                 float s = 0.0f;
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
@@ -213,7 +230,7 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
                     s += hi_bf16(wv[r][j]) * hv[t][j >> 1][2 * (j & 1) + 1];
                 }
                 s = wave_sum(s);
-                if (lane == 0 && t < T) a.ys[(size_t)t * D + o + r] = s;
+                if (lane == 0) a.ys[(size_t)t * D + o + r] = s;
             }
         return;
     }
@@ -290,51 +307,62 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
 }
 
 // ------------------------------------------------------------------ D
+// NT = T tokens (compiled per token count: every loop bound is a constant).
+template <int NT>
 __global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t hl[TINY_T * K][F];   // h of every pair, fp16 perm8
-    __shared__ float hsum[TINY_T * K][F / 32];                            // piece sums of h
-    __shared__ float dv[TINY_T * K][TD_ROWS];                             // down outputs
+    __shared__ __attribute__((aligned(16))) uint16_t hl[NT * K][F];   // h of every pair, fp16 perm8
+    __shared__ float hsum[NT * K][F / 32];                            // piece sums of h
+    __shared__ float dv[NT * K][TD_ROWS];                             // down outputs
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int T = a.T, NP = T * K;
+    constexpr int T = NT, NP = T * K;
     // Row tile: block id b runs on XCD b % 8; stage C's block for feature
     // chunk fc (rows 32 fc .. +31, row tiles 4 fc .. 4 fc + 3) ran on XCD
     // fc % 8, so b takes a row tile of a chunk with fc % 8 = b % 8.
     const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
     const int o0 = TD_ROWS * (32 * (jb >> 2) + 4 * xcd + (jb & 3));
-    // the combine's operands, loaded with the first round trip
-    float wr[K], sgv = 0.0f, ysv = 0.0f;
-    if (tid < T * TD_ROWS) {
-        const int t = tid / TD_ROWS, i = tid % TD_ROWS;
+    // Every load of the block is issued before any is waited for, in the
+    // order of use: the expert ids, h, the codes, the combine's operands.
+    // Loads sit under no lane-dependent branch (the compiler would wait for
+    // such a load at once) and no address waits on another load except the
+    // codes' on the expert ids, which come from one load per lane shared
+    // through lane shuffles (a load per unit would wait for each in turn).
+    const int e_lane = a.idx[min(lane, NP - 1)] & (E - 1);  // lane l: expert of pair min(l, 8T - 1)
+    // h of every pair: 8T rows x 64 pieces of 16 bytes, pieces tid + 256 i
+    constexpr int NH = NP * (F / 8) / 256;
+    u32x4 hv[NH];
 #pragma unroll
-        for (int r = 0; r < K; r++) wr[r] = a.w[t * K + r];
-        if (a.sg) {
-            sgv = a.sgate[t];
-            ysv = a.ys[(size_t)t * D + o0 + i];
-        }
-    }
+    for (int i = 0; i < NH; i++) hv[i] = *(const u32x4*)(a.h + (size_t)(tid + 256 * i) * 8);
     // units u = (pair u >> 3, row u & 7); lanes 16j .. 16j+15 share a unit,
     // lane piece c = lane & 15 holds 32 codes at K = 32c.  Wave w takes the
     // units 16T*w .. 16T*w + 16T - 1, four per load instruction (1 KB).
     const int c = lane & 15, sub = lane >> 4;
-    constexpr int MAXJ = TINY_T * 4;
-    u32x4 cv[MAXJ];
-    uint32_t sv[MAXJ], bv[MAXJ];
-    const int nj = 4 * T;
+    constexpr int nj = 4 * T;
+    u32x4 cv[nj];
+    uint32_t sv[nj], bv[nj];
 #pragma unroll
-    for (int j = 0; j < MAXJ; j++) {
-        if (j < nj) {
-            const int u = (wave * nj + j) * 4 + sub;
-            const int pp = u >> 3, i = u & 7;
-            const size_t row = (size_t)(a.idx[pp] & (E - 1)) * D + o0 + i;
-            cv[j] = *(const u32x4*)(a.dq + row * (F / 8) + 4 * c);
-            sv[j] = *(const uint32_t*)(a.ds + row * (F / G) + 2 * (c >> 2));
-            bv[j] = *(const uint32_t*)(a.db + row * (F / G) + 2 * (c >> 2));
-        }
+    for (int j = 0; j < nj; j++) {
+        const int u = (wave * nj + j) * 4 + sub;
+        const int pp = u >> 3, i = u & 7;
+        const size_t row = (size_t)__shfl(e_lane, pp) * D + o0 + i;
+        cv[j] = *(const u32x4*)(a.dq + row * (F / 8) + 4 * c);
+        sv[j] = *(const uint32_t*)(a.ds + row * (F / G) + 2 * (c >> 2));
+        bv[j] = *(const uint32_t*)(a.db + row * (F / G) + 2 * (c >> 2));
     }
-    // stage h (8T rows x 1 KB) and its piece sums: thread takes 16 bytes
-    for (int q = tid; q < NP * (F / 8); q += 256) {
+    // the combine's operands: thread tid < T * TD_ROWS takes (token tid / 8,
+    // row tid % 8); the others load a clamped copy they never use
+    const int ct = min(tid / TD_ROWS, T - 1), ci = tid % TD_ROWS;
+    float wr[K];
+#pragma unroll
+    for (int r = 0; r < K; r++) wr[r] = a.w[ct * K + r];
+    const float sgv = a.sg ? a.sgate[ct] : 0.0f;
+    const float ysv = a.sg ? a.ys[(size_t)ct * D + o0 + ci] : 0.0f;
+    // stage h (8T rows x 1 KB) and its piece sums: thread takes 16-byte
+    // pieces tid + 256 i (loaded above, before the codes: h is needed first)
+#pragma unroll
+    for (int i = 0; i < NH; i++) {
+        const int q = tid + 256 * i;
         const int pp = q / (F / 8), k8 = q % (F / 8);
-        const u32x4 v = *(const u32x4*)(a.h + (size_t)pp * F + 8 * k8);
+        const u32x4 v = hv[i];
         *(u32x4*)&hl[pp][8 * k8] = v;
         float s = 0.0f;
 #pragma unroll
@@ -350,17 +378,15 @@ __global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
     __syncthreads();
     const int g = c >> 1;
 #pragma unroll
-    for (int j = 0; j < MAXJ; j++) {
-        if (j < nj) {
-            const int u = (wave * nj + j) * 4 + sub;
-            const int pp = u >> 3, i = u & 7;
-            float acc = 0.0f;
+    for (int j = 0; j < nj; j++) {
+        const int u = (wave * nj + j) * 4 + sub;
+        const int pp = u >> 3, i = u & 7;
+        float acc = 0.0f;
 #pragma unroll
-            for (int w = 0; w < 4; w++) acc = dot_codes_f16(cv[j][w], *(const u32x4*)&hl[pp][32 * c + 8 * w], acc);
-            const float s = group_param(sv[j], g), bb = group_param(bv[j], g);
-            const float v = row16_sum(s * acc + (bb - 1024.0f * s) * hsum[pp][c]);
-            if (c == 0) dv[pp][i] = v;
-        }
+        for (int w = 0; w < 4; w++) acc = dot_codes_f16(cv[j][w], *(const u32x4*)&hl[pp][32 * c + 8 * w], acc);
+        const float s = group_param(sv[j], g), bb = group_param(bv[j], g);
+        const float v = row16_sum(s * acc + (bb - 1024.0f * s) * hsum[pp][c]);
+        if (c == 0) dv[pp][i] = v;
     }
     __syncthreads();
     if (tid < T * TD_ROWS) {
@@ -373,12 +399,23 @@ __global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
     }
 }
 
-hipError_t launch_decode_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
-    const int n_gu = a.T * K * (F / TC_FEAT);
-    tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a, dim3(TA_ROUTER_BLK + TA_SHARED_BLK + 1), dim3(256), 0, s, a);
-    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_tiny_c, dim3(n_gu + (a.sd ? TC_SDOWN_BLK : 0)), dim3(256), 0, s, a, n_gu);
-    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_tiny_d, dim3(D / TD_ROWS), dim3(256), 0, s, a);
+template <int NT>
+hipError_t launch_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
+    const int n_gu = NT * K * (F / TC_FEAT);
+    tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a<NT>, dim3(TA_ROUTER_BLK + TA_SHARED_BLK + 1), dim3(256), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_tiny_c<NT>, dim3(n_gu + (a.sd ? TC_SDOWN_BLK : 0)), dim3(256), 0, s, a, n_gu);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_tiny_d<NT>, dim3(D / TD_ROWS), dim3(256), 0, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_decode_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
+    switch (a.T) {
+        case 1: return launch_tiny<1>(a, tr, s);
+        case 2: return launch_tiny<2>(a, tr, s);
+        case 3: return launch_tiny<3>(a, tr, s);
+        case 4: return launch_tiny<4>(a, tr, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace moe
