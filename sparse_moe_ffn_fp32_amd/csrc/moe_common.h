@@ -128,11 +128,42 @@ __device__ __forceinline__ void wave_argmax(float cv, int ci, float& bv, int& bi
     bi = __builtin_amdgcn_readlane(ci, 63);
 }
 
+// Signed-integer key with the order of a float that is not NaN: the bits
+// as they are for v >= 0, the magnitude bits flipped for v < 0; -0 becomes
+// +0 first, so equal keys mean equal floats.
+__device__ __forceinline__ int order_key(float v) {
+    const int b = __builtin_bit_cast(int, v + 0.0f);
+    return b ^ ((b >> 31) & 0x7fffffff);
+}
+
+// Wave-wide maximum of an int, the same value in every lane: row maxima
+// through DPP, then rows (0,1) and (2,3) through v_permlane16_swap and the
+// halves through v_permlane32_swap.
+template <int CTRL>
+__device__ __forceinline__ int dpp_max_step(int v) {
+    return max(v, __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ int wave_max(int v) {
+    v = dpp_max_step<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max_step<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max_step<0x141>(v);  // row_half_mirror
+    v = dpp_max_step<0x140>(v);  // row_mirror
+    const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = max((int)p[0], (int)p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    return max((int)q[0], (int)q[1]);
+}
+
 // Top-8 of 256 scores held by one wave (lane l holds experts l, l+64,
-// l+128, l+192 in v[0..3]), ordered by (score desc, index asc).  Each lane
-// sorts its four candidates once; each of the eight rounds is then one wave
-// arg-max over the lanes' current heads, and the winning lane advances its
-// head.  The results are wave-uniform.
+// l+128, l+192 in v[0..3]), ordered by (score desc, index asc); the scores
+// are finite or -inf, never NaN.  Each lane sorts its four candidates once;
+// in each of the eight rounds the winner is then the lowest index among the
+// lane heads equal to the wave maximum (a lane's other candidates equal to
+// it would sit behind a head of the same score and a lower index).  A round
+// takes the wave maximum of the heads' order keys and a ballot of the heads
+// that equal it: one such head wins outright, and only equal scores in
+// several lanes need the (score, index) arg-max.  The winning lane advances its head.
+// The results are wave-uniform.
 __device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v, int* sel_i) {
     float a[4];
     int ai[4];
@@ -154,14 +185,23 @@ __device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v
         a[q] = sw ? tv : a[q];
         ai[q] = sw ? ti : ai[q];
     }
-    // the lane's head candidate; a lane that has given all four holds -inf
+    // the lane's head candidate and its order key; a lane that has given all
+    // four holds -inf
     float hv = a[0];
-    int hi = ai[0];
+    int hi = ai[0], hk = order_key(hv);
 #pragma unroll
     for (int r = 0; r < 8; r++) {
+        const int mk = wave_max(hk);
+        const uint64_t at_max = __ballot(hk == mk);
         float bv;
         int bi;
-        wave_argmax(hv, hi, bv, bi);
+        if (__popcll(at_max) == 1) {
+            const int wl = __ffsll((unsigned long long)at_max) - 1;
+            bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hv), wl));
+            bi = __builtin_amdgcn_readlane(hi, wl);
+        } else {
+            wave_argmax(hv, hi, bv, bi);  // equal maxima in several lanes
+        }
         sel_v[r] = bv;
         sel_i[r] = bi;
         if (bi == hi) {  // this lane gave the winner: shift its list
@@ -171,6 +211,7 @@ __device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v
             a[3] = -INFINITY; ai[3] = 0x7fffffff;
             hv = a[0];
             hi = ai[0];
+            hk = order_key(hv);
         }
     }
 }

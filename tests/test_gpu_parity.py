@@ -96,6 +96,32 @@ def test_layer_variants(gpu, variant):
     _say(output_check(layer, x, y))
 
 
+@pytest.fixture(scope="module")
+def tied_layer():
+    """Router rows in identical pairs (row 2k+1 copies row 2k), so every
+    pair of experts has bit-equal logits on both sides."""
+    layer = synth.make_layer(11)
+    layer.router_w[1::2] = layer.router_w[0::2]
+    return layer
+
+
+@pytest.mark.parametrize("T", [1, 4, 37, 300])
+def test_exact_router_ties(gpu, tied_layer, T):
+    """Every top-8 round meets an exact tie, which the lower expert index
+    wins: the selection is four whole pairs (2a, 2a+1) in rank order.  The
+    inputs keep the oracle's top-8/top-9 margin (between the fourth and
+    fifth pair), so the selected set is unique."""
+    x, _, _ = workloads.enforce_margin(tied_layer, T, 11)
+    _say(f"exact router ties T={T}")
+    y, idx, w = gpu.run(tied_layer, x)
+    ref = oracle.get().route(tied_layer, x)
+    assert np.array_equal(idx, ref["idx"]), "expert order differs from the oracle's"
+    assert np.all(idx[:, 1::2] == idx[:, 0::2] + 1) and np.all(idx[:, 0::2] % 2 == 0)
+    assert np.array_equal(w[:, 0::2], w[:, 1::2]), "tied experts got different weights"
+    routing_check(tied_layer, x, idx, w)
+    _say(output_check(tied_layer, x, y))
+
+
 def test_zero_tokens(gpu, layer0):
     import sparse_moe_ffn_fp32_amd as moe
     torch = gpu.torch
