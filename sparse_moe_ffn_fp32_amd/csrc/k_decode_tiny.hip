@@ -22,8 +22,8 @@
 // a run-time guard makes the compiler copy registers and wait for it at once.
 //
 // Launches:
-//   A  router logits (fp32 weights, 2 experts per block, K halves over wave
-//      pairs) and shared gate/up + SwiGLU (2 features per block, one row per
+//   A  router logits (fp32 weights, 4 experts per block, K halves over wave
+//      pairs) and shared gate/up + SwiGLU (4 features per block, one row per
 //      wave); one block copies x into the codes' K order, sums its pieces
 //      and computes the shared-expert gate, from one round trip.
 //   C  routed gate/up + SwiGLU: block = one (token, rank) pair x 8 features;
@@ -39,11 +39,12 @@
 
 namespace moe {
 
-constexpr int TA_ROUTER_BLK = E / 2;  // 2 experts per block
-constexpr int TA_SHARED_BLK = FS / 2; // 2 features (4 rows) per block
+constexpr int TA_ROUTER_BLK = E / 4;  // 4 experts per block (8 waves)
+constexpr int TA_SHARED_BLK = FS / 4; // 4 features (8 rows) per block
 constexpr int TC_FEAT = 8;            // features per routed gate/up block
 constexpr int TC_SDOWN_BLK = D / 8;   // shared-down blocks, 8 rows each
 constexpr int TD_ROWS = 8;            // output rows per down block
+constexpr int TD_THREADS = 512;       // threads per down block (8 waves)
 constexpr int XPIECES = D / 32;       // 32-element pieces of an x row
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -86,38 +87,41 @@ __device__ __forceinline__ float group_param(uint32_t pairw, int g) {
 // ------------------------------------------------------------------ A
 // NT = T tokens (compiled per token count: every loop bound is a constant).
 template <int NT>
-__global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
-    __shared__ float red[4][2 * NT];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ void __launch_bounds__(512) k_tiny_a(DecodeArgs a) {
+    __shared__ float red[8][2 * NT];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x;
     if (b == TA_ROUTER_BLK + TA_SHARED_BLK) {
         // x -> perm8 copy (pairs j, j+4 of every 8-block), its 32-element
         // piece sums and the shared-expert gate, from one round trip: thread
-        // tid holds elements 8 tid .. 8 tid + 7 of every token
-        u32x4 d[NT];
+        // tid < 256 (waves 0-3) holds elements 8 tid .. 8 tid + 7 of every
+        // token
+        if (wave < 4) {  // every wave reaches the barrier below
+            u32x4 d[NT];
 #pragma unroll
-        for (int t = 0; t < NT; t++) d[t] = ((const u32x4*)(a.x + (size_t)t * D))[tid];
-        const u32x4 gi = a.sgi ? ((const u32x4*)a.sgi)[tid] : u32x4{0u, 0u, 0u, 0u};
+            for (int t = 0; t < NT; t++) d[t] = ((const u32x4*)(a.x + (size_t)t * D))[tid];
+            const u32x4 gi = a.sgi ? ((const u32x4*)a.sgi)[tid] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            u32x4 o;
-            o[0] = (d[t][0] & 0xffffu) | (d[t][2] << 16);
-            o[1] = (d[t][0] >> 16) | (d[t][2] & 0xffff0000u);
-            o[2] = (d[t][1] & 0xffffu) | (d[t][3] << 16);
-            o[3] = (d[t][1] >> 16) | (d[t][3] & 0xffff0000u);
-            ((u32x4*)(a.xp + (size_t)t * D))[tid] = o;
-            float s = 0.0f, z = 0.0f;
+            for (int t = 0; t < NT; t++) {
+                u32x4 o;
+                o[0] = (d[t][0] & 0xffffu) | (d[t][2] << 16);
+                o[1] = (d[t][0] >> 16) | (d[t][2] & 0xffff0000u);
+                o[2] = (d[t][1] & 0xffffu) | (d[t][3] << 16);
+                o[3] = (d[t][1] >> 16) | (d[t][3] & 0xffff0000u);
+                ((u32x4*)(a.xp + (size_t)t * D))[tid] = o;
+                float s = 0.0f, z = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const uint32_t xj = d[t][j], gj = gi[j];
-                s += lo_bf16(xj) + hi_bf16(xj);
-                z += lo_bf16(xj) * lo_bf16(gj) + hi_bf16(xj) * hi_bf16(gj);
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t xj = d[t][j], gj = gi[j];
+                    s += lo_bf16(xj) + hi_bf16(xj);
+                    z += lo_bf16(xj) * lo_bf16(gj) + hi_bf16(xj) * hi_bf16(gj);
+                }
+                // one lane quad holds one 32-element piece
+                s = quad_sum(s);
+                if ((lane & 3) == 0) a.xsum[t * XPIECES + (tid >> 2)] = s;
+                z = wave_sum(z);
+                if (lane == 0) red[wave][t] = z;
             }
-            // one lane quad holds one 32-element piece
-            s = quad_sum(s);
-            if ((lane & 3) == 0) a.xsum[t * XPIECES + (tid >> 2)] = s;
-            z = wave_sum(z);
-            if (lane == 0) red[wave][t] = z;
         }
         __syncthreads();
         if (tid < NT) {
@@ -127,9 +131,9 @@ __global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
         return;
     }
     if (b < TA_ROUTER_BLK) {
-        // experts 2b + (wave >> 1); the wave pair splits the row's 512 pieces
+        // experts 4b + (wave >> 1); the wave pair splits the row's 512 pieces
         // of 4 fp32 weights (K = 4c) into alternating 64-piece runs
-        const int e = 2 * b + (wave >> 1), kh = wave & 1;
+        const int e = 4 * b + (wave >> 1), kh = wave & 1;
         const float* wrow = a.wr + (size_t)e * D;
         f32x4 wv[4];
         u32x2 xv[NT][4];
@@ -158,18 +162,19 @@ __global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
 #pragma unroll
             for (int t = 0; t < NT; t++) red[wave][t] = acc[t];
         __syncthreads();
-        if (tid < 2 * NT) {
+        if (tid < 4 * NT) {
             const int r = tid / NT, t = tid % NT;
             const float s = red[2 * r][t] + red[2 * r + 1][t];
-            a.logits[(size_t)t * E + 2 * b + r] = s + (a.rbias ? a.rbias[2 * b + r] : 0.0f);
+            a.logits[(size_t)t * E + 4 * b + r] = s + (a.rbias ? a.rbias[4 * b + r] : 0.0f);
         }
         return;
     }
-    // shared gate/up: features f0, f0 + 1; wave w: row (gate f0, gate f0+1,
-    // up f0, up f0+1)[w]; lane piece c = lane + 64 i holds 8 bf16 at K = 8c
+    // shared gate/up: features f0 .. f0 + 3; wave w: gate row f0 + w (w < 4),
+    // up row f0 + w - 4 (w >= 4); lane piece c = lane + 64 i holds 8 bf16 at
+    // K = 8c
     if (!a.sg) return;
-    const int f0 = 2 * (b - TA_ROUTER_BLK);
-    const uint16_t* wrow = (wave < 2 ? a.sg : a.su) + (size_t)(f0 + (wave & 1)) * D;
+    const int f0 = 4 * (b - TA_ROUTER_BLK);
+    const uint16_t* wrow = (wave < 4 ? a.sg : a.su) + (size_t)(f0 + (wave & 3)) * D;
     u32x4 wv[4], xv[NT][4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -194,9 +199,9 @@ __global__ void __launch_bounds__(256) k_tiny_a(DecodeArgs a) {
         if (lane == 0) red[wave][t] = s;
     }
     __syncthreads();
-    if (tid < 2 * NT) {
+    if (tid < 4 * NT) {
         const int i = tid / NT, t = tid % NT;
-        a.hs[(size_t)t * FS + f0 + i] = silu_f32(red[i][t]) * red[2 + i][t];
+        a.hs[(size_t)t * FS + f0 + i] = silu_f32(red[i][t]) * red[4 + i][t];
     }
 }
 
@@ -309,7 +314,7 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
 // ------------------------------------------------------------------ D
 // NT = T tokens (compiled per token count: every loop bound is a constant).
 template <int NT>
-__global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
+__global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t hl[NT * K][F];   // h of every pair, fp16 perm8
     __shared__ float hsum[NT * K][F / 32];                            // piece sums of h
     __shared__ float dv[NT * K][TD_ROWS];                             // down outputs
@@ -327,16 +332,16 @@ __global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
     // codes' on the expert ids, which come from one load per lane shared
     // through lane shuffles (a load per unit would wait for each in turn).
     const int e_lane = a.idx[min(lane, NP - 1)] & (E - 1);  // lane l: expert of pair min(l, 8T - 1)
-    // h of every pair: 8T rows x 64 pieces of 16 bytes, pieces tid + 256 i
-    constexpr int NH = NP * (F / 8) / 256;
+    // h of every pair: 8T rows x 64 pieces of 16 bytes, pieces tid + 512 i
+    constexpr int NH = NP * (F / 8) / TD_THREADS;
     u32x4 hv[NH];
 #pragma unroll
-    for (int i = 0; i < NH; i++) hv[i] = *(const u32x4*)(a.h + (size_t)(tid + 256 * i) * 8);
+    for (int i = 0; i < NH; i++) hv[i] = *(const u32x4*)(a.h + (size_t)(tid + TD_THREADS * i) * 8);
     // units u = (pair u >> 3, row u & 7); lanes 16j .. 16j+15 share a unit,
     // lane piece c = lane & 15 holds 32 codes at K = 32c.  Wave w takes the
-    // units 16T*w .. 16T*w + 16T - 1, four per load instruction (1 KB).
+    // units 8T*w .. 8T*w + 8T - 1, four per load instruction (1 KB).
     const int c = lane & 15, sub = lane >> 4;
-    constexpr int nj = 4 * T;
+    constexpr int nj = 2 * T;
     u32x4 cv[nj];
     uint32_t sv[nj], bv[nj];
 #pragma unroll
@@ -357,10 +362,10 @@ __global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
     const float sgv = a.sg ? a.sgate[ct] : 0.0f;
     const float ysv = a.sg ? a.ys[(size_t)ct * D + o0 + ci] : 0.0f;
     // stage h (8T rows x 1 KB) and its piece sums: thread takes 16-byte
-    // pieces tid + 256 i (loaded above, before the codes: h is needed first)
+    // pieces tid + 512 i (loaded above, before the codes: h is needed first)
 #pragma unroll
     for (int i = 0; i < NH; i++) {
-        const int q = tid + 256 * i;
+        const int q = tid + TD_THREADS * i;
         const int pp = q / (F / 8), k8 = q % (F / 8);
         const u32x4 v = hv[i];
         *(u32x4*)&hl[pp][8 * k8] = v;
@@ -402,9 +407,9 @@ __global__ void __launch_bounds__(256) k_tiny_d(DecodeArgs a) {
 template <int NT>
 hipError_t launch_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
     const int n_gu = NT * K * (F / TC_FEAT);
-    tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a<NT>, dim3(TA_ROUTER_BLK + TA_SHARED_BLK + 1), dim3(256), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a<NT>, dim3(TA_ROUTER_BLK + TA_SHARED_BLK + 1), dim3(512), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_tiny_c<NT>, dim3(n_gu + (a.sd ? TC_SDOWN_BLK : 0)), dim3(256), 0, s, a, n_gu);
-    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_tiny_d<NT>, dim3(D / TD_ROWS), dim3(256), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_tiny_d<NT>, dim3(D / TD_ROWS), dim3(TD_THREADS), 0, s, a);
     return hipGetLastError();
 }
 
