@@ -28,9 +28,9 @@
 //
 // Launches (all on the caller's stream):
 //   A      router logits (fp32 weights split exactly into three bf16 terms)
-//          and the shared expert's gate/up + SwiGLU, K split over the 16
-//          waves of a block and reduced in LDS in fixed order; x copied into
-//          the K order of the codes.
+//          and the shared expert's gate/up + SwiGLU, per (row group, token
+//          tile) block with K split over its 16 waves and reduced in LDS in
+//          fixed order; x copied into the K order of the codes.
 //   route  one block: softmax/top-8/renormalise per token, sgate, the
 //          distinct experts with their (token, rank) pairs.
 //   C      routed gate/up + SwiGLU: 256 persistent workgroups stream the
@@ -49,8 +49,6 @@
 
 namespace moe {
 
-constexpr int N_ROUTER_BLK = E / 16;
-constexpr int N_SGU_BLK = FS / 16;
 constexpr int N_SDOWN_BLK = D / 16;
 
 __device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8& a, const bf16x8& b, f32x4 c) {
@@ -125,17 +123,30 @@ __device__ __forceinline__ void split2(const float* v, u32x4& hi, u32x4& lo) {
 
 
 // ------------------------------------------------------------------ stage A
-// Router blocks: 16 experts; shared blocks: 16 gate + 16 up rows.  Wave w
-// takes K in [128w, 128w + 128).
-template <int NMT>
-__global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a) {
-    __shared__ float red[16][NMT * 16][17];
+// Block = (row group, token tile of 16): router groups of SA_ROWS experts,
+// shared groups of SA_ROWS features (their gate and up rows, 16 MFMA
+// columns); wave w takes K in [128w, 128w + 128) and the 16 K-slices are
+// summed in LDS in wave order.  A workgroup can keep only so many bytes in
+// flight, so the work is cut fine enough to spread over the chip (about
+// 64 KB of weights and 64 KB of activations per block at 64 tokens), with
+// the token-tile index in the high part of the block id: the blocks that
+// share a row group run on one XCD and read its weights from HBM once.
+// The last ceil(T / 4) blocks copy x into the K order of the codes.
+constexpr int SA_ROWS = 8;
+constexpr int N_ROUTER_GRP = E / SA_ROWS;
+constexpr int N_SGU_GRP = FS / SA_ROWS;
+static_assert(N_ROUTER_GRP % 8 == 0 && N_SGU_GRP % 8 == 0, "a row group's blocks share an XCD");
+
+__global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a, int nmt) {
+    __shared__ float red[16][16][17];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
     const int b = blockIdx.x;
-    if (b == N_ROUTER_BLK + N_SGU_BLK) {  // x -> perm8 copy
-        for (int i = tid; i < T * (D / 8); i += 1024) {
+    const int nr = N_ROUTER_GRP * nmt, ns = N_SGU_GRP * nmt;
+    if (b >= nr + ns) {  // x -> perm8 copy: 4 tokens (1024 pieces of 16 bytes) per block
+        const int i = 1024 * (b - nr - ns) + tid;
+        if (i < T * (D / 8)) {
             const u32x4 d = ((const u32x4*)a.x)[i];
             u32x4 o;
             o[0] = (d[0] & 0xffffu) | (d[2] << 16);
@@ -146,31 +157,28 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a) {
         }
         return;
     }
-    const bool router = b < N_ROUTER_BLK;
+    const bool router = b < nr;
     if (!router && !a.sg) return;
-    const int row0 = router ? 16 * b : 16 * (b - N_ROUTER_BLK);
+    const int bb = router ? b : b - nr;
+    const int ngrp = router ? N_ROUTER_GRP : N_SGU_GRP;
+    const int r0 = SA_ROWS * (bb % ngrp), m = bb / ngrp;
     const int kb = 128 * wave + 8 * kq;
+    // router bias of output column tid % 8, loaded with the first round trip
+    const float bias = router && a.rbias ? a.rbias[r0 + (tid & (SA_ROWS - 1))] : 0.0f;
 
-    // activation row of this lane's A operand (row = lane % 16); token slots
-    // past T read token 0's row and are dropped
-    const uint16_t* xrow[NMT];
-#pragma unroll
-    for (int m = 0; m < NMT; m++) {
-        const int t = 16 * m + n;
-        xrow[m] = a.x + (size_t)(t < T ? t : 0) * D + kb;
-    }
-    f32x4 acc0[NMT], acc1[NMT];
-#pragma unroll
-    for (int m = 0; m < NMT; m++) acc0[m] = acc1[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A operand: token 16m + n (slots past T read token 0's row; dropped)
+    const int tA = 16 * m + n;
+    const uint16_t* xrow = a.x + (size_t)(tA < T ? tA : 0) * D + kb;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (router) {
-        const float* wrow = a.wr + (size_t)(row0 + n) * D + kb;
-        u32x4 wv[4][2], xv[4][NMT];
+        // B column n: expert r0 + (n & 7) (columns 8..15 repeat 0..7)
+        const float* wrow = a.wr + (size_t)(r0 + (n & 7)) * D + kb;
+        u32x4 wv[4][2], xv[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) {
             wv[ks][0] = *(const u32x4*)(wrow + 32 * ks);
             wv[ks][1] = *(const u32x4*)(wrow + 32 * ks + 4);
-#pragma unroll
-            for (int m = 0; m < NMT; m++) xv[ks][m] = *(const u32x4*)(xrow[m] + 32 * ks);
+            xv[ks] = *(const u32x4*)(xrow + 32 * ks);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
 #pragma unroll
@@ -183,56 +191,41 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a) {
             }
             u32x4 hi, mid, lo;
             split3(v, hi, mid, lo);
-#pragma unroll
-            for (int m = 0; m < NMT; m++) {
-                const bf16x8 av = as_bf16x8(xv[ks][m]);
-                acc0[m] = mfma16_bf16(av, as_bf16x8(lo), acc0[m]);
-                acc0[m] = mfma16_bf16(av, as_bf16x8(mid), acc0[m]);
-                acc0[m] = mfma16_bf16(av, as_bf16x8(hi), acc0[m]);
-            }
+            const bf16x8 av = as_bf16x8(xv[ks]);
+            acc = mfma16_bf16(av, as_bf16x8(lo), acc);
+            acc = mfma16_bf16(av, as_bf16x8(mid), acc);
+            acc = mfma16_bf16(av, as_bf16x8(hi), acc);
         }
     } else {
-        const uint16_t* grow = a.sg + (size_t)(row0 + n) * D + kb;
-        const uint16_t* urow = a.su + (size_t)(row0 + n) * D + kb;
-        u32x4 gv[4], uv[4], xv[4][NMT];
+        // B column n: gate row r0 + n (n < 8), up row r0 + n - 8 (n >= 8)
+        const uint16_t* wrow = (n < 8 ? a.sg : a.su) + (size_t)(r0 + (n & 7)) * D + kb;
+        u32x4 wv[4], xv[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) {
-            gv[ks] = *(const u32x4*)(grow + 32 * ks);
-            uv[ks] = *(const u32x4*)(urow + 32 * ks);
-#pragma unroll
-            for (int m = 0; m < NMT; m++) xv[ks][m] = *(const u32x4*)(xrow[m] + 32 * ks);
+            wv[ks] = *(const u32x4*)(wrow + 32 * ks);
+            xv[ks] = *(const u32x4*)(xrow + 32 * ks);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-#pragma unroll
-            for (int m = 0; m < NMT; m++) {
-                const bf16x8 av = as_bf16x8(xv[ks][m]);
-                acc0[m] = mfma16_bf16(av, as_bf16x8(gv[ks]), acc0[m]);
-                acc1[m] = mfma16_bf16(av, as_bf16x8(uv[ks]), acc1[m]);
-            }
+        for (int ks = 0; ks < 4; ks++) acc = mfma16_bf16(as_bf16x8(xv[ks]), as_bf16x8(wv[ks]), acc);
     }
-    // sum the 16 K-slices in LDS in wave order: first acc0, then acc1
-    float s0[2] = {0.f, 0.f};
-    for (int pass = 0; pass < (router ? 1 : 2); pass++) {
+    // lane (n, kq) holds tokens 4kq .. 4kq + 3 of column n; sum the 16
+    // K-slices in wave order
 #pragma unroll
-        for (int m = 0; m < NMT; m++)
+    for (int v = 0; v < 4; v++) red[wave][4 * kq + v][n] = acc[v];
+    __syncthreads();
+    if (tid < 16 * SA_ROWS) {
+        const int tt = tid / SA_ROWS, c = tid % SA_ROWS, t = 16 * m + tt;
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-            for (int v = 0; v < 4; v++) red[wave][16 * m + 4 * kq + v][n] = pass ? acc1[m][v] : acc0[m][v];
-        __syncthreads();
-        if (tid < T * 16) {
-            const int t = tid >> 4, c = tid & 15;
-            float s = 0.f;
-#pragma unroll
-            for (int w = 0; w < 16; w++) s += red[w][t][c];
-            s0[pass] = s;
+        for (int w = 0; w < 16; w++) {
+            s0 += red[w][tt][c];
+            s1 += red[w][tt][SA_ROWS + c];
         }
-        __syncthreads();
-    }
-    if (tid < T * 16) {
-        const int t = tid >> 4, c = tid & 15;
-        if (router) a.logits[(size_t)t * E + row0 + c] = s0[0] + (a.rbias ? a.rbias[row0 + c] : 0.0f);
-        else a.hs[(size_t)t * FS + row0 + c] = silu_f32(s0[0]) * s0[1];
+        if (t < T) {
+            if (router) a.logits[(size_t)t * E + r0 + c] = s0 + bias;
+            else a.hs[(size_t)t * FS + r0 + c] = silu_f32(s0) * s1;
+        }
     }
 }
 
@@ -841,10 +834,11 @@ size_t decode_workspace_bytes(int T, DecodeLayout* L) {
     return o;
 }
 
-template <int NMT>
 static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
+    const int nmt = (a.T + 15) / 16;  // token tiles of 16
     const int n_gu = GU_BLOCKS;
-    tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<NMT>, dim3(N_ROUTER_BLK + N_SGU_BLK + 1), dim3(1024), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a, dim3((N_ROUTER_GRP + N_SGU_GRP) * nmt + (a.T + 3) / 4), dim3(1024), 0,
+              s, a, nmt);
     hipLaunchKernelGGL(k_dec_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
     const int n_sd = a.sg ? N_SDOWN_BLK : 0;
@@ -879,13 +873,7 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     a.xsum = (float*)(ws + L.xsum);
     a.y = p.y;
     if (p.T <= TINY_T) return launch_decode_tiny(a, tr, s);
-    const int nmt = (p.T + 15) / 16;
-    switch (nmt) {
-        case 1: launch_decode_t<1>(a, tr, s); break;
-        case 2: launch_decode_t<2>(a, tr, s); break;
-        case 3: launch_decode_t<3>(a, tr, s); break;
-        default: launch_decode_t<4>(a, tr, s); break;
-    }
+    launch_decode_t(a, tr, s);
     return hipGetLastError();
 }
 
