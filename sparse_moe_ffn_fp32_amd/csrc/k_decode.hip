@@ -67,24 +67,6 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
 }
 
 
-// One u32 of eight nibbles -> eight codes c + q in perm8 order: dword j
-// holds nibbles j and j + 4 in its low and high halves, each as the 16-bit
-// pattern (magic byte, nibble).  `magic4` holds the high byte of c in all
-// four bytes (0x43 for bf16 128, 0x64 for fp16 1024).  The even and odd
-// nibbles are masked into bytes once, then v_perm_b32 places two of them
-// beside two magic bytes per dword: 7 VALU ops per word instead of 11.
-__device__ __forceinline__ u32x4 nibbles_to_codes(uint32_t w, uint32_t magic4) {
-    const uint32_t ev = w & 0x0f0f0f0fu;         // bytes: nibbles 0, 2, 4, 6
-    const uint32_t od = (w >> 4) & 0x0f0f0f0fu;  // bytes: nibbles 1, 3, 5, 7
-    // selector bytes 0..3 pick the second operand's bytes, 4..7 the first's
-    u32x4 o;
-    o[0] = __builtin_amdgcn_perm(magic4, ev, 0x04020400u);  // nibbles 0, 4
-    o[1] = __builtin_amdgcn_perm(magic4, od, 0x04020400u);  // nibbles 1, 5
-    o[2] = __builtin_amdgcn_perm(magic4, ev, 0x04030401u);  // nibbles 2, 6
-    o[3] = __builtin_amdgcn_perm(magic4, od, 0x04030401u);  // nibbles 3, 7
-    return o;
-}
-
 // Group g's bf16 from a vector of eight packed bf16 (two per dword), as fp32.
 __device__ __forceinline__ float bf16_at(const u32x4& v, int g) {
     const uint32_t d = v[g >> 1];
@@ -492,10 +474,10 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
                 // refill can take the slot's own registers, so the loop
                 // back-edge needs no copies (a copy would wait for its load
                 // and drain the ring)
-                bg[0] = nibbles_to_codes(g02[0], 0x43434343u); bg[1] = nibbles_to_codes(g13[0], 0x43434343u);
-                bg[2] = nibbles_to_codes(g02[1], 0x43434343u); bg[3] = nibbles_to_codes(g13[1], 0x43434343u);
-                bu[0] = nibbles_to_codes(u02[0], 0x43434343u); bu[1] = nibbles_to_codes(u13[0], 0x43434343u);
-                bu[2] = nibbles_to_codes(u02[1], 0x43434343u); bu[3] = nibbles_to_codes(u13[1], 0x43434343u);
+                bg[0] = nibble_codes(g02[0], 0x43434343u); bg[1] = nibble_codes(g13[0], 0x43434343u);
+                bg[2] = nibble_codes(g02[1], 0x43434343u); bg[3] = nibble_codes(g13[1], 0x43434343u);
+                bu[0] = nibble_codes(u02[0], 0x43434343u); bu[1] = nibble_codes(u13[0], 0x43434343u);
+                bu[2] = nibble_codes(u02[1], 0x43434343u); bu[3] = nibble_codes(u13[1], 0x43434343u);
                 __builtin_amdgcn_sched_barrier(0);
                 gw[q] = ld_codes(rgq, rn, ghn / 2 + q);
                 uw[q] = ld_codes(ruq, rn, ghn / 2 + q);
@@ -767,8 +749,8 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
                     // across the loop back-edge)
                     const auto w02 = __builtin_amdgcn_permlane32_swap(ring[rs][0], ring[rs][2], false, false);
                     const auto w13 = __builtin_amdgcn_permlane32_swap(ring[rs][1], ring[rs][3], false, false);
-                    b[0] = nibbles_to_codes(w02[0], 0x64646464u); b[1] = nibbles_to_codes(w13[0], 0x64646464u);
-                    b[2] = nibbles_to_codes(w02[1], 0x64646464u); b[3] = nibbles_to_codes(w13[1], 0x64646464u);
+                    b[0] = nibble_codes(w02[0], 0x64646464u); b[1] = nibble_codes(w13[0], 0x64646464u);
+                    b[2] = nibble_codes(w02[1], 0x64646464u); b[3] = nibble_codes(w13[1], 0x64646464u);
                     __builtin_amdgcn_sched_barrier(0);
                     ring[rs] = ld_codes(rn, g >> 1);
                 }

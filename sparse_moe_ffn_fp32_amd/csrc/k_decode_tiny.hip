@@ -60,20 +60,20 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 // Dot product of one u32 of eight 4-bit codes, as (magic + q) pairs in the
 // perm8 order, with four 16-bit activation pairs (one u32x4, perm8).
 __device__ __forceinline__ float dot_codes_bf16(uint32_t w, const u32x4& x, float acc) {
+    const u32x4 c = nibble_codes(w, 0x43434343u);  // bf16 128 + q
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const uint32_t c = ((w >> (4 * j)) & 0x000f000fu) | 0x43004300u;  // bf16 128 + q
-        const uint32_t xj = x[j];
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(c), as_bf16x2(xj), acc, false);
+        const uint32_t cj = c[j], xj = x[j];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(cj), as_bf16x2(xj), acc, false);
     }
     return acc;
 }
 __device__ __forceinline__ float dot_codes_f16(uint32_t w, const u32x4& h, float acc) {
+    const u32x4 c = nibble_codes(w, 0x64646464u);  // fp16 1024 + q
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const uint32_t c = ((w >> (4 * j)) & 0x000f000fu) | 0x64006400u;  // fp16 1024 + q
-        const uint32_t hj = h[j];
-        acc = __builtin_amdgcn_fdot2(as_f16x2(c), as_f16x2(hj), acc, false);
+        const uint32_t cj = c[j], hj = h[j];
+        acc = __builtin_amdgcn_fdot2(as_f16x2(cj), as_f16x2(hj), acc, false);
     }
     return acc;
 }

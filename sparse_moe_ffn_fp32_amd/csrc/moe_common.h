@@ -57,18 +57,35 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8_perm(u32x4 v) {
     return o;
 }
 
+// One u32 of eight nibbles -> four dwords of 16-bit patterns (magic byte,
+// nibble) in perm8 order: dword j holds nibbles j and j + 4 in its low and
+// high halves.  `magic4` holds the magic byte in all four bytes (0x64: fp16
+// 1024 + q; 0x43: bf16 128 + q).  The even and odd nibbles are masked into
+// bytes once; v_perm_b32 then places two of them beside two magic bytes per
+// dword (7 VALU ops per word instead of 11 for shift, mask and or per pair).
+__device__ __forceinline__ u32x4 nibble_codes(uint32_t w, uint32_t magic4) {
+    const uint32_t ev = w & 0x0f0f0f0fu;         // bytes: nibbles 0, 2, 4, 6
+    const uint32_t od = (w >> 4) & 0x0f0f0f0fu;  // bytes: nibbles 1, 3, 5, 7
+    // selector bytes 0..3 pick the second operand's bytes, 4..7 the first's
+    u32x4 o;
+    o[0] = __builtin_amdgcn_perm(magic4, ev, 0x04020400u);  // nibbles 0, 4
+    o[1] = __builtin_amdgcn_perm(magic4, od, 0x04020400u);  // nibbles 1, 5
+    o[2] = __builtin_amdgcn_perm(magic4, ev, 0x04030401u);  // nibbles 2, 6
+    o[3] = __builtin_amdgcn_perm(magic4, od, 0x04030401u);  // nibbles 3, 7
+    return o;
+}
+
 // One u32 of eight 4-bit codes -> eight fp16 weights s*q + b (one rounding,
 // fused multiply-add) in perm8 order.  s2, b2 hold the group's scale and
 // bias in both halves.
 __device__ __forceinline__ u32x4 q4_word_to_f16x8(uint32_t w, f16x2 s2, f16x2 b2) {
     const f16x2 k1024 = {(f16)1024.0f, (f16)1024.0f};
+    const u32x4 c = nibble_codes(w, 0x64646464u);  // fp16 1024 + q: the 10-bit mantissa holds q exactly
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        // (1024 + q) in each fp16 half: 0x6400 is 1024.0 and the 10-bit
-        // mantissa holds the nibble exactly
-        uint32_t code = ((w >> (4 * j)) & 0x000f000fu) | 0x64006400u;
-        f16x2 q = __builtin_bit_cast(f16x2, code) - k1024;  // exact
+        const uint32_t cj = c[j];
+        f16x2 q = __builtin_bit_cast(f16x2, cj) - k1024;  // exact
         f16x2 r = __builtin_elementwise_fma(q, s2, b2);
         o[j] = __builtin_bit_cast(uint32_t, r);
     }
