@@ -163,6 +163,48 @@ int moe_ffn_forward_traced(const moe_ffn_dims *dims, int64_t T, const uint16_t *
                            int32_t *topk_idx, float *topk_weight, void *workspace, size_t workspace_bytes,
                            void *stream, int path, const moe_ffn_trace *trace);
 
+/* ---- The FFN sub-block of a layer, with its boundary steps.
+ *
+ * "qwen35moe - Forward-Pass Design", section "Block scaffold": every layer is
+ * a pre-norm sandwich; the shared-MoE FFN reads the post-attention
+ * RMS-normalised stream and its output is added back to the un-normalised
+ * stream.  RMS normalisation as in "ds4.c study notes" Part 3, section 3,
+ * trace 1: out[i] = x[i] / sqrt(mean(x^2) + eps) * weight[i].  So:
+ *
+ *   xn = bf16( h * (1 / sqrt(mean(h^2) + eps)) * norm_weight )   (per token)
+ *   y  = bf16( h + FFN(xn) )                                     (one rounding)
+ *
+ * with FFN the function of moe_ffn_forward.  Readings taken where the pages
+ * leave a step open: the normalised row is rounded once to bf16, the FFN's
+ * input type; the sum of squares and the scale are computed in fp32 here
+ * (the pages accumulate in double, which the reference computation does); the
+ * FFN output is not rounded before the residual is added.  eps is the
+ * caller's (the pages name it but give no value); it must be finite and
+ * >= 0.
+ *
+ * h bf16 [T, d_model]: the residual stream, read only.  norm_weight fp32
+ * [d_model] (post_attention_norm), required.  y bf16 [T, d_model] may be h
+ * itself (in-place update of the residual stream) but must not overlap it
+ * otherwise.  Every other argument, status and the rules of the conventions
+ * above are those of moe_ffn_forward_path / moe_ffn_forward_traced. */
+
+/* Bytes of device workspace for moe_ffn_block_forward* with T tokens:
+ * moe_ffn_workspace_size plus room for the normalised rows of one pass. */
+size_t moe_ffn_block_workspace_size(const moe_ffn_dims *dims, int64_t T);
+
+int moe_ffn_block_forward(const moe_ffn_dims *dims, int64_t T, const uint16_t *h, const float *norm_weight, float eps,
+                          const moe_ffn_router *router, const moe_ffn_experts *experts, const moe_ffn_shared *shared,
+                          uint16_t *y, int32_t *topk_idx, float *topk_weight, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* moe_ffn_block_forward with the execution path forced and an optional
+ * trace (both as in moe_ffn_forward_traced). */
+int moe_ffn_block_forward_traced(const moe_ffn_dims *dims, int64_t T, const uint16_t *h, const float *norm_weight,
+                                 float eps, const moe_ffn_router *router, const moe_ffn_experts *experts,
+                                 const moe_ffn_shared *shared, uint16_t *y, int32_t *topk_idx, float *topk_weight,
+                                 void *workspace, size_t workspace_bytes, void *stream, int path,
+                                 const moe_ffn_trace *trace);
+
 /* Static string for a status code. */
 const char *moe_ffn_status_string(int status);
 

@@ -79,6 +79,10 @@ class Oracle:
                                          vp, vp, vp, vp, vp, ctypes.c_int]
         L.moe_oracle_forward.restype = ctypes.c_int
         L.moe_oracle_route.argtypes = L.moe_oracle_forward.argtypes[:6] + [vp, vp, vp, vp, ctypes.c_int]
+        L.moe_oracle_rmsnorm_bf16.argtypes = [vp, vp, i64, ctypes.c_double, vp]
+        L.moe_oracle_rmsnorm_bf16.restype = None
+        L.moe_oracle_block_forward.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Layer), i64, vp, vp,
+                                               ctypes.c_double, vp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int]
         L.moe_oracle_route.restype = ctypes.c_int
         self.L = L
         self.path = lib_path
@@ -165,6 +169,44 @@ class Oracle:
             out["logits"] = logits
         return out
 
+
+    def rmsnorm_bf16(self, x_row: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+        """One row: bf16 bits -> bf16 bits of x / sqrt(mean(x^2) + eps) * weight."""
+        x = np.ascontiguousarray(x_row, dtype=np.uint16)
+        wv = np.ascontiguousarray(weight, dtype=np.float32)
+        assert wv.shape == x.shape
+        out = np.empty_like(x)
+        self.L.moe_oracle_rmsnorm_bf16(x.ctypes.data, wv.ctypes.data, x.size, float(eps), out.ctypes.data)
+        return out
+
+    def block_forward(self, lay, h: np.ndarray, norm_w: np.ndarray, eps: float, tokens=None, nthreads=None,
+                      want_logits=False) -> dict:
+        """y = h + FFN(RMSNorm(h) * norm_w) in double; also the bf16 rows xn."""
+        h = np.ascontiguousarray(h, dtype=np.uint16)
+        nw = np.ascontiguousarray(norm_w, dtype=np.float32)
+        T, D = h.shape
+        assert nw.shape == (D,)
+        tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
+        n = T if tok is None else tok.size
+        k, E = lay.dims.top_k, lay.dims.n_experts
+        xn = np.empty((T, D), dtype=np.uint16)
+        y = np.empty((n, D), dtype=np.float64)
+        idx = np.empty((n, k), dtype=np.int32)
+        w = np.empty((n, k), dtype=np.float64)
+        margin = np.empty(n, dtype=np.float64)
+        logits = np.empty((n, E), dtype=np.float64) if want_logits else None
+        d, l = self._dims(lay.dims), self._layer(lay)
+        st = self.L.moe_oracle_block_forward(ctypes.byref(d), ctypes.byref(l), T, h.ctypes.data, nw.ctypes.data,
+                                             float(eps), None if tok is None else tok.ctypes.data, n,
+                                             xn.ctypes.data, y.ctypes.data, idx.ctypes.data, w.ctypes.data,
+                                             margin.ctypes.data, None if logits is None else logits.ctypes.data,
+                                             nthreads or default_threads())
+        if st != 0:
+            raise ValueError(f"moe_oracle_block_forward failed: {st}")
+        out = dict(y=y, idx=idx, w=w, margin=margin, xn=xn)
+        if want_logits:
+            out["logits"] = logits
+        return out
 
     def route(self, lay, x: np.ndarray, tokens=None, nthreads=None, want_logits=False) -> dict:
         x = np.ascontiguousarray(x, dtype=np.uint16)

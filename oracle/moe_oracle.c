@@ -306,3 +306,55 @@ int moe_oracle_route(const moe_oracle_dims *d, const moe_oracle_layer *L, int64_
     }
     return st;
 }
+
+/* ------------------------------------------------------- block boundary */
+/* Nearest bf16 of a double, ties to even; bf16 keeps 8 significant bits and
+ * the fp32 exponent range (subnormals down to 2^-133). */
+static uint16_t f64_to_bf16(double v) {
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    const double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a) || isnan(a)) return isnan(a) ? 0x7fc0u : (uint16_t)(sign | 0x7f80u);
+    double r;
+    if (a < ldexp(1.0, -126)) {
+        r = ldexp(rint(ldexp(a, 133)), -133); /* subnormal step 2^-133 */
+    } else {
+        int e;
+        const double m = frexp(a, &e);        /* a = m * 2^e, m in [0.5, 1) */
+        r = ldexp(rint(ldexp(m, 8)), e - 8);  /* 8 significant bits; rint: ties to even */
+    }
+    if (r > ldexp(2.0 - ldexp(1.0, -7), 127)) return (uint16_t)(sign | 0x7f80u); /* past the largest bf16 */
+    const float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+void moe_oracle_rmsnorm_bf16(const uint16_t *x_row, const float *weight, int64_t n, double eps, uint16_t *out_row) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        const double v = (double)moe_oracle_bf16_to_f32(x_row[i]);
+        ss += v * v;
+    }
+    const double scale = 1.0 / sqrt(ss / (double)n + eps);
+    for (int64_t i = 0; i < n; i++)
+        out_row[i] = f64_to_bf16((double)moe_oracle_bf16_to_f32(x_row[i]) * scale * (double)weight[i]);
+}
+
+int moe_oracle_block_forward(const moe_oracle_dims *d, const moe_oracle_layer *L, int64_t T, const uint16_t *h,
+                             const float *norm_w, double eps, const int64_t *tokens, int64_t n_tok, uint16_t *xn,
+                             double *y, int32_t *idx, double *w, double *margin, double *logits, int nthreads) {
+    if (!d || !norm_w || (!h && T > 0) || T < 0 || !(eps >= 0.0)) return MOE_ORACLE_EINVAL;
+    const int64_t D = d->d_model;
+    uint16_t *xr = xn ? xn : (uint16_t *)calloc((size_t)(T > 0 ? T * D : 1), sizeof(uint16_t));
+    if (!xr) return MOE_ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; t++) moe_oracle_rmsnorm_bf16(h + t * D, norm_w, D, eps, xr + t * D);
+    int st = moe_oracle_forward(d, L, T, xr, tokens, n_tok, y, idx, w, margin, logits, nthreads);
+    if (st == MOE_ORACLE_OK)
+        for (int64_t n = 0; n < n_tok; n++) {
+            const int64_t t = tokens ? tokens[n] : n;
+            for (int64_t o = 0; o < D; o++) y[n * D + o] += (double)moe_oracle_bf16_to_f32(h[t * D + o]);
+        }
+    if (!xn) free(xr);
+    return st;
+}

@@ -111,6 +111,24 @@ int moe_oracle_route(const moe_oracle_dims *d, const moe_oracle_layer *L, int64_
                      const int64_t *tokens, int64_t n_tok, int32_t *idx, double *w, double *margin, double *logits,
                      int nthreads);
 
+/* The FFN sub-block with its boundary steps.  qwen35moe page, "Block
+ * scaffold": the FFN reads the RMS-normalised stream and its output is added
+ * to the un-normalised input.  ds4.c study notes Part 3, section 3, trace 1:
+ * out[i] = x[i] / sqrt(mean(x^2) + eps) * weight[i], squares summed in
+ * double.  Readings: everything in double here, and the normalised row is
+ * rounded once to bf16 (to nearest, ties to even), the FFN's input type.
+ *
+ * moe_oracle_rmsnorm_bf16: one row of n bf16 values -> n bf16 values. */
+void moe_oracle_rmsnorm_bf16(const uint16_t *x_row, const float *weight, int64_t n, double eps, uint16_t *out_row);
+
+/* y = h + FFN(xn) in double (not rounded) for the listed tokens, with xn the
+ * rows of moe_oracle_rmsnorm_bf16(h); idx, w, margin, logits as in
+ * moe_oracle_forward (of xn).  xn (optional, [T, D] bf16) receives every
+ * normalised row. */
+int moe_oracle_block_forward(const moe_oracle_dims *d, const moe_oracle_layer *L, int64_t T, const uint16_t *h,
+                             const float *norm_w, double eps, const int64_t *tokens, int64_t n_tok, uint16_t *xn,
+                             double *y, int32_t *idx, double *w, double *margin, double *logits, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

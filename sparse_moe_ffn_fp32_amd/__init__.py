@@ -26,6 +26,7 @@ PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 DECODE_MAX_T = 64
 
 EXPORTED = ("moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_path", "moe_ffn_forward_traced",
+            "moe_ffn_block_workspace_size", "moe_ffn_block_forward", "moe_ffn_block_forward_traced",
             "moe_ffn_status_string")
 KERNEL_ROUTER, KERNEL_EXPERT_GU, KERNEL_EXPERT_DOWN, KERNEL_COMBINE = 1, 2, 3, 4
 
@@ -87,6 +88,14 @@ def lib(path: str = LIB_PATH):
         L.moe_ffn_forward_path.restype = ctypes.c_int
         L.moe_ffn_forward_traced.argtypes = fwd + [ctypes.c_int, ctypes.POINTER(Trace)]
         L.moe_ffn_forward_traced.restype = ctypes.c_int
+        L.moe_ffn_block_workspace_size.argtypes = [ctypes.POINTER(Dims), i64]
+        L.moe_ffn_block_workspace_size.restype = ctypes.c_size_t
+        blk = [ctypes.POINTER(Dims), i64, vp, vp, ctypes.c_float, ctypes.POINTER(Router), ctypes.POINTER(Experts),
+               ctypes.POINTER(Shared), vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.moe_ffn_block_forward.argtypes = blk
+        L.moe_ffn_block_forward.restype = ctypes.c_int
+        L.moe_ffn_block_forward_traced.argtypes = blk + [ctypes.c_int, ctypes.POINTER(Trace)]
+        L.moe_ffn_block_forward_traced.restype = ctypes.c_int
         L.moe_ffn_status_string.argtypes = [ctypes.c_int]
         L.moe_ffn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -193,8 +202,46 @@ def moe_ffn_forward(x, layer: DeviceLayer, y, workspace, topk_idx=None, topk_wei
     return moe_ffn_forward_path(x, layer, y, workspace, topk_idx, topk_weight, stream, PATH_AUTO, **kw)
 
 
-def alloc_workspace(T: int, device="cuda"):
-    """A workspace for calls with up to T tokens (uninitialised memory)."""
+def alloc_workspace(T: int, device="cuda", block: bool = False):
+    """A workspace for calls with up to T tokens (uninitialised memory); with
+    block=True, for the block entry point (moe_ffn_block_forward*)."""
     import torch
-    n = moe_ffn_workspace_size(T)
+    n = moe_ffn_block_workspace_size(T) if block else moe_ffn_workspace_size(T)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_ffn_block_workspace_size(T: int, dims: Dims = DIMS) -> int:
+    return int(lib().moe_ffn_block_workspace_size(ctypes.byref(dims), T))
+
+
+def moe_ffn_block_forward_traced(h, norm_weight, eps: float, layer: DeviceLayer, y, workspace, topk_idx=None,
+                                 topk_weight=None, stream=None, path: int = PATH_AUTO, trace: Optional[Trace] = None,
+                                 dims: Dims = DIMS, T: Optional[int] = None, check: bool = True) -> int:
+    """y = h + FFN(RMSNorm(h) * norm_weight) (moe_ffn_block_forward_traced):
+    h, y bf16 bits [T, D] (y may be h), norm_weight fp32 [D]."""
+    r, ex, sh = layer.structs()
+    T = h.shape[0] if T is None else T
+    wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    st = lib().moe_ffn_block_forward_traced(ctypes.byref(dims), T, _ptr(h), _ptr(norm_weight), float(eps),
+                                            ctypes.byref(r), ctypes.byref(ex),
+                                            ctypes.byref(sh) if sh is not None else None, _ptr(y), _ptr(topk_idx),
+                                            _ptr(topk_weight), _ptr(workspace), wsb, _stream_ptr(stream), path,
+                                            ctypes.byref(trace) if trace is not None else None)
+    if check and st != MOE_FFN_OK:
+        raise MoeFfnError(st, moe_ffn_status_string(st))
+    return st
+
+
+def moe_ffn_block_forward(h, norm_weight, eps: float, layer: DeviceLayer, y, workspace, topk_idx=None,
+                          topk_weight=None, stream=None, dims: Dims = DIMS, T: Optional[int] = None,
+                          check: bool = True) -> int:
+    """moe_ffn_block_forward: the FFN sub-block with its boundary steps."""
+    r, ex, sh = layer.structs()
+    T = h.shape[0] if T is None else T
+    wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    st = lib().moe_ffn_block_forward(ctypes.byref(dims), T, _ptr(h), _ptr(norm_weight), float(eps), ctypes.byref(r),
+                                     ctypes.byref(ex), ctypes.byref(sh) if sh is not None else None, _ptr(y),
+                                     _ptr(topk_idx), _ptr(topk_weight), _ptr(workspace), wsb, _stream_ptr(stream))
+    if check and st != MOE_FFN_OK:
+        raise MoeFfnError(st, moe_ffn_status_string(st))
+    return st

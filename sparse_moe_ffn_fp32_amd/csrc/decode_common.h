@@ -32,6 +32,7 @@ struct DecodeArgs {
     int32_t* ucnt;   // [E]
     int32_t* uoff;   // [E]
     int32_t* pairs;  // [8T] (t*8 + r), grouped by distinct expert, t ascending
+    const uint16_t* resid;  // bf16 [T, D] added to y before its rounding, or nullptr
     uint16_t* y;
 };
 

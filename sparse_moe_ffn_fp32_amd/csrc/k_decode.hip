@@ -786,8 +786,8 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
     }
 }
 
-// y = sum_{r=0..7} w_r * partial_r + sgate * shexp, fixed order, one bf16
-// rounding (T > 4).
+// y = sum_{r=0..7} w_r * partial_r + sgate * shexp (+ the residual), fixed
+// order, one bf16 rounding (T > 4).
 __global__ void __launch_bounds__(256) k_dec_combine(DecodeArgs a) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= a.T * D) return;
@@ -796,6 +796,7 @@ __global__ void __launch_bounds__(256) k_dec_combine(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < K; r++) sum += a.w[t * K + r] * a.part[(size_t)(t * K + r) * D + o];
     if (a.sg) sum += a.sgate[t] * a.ys[i];
+    if (a.resid) sum += bf16_to_f32(a.resid[i]);
     a.y[i] = f32_to_bf16_rne(sum);
 }
 
@@ -862,6 +863,7 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     a.pairs = (int32_t*)(ws + L.pairs);
     a.xsum = (float*)(ws + L.xsum);
     a.y = p.y;
+    a.resid = p.resid;
     if (p.T <= TINY_T) return launch_decode_tiny(a, tr, s);
     launch_decode_t(a, tr, s);
     return hipGetLastError();

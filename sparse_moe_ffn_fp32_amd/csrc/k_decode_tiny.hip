@@ -32,8 +32,9 @@
 //      pulls the down rows stage D will read into cache; shared down (8 rows
 //      per block).
 //   D  routed down: block = 8 output rows x every pair; h staged in LDS;
-//      then the combine  y = sum_{r=0..7} w_r * down_r + sgate * shexp  in
-//      fixed order with one bf16 rounding.
+//      then the combine  y = sum_{r=0..7} w_r * down_r + sgate * shexp (+ the
+//      residual of the block entry point)  in fixed order with one bf16
+//      rounding.
 #include "../../include/moe_ffn.h"
 #include "decode_common.h"
 
@@ -361,6 +362,7 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
     for (int r = 0; r < K; r++) wr[r] = a.w[ct * K + r];
     const float sgv = a.sg ? a.sgate[ct] : 0.0f;
     const float ysv = a.sg ? a.ys[(size_t)ct * D + o0 + ci] : 0.0f;
+    const float rsv = a.resid ? bf16_to_f32(a.resid[(size_t)ct * D + o0 + ci]) : 0.0f;
     // stage h (8T rows x 1 KB) and its piece sums: thread takes 16-byte
     // pieces tid + 512 i (loaded above, before the codes: h is needed first)
 #pragma unroll
@@ -400,6 +402,7 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < K; r++) sum += wr[r] * dv[t * K + r][i];
         if (a.sg) sum += sgv * ysv;
+        if (a.resid) sum += rsv;  // the residual, last before the one rounding
         a.y[(size_t)t * D + o0 + i] = f32_to_bf16_rne(sum);
     }
 }

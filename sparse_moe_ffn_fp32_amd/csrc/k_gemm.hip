@@ -117,6 +117,7 @@ struct GemmArgs {
     uint16_t* p_out;         // DOWN: fp16 partials [N_assign, D]
     uint16_t* hs_out;        // SGU
     uint16_t* y;             // SDOWN: bf16 [T, D]
+    const uint16_t* resid;   // SDOWN: bf16 [T, D] added before the rounding of y, or null
     const uint16_t* p_in;    // SDOWN: fp16 partials
     const uint16_t* wr2;     // ROUTER: fp16 [2, E, D] (hi, lo planes; perm8)
     const float* rbias;      // ROUTER: fp32 [E] or null
@@ -517,11 +518,14 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
                         }
                     }
                     const float sg = g.sgate[t];
+                    // the residual (added last, before the one rounding)
+                    const u32x4 rv = g.resid ? *(const u32x4*)&g.resid[(size_t)t * D + o] : u32x4{0u, 0u, 0u, 0u};
                     u32x4 out;
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
-                        const float y0 = sum[2 * j] * (1.0f / PARTIAL_SCALE) + sg * yb[r * YS + 8 * c + 2 * j];
-                        const float y1 = sum[2 * j + 1] * (1.0f / PARTIAL_SCALE) + sg * yb[r * YS + 8 * c + 2 * j + 1];
+                        const uint32_t rj = rv[j];
+                        const float y0 = sum[2 * j] * (1.0f / PARTIAL_SCALE) + sg * yb[r * YS + 8 * c + 2 * j] + bf16_to_f32(rj & 0xffffu);
+                        const float y1 = sum[2 * j + 1] * (1.0f / PARTIAL_SCALE) + sg * yb[r * YS + 8 * c + 2 * j + 1] + bf16_to_f32(rj >> 16);
                         out[j] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
                     }
                     *(u32x4*)&g.y[(size_t)t * D + o] = out;
@@ -830,16 +834,18 @@ __global__ void __launch_bounds__(256) k_gemm_router_sgu(GemmArgs g, int n_route
         gemm_block<MODE_SGU>(g, *reinterpret_cast<GemmSmem<MODE_SGU>*>(sm), blockIdx.x - n_router);
 }
 
-// y = sum_r partial_r, for layers without a shared expert.
+// y = sum_r partial_r (+ the residual), for layers without a shared expert.
 __global__ void __launch_bounds__(256) k_combine_routed(const uint16_t* __restrict__ p, const int32_t* __restrict__ pos_of,
-                                                        uint16_t* __restrict__ y, int T) {
+                                                        const uint16_t* resid, uint16_t* y, int T) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= T * D) return;
     const int t = i / D, o = i % D;
     float sum = 0.0f;
 #pragma unroll
     for (int r = 0; r < K; r++) sum += (float)__builtin_bit_cast(f16, p[(size_t)pos_of[t * K + r] * D + o]);
-    y[i] = f32_to_bf16_rne(sum * (1.0f / PARTIAL_SCALE));
+    sum *= 1.0f / PARTIAL_SCALE;
+    if (resid) sum += bf16_to_f32(resid[i]);
+    y[i] = f32_to_bf16_rne(sum);
 }
 
 // x bf16 [T, D] -> fp16 [T, D] in perm8 order.
@@ -898,11 +904,11 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     else tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm<MODE_DOWN>, grid(max_tiles * (D / GEMM_BN)), dim3(256), 0, s, g);
     // combine
     if (p.sh_gate) {
-        g.sw[0] = p.sh_down; g.p_in = p.partial; g.y = p.y;
+        g.sw[0] = p.sh_down; g.p_in = p.partial; g.y = p.y; g.resid = p.resid;
         tr.launch(MOE_FFN_KERNEL_COMBINE, k_gemm<MODE_SDOWN>, grid(mt * (D / GEMM_BN)), dim3(256), 0, s, g);
     } else {
         tr.launch(MOE_FFN_KERNEL_COMBINE, k_combine_routed, dim3((p.T * D + 255) / 256), dim3(256), 0, s,
-                  (const uint16_t*)p.partial, (const int32_t*)p.pos_of, p.y, p.T);
+                  (const uint16_t*)p.partial, (const int32_t*)p.pos_of, p.resid, p.y, p.T);
     }
     return hipGetLastError();
 }

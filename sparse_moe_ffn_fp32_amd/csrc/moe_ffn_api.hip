@@ -84,9 +84,17 @@ int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_f
     return MOE_FFN_OK;
 }
 
+// Workspace of the block entry point: the FFN's own, then the normalised
+// input of one pass (T tokens on the decode path, at most
+// MOE_FFN_PREFILL_CHUNK_T on the prefill path).
+size_t block_workspace_bytes(int64_t T) {
+    const int64_t tc = T < MOE_FFN_PREFILL_CHUNK_T ? T : MOE_FFN_PREFILL_CHUNK_T;
+    return up(workspace_bytes(T)) + up((size_t)tc * D * 2);
+}
+
 int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const moe_ffn_experts* ex,
                 const moe_ffn_shared* sh, uint16_t* y, int32_t* idx_user, float* w_user, char* ws,
-                const Tracer& tr, hipStream_t s) {
+                const uint16_t* resid, const Tracer& tr, hipStream_t s) {
     const Layout L = layout(T);
     const int N = T * K;
     auto at = [&](size_t off) { return (void*)(ws + off); };
@@ -129,10 +137,63 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     p.sh_up = sh ? sh->up : nullptr;
     p.sh_down = sh ? sh->down : nullptr;
     p.partial = (uint16_t*)at(L.partial);
+    p.resid = resid;
     p.y = y;
     p.T = T;
     chk(launch_prefill_gemms(p, tr, s));
     return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
+}
+
+// The FFN of every entry point.  With norm_w == nullptr: y = FFN(x).  With
+// norm_w: x is the residual stream, each pass first writes its rows of
+// RMSNorm(x) * norm_w (bf16) into xn, runs the FFN on them and adds x to the
+// output before its rounding.
+int forward_impl(int64_t T, const uint16_t* x, const float* norm_w, float eps, uint16_t* xn,
+                 const moe_ffn_router* router, const moe_ffn_experts* experts, const moe_ffn_shared* shared,
+                 uint16_t* y, int32_t* topk_idx, float* topk_weight, void* workspace, hipStream_t stream, int path,
+                 const moe_ffn_trace* trace) {
+    Tracer tr;
+    if (trace) {
+        tr.kernel = trace->kernel;
+        tr.start = (hipEvent_t)trace->start;
+        tr.stop = (hipEvent_t)trace->stop;
+    }
+    const bool decode = path == MOE_FFN_PATH_DECODE || (path == MOE_FFN_PATH_AUTO && T <= MOE_FFN_DECODE_MAX_T);
+    if (!decode) {
+        // passes over token slices of at most MOE_FFN_PREFILL_CHUNK_T (a
+        // traced kernel is bracketed in every pass; the events keep the last)
+        for (int64_t c0 = 0; c0 < T; c0 += MOE_FFN_PREFILL_CHUNK_T) {
+            const int tc = (int)(T - c0 < MOE_FFN_PREFILL_CHUNK_T ? T - c0 : MOE_FFN_PREFILL_CHUNK_T);
+            const uint16_t* xin = x + c0 * D;
+            if (norm_w) {
+                if (launch_rmsnorm(x + c0 * D, norm_w, eps, xn, tc, stream) != hipSuccess) return MOE_FFN_EHIP;
+                xin = xn;
+            }
+            const int r = run_prefill(tc, xin, router, experts, shared, y + c0 * D,
+                                      topk_idx ? topk_idx + c0 * K : nullptr, topk_weight ? topk_weight + c0 * K : nullptr,
+                                      (char*)workspace, norm_w ? x + c0 * D : nullptr, tr, stream);
+            if (r != MOE_FFN_OK) return r;
+        }
+        return MOE_FFN_OK;
+    }
+    if (norm_w && launch_rmsnorm(x, norm_w, eps, xn, (int)T, stream) != hipSuccess) return MOE_FFN_EHIP;
+    DecodeParams p{};
+    p.x = norm_w ? xn : x;
+    p.T = (int)T;
+    p.router_w = router->weight;
+    p.router_b = router->bias;
+    p.sh_gate_inp = shared ? shared->gate_inp : nullptr;
+    p.sh_gate = shared ? shared->gate : nullptr;
+    p.sh_up = shared ? shared->up : nullptr;
+    p.sh_down = shared ? shared->down : nullptr;
+    p.gate_q = experts->gate.qweight; p.gate_s = experts->gate.scales; p.gate_b = experts->gate.biases;
+    p.up_q = experts->up.qweight;     p.up_s = experts->up.scales;     p.up_b = experts->up.biases;
+    p.down_q = experts->down.qweight; p.down_s = experts->down.scales; p.down_b = experts->down.biases;
+    p.idx = topk_idx;
+    p.w = topk_weight;
+    p.resid = norm_w ? x : nullptr;
+    p.y = y;
+    return launch_decode(p, (char*)workspace, tr, stream) == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
 }
 
 }  // namespace
@@ -151,41 +212,37 @@ int moe_ffn_forward_traced(const moe_ffn_dims* dims, int64_t T, const uint16_t* 
     int st = validate(dims, T, x, router, experts, shared, y, topk_idx, topk_weight, workspace, workspace_bytes,
                       path);
     if (st != MOE_FFN_OK || T == 0) return st;
-    Tracer tr;
-    if (trace) {
-        tr.kernel = trace->kernel;
-        tr.start = (hipEvent_t)trace->start;
-        tr.stop = (hipEvent_t)trace->stop;
-    }
-    const bool decode = path == MOE_FFN_PATH_DECODE || (path == MOE_FFN_PATH_AUTO && T <= MOE_FFN_DECODE_MAX_T);
-    if (!decode) {
-        // passes over token slices of at most MOE_FFN_PREFILL_CHUNK_T (a
-        // traced kernel is bracketed in every pass; the events keep the last)
-        for (int64_t c0 = 0; c0 < T; c0 += MOE_FFN_PREFILL_CHUNK_T) {
-            const int tc = (int)(T - c0 < MOE_FFN_PREFILL_CHUNK_T ? T - c0 : MOE_FFN_PREFILL_CHUNK_T);
-            const int r = run_prefill(tc, x + c0 * D, router, experts, shared, y + c0 * D,
-                                      topk_idx ? topk_idx + c0 * K : nullptr, topk_weight ? topk_weight + c0 * K : nullptr,
-                                      (char*)workspace, tr, (hipStream_t)stream);
-            if (r != MOE_FFN_OK) return r;
-        }
-        return MOE_FFN_OK;
-    }
-    DecodeParams p{};
-    p.x = x;
-    p.T = (int)T;
-    p.router_w = router->weight;
-    p.router_b = router->bias;
-    p.sh_gate_inp = shared ? shared->gate_inp : nullptr;
-    p.sh_gate = shared ? shared->gate : nullptr;
-    p.sh_up = shared ? shared->up : nullptr;
-    p.sh_down = shared ? shared->down : nullptr;
-    p.gate_q = experts->gate.qweight; p.gate_s = experts->gate.scales; p.gate_b = experts->gate.biases;
-    p.up_q = experts->up.qweight;     p.up_s = experts->up.scales;     p.up_b = experts->up.biases;
-    p.down_q = experts->down.qweight; p.down_s = experts->down.scales; p.down_b = experts->down.biases;
-    p.idx = topk_idx;
-    p.w = topk_weight;
-    p.y = y;
-    return launch_decode(p, (char*)workspace, tr, (hipStream_t)stream) == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
+    return forward_impl(T, x, nullptr, 0.0f, nullptr, router, experts, shared, y, topk_idx, topk_weight, workspace,
+                        (hipStream_t)stream, path, trace);
+}
+
+size_t moe_ffn_block_workspace_size(const moe_ffn_dims* dims, int64_t T) {
+    if (!dims || !dims_ok(dims) || T <= 0 || T > MOE_FFN_MAX_T) return 0;
+    return block_workspace_bytes(T);
+}
+
+int moe_ffn_block_forward_traced(const moe_ffn_dims* dims, int64_t T, const uint16_t* h, const float* norm_weight,
+                                 float eps, const moe_ffn_router* router, const moe_ffn_experts* experts,
+                                 const moe_ffn_shared* shared, uint16_t* y, int32_t* topk_idx, float* topk_weight,
+                                 void* workspace, size_t ws_bytes, void* stream, int path,
+                                 const moe_ffn_trace* trace) {
+    // the FFN's own checks, then the norm's, then the larger workspace
+    const int st = validate(dims, T, h, router, experts, shared, y, topk_idx, topk_weight, workspace, ws_bytes, path);
+    if (T == 0 || (st != MOE_FFN_OK && st != MOE_FFN_EWORKSPACE)) return st;
+    if (!norm_weight || !(eps >= 0.0f) || !__builtin_isfinite(eps)) return MOE_FFN_EINVAL;
+    if (!al16(norm_weight)) return MOE_FFN_EALIGN;
+    if (st != MOE_FFN_OK || ws_bytes < block_workspace_bytes(T)) return MOE_FFN_EWORKSPACE;
+    uint16_t* xn = (uint16_t*)((char*)workspace + up(workspace_bytes(T)));
+    return forward_impl(T, h, norm_weight, eps, xn, router, experts, shared, y, topk_idx, topk_weight, workspace,
+                        (hipStream_t)stream, path, trace);
+}
+
+int moe_ffn_block_forward(const moe_ffn_dims* dims, int64_t T, const uint16_t* h, const float* norm_weight, float eps,
+                          const moe_ffn_router* router, const moe_ffn_experts* experts, const moe_ffn_shared* shared,
+                          uint16_t* y, int32_t* topk_idx, float* topk_weight, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    return moe_ffn_block_forward_traced(dims, T, h, norm_weight, eps, router, experts, shared, y, topk_idx,
+                                        topk_weight, workspace, workspace_bytes, stream, MOE_FFN_PATH_AUTO, nullptr);
 }
 
 int moe_ffn_forward_path(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,

@@ -50,6 +50,7 @@ struct PrefillGemmParams {
     const uint16_t *gate_b, *up_b, *down_b;
     const uint16_t *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
     uint16_t* partial;  // fp16 [N_assign, D]
+    const uint16_t* resid;  // bf16 [T, D] added to y before its rounding, or nullptr
     uint16_t* y;
     int T;
 };
@@ -60,6 +61,8 @@ hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const flo
                               const uint16_t* sh_gate, const uint16_t* sh_up, uint16_t* hs, int T, const Tracer& tr,
                               hipStream_t s);
 hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hipStream_t s);
+// xn[T, D] bf16 = RMS-normalised h times w (k_norm.hip)
+hipError_t launch_rmsnorm(const uint16_t* h, const float* w, float eps, uint16_t* xn, int T, hipStream_t s);
 
 // ---- decode path (k_decode.hip), T <= 64
 struct DecodeLayout {
@@ -74,6 +77,7 @@ struct DecodeParams {
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
     int32_t* idx;  // user outputs or nullptr
     float* w;
+    const uint16_t* resid;  // bf16 [T, D] added to y before its rounding, or nullptr
     uint16_t* y;
 };
 size_t decode_workspace_bytes(int T, DecodeLayout* L);

@@ -273,4 +273,94 @@ def pin_gate_up_order(O):
     assert all(rel(b[t], a[t]) > 0.2 for t in range(x.shape[0]))
 
 
+# ----------------------------------------------------------------- block boundary
+def _bf(v: float) -> int:
+    """bf16 bits of a value that bf16 holds exactly."""
+    f = np.array([v], dtype=np.float32)
+    b = int(f.view(np.uint32)[0])
+    assert b & 0xFFFF == 0, v
+    return b >> 16
+
+
+def pin_rmsnorm_one_hot(O):
+    """A one-hot row a*e_j of n = 64 values has mean(x^2) = a^2/64, so with
+    eps = 0 the scale is 8/|a| and only entry j is non-zero: sign(a) * 8 *
+    w_j, exact in bf16 for these weights; with eps = 3 and a = 8 the mean is
+    1, sqrt(1 + 3) = 2 and the entry is 4 * w_j."""
+    n = 64
+    w = np.linspace(0.25, 2.0, n, dtype=np.float32) * np.float32(0.5)  # distinct, exact in bf16 x 8
+    w = synth.bf16_to_f32(synth.f32_to_bf16(w))
+    for j, a, eps, want in ((5, 3.0, 0.0, 8.0), (40, -0.75, 0.0, -8.0), (17, 8.0, 3.0, 4.0)):
+        x = np.zeros(n, dtype=np.uint16)
+        x[j] = _bf(a)
+        out = O.rmsnorm_bf16(x, w, eps)
+        assert np.count_nonzero(out) == 1, (j, a)
+        assert out[j] == _bf(float(np.float32(want) * w[j])), (j, hex(out[j]))
+
+
+def pin_rmsnorm_constant_row(O):
+    """A constant row c: mean(x^2) = c^2.  eps = 0 gives sign(c) * w exactly;
+    eps = 3c^2 gives sqrt(4c^2) = 2|c|, so sign(c) * w / 2 exactly."""
+    n = 2048
+    w = synth.bf16_to_f32(synth.f32_to_bf16(np.linspace(0.5, 1.5, n, dtype=np.float32)))
+    for c in (2.0, -0.375, 1.5):
+        x = np.full(n, _bf(c), dtype=np.uint16)
+        out = synth.bf16_to_f32(O.rmsnorm_bf16(x, w, 0.0))
+        assert np.array_equal(out, np.sign(c) * w), c
+        out = synth.bf16_to_f32(O.rmsnorm_bf16(x, w, 3.0 * c * c))
+        assert np.array_equal(out, np.sign(c) * w * np.float32(0.5)), c
+
+
+def pin_rmsnorm_ties_to_even(O):
+    """The normalised value is rounded once to bf16, halfway cases to even:
+    one-hot rows of n = 64 (scale 8/a) with weights putting 8 * w exactly
+    halfway between two bf16 values (1 + 2^-8 -> 1, 1 + 3*2^-8 -> 1 + 2^-6)."""
+    n = 64
+    for wv, want in ((1.0 + 2.0 ** -8, 1.0), (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6), (1.0 + 2.0 ** -9, 1.0)):
+        w = np.full(n, np.float32(wv / 8.0), dtype=np.float32)
+        assert float(w[0]) * 8.0 == wv
+        x = np.zeros(n, dtype=np.uint16)
+        x[9] = _bf(1.0)
+        assert O.rmsnorm_bf16(x, w, 0.0)[9] == _bf(want), wv
+
+
+def pin_rmsnorm_invariants(O):
+    """With eps = 0 the normalisation ignores power-of-two scalings of the
+    row (exact in binary) and is odd in x."""
+    x = synth.x_rows(21, 1, 2048, nthreads=1)[0]
+    w = synth.bf16_to_f32(synth.f32_to_bf16(np.linspace(0.8, 1.2, 2048, dtype=np.float32)))
+    base = O.rmsnorm_bf16(x, w, 0.0)
+    for k in (-3, 1, 4):
+        xs = synth.f32_to_bf16(synth.bf16_to_f32(x) * np.float32(2.0 ** k))
+        assert np.array_equal(O.rmsnorm_bf16(xs, w, 0.0), base), k
+    neg = (x ^ np.uint16(0x8000)).astype(np.uint16)
+    got = O.rmsnorm_bf16(neg, w, 0.0)
+    nz = synth.bf16_to_f32(base) != 0
+    assert np.array_equal(got[nz], (base ^ np.uint16(0x8000))[nz])
+
+
+def pin_block_residual(O):
+    """The block adds the un-normalised input: with every routed scale and
+    bias zero and no shared expert the FFN is 0 and y = h exactly; in
+    general the FFN part is the forward of the normalised rows."""
+    lay = tiny_layer(shared=False)
+    for arr in (lay.gate.scales, lay.gate.biases, lay.up.scales, lay.up.biases, lay.down.scales, lay.down.biases):
+        arr[:] = 0
+    h = tiny_x(seed=8, T=5)
+    w = synth.bf16_to_f32(synth.f32_to_bf16(np.linspace(0.5, 1.5, TINY.d_model, dtype=np.float32)))
+    r = O.block_forward(lay, h, w, 1e-6, nthreads=1)
+    assert np.array_equal(r["y"], synth.bf16_to_f32(h).astype(np.float64))
+    lay = tiny_layer()
+    r = O.block_forward(lay, h, w, 1e-6, nthreads=2)
+    for t in range(h.shape[0]):
+        assert np.array_equal(r["xn"][t], O.rmsnorm_bf16(h[t], w, 1e-6))
+    f = O.forward(lay, r["xn"], nthreads=1)
+    assert np.array_equal(r["idx"], f["idx"]) and np.array_equal(r["w"], f["w"])
+    ffn = r["y"] - synth.bf16_to_f32(h).astype(np.float64)
+    for t in range(h.shape[0]):
+        assert rel(ffn[t], f["y"][t]) <= 1e-12
+    r2 = O.block_forward(lay, h, w, 1e-6, tokens=np.array([3, 0]), nthreads=1)
+    assert np.array_equal(r2["y"], r["y"][[3, 0]])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -101,6 +101,37 @@ def test_rejects_bad_arguments(L):
 
 
 
+def _block(L, T=4, h=0x20000000, nw=0x21000000, eps=1e-6, y=0x30000000, ws=0x40000000, wsb=None, path=0,
+           layer=None):
+    layer = layer or _layer()
+    r, ex, sh = layer.structs()
+    wsb = moe.moe_ffn_block_workspace_size(max(T, 1)) if wsb is None else wsb
+    return L.moe_ffn_block_forward_traced(ctypes.byref(moe.DIMS), T, h, nw, eps, ctypes.byref(r), ctypes.byref(ex),
+                                          ctypes.byref(sh), y, None, None, ws, wsb, None, path, None)
+
+
+def test_block_entry_point_rejects_bad_arguments(L):
+    """The block entry point: the FFN's checks, then the norm weight and eps,
+    then its larger workspace (the FFN's size alone is not enough)."""
+    assert _block(L, T=0) == moe.MOE_FFN_OK
+    assert _block(L, T=-1) == moe.MOE_FFN_EINVAL
+    assert _block(L, h=None) == moe.MOE_FFN_EINVAL
+    assert _block(L, nw=None) == moe.MOE_FFN_EINVAL
+    assert _block(L, eps=-1e-6) == moe.MOE_FFN_EINVAL
+    assert _block(L, eps=float("nan")) == moe.MOE_FFN_EINVAL
+    assert _block(L, eps=float("inf")) == moe.MOE_FFN_EINVAL
+    assert _block(L, nw=0x21000004) == moe.MOE_FFN_EALIGN
+    assert _block(L, h=0x20000002) == moe.MOE_FFN_EALIGN
+    assert _block(L, ws=None) == moe.MOE_FFN_EWORKSPACE
+    assert _block(L, wsb=moe.moe_ffn_workspace_size(4)) == moe.MOE_FFN_EWORKSPACE
+    assert _block(L, path=9) == moe.MOE_FFN_EINVAL
+    for T in (1, 64, 65, 4096, 32768, 100000):
+        b, f = moe.moe_ffn_block_workspace_size(T), moe.moe_ffn_workspace_size(T)
+        assert b >= f + min(T, 32768) * 2048 * 2 and b % 256 == 0
+    assert moe.moe_ffn_block_workspace_size(40000) == moe.moe_ffn_block_workspace_size(32768)
+    assert moe.moe_ffn_block_workspace_size(0) == 0
+
+
 def test_workspace_is_bounded_by_the_prefill_slice(L):
     """Prefill runs in passes of at most MOE_FFN_PREFILL_CHUNK_T tokens, so
     the workspace stops growing there (and is never smaller than a pass

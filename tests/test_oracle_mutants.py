@@ -52,6 +52,14 @@ MUTANTS = [
      "for (int64_t o = 0; o < D; o++) yr[o] += eo[o];"),
     ("renorm_wrong_set", "for (int64_t r = 0; r < k; r++) ps += exp(logits[sel[r]] - mx) / z;",
      "for (int64_t r = 0; r < k; r++) ps += exp(logits[r] - mx) / z;"),
+    ("rms_sum_not_mean", "1.0 / sqrt(ss / (double)n + eps)", "1.0 / sqrt(ss + eps)"),
+    ("rms_no_eps", "1.0 / sqrt(ss / (double)n + eps)", "1.0 / sqrt(ss / (double)n)"),
+    ("rms_no_sqrt", "1.0 / sqrt(ss / (double)n + eps)", "1.0 / (ss / (double)n + eps)"),
+    ("rms_weight_shifted", "* scale * (double)weight[i]);", "* scale * (double)weight[(i + 1) % n]);"),
+    ("bf16_round_down", "r = ldexp(rint(ldexp(m, 8)), e - 8);", "r = ldexp(floor(ldexp(m, 8)), e - 8);"),
+    ("residual_missing", "y[n * D + o] += (double)moe_oracle_bf16_to_f32(h[t * D + o]);", ";"),
+    ("residual_of_normed", "y[n * D + o] += (double)moe_oracle_bf16_to_f32(h[t * D + o]);",
+     "y[n * D + o] += (double)moe_oracle_bf16_to_f32(xr[t * D + o]);"),
 ]
 
 
