@@ -8,6 +8,11 @@ token through all 40 layers (40 library calls on one stream).  Other
 workloads (single layers, flushed between repetitions) are available with
 --workload for measurement.
 
+With --block every call is the FFN sub-block with its boundary steps
+(moe_ffn_block_forward: RMSNorm of the input on the way in, residual add on
+the way out), with seeded per-layer norm weights; the workload name carries a
+"+block" suffix.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -122,6 +127,8 @@ def main():
     ap.add_argument("--flush", choices=["read", "write"], default="read",
                     help="how single-layer workloads evict the caches between calls: read 1 GiB (leaves clean "
                          "lines) or write 1 GiB (leaves the infinity cache full of dirty lines to write back)")
+    ap.add_argument("--block", action="store_true",
+                    help="time the FFN sub-block (RMSNorm in, residual out) instead of the bare FFN")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (calibrates PMC byte counters)")
     args = ap.parse_args()
@@ -154,15 +161,19 @@ def main():
 
     # ---------------------------------------------------------------- inputs
     n_cpu_layers = min(nlayers, 8)
-    host_layers, dev_layers, xs = [], [], []
+    host_layers, dev_layers, xs, nws = [], [], [], []
+    EPS = float(np.float32(1e-6))
     t0 = time.time()
     for l in range(nlayers):
         layer = synth.make_layer(l, zipf_s=wl["zipf"])
         x = synth.x_rows(l, T, 2048)
         dev_layers.append(moe.DeviceLayer.from_host(layer, dev))
         xs.append(torch.from_numpy(x.view(np.int16)).to(dev))
+        nw = (1.0 + 0.2 * np.random.default_rng(1000 + l).standard_normal(2048)).astype(np.float32)
+        nw = synth.bf16_to_f32(synth.f32_to_bf16(nw))
+        nws.append(torch.from_numpy(nw).to(dev))
         if l < n_cpu_layers:
-            host_layers.append((layer, x))
+            host_layers.append((layer, x, nw))
         del layer
         if nlayers > 1 and (l % 8 == 7 or l == nlayers - 1):
             log(f"generated and uploaded layer {l + 1}/{nlayers} ({time.time() - t0:.1f}s)")
@@ -170,7 +181,7 @@ def main():
     ys = [torch.empty((T, 2048), dtype=torch.int16, device=dev) for _ in range(nlayers)]
     idxs = [torch.empty((T, 8), dtype=torch.int32, device=dev) for _ in range(nlayers)]
     ws_ = [torch.empty((T, 8), dtype=torch.float32, device=dev) for _ in range(nlayers)]
-    wspace = moe.alloc_workspace(T, dev)
+    wspace = moe.alloc_workspace(T, dev, block=args.block)
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if wl["flush"] else None
     if flush_buf is not None:
         flush_buf.fill_(1)
@@ -178,9 +189,14 @@ def main():
         flush_sink = torch.empty((), dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
 
-    def call(l, trace=None):
-        moe.moe_ffn_forward_traced(xs[l], dev_layers[l], ys[l], wspace, idxs[l], ws_[l], stream=stream,
-                                   path=args.path, trace=trace)
+    def call(l, trace=None, strm=None):
+        strm = strm or stream
+        if args.block:
+            moe.moe_ffn_block_forward_traced(xs[l], nws[l], EPS, dev_layers[l], ys[l], wspace, idxs[l], ws_[l],
+                                             stream=strm, path=args.path, trace=trace)
+        else:
+            moe.moe_ffn_forward_traced(xs[l], dev_layers[l], ys[l], wspace, idxs[l], ws_[l], stream=strm,
+                                       path=args.path, trace=trace)
 
     dom_kernel = moe.KERNEL_EXPERT_GU
 
@@ -229,8 +245,7 @@ def main():
         with torch.cuda.graph(g, stream=cap):
             for s in range(nsteps):
                 for l in range(nlayers):
-                    moe.moe_ffn_forward_path(xs[l], dev_layers[l], ys[l], wspace, idxs[l], ws_[l], stream=cap,
-                                             path=args.path)
+                    call(l, strm=cap)
         torch.cuda.synchronize()
         t = time.perf_counter()
         g.replay()
@@ -302,7 +317,7 @@ def main():
                     kernel="expert_gate_up", alg_flops_per_launch=flops,
                     avg_launch_us=round(kernel_ms * 1e3, 2))
     step_bytes = sum(d * EXPERT_BYTES + SHARED_BYTES + ROUTER_BYTES + GATE_INP_BYTES + T * 2048 * 4
-                     for d in distinct)
+                     + (2048 * 4 + T * 2048 * 2 if args.block else 0) for d in distinct)
     log(f"step {ms_per_step * 1e3:.1f} us, {value:.1f} tok/s, step bytes {step_bytes / 1e6:.1f} MB "
         f"-> {step_bytes / (wall / args.steps) / 1e9:.0f} GB/s; dominant kernel {kernel_ms * 1e3:.2f} us/launch")
 
@@ -328,7 +343,8 @@ def main():
             done, t = 0, time.perf_counter()
             with cf.ThreadPoolExecutor(threads) as ex:
                 while time.perf_counter() - t < 10.0:
-                    list(ex.map(lambda hx: O.forward(hx[0], hx[1], nthreads=1), host_layers))
+                    list(ex.map(lambda hx: (O.block_forward(hx[0], hx[1], hx[2], EPS, nthreads=1) if args.block
+                                            else O.forward(hx[0], hx[1], nthreads=1)), host_layers))
                     done += len(host_layers)
             el = time.perf_counter() - t
             cpu = dict(value=round((done / nlayers) * T / el, 3), unit="tokens/s", cores=threads, kind="oracle",
@@ -337,12 +353,15 @@ def main():
         else:
             # strided slices of the layer's tokens (every stride-th token, next
             # offset each pass, wrapping around) until about 10 s have passed
-            layer, x = host_layers[0]
+            layer, x, nw0 = host_layers[0]
             stride = max(1, T // 256)
             done, passes, t = 0, 0, time.perf_counter()
             while time.perf_counter() - t < 10.0:
                 tok = np.arange(passes % stride, T, stride)
-                O.forward(layer, x, tokens=tok, nthreads=cores)
+                if args.block:
+                    O.block_forward(layer, x, nw0, EPS, tokens=tok, nthreads=cores)
+                else:
+                    O.forward(layer, x, tokens=tok, nthreads=cores)
                 done += tok.size
                 passes += 1
             el = time.perf_counter() - t
@@ -365,7 +384,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "T": T, "layers": nlayers,
+        "config": {"workload": args.workload + ("+block" if args.block else ""), "T": T, "layers": nlayers,
                    "router_bias_zipf_s": wl["zipf"], "distinct_experts_per_layer": float(np.mean(distinct)),
                    "alg_bytes_per_step": int(step_bytes)},
         "roofline": roof,
