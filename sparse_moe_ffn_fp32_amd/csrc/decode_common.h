@@ -33,6 +33,9 @@ struct DecodeArgs {
     int32_t* uoff;   // [E]
     int32_t* pairs;  // [8T] (t*8 + r), grouped by distinct expert, t ascending
     const uint16_t* resid;  // bf16 [T, D] added to y before its rounding, or nullptr
+    const float* nw;        // T <= TINY_T: RMSNorm weights (x un-normalised), or nullptr
+    float eps;
+    uint16_t* xn;           // T <= TINY_T with nw: the normalised rows, bf16 [T, D]
     uint16_t* y;
 };
 

@@ -864,7 +864,18 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     a.xsum = (float*)(ws + L.xsum);
     a.y = p.y;
     a.resid = p.resid;
-    if (p.T <= TINY_T) return launch_decode_tiny(a, tr, s);
+    if (p.T <= TINY_T) {
+        // the normalisation runs inside the first launch
+        a.nw = p.norm_w;
+        a.eps = p.eps;
+        a.xn = p.xn;
+        return launch_decode_tiny(a, tr, s);
+    }
+    if (p.norm_w) {
+        const hipError_t e = launch_rmsnorm(p.x, p.norm_w, p.eps, p.xn, p.T, s);
+        if (e != hipSuccess) return e;
+        a.x = p.xn;
+    }
     launch_decode_t(a, tr, s);
     return hipGetLastError();
 }

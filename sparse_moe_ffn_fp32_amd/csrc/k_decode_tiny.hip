@@ -26,6 +26,9 @@
 //      pairs) and shared gate/up + SwiGLU (4 features per block, one row per
 //      wave); one block copies x into the codes' K order, sums its pieces
 //      and computes the shared-expert gate, from one round trip.
+//      For the block entry point every block of A first RMS-normalises the
+//      rows itself (no launch of its own), and the copy block also writes
+//      the normalised rows out.
 //   C  routed gate/up + SwiGLU: block = one (token, rank) pair x 8 features;
 //      the block's first wave derives the pair's expert from the token's
 //      logits (DPP top-8) so no routing launch is needed; each block also
@@ -86,22 +89,83 @@ __device__ __forceinline__ float group_param(uint32_t pairw, int g) {
 }
 
 // ------------------------------------------------------------------ A
-// NT = T tokens (compiled per token count: every loop bound is a constant).
+// Block entry point: the RMS normalisation of the NT residual rows
+// (qwen35moe Forward-Pass Design, "Block scaffold"; ds4.c study notes Part 3,
+// section 3, trace 1: x / sqrt(mean(x^2) + eps) * weight, squares summed in
+// double) runs inside every block of this launch instead of in a launch of
+// its own.  Thread tid of the 512 holds elements 4 tid .. 4 tid + 3 of each
+// row (hx, nw: loaded before the block's own weight loads); the sum of
+// squares is reduced in one fixed order (lane order within a wave by a
+// butterfly, then waves 0..7), so every block forms bit-identical normalised
+// rows, each value rounded once from double to bf16.  They are left in LDS
+// (xs, [NT][D/2] u32) for the block's dot products.
 template <int NT>
+__device__ __forceinline__ void norm_rows_to_lds(const u32x2 (&hx)[NT], const f32x4& nw, float eps,
+                                                 double (*red)[NT], uint32_t* xs, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const double v0 = lo_bf16(hx[t][0]), v1 = hi_bf16(hx[t][0]), v2 = lo_bf16(hx[t][1]), v3 = hi_bf16(hx[t][1]);
+        double ss = v0 * v0;
+        ss += v1 * v1;
+        ss += v2 * v2;
+        ss += v3 * v3;
+        ss = wave_sum_f64(ss);
+        if (lane == 0) red[wave][t] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        double ss = red[0][t];
+#pragma unroll
+        for (int w = 1; w < 8; w++) ss += red[w][t];
+        const double scale = 1.0 / __builtin_sqrt(ss / (double)D + (double)eps);
+        const double v0 = lo_bf16(hx[t][0]), v1 = hi_bf16(hx[t][0]), v2 = lo_bf16(hx[t][1]), v3 = hi_bf16(hx[t][1]);
+        u32x2 o;
+        o[0] = (uint32_t)f64_to_bf16_rne(v0 * scale * (double)nw[0]) |
+               ((uint32_t)f64_to_bf16_rne(v1 * scale * (double)nw[1]) << 16);
+        o[1] = (uint32_t)f64_to_bf16_rne(v2 * scale * (double)nw[2]) |
+               ((uint32_t)f64_to_bf16_rne(v3 * scale * (double)nw[3]) << 16);
+        *(u32x2*)(xs + t * (D / 2) + 2 * tid) = o;
+    }
+    __syncthreads();
+}
+
+// NT = T tokens (compiled per token count: every loop bound is a constant);
+// NORM: x is the residual stream, normalised here first (a.nw, a.eps).
+template <int NT, bool NORM>
 __global__ void __launch_bounds__(512) k_tiny_a(DecodeArgs a) {
     __shared__ float red[8][2 * NT];
+    __shared__ double red64[8][NT];
+    __shared__ uint32_t xs[NORM ? NT * (D / 2) : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x;
+    u32x2 hx[NT];
+    f32x4 nw;
+    if (NORM) {
+#pragma unroll
+        for (int t = 0; t < NT; t++) hx[t] = *(const u32x2*)(a.x + (size_t)t * D + 4 * tid);
+        nw = *(const f32x4*)(a.nw + 4 * tid);
+    }
     if (b == TA_ROUTER_BLK + TA_SHARED_BLK) {
         // x -> perm8 copy (pairs j, j+4 of every 8-block), its 32-element
         // piece sums and the shared-expert gate, from one round trip: thread
         // tid < 256 (waves 0-3) holds elements 8 tid .. 8 tid + 7 of every
         // token
+        u32x4 gi = u32x4{0u, 0u, 0u, 0u};
+        if (wave < 4 && a.sgi) gi = ((const u32x4*)a.sgi)[tid];
+        if (NORM) norm_rows_to_lds<NT>(hx, nw, a.eps, red64, xs, tid);
         if (wave < 4) {  // every wave reaches the barrier below
             u32x4 d[NT];
 #pragma unroll
-            for (int t = 0; t < NT; t++) d[t] = ((const u32x4*)(a.x + (size_t)t * D))[tid];
-            const u32x4 gi = a.sgi ? ((const u32x4*)a.sgi)[tid] : u32x4{0u, 0u, 0u, 0u};
+            for (int t = 0; t < NT; t++) {
+                if (NORM) {
+                    d[t] = ((const u32x4*)(xs + t * (D / 2)))[tid];
+                    ((u32x4*)(a.xn + (size_t)t * D))[tid] = d[t];
+                } else {
+                    d[t] = ((const u32x4*)(a.x + (size_t)t * D))[tid];
+                }
+            }
 #pragma unroll
             for (int t = 0; t < NT; t++) {
                 u32x4 o;
@@ -142,10 +206,18 @@ __global__ void __launch_bounds__(512) k_tiny_a(DecodeArgs a) {
         for (int i = 0; i < 4; i++) {
             const int c = lane + 64 * (2 * i + kh);
             wv[i] = *(const f32x4*)(wrow + 4 * c);
+            if (!NORM)
 #pragma unroll
-            for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x2*)(a.x + (size_t)t * D + 4 * c);
+                for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x2*)(a.x + (size_t)t * D + 4 * c);
         }
         __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
+        if (NORM) {
+            norm_rows_to_lds<NT>(hx, nw, a.eps, red64, xs, tid);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x2*)(xs + t * (D / 2) + 2 * (lane + 64 * (2 * i + kh)));
+        }
         float acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; t++) {
@@ -181,10 +253,18 @@ __global__ void __launch_bounds__(512) k_tiny_a(DecodeArgs a) {
     for (int i = 0; i < 4; i++) {
         const int c = lane + 64 * i;
         wv[i] = *(const u32x4*)(wrow + 8 * c);
+        if (!NORM)
 #pragma unroll
-        for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x4*)(a.x + (size_t)t * D + 8 * c);
+            for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x4*)(a.x + (size_t)t * D + 8 * c);
     }
     __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
+    if (NORM) {
+        norm_rows_to_lds<NT>(hx, nw, a.eps, red64, xs, tid);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x4*)(xs + t * (D / 2) + 4 * (lane + 64 * i));
+    }
 #pragma unroll
     for (int t = 0; t < NT; t++) {
         float s = 0.0f;
@@ -410,7 +490,11 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
 template <int NT>
 hipError_t launch_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
     const int n_gu = NT * K * (F / TC_FEAT);
-    tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a<NT>, dim3(TA_ROUTER_BLK + TA_SHARED_BLK + 1), dim3(512), 0, s, a);
+    const dim3 ga(TA_ROUTER_BLK + TA_SHARED_BLK + 1);
+    if (a.nw)
+        tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a<NT, true>, ga, dim3(512), 0, s, a);
+    else
+        tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a<NT, false>, ga, dim3(512), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_tiny_c<NT>, dim3(n_gu + (a.sd ? TC_SDOWN_BLK : 0)), dim3(256), 0, s, a, n_gu);
     tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_tiny_d<NT>, dim3(D / TD_ROWS), dim3(TD_THREADS), 0, s, a);
     return hipGetLastError();

@@ -20,28 +20,6 @@
 
 namespace moe {
 
-// Nearest bf16 of a double, ties to even: round to fp32 by truncation with a
-// sticky last bit (round to odd: 24 bits keep the information the second
-// rounding needs), then to bf16 to nearest even.  Finite values only.
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
-    const float f = (float)d;
-    uint32_t u = __float_as_uint(f);
-    const double back = (double)f;
-    if (back != d) {
-        if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1;  // one fp32 ulp toward zero
-        u |= 1u;
-    }
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-    // fixed xor butterfly: every lane ends with the same, order-fixed value
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
-}
-
 __global__ void __launch_bounds__(256) k_rmsnorm(const uint16_t* __restrict__ h, const float* __restrict__ w, float eps,
                                                 uint16_t* __restrict__ xn, int T) {
     const int lane = threadIdx.x & 63;

@@ -33,6 +33,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Nearest bf16 of a finite double, ties to even: round to fp32 by truncation
+// with a sticky last bit (round to odd: 24 bits keep what the second rounding
+// needs), then to bf16 to nearest even.  One correct rounding overall.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
+    const float f = (float)d;
+    uint32_t u = __float_as_uint(f);
+    const double back = (double)f;
+    if (back != d) {
+        if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1;  // one fp32 ulp toward zero
+        u |= 1u;
+    }
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Double sum over the 64 lanes of a wave by a fixed xor butterfly: every lane
+// ends with the same, order-fixed value.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
 // K order inside every 8-element block of an fp16 operand row.  Position p
 // holds element kPerm8[p] = {0,4,1,5,2,6,3,7}[p]: the order in which one u32
 // of eight nibbles unpacks into four fp16 pairs (nibbles j and j+4 land in

@@ -176,9 +176,11 @@ int forward_impl(int64_t T, const uint16_t* x, const float* norm_w, float eps, u
         }
         return MOE_FFN_OK;
     }
-    if (norm_w && launch_rmsnorm(x, norm_w, eps, xn, (int)T, stream) != hipSuccess) return MOE_FFN_EHIP;
     DecodeParams p{};
-    p.x = norm_w ? xn : x;
+    p.x = x;
+    p.norm_w = norm_w;
+    p.eps = eps;
+    p.xn = xn;
     p.T = (int)T;
     p.router_w = router->weight;
     p.router_b = router->bias;

@@ -78,6 +78,12 @@ struct DecodeParams {
     int32_t* idx;  // user outputs or nullptr
     float* w;
     const uint16_t* resid;  // bf16 [T, D] added to y before its rounding, or nullptr
+    // norm_w != nullptr: x is the un-normalised residual stream; the path
+    // first forms xn = bf16(RMSNorm(x) * norm_w) (written to xn) and runs the
+    // FFN on it
+    const float* norm_w;
+    float eps;
+    uint16_t* xn;  // [T, D]
     uint16_t* y;
 };
 size_t decode_workspace_bytes(int T, DecodeLayout* L);

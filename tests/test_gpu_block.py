@@ -101,7 +101,7 @@ def check(layer, h, w, y, idx, wt, xn, O=None):
     return float(err.max())
 
 
-@pytest.mark.parametrize("T", [1, 4, 37, 64, 300])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 37, 64, 300])
 def test_block_forward(gpu, layer0, norm_w, T):
     h = block_inputs(layer0, norm_w, T, 400 + T)
     _say(f"block T={T}")
@@ -117,7 +117,7 @@ def test_block_forced_paths(gpu, layer0, norm_w, path):
     check(layer0, h, norm_w, y, idx, wt, xn)
 
 
-@pytest.mark.parametrize("T", [5, 300])
+@pytest.mark.parametrize("T", [2, 5, 300])
 def test_block_in_place(gpu, layer0, norm_w, T):
     """y written over h itself gives the out-of-place result, bit for bit."""
     h = block_inputs(layer0, norm_w, T, 90 + T)
@@ -128,7 +128,7 @@ def test_block_in_place(gpu, layer0, norm_w, T):
         assert np.array_equal(u, v)
 
 
-@pytest.mark.parametrize("T", [3, 100])
+@pytest.mark.parametrize("T", [1, 3, 100])
 def test_block_zero_ffn_returns_h(gpu, norm_w, T):
     """Every routed scale and bias zero and no shared expert: the FFN is
     exactly 0, so y = h bit for bit on both paths."""
