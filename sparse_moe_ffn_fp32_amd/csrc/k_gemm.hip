@@ -140,6 +140,7 @@ struct GemmSmem {
     uint32_t bq[C::Q4 ? QBUF : 1][C::Q4 ? GEMM_BN * BQS : 4];
     uint32_t sb[C::Q4 ? GEMM_BN * C::SROW : 4];  // (bias << 16) | scale, bf16 bits
     float rw[MODE == MODE_DOWN ? GEMM_BM : 4];   // DOWN: routing weight x 2^6 per row
+    int32_t pos[MODE == MODE_SDOWN ? GEMM_BM * K : 4];  // SDOWN: each row's partial positions
 };
 
 // One block's work; `bid` is the block's index within its mode's grid
@@ -244,6 +245,15 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     }
     if constexpr (MODE == MODE_DOWN) {
         if (tid < GEMM_BM) sm.rw[tid] = g.wflat[g.perm[seg + m0 + min(tid, rows - 1)]] * PARTIAL_SCALE;
+    }
+    if constexpr (MODE == MODE_SDOWN) {
+        // the combine's partial rows, read long before the epilogue needs
+        // them (rows past the end repeat the last valid row)
+#pragma unroll
+        for (int i = 0; i < GEMM_BM * K / 256; i++) {
+            const int q = tid + 256 * i;
+            sm.pos[q] = g.pos_of[(size_t)(m0 + min(q / K, rows - 1)) * K + q % K];
+        }
     }
 
     f32x16 acc[4][2];
@@ -496,39 +506,53 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
                         for (int nt = 0; nt < 2; nt++) yb[acc_row(mt, v) * YS + 64 * (wave & 1) + 32 * nt + l32] = acc[mt][nt][v];
             }
             __syncthreads();
-            // 128 rows x 16 pieces of 8 outputs
+            // 128 rows x 16 pieces of 8 outputs, four rows at a time: every
+            // load of the four (8 partials, residual, gate each) is issued
+            // before any is used; rows past the end load the last valid row
+            // and store nothing
+            const uint16_t* const p_in = pinned(g.p_in);
+            const uint16_t* const resid = pinned(g.resid);
+            uint16_t* const yo = pinned(g.y);
 #pragma unroll 1
-            for (int i = 0; i < 8; i++) {
-                const int pc = tid + 256 * i, r = pc >> 4, c = pc & 15;
-                if (r < rows) {
+            for (int i0 = 0; i0 < 8; i0 += 4) {
+                u32x4 pv[4][K], rv[4];
+                float sg[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int pc = tid + 256 * (i0 + u), r = min(pc >> 4, rows - 1), c = pc & 15;
                     const int t = m0 + r, o = nblk * GEMM_BN + pass * 128 + 8 * c;
+#pragma unroll
+                    for (int rr = 0; rr < K; rr++) pv[u][rr] = *(const u32x4*)&p_in[(size_t)sm.pos[r * K + rr] * D + o];
+                    rv[u] = resid ? *(const u32x4*)&resid[(size_t)t * D + o] : u32x4{0u, 0u, 0u, 0u};
+                    sg[u] = g.sgate[t];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int pc = tid + 256 * (i0 + u), r = pc >> 4, c = pc & 15;
                     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int rr = 0; rr < K; rr++) {
-                        const u32x4 pv = *(const u32x4*)&g.p_in[(size_t)g.pos_of[t * K + rr] * D + o];
+                    for (int rr = 0; rr < K; rr++)
 #pragma unroll
                         for (int j = 0; j < 4; j++) {
                             // copy the element to a scalar first: a bit cast of the
                             // vector-element expression itself is miscompiled by
                             // clang 22 (it reads element 0 for every j)
-                            const uint32_t pw = pv[j];
+                            const uint32_t pw = pv[u][rr][j];
                             const f16x2 h2 = __builtin_bit_cast(f16x2, pw);
                             sum[2 * j] += (float)h2[0];
                             sum[2 * j + 1] += (float)h2[1];
                         }
-                    }
-                    const float sg = g.sgate[t];
                     // the residual (added last, before the one rounding)
-                    const u32x4 rv = g.resid ? *(const u32x4*)&g.resid[(size_t)t * D + o] : u32x4{0u, 0u, 0u, 0u};
+                    const int rl = min(r, rows - 1);
                     u32x4 out;
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
-                        const uint32_t rj = rv[j];
-                        const float y0 = sum[2 * j] * (1.0f / PARTIAL_SCALE) + sg * yb[r * YS + 8 * c + 2 * j] + bf16_to_f32(rj & 0xffffu);
-                        const float y1 = sum[2 * j + 1] * (1.0f / PARTIAL_SCALE) + sg * yb[r * YS + 8 * c + 2 * j + 1] + bf16_to_f32(rj >> 16);
+                        const uint32_t rj = rv[u][j];
+                        const float y0 = sum[2 * j] * (1.0f / PARTIAL_SCALE) + sg[u] * yb[rl * YS + 8 * c + 2 * j] + bf16_to_f32(rj & 0xffffu);
+                        const float y1 = sum[2 * j + 1] * (1.0f / PARTIAL_SCALE) + sg[u] * yb[rl * YS + 8 * c + 2 * j + 1] + bf16_to_f32(rj >> 16);
                         out[j] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
                     }
-                    *(u32x4*)&g.y[(size_t)t * D + o] = out;
+                    if (r < rows) *(u32x4*)&yo[(size_t)(m0 + r) * D + nblk * GEMM_BN + pass * 128 + 8 * c] = out;
                 }
             }
             __syncthreads();
