@@ -141,3 +141,46 @@ def test_block_zero_ffn_returns_h(gpu, norm_w, T):
     _say(f"block zero FFN T={T}")
     y = run_block(gpu, lay, h, norm_w)[0]
     assert np.array_equal(y, h)
+
+
+def test_block_prefill_in_slices(gpu, layer0, norm_w):
+    """The block entry point over 32768 + 7 tokens runs in two slices inside
+    one slice's workspace (each slice normalised into the same buffer, its
+    residual rows offset): the result equals, bit for bit, two separate calls
+    on the slices, and the oracle's block result on a sample that includes
+    the slice boundary and the ragged tail."""
+    import sparse_moe_ffn_fp32_amd as moe
+    torch = gpu.torch
+    chunk, tail = 32768, 7
+    T = chunk + tail
+    h = synth.x_rows(4242, T, D, sd=2.0)
+    dl = gpu.device_layer(layer0)
+    hd = torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).cuda()
+    wd = torch.from_numpy(np.ascontiguousarray(norm_w, dtype=np.float32)).cuda()
+    ws = moe.alloc_workspace(T, block=True)
+    assert ws.numel() == moe.moe_ffn_block_workspace_size(chunk)
+
+    def call(lo, hi):
+        y = torch.empty((hi - lo, D), dtype=torch.int16, device="cuda")
+        idx = torch.empty((hi - lo, 8), dtype=torch.int32, device="cuda")
+        wt = torch.empty((hi - lo, 8), dtype=torch.float32, device="cuda")
+        moe.moe_ffn_block_forward_traced(hd[lo:hi], wd, EPS, dl, y, ws, idx, wt, path=2)
+        torch.cuda.synchronize()
+        return y.cpu().numpy().view(np.uint16), idx.cpu().numpy(), wt.cpu().numpy()
+
+    _say(f"block prefill in slices T={T}")
+    whole = call(0, T)
+    parts = [call(0, chunk), call(chunk, T)]
+    for u, a, b in zip(whole, parts[0], parts[1]):
+        assert np.array_equal(u, np.concatenate([a, b])), "sliced block pass differs from separate calls"
+    sample = np.unique(np.concatenate([np.arange(0, T, 1024), np.arange(chunk - 4, T)]))
+    ref = oracle.get().block_forward(layer0, h, norm_w, EPS, tokens=sample)
+    ok = ref["margin"] >= workloads.MIN_MARGIN  # tokens whose experts are decided beyond rounding
+    assert ok.sum() >= 0.9 * sample.size
+    y, idx, wt = whole[0][sample], whole[1][sample], whole[2][sample]
+    assert np.array_equal(idx[ok], ref["idx"][ok]), "experts differ from the oracle's"
+    assert np.abs(wt[ok].astype(np.float64) - ref["w"][ok]).max() <= W_ABS
+    got = bf16_to_f64(y[ok])
+    err = np.linalg.norm(got - ref["y"][ok], axis=1) / np.linalg.norm(ref["y"][ok], axis=1)
+    assert err.max() <= Y_REL_L2, f"rel L2 {err.max():.3e}"
+    _say(f"{int(ok.sum())} of {sample.size} sampled tokens checked, max rel L2 {err.max():.3e}")
