@@ -92,9 +92,20 @@ typedef struct {
 } moe_q4_tensor;
 
 /* ffn_{gate,up,down}_exps: gate and up are [E, d_ff, d_model] (out = d_ff),
- * down is [E, d_model, d_ff]. */
+ * down is [E, d_model, d_ff].
+ *
+ * gate_up_fused = 1 selects the fused gate/up layout of "SSD Streaming Expert
+ * Layers" (section Quantized Layout and its fused-gate_up note): one tensor
+ * [E, 2*d_ff, d_model] in `gate` (qweight [E, 2*d_ff, d_model/8], scales and
+ * biases [E, 2*d_ff, d_model/64]) in which expert e holds its d_ff gate rows
+ * and then its d_ff up rows (rows interleaved per expert, not all experts'
+ * gate rows followed by all experts' up rows); `up` must then be all NULL.
+ * gate_up_fused = 0 (the zero-initialised default): separate tensors.  Any
+ * other value, or `up` pointers given with the fused layout, is
+ * MOE_FFN_EINVAL.  Both layouts compute the same values bit for bit. */
 typedef struct {
     moe_q4_tensor gate, up, down;
+    int32_t gate_up_fused;
 } moe_ffn_experts;
 
 /* ffn_gate_inp: weight fp32 [E, d_model]; bias fp32 [E] or NULL, added to the

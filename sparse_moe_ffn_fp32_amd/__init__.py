@@ -44,7 +44,7 @@ class Q4Tensor(ctypes.Structure):
 
 
 class Experts(ctypes.Structure):
-    _fields_ = [("gate", Q4Tensor), ("up", Q4Tensor), ("down", Q4Tensor)]
+    _fields_ = [("gate", Q4Tensor), ("up", Q4Tensor), ("down", Q4Tensor), ("gate_up_fused", ctypes.c_int32)]
 
 
 class Router(ctypes.Structure):
@@ -120,9 +120,12 @@ class DeviceLayer:
     sh_gate: object
     sh_up: object
     sh_down: object
+    gate_up_fused: bool = False  # gate holds one [E, 2F, ...] tensor, up is empty
 
     @staticmethod
-    def from_host(layer, device="cuda") -> "DeviceLayer":
+    def from_host(layer, device="cuda", fused: bool = False) -> "DeviceLayer":
+        """fused: upload gate and up as one [E, 2F, ...] tensor, each
+        expert's F gate rows followed by its F up rows."""
         import numpy as np
         import torch
 
@@ -134,13 +137,23 @@ class DeviceLayer:
         def q(q4):
             return (t(q4.qweight, np.int32), t(q4.scales, np.int16), t(q4.biases, np.int16))
 
-        return DeviceLayer(t(layer.router_w, np.float32), t(layer.router_b, np.float32), q(layer.gate),
-                           q(layer.up), q(layer.down), t(layer.sh_gate_inp, np.int16), t(layer.sh_gate, np.int16),
-                           t(layer.sh_up, np.int16), t(layer.sh_down, np.int16))
+        if fused:
+            E = layer.dims.n_experts
+            cat = lambda a, b: np.concatenate([a.reshape(E, -1), b.reshape(E, -1)], axis=1)
+            gate = (t(cat(layer.gate.qweight, layer.up.qweight), np.int32),
+                    t(cat(layer.gate.scales, layer.up.scales), np.int16),
+                    t(cat(layer.gate.biases, layer.up.biases), np.int16))
+            up = (None, None, None)
+        else:
+            gate, up = q(layer.gate), q(layer.up)
+        return DeviceLayer(t(layer.router_w, np.float32), t(layer.router_b, np.float32), gate, up, q(layer.down),
+                           t(layer.sh_gate_inp, np.int16), t(layer.sh_gate, np.int16), t(layer.sh_up, np.int16),
+                           t(layer.sh_down, np.int16), fused)
 
     def structs(self):
         r = Router(_ptr(self.router_w), _ptr(self.router_b))
-        ex = Experts(*(Q4Tensor(*(_ptr(a) for a in m)) for m in (self.gate, self.up, self.down)))
+        ex = Experts(*(Q4Tensor(*(_ptr(a) for a in m)) for m in (self.gate, self.up, self.down)),
+                     int(self.gate_up_fused))
         sh = None
         if self.sh_gate is not None:
             sh = Shared(_ptr(self.sh_gate_inp), _ptr(self.sh_gate), _ptr(self.sh_up), _ptr(self.sh_down))

@@ -17,6 +17,7 @@ struct DecodeArgs {
     const uint16_t *sgi, *sg, *su, *sd;  // shared expert (sg == nullptr: none)
     const uint32_t *gq, *uq, *dq;
     const uint16_t *gs, *gb, *us, *ub, *ds, *db;
+    int gu_rows;     // rows per expert in the gate/up arrays (F, or 2F fused)
     float* logits;   // [T, E]
     uint16_t* xp;    // bf16 [T, D], perm8
     float* xsum;     // [T, D/32] sums of x over 32-element chunks (T <= TINY_T)

@@ -401,7 +401,7 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     // up share one row layout, so one byte offset serves both code arrays
     auto row_of = [&](int k) {
         const int kk = min(k, n_units - 1);
-        return (uint32_t)(__builtin_amdgcn_readfirstlane(sm.unit[kk][0]) * F + __builtin_amdgcn_readfirstlane(sm.unit[kk][1])) +
+        return (uint32_t)(__builtin_amdgcn_readfirstlane(sm.unit[kk][0]) * a.gu_rows + __builtin_amdgcn_readfirstlane(sm.unit[kk][1])) +
                (uint32_t)(16 * wave + n);
     };
     const __amdgpu_buffer_rsrc_t rgq = buffer_rsrc(a.gq), ruq = buffer_rsrc(a.uq);
@@ -847,6 +847,7 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     a.sgi = p.sh_gate_inp; a.sg = p.sh_gate; a.su = p.sh_up; a.sd = p.sh_down;
     a.gq = p.gate_q; a.uq = p.up_q; a.dq = p.down_q;
     a.gs = p.gate_s; a.gb = p.gate_b; a.us = p.up_s; a.ub = p.up_b; a.ds = p.down_s; a.db = p.down_b;
+    a.gu_rows = p.gu_rows;
     a.logits = (float*)(ws + L.logits);
     a.xp = (uint16_t*)(ws + L.xp);
     a.hs = (float*)(ws + L.hs);

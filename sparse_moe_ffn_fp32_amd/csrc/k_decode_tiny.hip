@@ -345,7 +345,7 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
     __syncthreads();
     const int e = s_expert & (E - 1);
     // wave w: features f0 + 2w, f0 + 2w + 1; rows gate f, gate f+1, up f, up f+1
-    const size_t row0 = (size_t)e * F + f0 + 2 * wave;
+    const size_t row0 = (size_t)e * a.gu_rows + f0 + 2 * wave;
     const uint32_t* rows[4] = {a.gq + row0 * (D / 8), a.gq + (row0 + 1) * (D / 8), a.uq + row0 * (D / 8),
                                a.uq + (row0 + 1) * (D / 8)};
     const uint16_t* srow[4] = {a.gs + row0 * (D / G), a.gs + (row0 + 1) * (D / G), a.us + row0 * (D / G),

@@ -109,6 +109,7 @@ struct GemmArgs {
     const int32_t* tile_count;
     const float* wflat;      // [T*K] routing weights by assignment
     const float* sgate;      // [T]
+    int gu_rows;             // GU: rows per expert in the gate/up arrays (F, or 2F fused)
     // weights
     const uint32_t* q[2];    // GU: gate, up; DOWN: down
     const uint16_t* sc[2];
@@ -470,7 +471,7 @@ __device__ __forceinline__ void gemm_block_w8(const GemmArgs& g, GemmSmem<MODE>&
     auto wrow = [&](int n, int& mat) -> size_t {  // global weight row of LDS row n
         if constexpr (C::PAIRED) {
             mat = (n >> 5) & 1;
-            return (size_t)e * F + nblk * 128 + 32 * (n >> 6) + (n & 31);
+            return (size_t)e * g.gu_rows + nblk * 128 + 32 * (n >> 6) + (n & 31);
         } else {
             mat = 0;
             return (size_t)e * D + nblk * GEMM_BN + n;
@@ -766,7 +767,7 @@ __device__ __forceinline__ void gemm_block_q4(const GemmArgs& g, Q4Smem<MODE>& s
     auto wrow = [&](int n, int& mat) -> size_t {  // global weight row of LDS row n
         if constexpr (C::PAIRED) {
             mat = (n >> 5) & 1;
-            return (size_t)e * F + nblk * 128 + 32 * (n >> 6) + (n & 31);
+            return (size_t)e * g.gu_rows + nblk * 128 + 32 * (n >> 6) + (n & 31);
         } else {
             mat = 0;
             return (size_t)e * D + nblk * GEMM_BN + n;
@@ -1053,6 +1054,7 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.xh = p.xh; g.h = p.h; g.hs = p.hs;
     g.perm = p.perm; g.pos_of = p.pos_of; g.offs = p.offs; g.tiles = p.tiles; g.tile_count = p.tile_count;
     g.wflat = p.wflat; g.sgate = p.sgate;
+    g.gu_rows = p.gu_rows;
     g.T = p.T;
     const int bm = gemm_bm(p.T);
     const int max_tiles = (p.T * K + bm - 1) / bm + E;  // bound on the sort's tile count

@@ -59,6 +59,26 @@ bool dims_ok(const moe_ffn_dims* d) {
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The gate and up tensors as the kernels see them: row (e, f) of gate at
+// gq + (e * rows + f) * D/8 (scales, biases at (e * rows + f) * D/G), the
+// same for up.  Separate tensors: rows = F.  Fused [E, 2F, ...] tensor:
+// rows = 2F, up = gate + F rows.
+struct GateUp {
+    const uint32_t *gq, *uq;
+    const uint16_t *gs, *us, *gb, *ub;
+    int rows;
+};
+GateUp resolve_gate_up(const moe_ffn_experts* ex) {
+    const moe_q4_tensor& g = ex->gate;
+    if (ex->gate_up_fused) {
+        if (!g.qweight || !g.scales || !g.biases) return {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 2 * F};
+        return {g.qweight, g.qweight + (size_t)F * (D / 8), g.scales, g.scales + (size_t)F * (D / G),
+                g.biases, g.biases + (size_t)F * (D / G), 2 * F};
+    }
+    const moe_q4_tensor& u = ex->up;
+    return {g.qweight, u.qweight, g.scales, u.scales, g.biases, u.biases, F};
+}
+
 int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
              const moe_ffn_experts* ex, const moe_ffn_shared* sh, uint16_t* y, int32_t* topk_idx,
              float* topk_weight, void* ws, size_t ws_bytes, int path) {
@@ -67,8 +87,10 @@ int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_f
     if (T > MOE_FFN_MAX_T) return MOE_FFN_EUNSUPPORTED;
     if (T == 0) return MOE_FFN_OK;
     if (!x || !y || !router || !router->weight || !ex) return MOE_FFN_EINVAL;
-    const void* req[] = {ex->gate.qweight, ex->gate.scales, ex->gate.biases, ex->up.qweight, ex->up.scales,
-                         ex->up.biases, ex->down.qweight, ex->down.scales, ex->down.biases};
+    if (ex->gate_up_fused != 0 && ex->gate_up_fused != 1) return MOE_FFN_EINVAL;
+    if (ex->gate_up_fused && (ex->up.qweight || ex->up.scales || ex->up.biases)) return MOE_FFN_EINVAL;
+    const GateUp gu = resolve_gate_up(ex);
+    const void* req[] = {gu.gq, gu.gs, gu.gb, gu.uq, gu.us, gu.ub, ex->down.qweight, ex->down.scales, ex->down.biases};
     for (const void* p : req)
         if (!p) return MOE_FFN_EINVAL;
     if (sh && (!sh->gate || !sh->up || !sh->down)) return MOE_FFN_EINVAL;
@@ -130,8 +152,10 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     p.tile_count = tile_count;
     p.wflat = w;
     p.sgate = sgate;
-    p.gate_q = ex->gate.qweight; p.gate_s = ex->gate.scales; p.gate_b = ex->gate.biases;
-    p.up_q = ex->up.qweight;     p.up_s = ex->up.scales;     p.up_b = ex->up.biases;
+    const GateUp gu = resolve_gate_up(ex);
+    p.gate_q = gu.gq; p.gate_s = gu.gs; p.gate_b = gu.gb;
+    p.up_q = gu.uq;   p.up_s = gu.us;   p.up_b = gu.ub;
+    p.gu_rows = gu.rows;
     p.down_q = ex->down.qweight; p.down_s = ex->down.scales; p.down_b = ex->down.biases;
     p.sh_gate = sh ? sh->gate : nullptr;
     p.sh_up = sh ? sh->up : nullptr;
@@ -188,8 +212,10 @@ int forward_impl(int64_t T, const uint16_t* x, const float* norm_w, float eps, u
     p.sh_gate = shared ? shared->gate : nullptr;
     p.sh_up = shared ? shared->up : nullptr;
     p.sh_down = shared ? shared->down : nullptr;
-    p.gate_q = experts->gate.qweight; p.gate_s = experts->gate.scales; p.gate_b = experts->gate.biases;
-    p.up_q = experts->up.qweight;     p.up_s = experts->up.scales;     p.up_b = experts->up.biases;
+    const GateUp gu = resolve_gate_up(experts);
+    p.gate_q = gu.gq; p.gate_s = gu.gs; p.gate_b = gu.gb;
+    p.up_q = gu.uq;   p.up_s = gu.us;   p.up_b = gu.ub;
+    p.gu_rows = gu.rows;
     p.down_q = experts->down.qweight; p.down_s = experts->down.scales; p.down_b = experts->down.biases;
     p.idx = topk_idx;
     p.w = topk_weight;

@@ -48,6 +48,7 @@ struct PrefillGemmParams {
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *up_s, *down_s;
     const uint16_t *gate_b, *up_b, *down_b;
+    int gu_rows;  // rows per expert in the gate/up arrays (F, or 2F for the fused layout)
     const uint16_t *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
     uint16_t* partial;  // fp16 [N_assign, D]
     const uint16_t* resid;  // bf16 [T, D] added to y before its rounding, or nullptr
@@ -75,6 +76,7 @@ struct DecodeParams {
     const uint16_t *sh_gate_inp, *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
+    int gu_rows;   // rows per expert in the gate/up arrays (F, or 2F for the fused layout)
     int32_t* idx;  // user outputs or nullptr
     float* w;
     const uint16_t* resid;  // bf16 [T, D] added to y before its rounding, or nullptr

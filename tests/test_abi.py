@@ -101,6 +101,35 @@ def test_rejects_bad_arguments(L):
 
 
 
+def test_fused_gate_up_arguments(L):
+    """The fused gate/up layout: one tensor in gate, up all NULL; accepted
+    layouts get as far as the workspace check (no launch here)."""
+    fused = _layer()
+    fused.up = (None, None, None)
+    fused.gate_up_fused = True
+    assert _call(L, layer=fused, ws=None) == moe.MOE_FFN_EWORKSPACE
+    both = _layer()
+    both.gate_up_fused = True  # up given as well
+    assert _call(L, layer=both) == moe.MOE_FFN_EINVAL
+    bad = _layer()
+    bad.up = (None, None, None)
+    bad.gate_up_fused = 2
+    assert _call(L, layer=bad) == moe.MOE_FFN_EINVAL
+    lay = _layer()
+    lay.up = (None, None, None)
+    lay.gate_up_fused = True
+    lay.gate = (lay.gate[0], None, lay.gate[2])
+    assert _call(L, layer=lay) == moe.MOE_FFN_EINVAL
+    lay = _layer()
+    lay.up = (None, None, None)
+    lay.gate_up_fused = True
+    lay.gate = (_Fake(0x60000008), lay.gate[1], lay.gate[2])
+    assert _call(L, layer=lay) == moe.MOE_FFN_EALIGN
+    sep = _layer()
+    sep.up = (None, None, None)  # separate layout without up
+    assert _call(L, layer=sep) == moe.MOE_FFN_EINVAL
+
+
 def _block(L, T=4, h=0x20000000, nw=0x21000000, eps=1e-6, y=0x30000000, ws=0x40000000, wsb=None, path=0,
            layer=None):
     layer = layer or _layer()

@@ -1,0 +1,90 @@
+"""GPU tests of the fused gate/up layout (SSD Streaming Expert Layers,
+section Quantized Layout: gate and up of an expert stored as one tensor,
+its gate rows on top of its up rows): bit-for-bit agreement with separate
+tensors on every path, agreement with the oracle, and detection of the
+whole-layer concatenation that mixes up the experts' rows."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import workloads
+from gpu_common import GpuRunner, output_check, bf16_to_f64, Y_REL_L2
+
+pytestmark = pytest.mark.gpu
+PATHS = {"auto": 0, "decode": 1, "prefill": 2}
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_moe_ffn_fp32_amd as moe
+    moe.lib()
+    return GpuRunner(torch)
+
+
+@pytest.fixture(scope="module")
+def layer0():
+    return workloads.layer_for(0)
+
+
+@pytest.fixture(scope="module")
+def fused0(gpu, layer0):
+    import sparse_moe_ffn_fp32_amd as moe
+    return moe.DeviceLayer.from_host(layer0, fused=True)
+
+
+@pytest.mark.parametrize("T,path", [(1, "auto"), (3, "auto"), (4, "auto"), (37, "decode"), (64, "auto"),
+                                    (37, "prefill"), (300, "auto")])
+def test_fused_gate_up_equals_separate(gpu, layer0, fused0, T, path):
+    x, _, _ = workloads.enforce_margin(layer0, T, 900 + T)
+    _say(f"fused gate/up T={T} path={path}")
+    a = gpu.run(layer0, x, path=PATHS[path])
+    b = gpu.run(layer0, x, path=PATHS[path], dl=fused0)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v), "fused layout differs from separate tensors"
+    _say(output_check(layer0, x, b[0]))
+
+
+def test_fused_gate_up_large_tiles(gpu, layer0, fused0):
+    """A pass of 16384 tokens runs the 256-row tile kernels: the same bit
+    for bit (inputs without a routing margin: only the two layouts are
+    compared)."""
+    T = 16384
+    x = synth.x_rows(55, T, 2048)
+    _say(f"fused gate/up T={T}")
+    a = gpu.run(layer0, x)
+    b = gpu.run(layer0, x, dl=fused0)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v), "fused layout differs from separate tensors"
+
+
+def test_whole_layer_concatenation_is_detected(gpu, layer0):
+    """All experts' gate rows followed by all experts' up rows is not the
+    fused layout: passed as one, expert e >= 1 reads other experts' rows and
+    the output leaves the tolerance on (nearly) every token."""
+    import sparse_moe_ffn_fp32_amd as moe
+    torch = gpu.torch
+    dl = moe.DeviceLayer.from_host(layer0)
+    wrong = moe.DeviceLayer.from_host(layer0)
+    wrong.gate = tuple(torch.cat([g.reshape(-1), u.reshape(-1)]) for g, u in zip(dl.gate, dl.up))
+    wrong.up = (None, None, None)
+    wrong.gate_up_fused = True
+    T = 37
+    x, _, _ = workloads.enforce_margin(layer0, T, 4242)
+    y = gpu.run(layer0, x, dl=wrong)[0]
+    ref = oracle.get().forward(layer0, x)["y"]
+    rel = np.linalg.norm(bf16_to_f64(y) - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    _say(f"whole-layer concatenation: rel L2 min {rel.min():.3e}")
+    assert np.mean(rel > 10 * Y_REL_L2) > 0.9
