@@ -109,10 +109,18 @@ typedef struct {
 } moe_ffn_experts;
 
 /* ffn_gate_inp: weight fp32 [E, d_model]; bias fp32 [E] or NULL, added to the
- * logits before the softmax (it moves both the selection and the weights). */
+ * logits before the softmax (it moves both the selection and the weights).
+ *
+ * weights_scale: the expert_weights_scale of the routed MoE call
+ * (qwen35moe Forward-Pass Design, "Shared-expert MoE FFN": gate = softmax,
+ * norm_topk_prob, scale = expert_weights_scale): every renormalised routing
+ * weight is multiplied by it before it weights its expert's output, and
+ * topk_weight reports the product.  0 (the zero-initialised default) is
+ * read as 1.  Negative, NaN or infinite values are MOE_FFN_EINVAL. */
 typedef struct {
     const float *weight;
     const float *bias;
+    float weights_scale;
 } moe_ffn_router;
 
 /* Shared expert, bf16: gate, up [d_ff_shared, d_model]; down [d_model,

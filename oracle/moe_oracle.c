@@ -85,6 +85,11 @@ int moe_oracle_select(const double *logits, int64_t E, int64_t k, int32_t *sel, 
     return MOE_ORACLE_OK;
 }
 
+/* The routed MoE call scales the renormalised weights by
+ * expert_weights_scale (qwen35moe Forward-Pass Design, "Shared-expert MoE
+ * FFN"); 0 stands for the unscaled default 1. */
+static double weights_scale(const moe_oracle_layer *L) { return L->weights_scale == 0.0 ? 1.0 : L->weights_scale; }
+
 /* silu(z) = z * sigmoid(z) (ds4.c notes Part 3, MoE trace 1). */
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
@@ -172,6 +177,7 @@ static int forward_one(const fwd_job *j, int64_t n) {
         for (int64_t i = 0; i < D; i++) xd[i] = (double)moe_oracle_bf16_to_f32(xr[i]);
         moe_oracle_router_logits(d, j->L, xr, lg);
         st = moe_oracle_select(lg, E, k, sel, ww, &mg);
+        for (int64_t r = 0; r < k; r++) ww[r] *= weights_scale(j->L);
     }
     if (st == MOE_ORACLE_OK) {
         double *yr = j->y + n * D;
@@ -266,6 +272,7 @@ static void *route_range(void *p) {
         double mg = 0.0;
         moe_oracle_router_logits(j->d, j->L, j->x + t * D, lg);
         j->status = moe_oracle_select(lg, E, k, sel, ww, &mg);
+        for (int64_t r = 0; r < k; r++) ww[r] *= weights_scale(j->L);
         if (j->idx) for (int64_t r = 0; r < k; r++) j->idx[n * k + r] = sel[r];
         if (j->w) for (int64_t r = 0; r < k; r++) j->w[n * k + r] = ww[r];
         if (j->margin) j->margin[n] = mg;

@@ -67,6 +67,7 @@ typedef struct {
     const uint16_t *sh_gate;      /* bf16 [Fs, D]; NULL => no shared expert */
     const uint16_t *sh_up;        /* bf16 [Fs, D] */
     const uint16_t *sh_down;      /* bf16 [D, Fs] */
+    double weights_scale;         /* expert_weights_scale; 0 is read as 1 */
 } moe_oracle_layer;
 
 enum { MOE_ORACLE_OK = 0, MOE_ORACLE_EINVAL = -1, MOE_ORACLE_ENOMEM = -2 };

@@ -48,7 +48,7 @@ class Experts(ctypes.Structure):
 
 
 class Router(ctypes.Structure):
-    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("weights_scale", ctypes.c_float)]
 
 
 class Shared(ctypes.Structure):
@@ -121,6 +121,7 @@ class DeviceLayer:
     sh_up: object
     sh_down: object
     gate_up_fused: bool = False  # gate holds one [E, 2F, ...] tensor, up is empty
+    weights_scale: float = 1.0   # expert_weights_scale (0 is read as 1)
 
     @staticmethod
     def from_host(layer, device="cuda", fused: bool = False) -> "DeviceLayer":
@@ -148,10 +149,10 @@ class DeviceLayer:
             gate, up = q(layer.gate), q(layer.up)
         return DeviceLayer(t(layer.router_w, np.float32), t(layer.router_b, np.float32), gate, up, q(layer.down),
                            t(layer.sh_gate_inp, np.int16), t(layer.sh_gate, np.int16), t(layer.sh_up, np.int16),
-                           t(layer.sh_down, np.int16), fused)
+                           t(layer.sh_down, np.int16), fused, float(getattr(layer, "weights_scale", 1.0)))
 
     def structs(self):
-        r = Router(_ptr(self.router_w), _ptr(self.router_b))
+        r = Router(_ptr(self.router_w), _ptr(self.router_b), float(self.weights_scale))
         ex = Experts(*(Q4Tensor(*(_ptr(a) for a in m)) for m in (self.gate, self.up, self.down)),
                      int(self.gate_up_fused))
         sh = None

@@ -14,6 +14,7 @@ struct DecodeArgs {
     int T;
     const float* wr;
     const float* rbias;
+    float wscale;    // factor on the renormalised routing weights
     const uint16_t *sgi, *sg, *su, *sd;  // shared expert (sg == nullptr: none)
     const uint32_t *gq, *uq, *dq;
     const uint16_t *gs, *gb, *us, *ub, *ds, *db;
@@ -59,7 +60,7 @@ __device__ inline void write_token_route(const DecodeArgs& a, int t, int lane, c
         p[r] = __expf(sel_v[r] - sel_v[0]);
         s += p[r];
     }
-    const float inv = 1.0f / s;
+    const float inv = a.wscale / s;  // expert_weights_scale folded into the normaliser
     if (lane < K) {
         float wv = 0.f;
         int iv = 0;

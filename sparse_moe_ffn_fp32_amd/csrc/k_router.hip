@@ -42,7 +42,8 @@ __global__ void __launch_bounds__(256) k_split_router(const float* __restrict__ 
 // and sgate.  Lane l holds experts l, l+64, l+128, l+192.
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, const uint16_t* __restrict__ x,
                                               const uint16_t* __restrict__ gate_inp, int32_t* __restrict__ idx_out,
-                                              float* __restrict__ w_out, float* __restrict__ sgate_out, int T) {
+                                              float* __restrict__ w_out, float* __restrict__ sgate_out, float wscale,
+                                              int T) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -60,7 +61,7 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
         p[r] = __expf(sel_v[r] - sel_v[0]);
         s += p[r];
     }
-    const float inv = 1.0f / s;
+    const float inv = wscale / s;  // expert_weights_scale folded into the normaliser
     if (lane < K) {
         float wv = 0.0f;
         int iv = 0;
@@ -100,8 +101,8 @@ hipError_t launch_split_router(const float* wr, uint16_t* wr2, hipStream_t s) {
 }
 
 hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
-                       float* sgate, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, gate_inp, idx, w, sgate, T);
+                       float* sgate, float wscale, int T, hipStream_t s) {
+    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, gate_inp, idx, w, sgate, wscale, T);
     return hipGetLastError();
 }
 

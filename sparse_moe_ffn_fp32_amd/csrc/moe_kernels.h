@@ -25,8 +25,9 @@ struct Tracer {
 
 // ---- router (k_router.hip)
 hipError_t launch_split_router(const float* wr, uint16_t* wr2, hipStream_t s);
+// wscale multiplies every renormalised routing weight
 hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
-                       float* sgate, int T, hipStream_t s);
+                       float* sgate, float wscale, int T, hipStream_t s);
 
 // ---- routing sort (k_sort.hip)
 int sort_blocks(int N);
@@ -73,6 +74,7 @@ struct DecodeParams {
     const uint16_t* x;
     int T;
     const float *router_w, *router_b;
+    float wscale;  // factor on the renormalised routing weights
     const uint16_t *sh_gate_inp, *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;

@@ -363,4 +363,39 @@ def pin_block_residual(O):
     assert np.array_equal(r2["y"], r["y"][[3, 0]])
 
 
+def pin_weights_scale(O):
+    """expert_weights_scale multiplies the renormalised weights and nothing
+    else: the routing is unchanged, the reported weights are the unscaled
+    ones times the factor, and without a shared expert a factor of 2 doubles
+    y exactly (a power of two commutes with every rounding of the double
+    sums); 0 stands for the unscaled default; with the shared expert only the
+    routed part scales (factor 0.3, to double rounding)."""
+    import copy
+    lay = tiny_layer(shared=False)
+    x = tiny_x(seed=12, T=6)
+    base = O.forward(lay, x, nthreads=1)
+    two = copy.copy(lay)
+    two.weights_scale = 2.0
+    r2 = O.forward(two, x, nthreads=1)
+    assert np.array_equal(r2["idx"], base["idx"])
+    assert np.array_equal(r2["w"], 2.0 * base["w"])
+    assert np.array_equal(r2["y"], 2.0 * base["y"])
+    assert np.array_equal(O.route(two, x)["w"], 2.0 * O.route(lay, x)["w"])
+    zero = copy.copy(lay)
+    zero.weights_scale = 0.0
+    r0 = O.forward(zero, x, nthreads=1)
+    assert np.array_equal(r0["y"], base["y"]) and np.array_equal(r0["w"], base["w"])
+    sh = tiny_layer()
+    no_routed = copy.deepcopy(sh)
+    for arr in (no_routed.down.scales, no_routed.down.biases):
+        arr[:] = 0
+    shared_part = O.forward(no_routed, x, nthreads=1)["y"]
+    s3 = copy.copy(sh)
+    s3.weights_scale = 0.3
+    a = O.forward(sh, x, nthreads=1)["y"] - shared_part
+    b = O.forward(s3, x, nthreads=1)["y"] - shared_part
+    for t in range(x.shape[0]):
+        assert rel(b[t], 0.3 * a[t]) <= 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -130,6 +130,19 @@ def test_fused_gate_up_arguments(L):
     assert _call(L, layer=sep) == moe.MOE_FFN_EINVAL
 
 
+def test_weights_scale_arguments(L):
+    """expert_weights_scale: finite and >= 0 (0 = unscaled); anything else is
+    rejected before any launch."""
+    for bad in (-1.0, float("nan"), float("inf"), -float("inf")):
+        lay = _layer()
+        lay.weights_scale = bad
+        assert _call(L, layer=lay) == moe.MOE_FFN_EINVAL, bad
+    for ok in (0.0, 1.0, 2.5):
+        lay = _layer()
+        lay.weights_scale = ok
+        assert _call(L, layer=lay, ws=None) == moe.MOE_FFN_EWORKSPACE, ok
+
+
 def _block(L, T=4, h=0x20000000, nw=0x21000000, eps=1e-6, y=0x30000000, ws=0x40000000, wsb=None, path=0,
            layer=None):
     layer = layer or _layer()

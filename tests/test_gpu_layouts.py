@@ -1,8 +1,10 @@
-"""GPU tests of the fused gate/up layout (SSD Streaming Expert Layers,
+"""GPU tests of the layout and router variants.  The fused gate/up layout (SSD Streaming Expert Layers,
 section Quantized Layout: gate and up of an expert stored as one tensor,
 its gate rows on top of its up rows): bit-for-bit agreement with separate
 tensors on every path, agreement with the oracle, and detection of the
-whole-layer concatenation that mixes up the experts' rows."""
+whole-layer concatenation that mixes up the experts' rows.
+expert_weights_scale: routing unchanged, weights and routed output scaled,
+checked against the oracle of the scaled layer."""
 from __future__ import annotations
 
 import sys
@@ -88,3 +90,30 @@ def test_whole_layer_concatenation_is_detected(gpu, layer0):
     rel = np.linalg.norm(bf16_to_f64(y) - ref, axis=1) / np.linalg.norm(ref, axis=1)
     _say(f"whole-layer concatenation: rel L2 min {rel.min():.3e}")
     assert np.mean(rel > 10 * Y_REL_L2) > 0.9
+
+
+@pytest.mark.parametrize("T,path", [(1, "auto"), (4, "auto"), (37, "decode"), (37, "prefill"), (300, "auto")])
+def test_weights_scale(gpu, layer0, T, path):
+    """expert_weights_scale 2.5 (qwen35moe Forward-Pass Design, "Shared-expert
+    MoE FFN"): the same experts, weights 2.5 times the unscaled ones, y
+    against the oracle of the scaled layer; 0 gives the unscaled result bit
+    for bit."""
+    import copy
+    import sparse_moe_ffn_fp32_amd as moe
+    from gpu_common import W_ABS
+    x, _, _ = workloads.enforce_margin(layer0, T, 700 + T)
+    lay = copy.copy(layer0)
+    lay.weights_scale = 2.5
+    _say(f"weights_scale 2.5 T={T} path={path}")
+    base = gpu.run(layer0, x, path=PATHS[path])
+    got = gpu.run(lay, x, path=PATHS[path], dl=moe.DeviceLayer.from_host(lay))
+    assert np.array_equal(got[1], base[1]), "the scale moved the routing"
+    ref = oracle.get().forward(lay, x)
+    assert np.array_equal(got[1], ref["idx"])
+    assert np.abs(got[2].astype(np.float64) - ref["w"]).max() <= 2.5 * W_ABS
+    _say(output_check(lay, x, got[0]))
+    zero = copy.copy(layer0)
+    zero.weights_scale = 0.0
+    z = gpu.run(zero, x, path=PATHS[path], dl=moe.DeviceLayer.from_host(zero))
+    for u, v in zip(z, base):
+        assert np.array_equal(u, v), "weights_scale 0 must be the unscaled default"

@@ -25,6 +25,9 @@ MUTANTS = [
     ("group_bias_index", "float b = moe_oracle_bf16_to_f32(bi[i / group]);",
      "float b = moe_oracle_bf16_to_f32(bi[(i / group + 1) % groups]);"),
     ("router_no_bias", "if (L->router_b) acc += (double)L->router_b[e];", ""),
+    ("weights_scale_ignored", "ww[r] *= weights_scale(j->L);", "ww[r] *= 1.0;"),
+    ("weights_scale_no_default", "L->weights_scale == 0.0 ? 1.0 : L->weights_scale", "L->weights_scale"),
+    ("weights_scale_squared", "ww[r] *= weights_scale(j->L);", "ww[r] *= weights_scale(j->L) * weights_scale(j->L);"),
     ("router_transposed", "L->router_w[e * d->d_model + i]", "L->router_w[i * d->n_experts + e]"),
     ("tie_upper_index", "if (!taken[e] && (best < 0 || logits[e] > logits[best])) best = e;",
      "if (!taken[e] && (best < 0 || logits[e] >= logits[best])) best = e;"),
