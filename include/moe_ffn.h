@@ -58,6 +58,11 @@ extern "C" {
 #define MOE_FFN_EHIP (-5)         /* a kernel launch failed (hipGetLastError) */
 
 /* execution paths (moe_ffn_forward_path) */
+/* Routing score (moe_ffn_router.gating). */
+#define MOE_FFN_GATING_SOFTMAX 0       /* softmax over the experts, top-k renormalised (qwen35moe) */
+#define MOE_FFN_GATING_SQRT_SOFTPLUS 1 /* score sqrt(softplus(logit)) (ds4.c study notes Part 3, MoE
+                                          trace 3, router probabilities), top-k renormalised */
+
 #define MOE_FFN_PATH_AUTO 0    /* decode for T <= MOE_FFN_DECODE_MAX_T, else prefill */
 #define MOE_FFN_PATH_DECODE 1  /* small-T path: weight-streaming GEMV kernels */
 #define MOE_FFN_PATH_PREFILL 2 /* large-T path: routing sort + grouped MFMA GEMMs */
@@ -121,6 +126,15 @@ typedef struct {
     const float *weight;
     const float *bias;
     float weights_scale;
+    /* gating: MOE_FFN_GATING_SOFTMAX (0, the default) or
+     * MOE_FFN_GATING_SQRT_SOFTPLUS: score_e = sqrt(softplus(logit_e)) with
+     * softplus(z) = log(1 + e^z) computed stably.  Both select the top_k
+     * experts by logit (the sqrt-softplus score rises strictly with the
+     * logit, so the ranking is the same; ties to the lower index) and weight
+     * them by their scores renormalised to sum 1 (for softmax: the selected
+     * softmax probabilities), times weights_scale.  Other values are
+     * MOE_FFN_EINVAL. */
+    int32_t gating;
 } moe_ffn_router;
 
 /* Shared expert, bf16: gate, up [d_ff_shared, d_model]; down [d_model,

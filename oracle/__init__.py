@@ -41,7 +41,8 @@ class _Layer(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("gate", _Q4), ("up", _Q4), ("down", _Q4),
                 ("sh_gate_inp", ctypes.c_void_p), ("sh_gate", ctypes.c_void_p),
-                ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p), ("weights_scale", ctypes.c_double)]
+                ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p), ("weights_scale", ctypes.c_double),
+                ("gating", ctypes.c_int32)]
 
 
 def _ptr(a):
@@ -99,7 +100,7 @@ class Oracle:
     def _layer(self, lay) -> _Layer:
         return _Layer(_ptr(lay.router_w), _ptr(lay.router_b), self._q4(lay.gate), self._q4(lay.up),
                       self._q4(lay.down), _ptr(lay.sh_gate_inp), _ptr(lay.sh_gate), _ptr(lay.sh_up),
-                      _ptr(lay.sh_down), float(lay.weights_scale))
+                      _ptr(lay.sh_down), float(lay.weights_scale), int(lay.gating))
 
     # ----------------------------------------------------------------- steps
     def bf16_to_f32(self, bits: int) -> float:

@@ -90,6 +90,23 @@ int moe_oracle_select(const double *logits, int64_t E, int64_t k, int32_t *sel, 
  * FFN"); 0 stands for the unscaled default 1. */
 static double weights_scale(const moe_oracle_layer *L) { return L->weights_scale == 0.0 ? 1.0 : L->weights_scale; }
 
+/* sqrt-softplus gating (ds4.c notes Part 3, MoE trace 3, router
+ * probabilities): score = sqrt(softplus(logit)), softplus(z) = log(1 + e^z)
+ * written as max(z, 0) + log1p(e^-|z|) (the same value, no overflow).  The
+ * score rises strictly with the logit, so the experts chosen by logit are
+ * the experts chosen by score; their scores are renormalised to sum 1 (the
+ * weight step is not printed for this router: the reading taken is the
+ * renormalisation used with the softmax gate). */
+static void sqrt_softplus_weights(const double *logits, const int32_t *sel, int64_t k, double *w) {
+    double s = 0.0;
+    for (int64_t r = 0; r < k; r++) {
+        const double z = logits[sel[r]];
+        w[r] = sqrt(fmax(z, 0.0) + log1p(exp(-fabs(z))));
+        s += w[r];
+    }
+    for (int64_t r = 0; r < k; r++) w[r] /= s;
+}
+
 /* silu(z) = z * sigmoid(z) (ds4.c notes Part 3, MoE trace 1). */
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
@@ -177,6 +194,7 @@ static int forward_one(const fwd_job *j, int64_t n) {
         for (int64_t i = 0; i < D; i++) xd[i] = (double)moe_oracle_bf16_to_f32(xr[i]);
         moe_oracle_router_logits(d, j->L, xr, lg);
         st = moe_oracle_select(lg, E, k, sel, ww, &mg);
+        if (j->L->gating == 1) sqrt_softplus_weights(lg, sel, k, ww);
         for (int64_t r = 0; r < k; r++) ww[r] *= weights_scale(j->L);
     }
     if (st == MOE_ORACLE_OK) {
@@ -272,6 +290,7 @@ static void *route_range(void *p) {
         double mg = 0.0;
         moe_oracle_router_logits(j->d, j->L, j->x + t * D, lg);
         j->status = moe_oracle_select(lg, E, k, sel, ww, &mg);
+        if (j->L->gating == 1) sqrt_softplus_weights(lg, sel, k, ww);
         for (int64_t r = 0; r < k; r++) ww[r] *= weights_scale(j->L);
         if (j->idx) for (int64_t r = 0; r < k; r++) j->idx[n * k + r] = sel[r];
         if (j->w) for (int64_t r = 0; r < k; r++) j->w[n * k + r] = ww[r];

@@ -68,6 +68,7 @@ typedef struct {
     const uint16_t *sh_up;        /* bf16 [Fs, D] */
     const uint16_t *sh_down;      /* bf16 [D, Fs] */
     double weights_scale;         /* expert_weights_scale; 0 is read as 1 */
+    int32_t gating;               /* 0: softmax; 1: sqrt(softplus(logit)) scores */
 } moe_oracle_layer;
 
 enum { MOE_ORACLE_OK = 0, MOE_ORACLE_EINVAL = -1, MOE_ORACLE_ENOMEM = -2 };

@@ -23,6 +23,7 @@ MOE_FFN_EALIGN = -3
 MOE_FFN_EWORKSPACE = -4
 MOE_FFN_EHIP = -5
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+GATING_SOFTMAX, GATING_SQRT_SOFTPLUS = 0, 1
 DECODE_MAX_T = 64
 
 EXPORTED = ("moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_path", "moe_ffn_forward_traced",
@@ -48,7 +49,8 @@ class Experts(ctypes.Structure):
 
 
 class Router(ctypes.Structure):
-    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("weights_scale", ctypes.c_float)]
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("weights_scale", ctypes.c_float),
+                ("gating", ctypes.c_int32)]
 
 
 class Shared(ctypes.Structure):
@@ -122,6 +124,7 @@ class DeviceLayer:
     sh_down: object
     gate_up_fused: bool = False  # gate holds one [E, 2F, ...] tensor, up is empty
     weights_scale: float = 1.0   # expert_weights_scale (0 is read as 1)
+    gating: int = 0              # GATING_SOFTMAX or GATING_SQRT_SOFTPLUS
 
     @staticmethod
     def from_host(layer, device="cuda", fused: bool = False) -> "DeviceLayer":
@@ -149,10 +152,11 @@ class DeviceLayer:
             gate, up = q(layer.gate), q(layer.up)
         return DeviceLayer(t(layer.router_w, np.float32), t(layer.router_b, np.float32), gate, up, q(layer.down),
                            t(layer.sh_gate_inp, np.int16), t(layer.sh_gate, np.int16), t(layer.sh_up, np.int16),
-                           t(layer.sh_down, np.int16), fused, float(getattr(layer, "weights_scale", 1.0)))
+                           t(layer.sh_down, np.int16), fused, float(getattr(layer, "weights_scale", 1.0)),
+                           int(getattr(layer, "gating", 0)))
 
     def structs(self):
-        r = Router(_ptr(self.router_w), _ptr(self.router_b), float(self.weights_scale))
+        r = Router(_ptr(self.router_w), _ptr(self.router_b), float(self.weights_scale), int(self.gating))
         ex = Experts(*(Q4Tensor(*(_ptr(a) for a in m)) for m in (self.gate, self.up, self.down)),
                      int(self.gate_up_fused))
         sh = None

@@ -15,6 +15,7 @@ struct DecodeArgs {
     const float* wr;
     const float* rbias;
     float wscale;    // factor on the renormalised routing weights
+    int gating;      // MOE_FFN_GATING_*
     const uint16_t *sgi, *sg, *su, *sd;  // shared expert (sg == nullptr: none)
     const uint32_t *gq, *uq, *dq;
     const uint16_t *gs, *gb, *us, *ub, *ds, *db;
@@ -50,14 +51,14 @@ __device__ __forceinline__ void token_top8(const DecodeArgs& a, int t, int lane,
 }
 
 // One wave: write token t's routing, the expert ids and renormalised weights
-// (the softmax normaliser cancels under norm_topk_prob, so the weights are
-// the softmax of the eight selected logits).
+// (the selected scores over their sum; for softmax the full normaliser
+// cancels under norm_topk_prob: the softmax of the eight selected logits).
 __device__ inline void write_token_route(const DecodeArgs& a, int t, int lane, const float* sel_v, const int* sel_i,
                                          int* sidx) {
     float p[K], s = 0.0f;
 #pragma unroll
     for (int r = 0; r < K; r++) {
-        p[r] = __expf(sel_v[r] - sel_v[0]);
+        p[r] = route_score(sel_v[r], sel_v[0], a.gating);
         s += p[r];
     }
     const float inv = a.wscale / s;  // expert_weights_scale folded into the normaliser

@@ -843,7 +843,7 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     decode_workspace_bytes(p.T, &L);
     DecodeArgs a{};
     a.x = p.x; a.T = p.T;
-    a.wr = p.router_w; a.rbias = p.router_b; a.wscale = p.wscale;
+    a.wr = p.router_w; a.rbias = p.router_b; a.wscale = p.wscale; a.gating = p.gating;
     a.sgi = p.sh_gate_inp; a.sg = p.sh_gate; a.su = p.sh_up; a.sd = p.sh_down;
     a.gq = p.gate_q; a.uq = p.up_q; a.dq = p.down_q;
     a.gs = p.gate_s; a.gb = p.gate_b; a.us = p.up_s; a.ub = p.up_b; a.ds = p.down_s; a.db = p.down_b;

@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(256) k_split_router(const float* __restrict__ 
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, const uint16_t* __restrict__ x,
                                               const uint16_t* __restrict__ gate_inp, int32_t* __restrict__ idx_out,
                                               float* __restrict__ w_out, float* __restrict__ sgate_out, float wscale,
-                                              int T) {
+                                              int gating, int T) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -53,12 +53,12 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
     float sel_v[K];
     int sel_i[K];
     wave_top8(v, lane, sel_v, sel_i);
-    // norm_topk_prob: the full-softmax normaliser cancels, so the weights are
-    // the softmax over the eight selected logits.
+    // norm_topk_prob: the eight selected scores renormalised (for softmax
+    // the full normaliser cancels: the softmax over the selected logits)
     float p[K], s = 0.0f;
 #pragma unroll
     for (int r = 0; r < K; r++) {
-        p[r] = __expf(sel_v[r] - sel_v[0]);
+        p[r] = route_score(sel_v[r], sel_v[0], gating);
         s += p[r];
     }
     const float inv = wscale / s;  // expert_weights_scale folded into the normaliser
@@ -101,8 +101,9 @@ hipError_t launch_split_router(const float* wr, uint16_t* wr2, hipStream_t s) {
 }
 
 hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
-                       float* sgate, float wscale, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, gate_inp, idx, w, sgate, wscale, T);
+                       float* sgate, float wscale, int gating, int T, hipStream_t s) {
+    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, gate_inp, idx, w, sgate, wscale, gating,
+                       T);
     return hipGetLastError();
 }
 

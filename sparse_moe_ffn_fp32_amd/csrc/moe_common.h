@@ -275,6 +275,16 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// Routing score of a selected logit v relative to the top one v0, before
+// the renormalisation over the top k: softmax exp(v - v0) (the full-softmax
+// normaliser cancels), or sqrt(softplus(v)), softplus computed stably
+// (log1p(e^v); v beyond +-20 is v or e^v to fp32 precision).
+__device__ __forceinline__ float route_score(float v, float v0, int gating) {
+    if (gating == 0) return __expf(v - v0);
+    const float sp = v > 20.0f ? v : (v < -20.0f ? __expf(v) : log1pf(__expf(v)));
+    return __builtin_sqrtf(sp);
+}
+
 // Sum over the 64 lanes of a wave, the same value in every lane: row sums,
 // then rows (0,1) and (2,3) through v_permlane16_swap, then the two halves
 // through v_permlane32_swap.

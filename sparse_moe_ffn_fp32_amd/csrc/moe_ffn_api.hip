@@ -91,6 +91,7 @@ int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_f
     if (T == 0) return MOE_FFN_OK;
     if (!x || !y || !router || !router->weight || !ex) return MOE_FFN_EINVAL;
     if (!(router->weights_scale >= 0.0f) || router->weights_scale == INFINITY) return MOE_FFN_EINVAL;
+    if (router->gating != MOE_FFN_GATING_SOFTMAX && router->gating != MOE_FFN_GATING_SQRT_SOFTPLUS) return MOE_FFN_EINVAL;
     if (ex->gate_up_fused != 0 && ex->gate_up_fused != 1) return MOE_FFN_EINVAL;
     if (ex->gate_up_fused && (ex->up.qweight || ex->up.scales || ex->up.biases)) return MOE_FFN_EINVAL;
     const GateUp gu = resolve_gate_up(ex);
@@ -143,7 +144,7 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     chk(launch_prep_x(x, xh, T, s));
     chk(launch_router_gemm(xh, wr2, router->bias, logits, sh ? sh->gate : nullptr, sh ? sh->up : nullptr,
                            (uint16_t*)at(L.hs), T, tr, s));
-    chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, weights_scale(router), T, s));
+    chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, weights_scale(router), router->gating, T, s));
     chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(T), s));
     PrefillGemmParams p{};
     p.xh = xh;
@@ -213,6 +214,7 @@ int forward_impl(int64_t T, const uint16_t* x, const float* norm_w, float eps, u
     p.router_w = router->weight;
     p.router_b = router->bias;
     p.wscale = weights_scale(router);
+    p.gating = router->gating;
     p.sh_gate_inp = shared ? shared->gate_inp : nullptr;
     p.sh_gate = shared ? shared->gate : nullptr;
     p.sh_up = shared ? shared->up : nullptr;

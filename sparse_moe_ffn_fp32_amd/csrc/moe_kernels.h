@@ -27,7 +27,7 @@ struct Tracer {
 hipError_t launch_split_router(const float* wr, uint16_t* wr2, hipStream_t s);
 // wscale multiplies every renormalised routing weight
 hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
-                       float* sgate, float wscale, int T, hipStream_t s);
+                       float* sgate, float wscale, int gating, int T, hipStream_t s);
 
 // ---- routing sort (k_sort.hip)
 int sort_blocks(int N);
@@ -75,6 +75,7 @@ struct DecodeParams {
     int T;
     const float *router_w, *router_b;
     float wscale;  // factor on the renormalised routing weights
+    int gating;    // MOE_FFN_GATING_*
     const uint16_t *sh_gate_inp, *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;

@@ -155,6 +155,7 @@ class Layer:
     sh_down: Optional[np.ndarray]        # bf16 [D, Fs]
     meta: dict = field(default_factory=dict)
     weights_scale: float = 1.0           # expert_weights_scale of the routed MoE call
+    gating: int = 0                      # 0: softmax scores; 1: sqrt(softplus(logit)) scores
 
 
 def make_layer(seed: int, dims: Dims = Dims(), *, w_sd: float = 0.02, zipf_s: Optional[float] = None,

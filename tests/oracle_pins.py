@@ -398,4 +398,41 @@ def pin_weights_scale(O):
         assert rel(b[t], 0.3 * a[t]) <= 1e-12
 
 
+def pin_sqrt_softplus_gating(O):
+    """sqrt(softplus) scores on logits set exactly through the router bias
+    (zero router weights): for logits >= 100, softplus is the logit itself
+    in double, so logits 6400, 1600, 400, 100 weigh 80:40:20:10 / 150; for
+    logits <= -40 softplus is e^z to double precision, so logits -40 and -42
+    weigh in the ratio e^1; the selection is the softmax gate's."""
+    import copy
+    lay = tiny_layer(shared=False)
+    E, k = lay.dims.n_experts, lay.dims.top_k
+    assert k == 4
+    lay.router_w = np.zeros_like(lay.router_w)
+    bias = np.full(E, -1000.0, dtype=np.float32)
+    bias[[5, 2, 9, 0]] = [6400.0, 1600.0, 400.0, 100.0]
+    lay.router_b = bias
+    lay.gating = 1
+    x = tiny_x(seed=4, T=3)
+    r = O.route(lay, x)
+    assert np.array_equal(r["idx"], np.tile([5, 2, 9, 0], (3, 1)))
+    want = np.array([80.0, 40.0, 20.0, 10.0]) / 150.0
+    assert np.abs(r["w"] - want).max() <= 1e-15
+    bias = np.full(E, -1000.0, dtype=np.float32)
+    bias[[1, 3, 6, 7]] = [-40.0, -42.0, -44.0, -46.0]
+    lay.router_b = bias
+    r = O.route(lay, x)
+    assert np.array_equal(r["idx"], np.tile([1, 3, 6, 7], (3, 1)))
+    w = r["w"][0]
+    for a in range(3):
+        assert abs(w[a] / w[a + 1] - np.e) <= 1e-12 * np.e
+    soft = copy.copy(lay)
+    soft.gating = 0
+    lay2 = tiny_layer()
+    lay2.gating = 1
+    x2 = tiny_x(seed=9, T=5)
+    assert np.array_equal(O.route(lay2, x2)["idx"], O.route(tiny_layer(), x2)["idx"])
+    assert abs(O.forward(lay2, x2, nthreads=1)["w"].sum(axis=1) - 1.0).max() <= 1e-14
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

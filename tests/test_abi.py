@@ -143,6 +143,14 @@ def test_weights_scale_arguments(L):
         assert _call(L, layer=lay, ws=None) == moe.MOE_FFN_EWORKSPACE, ok
 
 
+def test_gating_arguments(L):
+    for g, want in ((0, moe.MOE_FFN_EWORKSPACE), (1, moe.MOE_FFN_EWORKSPACE), (2, moe.MOE_FFN_EINVAL),
+                    (-1, moe.MOE_FFN_EINVAL)):
+        lay = _layer()
+        lay.gating = g
+        assert _call(L, layer=lay, ws=None) == want, g
+
+
 def _block(L, T=4, h=0x20000000, nw=0x21000000, eps=1e-6, y=0x30000000, ws=0x40000000, wsb=None, path=0,
            layer=None):
     layer = layer or _layer()

@@ -4,7 +4,8 @@ its gate rows on top of its up rows): bit-for-bit agreement with separate
 tensors on every path, agreement with the oracle, and detection of the
 whole-layer concatenation that mixes up the experts' rows.
 expert_weights_scale: routing unchanged, weights and routed output scaled,
-checked against the oracle of the scaled layer."""
+checked against the oracle of the scaled layer.  sqrt-softplus gating: the
+same selection, weights and output against the oracle."""
 from __future__ import annotations
 
 import sys
@@ -117,3 +118,30 @@ def test_weights_scale(gpu, layer0, T, path):
     z = gpu.run(zero, x, path=PATHS[path], dl=moe.DeviceLayer.from_host(zero))
     for u, v in zip(z, base):
         assert np.array_equal(u, v), "weights_scale 0 must be the unscaled default"
+
+
+@pytest.mark.parametrize("T,path,offset", [(1, "auto", 0.0), (4, "auto", 0.0), (37, "decode", 0.0),
+                                           (37, "prefill", 0.0), (300, "auto", 0.0), (4, "auto", 25.0),
+                                           (300, "auto", -25.0)])
+def test_sqrt_softplus_gating(gpu, layer0, T, path, offset):
+    """sqrt(softplus(logit)) scores (ds4.c study notes Part 3, MoE trace 3):
+    the same experts as the softmax gate, weights and y against the oracle;
+    a constant router-bias offset of +-25 moves every logit into the large
+    and small softplus branches."""
+    import copy
+    import sparse_moe_ffn_fp32_amd as moe
+    from gpu_common import W_ABS
+    lay = copy.copy(layer0)
+    if offset:
+        lay.router_b = np.full(layer0.dims.n_experts, offset, dtype=np.float32)
+    x, _, _ = workloads.enforce_margin(lay, T, 600 + T)
+    soft = copy.copy(lay)
+    lay.gating = moe.GATING_SQRT_SOFTPLUS
+    _say(f"sqrt-softplus gating T={T} path={path} offset={offset}")
+    base = gpu.run(soft, x, path=PATHS[path], dl=moe.DeviceLayer.from_host(soft))
+    got = gpu.run(lay, x, path=PATHS[path], dl=moe.DeviceLayer.from_host(lay))
+    assert np.array_equal(got[1], base[1]), "the gating changed the selection"
+    ref = oracle.get().forward(lay, x)
+    assert np.array_equal(got[1], ref["idx"])
+    assert np.abs(got[2].astype(np.float64) - ref["w"]).max() <= W_ABS
+    _say(output_check(lay, x, got[0]))

@@ -25,6 +25,10 @@ MUTANTS = [
     ("group_bias_index", "float b = moe_oracle_bf16_to_f32(bi[i / group]);",
      "float b = moe_oracle_bf16_to_f32(bi[(i / group + 1) % groups]);"),
     ("router_no_bias", "if (L->router_b) acc += (double)L->router_b[e];", ""),
+    ("softplus_no_sqrt", "w[r] = sqrt(fmax(z, 0.0) + log1p(exp(-fabs(z))));", "w[r] = fmax(z, 0.0) + log1p(exp(-fabs(z)));"),
+    ("softplus_relu", "w[r] = sqrt(fmax(z, 0.0) + log1p(exp(-fabs(z))));", "w[r] = sqrt(fmax(z, 0.0) + 1e-300);"),
+    ("softplus_not_renormalised", "for (int64_t r = 0; r < k; r++) w[r] /= s;", ";"),
+    ("gating_ignored", "if (j->L->gating == 1) sqrt_softplus_weights(lg, sel, k, ww);", ";"),
     ("weights_scale_ignored", "ww[r] *= weights_scale(j->L);", "ww[r] *= 1.0;"),
     ("weights_scale_no_default", "L->weights_scale == 0.0 ? 1.0 : L->weights_scale", "L->weights_scale"),
     ("weights_scale_squared", "ww[r] *= weights_scale(j->L);", "ww[r] *= weights_scale(j->L) * weights_scale(j->L);"),
