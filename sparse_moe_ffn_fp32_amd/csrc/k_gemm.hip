@@ -27,9 +27,11 @@
 //     read their fragments from LDS;
 //   4-bit weights: two lanes per weight row, 16 bytes of codes (32 weights)
 //     each, stored raw (a quarter of the fp16 bytes); each wave expands the
-//     codes of its own 64 rows straight into MFMA operand registers, fp16
-//     s*q + b with the group's scale and bias (staged in LDS once at the
-//     block's start), one step ahead of the MFMAs that use them;
+//     codes of its own 64 rows (on 8-wave blocks: its half of each step)
+//     straight into MFMA operand registers, fp16 s*q + b with the group's
+//     scale and bias (staged in LDS once at the block's start), one step
+//     ahead of the MFMAs that use them (8-wave blocks: in the step itself,
+//     the other wave of the SIMD covering it);
 //   16-bit weights (shared expert, router planes): converted to fp16 on the
 //     way into LDS and read back as fragments.
 // Global loads run ahead in a ring of register stages (three steps for 4-bit
