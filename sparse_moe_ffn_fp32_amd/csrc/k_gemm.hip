@@ -8,9 +8,9 @@
 //
 // Block tile: 128 activation rows (tokens) x 256 weight rows (output
 // features); 4 waves, wave w computing all 128 rows against weight rows
-// [64w, 64w + 64) as 4 x 2 tiles of v_mfma_f32_32x32x16_f16 (the 4-bit modes
-// on 128-row tiles run 8 waves, two per SIMD splitting every K step:
-// gemm_block_w8).  MFMA layout:
+// [64w, 64w + 64) as 4 x 2 tiles of v_mfma_f32_32x32x16_f16.  The 4-bit
+// modes on 128-row tiles run 8 waves, two per SIMD: gate/up splitting every
+// K step (gemm_block_w8), down on 512-column tiles (gemm_block_down_wide).  MFMA layout:
 // lane l holds A[l%32][8*(l/32) .. +8] and B[8*(l/32) .. +8][l%32];
 // accumulator lane l holds C[i][l%32] for i = 8*(v/4) + 4*(l/32) + v%4,
 // v = 0..15.  K advances in steps of 64, one quantisation group.  Both
@@ -427,7 +427,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
 }
 
 // ---------------------------------------------------------------- 8 waves
-// The 4-bit modes on 128-row tiles with two waves per SIMD.  Wave w (0..7)
+// The routed gate/up on 128-row tiles with two waves per SIMD.  Wave w (0..7)
 // computes activation rows [0, 128) against LDS weight rows [64ws, 64ws + 64),
 // ws = w & 3, over one half of every K step: kh = w >> 2 takes the MFMA
 // sub-steps kk = 2kh, 2kh + 1 (K [8kk, +8) and [32 + 8kk, +8)) and expands
@@ -441,7 +441,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
 template <int MODE>
 __device__ __forceinline__ void gemm_block_w8(const GemmArgs& g, GemmSmem<MODE>& sm, int bid) {
     using C = GemmCfg<MODE>;
-    static_assert(C::Q4, "4-bit modes only");
+    static_assert(MODE == MODE_GU, "routed gate/up only (down: gemm_block_down_wide)");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ws = wave & 3, kh = wave >> 2;
     const int l32 = lane & 31, kq = lane >> 5;
@@ -462,22 +462,14 @@ __device__ __forceinline__ void gemm_block_w8(const GemmArgs& g, GemmSmem<MODE>&
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int r = min(ar0 + 64 * i, rows - 1);
-        const uint16_t* p;
-        if constexpr (MODE == MODE_GU) p = g.xh + (size_t)(g.perm[seg + m0 + r] / K) * D;
-        else p = g.h + (size_t)(seg + m0 + r) * F;
-        apt[i] = p + 8 * ac;
+        apt[i] = g.xh + (size_t)(g.perm[seg + m0 + r] / K) * D + 8 * ac;
     }
 
     // ---- B: this thread covers lane half bh of LDS weight row br
     const int bh = tid & 1, br = tid >> 1;
     auto wrow = [&](int n, int& mat) -> size_t {  // global weight row of LDS row n
-        if constexpr (C::PAIRED) {
-            mat = (n >> 5) & 1;
-            return (size_t)e * g.gu_rows + nblk * 128 + 32 * (n >> 6) + (n & 31);
-        } else {
-            mat = 0;
-            return (size_t)e * D + nblk * GEMM_BN + n;
-        }
+        mat = (n >> 5) & 1;
+        return (size_t)e * g.gu_rows + nblk * 128 + 32 * (n >> 6) + (n & 31);
     };
     const u32x4* bpt;
     {
@@ -486,8 +478,7 @@ __device__ __forceinline__ void gemm_block_w8(const GemmArgs& g, GemmSmem<MODE>&
         bpt = (const u32x4*)(g.q[mat] + row * (C::KTOT / 8)) + bh;
     }
 
-    // ---- stage the block's scales and biases (LDS row n = tid < 256) and,
-    // for DOWN, the rows' routing weights
+    // ---- stage the block's scales and biases (LDS row n = tid < 256)
     if (tid < GEMM_BN) {
         int mat;
         const size_t row = wrow(tid, mat);
@@ -508,10 +499,6 @@ __device__ __forceinline__ void gemm_block_w8(const GemmArgs& g, GemmSmem<MODE>&
             *(u32x4*)(dst + 8 * i + 4) = u32x4{lo[2], hi[2], lo[3], hi[3]};
         }
     }
-    if constexpr (MODE == MODE_DOWN) {
-        if (tid < GEMM_BM) sm.rw[tid] = g.wflat[g.perm[seg + m0 + min(tid, rows - 1)]] * PARTIAL_SCALE;
-    }
-
     f32x16 acc[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
@@ -579,7 +566,7 @@ __device__ __forceinline__ void gemm_block_w8(const GemmArgs& g, GemmSmem<MODE>&
             ring[j].b = bpt[2 * min(j + 1, C::NK - 1)];
         }
         store_b(c0, 0);
-        __syncthreads();  // staged scales, biases, routing weights; codes of step 0
+        __syncthreads();  // staged scales and biases; codes of step 0
         store_a(ring[0].a, 0);
         store_b(ring[0].b, 1);
         __syncthreads();
@@ -642,7 +629,7 @@ __device__ __forceinline__ void gemm_block_w8(const GemmArgs& g, GemmSmem<MODE>&
     // acc[mt][nt] is activation row r = 32mt + 8(v/4) + 4kq + v%4 and LDS
     // weight row 64ws + 32nt + l32.
     auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
-    if constexpr (MODE == MODE_GU) {
+    {
         // h tile [128 rows][128 features] fp16 in LDS, then 16-byte row pieces
         constexpr int HS = 128 + 8;
         static_assert(GEMM_BM * HS * sizeof(f16) <= sizeof(sm.a), "h tile must fit the activation tiles");
@@ -670,35 +657,199 @@ __device__ __forceinline__ void gemm_block_w8(const GemmArgs& g, GemmSmem<MODE>&
             const int r = rb + 32 * i;
             if (r < rows) *(u32x4*)&h_out[(size_t)(seg + m0 + r) * F + fo] = hv[i];
         }
-    } else {
-        // partial tile [128 rows][256 outputs] fp16 (x 2^6 x routing weight)
-        constexpr int PS = GEMM_BN + 8;
-        static_assert(GEMM_BM * PS * sizeof(f16) <= offsetof(GemmSmem<MODE>, sb), "partial tile must fit a, b, bq");
-        f16* pb = &sm.a[0][0];
-        if (kh == 0)
+    }
+}
+
+// ---------------------------------------------------------------- wide down
+// The routed down projection on 128-row tiles with 512 output columns per
+// block: 8 waves, wave w computing all 128 rows against weight rows
+// [64w, 64w + 64) over the whole K (K = F: 8 steps).  Against two 256-column
+// blocks the tile's h rows are read once instead of twice and the block's
+// fixed costs (tile record, routing weights, prologue loads, epilogue) are
+// paid once; the 16-byte code rows, the ring and the epilogue are those of
+// gemm_block.
+constexpr int WBN = 512;  // output columns per wide block
+struct WideSmem {
+    f16 a[2][GEMM_BM * LDSB];
+    uint32_t bq[QBUF][WBN * BQS];
+    uint32_t sb[WBN * (F / G + 4)];  // (bias << 16) | scale, bf16 bits
+    float rw[GEMM_BM];               // routing weight x 2^6 per row
+};
+
+__device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem& sm, int bid) {
+    using C = GemmCfg<MODE_DOWN>;
+    constexpr int SROW = C::NG + 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, kq = lane >> 5;
+
+    constexpr int NB = D / WBN;
+    const int n_tiles = g.tile_count[0];
+    const int live = n_tiles * NB, per_xcd = (live + 7) >> 3;
+    const int slot = bid >> 3, item = (bid & 7) * per_xcd + slot;
+    if (slot >= per_xcd || item >= live) return;
+    const int tile = item / NB, nblk = item % NB;
+    const int4 rec = *(const int4*)&g.tiles[4 * tile];  // one dependent load
+    const int e = rec.x, m0 = rec.y, seg = rec.z, rows = rec.w;  // rows: 1 .. GEMM_BM
+
+    // ---- A (h rows): thread loads 16 bytes (chunk ac) of rows ar0 + 64i
+    const int ac = tid & 7, ar0 = tid >> 3;
+    const uint16_t* apt[2];
 #pragma unroll
-            for (int mt = 0; mt < 4; mt++)
+    for (int i = 0; i < 2; i++) apt[i] = g.h + (size_t)(seg + m0 + min(ar0 + 64 * i, rows - 1)) * F + 8 * ac;
+    // ---- B: thread covers lane half bh of LDS weight rows br0, br0 + 256
+    const int bh = tid & 1, br0 = tid >> 1;
+    const u32x4* bpt[2];
 #pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const int r = acc_row(mt, v);
-                    const float wt = sm.rw[r];
+    for (int i = 0; i < 2; i++)
+        bpt[i] = (const u32x4*)(g.q[0] + ((size_t)e * D + nblk * WBN + br0 + 256 * i) * (F / 8)) + bh;
+    // ---- scales and biases (LDS row n = tid), routing weights
+    {
+        const size_t row = (size_t)e * D + nblk * WBN + tid;
+        const u32x4 sv = *(const u32x4*)(g.sc[0] + row * C::NG), bv = *(const u32x4*)(g.bi[0] + row * C::NG);
+        u32x4 lo, hi;
 #pragma unroll
-                    for (int nt = 0; nt < 2; nt++) pb[r * PS + 64 * ws + 32 * nt + l32] = (f16)(wt * acc[mt][nt][v]);
-                }
-        uint16_t* const p_out = pinned(g.p_out);
+        for (int j = 0; j < 4; j++) {
+            lo[j] = (sv[j] & 0xffffu) | (bv[j] << 16);
+            hi[j] = (sv[j] >> 16) | (bv[j] & 0xffff0000u);
+        }
+        uint32_t* dst = &sm.sb[tid * SROW];
+        *(u32x4*)(dst) = u32x4{lo[0], hi[0], lo[1], hi[1]};
+        *(u32x4*)(dst + 4) = u32x4{lo[2], hi[2], lo[3], hi[3]};
+    }
+    if (tid < GEMM_BM) sm.rw[tid] = g.wflat[g.perm[seg + m0 + min(tid, rows - 1)]] * PARTIAL_SCALE;
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
+
+    auto mfma_step = [&](auto nmt_c, int abuf, const f16x8 (&bf)[2][4]) {
+        constexpr int NMT = decltype(nmt_c)::value;
+        const f16* ab = &sm.a[abuf][l32 * LDSB + 32 * kq];
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            f16x8 af[NMT];
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++)
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt][kk], acc[mt][nt], 0, 0, 0);
+        }
+    };
+    auto store_a = [&](const u32x4 (&av)[2], int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) *(u32x4*)&sm.a[buf][(ar0 + 64 * i) * LDSB + 8 * ac] = av[i];
+    };
+    auto load_a = [&](int k, u32x4 (&av)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) av[i] = *(const u32x4*)(apt[i] + k * BK);
+    };
+    auto load_b = [&](int k, u32x4 (&bv)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) bv[i] = bpt[i][2 * k];
+    };
+    auto store_b = [&](const u32x4 (&bv)[2], int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) *(u32x4*)&sm.bq[buf][(br0 + 256 * i) * BQS + 4 * bh] = bv[i];
+    };
+    auto dequant = [&](int k, int qbuf, f16x8 (&bf)[2][4]) {
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) {
+            const int n = 64 * wave + 32 * nt + l32;
+            const u32x4 codes = *(const u32x4*)&sm.bq[qbuf][n * BQS + 4 * kq];
+            const uint32_t sbw = sm.sb[n * SROW + k];
+            const f16 sv = (f16)bf16_to_f32(sbw & 0xffffu), bv = (f16)bf16_to_f32(sbw >> 16);
+            const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++) {
+                const uint32_t cw = codes[kk];
+                bf[nt][kk] = __builtin_bit_cast(f16x8, q4_word_to_f16x8(cw, s2, b2));
+            }
+        }
+    };
+    // ring stage j holds A(j) and the codes of step j + 1 (as in gemm_block)
+    constexpr int R = 4;
+    static_assert(C::NK % R == 0 && QBUF == R, "K steps must be a multiple of the ring size");
+    struct Stage { u32x4 a[2]; u32x4 b[2]; };
+    auto main_loop = [&](auto nmt_c) {
+        Stage ring[R];
+        u32x4 c0[2];
+        load_b(0, c0);
+#pragma unroll
+        for (int j = 0; j < R - 1; j++) {
+            load_a(j, ring[j].a);
+            load_b(min(j + 1, C::NK - 1), ring[j].b);
+        }
+        store_b(c0, 0);
+        __syncthreads();  // staged scales, biases, routing weights; codes of step 0
+        store_a(ring[0].a, 0);
+        store_b(ring[0].b, 1);
         __syncthreads();
-        // 128 rows x 32 pieces of 8 outputs: thread tid takes rows tid/32 + 16i,
-        // piece tid%32; all LDS reads first, then the stores
-        const int c = tid & 31, rb = tid >> 5;
+#pragma unroll 1
+        for (int k0 = 0; k0 < C::NK; k0 += R) {
+#pragma unroll
+            for (int j = 0; j < R; j++) {
+                const int k = k0 + j;
+                Stage& nx = ring[(j + R - 1) % R];
+                load_a(min(k + R - 1, C::NK - 1), nx.a);
+                load_b(min(k + R, C::NK - 1), nx.b);
+                __builtin_amdgcn_sched_barrier(0);
+                f16x8 bfr[2][4];
+                dequant(k, j % QBUF, bfr);
+                mfma_step(nmt_c, j & 1, bfr);
+                store_a(ring[(j + 1) % R].a, (j + 1) & 1);
+                store_b(ring[(j + 1) % R].b, (j + 2) % QBUF);
+                __syncthreads();
+            }
+        }
+    };
+    const int nmt = (rows + 31) >> 5;
+    if (nmt >= 4) main_loop(std::integral_constant<int, 4>{});
+    else if (nmt == 3) main_loop(std::integral_constant<int, 3>{});
+    else if (nmt == 2) main_loop(std::integral_constant<int, 2>{});
+    else main_loop(std::integral_constant<int, 1>{});
+
+    // ---- epilogue: partial tile [128 rows][512 outputs] fp16 (x 2^6 x
+    // routing weight) in LDS (a and bq), then 16-byte row pieces
+    constexpr int PS = WBN + 8;
+    static_assert(GEMM_BM * PS * sizeof(f16) <= offsetof(WideSmem, sb), "partial tile must fit a, bq");
+    f16* pb = &sm.a[0][0];
+    auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int r = acc_row(mt, v);
+            const float wt = sm.rw[r];
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++) pb[r * PS + 64 * wave + 32 * nt + l32] = (f16)(wt * acc[mt][nt][v]);
+        }
+    uint16_t* const p_out = pinned(g.p_out);
+    __syncthreads();
+    // 128 rows x 64 pieces of 8 outputs: thread tid takes rows tid/64 + 8i,
+    // piece tid%64; LDS reads in two halves of 8, each before its stores
+    const int c = tid & 63, rb = tid >> 6;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
         u32x4 pv[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) pv[i] = *(const u32x4*)&pb[(rb + 16 * i) * PS + 8 * c];
+        for (int i = 0; i < 8; i++) pv[i] = *(const u32x4*)&pb[(rb + 8 * (8 * h + i)) * PS + 8 * c];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int r = rb + 16 * i;
-            if (r < rows) *(u32x4*)&p_out[(size_t)(seg + m0 + r) * D + nblk * GEMM_BN + 8 * c] = pv[i];
+            const int r = rb + 8 * (8 * h + i);
+            if (r < rows) *(u32x4*)&p_out[(size_t)(seg + m0 + r) * D + nblk * WBN + 8 * c] = pv[i];
         }
     }
+}
+
+__global__ void __launch_bounds__(512) k_gemm_down_wide(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) WideSmem sm;
+    gemm_block_down_wide(g, sm, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- routed
@@ -1073,7 +1224,7 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.q[0] = p.down_q; g.sc[0] = p.down_s; g.bi[0] = p.down_b;
     g.p_out = p.partial;
     if (bm == QBM) tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm_q4<MODE_DOWN>, grid(max_tiles * (D / GEMM_BN)), dim3(256), 0, s, g);
-    else tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm_w8<MODE_DOWN>, grid(max_tiles * (D / GEMM_BN)), dim3(512), 0, s, g);
+    else tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm_down_wide, grid(max_tiles * (D / WBN)), dim3(512), 0, s, g);
     // combine
     if (p.sh_gate) {
         g.sw[0] = p.sh_down; g.p_in = p.partial; g.y = p.y; g.resid = p.resid;
