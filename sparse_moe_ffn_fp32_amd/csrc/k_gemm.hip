@@ -9,8 +9,8 @@
 // Block tile: 128 activation rows (tokens) x 256 weight rows (output
 // features); 4 waves, wave w computing all 128 rows against weight rows
 // [64w, 64w + 64) as 4 x 2 tiles of v_mfma_f32_32x32x16_f16.  The 4-bit
-// modes on 128-row tiles run 8 waves, two per SIMD: gate/up splitting every
-// K step (gemm_block_w8), down on 512-column tiles (gemm_block_down_wide).  MFMA layout:
+// modes on 128-row tiles run 8 waves (two per SIMD) on 512 weight rows:
+// gemm_block_gu_wide, gemm_block_down_wide.  MFMA layout:
 // lane l holds A[l%32][8*(l/32) .. +8] and B[8*(l/32) .. +8][l%32];
 // accumulator lane l holds C[i][l%32] for i = 8*(v/4) + 4*(l/32) + v%4,
 // v = 0..15.  K advances in steps of 64, one quantisation group.  Both
@@ -27,11 +27,10 @@
 //     read their fragments from LDS;
 //   4-bit weights: two lanes per weight row, 16 bytes of codes (32 weights)
 //     each, stored raw (a quarter of the fp16 bytes); each wave expands the
-//     codes of its own 64 rows (on 8-wave blocks: its half of each step)
-//     straight into MFMA operand registers, fp16 s*q + b with the group's
-//     scale and bias (staged in LDS once at the block's start), one step
-//     ahead of the MFMAs that use them (8-wave blocks: in the step itself,
-//     the other wave of the SIMD covering it);
+//     codes of its own 64 rows straight into MFMA operand registers, fp16
+//     s*q + b with the group's scale and bias (staged in LDS once at the
+//     block's start), one step ahead of the MFMAs that use them (8-wave
+//     blocks: in the step itself, the other wave of the SIMD covering it);
 //   16-bit weights (shared expert, router planes): converted to fp16 on the
 //     way into LDS and read back as fragments.
 // Global loads run ahead in a ring of register stages (three steps for 4-bit
@@ -159,7 +158,7 @@ struct GemmSmem {
 template <int MODE>
 __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm, int bid) {
     using C = GemmCfg<MODE>;
-    static_assert(!C::Q4, "the 4-bit modes run in gemm_block_w8 / gemm_block_q4");
+    static_assert(!C::Q4, "the 4-bit modes run in gemm_block_gu_wide / gemm_block_down_wide / gemm_block_q4");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, kq = lane >> 5;
@@ -426,240 +425,6 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     }
 }
 
-// ---------------------------------------------------------------- 8 waves
-// The routed gate/up on 128-row tiles with two waves per SIMD.  Wave w (0..7)
-// computes activation rows [0, 128) against LDS weight rows [64ws, 64ws + 64),
-// ws = w & 3, over one half of every K step: kh = w >> 2 takes the MFMA
-// sub-steps kk = 2kh, 2kh + 1 (K [8kk, +8) and [32 + 8kk, +8)) and expands
-// only those two code words of its rows.  The two waves of a SIMD (w and
-// w + 4) hold the same output slice over disjoint K and share no operand
-// registers, so one wave's MFMAs run while the other expands codes, reads
-// LDS or waits at the barrier; no code word is expanded twice.  After the
-// loop the halves are added through LDS in a fixed order (kh 0, then kh 1)
-// and the kh = 0 waves run the epilogue.  The tile schedule, LDS layout and
-// load ring are those of gemm_block.
-template <int MODE>
-__device__ __forceinline__ void gemm_block_w8(const GemmArgs& g, GemmSmem<MODE>& sm, int bid) {
-    using C = GemmCfg<MODE>;
-    static_assert(MODE == MODE_GU, "routed gate/up only (down: gemm_block_down_wide)");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ws = wave & 3, kh = wave >> 2;
-    const int l32 = lane & 31, kq = lane >> 5;
-
-    constexpr int NB = C::NB;
-    const int n_tiles = g.tile_count[0];
-    const int live = n_tiles * NB, per_xcd = (live + 7) >> 3;
-    const int slot = bid >> 3, item = (bid & 7) * per_xcd + slot;
-    if (slot >= per_xcd || item >= live) return;
-    const int tile = item / NB, nblk = item % NB;
-    const int4 rec = *(const int4*)&g.tiles[4 * tile];  // one dependent load
-    const int e = rec.x, m0 = rec.y, seg = rec.z, rows = rec.w;  // rows: 1 .. GEMM_BM
-
-    // ---- A: this thread loads 16 bytes (chunk ac) of rows ar0 + 64i, i < 2;
-    // rows past the end repeat the last valid row (their results are dropped)
-    const int ac = tid & 7, ar0 = tid >> 3;
-    const uint16_t* apt[2];
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int r = min(ar0 + 64 * i, rows - 1);
-        apt[i] = g.xh + (size_t)(g.perm[seg + m0 + r] / K) * D + 8 * ac;
-    }
-
-    // ---- B: this thread covers lane half bh of LDS weight row br
-    const int bh = tid & 1, br = tid >> 1;
-    auto wrow = [&](int n, int& mat) -> size_t {  // global weight row of LDS row n
-        mat = (n >> 5) & 1;
-        return (size_t)e * g.gu_rows + nblk * 128 + 32 * (n >> 6) + (n & 31);
-    };
-    const u32x4* bpt;
-    {
-        int mat;
-        const size_t row = wrow(br, mat);
-        bpt = (const u32x4*)(g.q[mat] + row * (C::KTOT / 8)) + bh;
-    }
-
-    // ---- stage the block's scales and biases (LDS row n = tid < 256)
-    if (tid < GEMM_BN) {
-        int mat;
-        const size_t row = wrow(tid, mat);
-        const uint16_t* sp = g.sc[mat] + row * C::NG;
-        const uint16_t* bp = g.bi[mat] + row * C::NG;
-        uint32_t* dst = &sm.sb[tid * C::SROW];
-#pragma unroll
-        for (int i = 0; i < C::NG / 8; i++) {
-            const u32x4 sv = *(const u32x4*)(sp + 8 * i), bv = *(const u32x4*)(bp + 8 * i);
-            u32x4 lo, hi;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                lo[j] = (sv[j] & 0xffffu) | (bv[j] << 16);
-                hi[j] = (sv[j] >> 16) | (bv[j] & 0xffff0000u);
-            }
-            // groups 8i + 2j (lo) and 8i + 2j + 1 (hi)
-            *(u32x4*)(dst + 8 * i) = u32x4{lo[0], hi[0], lo[1], hi[1]};
-            *(u32x4*)(dst + 8 * i + 4) = u32x4{lo[2], hi[2], lo[3], hi[3]};
-        }
-    }
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
-
-    // Eight MFMAs per 32-row group and sub-step (this wave's two) against
-    // the activation tile in LDS buffer abuf; groups past the tile's last
-    // row are not multiplied.
-    auto mfma_step = [&](auto nmt_c, int abuf, const f16x8 (&bf)[2][2]) {
-        constexpr int NMT = decltype(nmt_c)::value;
-        const f16* ab = &sm.a[abuf][l32 * LDSB + 32 * kq + 16 * kh];
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            f16x8 af[NMT];
-#pragma unroll
-            for (int mt = 0; mt < NMT; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * j);
-#pragma unroll
-            for (int mt = 0; mt < NMT; mt++)
-#pragma unroll
-                for (int nt = 0; nt < 2; nt++)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt][j], acc[mt][nt], 0, 0, 0);
-        }
-    };
-    auto store_a = [&](const u32x4 (&av)[2], int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; i++) *(u32x4*)&sm.a[buf][(ar0 + 64 * i) * LDSB + 8 * ac] = av[i];
-    };
-    auto load_a = [&](int k, u32x4 (&av)[2]) {
-#pragma unroll
-        for (int i = 0; i < 2; i++) av[i] = *(const u32x4*)(apt[i] + k * BK);
-    };
-    auto store_b = [&](const u32x4& bv, int buf) { *(u32x4*)&sm.bq[buf][br * BQS + 4 * bh] = bv; };
-    // this wave's two code words (sub-steps 2kh, 2kh + 1) of its rows, as
-    // fp16 s*q + b
-    auto dequant = [&](int k, int qbuf, f16x8 (&bf)[2][2]) {
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++) {
-            const int n = 64 * ws + 32 * nt + l32;
-            const u32x2 codes = *(const u32x2*)&sm.bq[qbuf][n * BQS + 4 * kq + 2 * kh];
-            const uint32_t sbw = sm.sb[n * C::SROW + k];
-            const f16 sv = (f16)bf16_to_f32(sbw & 0xffffu), bv = (f16)bf16_to_f32(sbw >> 16);
-            const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const uint32_t cw = codes[j];
-                bf[nt][j] = __builtin_bit_cast(f16x8, q4_word_to_f16x8(cw, s2, b2));
-            }
-        }
-    };
-    // Ring stage j holds A(j) and the codes of step j + 1; the codes of step
-    // j sit in LDS buffer j % 4, A(j) in buffer j % 2.  Loads run three steps
-    // ahead; each step's codes are expanded in the step itself.
-    constexpr int R = 4;
-    static_assert(C::NK % R == 0 && QBUF == R, "K steps must be a multiple of the ring size");
-    struct Stage { u32x4 a[2]; u32x4 b; };
-    auto main_loop = [&](auto nmt_c) {
-        Stage ring[R];
-        const u32x4 c0 = bpt[0];
-#pragma unroll
-        for (int j = 0; j < R - 1; j++) {
-            load_a(j, ring[j].a);
-            ring[j].b = bpt[2 * min(j + 1, C::NK - 1)];
-        }
-        store_b(c0, 0);
-        __syncthreads();  // staged scales and biases; codes of step 0
-        store_a(ring[0].a, 0);
-        store_b(ring[0].b, 1);
-        __syncthreads();
-#pragma unroll 1
-        for (int k0 = 0; k0 < C::NK; k0 += R) {
-#pragma unroll
-            for (int j = 0; j < R; j++) {
-                const int k = k0 + j;
-                Stage& nx = ring[(j + R - 1) % R];
-                load_a(min(k + R - 1, C::NK - 1), nx.a);
-                nx.b = bpt[2 * min(k + R, C::NK - 1)];
-                // keep the loads here: the scheduler would otherwise sink them
-                // towards their first use and undo the prefetch
-                __builtin_amdgcn_sched_barrier(0);
-                // expanded just before use: the other wave of the SIMD runs
-                // its MFMAs meanwhile
-                f16x8 bfr[2][2];
-                dequant(k, j % QBUF, bfr);
-                mfma_step(nmt_c, j & 1, bfr);
-                store_a(ring[(j + 1) % R].a, (j + 1) & 1);
-                store_b(ring[(j + 1) % R].b, (j + 2) % QBUF);
-                __syncthreads();
-            }
-        }
-    };
-    const int nmt = (rows + 31) >> 5;
-    if (nmt >= 4) main_loop(std::integral_constant<int, 4>{});
-    else if (nmt == 3) main_loop(std::integral_constant<int, 3>{});
-    else if (nmt == 2) main_loop(std::integral_constant<int, 2>{});
-    else main_loop(std::integral_constant<int, 1>{});
-
-    // ---- the two K halves: kh = 1 hands its sums to kh = 0 through LDS
-    // (the loop ended with a barrier: the operand tiles are free), two
-    // 32-row groups per round, lane-contiguous
-    {
-        float* red = (float*)&sm.a[0][0];
-        static_assert(4 * 2 * 2 * 16 * 64 * sizeof(float) <= offsetof(GemmSmem<MODE>, sb), "K-half exchange must fit a, b, bq");
-#pragma unroll
-        for (int rd = 0; rd < 2; rd++) {
-            if (kh == 1)
-#pragma unroll
-                for (int mi = 0; mi < 2; mi++)
-#pragma unroll
-                    for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-                        for (int v = 0; v < 16; v++) red[(((ws * 2 + mi) * 2 + nt) * 16 + v) * 64 + lane] = acc[2 * rd + mi][nt][v];
-            __syncthreads();
-            if (kh == 0)
-#pragma unroll
-                for (int mi = 0; mi < 2; mi++)
-#pragma unroll
-                    for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-                        for (int v = 0; v < 16; v++) acc[2 * rd + mi][nt][v] += red[(((ws * 2 + mi) * 2 + nt) * 16 + v) * 64 + lane];
-            __syncthreads();
-        }
-    }
-
-    // ---- epilogues (kh = 0 waves hold the sums).  Accumulator element v of
-    // acc[mt][nt] is activation row r = 32mt + 8(v/4) + 4kq + v%4 and LDS
-    // weight row 64ws + 32nt + l32.
-    auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
-    {
-        // h tile [128 rows][128 features] fp16 in LDS, then 16-byte row pieces
-        constexpr int HS = 128 + 8;
-        static_assert(GEMM_BM * HS * sizeof(f16) <= sizeof(sm.a), "h tile must fit the activation tiles");
-        f16* hb = &sm.a[0][0];
-        const int f = 32 * ws + l32;  // feature inside the block
-        if (kh == 0)
-#pragma unroll
-            for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const float hv = silu_f32(acc[mt][0][v]) * acc[mt][1][v];
-                    hb[acc_row(mt, v) * HS + ((f & ~7) | perm8_pos(f & 7))] = (f16)hv;
-                }
-        uint16_t* const h_out = pinned(g.h_out);
-        __syncthreads();
-        // 128 rows x 16 pieces of 8 features: thread tid takes rows
-        // tid/16 + 32i, piece tid%16; all LDS reads first, then the stores
-        const int c = tid & 15, rb = tid >> 4;
-        u32x4 hv[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) hv[i] = *(const u32x4*)&hb[(rb + 32 * i) * HS + 8 * c];
-        const int fo = nblk * 128 + 8 * c;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int r = rb + 32 * i;
-            if (r < rows) *(u32x4*)&h_out[(size_t)(seg + m0 + r) * F + fo] = hv[i];
-        }
-    }
-}
-
 // ---------------------------------------------------------------- wide down
 // The routed down projection on 128-row tiles with 512 output columns per
 // block: 8 waves, wave w computing all 128 rows against weight rows
@@ -850,6 +615,197 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
 __global__ void __launch_bounds__(512) k_gemm_down_wide(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) WideSmem sm;
     gemm_block_down_wide(g, sm, blockIdx.x);
+}
+
+// ---------------------------------------------------------------- wide gate/up
+// The routed gate/up on 128-row tiles with 256 features (512 gate and up
+// rows) per block: 8 waves, wave w computing all 128 rows against LDS weight
+// rows [64w, 64w + 64) (gate and up of features 32w .. 32w + 31) over the
+// whole K.  Against two 128-feature blocks the tile's gathered x rows (512
+// KB per tile) are read once instead of twice.  Each step's codes are
+// expanded in the step itself (the other wave of the SIMD covers it), so
+// they need to land only one step ahead: two code buffers, which leaves room
+// for the scales and biases of all 32 groups.
+struct WideGuSmem {
+    f16 a[2][GEMM_BM * LDSB];
+    uint32_t bq[2][WBN * BQS];
+    uint32_t sb[WBN * (D / G + 4)];  // (bias << 16) | scale, bf16 bits
+};
+
+__device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem& sm, int bid) {
+    using C = GemmCfg<MODE_GU>;
+    constexpr int SROW = C::NG + 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, kq = lane >> 5;
+
+    constexpr int NB = F / (WBN / 2);
+    const int n_tiles = g.tile_count[0];
+    const int live = n_tiles * NB, per_xcd = (live + 7) >> 3;
+    const int slot = bid >> 3, item = (bid & 7) * per_xcd + slot;
+    if (slot >= per_xcd || item >= live) return;
+    const int tile = item / NB, nblk = item % NB;
+    const int4 rec = *(const int4*)&g.tiles[4 * tile];  // one dependent load
+    const int e = rec.x, m0 = rec.y, seg = rec.z, rows = rec.w;  // rows: 1 .. GEMM_BM
+
+    // ---- A (x rows gathered through the sort): 16 bytes (chunk ac) of rows
+    // ar0 + 64i; rows past the end repeat the last valid row
+    const int ac = tid & 7, ar0 = tid >> 3;
+    const uint16_t* apt[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+        apt[i] = g.xh + (size_t)(g.perm[seg + m0 + min(ar0 + 64 * i, rows - 1)] / K) * D + 8 * ac;
+    // ---- B: LDS row n is gate (n & 32 == 0) or up row of feature
+    // nblk * 256 + 32 (n >> 6) + (n & 31); thread covers lane half bh of rows
+    // br0 and br0 + 256
+    auto wrow = [&](int n, int& mat) -> size_t {
+        mat = (n >> 5) & 1;
+        return (size_t)e * g.gu_rows + nblk * (WBN / 2) + 32 * (n >> 6) + (n & 31);
+    };
+    const int bh = tid & 1, br0 = tid >> 1;
+    const u32x4* bpt[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        int mat;
+        const size_t row = wrow(br0 + 256 * i, mat);
+        bpt[i] = (const u32x4*)(g.q[mat] + row * (D / 8)) + bh;
+    }
+    // ---- scales and biases of every group (LDS row n = tid)
+    {
+        int mat;
+        const size_t row = wrow(tid, mat);
+        const uint16_t* sp = g.sc[mat] + row * C::NG;
+        const uint16_t* bp = g.bi[mat] + row * C::NG;
+        uint32_t* dst = &sm.sb[tid * SROW];
+#pragma unroll
+        for (int i = 0; i < C::NG / 8; i++) {
+            const u32x4 sv = *(const u32x4*)(sp + 8 * i), bv = *(const u32x4*)(bp + 8 * i);
+            u32x4 lo, hi;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                lo[j] = (sv[j] & 0xffffu) | (bv[j] << 16);
+                hi[j] = (sv[j] >> 16) | (bv[j] & 0xffff0000u);
+            }
+            // groups 8i + 2j (lo) and 8i + 2j + 1 (hi)
+            *(u32x4*)(dst + 8 * i) = u32x4{lo[0], hi[0], lo[1], hi[1]};
+            *(u32x4*)(dst + 8 * i + 4) = u32x4{lo[2], hi[2], lo[3], hi[3]};
+        }
+    }
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
+
+    auto mfma_step = [&](auto nmt_c, int abuf, const f16x8 (&bf)[2][4]) {
+        constexpr int NMT = decltype(nmt_c)::value;
+        const f16* ab = &sm.a[abuf][l32 * LDSB + 32 * kq];
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            f16x8 af[NMT];
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++)
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt][kk], acc[mt][nt], 0, 0, 0);
+        }
+    };
+    auto dequant = [&](int k, int qbuf, f16x8 (&bf)[2][4]) {
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) {
+            const int n = 64 * wave + 32 * nt + l32;
+            const u32x4 codes = *(const u32x4*)&sm.bq[qbuf][n * BQS + 4 * kq];
+            const uint32_t sbw = sm.sb[n * SROW + k];
+            const f16 sv = (f16)bf16_to_f32(sbw & 0xffffu), bv = (f16)bf16_to_f32(sbw >> 16);
+            const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++) {
+                const uint32_t cw = codes[kk];
+                bf[nt][kk] = __builtin_bit_cast(f16x8, q4_word_to_f16x8(cw, s2, b2));
+            }
+        }
+    };
+    // ring stage j holds A(j) and the codes of step j; loads run three steps
+    // ahead; A(j) and codes(j) sit in LDS buffer j % 2 during step j
+    constexpr int R = 4;
+    static_assert(C::NK % R == 0, "K steps must be a multiple of the ring size");
+    struct Stage { u32x4 a[2]; u32x4 b[2]; };
+    auto load = [&](int k, Stage& st) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) st.a[i] = *(const u32x4*)(apt[i] + k * BK);
+#pragma unroll
+        for (int i = 0; i < 2; i++) st.b[i] = bpt[i][2 * k];
+    };
+    auto store = [&](const Stage& st, int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) *(u32x4*)&sm.a[buf][(ar0 + 64 * i) * LDSB + 8 * ac] = st.a[i];
+#pragma unroll
+        for (int i = 0; i < 2; i++) *(u32x4*)&sm.bq[buf][(br0 + 256 * i) * BQS + 4 * bh] = st.b[i];
+    };
+    auto main_loop = [&](auto nmt_c) {
+        Stage ring[R];
+#pragma unroll
+        for (int j = 0; j < R - 1; j++) load(j, ring[j]);
+        store(ring[0], 0);
+        __syncthreads();  // staged scales and biases; step 0's operands
+#pragma unroll 1
+        for (int k0 = 0; k0 < C::NK; k0 += R) {
+#pragma unroll
+            for (int j = 0; j < R; j++) {
+                const int k = k0 + j;
+                load(min(k + R - 1, C::NK - 1), ring[(j + R - 1) % R]);
+                __builtin_amdgcn_sched_barrier(0);
+                f16x8 bfr[2][4];
+                dequant(k, j & 1, bfr);
+                mfma_step(nmt_c, j & 1, bfr);
+                store(ring[(j + 1) % R], (j + 1) & 1);
+                __syncthreads();
+            }
+        }
+    };
+    const int nmt = (rows + 31) >> 5;
+    if (nmt >= 4) main_loop(std::integral_constant<int, 4>{});
+    else if (nmt == 3) main_loop(std::integral_constant<int, 3>{});
+    else if (nmt == 2) main_loop(std::integral_constant<int, 2>{});
+    else main_loop(std::integral_constant<int, 1>{});
+
+    // ---- epilogue: h tile [128 rows][256 features] fp16 in LDS (a, bq),
+    // SwiGLU of the lane's gate and up values, then 16-byte row pieces
+    constexpr int HS = WBN / 2 + 8;
+    static_assert(GEMM_BM * HS * sizeof(f16) <= offsetof(WideGuSmem, sb), "h tile must fit a, bq");
+    f16* hb = &sm.a[0][0];
+    auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
+    const int f = 32 * wave + l32;  // feature inside the block
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const float hv = silu_f32(acc[mt][0][v]) * acc[mt][1][v];
+            hb[acc_row(mt, v) * HS + ((f & ~7) | perm8_pos(f & 7))] = (f16)hv;
+        }
+    uint16_t* const h_out = pinned(g.h_out);
+    __syncthreads();
+    // 128 rows x 32 pieces of 8 features: thread tid takes rows tid/32 + 16i,
+    // piece tid%32; all LDS reads first, then the stores
+    const int c = tid & 31, rb = tid >> 5;
+    u32x4 hv[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) hv[i] = *(const u32x4*)&hb[(rb + 16 * i) * HS + 8 * c];
+    const int fo = nblk * (WBN / 2) + 8 * c;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int r = rb + 16 * i;
+        if (r < rows) *(u32x4*)&h_out[(size_t)(seg + m0 + r) * F + fo] = hv[i];
+    }
+}
+
+__global__ void __launch_bounds__(512) k_gemm_gu_wide(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) WideGuSmem sm;
+    gemm_block_gu_wide(g, sm, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- routed
@@ -1132,12 +1088,6 @@ __global__ void __launch_bounds__(256) k_gemm_q4(GemmArgs g) {
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(512) k_gemm_w8(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) GemmSmem<MODE> sm;
-    gemm_block_w8<MODE>(g, sm, blockIdx.x);
-}
-
-template <int MODE>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) GemmSmem<MODE> sm;
     gemm_block<MODE>(g, sm, blockIdx.x);
@@ -1218,7 +1168,7 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.q[1] = p.up_q; g.sc[1] = p.up_s; g.bi[1] = p.up_b;
     g.h_out = p.h;
     if (bm == QBM) tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm_q4<MODE_GU>, grid(max_tiles * (F / 128)), dim3(256), 0, s, g);
-    else tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm_w8<MODE_GU>, grid(max_tiles * (F / 128)), dim3(512), 0, s, g);
+    else tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm_gu_wide, grid(max_tiles * (F / (WBN / 2))), dim3(512), 0, s, g);
     // (the shared gate/up ran with the router logits)
     // routed down
     g.q[0] = p.down_q; g.sc[0] = p.down_s; g.bi[0] = p.down_b;
