@@ -158,7 +158,7 @@ struct GemmSmem {
 template <int MODE>
 __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm, int bid) {
     using C = GemmCfg<MODE>;
-    static_assert(!C::Q4, "the 4-bit modes run in gemm_block_gu_wide / gemm_block_down_wide / gemm_block_q4");
+    static_assert(!C::Q4, "the 4-bit modes run in gemm_block_gu_wide / gemm_block_down_wide");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, kq = lane >> 5;
@@ -808,285 +808,6 @@ __global__ void __launch_bounds__(512) k_gemm_gu_wide(GemmArgs g) {
     gemm_block_gu_wide(g, sm, blockIdx.x);
 }
 
-// ---------------------------------------------------------------- routed
-// 4-bit modes on 256-row tiles.  Wave w computes all 256 activation rows
-// against LDS weight rows [64w, 64w + 64): acc[mt][nt], mt < 8, 256
-// accumulators per lane.  Each weight fragment a wave expands from the raw
-// codes then feeds eight MFMAs (not four), halving the expansion work per
-// MFMA, and a block's fixed costs (tile lookup, scale staging, pipeline fill,
-// epilogue) cover twice the rows.  Activation rows come in NMT groups of 32
-// (a compile-time even count); groups past the tile's last row are neither
-// loaded nor multiplied.
-//
-// Pipeline, step k (j = k % 4): the activations of step k + 1 are loaded at
-// the start of step k (register stage (k + 1) % 2) and stored to LDS buffer
-// (k + 1) % 2 at its end; the codes of step k + 4 are loaded into register
-// slot k % 4, and the codes of step k + 2 (loaded two steps earlier) go to
-// LDS buffer (k + 2) % 4 at the end of step k.  During step k the waves
-// expand step k + 1's codes while the MFMAs of step k run.
-constexpr int QBM = 256;                 // activation rows per routed tile on this path
-// Passes of at least this many tokens use the 256-row tiles: below it the
-// tile count is too small to balance across the compute units (at 4096
-// tokens with Zipf routing, 214 tiles of 256 rows against 339 of 128).
-constexpr int QBM_MIN_T = 16384;
-template <int MODE>
-struct Q4Smem {
-    using C = GemmCfg<MODE>;
-    f16 a[2][QBM * LDSB];
-    uint32_t bq[QBUF][GEMM_BN * BQS];
-    uint32_t sb[GEMM_BN * C::SROW];      // (bias << 16) | scale, bf16 bits
-    float rw[MODE == MODE_DOWN ? QBM : 4];  // DOWN: routing weight x 2^6 per row
-};
-
-template <int MODE>
-__device__ __forceinline__ void gemm_block_q4(const GemmArgs& g, Q4Smem<MODE>& sm, int bid) {
-    using C = GemmCfg<MODE>;
-    static_assert(C::Q4, "4-bit modes only");
-    constexpr int NK = C::NK;
-    static_assert(NK % 4 == 0, "K steps must be a multiple of the code ring");
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, kq = lane >> 5;
-
-    // ---- (row tile, column block), as in gemm_block
-    constexpr int NB = C::NB;
-    const int n_tiles = g.tile_count[0];
-    const int live = n_tiles * NB, per_xcd = (live + 7) >> 3;
-    const int slot = bid >> 3, item = (bid & 7) * per_xcd + slot;
-    if (slot >= per_xcd || item >= live) return;
-    const int tile = item / NB, nblk = item % NB;
-    const int4 rec = *(const int4*)&g.tiles[4 * tile];  // one dependent load
-    const int e = rec.x, m0 = rec.y, seg = rec.z, rows = rec.w;  // rows: 1 .. QBM
-
-    // ---- A: 16 bytes (chunk ac) of rows ar0 + 32i, i < 8; rows past the
-    // end repeat the last valid row (their results are dropped)
-    // (buffer loads: array bases in scalar registers, 32-bit byte offsets)
-    const int ac = tid & 7, ar0 = tid >> 3;
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(MODE == MODE_GU ? g.xh : g.h);
-    uint32_t aoff[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int r = min(ar0 + 32 * i, rows - 1);
-        const uint32_t row = MODE == MODE_GU ? (uint32_t)(g.perm[seg + m0 + r] / K) * D : (uint32_t)(seg + m0 + r) * F;
-        aoff[i] = (row + 8 * ac) * 2;
-    }
-    // ---- codes: lane half bh of LDS rows br0 and br0 + 128 (one matrix per
-    // wave: LDS rows 64w .. 64w+63 are all gate or all up)
-    const int bh = tid & 1, br0 = tid >> 1;
-    auto wrow = [&](int n, int& mat) -> size_t {  // global weight row of LDS row n
-        if constexpr (C::PAIRED) {
-            mat = (n >> 5) & 1;
-            return (size_t)e * g.gu_rows + nblk * 128 + 32 * (n >> 6) + (n & 31);
-        } else {
-            mat = 0;
-            return (size_t)e * D + nblk * GEMM_BN + n;
-        }
-    };
-    uint32_t boff[2];
-    int bmat = 0;
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const size_t row = wrow(br0 + 128 * i, bmat);
-        boff[i] = (uint32_t)(row * (C::KTOT / 8) * 4) + 16 * bh;
-    }
-    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(g.q[__builtin_amdgcn_readfirstlane(bmat)]);
-    // ---- stage the block's scales and biases (LDS row n = tid) and, for
-    // DOWN, the rows' routing weights
-    {
-        int mat;
-        const size_t row = wrow(tid, mat);
-        const uint16_t* sp = g.sc[mat] + row * C::NG;
-        const uint16_t* bp = g.bi[mat] + row * C::NG;
-        uint32_t* dst = &sm.sb[tid * C::SROW];
-#pragma unroll
-        for (int i = 0; i < C::NG / 8; i++) {
-            const u32x4 sv = *(const u32x4*)(sp + 8 * i), bv = *(const u32x4*)(bp + 8 * i);
-            u32x4 lo, hi;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                lo[j] = (sv[j] & 0xffffu) | (bv[j] << 16);
-                hi[j] = (sv[j] >> 16) | (bv[j] & 0xffff0000u);
-            }
-            // groups 8i + 2j (lo) and 8i + 2j + 1 (hi)
-            *(u32x4*)(dst + 8 * i) = u32x4{lo[0], hi[0], lo[1], hi[1]};
-            *(u32x4*)(dst + 8 * i + 4) = u32x4{lo[2], hi[2], lo[3], hi[3]};
-        }
-    }
-    if constexpr (MODE == MODE_DOWN) sm.rw[tid] = g.wflat[g.perm[seg + m0 + min(tid, rows - 1)]] * PARTIAL_SCALE;
-
-    f32x16 acc[8][2];
-#pragma unroll
-    for (int mt = 0; mt < 8; mt++)
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
-
-    auto load_b = [&](int k, u32x4 (&bv)[2]) {
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-            bv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, boff[i], 32 * k, 0));
-    };
-    auto store_b = [&](const u32x4 (&bv)[2], int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; i++) *(u32x4*)&sm.bq[buf][(br0 + 128 * i) * BQS + 4 * bh] = bv[i];
-    };
-    auto dequant = [&](int k, int qbuf, f16x8 (&bf)[2][4]) {
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++) {
-            const int n = 64 * wave + 32 * nt + l32;
-            const u32x4 codes = *(const u32x4*)&sm.bq[qbuf][n * BQS + 4 * kq];
-            const uint32_t sbw = sm.sb[n * C::SROW + k];
-            const f16 sv = (f16)bf16_to_f32(sbw & 0xffffu), bv = (f16)bf16_to_f32(sbw >> 16);
-            const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
-#pragma unroll
-            for (int kk = 0; kk < 4; kk++) bf[nt][kk] = __builtin_bit_cast(f16x8, q4_word_to_f16x8(codes[kk], s2, b2));
-        }
-    };
-
-    auto main_loop = [&](auto nmt_c) {
-        constexpr int NMT = decltype(nmt_c)::value;
-        auto load_a = [&](int k, u32x4 (&av)[8]) {
-#pragma unroll
-            for (int i = 0; i < NMT; i++)
-                av[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i], 2 * BK * k, 0));
-        };
-        auto store_a = [&](const u32x4 (&av)[8], int buf) {
-#pragma unroll
-            for (int i = 0; i < NMT; i++) *(u32x4*)&sm.a[buf][(ar0 + 32 * i) * LDSB + 8 * ac] = av[i];
-        };
-        auto mfma_step = [&](int abuf, const f16x8 (&bf)[2][4]) {
-            const f16* ab = &sm.a[abuf][l32 * LDSB + 32 * kq];
-#pragma unroll
-            for (int kk = 0; kk < 4; kk++) {
-#pragma unroll
-                for (int mh = 0; mh < NMT; mh += 4) {  // four row groups per round of fragment reads
-                    f16x8 af[4];
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        if (mh + i < NMT) af[i] = *(const f16x8*)(ab + (mh + i) * 32 * LDSB + 8 * kk);
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        if (mh + i < NMT) {
-#pragma unroll
-                            for (int nt = 0; nt < 2; nt++)
-                                acc[mh + i][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[nt][kk], acc[mh + i][nt], 0, 0, 0);
-                        }
-                }
-            }
-        };
-        u32x4 aring[2][8];
-        u32x4 cring[4][2];
-#pragma unroll
-        for (int j = 0; j < 4; j++) load_b(j, cring[j]);
-        load_a(0, aring[0]);
-        store_b(cring[0], 0);
-        store_b(cring[1], 1);
-        store_a(aring[0], 0);
-        __syncthreads();  // staged scales, biases, routing weights; codes of steps 0, 1; A(0)
-        f16x8 bfr[2][2][4];
-        dequant(0, 0, bfr[0]);
-#pragma unroll 1
-        for (int k0 = 0; k0 < NK; k0 += 4) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int k = k0 + j;
-                load_a(min(k + 1, NK - 1), aring[(j + 1) & 1]);
-                load_b(min(k + 4, NK - 1), cring[j]);
-                // keep the loads here: the scheduler would otherwise sink them
-                // towards their first use and undo the prefetch
-                __builtin_amdgcn_sched_barrier(0);
-                dequant(min(k + 1, NK - 1), (j + 1) & 3, bfr[(j + 1) & 1]);
-                mfma_step(j & 1, bfr[j & 1]);
-                store_a(aring[(j + 1) & 1], (j + 1) & 1);
-                store_b(cring[(j + 2) & 3], (j + 2) & 3);
-                __syncthreads();
-            }
-        }
-    };
-    // tiles hold 1 .. 256 rows; row groups of 32 run in pairs
-    const int nmt = (rows + 31) >> 5;
-    if (nmt > 6) main_loop(std::integral_constant<int, 8>{});
-    else if (nmt > 4) main_loop(std::integral_constant<int, 6>{});
-    else if (nmt > 2) main_loop(std::integral_constant<int, 4>{});
-    else main_loop(std::integral_constant<int, 2>{});
-
-    // ---- epilogues (the loop ended with a barrier: the operand tiles are
-    // free).  Accumulator element v of acc[mt][nt] is activation row
-    // r = 32mt + 8(v/4) + 4kq + v%4 and LDS weight row 64w + 32nt + l32.
-    auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
-    if constexpr (MODE == MODE_GU) {
-        // h tile [256 rows][128 features] fp16 in LDS, then 16-byte row pieces
-        constexpr int HS = 128 + 8;
-        static_assert(QBM * HS * sizeof(f16) <= sizeof(sm.a), "h tile must fit the activation tiles");
-        f16* hb = &sm.a[0][0];
-        const int f = 32 * wave + l32;  // feature inside the block
-#pragma unroll
-        for (int mt = 0; mt < 8; mt++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const float hv = silu_f32(acc[mt][0][v]) * acc[mt][1][v];
-                hb[acc_row(mt, v) * HS + ((f & ~7) | perm8_pos(f & 7))] = (f16)hv;
-            }
-        uint16_t* const h_out = pinned(g.h_out);
-        __syncthreads();
-        // 256 rows x 16 pieces of 8 features: thread tid takes rows
-        // tid/16 + 16i, piece tid%16; LDS reads first, then the stores
-        const int c = tid & 15, rb = tid >> 4;
-        const int fo = nblk * 128 + 8 * c;
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-            u32x4 hv[8];
-#pragma unroll
-            for (int i = 0; i < 8; i++) hv[i] = *(const u32x4*)&hb[(rb + 16 * (8 * hh + i)) * HS + 8 * c];
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int r = rb + 16 * (8 * hh + i);
-                if (r < rows) *(u32x4*)&h_out[(size_t)(seg + m0 + r) * F + fo] = hv[i];
-            }
-        }
-    } else {
-        // partial tile in two halves of [128 rows][256 outputs] fp16
-        // (x 2^6 x routing weight), staged across the activation and code tiles
-        constexpr int PS = GEMM_BN + 8;
-        static_assert(128 * PS * sizeof(f16) <= offsetof(Q4Smem<MODE>, sb), "partial half tile must fit a, bq");
-        f16* pb = &sm.a[0][0];
-        uint16_t* const p_out = pinned(g.p_out);
-        const int c = tid & 31, rb = tid >> 5;
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-            if (hh) __syncthreads();  // the first half's LDS reads are done
-#pragma unroll
-            for (int mt = 4 * hh; mt < 4 * hh + 4; mt++)
-#pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const int r = acc_row(mt, v);
-                    const float wt = sm.rw[r];
-#pragma unroll
-                    for (int nt = 0; nt < 2; nt++)
-                        pb[(r - 128 * hh) * PS + 64 * wave + 32 * nt + l32] = (f16)(wt * acc[mt][nt][v]);
-                }
-            __syncthreads();
-            // 128 rows x 32 pieces of 8 outputs: thread tid takes rows
-            // tid/32 + 8i, piece tid%32; LDS reads first, then the stores
-            u32x4 pv[16];
-#pragma unroll
-            for (int i = 0; i < 16; i++) pv[i] = *(const u32x4*)&pb[(rb + 8 * i) * PS + 8 * c];
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 128 * hh + rb + 8 * i;
-                if (r < rows) *(u32x4*)&p_out[(size_t)(seg + m0 + r) * D + nblk * GEMM_BN + 8 * c] = pv[i];
-            }
-        }
-    }
-}
-
-template <int MODE>
-__global__ void __launch_bounds__(256) k_gemm_q4(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) Q4Smem<MODE> sm;
-    gemm_block_q4<MODE>(g, sm, blockIdx.x);
-}
-
 template <int MODE>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) GemmSmem<MODE> sm;
@@ -1127,7 +848,7 @@ __global__ void __launch_bounds__(256) k_prep_x(const uint16_t* __restrict__ x, 
     ((u32x4*)xh)[i] = bf16x8_to_f16x8_perm(((const u32x4*)x)[i]);
 }
 
-int gemm_bm(int T) { return T >= QBM_MIN_T ? QBM : GEMM_BM; }  // the routed tiles the sort builds
+int gemm_bm(int) { return GEMM_BM; }  // the routed tiles the sort builds
 
 hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits,
                               const uint16_t* sh_gate, const uint16_t* sh_up, uint16_t* hs, int T, const Tracer& tr,
@@ -1163,18 +884,16 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     const int max_tiles = (p.T * K + bm - 1) / bm + E;  // bound on the sort's tile count
     const int mt = (p.T + GEMM_BM - 1) / GEMM_BM;
     auto grid = [](int items) { return dim3(8 * ((items + 7) / 8)); };
-    // routed gate/up: 128 features (256 gate + up rows) per block
+    // routed gate/up: 256 features (512 gate + up rows) per block; down: 512 outputs
     g.q[0] = p.gate_q; g.sc[0] = p.gate_s; g.bi[0] = p.gate_b;
     g.q[1] = p.up_q; g.sc[1] = p.up_s; g.bi[1] = p.up_b;
     g.h_out = p.h;
-    if (bm == QBM) tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm_q4<MODE_GU>, grid(max_tiles * (F / 128)), dim3(256), 0, s, g);
-    else tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm_gu_wide, grid(max_tiles * (F / (WBN / 2))), dim3(512), 0, s, g);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm_gu_wide, grid(max_tiles * (F / (WBN / 2))), dim3(512), 0, s, g);
     // (the shared gate/up ran with the router logits)
     // routed down
     g.q[0] = p.down_q; g.sc[0] = p.down_s; g.bi[0] = p.down_b;
     g.p_out = p.partial;
-    if (bm == QBM) tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm_q4<MODE_DOWN>, grid(max_tiles * (D / GEMM_BN)), dim3(256), 0, s, g);
-    else tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm_down_wide, grid(max_tiles * (D / WBN)), dim3(512), 0, s, g);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm_down_wide, grid(max_tiles * (D / WBN)), dim3(512), 0, s, g);
     // combine
     if (p.sh_gate) {
         g.sw[0] = p.sh_down; g.p_in = p.partial; g.y = p.y; g.resid = p.resid;

@@ -61,8 +61,8 @@ def test_fused_gate_up_equals_separate(gpu, layer0, fused0, T, path):
 
 
 def test_fused_gate_up_large_tiles(gpu, layer0, fused0):
-    """A pass of 16384 tokens runs the 256-row tile kernels: the same bit
-    for bit (inputs without a routing margin: only the two layouts are
+    """A pass of 16384 tokens (the gate/up and down kernels over some 1,100
+    tiles): the same bit for bit (inputs without a routing margin: only the two layouts are
     compared)."""
     T = 16384
     x = synth.x_rows(55, T, 2048)
