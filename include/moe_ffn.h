@@ -27,15 +27,17 @@
  *     enqueues work on it: no host synchronisation, no device allocation.
  *     Faults inside kernels surface as HIP errors at the caller's next
  *     synchronisation, as for any HIP launch.
- *   - Inputs must be finite.  x, the router and shared-expert weights, and
- *     every dequantised routed weight s*q + b (and s, b themselves) must lie
- *     within the fp16 range |v| <= 65504: the GEMMs run on fp16 MFMA operands.
- *     Values below 2^-14 in magnitude lose relative precision (fp16
- *     subnormals); they contribute at most 2^-24 absolute error each.
- *     On the prefill path (MOE_FFN_PATH_PREFILL, which AUTO takes for
- *     T > MOE_FFN_DECODE_MAX_T) the intermediates are held in fp16 too:
- *     every h = silu(gate) * up must stay below 65504 in magnitude and every
- *     weighted routed-expert output w * down(h) below 1023.
+ *   - Inputs must be finite; NaN and infinite inputs are outside the
+ *     contract and are not checked.  Any finite x and weights are accepted:
+ *     no intermediate is kept in a type narrower in range than fp32.  The
+ *     decode path holds h = silu(gate) * up as two bf16 terms (16
+ *     significant bits); the prefill path's fp16 MFMA operands (x, weights,
+ *     h, the routed partials) each carry a power-of-two exponent per row
+ *     (or row piece) that scales the row's largest magnitude into
+ *     [2^14, 2^15) and is re-applied exactly in fp32.  A value far below its
+ *     row's largest (under 2^-28 of it) keeps less than fp16 precision.  The
+ *     result is only as finite as the fp32 arithmetic of the method: a
+ *     logit, gate/up value, h or output beyond the fp32 range gives inf.
  *   - Calls that share a workspace must not overlap in time (same stream, or
  *     ordered by events).
  */
@@ -208,10 +210,10 @@ int moe_ffn_forward_traced(const moe_ffn_dims *dims, int64_t T, const uint16_t *
  *   y  = bf16( h + FFN(xn) )                                     (one rounding)
  *
  * with FFN the function of moe_ffn_forward.  Readings taken where the pages
- * leave a step open: the normalised row is rounded once to bf16, the FFN's
- * input type; the sum of squares and the scale are computed in fp32 here
- * (the pages accumulate in double, which the reference computation does); the
- * FFN output is not rounded before the residual is added.  eps is the
+ * leave a step open: the sum of squares, the scale and each product are
+ * computed in double (the pages accumulate in double); the normalised row is
+ * rounded once to bf16, the FFN's input type; the FFN output is not rounded
+ * before the residual is added.  eps is the
  * caller's (the pages name it but give no value); it must be finite and
  * >= 0.
  *

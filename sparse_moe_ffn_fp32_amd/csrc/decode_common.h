@@ -25,7 +25,8 @@ struct DecodeArgs {
     float* xsum;     // [T, D/32] sums of x over 32-element chunks (T <= TINY_T)
     float* hs;       // [T, FS] shared SwiGLU output
     float* ys;       // [T, D] shared down output
-    uint16_t* h;     // fp16 [8T, F] (pair-major), perm8
+    uint16_t* h;     // bf16 [8T, F] (pair-major), perm8: h rounded to nearest
+    uint16_t* hl;    // bf16 [8T, F]: the rounded remainder h - hi (hi + lo: 16 significant bits)
     float* part;     // [8T, D] routed down outputs per pair (T > 4)
     int32_t* idx;
     float* w;

@@ -9,11 +9,12 @@
 // v_mfma_f32_16x16x32 per 32 inputs: the matrix core does the dot products,
 // so the vector ALUs only unpack nibbles and apply the per-group affine.
 //
-// Weights stay exact: the codes enter the MFMA as 128 + q (bf16) or 1024 + q
-// (fp16), both exact, and every quantisation group's partial dot product is
-// finished in fp32 as  s * acc + (b - c*s) * sum(x over the group), where the
-// group sum of the activations comes from one more MFMA against a ones
-// operand.  "Rows on N": the 16 weight rows are the MFMA's N columns, so each
+// Weights stay exact: the codes enter the MFMA as 128 + q (bf16, exact)
+// against bf16 x (gate/up) or against h held as two bf16 planes hi + lo
+// (down: 16 significant bits with the whole fp32 range, so a large h cannot
+// overflow its storage), and every quantisation group's partial dot product
+// is finished in fp32 as  s * acc + (b - 128 s) * sum(x over the group), where
+// the group sum of the activations comes from MFMAs against a ones operand.  "Rows on N": the 16 weight rows are the MFMA's N columns, so each
 // lane holds one weight row and needs one scale and one bias per group.
 //
 // Every wave issues its global loads up front, in the order it consumes
@@ -54,11 +55,7 @@ constexpr int N_SDOWN_BLK = D / 16;
 __device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8& a, const bf16x8& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma16_f16(const f16x8& a, const f16x8& b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
 // Wave-uniform read of memory that no kernel of the launch writes, through
 // the constant address space so it becomes a scalar load.
@@ -524,7 +521,12 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int slot = 4 * kq + v;
-                if (slot < tc) a.h[(size_t)sm.pairs[k][slot] * F + pc] = __builtin_bit_cast(uint16_t, (f16)(silu_f32(og[v]) * ou[v]));
+                if (slot < tc) {
+                    uint16_t hh, hlo;
+                    split_bf16(silu_f32(og[v]) * ou[v], hh, hlo);
+                    a.h[(size_t)sm.pairs[k][slot] * F + pc] = hh;
+                    a.hl[(size_t)sm.pairs[k][slot] * F + pc] = hlo;
+                }
             }
             og = f32x4{0.f, 0.f, 0.f, 0.f};
             ou = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -609,7 +611,7 @@ constexpr int DN_UNITS = DN_ITEMS * 4;              // token tiles of 16: at mos
 constexpr int DN_RING = 16;                         // groups of codes in flight per wave
 constexpr int HS_STRIDE = F + 8;                    // fp16 per staged h row (16-byte pad)
 struct DnSmem {
-    uint16_t hs[2][16][HS_STRIDE];  // token tiles of h (fp16, perm8 order), two buffers
+    uint16_t hs[2][2][16][HS_STRIDE];  // token tiles of h (bf16 hi, lo planes, perm8 order), two buffers
     int info[DN_ITEMS][4];          // expert, token count, first pair of each item
     int unit[DN_UNITS][8];          // expert, first output row, tokens in the tile, h buffer, first pair
     int pairs[DN_UNITS][16];        // pair ids of each unit's token slots
@@ -673,14 +675,21 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
     // a load under a lane-dependent branch makes the compiler wait for it
     // at once.
     const int hc = tid & 63, hr0 = tid >> 6;
-    auto load_h = [&](int k, u32x4 (&hv)[2]) {
+    auto load_h = [&](int k, u32x4 (&hv)[4]) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) hv[i] = *(const u32x4*)(a.h + (size_t)sm.pairs[k][hr0 + 8 * i] * F + 8 * hc);
+        for (int i = 0; i < 2; i++) {
+            const size_t off = (size_t)sm.pairs[k][hr0 + 8 * i] * F + 8 * hc;
+            hv[i] = *(const u32x4*)(a.h + off);
+            hv[2 + i] = *(const u32x4*)(a.hl + off);
+        }
     };
-    auto store_h = [&](int k, const u32x4 (&hv)[2]) {
+    auto store_h = [&](int k, const u32x4 (&hv)[4]) {
         const int buf = sm.unit[k][3];
 #pragma unroll
-        for (int i = 0; i < 2; i++) *(u32x4*)&sm.hs[buf][hr0 + 8 * i][8 * hc] = hv[i];
+        for (int i = 0; i < 2; i++) {
+            *(u32x4*)&sm.hs[buf][0][hr0 + 8 * i][8 * hc] = hv[i];
+            *(u32x4*)&sm.hs[buf][1][hr0 + 8 * i][8 * hc] = hv[2 + i];
+        }
     };
     // code and scale offsets of this lane's output row in unit k
     const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(a.dq);
@@ -703,7 +712,7 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
     // the first use of the scales in the loop waits for them)
     u32x4 sv, bv;
     ld_sc(row_of(0), sv, bv);
-    u32x4 hv0[2];
+    u32x4 hv0[4];
     load_h(0, hv0);
     __builtin_amdgcn_sched_barrier(0);
     constexpr int NPAIR = F / G / 2;  // group pairs per unit
@@ -718,7 +727,7 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
     store_h(0, hv0);
     __syncthreads();
 
-    const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
     static_assert(DN_RING == 2 * (F / G), "the ring holds two units");
     // bodies of two units: ring slot 4(k % 2) + q holds pair q of unit k and
     // is refilled with pair q of unit k + 2 (past the last unit: its copy)
@@ -730,14 +739,16 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
             const bool active = k < n_units;
             const int kc = min(k, n_units - 1);
             const bool next_tile = k + 1 < n_units && sm.unit[k + 1][3] != sm.unit[kc][3];
-            u32x4 hv[2];
+            u32x4 hv[4];
             if (next_tile) load_h(k + 1, hv);
             u32x4 svn, bvn;
             ld_sc(row_of(k + 1), svn, bvn);
             const uint32_t rn = row_of(k + 2);
             // A row: token slot n, at the K offset of the words this lane
             // holds after the regrouping (as in the gate/up stage)
-            const uint16_t* hrow = &sm.hs[sm.unit[kc][3]][min(n, sm.unit[kc][2] - 1)][32 * (kq & 1) + 16 * (kq >> 1)];
+            const int hb = sm.unit[kc][3], hslot = min(n, sm.unit[kc][2] - 1), hk = 32 * (kq & 1) + 16 * (kq >> 1);
+            const uint16_t* hrow = &sm.hs[hb][0][hslot][hk];
+            const uint16_t* lrow = &sm.hs[hb][1][hslot][hk];
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
             u32x4 b[4];
 #pragma unroll
@@ -749,21 +760,27 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
                     // across the loop back-edge)
                     const auto w02 = __builtin_amdgcn_permlane32_swap(ring[rs][0], ring[rs][2], false, false);
                     const auto w13 = __builtin_amdgcn_permlane32_swap(ring[rs][1], ring[rs][3], false, false);
-                    b[0] = nibble_codes(w02[0], 0x64646464u); b[1] = nibble_codes(w13[0], 0x64646464u);
-                    b[2] = nibble_codes(w02[1], 0x64646464u); b[3] = nibble_codes(w13[1], 0x64646464u);
+                    b[0] = nibble_codes(w02[0], 0x43434343u); b[1] = nibble_codes(w13[0], 0x43434343u);
+                    b[2] = nibble_codes(w02[1], 0x43434343u); b[3] = nibble_codes(w13[1], 0x43434343u);
                     __builtin_amdgcn_sched_barrier(0);
                     ring[rs] = ld_codes(rn, g >> 1);
                 }
                 const int h2 = 2 * (g & 1);
-                const f16x8 a0 = as_f16x8(*(const u32x4*)(hrow + 64 * g));
-                const f16x8 a1 = as_f16x8(*(const u32x4*)(hrow + 64 * g + 8));
+                const bf16x8 a0 = as_bf16x8(*(const u32x4*)(hrow + 64 * g));
+                const bf16x8 a1 = as_bf16x8(*(const u32x4*)(hrow + 64 * g + 8));
+                const bf16x8 l0 = as_bf16x8(*(const u32x4*)(lrow + 64 * g));
+                const bf16x8 l1 = as_bf16x8(*(const u32x4*)(lrow + 64 * g + 8));
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                f32x4 acc = mfma16_f16(a0, as_f16x8(b[h2]), z);
-                acc = mfma16_f16(a1, as_f16x8(b[h2 + 1]), acc);
-                f32x4 hsum = mfma16_f16(a0, as_f16x8(ones), z);
-                hsum = mfma16_f16(a1, as_f16x8(ones), hsum);
+                f32x4 acc = mfma16_bf16(a0, as_bf16x8(b[h2]), z);
+                acc = mfma16_bf16(a1, as_bf16x8(b[h2 + 1]), acc);
+                acc = mfma16_bf16(l0, as_bf16x8(b[h2]), acc);
+                acc = mfma16_bf16(l1, as_bf16x8(b[h2 + 1]), acc);
+                f32x4 hsum = mfma16_bf16(a0, as_bf16x8(ones), z);
+                hsum = mfma16_bf16(a1, as_bf16x8(ones), hsum);
+                hsum = mfma16_bf16(l0, as_bf16x8(ones), hsum);
+                hsum = mfma16_bf16(l1, as_bf16x8(ones), hsum);
                 const float sg = bf16_at(sv, g);
-                const float cg = bf16_at(bv, g) - 1024.0f * sg;
+                const float cg = bf16_at(bv, g) - 128.0f * sg;
 #pragma unroll
                 for (int v = 0; v < 4; v++) o[v] = __builtin_fmaf(cg, hsum[v], __builtin_fmaf(sg, acc[v], o[v]));
             }
@@ -809,7 +826,7 @@ size_t decode_workspace_bytes(int T, DecodeLayout* L) {
     l.xp = o;     o += up((size_t)T * D * 2);
     l.hs = o;     o += up((size_t)T * FS * 4);
     l.ys = o;     o += up((size_t)T * D * 4);
-    l.h = o;      o += up((size_t)T * K * F * 2);
+    l.h = o;      o += up((size_t)T * K * F * 2 * 2);  // hi and lo planes
     l.part = o;   o += up(T > TINY_T ? (size_t)T * K * D * 4 : 0);
     l.idx = o;    o += up((size_t)T * K * 4);
     l.w = o;      o += up((size_t)T * K * 4);
@@ -853,6 +870,7 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     a.hs = (float*)(ws + L.hs);
     a.ys = (float*)(ws + L.ys);
     a.h = (uint16_t*)(ws + L.h);
+    a.hl = a.h + (size_t)p.T * K * F;
     a.part = (float*)(ws + L.part);
     a.idx = p.idx ? p.idx : (int32_t*)(ws + L.idx);
     a.w = p.w ? p.w : (float*)(ws + L.w);

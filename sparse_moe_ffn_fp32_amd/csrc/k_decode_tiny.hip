@@ -11,11 +11,13 @@
 // over at least 256 blocks and each wave issues all of its loads before it
 // consumes any, so a launch costs one memory round trip.
 //
-// Weights stay exact: 4-bit codes become 128 + q (bf16, gate/up against bf16
-// x) or 1024 + q (fp16, down against fp16 h), and each 32-element piece is
-// finished in fp32 as  s * dot(code, x) + (b - c*s) * sum(x over the piece)
-// (c = 128 or 1024).  The piece sums of x come from the first launch, those
-// of h from the down launch's own staging.
+// Weights stay exact: 4-bit codes become 128 + q (bf16) against bf16 x
+// (gate/up) or against h held as two bf16 planes hi + lo (down: 16
+// significant bits and the whole fp32 range, so a large h cannot overflow
+// its storage), and each 32-element piece is finished in fp32 as
+// s * dot(code, x) + (b - 128 s) * sum(x over the piece).  The piece sums of
+// x come from the first launch, those of h from the down launch's own
+// staging.
 //
 // Every kernel is compiled per token count (T = 1 .. 4), so that all loop
 // bounds are constants: a load in a loop with a run-time trip count or under
@@ -72,12 +74,14 @@ __device__ __forceinline__ float dot_codes_bf16(uint32_t w, const u32x4& x, floa
     }
     return acc;
 }
-__device__ __forceinline__ float dot_codes_f16(uint32_t w, const u32x4& h, float acc) {
-    const u32x4 c = nibble_codes(w, 0x64646464u);  // fp16 1024 + q
+// The same codes against an activation held as two bf16 planes (hi + lo).
+__device__ __forceinline__ float dot_codes_bf16_2(uint32_t w, const u32x4& hh, const u32x4& hl, float acc) {
+    const u32x4 c = nibble_codes(w, 0x43434343u);  // bf16 128 + q
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const uint32_t cj = c[j], hj = h[j];
-        acc = __builtin_amdgcn_fdot2(as_f16x2(cj), as_f16x2(hj), acc, false);
+        const uint32_t cj = c[j], hj = hh[j], lj = hl[j];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(cj), as_bf16x2(hj), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(cj), as_bf16x2(lj), acc, false);
     }
     return acc;
 }
@@ -387,7 +391,10 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
         const int f = f0 + 2 * wave + lane;
         const float hv = silu_f32(lane ? out[1] : out[0]) * (lane ? out[3] : out[2]);
         const int pc = (f & ~7) | perm8_pos(f & 7);
-        a.h[(size_t)p * F + pc] = __builtin_bit_cast(uint16_t, (f16)hv);
+        uint16_t hh, hlo;
+        split_bf16(hv, hh, hlo);
+        a.h[(size_t)p * F + pc] = hh;
+        a.hl[(size_t)p * F + pc] = hlo;
     }
     asm volatile("" ::"v"(pf));  // the prefetch completes before the wave ends
 }
@@ -396,8 +403,8 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
 // NT = T tokens (compiled per token count: every loop bound is a constant).
 template <int NT>
 __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t hl[NT * K][F];   // h of every pair, fp16 perm8
-    __shared__ float hsum[NT * K][F / 32];                            // piece sums of h
+    __shared__ __attribute__((aligned(16))) uint16_t hl[2][NT * K][F];  // h of every pair, bf16 hi, lo planes, perm8
+    __shared__ float hsum[NT * K][F / 32];                               // piece sums of h
     __shared__ float dv[NT * K][TD_ROWS];                             // down outputs
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int T = NT, NP = T * K;
@@ -415,9 +422,12 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
     const int e_lane = a.idx[min(lane, NP - 1)] & (E - 1);  // lane l: expert of pair min(l, 8T - 1)
     // h of every pair: 8T rows x 64 pieces of 16 bytes, pieces tid + 512 i
     constexpr int NH = NP * (F / 8) / TD_THREADS;
-    u32x4 hv[NH];
+    u32x4 hv[NH], hw[NH];
 #pragma unroll
-    for (int i = 0; i < NH; i++) hv[i] = *(const u32x4*)(a.h + (size_t)(tid + TD_THREADS * i) * 8);
+    for (int i = 0; i < NH; i++) {
+        hv[i] = *(const u32x4*)(a.h + (size_t)(tid + TD_THREADS * i) * 8);
+        hw[i] = *(const u32x4*)(a.hl + (size_t)(tid + TD_THREADS * i) * 8);
+    }
     // units u = (pair u >> 3, row u & 7); lanes 16j .. 16j+15 share a unit,
     // lane piece c = lane & 15 holds 32 codes at K = 32c.  Wave w takes the
     // units 8T*w .. 8T*w + 8T - 1, four per load instruction (1 KB).
@@ -449,14 +459,14 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
     for (int i = 0; i < NH; i++) {
         const int q = tid + TD_THREADS * i;
         const int pp = q / (F / 8), k8 = q % (F / 8);
-        const u32x4 v = hv[i];
-        *(u32x4*)&hl[pp][8 * k8] = v;
+        const u32x4 v = hv[i], vl = hw[i];
+        *(u32x4*)&hl[0][pp][8 * k8] = v;
+        *(u32x4*)&hl[1][pp][8 * k8] = vl;
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const uint32_t vj = v[j];
-            const f16x2 h2 = as_f16x2(vj);
-            s += (float)h2[0] + (float)h2[1];
+            const uint32_t vj = v[j], lj = vl[j];
+            s += (lo_bf16(vj) + lo_bf16(lj)) + (hi_bf16(vj) + hi_bf16(lj));
         }
         // four consecutive threads (one lane quad) hold one 32-element piece
         s = quad_sum(s);
@@ -470,9 +480,11 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
         const int pp = u >> 3, i = u & 7;
         float acc = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; w++) acc = dot_codes_f16(cv[j][w], *(const u32x4*)&hl[pp][32 * c + 8 * w], acc);
+        for (int w = 0; w < 4; w++)
+            acc = dot_codes_bf16_2(cv[j][w], *(const u32x4*)&hl[0][pp][32 * c + 8 * w],
+                                   *(const u32x4*)&hl[1][pp][32 * c + 8 * w], acc);
         const float s = group_param(sv[j], g), bb = group_param(bv[j], g);
-        const float v = row16_sum(s * acc + (bb - 1024.0f * s) * hsum[pp][c]);
+        const float v = row16_sum(s * acc + (bb - 128.0f * s) * hsum[pp][c]);
         if (c == 0) dv[pp][i] = v;
     }
     __syncthreads();

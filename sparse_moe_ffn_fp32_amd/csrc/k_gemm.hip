@@ -15,10 +15,16 @@
 // accumulator lane l holds C[i][l%32] for i = 8*(v/4) + 4*(l/32) + v%4,
 // v = 0..15.  K advances in steps of 64, one quantisation group.  Both
 // operands are fp16 with K inside every 8-block in the perm8 order (see
-// moe_common.h); a dequantised weight is fp16(s*q + b) rounded once, x is
-// converted from bf16 exactly (within the fp16 range), h is rounded once to
-// fp16.  Inside a K step, MFMA sub-step kk and lane half kq = l/32 use K in
-// [32kq + 8kk, +8) for both operands.
+// moe_common.h).  Every operand row carries a power-of-two exponent that
+// puts its largest magnitude in [2^14, 2^15) (row_exp), so no finite input
+// or intermediate overflows fp16 or sinks into its subnormals: x rows
+// (converted from bf16 exactly), router and shared-expert rows (prepared per
+// call), routed weight rows (the group scales and biases of the row scaled
+// before s*q + b is formed, one fp16 rounding), h per (row, 256 features),
+// the shared h per (row, 128 features) and the partials per (row, 512
+// outputs).  The exponents are re-applied to the fp32 results exactly
+// (ldexp).  Inside a K step, MFMA sub-step kk and lane half kq = l/32 use K
+// in [32kq + 8kk, +8) for both operands.
 //
 // Per K step every operand goes global -> registers -> LDS in coalesced
 // pieces:
@@ -31,8 +37,8 @@
 //     s*q + b with the group's scale and bias (staged in LDS once at the
 //     block's start), one step ahead of the MFMAs that use them (8-wave
 //     blocks: in the step itself, the other wave of the SIMD covering it);
-//   16-bit weights (shared expert, router planes): converted to fp16 on the
-//     way into LDS and read back as fragments.
+//   16-bit weights (shared expert, router planes): fp16 rows prepared per
+//     call (k_prep_weights), staged in LDS and read back as fragments.
 // Global loads run ahead in a ring of register stages (three steps for 4-bit
 // weights, one otherwise); activation tiles are double-buffered, code tiles
 // quadruple-buffered; one barrier per step.  Epilogues stage the output tile
@@ -40,18 +46,20 @@
 //
 // Modes:
 //   GU     routed gate/up over the expert-sorted rows; epilogue SwiGLU
-//          h = silu(gate) * up -> fp16 (fused chain (i) of the Lily page,
-//          "Sumazinti tarpini ir busenos srauta");
+//          h = silu(gate) * up in fp32 -> fp16 with its row exponent (fused
+//          chain (i) of the Lily page, "Sumazinti tarpini ir busenos
+//          srauta");
 //   DOWN   routed down over h; epilogue * routing weight -> fp16 partials
-//          (one per assignment, scaled by 2^6, summed in fp32 by the combine);
-//   SGU    shared gate/up over all tokens (bf16 weights converted to fp16);
+//          (one per assignment, with an exponent per 512 outputs, summed in
+//          fp32 by the combine);
+//   SGU    shared gate/up over all tokens;
 //   SDOWN  shared down; epilogue = the combine: y = sum_{r=0..7} partial_r
 //          + sgate * shexp, fixed order, one bf16 rounding, no atomics
 //          (fused chain (ii));
 //   ROUTER router logits over all tokens: B = the fp32 router weights as two
-//          fp16 planes hi + lo (|w - hi - lo| <= 2^-22 |w|), paired like gate
-//          and up so one lane adds the two planes of an expert; epilogue
-//          + router bias -> fp32 logits.
+//          fp16 planes hi + lo (|w' - hi - lo| <= 2^-22 |w'|), paired like
+//          gate and up so one lane adds the two planes of an expert;
+//          epilogue + router bias -> fp32 logits.
 #include <type_traits>
 
 #include "moe_common.h"
@@ -66,10 +74,13 @@ constexpr int GEMM_BM = 128;          // activation rows per block
 constexpr int GEMM_BN = 256;          // weight rows per block
 constexpr int BK = 64;
 constexpr int LDSB = BK + 8;          // fp16 per LDS operand row (16-byte pad)
-// Partials are stored as fp16(2^6 * w * out): the power of two moves the
-// typical magnitudes (1e-6 .. 1) clear of the fp16 subnormal range and is
-// removed exactly in the combine; |w * out| must stay below 1023.
-constexpr float PARTIAL_SCALE = 64.0f;
+// A partial w * down(h) of assignment row r and output column o is stored
+// as fp16(w * acc * 2^(ew[o] - ew_max - E_w - PART_BOUND)), acc being the
+// fp32 sum over the row-normalised operands (|acc| < 512 * 2^30 = 2^39),
+// w < 2^E_w, ew[o] <= ew_max the down rows' exponents: the stored value is
+// below 2^15 whatever the magnitudes, typically about 2^5.  Its exponent
+// eh_max + ew_max + E_w + PART_BOUND is kept per (row, 512 outputs).
+constexpr int PART_BOUND = 24;
 
 // A kernel-argument pointer pinned in scalar registers.  Without this the
 // compiler reloads the argument inside every predicated store of an epilogue
@@ -85,7 +96,7 @@ struct GemmCfg {
     static constexpr bool GATED = (MODE == MODE_GU || MODE == MODE_SGU);
     static constexpr bool PAIRED = GATED || MODE == MODE_ROUTER;  // B rows in pairs of 32-row tiles
     static constexpr bool Q4 = (MODE == MODE_GU || MODE == MODE_DOWN);
-    static constexpr bool F16SRC = (MODE == MODE_ROUTER);          // B already fp16 in perm8 order
+    static constexpr bool F16SRC = !Q4;                              // B already fp16 in perm8 order
     static constexpr bool ROUTED = (MODE == MODE_GU || MODE == MODE_DOWN);
     static constexpr int KTOT = (GATED || MODE == MODE_ROUTER) ? D : (MODE == MODE_DOWN ? F : FS);
     static constexpr int NK = KTOT / BK;
@@ -98,10 +109,14 @@ struct GemmCfg {
 };
 
 struct GemmArgs {
-    // activations
+    // activations, fp16 rows each with its power-of-two exponent
     const uint16_t* xh;      // fp16 [T, D] (perm8)
+    const int32_t* ex;       // [T]
     const uint16_t* h;       // fp16 [N_assign, F] (perm8), expert-sorted rows
+    int32_t* eh;             // [N_assign, 2]: per 256 features (GU writes, DOWN reads)
     const uint16_t* hs;      // fp16 [T, FS] (perm8)
+    int32_t* ehs;            // [T, 4]: per 128 features (SGU writes, SDOWN reads)
+    int32_t* ep;             // [N_assign, 4]: partials per 512 outputs (DOWN writes, combine reads)
     // routing
     const int32_t* perm;     // sorted position -> assignment
     const int32_t* pos_of;   // assignment -> sorted position
@@ -115,7 +130,8 @@ struct GemmArgs {
     const uint32_t* q[2];    // GU: gate, up; DOWN: down
     const uint16_t* sc[2];
     const uint16_t* bi[2];
-    const uint16_t* sw[2];   // SGU: shared gate, up; SDOWN: shared down
+    const uint16_t* shw;     // SGU, SDOWN: shared fp16 [gate FS x D | up FS x D | down D x FS] (perm8)
+    const int32_t* es;       // their row exponents [2 FS + D]
     // outputs
     uint16_t* h_out;         // GU
     uint16_t* p_out;         // DOWN: fp16 partials [N_assign, D]
@@ -124,6 +140,7 @@ struct GemmArgs {
     const uint16_t* resid;   // SDOWN: bf16 [T, D] added before the rounding of y, or null
     const uint16_t* p_in;    // SDOWN: fp16 partials
     const uint16_t* wr2;     // ROUTER: fp16 [2, E, D] (hi, lo planes; perm8)
+    const int32_t* er;       // ROUTER: row exponents [E]
     const float* rbias;      // ROUTER: fp32 [E] or null
     float* logits;           // ROUTER: fp32 [T, E]
     int T;
@@ -138,13 +155,12 @@ constexpr int QBUF = 4;  // raw-code LDS buffers (codes are stored two steps ahe
 // tile.  The epilogues reuse the operand tiles (a, then b or bq).
 template <int MODE>
 struct GemmSmem {
-    using C = GemmCfg<MODE>;
     f16 a[2][GEMM_BM * LDSB];
-    f16 b[C::Q4 ? 1 : 2][C::Q4 ? 8 : GEMM_BN * LDSB];
-    uint32_t bq[C::Q4 ? QBUF : 1][C::Q4 ? GEMM_BN * BQS : 4];
-    uint32_t sb[C::Q4 ? GEMM_BN * C::SROW : 4];  // (bias << 16) | scale, bf16 bits
-    float rw[MODE == MODE_DOWN ? GEMM_BM : 4];   // DOWN: routing weight x 2^6 per row
+    f16 b[2][GEMM_BN * LDSB];
+    int32_t ea[GEMM_BM];                                // the activation rows' exponents
+    uint32_t fac[MODE == MODE_SDOWN ? GEMM_BM : 1][4];  // SDOWN: fp16 2^(ehs - ehs_max) per 128 features, both halves
     int32_t pos[MODE == MODE_SDOWN ? GEMM_BM * K : 4];  // SDOWN: each row's partial positions
+    int32_t epp[MODE == MODE_SDOWN ? GEMM_BM * K : 4];  // SDOWN: and those partials' exponents
 };
 
 // One block's work; `bid` is the block's index within its mode's grid
@@ -191,38 +207,54 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     }
 
     // ---- B: this thread covers lane half bh (K [32bh, 32bh+32) of a step) of
-    // LDS weight rows br0 and br0 + 128.
+    // LDS weight rows br0 and br0 + 128, fp16 rows of the prepared arrays
     const int bh = tid & 1, br0 = tid >> 1;
-    auto wrow = [&](int n, int& mat) -> size_t {  // global weight row of LDS row n
+    auto wrow = [&](int n) -> const uint16_t* {  // global fp16 weight row of LDS row n
         if constexpr (C::PAIRED) {
-            mat = (n >> 5) & 1;
+            const int mat = (n >> 5) & 1;
             const int feat = nblk * 128 + 32 * (n >> 6) + (n & 31);
-            if constexpr (MODE == MODE_ROUTER) return (size_t)mat * E + feat;  // plane, expert
-            return (size_t)feat;
+            if constexpr (MODE == MODE_ROUTER) return g.wr2 + ((size_t)mat * E + feat) * D;  // plane, expert
+            else return g.shw + ((size_t)mat * FS + feat) * D;                               // gate / up
         } else {
-            mat = 0;
-            const int o = nblk * GEMM_BN + n;
-            return (size_t)o;
+            return g.shw + 2 * (size_t)FS * D + (size_t)(nblk * GEMM_BN + n) * FS;           // shared down
         }
     };
     const u32x4* bpt[2];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        int mat;
-        const size_t row = wrow(br0 + 128 * i, mat);
-        if constexpr (C::F16SRC) bpt[i] = (const u32x4*)(g.wr2 + row * C::KTOT) + 4 * bh;
-        else bpt[i] = (const u32x4*)(g.sw[mat] + row * C::KTOT) + 4 * bh;
-    }
+    for (int i = 0; i < 2; i++) bpt[i] = (const u32x4*)wrow(br0 + 128 * i) + 4 * bh;
 
+    // ---- the activation rows' exponents; SDOWN: the shared h rows come in
+    // four 128-feature pieces with exponents of their own, brought to the
+    // row's largest one when staged (factor 2^(e_piece - e_max) <= 1), and the
+    // combine's partial rows with their exponents, read long before the
+    // epilogue needs them (rows past the end repeat the last valid row)
+    if (tid < GEMM_BM) {
+        const int t = m0 + min(tid, rows - 1);
+        if constexpr (MODE == MODE_SDOWN) {
+            const int4 e4 = *(const int4*)&g.ehs[(size_t)t * 4];
+            const int em = max(max(e4.x, e4.y), max(e4.z, e4.w));
+            sm.ea[tid] = em;
+            const int ev[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const f16 f = pow2_f16(ev[b] - em);
+                sm.fac[tid][b] = __builtin_bit_cast(uint32_t, f16x2{f, f});
+            }
+        } else {
+            sm.ea[tid] = g.ex[t];
+        }
+    }
     if constexpr (MODE == MODE_SDOWN) {
-        // the combine's partial rows, read long before the epilogue needs
-        // them (rows past the end repeat the last valid row)
+        const int pblk = (nblk * GEMM_BN) / 512;  // the partials' 512-column exponent block
 #pragma unroll
         for (int i = 0; i < GEMM_BM * K / 256; i++) {
             const int q = tid + 256 * i;
-            sm.pos[q] = g.pos_of[(size_t)(m0 + min(q / K, rows - 1)) * K + q % K];
+            const int pos = g.pos_of[(size_t)(m0 + min(q / K, rows - 1)) * K + q % K];
+            sm.pos[q] = pos;
+            sm.epp[q] = g.ep[(size_t)pos * 4 + pblk];
         }
     }
+    __syncthreads();  // exponents and factors before the first A store
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -232,56 +264,54 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
 
-    // Eight MFMAs per 32-row group (NMT groups, a compile-time count; all
-    // four on these token-order tiles) and sub-step kk against the
-    // activation tile in LDS buffer abuf.
-    auto mfma_step = [&](auto nmt_c, int abuf, const f16x8 (&bf)[2][4]) {
-        constexpr int NMT = decltype(nmt_c)::value;
+    // Eight MFMAs per 32-row group and sub-step kk against the activation
+    // tile in LDS buffer abuf.
+    auto mfma_step = [&](int abuf, const f16x8 (&bf)[2][4]) {
         const f16* ab = &sm.a[abuf][l32 * LDSB + 32 * kq];
 #pragma unroll
         for (int kk = 0; kk < 4; kk++) {
-            f16x8 af[NMT];
+            f16x8 af[4];
 #pragma unroll
-            for (int mt = 0; mt < NMT; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
+            for (int mt = 0; mt < 4; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
 #pragma unroll
-            for (int mt = 0; mt < NMT; mt++)
+            for (int mt = 0; mt < 4; mt++)
 #pragma unroll
                 for (int nt = 0; nt < 2; nt++)
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt][kk], acc[mt][nt], 0, 0, 0);
         }
     };
-    auto store_a = [&](auto nmt_c, const u32x4 (&av)[4], int buf) {
-#pragma unroll
-        for (int i = 0; i < decltype(nmt_c)::value; i++) *(u32x4*)&sm.a[buf][(ar0 + 32 * i) * LDSB + 8 * ac] = av[i];
-    };
-    auto load_a = [&](auto nmt_c, int k, u32x4 (&av)[4]) {
-#pragma unroll
-        for (int i = 0; i < decltype(nmt_c)::value; i++) av[i] = *(const u32x4*)(apt[i] + k * BK);
-    };
-    using All = std::integral_constant<int, 4>;
 
-    // ---- 16-bit weights: converted to fp16 (perm8) on the way into LDS,
-    // read back as MFMA operands.  Loads run one step ahead.
+    // ---- operands: global -> registers one step ahead -> LDS
     constexpr int R = 2;
     static_assert(C::NK % R == 0, "K steps must be a multiple of the ring size");
     struct Stage { u32x4 a[4]; u32x4 b[2][4]; };
     auto load = [&](int k, Stage& st) {
-        load_a(All{}, k, st.a);
+#pragma unroll
+        for (int i = 0; i < 4; i++) st.a[i] = *(const u32x4*)(apt[i] + k * BK);
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int w = 0; w < 4; w++) st.b[i][w] = bpt[i][8 * k + w];
     };
-    auto store = [&](const Stage& st, int buf) {
-        store_a(All{}, st.a, buf);
+    auto store = [&](const Stage& st, int k, int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            u32x4 v = st.a[i];
+            if constexpr (MODE == MODE_SDOWN) {  // this 128-feature piece to the row's exponent
+                const f16x2 f = __builtin_bit_cast(f16x2, sm.fac[ar0 + 32 * i][k >> 1]);
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t vj = v[j];
+                    v[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, vj) * f);
+                }
+            }
+            *(u32x4*)&sm.a[buf][(ar0 + 32 * i) * LDSB + 8 * ac] = v;
+        }
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             f16* dst = &sm.b[buf][(br0 + 128 * i) * LDSB + 32 * bh];
 #pragma unroll
-            for (int w = 0; w < 4; w++) {
-                if constexpr (C::F16SRC) *(u32x4*)(dst + 8 * w) = st.b[i][w];
-                else *(u32x4*)(dst + 8 * w) = bf16x8_to_f16x8_perm(st.b[i][w]);
-            }
+            for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = st.b[i][w];
         }
     };
     auto read_b = [&](int buf, f16x8 (&bf)[2][4]) {
@@ -294,7 +324,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     };
     Stage ring[R];
     load(0, ring[0]);
-    store(ring[0], 0);
+    store(ring[0], 0, 0);
     __syncthreads();
 #pragma unroll 1
     for (int k0 = 0; k0 < C::NK; k0 += R) {
@@ -305,8 +335,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
             __builtin_amdgcn_sched_barrier(0);
             f16x8 bf[2][4];
             read_b(j & 1, bf);
-            mfma_step(All{}, j & 1, bf);
-            store(ring[(j + 1) % R], (j + 1) & 1);
+            mfma_step(j & 1, bf);
+            store(ring[(j + 1) % R], min(k + 1, C::NK - 1), (j + 1) & 1);
             __syncthreads();
         }
     }
@@ -318,57 +348,74 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     if constexpr (MODE == MODE_ROUTER) {
         const int ex = nblk * 128 + 32 * wave + l32;
         const float b = g.rbias ? g.rbias[ex] : 0.0f;
+        const int ew = g.er[ex];
 #pragma unroll
         for (int mt = 0; mt < 4; mt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int r = acc_row(mt, v);
-                if (r < rows) g.logits[(size_t)(m0 + r) * E + ex] = (acc[mt][0][v] + acc[mt][1][v]) + b;
+                if (r < rows)
+                    g.logits[(size_t)(m0 + r) * E + ex] = __builtin_ldexpf(acc[mt][0][v] + acc[mt][1][v], sm.ea[r] + ew) + b;
             }
     } else if constexpr (C::GATED) {
-        // h tile [128 rows][128 features] fp16 in LDS, then 16-byte row pieces
-        constexpr int HS = 128 + 8;
-        static_assert(GEMM_BM * HS * sizeof(f16) <= sizeof(sm.a), "h tile must fit the activation tiles");
-        f16* hb = &sm.a[0][0];
+        // h tile [128 rows][128 features] fp32 in LDS; then per row piece of
+        // 8 features: the row's largest |h| over the block's 128 features
+        // (16 lanes), its exponent, fp16 in perm8 order, 16-byte stores
+        constexpr int HS = 128 + 4;
+        static_assert(GEMM_BM * HS * sizeof(float) <= offsetof(GemmSmem<MODE>, ea), "h tile must fit a, b");
+        float* hb = (float*)&sm.a[0][0];
         const int f = 32 * wave + l32;  // feature inside the block
+        const int eg = g.es[nblk * 128 + f], eu = g.es[FS + nblk * 128 + f];
 #pragma unroll
         for (int mt = 0; mt < 4; mt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const float hv = silu_f32(acc[mt][0][v]) * acc[mt][1][v];
-                hb[acc_row(mt, v) * HS + ((f & ~7) | perm8_pos(f & 7))] = (f16)hv;
+                const int r = acc_row(mt, v);
+                const float gv = __builtin_ldexpf(acc[mt][0][v], sm.ea[r] + eg);
+                const float uv = __builtin_ldexpf(acc[mt][1][v], sm.ea[r] + eu);
+                hb[r * HS + f] = silu_f32(gv) * uv;
             }
         uint16_t* const hs_out = pinned(g.hs_out);
+        int32_t* const ehs = pinned(g.ehs);
         __syncthreads();
-        // 128 rows x 16 pieces of 8 features: thread tid takes rows
-        // tid/16 + 16i, piece tid%16; all LDS reads first, then the stores
+        // 128 rows x 16 pieces: thread tid takes rows tid/16 + 16i, piece tid%16
         const int c = tid & 15, rb = tid >> 4;
-        u32x4 hv[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) hv[i] = *(const u32x4*)&hb[(rb + 16 * i) * HS + 8 * c];
-        const int fo = nblk * 128 + 8 * c;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int r = rb + 16 * i;
+            const f32x4 p0 = *(const f32x4*)&hb[r * HS + 8 * c], p1 = *(const f32x4*)&hb[r * HS + 8 * c + 4];
+            const float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            float m = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+            const int e = row_exp(row16_max(m));
+            const u32x4 o = f32x8_to_f16x8_perm_scaled(v, e);
             if (r < rows) {
-                *(u32x4*)&hs_out[(size_t)(m0 + r) * FS + fo] = hv[i];
+                *(u32x4*)&hs_out[(size_t)(m0 + r) * FS + nblk * 128 + 8 * c] = o;
+                if (c == 0) ehs[(size_t)(m0 + r) * 4 + nblk] = e;
             }
         }
     } else {
-        // combine: y = 2^-6 * sum_r partial_r + sgate * shexp, in two passes
+        // combine: y = sum_r partial_r * 2^ep_r + sgate * shexp, in two passes
         // of 128 columns (the fp32 shared tile of waves 2p, 2p + 1 in pass p)
         constexpr int YS = 128 + 4;
-        static_assert(GEMM_BM * YS * sizeof(float) <= offsetof(GemmSmem<MODE>, bq), "shared tile must fit a, b");
+        static_assert(GEMM_BM * YS * sizeof(float) <= offsetof(GemmSmem<MODE>, ea), "shared tile must fit a, b");
         float* yb = (float*)&sm.a[0][0];  // 128 x 132 fp32 = 67.6 KB
 #pragma unroll
         for (int pass = 0; pass < 2; pass++) {
             if ((wave >> 1) == pass) {
 #pragma unroll
-                for (int mt = 0; mt < 4; mt++)
+                for (int nt = 0; nt < 2; nt++) {
+                    const int col = 64 * (wave & 1) + 32 * nt + l32;
+                    const int ew = g.es[2 * FS + nblk * GEMM_BN + pass * 128 + col];
 #pragma unroll
-                    for (int v = 0; v < 16; v++)
+                    for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-                        for (int nt = 0; nt < 2; nt++) yb[acc_row(mt, v) * YS + 64 * (wave & 1) + 32 * nt + l32] = acc[mt][nt][v];
+                        for (int v = 0; v < 16; v++) {
+                            const int r = acc_row(mt, v);
+                            yb[r * YS + col] = __builtin_ldexpf(acc[mt][nt][v], sm.ea[r] + ew);
+                        }
+                }
             }
             __syncthreads();
             // 128 rows x 16 pieces of 8 outputs, four rows at a time: every
@@ -394,9 +441,11 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     const int pc = tid + 256 * (i0 + u), r = pc >> 4, c = pc & 15;
+                    const int rl = min(r, rows - 1);
                     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int rr = 0; rr < K; rr++)
+                    for (int rr = 0; rr < K; rr++) {
+                        const int ep = sm.epp[rl * K + rr];
 #pragma unroll
                         for (int j = 0; j < 4; j++) {
                             // copy the element to a scalar first: a bit cast of the
@@ -404,17 +453,17 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
                             // clang 22 (it reads element 0 for every j)
                             const uint32_t pw = pv[u][rr][j];
                             const f16x2 h2 = __builtin_bit_cast(f16x2, pw);
-                            sum[2 * j] += (float)h2[0];
-                            sum[2 * j + 1] += (float)h2[1];
+                            sum[2 * j] += __builtin_ldexpf((float)h2[0], ep);
+                            sum[2 * j + 1] += __builtin_ldexpf((float)h2[1], ep);
                         }
+                    }
                     // the residual (added last, before the one rounding)
-                    const int rl = min(r, rows - 1);
                     u32x4 out;
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
                         const uint32_t rj = rv[u][j];
-                        const float y0 = sum[2 * j] * (1.0f / PARTIAL_SCALE) + sg[u] * yb[rl * YS + 8 * c + 2 * j] + bf16_to_f32(rj & 0xffffu);
-                        const float y1 = sum[2 * j + 1] * (1.0f / PARTIAL_SCALE) + sg[u] * yb[rl * YS + 8 * c + 2 * j + 1] + bf16_to_f32(rj >> 16);
+                        const float y0 = sum[2 * j] + sg[u] * yb[rl * YS + 8 * c + 2 * j] + bf16_to_f32(rj & 0xffffu);
+                        const float y1 = sum[2 * j + 1] + sg[u] * yb[rl * YS + 8 * c + 2 * j + 1] + bf16_to_f32(rj >> 16);
                         out[j] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
                     }
                     if (r < rows) *(u32x4*)&yo[(size_t)(m0 + r) * D + nblk * GEMM_BN + pass * 128 + 8 * c] = out;
@@ -437,9 +486,44 @@ constexpr int WBN = 512;  // output columns per wide block
 struct WideSmem {
     f16 a[2][GEMM_BM * LDSB];
     uint32_t bq[QBUF][WBN * BQS];
-    uint32_t sb[WBN * (F / G + 4)];  // (bias << 16) | scale, bf16 bits
-    float rw[GEMM_BM];               // routing weight x 2^6 per row
+    uint32_t sb[WBN * (F / G + 4)];  // (bias' << 16) | scale', fp16 bits (row-scaled)
+    float rw[GEMM_BM];               // routing weight * 2^-(E_w + PART_BOUND) per row
+    int32_t eprow[GEMM_BM];          // eh_max + E_w + PART_BOUND per row
+    uint32_t fac[GEMM_BM];           // fp16 2^(eh_half - eh_max) for halves 0 (low) and 1 (high)
+    int32_t ew[WBN];                 // the down rows' exponents
+    int32_t red[8];
 };
+
+// A row's group scales and biases (bf16) -> the row exponent and the scaled
+// pairs (bias' << 16) | scale' in fp16 (exact: bf16 has fewer significant
+// bits), so that every dequantised weight s' q + b' of the row lies below
+// 2^15 (the affine map is monotone in q, so its extremes are b and 15 s + b).
+template <int NG>
+__device__ __forceinline__ int scale_row_params(const uint32_t (&sw)[NG / 2], const uint32_t (&bw)[NG / 2],
+                                                uint32_t (&out)[NG]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NG; i++) {
+        const float sv = (i & 1) ? __uint_as_float(sw[i >> 1] & 0xffff0000u) : __uint_as_float(sw[i >> 1] << 16);
+        const float bv = (i & 1) ? __uint_as_float(bw[i >> 1] & 0xffff0000u) : __uint_as_float(bw[i >> 1] << 16);
+        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(bv), __builtin_fabsf(__builtin_fmaf(15.0f, sv, bv))));
+    }
+    const int e = row_exp(m);
+#pragma unroll
+    for (int i = 0; i < NG; i++) {
+        const float sv = (i & 1) ? __uint_as_float(sw[i >> 1] & 0xffff0000u) : __uint_as_float(sw[i >> 1] << 16);
+        const float bv = (i & 1) ? __uint_as_float(bw[i >> 1] & 0xffff0000u) : __uint_as_float(bw[i >> 1] << 16);
+        const f16x2 p = {(f16)__builtin_ldexpf(sv, -e), (f16)__builtin_ldexpf(bv, -e)};
+        out[i] = __builtin_bit_cast(uint32_t, p);
+    }
+    return e;
+}
+
+// Group g's fp16 scale and bias from a staged pair, each in both halves.
+__device__ __forceinline__ void group_sb(uint32_t sbw, f16x2& s2, f16x2& b2) {
+    s2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sbw, sbw, 0x01000100u));
+    b2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sbw, sbw, 0x03020302u));
+}
 
 __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem& sm, int bid) {
     using C = GemmCfg<MODE_DOWN>;
@@ -467,21 +551,34 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
 #pragma unroll
     for (int i = 0; i < 2; i++)
         bpt[i] = (const u32x4*)(g.q[0] + ((size_t)e * D + nblk * WBN + br0 + 256 * i) * (F / 8)) + bh;
-    // ---- scales and biases (LDS row n = tid), routing weights
+    // ---- scales and biases of LDS row n = tid, scaled by the row's exponent
+    // ew (and the block's largest, ew_max); per tile row: the h exponents of
+    // its two 256-feature halves (the staged A rows are brought to the larger
+    // one) and the routing weight w with its binary exponent E_w
     {
         const size_t row = (size_t)e * D + nblk * WBN + tid;
         const u32x4 sv = *(const u32x4*)(g.sc[0] + row * C::NG), bv = *(const u32x4*)(g.bi[0] + row * C::NG);
-        u32x4 lo, hi;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            lo[j] = (sv[j] & 0xffffu) | (bv[j] << 16);
-            hi[j] = (sv[j] >> 16) | (bv[j] & 0xffff0000u);
-        }
+        const uint32_t sw[4] = {sv[0], sv[1], sv[2], sv[3]}, bw[4] = {bv[0], bv[1], bv[2], bv[3]};
+        uint32_t pr[C::NG];
+        const int ew = scale_row_params<C::NG>(sw, bw, pr);
         uint32_t* dst = &sm.sb[tid * SROW];
-        *(u32x4*)(dst) = u32x4{lo[0], hi[0], lo[1], hi[1]};
-        *(u32x4*)(dst + 4) = u32x4{lo[2], hi[2], lo[3], hi[3]};
+        *(u32x4*)(dst) = u32x4{pr[0], pr[1], pr[2], pr[3]};
+        *(u32x4*)(dst + 4) = u32x4{pr[4], pr[5], pr[6], pr[7]};
+        sm.ew[tid] = ew;
+        const int wm = wave_max(ew);
+        if (lane == 0) sm.red[wave] = wm;
     }
-    if (tid < GEMM_BM) sm.rw[tid] = g.wflat[g.perm[seg + m0 + min(tid, rows - 1)]] * PARTIAL_SCALE;
+    if (tid < GEMM_BM) {
+        const int sr = seg + m0 + min(tid, rows - 1);
+        const int2 e2 = *(const int2*)&g.eh[(size_t)sr * 2];
+        const int em = max(e2.x, e2.y);
+        sm.fac[tid] = __builtin_bit_cast(uint32_t, f16x2{pow2_f16(e2.x - em), pow2_f16(e2.y - em)});
+        const float w = g.wflat[g.perm[sr]];
+        int ewt;
+        __builtin_frexpf(w, &ewt);  // w < 2^ewt
+        sm.rw[tid] = __builtin_ldexpf(w, -ewt - PART_BOUND);
+        sm.eprow[tid] = em + ewt + PART_BOUND;
+    }
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -506,9 +603,21 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt][kk], acc[mt][nt], 0, 0, 0);
         }
     };
-    auto store_a = [&](const u32x4 (&av)[2], int buf) {
+    // the A rows of step k times their half's factor (k < 4: features
+    // 0..255, else 256..511)
+    auto store_a = [&](const u32x4 (&av)[2], int k, int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) *(u32x4*)&sm.a[buf][(ar0 + 64 * i) * LDSB + 8 * ac] = av[i];
+        for (int i = 0; i < 2; i++) {
+            const uint32_t fw = sm.fac[ar0 + 64 * i];
+            const f16x2 f = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(fw, fw, k < 4 ? 0x01000100u : 0x03020302u));
+            u32x4 v = av[i];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint32_t vj = v[j];
+                v[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, vj) * f);
+            }
+            *(u32x4*)&sm.a[buf][(ar0 + 64 * i) * LDSB + 8 * ac] = v;
+        }
     };
     auto load_a = [&](int k, u32x4 (&av)[2]) {
 #pragma unroll
@@ -527,9 +636,8 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
         for (int nt = 0; nt < 2; nt++) {
             const int n = 64 * wave + 32 * nt + l32;
             const u32x4 codes = *(const u32x4*)&sm.bq[qbuf][n * BQS + 4 * kq];
-            const uint32_t sbw = sm.sb[n * SROW + k];
-            const f16 sv = (f16)bf16_to_f32(sbw & 0xffffu), bv = (f16)bf16_to_f32(sbw >> 16);
-            const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
+            f16x2 s2, b2;
+            group_sb(sm.sb[n * SROW + k], s2, b2);
 #pragma unroll
             for (int kk = 0; kk < 4; kk++) {
                 const uint32_t cw = codes[kk];
@@ -551,8 +659,8 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
             load_b(min(j + 1, C::NK - 1), ring[j].b);
         }
         store_b(c0, 0);
-        __syncthreads();  // staged scales, biases, routing weights; codes of step 0
-        store_a(ring[0].a, 0);
+        __syncthreads();  // staged scales, biases, exponents, routing weights; codes of step 0
+        store_a(ring[0].a, 0, 0);
         store_b(ring[0].b, 1);
         __syncthreads();
 #pragma unroll 1
@@ -567,7 +675,7 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
                 f16x8 bfr[2][4];
                 dequant(k, j % QBUF, bfr);
                 mfma_step(nmt_c, j & 1, bfr);
-                store_a(ring[(j + 1) % R].a, (j + 1) & 1);
+                store_a(ring[(j + 1) % R].a, min(k + 1, C::NK - 1), (j + 1) & 1);
                 store_b(ring[(j + 1) % R].b, (j + 2) % QBUF);
                 __syncthreads();
             }
@@ -579,22 +687,30 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
     else if (nmt == 2) main_loop(std::integral_constant<int, 2>{});
     else main_loop(std::integral_constant<int, 1>{});
 
-    // ---- epilogue: partial tile [128 rows][512 outputs] fp16 (x 2^6 x
-    // routing weight) in LDS (a and bq), then 16-byte row pieces
+    // ---- epilogue: partial tile [128 rows][512 outputs] fp16 (routing
+    // weight, exponents as PART_BOUND states) in LDS (a and bq), then 16-byte
+    // row pieces; the rows' exponents
     constexpr int PS = WBN + 8;
     static_assert(GEMM_BM * PS * sizeof(f16) <= offsetof(WideSmem, sb), "partial tile must fit a, bq");
     f16* pb = &sm.a[0][0];
     auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
+    int ewmax = sm.red[0];
 #pragma unroll
-    for (int mt = 0; mt < 4; mt++)
+    for (int w = 1; w < 8; w++) ewmax = max(ewmax, sm.red[w]);
 #pragma unroll
-        for (int v = 0; v < 16; v++) {
-            const int r = acc_row(mt, v);
-            const float wt = sm.rw[r];
+    for (int nt = 0; nt < 2; nt++) {
+        const int col = 64 * wave + 32 * nt + l32;
+        const int sh = sm.ew[col] - ewmax;  // <= 0
 #pragma unroll
-            for (int nt = 0; nt < 2; nt++) pb[r * PS + 64 * wave + 32 * nt + l32] = (f16)(wt * acc[mt][nt][v]);
-        }
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int r = acc_row(mt, v);
+                pb[r * PS + col] = (f16)__builtin_ldexpf(sm.rw[r] * acc[mt][nt][v], sh);
+            }
+    }
     uint16_t* const p_out = pinned(g.p_out);
+    if (tid < rows) g.ep[(size_t)(seg + m0 + tid) * 4 + nblk] = sm.eprow[tid] + ewmax;
     __syncthreads();
     // 128 rows x 64 pieces of 8 outputs: thread tid takes rows tid/64 + 8i,
     // piece tid%64; LDS reads in two halves of 8, each before its stores
@@ -629,7 +745,9 @@ __global__ void __launch_bounds__(512) k_gemm_down_wide(GemmArgs g) {
 struct WideGuSmem {
     f16 a[2][GEMM_BM * LDSB];
     uint32_t bq[2][WBN * BQS];
-    uint32_t sb[WBN * (D / G + 4)];  // (bias << 16) | scale, bf16 bits
+    uint32_t sb[WBN * (D / G + 4)];  // (bias' << 16) | scale', fp16 bits (row-scaled)
+    int32_t ea[GEMM_BM];             // the gathered x rows' exponents
+    int32_t ew[WBN];                 // the gate/up rows' exponents
 };
 
 __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem& sm, int bid) {
@@ -669,27 +787,30 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
         const size_t row = wrow(br0 + 256 * i, mat);
         bpt[i] = (const u32x4*)(g.q[mat] + row * (D / 8)) + bh;
     }
-    // ---- scales and biases of every group (LDS row n = tid)
+    // ---- scales and biases of every group of LDS row n = tid, scaled by
+    // the row's exponent; the gathered x rows' exponents
     {
         int mat;
         const size_t row = wrow(tid, mat);
         const uint16_t* sp = g.sc[mat] + row * C::NG;
         const uint16_t* bp = g.bi[mat] + row * C::NG;
-        uint32_t* dst = &sm.sb[tid * SROW];
+        uint32_t sw[C::NG / 2], bw[C::NG / 2];
 #pragma unroll
         for (int i = 0; i < C::NG / 8; i++) {
             const u32x4 sv = *(const u32x4*)(sp + 8 * i), bv = *(const u32x4*)(bp + 8 * i);
-            u32x4 lo, hi;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                lo[j] = (sv[j] & 0xffffu) | (bv[j] << 16);
-                hi[j] = (sv[j] >> 16) | (bv[j] & 0xffff0000u);
+                sw[4 * i + j] = sv[j];
+                bw[4 * i + j] = bv[j];
             }
-            // groups 8i + 2j (lo) and 8i + 2j + 1 (hi)
-            *(u32x4*)(dst + 8 * i) = u32x4{lo[0], hi[0], lo[1], hi[1]};
-            *(u32x4*)(dst + 8 * i + 4) = u32x4{lo[2], hi[2], lo[3], hi[3]};
         }
+        uint32_t pr[C::NG];
+        sm.ew[tid] = scale_row_params<C::NG>(sw, bw, pr);
+        uint32_t* dst = &sm.sb[tid * SROW];
+#pragma unroll
+        for (int i = 0; i < C::NG / 4; i++) *(u32x4*)(dst + 4 * i) = u32x4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
     }
+    if (tid < GEMM_BM) sm.ea[tid] = g.ex[g.perm[seg + m0 + min(tid, rows - 1)] / K];
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -719,9 +840,8 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
         for (int nt = 0; nt < 2; nt++) {
             const int n = 64 * wave + 32 * nt + l32;
             const u32x4 codes = *(const u32x4*)&sm.bq[qbuf][n * BQS + 4 * kq];
-            const uint32_t sbw = sm.sb[n * SROW + k];
-            const f16 sv = (f16)bf16_to_f32(sbw & 0xffffu), bv = (f16)bf16_to_f32(sbw >> 16);
-            const f16x2 s2 = {sv, sv}, b2 = {bv, bv};
+            f16x2 s2, b2;
+            group_sb(sm.sb[n * SROW + k], s2, b2);
 #pragma unroll
             for (int kk = 0; kk < 4; kk++) {
                 const uint32_t cw = codes[kk];
@@ -773,33 +893,47 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
     else if (nmt == 2) main_loop(std::integral_constant<int, 2>{});
     else main_loop(std::integral_constant<int, 1>{});
 
-    // ---- epilogue: h tile [128 rows][256 features] fp16 in LDS (a, bq),
-    // SwiGLU of the lane's gate and up values, then 16-byte row pieces
-    constexpr int HS = WBN / 2 + 8;
-    static_assert(GEMM_BM * HS * sizeof(f16) <= offsetof(WideGuSmem, sb), "h tile must fit a, bq");
-    f16* hb = &sm.a[0][0];
+    // ---- epilogue: h tile [128 rows][256 features] fp32 in LDS (a, bq,
+    // sb): SwiGLU of the lane's gate and up values with their exponents
+    // applied; then per row piece of 8 features: the row's largest |h| over
+    // the block's 256 features (32 lanes), its exponent, fp16 in perm8
+    // order, 16-byte stores
+    constexpr int HS = WBN / 2 + 4;
+    static_assert(GEMM_BM * HS * sizeof(float) <= offsetof(WideGuSmem, ea), "h tile must fit a, bq, sb");
+    float* hb = (float*)&sm.a[0][0];
     auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
     const int f = 32 * wave + l32;  // feature inside the block
+    const int eg = sm.ew[64 * wave + l32], eu = sm.ew[64 * wave + 32 + l32];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
         for (int v = 0; v < 16; v++) {
-            const float hv = silu_f32(acc[mt][0][v]) * acc[mt][1][v];
-            hb[acc_row(mt, v) * HS + ((f & ~7) | perm8_pos(f & 7))] = (f16)hv;
+            const int r = acc_row(mt, v);
+            const float gv = __builtin_ldexpf(acc[mt][0][v], sm.ea[r] + eg);
+            const float uv = __builtin_ldexpf(acc[mt][1][v], sm.ea[r] + eu);
+            hb[r * HS + f] = silu_f32(gv) * uv;
         }
     uint16_t* const h_out = pinned(g.h_out);
+    int32_t* const eh = pinned(g.eh);
     __syncthreads();
     // 128 rows x 32 pieces of 8 features: thread tid takes rows tid/32 + 16i,
-    // piece tid%32; all LDS reads first, then the stores
+    // piece tid%32 (a half-wave per row)
     const int c = tid & 31, rb = tid >> 5;
-    u32x4 hv[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) hv[i] = *(const u32x4*)&hb[(rb + 16 * i) * HS + 8 * c];
     const int fo = nblk * (WBN / 2) + 8 * c;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         const int r = rb + 16 * i;
-        if (r < rows) *(u32x4*)&h_out[(size_t)(seg + m0 + r) * F + fo] = hv[i];
+        const f32x4 p0 = *(const f32x4*)&hb[r * HS + 8 * c], p1 = *(const f32x4*)&hb[r * HS + 8 * c + 4];
+        const float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+        const int e = row_exp(half32_max(m));
+        const u32x4 o = f32x8_to_f16x8_perm_scaled(v, e);
+        if (r < rows) {
+            *(u32x4*)&h_out[(size_t)(seg + m0 + r) * F + fo] = o;
+            if (c == 0) eh[(size_t)(seg + m0 + r) * 2 + nblk] = e;
+        }
     }
 }
 
@@ -827,38 +961,72 @@ __global__ void __launch_bounds__(256) k_gemm_router_sgu(GemmArgs g, int n_route
         gemm_block<MODE_SGU>(g, *reinterpret_cast<GemmSmem<MODE_SGU>*>(sm), blockIdx.x - n_router);
 }
 
-// y = sum_r partial_r (+ the residual), for layers without a shared expert.
-__global__ void __launch_bounds__(256) k_combine_routed(const uint16_t* __restrict__ p, const int32_t* __restrict__ pos_of,
-                                                        const uint16_t* resid, uint16_t* y, int T) {
+// y = sum_r partial_r * 2^ep_r (+ the residual), for layers without a
+// shared expert.
+__global__ void __launch_bounds__(256) k_combine_routed(const uint16_t* __restrict__ p, const int32_t* __restrict__ ep,
+                                                        const int32_t* __restrict__ pos_of, const uint16_t* resid,
+                                                        uint16_t* y, int T) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= T * D) return;
     const int t = i / D, o = i % D;
     float sum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < K; r++) sum += (float)__builtin_bit_cast(f16, p[(size_t)pos_of[t * K + r] * D + o]);
-    sum *= 1.0f / PARTIAL_SCALE;
+    for (int r = 0; r < K; r++) {
+        const int pos = pos_of[t * K + r];
+        sum += __builtin_ldexpf((float)__builtin_bit_cast(f16, p[(size_t)pos * D + o]), ep[(size_t)pos * 4 + o / 512]);
+    }
     if (resid) sum += bf16_to_f32(resid[i]);
     y[i] = f32_to_bf16_rne(sum);
 }
 
-// x bf16 [T, D] -> fp16 [T, D] in perm8 order.
-__global__ void __launch_bounds__(256) k_prep_x(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh, int n8) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    ((u32x4*)xh)[i] = bf16x8_to_f16x8_perm(((const u32x4*)x)[i]);
+// x bf16 [T, D] -> fp16 [T, D] in perm8 order, each row times 2^-ex[t] with
+// its exponent (row_exp of its largest |x|); exact where the scaled value is
+// an fp16 normal.  One wave per row, lane pieces lane + 64 i.
+__global__ void __launch_bounds__(256) k_prep_x(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
+                                                int32_t* __restrict__ ex, int T) {
+    const int lane = threadIdx.x & 63, t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const u32x4* src = (const u32x4*)(x + (size_t)t * D);
+    u32x4 d[4];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        d[i] = src[lane + 64 * i];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t w = d[i][j];
+            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w << 16)),
+                                                   __builtin_fabsf(__uint_as_float(w & 0xffff0000u))));
+        }
+    }
+    m = __builtin_bit_cast(float, wave_max(__builtin_bit_cast(int, m)));
+    const int e = row_exp(m);
+    u32x4* dst = (u32x4*)(xh + (size_t)t * D);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t w = d[i][j];
+            f[2 * j] = __uint_as_float(w << 16);
+            f[2 * j + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+        dst[lane + 64 * i] = f32x8_to_f16x8_perm_scaled(f, e);
+    }
+    if (lane == 0) ex[t] = e;
 }
 
 int gemm_bm(int) { return GEMM_BM; }  // the routed tiles the sort builds
 
-hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits,
-                              const uint16_t* sh_gate, const uint16_t* sh_up, uint16_t* hs, int T, const Tracer& tr,
-                              hipStream_t s) {
+hipError_t launch_router_gemm(const uint16_t* xh, const int32_t* ex, const uint16_t* wr2, const int32_t* er,
+                              const float* bias, float* logits, const uint16_t* shw, const int32_t* es, uint16_t* hs,
+                              int32_t* ehs, int T, const Tracer& tr, hipStream_t s) {
     GemmArgs g = {};
-    g.xh = xh; g.wr2 = wr2; g.rbias = bias; g.logits = logits; g.T = T;
+    g.xh = xh; g.ex = ex; g.wr2 = wr2; g.er = er; g.rbias = bias; g.logits = logits; g.T = T;
     const int mt = (T + GEMM_BM - 1) / GEMM_BM;
     const int n_router = 8 * ((mt * (E / 128) + 7) / 8);
-    if (sh_gate) {
-        g.sw[0] = sh_gate; g.sw[1] = sh_up; g.hs_out = hs;
+    if (shw) {
+        g.shw = shw; g.es = es; g.hs_out = hs; g.ehs = ehs;
         const int n_sgu = 8 * ((mt * (FS / 128) + 7) / 8);
         tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm_router_sgu, dim3(n_router + n_sgu), dim3(256), 0, s, g, n_router);
     } else {
@@ -867,15 +1035,15 @@ hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const flo
     return hipGetLastError();
 }
 
-hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s) {
-    const int n8 = T * D / 8;
-    hipLaunchKernelGGL(k_prep_x, dim3((n8 + 255) / 256), dim3(256), 0, s, x, xh, n8);
+hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int32_t* ex, int T, hipStream_t s) {
+    hipLaunchKernelGGL(k_prep_x, dim3((T + 3) / 4), dim3(256), 0, s, x, xh, ex, T);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hipStream_t s) {
     GemmArgs g = {};
-    g.xh = p.xh; g.h = p.h; g.hs = p.hs;
+    g.xh = p.xh; g.ex = p.ex; g.h = p.h; g.eh = p.eh; g.hs = p.hs; g.ehs = p.ehs; g.ep = p.ep;
+    g.shw = p.shw; g.es = p.es;
     g.perm = p.perm; g.pos_of = p.pos_of; g.offs = p.offs; g.tiles = p.tiles; g.tile_count = p.tile_count;
     g.wflat = p.wflat; g.sgate = p.sgate;
     g.gu_rows = p.gu_rows;
@@ -895,12 +1063,12 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.p_out = p.partial;
     tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_gemm_down_wide, grid(max_tiles * (D / WBN)), dim3(512), 0, s, g);
     // combine
-    if (p.sh_gate) {
-        g.sw[0] = p.sh_down; g.p_in = p.partial; g.y = p.y; g.resid = p.resid;
+    if (p.shw) {
+        g.p_in = p.partial; g.y = p.y; g.resid = p.resid;
         tr.launch(MOE_FFN_KERNEL_COMBINE, k_gemm<MODE_SDOWN>, grid(mt * (D / GEMM_BN)), dim3(256), 0, s, g);
     } else {
         tr.launch(MOE_FFN_KERNEL_COMBINE, k_combine_routed, dim3((p.T * D + 255) / 256), dim3(256), 0, s,
-                  (const uint16_t*)p.partial, (const int32_t*)p.pos_of, p.resid, p.y, p.T);
+                  (const uint16_t*)p.partial, (const int32_t*)p.ep, (const int32_t*)p.pos_of, p.resid, p.y, p.T);
     }
     return hipGetLastError();
 }

@@ -7,11 +7,12 @@
 // ffn_gate_inp_shexp . x).
 //
 // Large T: the logits are a [T, 2048] x [2048, 256] GEMM on fp16 MFMA (the
-// grouped-GEMM kernel's router mode).  x is exact in fp16 within the fp16
-// range; each fp32 router weight is split into two fp16 planes hi + lo with
-// |w - hi - lo| <= max(2^-22 |w|, 2^-25) (hi = fp16(w), lo = fp16(w - hi),
-// w - hi exact in fp32; the absolute term is fp16's subnormal spacing), so a
-// logit over 2048 inputs of unit size is off by ~1e-6 at most: far below the
+// grouped-GEMM kernel's router mode).  Each x row and each router row is
+// scaled by its own power of two into the fp16 range (x exactly, bf16 having
+// fewer significant bits than fp16), each fp32 router weight split into two
+// fp16 planes hi + lo with |w' - hi - lo| <= 2^-22 |w'|, and the exponents
+// are re-applied exactly to the fp32 sums, so a logit over 2048 inputs of
+// unit size is off by ~1e-6 at most whatever the magnitudes: far below the
 // 1e-4 top-8/top-9 margin the index-exactness bar is stated for.
 #include "moe_common.h"
 #include "moe_kernels.h"
@@ -19,23 +20,98 @@
 
 namespace moe {
 
-// Wr fp32 [E, D] -> Wr2 fp16 [2, E, D] (hi, lo), K in the perm8 order.  One
-// thread per 8-element block.
-__global__ void __launch_bounds__(256) k_split_router(const float* __restrict__ wr, uint16_t* __restrict__ wr2) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= E * D / 8) return;
-    const f32x4 a = ((const f32x4*)wr)[2 * i], b = ((const f32x4*)wr)[2 * i + 1];
-    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    u32x4 hi, lo;
+// The fp16 operands of the prefill GEMMs that come from weight matrices
+// given in other types, one wave per row, each row with its power-of-two
+// exponent (row_exp: the row's largest magnitude scaled into [2^14, 2^15)):
+//   rows [0, E):  router fp32 [E, D] -> wr2 fp16 [2, E, D], hi = fp16(w'),
+//                 lo = fp16(w' - hi) for w' = w 2^-e (w' - hi is exact in
+//                 fp32), so |w' - hi - lo| <= 2^-22 |w'| (or 2^-25 absolute
+//                 in the subnormals, under 2^-39 of the row's largest
+//                 value); er[row] = e;
+//   rows [E, E + 2 FS + D): the shared expert's gate, up (K = D) and down
+//                 (K = FS) rows, bf16 -> fp16 (exact within the scaled
+//                 range) in shw = [gate FS x D | up FS x D | down D x FS];
+//                 es[row - E] = e.
+// K is in the perm8 order everywhere.
+__global__ void __launch_bounds__(256) k_prep_weights(const float* __restrict__ wr, uint16_t* __restrict__ wr2,
+                                                      int32_t* __restrict__ er, const uint16_t* __restrict__ sg,
+                                                      const uint16_t* __restrict__ su, const uint16_t* __restrict__ sd,
+                                                      uint16_t* __restrict__ shw, int32_t* __restrict__ es, int n_rows) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n_rows) return;
+    if (row < E) {
+        // 256 pieces of 8 weights: lane takes pieces lane + 64 i
+        const f32x4* src = (const f32x4*)(wr + (size_t)row * D);
+        float v[4][8];
+        float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {  // perm8: pair j holds elements j and j + 4
-        const f16 h0 = (f16)v[j], h1 = (f16)v[j + 4];
-        const f16 l0 = (f16)(v[j] - (float)h0), l1 = (f16)(v[j + 4] - (float)h1);
-        hi[j] = __builtin_bit_cast(uint32_t, f16x2{h0, h1});
-        lo[j] = __builtin_bit_cast(uint32_t, f16x2{l0, l1});
+        for (int i = 0; i < 4; i++) {
+            const f32x4 a = src[2 * (lane + 64 * i)], b = src[2 * (lane + 64 * i) + 1];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                v[i][j] = a[j];
+                v[i][4 + j] = b[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; j++) m = __builtin_fmaxf(m, __builtin_fabsf(v[i][j]));
+        }
+        m = __builtin_bit_cast(float, wave_max(__builtin_bit_cast(int, m)));
+        const int e = row_exp(m);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            u32x4 hi, lo;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {  // perm8: pair j holds elements j and j + 4
+                const float w0 = __builtin_ldexpf(v[i][j], -e), w1 = __builtin_ldexpf(v[i][j + 4], -e);
+                const f16 h0 = (f16)w0, h1 = (f16)w1;
+                const f16 l0 = (f16)(w0 - (float)h0), l1 = (f16)(w1 - (float)h1);
+                hi[j] = __builtin_bit_cast(uint32_t, f16x2{h0, h1});
+                lo[j] = __builtin_bit_cast(uint32_t, f16x2{l0, l1});
+            }
+            u32x4* dst = (u32x4*)(wr2 + (size_t)row * D) + lane + 64 * i;
+            dst[0] = hi;
+            dst[E * D / 8] = lo;
+        }
+        if (lane == 0) er[row] = e;
+        return;
     }
-    ((u32x4*)wr2)[i] = hi;
-    ((u32x4*)wr2)[E * D / 8 + i] = lo;
+    const int r = row - E;
+    const bool down = r >= 2 * FS;
+    const int kdim = down ? FS : D;
+    const uint16_t* src = r < FS ? sg + (size_t)r * D : r < 2 * FS ? su + (size_t)(r - FS) * D : sd + (size_t)(r - 2 * FS) * FS;
+    uint16_t* dst = shw + (size_t)(down ? 2 * FS * D + (r - 2 * FS) * FS : r * D);
+    const int npc = kdim / 8 / 64;  // pieces of 8 per lane: 4 (K = D) or 1 (K = FS)
+    u32x4 d[4];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (i < npc) {
+            d[i] = ((const u32x4*)src)[lane + 64 * i];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint32_t w = d[i][j];
+                m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w << 16)),
+                                                       __builtin_fabsf(__uint_as_float(w & 0xffff0000u))));
+            }
+        }
+    }
+    m = __builtin_bit_cast(float, wave_max(__builtin_bit_cast(int, m)));
+    const int e = row_exp(m);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (i < npc) {
+            float f[8];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint32_t w = d[i][j];
+                f[2 * j] = __uint_as_float(w << 16);
+                f[2 * j + 1] = __uint_as_float(w & 0xffff0000u);
+            }
+            ((u32x4*)dst)[lane + 64 * i] = f32x8_to_f16x8_perm_scaled(f, e);
+        }
+    }
+    if (lane == 0) es[r] = e;
 }
 
 // One wave per token: top-8 of the 256 logits, renormalised softmax weights,
@@ -95,8 +171,10 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
     }
 }
 
-hipError_t launch_split_router(const float* wr, uint16_t* wr2, hipStream_t s) {
-    hipLaunchKernelGGL(k_split_router, dim3((E * D / 8 + 255) / 256), dim3(256), 0, s, wr, wr2);
+hipError_t launch_prep_weights(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
+                               const uint16_t* sd, uint16_t* shw, int32_t* es, hipStream_t s) {
+    const int n_rows = E + (sg ? 2 * FS + D : 0);
+    hipLaunchKernelGGL(k_prep_weights, dim3((n_rows + 3) / 4), dim3(256), 0, s, wr, wr2, er, sg, su, sd, shw, es, n_rows);
     return hipGetLastError();
 }
 

@@ -33,6 +33,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// A finite fp32 value as two bf16: hi = v truncated to bf16 (never
+// overflows), lo = the remainder v - hi (exact in fp32) rounded to bf16.
+// hi + lo carries 16 significant bits of v (|v - hi - lo| <= 2^-16 |v|) with
+// the whole fp32 range, so intermediates stored this way cannot overflow
+// where fp16 would.
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+    const uint32_t h = __float_as_uint(v) & 0xffff0000u;
+    hi = (uint16_t)(h >> 16);
+    lo = f32_to_bf16_rne(v - __uint_as_float(h));
+}
+
 // Nearest bf16 of a finite double, ties to even: round to fp32 by truncation
 // with a sticky last bit (round to odd: 24 bits keep what the second rounding
 // needs), then to bf16 to nearest even.  One correct rounding overall.
@@ -113,6 +124,64 @@ __device__ __forceinline__ u32x4 q4_word_to_f16x8(uint32_t w, f16x2 s2, f16x2 b2
         o[j] = __builtin_bit_cast(uint32_t, r);
     }
     return o;
+}
+
+// ---- Power-of-two row exponents of the fp16 MFMA operands.
+//
+// Every fp16 operand row (activations, dequantised or converted weights,
+// intermediates) is stored as v * 2^-e with e chosen from the row's largest
+// magnitude m so that m * 2^-e lies in [2^14, 2^15): no finite input
+// overflows the fp16 range, values down to 2^-28 m keep their full 11-bit
+// significand, and the exponents are re-applied exactly (ldexp) in fp32.
+// An all-zero row gets EXP_ZERO, below any real exponent, so it never
+// dominates a maximum of exponents.
+constexpr int EXP_ZERO = -1000;
+__device__ __forceinline__ int row_exp(float m) {
+    if (!(m > 0.0f)) return EXP_ZERO;
+    int e;
+    __builtin_frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
+    return e - 15;
+}
+
+// Largest value of a non-negative float over each 16-lane row (every lane
+// of the row gets it); and over each half-wave of 32 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_fmax_step(float v) {
+    return __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false)));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = dpp_fmax_step<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_fmax_step<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_fmax_step<0x141>(v);  // row_half_mirror
+    v = dpp_fmax_step<0x140>(v);  // row_mirror
+    return v;
+}
+__device__ __forceinline__ float half32_max(float v) {
+    v = row16_max(v);
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);  // rows 0<->1, 2<->3
+    return __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+}
+
+// Eight fp32 values (natural order) scaled by 2^-e -> eight fp16 in the
+// perm8 order (pairs j, j + 4), each rounded once.
+__device__ __forceinline__ u32x4 f32x8_to_f16x8_perm_scaled(const float* v, int e) {
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const f16x2 p = {(f16)__builtin_ldexpf(v[j], -e), (f16)__builtin_ldexpf(v[j + 4], -e)};
+        o[j] = __builtin_bit_cast(uint32_t, p);
+    }
+    return o;
+}
+
+// fp16 2^d for d <= 0 (0 below the smallest subnormal, 2^-24): the factor
+// that moves a row piece stored with exponent e_piece to the row's largest
+// exponent e_max, d = e_piece - e_max.  Multiplying fp16 values by it is
+// exact while the result stays normal; what falls below is under 2^-25 of
+// the row's largest value.
+__device__ __forceinline__ f16 pow2_f16(int d) {
+    return d < -24 ? (f16)0.0f : (f16)__builtin_ldexpf(1.0f, d);
 }
 
 // Raw buffer resource over an array of at most 2 GiB (no stride, bounds

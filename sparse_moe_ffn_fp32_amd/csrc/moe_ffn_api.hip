@@ -13,7 +13,8 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 // Byte offsets of every workspace region for T tokens.
 struct Layout {
-    size_t wr2, logits, idx, w, sgate, xh, cnt, offs, tiles, tile_count, perm, pos_of, h, hs, partial, total;
+    size_t wr2, er, shw, es, logits, idx, w, sgate, xh, ex, cnt, offs, tiles, tile_count, perm, pos_of, h, eh, hs, ehs,
+        partial, ep, total;
 };
 
 Layout layout(int64_t T) {
@@ -23,11 +24,15 @@ Layout layout(int64_t T) {
     Layout L{};
     size_t o = 0;
     L.wr2 = o;        o += up((size_t)2 * E * D * 2);
+    L.er = o;         o += up((size_t)E * 4);
+    L.shw = o;        o += up((size_t)(2 * FS * D + D * FS) * 2);
+    L.es = o;         o += up((size_t)(2 * FS + D) * 4);
     L.logits = o;     o += up((size_t)T * E * 4);
     L.idx = o;        o += up(N * 4);
     L.w = o;          o += up(N * 4);
     L.sgate = o;      o += up((size_t)T * 4);
     L.xh = o;         o += up((size_t)T * D * 2);
+    L.ex = o;         o += up((size_t)T * 4);
     L.cnt = o;        o += up((size_t)nblk * E * 4);
     L.offs = o;       o += up((E + 1) * 4);
     L.tiles = o;      o += up(max_tiles * 4 * 4);
@@ -35,8 +40,11 @@ Layout layout(int64_t T) {
     L.perm = o;       o += up(N * 4);
     L.pos_of = o;     o += up(N * 4);
     L.h = o;          o += up(N * F * 2);
+    L.eh = o;         o += up(N * 2 * 4);
     L.hs = o;         o += up((size_t)T * FS * 2);
+    L.ehs = o;        o += up((size_t)T * 4 * 4);
     L.partial = o;    o += up(N * D * 2);
+    L.ep = o;         o += up(N * 4 * 4);
     L.total = o;
     return L;
 }
@@ -138,18 +146,30 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     int32_t* perm = (int32_t*)at(L.perm);
     int32_t* pos_of = (int32_t*)at(L.pos_of);
 
+    int32_t* er = (int32_t*)at(L.er);
+    uint16_t* shw = sh ? (uint16_t*)at(L.shw) : nullptr;
+    int32_t* es = (int32_t*)at(L.es);
+    int32_t* xe = (int32_t*)at(L.ex);
+
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-    chk(launch_split_router(router->weight, wr2, s));
-    chk(launch_prep_x(x, xh, T, s));
-    chk(launch_router_gemm(xh, wr2, router->bias, logits, sh ? sh->gate : nullptr, sh ? sh->up : nullptr,
-                           (uint16_t*)at(L.hs), T, tr, s));
+    chk(launch_prep_weights(router->weight, wr2, er, sh ? sh->gate : nullptr, sh ? sh->up : nullptr,
+                            sh ? sh->down : nullptr, shw, es, s));
+    chk(launch_prep_x(x, xh, xe, T, s));
+    chk(launch_router_gemm(xh, xe, wr2, er, router->bias, logits, shw, es, (uint16_t*)at(L.hs), (int32_t*)at(L.ehs), T,
+                           tr, s));
     chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, weights_scale(router), router->gating, T, s));
     chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(T), s));
     PrefillGemmParams p{};
     p.xh = xh;
+    p.ex = xe;
+    p.shw = shw;
+    p.es = es;
     p.h = (uint16_t*)at(L.h);
+    p.eh = (int32_t*)at(L.eh);
     p.hs = (uint16_t*)at(L.hs);
+    p.ehs = (int32_t*)at(L.ehs);
+    p.ep = (int32_t*)at(L.ep);
     p.perm = perm;
     p.pos_of = pos_of;
     p.offs = offs;
@@ -162,9 +182,6 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     p.up_q = gu.uq;   p.up_s = gu.us;   p.up_b = gu.ub;
     p.gu_rows = gu.rows;
     p.down_q = ex->down.qweight; p.down_s = ex->down.scales; p.down_b = ex->down.biases;
-    p.sh_gate = sh ? sh->gate : nullptr;
-    p.sh_up = sh ? sh->up : nullptr;
-    p.sh_down = sh ? sh->down : nullptr;
     p.partial = (uint16_t*)at(L.partial);
     p.resid = resid;
     p.y = y;

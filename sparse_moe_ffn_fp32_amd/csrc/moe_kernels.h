@@ -24,7 +24,11 @@ struct Tracer {
 
 
 // ---- router (k_router.hip)
-hipError_t launch_split_router(const float* wr, uint16_t* wr2, hipStream_t s);
+// router fp32 -> fp16 hi/lo planes wr2 [2, E, D] with row exponents er [E];
+// shared bf16 (when sg != nullptr) -> fp16 shw [gate | up | down] with row
+// exponents es [2 FS + D]
+hipError_t launch_prep_weights(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
+                               const uint16_t* sd, uint16_t* shw, int32_t* es, hipStream_t s);
 // wscale multiplies every renormalised routing weight
 hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
                        float* sgate, float wscale, int gating, int T, hipStream_t s);
@@ -37,8 +41,14 @@ hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, i
 // ---- grouped GEMMs (k_gemm.hip)
 struct PrefillGemmParams {
     const uint16_t* xh;
+    const int32_t* ex;   // [T] exponents of the fp16 x rows
+    const uint16_t* shw; // shared expert fp16 [gate FS x D | up FS x D | down D x FS]
+    const int32_t* es;   // their row exponents [2 FS + D]
     uint16_t* h;
+    int32_t* eh;         // [N_assign, 2] exponents of h (per 256-feature half)
     uint16_t* hs;
+    int32_t* ehs;        // [T, 4] exponents of the shared h (per 128 features)
+    int32_t* ep;         // [N_assign, 4] exponents of the partials (per 512 outputs)
     const int32_t* perm;
     const int32_t* pos_of;
     const int32_t* offs;
@@ -50,18 +60,19 @@ struct PrefillGemmParams {
     const uint16_t *gate_s, *up_s, *down_s;
     const uint16_t *gate_b, *up_b, *down_b;
     int gu_rows;  // rows per expert in the gate/up arrays (F, or 2F for the fused layout)
-    const uint16_t *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
-    uint16_t* partial;  // fp16 [N_assign, D]
+    uint16_t* partial;  // fp16 [N_assign, D], times 2^-ep
     const uint16_t* resid;  // bf16 [T, D] added to y before its rounding, or nullptr
     uint16_t* y;
     int T;
 };
 int gemm_bm(int T);  // rows per routed tile for a prefill pass of T tokens
-hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int T, hipStream_t s);
-// router logits, and the shared expert's gate/up + SwiGLU into hs when sh_gate != nullptr
-hipError_t launch_router_gemm(const uint16_t* xh, const uint16_t* wr2, const float* bias, float* logits,
-                              const uint16_t* sh_gate, const uint16_t* sh_up, uint16_t* hs, int T, const Tracer& tr,
-                              hipStream_t s);
+// x bf16 [T, D] -> fp16 xh (perm8) with row exponents ex [T]
+hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int32_t* ex, int T, hipStream_t s);
+// router logits, and the shared expert's gate/up + SwiGLU into hs (ehs)
+// when shw != nullptr
+hipError_t launch_router_gemm(const uint16_t* xh, const int32_t* ex, const uint16_t* wr2, const int32_t* er,
+                              const float* bias, float* logits, const uint16_t* shw, const int32_t* es, uint16_t* hs,
+                              int32_t* ehs, int T, const Tracer& tr, hipStream_t s);
 hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hipStream_t s);
 // xn[T, D] bf16 = RMS-normalised h times w (k_norm.hip)
 hipError_t launch_rmsnorm(const uint16_t* h, const float* w, float eps, uint16_t* xn, int T, hipStream_t s);
