@@ -110,6 +110,37 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _check(t, name: str, dtypes, rows: Optional[int] = None, cols: Optional[int] = None):
+    """Refuse a torch tensor the kernels would misread: not on a GPU, not
+    contiguous, of another element type, or too small for `rows` x `cols`.
+    Objects that are not torch tensors (raw pointers) pass unchecked."""
+    if t is None:
+        return
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        return
+    if not isinstance(t, torch.Tensor):
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if rows is not None and cols is not None:
+        if t.dim() != 2 or t.shape[0] < rows or t.shape[1] != cols:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [>= {rows}, {cols}]")
+
+
+def _check_call(x, y, topk_idx, topk_weight, T: int, dims):
+    import torch
+    _check(x, "x", (torch.int16, torch.uint16, torch.bfloat16), T, dims.d_model)
+    _check(y, "y", (torch.int16, torch.uint16, torch.bfloat16), T, dims.d_model)
+    _check(topk_idx, "topk_idx", (torch.int32,), T, dims.top_k)
+    _check(topk_weight, "topk_weight", (torch.float32,), T, dims.top_k)
+
+
 @dataclass
 class DeviceLayer:
     """Device-resident weights of one layer (torch tensors; bf16 as int16 bits)."""
@@ -156,6 +187,15 @@ class DeviceLayer:
                            int(getattr(layer, "gating", 0)))
 
     def structs(self):
+        import torch
+        f32, i32, i16 = (torch.float32,), (torch.int32,), (torch.int16, torch.uint16, torch.bfloat16)
+        for name, t, dt in (("router_w", self.router_w, f32), ("router_b", self.router_b, f32),
+                            ("sh_gate_inp", self.sh_gate_inp, i16), ("sh_gate", self.sh_gate, i16),
+                            ("sh_up", self.sh_up, i16), ("sh_down", self.sh_down, i16)):
+            _check(t, name, dt)
+        for name, q in (("gate", self.gate), ("up", self.up), ("down", self.down)):
+            for part, t, dt in zip(("qweight", "scales", "biases"), q, (i32, i16, i16)):
+                _check(t, f"{name}.{part}", dt)
         r = Router(_ptr(self.router_w), _ptr(self.router_b), float(self.weights_scale), int(self.gating))
         ex = Experts(*(Q4Tensor(*(_ptr(a) for a in m)) for m in (self.gate, self.up, self.down)),
                      int(self.gate_up_fused))
@@ -187,6 +227,7 @@ def moe_ffn_forward_path(x, layer: DeviceLayer, y, workspace, topk_idx=None, top
     raises MoeFfnError on a non-zero status when check is True."""
     r, ex, sh = layer.structs()
     T = x.shape[0] if T is None else T
+    _check_call(x, y, topk_idx, topk_weight, T, dims)
     wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
     if workspace_bytes is not None:
         wsb = workspace_bytes
@@ -205,6 +246,7 @@ def moe_ffn_forward_traced(x, layer: DeviceLayer, y, workspace, topk_idx=None, t
     hipEvent_t handles as integers) bracketing one kernel of the call."""
     r, ex, sh = layer.structs()
     T = x.shape[0] if T is None else T
+    _check_call(x, y, topk_idx, topk_weight, T, dims)
     wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
     st = lib().moe_ffn_forward_traced(ctypes.byref(dims), T, _ptr(x), ctypes.byref(r), ctypes.byref(ex),
                                       ctypes.byref(sh) if sh is not None else None, _ptr(y), _ptr(topk_idx),
@@ -239,6 +281,8 @@ def moe_ffn_block_forward_traced(h, norm_weight, eps: float, layer: DeviceLayer,
     h, y bf16 bits [T, D] (y may be h), norm_weight fp32 [D]."""
     r, ex, sh = layer.structs()
     T = h.shape[0] if T is None else T
+    _check_call(h, y, topk_idx, topk_weight, T, dims)
+    _check(norm_weight, "norm_weight", (__import__("torch").float32,))
     wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
     st = lib().moe_ffn_block_forward_traced(ctypes.byref(dims), T, _ptr(h), _ptr(norm_weight), float(eps),
                                             ctypes.byref(r), ctypes.byref(ex),
@@ -256,6 +300,8 @@ def moe_ffn_block_forward(h, norm_weight, eps: float, layer: DeviceLayer, y, wor
     """moe_ffn_block_forward: the FFN sub-block with its boundary steps."""
     r, ex, sh = layer.structs()
     T = h.shape[0] if T is None else T
+    _check_call(h, y, topk_idx, topk_weight, T, dims)
+    _check(norm_weight, "norm_weight", (__import__("torch").float32,))
     wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
     st = lib().moe_ffn_block_forward(ctypes.byref(dims), T, _ptr(h), _ptr(norm_weight), float(eps), ctypes.byref(r),
                                      ctypes.byref(ex), ctypes.byref(sh) if sh is not None else None, _ptr(y),
@@ -263,3 +309,4 @@ def moe_ffn_block_forward(h, norm_weight, eps: float, layer: DeviceLayer, y, wor
     if check and st != MOE_FFN_OK:
         raise MoeFfnError(st, moe_ffn_status_string(st))
     return st
+

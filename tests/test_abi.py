@@ -192,3 +192,18 @@ def test_workspace_is_bounded_by_the_prefill_slice(L):
     assert moe.moe_ffn_workspace_size(1 << 20) == w
     assert moe.moe_ffn_workspace_size(chunk - 1) < w
     assert "#define MOE_FFN_PREFILL_CHUNK_T 32768" in open(HEADER).read()
+
+
+def test_binding_refuses_misshapen_tensors(L):
+    """The binding checks torch tensors before any call: a host tensor, a
+    strided view, another dtype or too few rows never reach the library."""
+    torch = pytest.importorskip("torch")
+    lay = _layer()
+    y = _Fake(0x30000000)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_ffn_forward(torch.zeros((4, 2048), dtype=torch.int16), lay, y, None)
+    bad = _layer()
+    bad.router_w = torch.zeros((256, 2048), dtype=torch.float32)
+    with pytest.raises(ValueError, match="router_w"):
+        moe.moe_ffn_forward(_Fake(0x20000000), bad, y, None, T=4)
+
