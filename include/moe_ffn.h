@@ -58,6 +58,7 @@ extern "C" {
 #define MOE_FFN_EALIGN (-3)       /* a pointer is not 16-byte aligned */
 #define MOE_FFN_EWORKSPACE (-4)   /* workspace NULL or smaller than moe_ffn_workspace_size */
 #define MOE_FFN_EHIP (-5)         /* a kernel launch failed (hipGetLastError) */
+#define MOE_FFN_ETOOBIG (-6)      /* T above MOE_FFN_NOALLOC_MAX_T in moe_ffn_forward_noalloc */
 
 /* execution paths (moe_ffn_forward_path) */
 /* Routing score (moe_ffn_router.gating). */
@@ -239,6 +240,32 @@ int moe_ffn_block_forward_traced(const moe_ffn_dims *dims, int64_t T, const uint
                                  const moe_ffn_shared *shared, uint16_t *y, int32_t *topk_idx, float *topk_weight,
                                  void *workspace, size_t workspace_bytes, void *stream, int path,
                                  const moe_ffn_trace *trace);
+
+/* ---- Entry point that allocates nothing.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * moe_ffn_forward for 1 <= T <= MOE_FFN_NOALLOC_MAX_T (always the decode
+ * path) without a workspace argument: its scratch is a static device array of
+ * MOE_FFN_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, which
+ * each GPU the library runs on holds until the process ends.  The array's
+ * device address is looked up once per device, on the first call made with
+ * that device current; make every call with the stream's device current.
+ * No call allocates or frees memory.
+ *
+ * T > MOE_FFN_NOALLOC_MAX_T returns MOE_FFN_ETOOBIG without launching; the
+ * other statuses are moe_ffn_forward's (there is no MOE_FFN_EWORKSPACE).
+ * Every call on one GPU uses that GPU's one scratch array: calls that may
+ * overlap in time on the same GPU (other streams, or host threads without
+ * ordering) race on it and must be ordered by the caller.  The scratch
+ * needs no clearing: a call writes every scratch element before it reads it,
+ * so what a previous call left there does not matter. */
+#define MOE_FFN_NOALLOC_MAX_T 64
+#define MOE_FFN_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+int moe_ffn_forward_noalloc(const moe_ffn_dims *dims, int64_t T, const uint16_t *x, const moe_ffn_router *router,
+                            const moe_ffn_experts *experts, const moe_ffn_shared *shared, uint16_t *y,
+                            int32_t *topk_idx, float *topk_weight, void *stream);
 
 /* Static string for a status code. */
 const char *moe_ffn_status_string(int status);

@@ -22,13 +22,15 @@ MOE_FFN_EUNSUPPORTED = -2
 MOE_FFN_EALIGN = -3
 MOE_FFN_EWORKSPACE = -4
 MOE_FFN_EHIP = -5
+MOE_FFN_ETOOBIG = -6
+NOALLOC_MAX_T = 64
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 GATING_SOFTMAX, GATING_SQRT_SOFTPLUS = 0, 1
 DECODE_MAX_T = 64
 
 EXPORTED = ("moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_path", "moe_ffn_forward_traced",
             "moe_ffn_block_workspace_size", "moe_ffn_block_forward", "moe_ffn_block_forward_traced",
-            "moe_ffn_status_string")
+            "moe_ffn_forward_noalloc", "moe_ffn_status_string")
 KERNEL_ROUTER, KERNEL_EXPERT_GU, KERNEL_EXPERT_DOWN, KERNEL_COMBINE = 1, 2, 3, 4
 
 
@@ -98,6 +100,8 @@ def lib(path: str = LIB_PATH):
         L.moe_ffn_block_forward.restype = ctypes.c_int
         L.moe_ffn_block_forward_traced.argtypes = blk + [ctypes.c_int, ctypes.POINTER(Trace)]
         L.moe_ffn_block_forward_traced.restype = ctypes.c_int
+        L.moe_ffn_forward_noalloc.argtypes = fwd[:9] + [vp]
+        L.moe_ffn_forward_noalloc.restype = ctypes.c_int
         L.moe_ffn_status_string.argtypes = [ctypes.c_int]
         L.moe_ffn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -310,3 +314,17 @@ def moe_ffn_block_forward(h, norm_weight, eps: float, layer: DeviceLayer, y, wor
         raise MoeFfnError(st, moe_ffn_status_string(st))
     return st
 
+
+def moe_ffn_forward_noalloc(x, layer: DeviceLayer, y, topk_idx=None, topk_weight=None, stream=None,
+                            dims: Dims = DIMS, T: Optional[int] = None, check: bool = True) -> int:
+    """moe_ffn_forward_noalloc: T <= NOALLOC_MAX_T tokens with the library's
+    own static device scratch (no workspace, no allocation anywhere)."""
+    r, ex, sh = layer.structs()
+    T = x.shape[0] if T is None else T
+    _check_call(x, y, topk_idx, topk_weight, T, dims)
+    st = lib().moe_ffn_forward_noalloc(ctypes.byref(dims), T, _ptr(x), ctypes.byref(r), ctypes.byref(ex),
+                                       ctypes.byref(sh) if sh is not None else None, _ptr(y), _ptr(topk_idx),
+                                       _ptr(topk_weight), _stream_ptr(stream))
+    if check and st != MOE_FFN_OK:
+        raise MoeFfnError(st, moe_ffn_status_string(st))
+    return st

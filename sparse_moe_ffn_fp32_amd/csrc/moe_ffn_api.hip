@@ -1,8 +1,16 @@
 // C-ABI entry points: argument validation, workspace carve-up, path choice,
 // launches on the caller's stream.  See include/moe_ffn.h for the contract.
+#include <atomic>
+#include <mutex>
+
 #include "../../include/moe_ffn.h"
 #include "moe_common.h"
 #include "moe_kernels.h"
+
+// Scratch of moe_ffn_forward_noalloc: one copy per GPU, alive until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in): the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[MOE_FFN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -90,9 +98,10 @@ GateUp resolve_gate_up(const moe_ffn_experts* ex) {
     return {g.qweight, u.qweight, g.scales, u.scales, g.biases, u.biases, F};
 }
 
-int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
-             const moe_ffn_experts* ex, const moe_ffn_shared* sh, uint16_t* y, int32_t* topk_idx,
-             float* topk_weight, void* ws, size_t ws_bytes, int path) {
+// Every argument check except the workspace's.
+int validate_args(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
+                  const moe_ffn_experts* ex, const moe_ffn_shared* sh, uint16_t* y, int32_t* topk_idx,
+                  float* topk_weight, int path) {
     if (!dims || T < 0 || path < MOE_FFN_PATH_AUTO || path > MOE_FFN_PATH_PREFILL) return MOE_FFN_EINVAL;
     if (!dims_ok(dims)) return MOE_FFN_EUNSUPPORTED;
     if (T > MOE_FFN_MAX_T) return MOE_FFN_EUNSUPPORTED;
@@ -111,10 +120,19 @@ int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_f
         if (!al16(p)) return MOE_FFN_EALIGN;
     const void* opt[] = {x, y, router->weight, router->bias, topk_idx, topk_weight,
                          sh ? sh->gate : nullptr, sh ? sh->up : nullptr, sh ? sh->down : nullptr,
-                         sh ? sh->gate_inp : nullptr, ws};
+                         sh ? sh->gate_inp : nullptr};
     for (const void* p : opt)
         if (p && !al16(p)) return MOE_FFN_EALIGN;
     if (path == MOE_FFN_PATH_DECODE && T > MOE_FFN_DECODE_MAX_T) return MOE_FFN_EUNSUPPORTED;
+    return MOE_FFN_OK;
+}
+
+int validate(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
+             const moe_ffn_experts* ex, const moe_ffn_shared* sh, uint16_t* y, int32_t* topk_idx,
+             float* topk_weight, void* ws, size_t ws_bytes, int path) {
+    const int st = validate_args(dims, T, x, router, ex, sh, y, topk_idx, topk_weight, path);
+    if (st != MOE_FFN_OK || T == 0) return st;
+    if (ws && !al16(ws)) return MOE_FFN_EALIGN;
     if (!ws || ws_bytes < workspace_bytes(T)) return MOE_FFN_EWORKSPACE;
     return MOE_FFN_OK;
 }
@@ -248,9 +266,45 @@ int forward_impl(int64_t T, const uint16_t* x, const float* norm_w, float eps, u
     return launch_decode(p, (char*)workspace, tr, stream) == hipSuccess ? MOE_FFN_OK : MOE_FFN_EHIP;
 }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept per device.
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return MOE_FFN_EHIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_FFN_EHIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MOE_FFN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int moe_ffn_forward_noalloc(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const moe_ffn_router* router,
+                            const moe_ffn_experts* experts, const moe_ffn_shared* shared, uint16_t* y,
+                            int32_t* topk_idx, float* topk_weight, void* stream) {
+    if (dims && dims_ok(dims) && T > MOE_FFN_NOALLOC_MAX_T && T <= MOE_FFN_MAX_T) return MOE_FFN_ETOOBIG;
+    int st = validate_args(dims, T, x, router, experts, shared, y, topk_idx, topk_weight, MOE_FFN_PATH_DECODE);
+    if (st != MOE_FFN_OK || T == 0) return st;
+    if (decode_workspace_bytes((int)T, nullptr) > MOE_FFN_NOALLOC_SCRATCH_BYTES) return MOE_FFN_ETOOBIG;
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != MOE_FFN_OK) return st;
+    return forward_impl(T, x, nullptr, 0.0f, nullptr, router, experts, shared, y, topk_idx, topk_weight, ws,
+                        (hipStream_t)stream, MOE_FFN_PATH_DECODE, nullptr);
+}
 
 size_t moe_ffn_workspace_size(const moe_ffn_dims* dims, int64_t T) {
     if (!dims || !dims_ok(dims) || T <= 0 || T > MOE_FFN_MAX_T) return 0;
@@ -320,6 +374,7 @@ const char* moe_ffn_status_string(int status) {
         case MOE_FFN_EALIGN: return "pointer not 16-byte aligned";
         case MOE_FFN_EWORKSPACE: return "workspace missing or too small";
         case MOE_FFN_EHIP: return "HIP launch error";
+        case MOE_FFN_ETOOBIG: return "token count above the no-allocation entry point's maximum";
         default: return "unknown status";
     }
 }

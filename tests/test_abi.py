@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert moe.moe_ffn_status_string(st)
     assert moe.moe_ffn_status_string(-99) == "unknown status"
 
@@ -202,8 +202,30 @@ def test_binding_refuses_misshapen_tensors(L):
     y = _Fake(0x30000000)
     with pytest.raises(ValueError, match="GPU tensor"):
         moe.moe_ffn_forward(torch.zeros((4, 2048), dtype=torch.int16), lay, y, None)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_ffn_forward_noalloc(torch.zeros((4, 2048), dtype=torch.int16), lay, y)
     bad = _layer()
     bad.router_w = torch.zeros((256, 2048), dtype=torch.float32)
     with pytest.raises(ValueError, match="router_w"):
         moe.moe_ffn_forward(_Fake(0x20000000), bad, y, None, T=4)
 
+
+def test_noalloc_rejects_before_launch(L):
+    """moe_ffn_forward_noalloc: T above its maximum is MOE_FFN_ETOOBIG, bad
+    arguments get moe_ffn_forward's statuses, T == 0 launches nothing."""
+    layer = _layer()
+    r, ex, sh = layer.structs()
+
+    def call(T, x=0x20000000, y=0x30000000, dims=moe.DIMS):
+        return L.moe_ffn_forward_noalloc(ctypes.byref(dims), T, x, ctypes.byref(r), ctypes.byref(ex),
+                                         ctypes.byref(sh), y, None, None, None)
+
+    assert call(0) == moe.MOE_FFN_OK
+    assert call(moe.NOALLOC_MAX_T + 1) == moe.MOE_FFN_ETOOBIG
+    assert call(4096) == moe.MOE_FFN_ETOOBIG
+    assert call(-1) == moe.MOE_FFN_EINVAL
+    assert call(4, x=None) == moe.MOE_FFN_EINVAL
+    assert call(4, x=0x20000008) == moe.MOE_FFN_EALIGN
+    assert call(4, dims=moe.Dims(2048, 256, 8, 512, 512, 32)) == moe.MOE_FFN_EUNSUPPORTED
+    assert moe.moe_ffn_status_string(moe.MOE_FFN_ETOOBIG) != "unknown status"
+    assert "#define MOE_FFN_NOALLOC_MAX_T 64" in open(HEADER).read()
