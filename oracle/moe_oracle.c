@@ -90,18 +90,32 @@ int moe_oracle_select(const double *logits, int64_t E, int64_t k, int32_t *sel, 
  * FFN"); 0 stands for the unscaled default 1. */
 static double weights_scale(const moe_oracle_layer *L) { return L->weights_scale == 0.0 ? 1.0 : L->weights_scale; }
 
+/* log(softplus(z)), softplus(z) = log(1 + e^z) written as max(z, 0) +
+ * log1p(e^-|z|) (the same value, no overflow).  Below z = -30, softplus(z)
+ * = e^z (1 - e^z / 2 + O(e^2z)), so its log is z + log1p(-e^z / 2) to
+ * double precision, with no underflow however negative z is. */
+static double log_softplus(double z) {
+    if (z > -30.0) return log(fmax(z, 0.0) + log1p(exp(-fabs(z))));
+    return z + log1p(-0.5 * exp(z));
+}
+
 /* sqrt-softplus gating (ds4.c notes Part 3, MoE trace 3, router
- * probabilities): score = sqrt(softplus(logit)), softplus(z) = log(1 + e^z)
- * written as max(z, 0) + log1p(e^-|z|) (the same value, no overflow).  The
- * score rises strictly with the logit, so the experts chosen by logit are
- * the experts chosen by score; their scores are renormalised to sum 1 (the
- * weight step is not printed for this router: the reading taken is the
- * renormalisation used with the softmax gate). */
+ * probabilities): score = sqrt(softplus(logit)).  The score rises strictly
+ * with the logit, so the experts chosen by logit are the experts chosen by
+ * score; their scores are renormalised to sum 1 (the weight step is not
+ * printed for this router: the reading taken is the renormalisation used
+ * with the softmax gate).  The ratio score_r / sum(score) is formed from
+ * log scores, 0.5 log softplus(z), relative to the largest: the same value,
+ * and defined where every score underflows (logits below about -1500). */
 static void sqrt_softplus_weights(const double *logits, const int32_t *sel, int64_t k, double *w) {
+    double mx = -INFINITY;
+    for (int64_t r = 0; r < k; r++) {
+        w[r] = 0.5 * log_softplus(logits[sel[r]]);
+        if (w[r] > mx) mx = w[r];
+    }
     double s = 0.0;
     for (int64_t r = 0; r < k; r++) {
-        const double z = logits[sel[r]];
-        w[r] = sqrt(fmax(z, 0.0) + log1p(exp(-fabs(z))));
+        w[r] = exp(w[r] - mx);
         s += w[r];
     }
     for (int64_t r = 0; r < k; r++) w[r] /= s;

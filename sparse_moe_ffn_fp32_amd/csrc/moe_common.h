@@ -344,14 +344,17 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// Routing score of a selected logit v relative to the top one v0, before
-// the renormalisation over the top k: softmax exp(v - v0) (the full-softmax
+// Routing score of a selected logit v given the top one v0, before the
+// renormalisation over the top k: softmax exp(v - v0) (the full-softmax
 // normaliser cancels), or sqrt(softplus(v)), softplus computed stably
-// (log1p(e^v); v beyond +-20 is v or e^v to fp32 precision).
+// (log1p(e^v); v beyond +-20 is v or e^v to fp32 precision, and sqrt(e^v)
+// is e^(v/2)).  When even the top logit is below -20, every selected score
+// is e^(v/2) and the common factor e^(v0/2) cancels in the renormalisation:
+// the scores are taken as e^((v - v0)/2), which no logit underflows.
 __device__ __forceinline__ float route_score(float v, float v0, int gating) {
     if (gating == 0) return __expf(v - v0);
-    const float sp = v > 20.0f ? v : (v < -20.0f ? __expf(v) : log1pf(__expf(v)));
-    return __builtin_sqrtf(sp);
+    if (v < -20.0f) return __expf(0.5f * (v0 < -20.0f ? v - v0 : v));
+    return __builtin_sqrtf(v > 20.0f ? v : log1pf(__expf(v)));
 }
 
 // Sum over the 64 lanes of a wave, the same value in every lane: row sums,

@@ -435,4 +435,31 @@ def pin_sqrt_softplus_gating(O):
     assert abs(O.forward(lay2, x2, nthreads=1)["w"].sum(axis=1) - 1.0).max() <= 1e-14
 
 
+def pin_sqrt_softplus_extremes(O):
+    """sqrt(softplus) scores where they are closed forms: a logit of 0 has
+    softplus ln 2, logits <= -40 have softplus e^z (to double precision), so
+    logits 0, -40, -42, -44 weigh sqrt(ln 2) e^20 : 1 : e^-1 : e^-2; and
+    logits -1000, -1002, -1004, -1006 (every score far below the smallest
+    double) still weigh 1 : e^-1 : e^-2 : e^-3, each normalised to sum 1."""
+    lay = tiny_layer(shared=False)
+    E = lay.dims.n_experts
+    lay.router_w = np.zeros_like(lay.router_w)
+    lay.gating = 1
+    x = tiny_x(seed=5, T=2)
+    bias = np.full(E, -5000.0, dtype=np.float32)
+    bias[[4, 7, 1, 12]] = [0.0, -40.0, -42.0, -44.0]
+    lay.router_b = bias
+    r = O.route(lay, x)
+    assert np.array_equal(r["idx"], np.tile([4, 7, 1, 12], (2, 1)))
+    raw = np.array([np.sqrt(np.log(2.0)) * np.exp(20.0), 1.0, np.exp(-1.0), np.exp(-2.0)])
+    assert np.abs(r["w"] - raw / raw.sum()).max() <= 1e-15
+    bias = np.full(E, -5000.0, dtype=np.float32)
+    bias[[3, 9, 0, 6]] = [-1000.0, -1002.0, -1004.0, -1006.0]
+    lay.router_b = bias
+    r = O.route(lay, x)
+    assert np.array_equal(r["idx"], np.tile([3, 9, 0, 6], (2, 1)))
+    raw = np.exp(-np.arange(4.0))
+    assert np.isfinite(r["w"]).all() and np.abs(r["w"] - raw / raw.sum()).max() <= 1e-15
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -141,6 +141,8 @@ def test_block_zero_ffn_returns_h(gpu, norm_w, T):
     _say(f"block zero FFN T={T}")
     y = run_block(gpu, lay, h, norm_w)[0]
     assert np.array_equal(y, h)
+    ref = oracle.get().block_forward(lay, h, norm_w, EPS)["y"]  # h + 0, exact in fp64
+    assert np.array_equal(bf16_to_f64(y), ref)
 
 
 def test_block_prefill_in_slices(gpu, layer0, norm_w):

@@ -122,12 +122,14 @@ def test_weights_scale(gpu, layer0, T, path):
 
 @pytest.mark.parametrize("T,path,offset", [(1, "auto", 0.0), (4, "auto", 0.0), (37, "decode", 0.0),
                                            (37, "prefill", 0.0), (300, "auto", 0.0), (4, "auto", 25.0),
-                                           (300, "auto", -25.0)])
+                                           (300, "auto", -25.0), (1, "auto", -150.0), (37, "decode", -150.0),
+                                           (300, "auto", -600.0)])
 def test_sqrt_softplus_gating(gpu, layer0, T, path, offset):
     """sqrt(softplus(logit)) scores (ds4.c study notes Part 3, MoE trace 3):
     the same experts as the softmax gate, weights and y against the oracle;
     a constant router-bias offset of +-25 moves every logit into the large
-    and small softplus branches."""
+    and small softplus branches, offsets of -150 and -600 put every selected
+    score below the fp32 (and, at -600, near the fp64) underflow."""
     import copy
     import sparse_moe_ffn_fp32_amd as moe
     from gpu_common import W_ABS

@@ -25,8 +25,12 @@ MUTANTS = [
     ("group_bias_index", "float b = moe_oracle_bf16_to_f32(bi[i / group]);",
      "float b = moe_oracle_bf16_to_f32(bi[(i / group + 1) % groups]);"),
     ("router_no_bias", "if (L->router_b) acc += (double)L->router_b[e];", ""),
-    ("softplus_no_sqrt", "w[r] = sqrt(fmax(z, 0.0) + log1p(exp(-fabs(z))));", "w[r] = fmax(z, 0.0) + log1p(exp(-fabs(z)));"),
-    ("softplus_relu", "w[r] = sqrt(fmax(z, 0.0) + log1p(exp(-fabs(z))));", "w[r] = sqrt(fmax(z, 0.0) + 1e-300);"),
+    ("softplus_no_sqrt", "w[r] = 0.5 * log_softplus(logits[sel[r]]);", "w[r] = log_softplus(logits[sel[r]]);"),
+    ("softplus_relu", "if (z > -30.0) return log(fmax(z, 0.0) + log1p(exp(-fabs(z))));",
+     "if (z > -30.0) return log(fmax(z, 0.0) + 1e-300);"),
+    ("softplus_tail_sign", "return z + log1p(-0.5 * exp(z));", "return -z + log1p(-0.5 * exp(z));"),
+    ("softplus_underflows", "w[r] = 0.5 * log_softplus(logits[sel[r]]);",
+     "w[r] = 0.5 * log(fmax(logits[sel[r]], 0.0) + log1p(exp(-fabs(logits[sel[r]]))));"),
     ("softplus_not_renormalised", "for (int64_t r = 0; r < k; r++) w[r] /= s;", ";"),
     ("gating_ignored", "if (j->L->gating == 1) sqrt_softplus_weights(lg, sel, k, ww);", ";"),
     ("weights_scale_ignored", "ww[r] *= weights_scale(j->L);", "ww[r] *= 1.0;"),
