@@ -82,6 +82,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_cpus():
+    """CPUs this process may run on (the affinity mask), and nproc's view."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    return avail, os.cpu_count() or 1
+
+
+def cpu_threads():
+    """Threads of the CPU baseline: every CPU the process may use, at most 16
+    (the host share of one GPU on the measurement machines)."""
+    return max(1, min(16, host_cpus()[0]))
+
+
 class Hip:
     """hipEvent_t handles through the HIP runtime's C API."""
 
@@ -160,7 +175,8 @@ def main():
         del src, dst
 
     # ---------------------------------------------------------------- inputs
-    n_cpu_layers = min(nlayers, 8)
+    # the CPU baseline runs one sampled layer per host thread
+    n_cpu_layers = min(nlayers, cpu_threads())
     host_layers, dev_layers, xs, nws = [], [], [], []
     EPS = float(np.float32(1e-6))
     t0 = time.time()
@@ -200,6 +216,8 @@ def main():
 
     dom_kernel = moe.KERNEL_EXPERT_GU
 
+    last_step_ms = []  # per-call ms of the last single-layer run
+
     def run_steps_eager(nsteps, kernel=None):
         """nsteps steps launched directly; returns (wall seconds, per-launch ms of `kernel`)."""
         ev = [(hip.event(), hip.event()) for _ in range(nsteps * nlayers)] if kernel is not None else []
@@ -228,6 +246,7 @@ def main():
                 step_ms.append(hip.elapsed_ms(se, ee))
             hip.destroy(se)
             hip.destroy(ee)
+            last_step_ms[:] = step_ms
             wall = float(np.median(step_ms)) * 1e-3 * nsteps
         kms = [hip.elapsed_ms(a, b) for a, b in ev]
         for a, b in ev:
@@ -253,6 +272,28 @@ def main():
         wall = time.perf_counter() - t
         del g
         return wall
+
+    def step_times_graph(nsteps):
+        """Per-step ms of nsteps replays of a one-step graph, each between two
+        events on the replay stream (for the spread of the step time)."""
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=cap):
+            for l in range(nlayers):
+                call(l, strm=cap)
+        torch.cuda.synchronize()
+        out = []
+        a, b = hip.event(), hip.event()
+        for _ in range(nsteps):
+            hip.record(a, stream)
+            g.replay()
+            hip.record(b, stream)
+            out.append(hip.elapsed_ms(a, b))
+        hip.destroy(a)
+        hip.destroy(b)
+        del g
+        return out
 
     def kernel_times(nsteps, kernel):
         """Per-launch ms of `kernel` over nsteps steps, from HIP events that the
@@ -287,6 +328,12 @@ def main():
 
     log(f"timing {args.steps} steps")
     wall = run_steps(args.steps)
+    if flush_buf is None and not args.eager:
+        step_ms = step_times_graph(args.steps)
+    elif flush_buf is not None:
+        step_ms = list(last_step_ms)
+    else:
+        step_ms = []
     kms = kernel_times(args.steps, dom_kernel)
     ms_per_step = 1000.0 * wall / args.steps
     tokens_per_step = T  # one step pushes T tokens through all `nlayers` layers
@@ -337,7 +384,8 @@ def main():
 
         import oracle
         O = oracle.get()
-        cores = max(1, min(16, os.cpu_count() or 1))
+        cores = cpu_threads()
+        avail, nproc = host_cpus()
         if nlayers > 1:
             threads = min(cores, len(host_layers))
             done, t = 0, time.perf_counter()
@@ -348,6 +396,7 @@ def main():
                     done += len(host_layers)
             el = time.perf_counter() - t
             cpu = dict(value=round((done / nlayers) * T / el, 3), unit="tokens/s", cores=threads, kind="oracle",
+                       nproc=nproc, cpus_available=avail,
                        sample=f"{len(host_layers)} of the {nlayers} layers at T={T}, {done} layer calls in "
                               f"{el:.1f}s, one layer per thread; tokens/s scaled to the {nlayers}-layer step")
         else:
@@ -366,7 +415,7 @@ def main():
                 passes += 1
             el = time.perf_counter() - t
             cpu = dict(value=round(done / el, 2), unit="tokens/s", cores=min(cores, (T + stride - 1) // stride),
-                       kind="oracle",
+                       kind="oracle", nproc=nproc, cpus_available=avail,
                        sample=f"{passes} passes over strided slices of {T} tokens (every {stride}th token, "
                               f"offset advancing per pass), {done} tokens in {el:.1f}s")
         log(f"oracle: {cpu}")
@@ -382,7 +431,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        # operand type of the expert contractions (fp32 accumulation): the
+        # decode kernels take bf16 activations and exact bf16 codes 128 + q,
+        # the prefill GEMMs row-scaled fp16 on MFMA
+        "dtype": "bf16" if (T <= 64 and args.path != 2) else "f16",
         "data": "synthetic",
         "config": {"workload": args.workload + ("+block" if args.block else ""), "T": T, "layers": nlayers,
                    "router_bias_zipf_s": wl["zipf"], "distinct_experts_per_layer": float(np.mean(distinct)),
@@ -390,6 +442,12 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if step_ms:
+        q = np.nanpercentile(np.array(step_ms) * 1e3, [10, 50, 90])
+        out["step_us"] = {"p10": round(float(q[0]), 2), "p50": round(float(q[1]), 2), "p90": round(float(q[2]), 2),
+                          "n": len(step_ms),
+                          "how": "one-step graph replays between events" if nlayers > 1 else
+                                 "per call between events, caches evicted before each"}
     print(json.dumps(out), flush=True)
 
 

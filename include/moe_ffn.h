@@ -138,6 +138,22 @@ typedef struct {
      * softmax probabilities), times weights_scale.  Other values are
      * MOE_FFN_EINVAL. */
     int32_t gating;
+    /* Hash routing (ds4.c study notes Part 3, MoE trace 3, hash table
+     * routing: selected[i] = table[i * n_vocab + token]).  tid2eid: int32
+     * [top_k, n_vocab], or NULL (the zero-initialised default) for routing by
+     * logit.  With a table, token t's experts are tid2eid[r * n_vocab +
+     * token_ids[t]] for r = 0 .. top_k - 1, in that order (a repeated entry
+     * is used once per rank), instead of the top_k by logit; their weights
+     * are the gating's scores of those experts renormalised to sum 1, times
+     * weights_scale (the router logits are still computed for them).
+     * token_ids: int32 [T], the call's token ids, required with a table.
+     * n_vocab >= 1 with a table.  Entries must lie in [0, n_experts) and ids
+     * in [0, n_vocab); values outside are clamped into those ranges (never
+     * read out of bounds) and give an unspecified choice of experts.  A
+     * table without token ids, or n_vocab < 1, is MOE_FFN_EINVAL. */
+    const int32_t *tid2eid;
+    const int32_t *token_ids;
+    int32_t n_vocab;
 } moe_ffn_router;
 
 /* Shared expert, bf16: gate, up [d_ff_shared, d_model]; down [d_model,
@@ -161,7 +177,8 @@ size_t moe_ffn_workspace_size(const moe_ffn_dims *dims, int64_t T);
  * router, experts: required.  shared: NULL means no shared expert (y =
  * moe_out).  topk_idx int32 [T, top_k] and topk_weight fp32 [T, top_k]:
  * optional outputs (NULL to skip): the selected experts in descending logit
- * order (ties to the lower index) and their renormalised softmax weights.
+ * order (ties to the lower index; table order with hash routing) and their
+ * renormalised weights.
  * Routing uses fp32 logits.  y is rounded once, to nearest even.
  * T == 0 returns MOE_FFN_OK without launching anything. */
 int moe_ffn_forward(const moe_ffn_dims *dims, int64_t T, const uint16_t *x, const moe_ffn_router *router,

@@ -42,7 +42,8 @@ class _Layer(ctypes.Structure):
                 ("gate", _Q4), ("up", _Q4), ("down", _Q4),
                 ("sh_gate_inp", ctypes.c_void_p), ("sh_gate", ctypes.c_void_p),
                 ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p), ("weights_scale", ctypes.c_double),
-                ("gating", ctypes.c_int32)]
+                ("gating", ctypes.c_int32), ("tid2eid", ctypes.c_void_p), ("n_vocab", ctypes.c_int64),
+                ("token_ids", ctypes.c_void_p)]
 
 
 def _ptr(a):
@@ -97,10 +98,17 @@ class Oracle:
     def _q4(q) -> _Q4:
         return _Q4(_ptr(q.qweight), _ptr(q.scales), _ptr(q.biases))
 
-    def _layer(self, lay) -> _Layer:
+    def _layer(self, lay, token_ids=None) -> _Layer:
+        """The layer struct; with a hash table (lay.tid2eid, int32 [k,
+        n_vocab]) the call's token ids (int32 [T]) are required."""
+        tab = getattr(lay, "tid2eid", None)
+        if tab is not None:
+            assert tab.dtype == np.int32 and tab.ndim == 2 and tab.shape[0] == lay.dims.top_k
+            assert token_ids is not None and token_ids.dtype == np.int32, "hash routing needs the token ids"
         return _Layer(_ptr(lay.router_w), _ptr(lay.router_b), self._q4(lay.gate), self._q4(lay.up),
                       self._q4(lay.down), _ptr(lay.sh_gate_inp), _ptr(lay.sh_gate), _ptr(lay.sh_up),
-                      _ptr(lay.sh_down), float(lay.weights_scale), int(lay.gating))
+                      _ptr(lay.sh_down), float(lay.weights_scale), int(lay.gating), _ptr(tab),
+                      0 if tab is None else tab.shape[1], _ptr(token_ids) if tab is not None else None)
 
     # ----------------------------------------------------------------- steps
     def bf16_to_f32(self, bits: int) -> float:
@@ -145,7 +153,7 @@ class Oracle:
                                  sg.ctypes.data)
         return out, float(sg[0])
 
-    def forward(self, lay, x: np.ndarray, tokens=None, nthreads=None, want_logits=False) -> dict:
+    def forward(self, lay, x: np.ndarray, tokens=None, nthreads=None, want_logits=False, token_ids=None) -> dict:
         x = np.ascontiguousarray(x, dtype=np.uint16)
         T, D = x.shape
         assert D == lay.dims.d_model
@@ -157,7 +165,8 @@ class Oracle:
         w = np.empty((n, k), dtype=np.float64)
         margin = np.empty(n, dtype=np.float64)
         logits = np.empty((n, E), dtype=np.float64) if want_logits else None
-        d, l = self._dims(lay.dims), self._layer(lay)
+        tid = None if token_ids is None else np.ascontiguousarray(token_ids, dtype=np.int32)
+        d, l = self._dims(lay.dims), self._layer(lay, tid)
         st = self.L.moe_oracle_forward(ctypes.byref(d), ctypes.byref(l), T, x.ctypes.data,
                                        None if tok is None else tok.ctypes.data, n, y.ctypes.data,
                                        idx.ctypes.data, w.ctypes.data, margin.ctypes.data,
@@ -181,7 +190,7 @@ class Oracle:
         return out
 
     def block_forward(self, lay, h: np.ndarray, norm_w: np.ndarray, eps: float, tokens=None, nthreads=None,
-                      want_logits=False) -> dict:
+                      want_logits=False, token_ids=None) -> dict:
         """y = h + FFN(RMSNorm(h) * norm_w) in double; also the bf16 rows xn."""
         h = np.ascontiguousarray(h, dtype=np.uint16)
         nw = np.ascontiguousarray(norm_w, dtype=np.float32)
@@ -196,7 +205,8 @@ class Oracle:
         w = np.empty((n, k), dtype=np.float64)
         margin = np.empty(n, dtype=np.float64)
         logits = np.empty((n, E), dtype=np.float64) if want_logits else None
-        d, l = self._dims(lay.dims), self._layer(lay)
+        tid = None if token_ids is None else np.ascontiguousarray(token_ids, dtype=np.int32)
+        d, l = self._dims(lay.dims), self._layer(lay, tid)
         st = self.L.moe_oracle_block_forward(ctypes.byref(d), ctypes.byref(l), T, h.ctypes.data, nw.ctypes.data,
                                              float(eps), None if tok is None else tok.ctypes.data, n,
                                              xn.ctypes.data, y.ctypes.data, idx.ctypes.data, w.ctypes.data,
@@ -209,7 +219,7 @@ class Oracle:
             out["logits"] = logits
         return out
 
-    def route(self, lay, x: np.ndarray, tokens=None, nthreads=None, want_logits=False) -> dict:
+    def route(self, lay, x: np.ndarray, tokens=None, nthreads=None, want_logits=False, token_ids=None) -> dict:
         x = np.ascontiguousarray(x, dtype=np.uint16)
         T, D = x.shape
         tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
@@ -219,7 +229,8 @@ class Oracle:
         w = np.empty((n, k), dtype=np.float64)
         margin = np.empty(n, dtype=np.float64)
         logits = np.empty((n, E), dtype=np.float64) if want_logits else None
-        d, l = self._dims(lay.dims), self._layer(lay)
+        tid = None if token_ids is None else np.ascontiguousarray(token_ids, dtype=np.int32)
+        d, l = self._dims(lay.dims), self._layer(lay, tid)
         st = self.L.moe_oracle_route(ctypes.byref(d), ctypes.byref(l), T, x.ctypes.data,
                                      None if tok is None else tok.ctypes.data, n, idx.ctypes.data, w.ctypes.data,
                                      margin.ctypes.data, None if logits is None else logits.ctypes.data,

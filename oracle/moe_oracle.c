@@ -121,6 +121,41 @@ static void sqrt_softplus_weights(const double *logits, const int32_t *sel, int6
     for (int64_t r = 0; r < k; r++) w[r] /= s;
 }
 
+/* Softmax over all E logits, then the probabilities of the k listed
+ * experts renormalised to sum 1 (norm_topk_prob): the weights of experts
+ * chosen by a table rather than by their logits. */
+static void softmax_weights(const double *logits, int64_t E, const int32_t *sel, int64_t k, double *w) {
+    double top = logits[0];
+    for (int64_t e = 1; e < E; e++)
+        if (logits[e] > top) top = logits[e];
+    double norm = 0.0;
+    for (int64_t e = 0; e < E; e++) norm += exp(logits[e] - top);
+    double chosen = 0.0;
+    for (int64_t r = 0; r < k; r++) chosen += exp(logits[sel[r]] - top) / norm;
+    for (int64_t r = 0; r < k; r++) w[r] = (exp(logits[sel[r]] - top) / norm) / chosen;
+}
+
+/* The routing of token t from its logits: the experts (by logit, or by the
+ * hash table: ds4.c notes Part 3, MoE trace 3 looks them up as
+ * table[r * n_vocab + token]), their renormalised weights under the layer's
+ * gating, times expert_weights_scale; margin as moe_oracle_select's (+inf
+ * for table routing, whose choice does not depend on the logits). */
+static int route_token(const moe_oracle_dims *d, const moe_oracle_layer *L, int64_t t, const double *lg, int32_t *sel,
+                       double *ww, double *mg) {
+    const int64_t E = d->n_experts, k = d->top_k;
+    int st = MOE_ORACLE_OK;
+    if (L->tid2eid) {
+        for (int64_t r = 0; r < k; r++) sel[r] = L->tid2eid[r * L->n_vocab + L->token_ids[t]];
+        softmax_weights(lg, E, sel, k, ww);
+        *mg = INFINITY;
+    } else {
+        st = moe_oracle_select(lg, E, k, sel, ww, mg);
+    }
+    if (L->gating == 1) sqrt_softplus_weights(lg, sel, k, ww);
+    for (int64_t r = 0; r < k; r++) ww[r] *= weights_scale(L);
+    return st;
+}
+
 /* silu(z) = z * sigmoid(z) (ds4.c notes Part 3, MoE trace 1). */
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
@@ -180,6 +215,18 @@ void moe_oracle_shared(const moe_oracle_dims *d, const moe_oracle_layer *L, cons
     free(h);
 }
 
+/* A hash table with its token ids, every entry an expert and every id a
+ * column of the table (or no table). */
+static int hash_table_ok(const moe_oracle_dims *d, const moe_oracle_layer *L, int64_t T) {
+    if (!L->tid2eid) return 1;
+    if (!L->token_ids || L->n_vocab < 1) return 0;
+    for (int64_t i = 0; i < d->top_k * L->n_vocab; i++)
+        if (L->tid2eid[i] < 0 || L->tid2eid[i] >= d->n_experts) return 0;
+    for (int64_t t = 0; t < T; t++)
+        if (L->token_ids[t] < 0 || L->token_ids[t] >= L->n_vocab) return 0;
+    return 1;
+}
+
 /* ------------------------------------------------------------- forward */
 typedef struct {
     const moe_oracle_dims *d;
@@ -207,9 +254,7 @@ static int forward_one(const fwd_job *j, int64_t n) {
     if (st == MOE_ORACLE_OK) {
         for (int64_t i = 0; i < D; i++) xd[i] = (double)moe_oracle_bf16_to_f32(xr[i]);
         moe_oracle_router_logits(d, j->L, xr, lg);
-        st = moe_oracle_select(lg, E, k, sel, ww, &mg);
-        if (j->L->gating == 1) sqrt_softplus_weights(lg, sel, k, ww);
-        for (int64_t r = 0; r < k; r++) ww[r] *= weights_scale(j->L);
+        st = route_token(d, j->L, t, lg, sel, ww, &mg);
     }
     if (st == MOE_ORACLE_OK) {
         double *yr = j->y + n * D;
@@ -257,6 +302,7 @@ int moe_oracle_forward(const moe_oracle_dims *d, const moe_oracle_layer *L, int6
     if (tokens)
         for (int64_t n = 0; n < n_tok; n++)
             if (tokens[n] < 0 || tokens[n] >= T) return MOE_ORACLE_EINVAL;
+    if (!hash_table_ok(d, L, T)) return MOE_ORACLE_EINVAL;
     if (n_tok == 0) return MOE_ORACLE_OK;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
@@ -303,9 +349,7 @@ static void *route_range(void *p) {
         const int64_t t = j->tokens ? j->tokens[n] : n;
         double mg = 0.0;
         moe_oracle_router_logits(j->d, j->L, j->x + t * D, lg);
-        j->status = moe_oracle_select(lg, E, k, sel, ww, &mg);
-        if (j->L->gating == 1) sqrt_softplus_weights(lg, sel, k, ww);
-        for (int64_t r = 0; r < k; r++) ww[r] *= weights_scale(j->L);
+        j->status = route_token(j->d, j->L, t, lg, sel, ww, &mg);
         if (j->idx) for (int64_t r = 0; r < k; r++) j->idx[n * k + r] = sel[r];
         if (j->w) for (int64_t r = 0; r < k; r++) j->w[n * k + r] = ww[r];
         if (j->margin) j->margin[n] = mg;
@@ -324,6 +368,7 @@ int moe_oracle_route(const moe_oracle_dims *d, const moe_oracle_layer *L, int64_
     if (tokens)
         for (int64_t n = 0; n < n_tok; n++)
             if (tokens[n] < 0 || tokens[n] >= T) return MOE_ORACLE_EINVAL;
+    if (!hash_table_ok(d, L, T)) return MOE_ORACLE_EINVAL;
     if (n_tok == 0) return MOE_ORACLE_OK;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;

@@ -69,6 +69,15 @@ typedef struct {
     const uint16_t *sh_down;      /* bf16 [D, Fs] */
     double weights_scale;         /* expert_weights_scale; 0 is read as 1 */
     int32_t gating;               /* 0: softmax; 1: sqrt(softplus(logit)) scores */
+    /* hash routing (ds4.c study notes Part 3, MoE trace 3, hash table
+     * routing): when tid2eid != NULL, token t's experts are
+     * tid2eid[r * n_vocab + token_ids[t]], r < top_k, in that order, instead
+     * of the top_k by logit; the weights are the gating's scores of those
+     * experts renormalised (reading: the same step as after a top-k).
+     * Entries must lie in [0, n_experts) and ids in [0, n_vocab). */
+    const int32_t *tid2eid;       /* [top_k, n_vocab] or NULL */
+    int64_t n_vocab;
+    const int32_t *token_ids;     /* [T], the call's token ids (with tid2eid) */
 } moe_oracle_layer;
 
 enum { MOE_ORACLE_OK = 0, MOE_ORACLE_EINVAL = -1, MOE_ORACLE_ENOMEM = -2 };

@@ -14,7 +14,8 @@ from dataclasses import dataclass
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
+# the in-tree build; MOE_FFN_LIB names another build of the same library
+LIB_PATH = os.environ.get("MOE_FFN_LIB") or os.path.join(HERE, "libmoe_ffn.so")
 
 MOE_FFN_OK = 0
 MOE_FFN_EINVAL = -1
@@ -52,7 +53,8 @@ class Experts(ctypes.Structure):
 
 class Router(ctypes.Structure):
     _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("weights_scale", ctypes.c_float),
-                ("gating", ctypes.c_int32)]
+                ("gating", ctypes.c_int32), ("tid2eid", ctypes.c_void_p), ("token_ids", ctypes.c_void_p),
+                ("n_vocab", ctypes.c_int32)]
 
 
 class Shared(ctypes.Structure):
@@ -160,6 +162,7 @@ class DeviceLayer:
     gate_up_fused: bool = False  # gate holds one [E, 2F, ...] tensor, up is empty
     weights_scale: float = 1.0   # expert_weights_scale (0 is read as 1)
     gating: int = 0              # GATING_SOFTMAX or GATING_SQRT_SOFTPLUS
+    tid2eid: object = None       # hash routing table, int32 [top_k, n_vocab], or None
 
     @staticmethod
     def from_host(layer, device="cuda", fused: bool = False) -> "DeviceLayer":
@@ -188,9 +191,11 @@ class DeviceLayer:
         return DeviceLayer(t(layer.router_w, np.float32), t(layer.router_b, np.float32), gate, up, q(layer.down),
                            t(layer.sh_gate_inp, np.int16), t(layer.sh_gate, np.int16), t(layer.sh_up, np.int16),
                            t(layer.sh_down, np.int16), fused, float(getattr(layer, "weights_scale", 1.0)),
-                           int(getattr(layer, "gating", 0)))
+                           int(getattr(layer, "gating", 0)), t(getattr(layer, "tid2eid", None), np.int32))
 
-    def structs(self):
+    def structs(self, token_ids=None):
+        """The C structs; token_ids (int32 [T] on the GPU) are the call's,
+        required with a hash table."""
         import torch
         f32, i32, i16 = (torch.float32,), (torch.int32,), (torch.int16, torch.uint16, torch.bfloat16)
         for name, t, dt in (("router_w", self.router_w, f32), ("router_b", self.router_b, f32),
@@ -200,7 +205,13 @@ class DeviceLayer:
         for name, q in (("gate", self.gate), ("up", self.up), ("down", self.down)):
             for part, t, dt in zip(("qweight", "scales", "biases"), q, (i32, i16, i16)):
                 _check(t, f"{name}.{part}", dt)
-        r = Router(_ptr(self.router_w), _ptr(self.router_b), float(self.weights_scale), int(self.gating))
+        _check(self.tid2eid, "tid2eid", i32)
+        _check(token_ids, "token_ids", i32)
+        if self.tid2eid is not None and token_ids is None:
+            raise ValueError("hash routing needs the call's token_ids")
+        n_vocab = int(self.tid2eid.shape[1]) if self.tid2eid is not None else 0
+        r = Router(_ptr(self.router_w), _ptr(self.router_b), float(self.weights_scale), int(self.gating),
+                   _ptr(self.tid2eid), _ptr(token_ids) if self.tid2eid is not None else None, n_vocab)
         ex = Experts(*(Q4Tensor(*(_ptr(a) for a in m)) for m in (self.gate, self.up, self.down)),
                      int(self.gate_up_fused))
         sh = None
@@ -225,11 +236,11 @@ def _stream_ptr(stream):
 
 def moe_ffn_forward_path(x, layer: DeviceLayer, y, workspace, topk_idx=None, topk_weight=None, stream=None,
                          path: int = PATH_AUTO, dims: Dims = DIMS, T: Optional[int] = None,
-                         workspace_bytes: Optional[int] = None, check: bool = True) -> int:
+                         workspace_bytes: Optional[int] = None, check: bool = True, token_ids=None) -> int:
     """Enqueue one FFN call on `stream` (default: torch's current stream).
     x, y: int16 tensors [T, d_model] holding bf16 bits.  Returns the status;
     raises MoeFfnError on a non-zero status when check is True."""
-    r, ex, sh = layer.structs()
+    r, ex, sh = layer.structs(token_ids)
     T = x.shape[0] if T is None else T
     _check_call(x, y, topk_idx, topk_weight, T, dims)
     wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
@@ -245,10 +256,10 @@ def moe_ffn_forward_path(x, layer: DeviceLayer, y, workspace, topk_idx=None, top
 
 def moe_ffn_forward_traced(x, layer: DeviceLayer, y, workspace, topk_idx=None, topk_weight=None, stream=None,
                            path: int = PATH_AUTO, trace: Optional[Trace] = None, dims: Dims = DIMS,
-                           T: Optional[int] = None, check: bool = True) -> int:
+                           T: Optional[int] = None, check: bool = True, token_ids=None) -> int:
     """moe_ffn_forward_path plus an optional Trace (kernel id and two
     hipEvent_t handles as integers) bracketing one kernel of the call."""
-    r, ex, sh = layer.structs()
+    r, ex, sh = layer.structs(token_ids)
     T = x.shape[0] if T is None else T
     _check_call(x, y, topk_idx, topk_weight, T, dims)
     wsb = (workspace.numel() * workspace.element_size()) if workspace is not None else 0
@@ -280,10 +291,10 @@ def moe_ffn_block_workspace_size(T: int, dims: Dims = DIMS) -> int:
 
 def moe_ffn_block_forward_traced(h, norm_weight, eps: float, layer: DeviceLayer, y, workspace, topk_idx=None,
                                  topk_weight=None, stream=None, path: int = PATH_AUTO, trace: Optional[Trace] = None,
-                                 dims: Dims = DIMS, T: Optional[int] = None, check: bool = True) -> int:
+                                 dims: Dims = DIMS, T: Optional[int] = None, check: bool = True, token_ids=None) -> int:
     """y = h + FFN(RMSNorm(h) * norm_weight) (moe_ffn_block_forward_traced):
     h, y bf16 bits [T, D] (y may be h), norm_weight fp32 [D]."""
-    r, ex, sh = layer.structs()
+    r, ex, sh = layer.structs(token_ids)
     T = h.shape[0] if T is None else T
     _check_call(h, y, topk_idx, topk_weight, T, dims)
     _check(norm_weight, "norm_weight", (__import__("torch").float32,))
@@ -300,9 +311,9 @@ def moe_ffn_block_forward_traced(h, norm_weight, eps: float, layer: DeviceLayer,
 
 def moe_ffn_block_forward(h, norm_weight, eps: float, layer: DeviceLayer, y, workspace, topk_idx=None,
                           topk_weight=None, stream=None, dims: Dims = DIMS, T: Optional[int] = None,
-                          check: bool = True) -> int:
+                          check: bool = True, token_ids=None) -> int:
     """moe_ffn_block_forward: the FFN sub-block with its boundary steps."""
-    r, ex, sh = layer.structs()
+    r, ex, sh = layer.structs(token_ids)
     T = h.shape[0] if T is None else T
     _check_call(h, y, topk_idx, topk_weight, T, dims)
     _check(norm_weight, "norm_weight", (__import__("torch").float32,))
@@ -316,10 +327,10 @@ def moe_ffn_block_forward(h, norm_weight, eps: float, layer: DeviceLayer, y, wor
 
 
 def moe_ffn_forward_noalloc(x, layer: DeviceLayer, y, topk_idx=None, topk_weight=None, stream=None,
-                            dims: Dims = DIMS, T: Optional[int] = None, check: bool = True) -> int:
+                            dims: Dims = DIMS, T: Optional[int] = None, check: bool = True, token_ids=None) -> int:
     """moe_ffn_forward_noalloc: T <= NOALLOC_MAX_T tokens with the library's
     own static device scratch (no workspace, no allocation anywhere)."""
-    r, ex, sh = layer.structs()
+    r, ex, sh = layer.structs(token_ids)
     T = x.shape[0] if T is None else T
     _check_call(x, y, topk_idx, topk_weight, T, dims)
     st = lib().moe_ffn_forward_noalloc(ctypes.byref(dims), T, _ptr(x), ctypes.byref(r), ctypes.byref(ex),

@@ -16,6 +16,9 @@ struct DecodeArgs {
     const float* rbias;
     float wscale;    // factor on the renormalised routing weights
     int gating;      // MOE_FFN_GATING_*
+    const int32_t* tid2eid;    // hash routing table [K, n_vocab] or nullptr
+    const int32_t* token_ids;  // [T] with the table
+    int n_vocab;
     const uint16_t *sgi, *sg, *su, *sd;  // shared expert (sg == nullptr: none)
     const uint32_t *gq, *uq, *dq;
     const uint16_t *gs, *gb, *us, *ub, *ds, *db;
@@ -43,23 +46,25 @@ struct DecodeArgs {
     uint16_t* y;
 };
 
-// Top-8 of token t's logits (one wave, result wave-uniform).
-__device__ __forceinline__ void token_top8(const DecodeArgs& a, int t, int lane, float* sel_v, int* sel_i) {
-    float v[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) v[c] = a.logits[(size_t)t * E + lane + 64 * c];
-    wave_top8(v, lane, sel_v, sel_i);
+// The experts of token t (top 8 by logit, or looked up in the hash table)
+// with their logits (one wave, result wave-uniform).
+template <bool HASH>
+__device__ __forceinline__ void token_select(const DecodeArgs& a, int t, int lane, float* sel_v, int* sel_i) {
+    select_experts<HASH>(a.logits + (size_t)t * E, a.tid2eid, a.n_vocab, HASH ? a.token_ids[t] : 0, lane, sel_v,
+                         sel_i);
 }
 
 // One wave: write token t's routing, the expert ids and renormalised weights
 // (the selected scores over their sum; for softmax the full normaliser
 // cancels under norm_topk_prob: the softmax of the eight selected logits).
+template <bool HASH>
 __device__ inline void write_token_route(const DecodeArgs& a, int t, int lane, const float* sel_v, const int* sel_i,
                                          int* sidx) {
     float p[K], s = 0.0f;
+    const float vmax = selected_max<HASH>(sel_v);
 #pragma unroll
     for (int r = 0; r < K; r++) {
-        p[r] = route_score(sel_v[r], sel_v[0], a.gating);
+        p[r] = route_score(sel_v[r], vmax, a.gating);
         s += p[r];
     }
     const float inv = a.wscale / s;  // expert_weights_scale folded into the normaliser

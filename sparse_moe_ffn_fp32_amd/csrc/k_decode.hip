@@ -14,7 +14,8 @@
 // (down: 16 significant bits with the whole fp32 range, so a large h cannot
 // overflow its storage), and every quantisation group's partial dot product
 // is finished in fp32 as  s * acc + (b - 128 s) * sum(x over the group), where
-// the group sum of the activations comes from MFMAs against a ones operand.  "Rows on N": the 16 weight rows are the MFMA's N columns, so each
+// the group sums of the activations are formed once per token tile when it is
+// staged in LDS.  "Rows on N": the 16 weight rows are the MFMA's N columns, so each
 // lane holds one weight row and needs one scale and one bias per group.
 //
 // Every wave issues its global loads up front, in the order it consumes
@@ -108,6 +109,21 @@ __device__ __forceinline__ void split2(const float* v, u32x4& hi, u32x4& lo) {
 
 
 
+
+// Sum of a u32x4 of eight bf16 (as fp32), then over the 8 consecutive lanes
+// holding one 64-element quantisation group of a row (lane quads, then
+// half-rows): every lane of the eight ends with the group's sum, in a fixed
+// order.
+__device__ __forceinline__ float group_sum8(const u32x4& v) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint32_t w = v[j];
+        s += __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+    }
+    s = quad_sum(s);
+    return s + dpp_mov<0x141>(s);  // row_half_mirror: the other quad of the eight
+}
 
 // ------------------------------------------------------------------ stage A
 // Block = (row group, token tile of 16): router groups of SA_ROWS experts,
@@ -220,16 +236,14 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a, int nmt) {
 // One wave per token: DPP top-8 of the logits, renormalised weights and
 // sgate, with the token's logits, x and gate vector loaded together.  Many
 // small blocks, so the 8T arg-max rounds spread over the chip.
+template <bool HASH>
 __global__ void __launch_bounds__(256) k_dec_topk(DecodeArgs a) {
     const int lane = threadIdx.x & 63, t = 4 * blockIdx.x + (threadIdx.x >> 6);
     if (t >= a.T) return;
-    float v[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) v[c] = a.logits[(size_t)t * E + lane + 64 * c];
     float sel_v[K];
     int sel_i[K];
-    wave_top8(v, lane, sel_v, sel_i);
-    write_token_route(a, t, lane, sel_v, sel_i, nullptr);
+    token_select<HASH>(a, t, lane, sel_v, sel_i);
+    write_token_route<HASH>(a, t, lane, sel_v, sel_i, nullptr);
     write_token_sgate(a, t, lane);
 }
 
@@ -321,6 +335,7 @@ constexpr int GU_UNITS = GU_ITEMS * 4;       // token tiles of 16: at most 64 to
 constexpr int XS_STRIDE = D + 8;             // bf16 per staged x row (16-byte pad)
 struct GuSmem {
     uint16_t xs[16][XS_STRIDE];              // token tile of x (bf16, perm8 K order)
+    float xsum[D / G][16];                   // its sums over each quantisation group
     int info[GU_ITEMS][4];                   // expert, token count, first pair of each item
     int unit[GU_UNITS][8];                   // expert, first feature, tokens in the tile, tile parity, first pair
     int pairs[GU_UNITS][16];                 // pair ids of each unit's token slots
@@ -392,7 +407,11 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     };
     auto store_x = [&](const u32x4 (&xv)[8]) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) *(u32x4*)&sm.xs[xr0 + 2 * i][8 * xc] = xv[i];
+        for (int i = 0; i < 8; i++) {
+            *(u32x4*)&sm.xs[xr0 + 2 * i][8 * xc] = xv[i];
+            const float gs = group_sum8(xv[i]);  // pieces 8g .. 8g + 7: one group
+            if ((xc & 7) == 0) sm.xsum[xc >> 3][xr0 + 2 * i] = gs;
+        }
     };
     // this lane's gate/up row in unit k (clamped to the last unit); gate and
     // up share one row layout, so one byte offset serves both code arrays
@@ -435,7 +454,6 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     store_x(xv);
     __syncthreads();
 
-    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
     f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
     u32x4 xn[8];
     // bodies of GU_RING groups, two per unit: ring slot q holds pair q of the
@@ -487,8 +505,7 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
             ag = mfma16_bf16(a1, as_bf16x8(bg[h2 + 1]), ag);
             f32x4 au = mfma16_bf16(a0, as_bf16x8(bu[h2]), z);
             au = mfma16_bf16(a1, as_bf16x8(bu[h2 + 1]), au);
-            f32x4 xsum = mfma16_bf16(a0, as_bf16x8(ones), z);
-            xsum = mfma16_bf16(a1, as_bf16x8(ones), xsum);
+            const f32x4 xsum = *(const f32x4*)&sm.xsum[g][4 * kq];  // token slots 4kq .. 4kq + 3
             const int gs8 = gi & 7;
             if ((gs8 & 1) == 0) {
                 // dword gs8/2 of the four arrays: after the 16-lane swap p0
@@ -612,6 +629,7 @@ constexpr int DN_RING = 16;                         // groups of codes in flight
 constexpr int HS_STRIDE = F + 8;                    // fp16 per staged h row (16-byte pad)
 struct DnSmem {
     uint16_t hs[2][2][16][HS_STRIDE];  // token tiles of h (bf16 hi, lo planes, perm8 order), two buffers
+    float hsum[2][F / G][16];          // their sums over each quantisation group
     int info[DN_ITEMS][4];          // expert, token count, first pair of each item
     int unit[DN_UNITS][8];          // expert, first output row, tokens in the tile, h buffer, first pair
     int pairs[DN_UNITS][16];        // pair ids of each unit's token slots
@@ -689,6 +707,8 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
         for (int i = 0; i < 2; i++) {
             *(u32x4*)&sm.hs[buf][0][hr0 + 8 * i][8 * hc] = hv[i];
             *(u32x4*)&sm.hs[buf][1][hr0 + 8 * i][8 * hc] = hv[2 + i];
+            const float gs = group_sum8(hv[i]) + group_sum8(hv[2 + i]);  // hi + lo of one group
+            if ((hc & 7) == 0) sm.hsum[buf][hc >> 3][hr0 + 8 * i] = gs;
         }
     };
     // code and scale offsets of this lane's output row in unit k
@@ -727,7 +747,6 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
     store_h(0, hv0);
     __syncthreads();
 
-    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
     static_assert(DN_RING == 2 * (F / G), "the ring holds two units");
     // bodies of two units: ring slot 4(k % 2) + q holds pair q of unit k and
     // is refilled with pair q of unit k + 2 (past the last unit: its copy)
@@ -775,10 +794,7 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
                 acc = mfma16_bf16(a1, as_bf16x8(b[h2 + 1]), acc);
                 acc = mfma16_bf16(l0, as_bf16x8(b[h2]), acc);
                 acc = mfma16_bf16(l1, as_bf16x8(b[h2 + 1]), acc);
-                f32x4 hsum = mfma16_bf16(a0, as_bf16x8(ones), z);
-                hsum = mfma16_bf16(a1, as_bf16x8(ones), hsum);
-                hsum = mfma16_bf16(l0, as_bf16x8(ones), hsum);
-                hsum = mfma16_bf16(l1, as_bf16x8(ones), hsum);
+                const f32x4 hsum = *(const f32x4*)&sm.hsum[hb][g][4 * kq];  // token slots 4kq .. 4kq + 3
                 const float sg = bf16_at(sv, g);
                 const float cg = bf16_at(bv, g) - 128.0f * sg;
 #pragma unroll
@@ -847,7 +863,10 @@ static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s
     const int n_gu = GU_BLOCKS;
     tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a, dim3((N_ROUTER_GRP + N_SGU_GRP) * nmt + (a.T + 3) / 4), dim3(1024), 0,
               s, a, nmt);
-    hipLaunchKernelGGL(k_dec_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+    if (a.tid2eid)
+        hipLaunchKernelGGL(k_dec_topk<true>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_dec_topk<false>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
     const int n_sd = a.sg ? N_SDOWN_BLK : 0;
     tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_sd + n_gu), dim3(512), 0, s, a, n_sd);
@@ -861,6 +880,7 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     DecodeArgs a{};
     a.x = p.x; a.T = p.T;
     a.wr = p.router_w; a.rbias = p.router_b; a.wscale = p.wscale; a.gating = p.gating;
+    a.tid2eid = p.tid2eid; a.token_ids = p.token_ids; a.n_vocab = p.n_vocab;
     a.sgi = p.sh_gate_inp; a.sg = p.sh_gate; a.su = p.sh_up; a.sd = p.sh_down;
     a.gq = p.gate_q; a.uq = p.up_q; a.dq = p.down_q;
     a.gs = p.gate_s; a.gb = p.gate_b; a.us = p.up_s; a.ub = p.up_b; a.ds = p.down_s; a.db = p.down_b;

@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(512) k_tiny_a(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ C
-template <int NT>
+template <int NT, bool HASH>
 __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if ((int)blockIdx.x >= n_gu_blocks) {
@@ -339,8 +339,8 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
     if (wave == 0) {
         float sel_v[K];
         int sel_i[K];
-        token_top8(a, t, lane, sel_v, sel_i);
-        if (r == 0 && fc == 0) write_token_route(a, t, lane, sel_v, sel_i, nullptr);  // sgate: stage A
+        token_select<HASH>(a, t, lane, sel_v, sel_i);
+        if (r == 0 && fc == 0) write_token_route<HASH>(a, t, lane, sel_v, sel_i, nullptr);  // sgate: stage A
         int er = sel_i[0];
 #pragma unroll
         for (int k = 1; k < K; k++) er = (k == r) ? sel_i[k] : er;
@@ -474,18 +474,35 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
     }
     __syncthreads();
     const int g = c >> 1;
+    // two units at a time: every LDS read of both (h hi and lo planes, the
+    // piece sums) is issued before the first dot product waits for one
 #pragma unroll
-    for (int j = 0; j < nj; j++) {
-        const int u = (wave * nj + j) * 4 + sub;
-        const int pp = u >> 3, i = u & 7;
-        float acc = 0.0f;
+    for (int j0 = 0; j0 < nj; j0 += 2) {
+        u32x4 hh[2][4], hw[2][4];
+        float hs[2];
 #pragma unroll
-        for (int w = 0; w < 4; w++)
-            acc = dot_codes_bf16_2(cv[j][w], *(const u32x4*)&hl[0][pp][32 * c + 8 * w],
-                                   *(const u32x4*)&hl[1][pp][32 * c + 8 * w], acc);
-        const float s = group_param(sv[j], g), bb = group_param(bv[j], g);
-        const float v = row16_sum(s * acc + (bb - 128.0f * s) * hsum[pp][c]);
-        if (c == 0) dv[pp][i] = v;
+        for (int jj = 0; jj < 2; jj++) {
+            const int pp = ((wave * nj + j0 + jj) * 4 + sub) >> 3;
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                hh[jj][w] = *(const u32x4*)&hl[0][pp][32 * c + 8 * w];
+                hw[jj][w] = *(const u32x4*)&hl[1][pp][32 * c + 8 * w];
+            }
+            hs[jj] = hsum[pp][c];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+            const int j = j0 + jj;
+            const int u = (wave * nj + j) * 4 + sub;
+            const int pp = u >> 3, i = u & 7;
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; w++) acc = dot_codes_bf16_2(cv[j][w], hh[jj][w], hw[jj][w], acc);
+            const float s = group_param(sv[j], g), bb = group_param(bv[j], g);
+            const float v = row16_sum(s * acc + (bb - 128.0f * s) * hs[jj]);
+            if (c == 0) dv[pp][i] = v;
+        }
     }
     __syncthreads();
     if (tid < T * TD_ROWS) {
@@ -507,7 +524,11 @@ hipError_t launch_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
         tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a<NT, true>, ga, dim3(512), 0, s, a);
     else
         tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a<NT, false>, ga, dim3(512), 0, s, a);
-    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_tiny_c<NT>, dim3(n_gu + (a.sd ? TC_SDOWN_BLK : 0)), dim3(256), 0, s, a, n_gu);
+    const dim3 gc(n_gu + (a.sd ? TC_SDOWN_BLK : 0));
+    if (a.tid2eid)
+        tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_tiny_c<NT, true>, gc, dim3(256), 0, s, a, n_gu);
+    else
+        tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_tiny_c<NT, false>, gc, dim3(256), 0, s, a, n_gu);
     tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_tiny_d<NT>, dim3(D / TD_ROWS), dim3(TD_THREADS), 0, s, a);
     return hipGetLastError();
 }

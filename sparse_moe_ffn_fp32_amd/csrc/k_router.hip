@@ -116,25 +116,25 @@ __global__ void __launch_bounds__(256) k_prep_weights(const float* __restrict__ 
 
 // One wave per token: top-8 of the 256 logits, renormalised softmax weights,
 // and sgate.  Lane l holds experts l, l+64, l+128, l+192.
+template <bool HASH>
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, const uint16_t* __restrict__ x,
                                               const uint16_t* __restrict__ gate_inp, int32_t* __restrict__ idx_out,
                                               float* __restrict__ w_out, float* __restrict__ sgate_out, float wscale,
-                                              int gating, int T) {
+                                              int gating, const int32_t* __restrict__ tid2eid,
+                                              const int32_t* __restrict__ token_ids, int n_vocab, int T) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    float v[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) v[c] = logits[(size_t)t * E + lane + 64 * c];
     float sel_v[K];
     int sel_i[K];
-    wave_top8(v, lane, sel_v, sel_i);
+    select_experts<HASH>(logits + (size_t)t * E, tid2eid, n_vocab, HASH ? token_ids[t] : 0, lane, sel_v, sel_i);
     // norm_topk_prob: the eight selected scores renormalised (for softmax
     // the full normaliser cancels: the softmax over the selected logits)
     float p[K], s = 0.0f;
+    const float vmax = selected_max<HASH>(sel_v);
 #pragma unroll
     for (int r = 0; r < K; r++) {
-        p[r] = route_score(sel_v[r], sel_v[0], gating);
+        p[r] = route_score(sel_v[r], vmax, gating);
         s += p[r];
     }
     const float inv = wscale / s;  // expert_weights_scale folded into the normaliser
@@ -179,9 +179,14 @@ hipError_t launch_prep_weights(const float* wr, uint16_t* wr2, int32_t* er, cons
 }
 
 hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
-                       float* sgate, float wscale, int gating, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, gate_inp, idx, w, sgate, wscale, gating,
-                       T);
+                       float* sgate, float wscale, int gating, const int32_t* tid2eid, const int32_t* token_ids,
+                       int n_vocab, int T, hipStream_t s) {
+    if (tid2eid)
+        hipLaunchKernelGGL(k_topk<true>, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, gate_inp, idx, w, sgate, wscale,
+                           gating, tid2eid, token_ids, n_vocab, T);
+    else
+        hipLaunchKernelGGL(k_topk<false>, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, gate_inp, idx, w, sgate,
+                           wscale, gating, tid2eid, token_ids, n_vocab, T);
     return hipGetLastError();
 }
 

@@ -325,6 +325,33 @@ __device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v
     }
 }
 
+// The experts of one token and their logits (lrow: the token's E logits),
+// wave-uniform in sel_i / sel_v: the top K by logit (wave_top8), or with a
+// hash table (ds4.c study notes Part 3, MoE trace 3: experts looked up by
+// token id in a precomputed [K, n_vocab] table) column `tok` of the table in
+// table order.  The id and the entries are clamped into range.
+// HASH is a compile-time choice so that the top-K path carries no trace of
+// the table path.
+template <bool HASH>
+__device__ __forceinline__ void select_experts(const float* lrow, const int32_t* tid2eid, int n_vocab, int tok,
+                                               int lane, float* sel_v, int* sel_i) {
+    if constexpr (HASH) {
+        tok = min(max(tok, 0), n_vocab - 1);
+        const int e = min(max(tid2eid[(size_t)min(lane, K - 1) * n_vocab + tok], 0), E - 1);
+        const float v = lrow[e];
+#pragma unroll
+        for (int r = 0; r < K; r++) {
+            sel_i[r] = __builtin_amdgcn_readlane(e, r);
+            sel_v[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), r));
+        }
+    } else {
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) v[c] = lrow[lane + 64 * c];
+        wave_top8(v, lane, sel_v, sel_i);
+    }
+}
+
 // Sum over each 16-lane row; every lane of the row ends with the same,
 // order-fixed value (each step adds a lane's partner, and the partner adds
 // the same two terms).
@@ -344,7 +371,19 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// Routing score of a selected logit v given the top one v0, before the
+// Largest of the K selected logits: the first one of a top-K selection,
+// any of them for a table's.
+template <bool HASH>
+__device__ __forceinline__ float selected_max(const float* sel_v) {
+    float m = sel_v[0];
+    if constexpr (HASH) {
+#pragma unroll
+        for (int r = 1; r < K; r++) m = __builtin_fmaxf(m, sel_v[r]);
+    }
+    return m;
+}
+
+// Routing score of a selected logit v given the largest selected one v0, before the
 // renormalisation over the top k: softmax exp(v - v0) (the full-softmax
 // normaliser cancels), or sqrt(softplus(v)), softplus computed stably
 // (log1p(e^v); v beyond +-20 is v or e^v to fp32 precision, and sqrt(e^v)

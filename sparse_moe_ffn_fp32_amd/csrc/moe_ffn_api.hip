@@ -109,6 +109,7 @@ int validate_args(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const 
     if (!x || !y || !router || !router->weight || !ex) return MOE_FFN_EINVAL;
     if (!(router->weights_scale >= 0.0f) || router->weights_scale == INFINITY) return MOE_FFN_EINVAL;
     if (router->gating != MOE_FFN_GATING_SOFTMAX && router->gating != MOE_FFN_GATING_SQRT_SOFTPLUS) return MOE_FFN_EINVAL;
+    if (router->tid2eid && (!router->token_ids || router->n_vocab < 1)) return MOE_FFN_EINVAL;
     if (ex->gate_up_fused != 0 && ex->gate_up_fused != 1) return MOE_FFN_EINVAL;
     if (ex->gate_up_fused && (ex->up.qweight || ex->up.scales || ex->up.biases)) return MOE_FFN_EINVAL;
     const GateUp gu = resolve_gate_up(ex);
@@ -118,7 +119,8 @@ int validate_args(const moe_ffn_dims* dims, int64_t T, const uint16_t* x, const 
     if (sh && (!sh->gate || !sh->up || !sh->down)) return MOE_FFN_EINVAL;
     for (const void* p : req)
         if (!al16(p)) return MOE_FFN_EALIGN;
-    const void* opt[] = {x, y, router->weight, router->bias, topk_idx, topk_weight,
+    const void* opt[] = {x, y, router->weight, router->bias, topk_idx, topk_weight, router->tid2eid,
+                         router->tid2eid ? router->token_ids : nullptr,
                          sh ? sh->gate : nullptr, sh ? sh->up : nullptr, sh ? sh->down : nullptr,
                          sh ? sh->gate_inp : nullptr};
     for (const void* p : opt)
@@ -176,7 +178,8 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     chk(launch_prep_x(x, xh, xe, T, s));
     chk(launch_router_gemm(xh, xe, wr2, er, router->bias, logits, shw, es, (uint16_t*)at(L.hs), (int32_t*)at(L.ehs), T,
                            tr, s));
-    chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, weights_scale(router), router->gating, T, s));
+    chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, weights_scale(router), router->gating,
+                    router->tid2eid, router->token_ids, router->n_vocab, T, s));
     chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(T), s));
     PrefillGemmParams p{};
     p.xh = xh;
@@ -229,11 +232,13 @@ int forward_impl(int64_t T, const uint16_t* x, const float* norm_w, float eps, u
         for (int64_t c0 = 0; c0 < T; c0 += MOE_FFN_PREFILL_CHUNK_T) {
             const int tc = (int)(T - c0 < MOE_FFN_PREFILL_CHUNK_T ? T - c0 : MOE_FFN_PREFILL_CHUNK_T);
             const uint16_t* xin = x + c0 * D;
+            moe_ffn_router rc = *router;  // this slice's token ids
+            if (rc.tid2eid) rc.token_ids += c0;
             if (norm_w) {
                 if (launch_rmsnorm(x + c0 * D, norm_w, eps, xn, tc, stream) != hipSuccess) return MOE_FFN_EHIP;
                 xin = xn;
             }
-            const int r = run_prefill(tc, xin, router, experts, shared, y + c0 * D,
+            const int r = run_prefill(tc, xin, &rc, experts, shared, y + c0 * D,
                                       topk_idx ? topk_idx + c0 * K : nullptr, topk_weight ? topk_weight + c0 * K : nullptr,
                                       (char*)workspace, norm_w ? x + c0 * D : nullptr, tr, stream);
             if (r != MOE_FFN_OK) return r;
@@ -250,6 +255,9 @@ int forward_impl(int64_t T, const uint16_t* x, const float* norm_w, float eps, u
     p.router_b = router->bias;
     p.wscale = weights_scale(router);
     p.gating = router->gating;
+    p.tid2eid = router->tid2eid;
+    p.token_ids = router->token_ids;
+    p.n_vocab = router->n_vocab;
     p.sh_gate_inp = shared ? shared->gate_inp : nullptr;
     p.sh_gate = shared ? shared->gate : nullptr;
     p.sh_up = shared ? shared->up : nullptr;

@@ -30,8 +30,10 @@ struct Tracer {
 hipError_t launch_prep_weights(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
                                const uint16_t* sd, uint16_t* shw, int32_t* es, hipStream_t s);
 // wscale multiplies every renormalised routing weight
+// tid2eid != nullptr: hash routing with token_ids [T] (n_vocab table columns)
 hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
-                       float* sgate, float wscale, int gating, int T, hipStream_t s);
+                       float* sgate, float wscale, int gating, const int32_t* tid2eid, const int32_t* token_ids,
+                       int n_vocab, int T, hipStream_t s);
 
 // ---- routing sort (k_sort.hip)
 int sort_blocks(int N);
@@ -87,6 +89,9 @@ struct DecodeParams {
     const float *router_w, *router_b;
     float wscale;  // factor on the renormalised routing weights
     int gating;    // MOE_FFN_GATING_*
+    const int32_t* tid2eid;    // hash routing table [K, n_vocab] or nullptr
+    const int32_t* token_ids;  // [T] with the table
+    int n_vocab;
     const uint16_t *sh_gate_inp, *sh_gate, *sh_up, *sh_down;  // sh_gate == nullptr: no shared expert
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;

@@ -156,6 +156,7 @@ class Layer:
     meta: dict = field(default_factory=dict)
     weights_scale: float = 1.0           # expert_weights_scale of the routed MoE call
     gating: int = 0                      # 0: softmax scores; 1: sqrt(softplus(logit)) scores
+    tid2eid: Optional[np.ndarray] = None  # hash routing table int32 [top_k, n_vocab], or None
 
 
 def make_layer(seed: int, dims: Dims = Dims(), *, w_sd: float = 0.02, zipf_s: Optional[float] = None,

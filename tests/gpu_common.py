@@ -33,7 +33,7 @@ class GpuRunner:
             self.layers[key] = (layer, moe.DeviceLayer.from_host(layer))
         return self.layers[key][1]
 
-    def run(self, layer, x: np.ndarray, path=moe.PATH_AUTO, dl=None, poison=False, T=None):
+    def run(self, layer, x: np.ndarray, path=moe.PATH_AUTO, dl=None, poison=False, T=None, token_ids=None):
         torch = self.torch
         dl = dl or self.device_layer(layer)
         T = x.shape[0] if T is None else T
@@ -44,20 +44,23 @@ class GpuRunner:
         ws = moe.alloc_workspace(max(T, 1))
         if poison:
             ws.fill_(0xFF)
-        moe.moe_ffn_forward_path(xd, dl, y, ws, idx, w, path=path, T=T)
+        tid = None if token_ids is None else torch.from_numpy(np.ascontiguousarray(token_ids, dtype=np.int32)).cuda()
+        moe.moe_ffn_forward_path(xd, dl, y, ws, idx, w, path=path, T=T, token_ids=tid)
         torch.cuda.synchronize()
         return (y.cpu().numpy().view(np.uint16)[:T], idx.cpu().numpy()[:T], w.cpu().numpy()[:T])
 
 
-def routing_check(layer, x, idx_gpu, w_gpu, O=None, tokens=None):
+def routing_check(layer, x, idx_gpu, w_gpu, O=None, tokens=None, token_ids=None):
     """Compare routing on the listed tokens (all when None).  Returns stats."""
     O = O or oracle.get()
     tok = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
-    r = O.route(layer, x, tokens=tok, want_logits=True)
+    r = O.route(layer, x, tokens=tok, want_logits=True, token_ids=token_ids)
     k = layer.dims.top_k
     lg = r["logits"]
     top = -np.sort(-lg, axis=1)[:, : k + 1]
     unique_order = np.all(-np.diff(top, axis=1) >= ORDER_GAP, axis=1)
+    if getattr(layer, "tid2eid", None) is not None:
+        unique_order[:] = True  # a table's order does not depend on the logits
     gi, gw = idx_gpu[tok], w_gpu[tok]
     set_ok = np.array([set(a) == set(b) for a, b in zip(gi.tolist(), r["idx"].tolist())])
     assert set_ok.all(), f"expert sets differ on tokens {tok[~set_ok][:10]}"
@@ -73,10 +76,10 @@ def routing_check(layer, x, idx_gpu, w_gpu, O=None, tokens=None):
     return dict(tokens=int(tok.size), unique_order=int(unique_order.sum()), w_err=float(werr))
 
 
-def output_check(layer, x, y_gpu, O=None, tokens=None, nthreads=None, tol=Y_REL_L2):
+def output_check(layer, x, y_gpu, O=None, tokens=None, nthreads=None, tol=Y_REL_L2, token_ids=None):
     O = O or oracle.get()
     tok = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
-    ref = O.forward(layer, x, tokens=tok, nthreads=nthreads)["y"]
+    ref = O.forward(layer, x, tokens=tok, nthreads=nthreads, token_ids=token_ids)["y"]
     got = bf16_to_f64(y_gpu[tok])
     nrm = np.linalg.norm(ref, axis=1)
     err = np.linalg.norm(got - ref, axis=1)

@@ -462,4 +462,86 @@ def pin_sqrt_softplus_extremes(O):
     assert np.isfinite(r["w"]).all() and np.abs(r["w"] - raw / raw.sum()).max() <= 1e-15
 
 
+def _hash_table(k, n_vocab, E):
+    """Column v of the table lists experts (3v + 5r + 1) mod E, r < k:
+    distinct within a column for k <= 3 (and for r = 0..3 with E = 16)."""
+    r = np.arange(k)[:, None]
+    v = np.arange(n_vocab)[None, :]
+    return ((3 * v + 5 * r + 1) % E).astype(np.int32)
+
+
+def pin_hash_routing(O):
+    """Hash routing (ds4.c notes Part 3, MoE trace 3): the experts of token t
+    are column token_ids[t] of the [k, n_vocab] table, in table order, for
+    any x; with zero router weights the logits are the bias exactly, so the
+    softmax weights are e^b / sum e^b over the looked-up experts (a repeated
+    expert gets its share once per rank), sqrt-softplus weights of logits
+    >= 100 are sqrt(b) / sum sqrt(b), and expert_weights_scale multiplies
+    them; the whole forward is sum_r w_r SwiGLU_e_r(x) from dense numpy."""
+    import copy
+    lay = tiny_layer(shared=False)
+    E, k = lay.dims.n_experts, lay.dims.top_k
+    nv = 10
+    lay.tid2eid = _hash_table(k, nv, E)
+    tid = np.array([0, 9, 3, 3, 7, 1], dtype=np.int32)
+    x = tiny_x(seed=6, T=6)
+    r = O.route(lay, x, token_ids=tid)
+    want_idx = lay.tid2eid[:, tid].T
+    assert np.array_equal(r["idx"], want_idx) and np.isinf(r["margin"]).all()
+    assert np.array_equal(O.route(lay, tiny_x(seed=7, T=6), token_ids=tid)["idx"], want_idx)
+    flat = copy.deepcopy(lay)
+    flat.router_w = np.zeros_like(lay.router_w)
+    flat.router_b = (np.arange(E) % 5).astype(np.float32)
+    w = O.route(flat, x, token_ids=tid)["w"]
+    eb = np.exp(flat.router_b.astype(np.float64)[want_idx])
+    assert np.abs(w - eb / eb.sum(axis=1, keepdims=True)).max() <= 1e-15
+    dup = copy.deepcopy(flat)
+    dup.tid2eid = dup.tid2eid.copy()
+    dup.tid2eid[1] = dup.tid2eid[0]  # rank 1 repeats rank 0's expert
+    wd = O.route(dup, x, token_ids=tid)["w"]
+    eb2 = np.exp(flat.router_b.astype(np.float64)[dup.tid2eid[:, tid].T])
+    assert np.abs(wd - eb2 / eb2.sum(axis=1, keepdims=True)).max() <= 1e-15 and np.all(wd[:, 0] == wd[:, 1])
+    sp = copy.deepcopy(flat)
+    sp.router_b = (100.0 * (np.arange(E) + 1) ** 2).astype(np.float32)
+    sp.gating = 1
+    sp.weights_scale = 2.0
+    ws = O.route(sp, x, token_ids=tid)["w"]
+    sq = 10.0 * (want_idx + 1).astype(np.float64)
+    assert np.abs(ws - 2.0 * sq / sq.sum(axis=1, keepdims=True)).max() <= 1e-14
+    out = O.forward(flat, x, token_ids=tid, nthreads=1)
+    g = flat.dims.group_size
+    xd = npr.bf16(x).astype(np.float64)
+    for t in range(x.shape[0]):
+        y = np.zeros(flat.dims.d_model)
+        for rr in range(k):
+            e = int(want_idx[t, rr])
+            y += out["w"][t, rr] * npr.swiglu(npr.dequant(flat.gate, e, g).astype(np.float64),
+                                              npr.dequant(flat.up, e, g).astype(np.float64),
+                                              npr.dequant(flat.down, e, g).astype(np.float64), xd[t])
+        assert rel(out["y"][t], y) <= 1e-12
+
+
+def pin_hash_table_validated(O):
+    """Table entries outside [0, E) and token ids outside [0, n_vocab) are
+    refused rather than read out of range."""
+    lay = tiny_layer(shared=False)
+    E, k = lay.dims.n_experts, lay.dims.top_k
+    lay.tid2eid = _hash_table(k, 4, E)
+    x = tiny_x(seed=6, T=2)
+    for bad_ids in (np.array([0, 4], dtype=np.int32), np.array([-1, 0], dtype=np.int32)):
+        try:
+            O.route(lay, x, token_ids=bad_ids)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("out-of-range token id accepted")
+    lay.tid2eid[2, 1] = E
+    try:
+        O.route(lay, x, token_ids=np.array([0, 1], dtype=np.int32))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("out-of-range table entry accepted")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -229,3 +229,22 @@ def test_noalloc_rejects_before_launch(L):
     assert call(4, dims=moe.Dims(2048, 256, 8, 512, 512, 32)) == moe.MOE_FFN_EUNSUPPORTED
     assert moe.moe_ffn_status_string(moe.MOE_FFN_ETOOBIG) != "unknown status"
     assert "#define MOE_FFN_NOALLOC_MAX_T 64" in open(HEADER).read()
+
+
+def test_hash_router_arguments(L):
+    """A hash table needs token ids and n_vocab >= 1, both 16-byte aligned;
+    accepted arguments get as far as the workspace check."""
+    layer = _layer()
+    r, ex, sh = layer.structs()
+
+    def call(tab, ids, nv, ws=0x40000000):
+        r.tid2eid, r.token_ids, r.n_vocab = tab, ids, nv
+        return L.moe_ffn_forward_path(ctypes.byref(moe.DIMS), 4, 0x20000000, ctypes.byref(r), ctypes.byref(ex),
+                                      ctypes.byref(sh), 0x30000000, None, None, ws, 16, None, 0)
+
+    assert call(0x50000000, None, 100) == moe.MOE_FFN_EINVAL
+    assert call(0x50000000, 0x51000000, 0) == moe.MOE_FFN_EINVAL
+    assert call(0x50000004, 0x51000000, 100) == moe.MOE_FFN_EALIGN
+    assert call(0x50000000, 0x51000008, 100) == moe.MOE_FFN_EALIGN
+    assert call(0x50000000, 0x51000000, 100) == moe.MOE_FFN_EWORKSPACE
+    assert call(None, None, 0) == moe.MOE_FFN_EWORKSPACE

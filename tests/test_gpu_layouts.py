@@ -147,3 +147,39 @@ def test_sqrt_softplus_gating(gpu, layer0, T, path, offset):
     assert np.array_equal(got[1], ref["idx"])
     assert np.abs(got[2].astype(np.float64) - ref["w"]).max() <= W_ABS
     _say(output_check(lay, x, got[0]))
+
+
+def _hash_layer(base, n_vocab, seed, dup):
+    """base with a seeded hash table [8, n_vocab] of experts (with dup, rank 1
+    repeats rank 0's expert in every column)."""
+    import copy
+    lay = copy.copy(base)
+    tab = np.random.default_rng(seed).integers(0, base.dims.n_experts, size=(base.dims.top_k, n_vocab))
+    tab = tab.astype(np.int32)
+    if dup:
+        tab[1] = tab[0]
+    lay.tid2eid = tab
+    return lay
+
+
+@pytest.mark.parametrize("T,path,gating,dup", [(1, "auto", 0, False), (4, "auto", 1, True), (37, "decode", 0, False),
+                                               (37, "prefill", 1, False), (300, "auto", 0, True),
+                                               (300, "auto", 1, False)])
+def test_hash_routing(gpu, layer0, T, path, gating, dup):
+    """Hash routing (ds4.c study notes Part 3, MoE trace 3): token t's experts
+    are column token_ids[t] of the [8, n_vocab] table, exactly and in table
+    order, on every path; the weights (the gating's scores of those experts,
+    renormalised) and y against the oracle.  No routing margin is needed:
+    the choice does not depend on the logits."""
+    import sparse_moe_ffn_fp32_amd as moe
+    from gpu_common import W_ABS
+    lay = _hash_layer(layer0, 1000, 40 + T, dup)
+    lay.gating = gating
+    tid = np.random.default_rng(T).integers(0, 1000, size=T).astype(np.int32)
+    x = synth.x_rows(700 + T, T, 2048)
+    _say(f"hash routing T={T} path={path} gating={gating} dup={dup}")
+    y, idx, w = gpu.run(lay, x, path=PATHS[path], dl=moe.DeviceLayer.from_host(lay), token_ids=tid)
+    assert np.array_equal(idx, lay.tid2eid[:, tid].T), "experts differ from the table lookup"
+    ref = oracle.get().forward(lay, x, token_ids=tid)
+    assert np.abs(w.astype(np.float64) - ref["w"]).max() <= W_ABS
+    _say(output_check(lay, x, y, token_ids=tid))

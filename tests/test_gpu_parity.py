@@ -296,6 +296,23 @@ def test_config1_40_layers_graph_replays(gpu):
     _say("config1: 3 graph replays reproduce the eager pass bit for bit")
 
 
+def test_hash_routing_in_slices(gpu, layer0):
+    """Hash routing over 32768 + 7 tokens: the second prefill slice reads its
+    own token ids (offset by the slice start), so every token's experts are
+    its table column."""
+    import sparse_moe_ffn_fp32_amd as moe
+    T = 32768 + 7
+    lay = copy.copy(layer0)
+    lay.tid2eid = np.random.default_rng(3).integers(0, 256, size=(8, 5000)).astype(np.int32)
+    tid = np.random.default_rng(4).integers(0, 5000, size=T).astype(np.int32)
+    x = synth.x_rows(778, T, 2048)
+    _say(f"hash routing in slices T={T}")
+    y, idx, w = gpu.run(lay, x, path=PATHS["prefill"], dl=moe.DeviceLayer.from_host(lay), token_ids=tid)
+    assert np.array_equal(idx, lay.tid2eid[:, tid].T), "experts differ from the table lookup"
+    sample = np.unique(np.concatenate([np.arange(0, T, 1024), np.arange(32768 - 4, T)]))
+    _say(output_check(lay, x, y, tokens=sample, token_ids=tid))
+
+
 def test_prefill_in_slices_matches_one_pass(gpu, layer0):
     """A call longer than MOE_FFN_PREFILL_CHUNK_T runs in token slices inside
     a workspace of one slice's size: 32768 + 7 tokens give, bit for bit, what

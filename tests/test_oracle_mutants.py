@@ -32,10 +32,19 @@ MUTANTS = [
     ("softplus_underflows", "w[r] = 0.5 * log_softplus(logits[sel[r]]);",
      "w[r] = 0.5 * log(fmax(logits[sel[r]], 0.0) + log1p(exp(-fabs(logits[sel[r]]))));"),
     ("softplus_not_renormalised", "for (int64_t r = 0; r < k; r++) w[r] /= s;", ";"),
-    ("gating_ignored", "if (j->L->gating == 1) sqrt_softplus_weights(lg, sel, k, ww);", ";"),
-    ("weights_scale_ignored", "ww[r] *= weights_scale(j->L);", "ww[r] *= 1.0;"),
+    ("gating_ignored", "if (L->gating == 1) sqrt_softplus_weights(lg, sel, k, ww);", ";"),
+    ("weights_scale_ignored", "ww[r] *= weights_scale(L);", "ww[r] *= 1.0;"),
     ("weights_scale_no_default", "L->weights_scale == 0.0 ? 1.0 : L->weights_scale", "L->weights_scale"),
-    ("weights_scale_squared", "ww[r] *= weights_scale(j->L);", "ww[r] *= weights_scale(j->L) * weights_scale(j->L);"),
+    ("weights_scale_squared", "ww[r] *= weights_scale(L);", "ww[r] *= weights_scale(L) * weights_scale(L);"),
+    ("hash_ignored", "if (L->tid2eid) {", "if (0) {"),
+    ("hash_table_transposed", "sel[r] = L->tid2eid[r * L->n_vocab + L->token_ids[t]];",
+     "sel[r] = L->tid2eid[L->token_ids[t] * d->top_k + r];"),
+    ("hash_rank_reversed", "sel[r] = L->tid2eid[r * L->n_vocab + L->token_ids[t]];",
+     "sel[r] = L->tid2eid[(k - 1 - r) * L->n_vocab + L->token_ids[t]];"),
+    ("hash_weights_by_rank", "for (int64_t r = 0; r < k; r++) w[r] = (exp(logits[sel[r]] - top) / norm) / chosen;",
+     "for (int64_t r = 0; r < k; r++) w[r] = (exp(logits[r] - top) / norm) / chosen;"),
+    ("hash_not_renormalised", "for (int64_t r = 0; r < k; r++) w[r] = (exp(logits[sel[r]] - top) / norm) / chosen;",
+     "for (int64_t r = 0; r < k; r++) w[r] = exp(logits[sel[r]] - top) / norm;"),
     ("router_transposed", "L->router_w[e * d->d_model + i]", "L->router_w[i * d->n_experts + e]"),
     ("tie_upper_index", "if (!taken[e] && (best < 0 || logits[e] > logits[best])) best = e;",
      "if (!taken[e] && (best < 0 || logits[e] >= logits[best])) best = e;"),
