@@ -121,7 +121,8 @@ struct GemmArgs {
     const int32_t* perm;     // sorted position -> assignment
     const int32_t* pos_of;   // assignment -> sorted position
     const int32_t* offs;     // [E+1] expert segment starts
-    const int32_t* tiles;    // [4i..4i+3] expert, first row, segment start, rows
+    const int32_t* tiles;    // [4i..4i+3] expert, first row, segment start, rows; longest first
+    const int32_t* tiles_e;  // the same records in expert order
     const int32_t* tile_count;
     const float* wflat;      // [T*K] routing weights by assignment
     const float* sgate;      // [T]
@@ -474,6 +475,29 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     }
 }
 
+// The (tile, column block) item of routed block `bid`.  Workgroups are dealt
+// to the 8 XCDs in turn by id (XCD bid % 8) and started in id order as
+// compute units free up.  The tile map lists the longest tiles first; pairs
+// of consecutive tiles (TPAIR) are dealt to the XCDs in turn, and each XCD
+// runs all NB column blocks of a tile back to back: the tile's activation
+// rows and, within a pair, an expert's weights meet in one L2, and every XCD
+// works through the list from its longest tiles to its shortest.  Ids that
+// map past the last tile return false.
+constexpr int TPAIR = 2;
+template <int NB>
+__device__ __forceinline__ bool tile_of_block(int bid, int n_tiles, int& tile, int& nblk) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int k = slot / NB;  // the XCD's k-th tile
+    nblk = slot % NB;
+    tile = (k / TPAIR) * (8 * TPAIR) + xcd * TPAIR + k % TPAIR;
+    return tile < n_tiles;
+}
+// Blocks of a routed launch: every XCD gets slots for its share of max_tiles.
+template <int NB>
+__host__ __device__ constexpr int routed_grid(int max_tiles) {
+    return 8 * ((max_tiles + 8 * TPAIR - 1) / (8 * TPAIR)) * TPAIR * NB;
+}
+
 // ---------------------------------------------------------------- wide down
 // The routed down projection on 128-row tiles with 512 output columns per
 // block: 8 waves, wave w computing all 128 rows against weight rows
@@ -531,13 +555,17 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, kq = lane >> 5;
 
+    // (tile, column block) item: the tiles in expert order, XCD p % 8 taking
+    // one contiguous run of items, column block fastest: the blocks sharing
+    // a tile's h rows, and the tiles sharing an expert's weights (590 KB, the
+    // larger operand here), meet in one L2
     constexpr int NB = D / WBN;
     const int n_tiles = g.tile_count[0];
     const int live = n_tiles * NB, per_xcd = (live + 7) >> 3;
     const int slot = bid >> 3, item = (bid & 7) * per_xcd + slot;
     if (slot >= per_xcd || item >= live) return;
     const int tile = item / NB, nblk = item % NB;
-    const int4 rec = *(const int4*)&g.tiles[4 * tile];  // one dependent load
+    const int4 rec = *(const int4*)&g.tiles_e[4 * tile];  // one dependent load
     const int e = rec.x, m0 = rec.y, seg = rec.z, rows = rec.w;  // rows: 1 .. GEMM_BM
 
     // ---- A (h rows): thread loads 16 bytes (chunk ac) of rows ar0 + 64i
@@ -757,11 +785,8 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
     const int l32 = lane & 31, kq = lane >> 5;
 
     constexpr int NB = F / (WBN / 2);
-    const int n_tiles = g.tile_count[0];
-    const int live = n_tiles * NB, per_xcd = (live + 7) >> 3;
-    const int slot = bid >> 3, item = (bid & 7) * per_xcd + slot;
-    if (slot >= per_xcd || item >= live) return;
-    const int tile = item / NB, nblk = item % NB;
+    int tile, nblk;
+    if (!tile_of_block<NB>(bid, g.tile_count[0], tile, nblk)) return;
     const int4 rec = *(const int4*)&g.tiles[4 * tile];  // one dependent load
     const int e = rec.x, m0 = rec.y, seg = rec.z, rows = rec.w;  // rows: 1 .. GEMM_BM
 
@@ -981,17 +1006,31 @@ __global__ void __launch_bounds__(256) k_combine_routed(const uint16_t* __restri
 
 // x bf16 [T, D] -> fp16 [T, D] in perm8 order, each row times 2^-ex[t] with
 // its exponent (row_exp of its largest |x|); exact where the scaled value is
-// an fp16 normal.  One wave per row, lane pieces lane + 64 i.
+// an fp16 normal.  With the row at hand, also the shared-expert gate
+// (qwen35moe page, "Shared-expert MoE FFN"): sgate[t] = sigmoid(gate_inp . x)
+// (1 when the layer has no gate vector).  One wave per row, lane pieces
+// lane + 64 i.
 __global__ void __launch_bounds__(256) k_prep_x(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
-                                                int32_t* __restrict__ ex, int T) {
+                                                int32_t* __restrict__ ex, const uint16_t* __restrict__ gate_inp,
+                                                float* __restrict__ sgate, int T) {
     const int lane = threadIdx.x & 63, t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const u32x4* src = (const u32x4*)(x + (size_t)t * D);
-    u32x4 d[4];
-    float m = 0.0f;
+    u32x4 d[4], gv[4];
+    float m = 0.0f, z = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         d[i] = src[lane + 64 * i];
+        gv[i] = gate_inp ? ((const u32x4*)gate_inp)[lane + 64 * i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t w = d[i][j], gw = gv[i][j];
+            z += __uint_as_float(w << 16) * __uint_as_float(gw << 16);
+            z += __uint_as_float(w & 0xffff0000u) * __uint_as_float(gw & 0xffff0000u);
+        }
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const uint32_t w = d[i][j];
@@ -1000,6 +1039,8 @@ __global__ void __launch_bounds__(256) k_prep_x(const uint16_t* __restrict__ x, 
         }
     }
     m = __builtin_bit_cast(float, wave_max(__builtin_bit_cast(int, m)));
+    z = wave_sum(z);
+    if (lane == 0) sgate[t] = gate_inp ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
     const int e = row_exp(m);
     u32x4* dst = (u32x4*)(xh + (size_t)t * D);
 #pragma unroll
@@ -1035,8 +1076,9 @@ hipError_t launch_router_gemm(const uint16_t* xh, const int32_t* ex, const uint1
     return hipGetLastError();
 }
 
-hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int32_t* ex, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_prep_x, dim3((T + 3) / 4), dim3(256), 0, s, x, xh, ex, T);
+hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int32_t* ex, const uint16_t* gate_inp, float* sgate, int T,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(k_prep_x, dim3((T + 3) / 4), dim3(256), 0, s, x, xh, ex, gate_inp, sgate, T);
     return hipGetLastError();
 }
 
@@ -1044,7 +1086,8 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     GemmArgs g = {};
     g.xh = p.xh; g.ex = p.ex; g.h = p.h; g.eh = p.eh; g.hs = p.hs; g.ehs = p.ehs; g.ep = p.ep;
     g.shw = p.shw; g.es = p.es;
-    g.perm = p.perm; g.pos_of = p.pos_of; g.offs = p.offs; g.tiles = p.tiles; g.tile_count = p.tile_count;
+    g.perm = p.perm; g.pos_of = p.pos_of; g.offs = p.offs; g.tiles = p.tiles; g.tiles_e = p.tiles_e;
+    g.tile_count = p.tile_count;
     g.wflat = p.wflat; g.sgate = p.sgate;
     g.gu_rows = p.gu_rows;
     g.T = p.T;
@@ -1056,7 +1099,8 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.q[0] = p.gate_q; g.sc[0] = p.gate_s; g.bi[0] = p.gate_b;
     g.q[1] = p.up_q; g.sc[1] = p.up_s; g.bi[1] = p.up_b;
     g.h_out = p.h;
-    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm_gu_wide, grid(max_tiles * (F / (WBN / 2))), dim3(512), 0, s, g);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_gemm_gu_wide, dim3(routed_grid<F / (WBN / 2)>(max_tiles)), dim3(512), 0, s,
+              g);
     // (the shared gate/up ran with the router logits)
     // routed down
     g.q[0] = p.down_q; g.sc[0] = p.down_s; g.bi[0] = p.down_b;

@@ -114,12 +114,12 @@ __global__ void __launch_bounds__(256) k_prep_weights(const float* __restrict__ 
     if (lane == 0) es[r] = e;
 }
 
-// One wave per token: top-8 of the 256 logits, renormalised softmax weights,
-// and sgate.  Lane l holds experts l, l+64, l+128, l+192.
+// One wave per token: top-8 of the 256 logits (or the hash table's
+// experts) and their renormalised weights.  Lane l holds experts l, l+64,
+// l+128, l+192.
 template <bool HASH>
-__global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, const uint16_t* __restrict__ x,
-                                              const uint16_t* __restrict__ gate_inp, int32_t* __restrict__ idx_out,
-                                              float* __restrict__ w_out, float* __restrict__ sgate_out, float wscale,
+__global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int32_t* __restrict__ idx_out,
+                                              float* __restrict__ w_out, float wscale,
                                               int gating, const int32_t* __restrict__ tid2eid,
                                               const int32_t* __restrict__ token_ids, int n_vocab, int T) {
     const int lane = threadIdx.x & 63;
@@ -150,25 +150,6 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
         idx_out[(size_t)t * K + lane] = iv;
         w_out[(size_t)t * K + lane] = wv;
     }
-    // sgate = sigmoid(gate_inp . x); lane l covers inputs [32l, 32l+32)
-    if (sgate_out) {
-        float z = 0.0f;
-        if (gate_inp) {
-            const u32x4* xp = (const u32x4*)(x + (size_t)t * D + 32 * lane);
-            const u32x4* gp = (const u32x4*)(gate_inp + 32 * lane);
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                u32x4 xv = xp[q], gv = gp[q];
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    z += __uint_as_float(xv[j] << 16) * __uint_as_float(gv[j] << 16);
-                    z += __uint_as_float(xv[j] & 0xffff0000u) * __uint_as_float(gv[j] & 0xffff0000u);
-                }
-            }
-            z = wave_sum(z);
-        }
-        if (lane == 0) sgate_out[t] = gate_inp ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
-    }
 }
 
 hipError_t launch_prep_weights(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
@@ -178,15 +159,14 @@ hipError_t launch_prep_weights(const float* wr, uint16_t* wr2, int32_t* er, cons
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
-                       float* sgate, float wscale, int gating, const int32_t* tid2eid, const int32_t* token_ids,
-                       int n_vocab, int T, hipStream_t s) {
+hipError_t launch_topk(const float* logits, int32_t* idx, float* w, float wscale, int gating, const int32_t* tid2eid,
+                       const int32_t* token_ids, int n_vocab, int T, hipStream_t s) {
     if (tid2eid)
-        hipLaunchKernelGGL(k_topk<true>, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, gate_inp, idx, w, sgate, wscale,
-                           gating, tid2eid, token_ids, n_vocab, T);
+        hipLaunchKernelGGL(k_topk<true>, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx, w, wscale, gating, tid2eid,
+                           token_ids, n_vocab, T);
     else
-        hipLaunchKernelGGL(k_topk<false>, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, gate_inp, idx, w, sgate,
-                           wscale, gating, tid2eid, token_ids, n_vocab, T);
+        hipLaunchKernelGGL(k_topk<false>, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx, w, wscale, gating, tid2eid,
+                           token_ids, n_vocab, T);
     return hipGetLastError();
 }
 

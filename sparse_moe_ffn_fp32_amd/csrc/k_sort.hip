@@ -31,49 +31,138 @@ __global__ void __launch_bounds__(256) k_sort_hist(const int32_t* __restrict__ i
     cnt[blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
 }
 
-// Exclusive scan of 256 ints held one per thread; returns the total.
-__device__ int block_exclusive_scan_256(int v, int* smem, int& total) {
-    const int tid = threadIdx.x;
-    smem[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        int t = tid >= off ? smem[tid - off] : 0;
-        __syncthreads();
-        smem[tid] += t;
-        __syncthreads();
-    }
-    int incl = smem[tid];
-    total = smem[255];
-    __syncthreads();
-    return incl - v;
-}
-
 // One block: per-(block, expert) bases, expert offsets offs[0..E], and the
 // tile map: record i is tiles[4i .. 4i+3] = {expert, first row of the tile
 // within the expert's segment, segment start, rows in the tile (1..bm)};
 // tile_count[0] = number of tiles.
-__global__ void __launch_bounds__(256) k_sort_scan(int32_t* __restrict__ cnt, int nblk, int32_t* __restrict__ offs,
-                                                   int32_t* __restrict__ tiles, int32_t* __restrict__ tile_count,
-                                                   int bm) {
-    __shared__ int smem[256];
-    const int e = threadIdx.x;
-    int run = 0;
-    for (int b = 0; b < nblk; b++) {
-        int c = cnt[b * E + e];
-        cnt[b * E + e] = run;
-        run += c;
+//
+// The records are listed longest first: tiles with four live 32-row groups
+// (every full tile, and partial tiles of more than 96 rows), then three,
+// two, one; inside a class in expert order.  The grouped GEMMs take work
+// item = block id in this order, and blocks are started in id order as
+// compute units free up, so the longest items start first and the short
+// ones fill the tail (list scheduling, longest first).
+constexpr int SCAN_THREADS = 1024;  // four threads per expert for the count passes
+
+// Exclusive scan of the 256 values held by threads 0..255 of a 1024-thread
+// block (every thread calls it; the others pass and get 0); returns the
+// total to every thread.
+__device__ int scan_256_of_1024(int v, int* smem, int& total) {
+    const int tid = threadIdx.x;
+    if (tid < 256) smem[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int t = (tid < 256 && tid >= off) ? smem[tid - off] : 0;
+        __syncthreads();
+        if (tid < 256) smem[tid] += t;
+        __syncthreads();
     }
+    const int incl = tid < 256 ? smem[tid] : 0;
+    total = smem[255];
+    __syncthreads();
+    return tid < 256 ? incl - v : 0;
+}
+
+__global__ void __launch_bounds__(SCAN_THREADS) k_sort_scan(int32_t* __restrict__ cnt, int nblk,
+                                                            int32_t* __restrict__ offs, int32_t* __restrict__ tiles,
+                                                            int32_t* __restrict__ tiles_e,
+                                                            int32_t* __restrict__ tile_count, int bm) {
+    __shared__ int smem[256];
+    __shared__ int part[4][E];     // each quarter's count of every expert
+    __shared__ int start4[E + 1];  // exclusive start of each expert's tiles in the four-group class
+    __shared__ int starte[E + 1];  // the same in expert order
+    __shared__ int s_run[E], s_off[E];
+    const int tid = threadIdx.x, e = tid & (E - 1), qt = tid >> 8;
+    // counts: quarter qt of the block rows, sixteen independent loads at a
+    // time, in both passes
+    const int nq = (nblk + 3) / 4, b_lo = qt * nq, b_hi = min(nblk, b_lo + nq);
+    int run_q = 0;
+    for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) c[i] = b0 + i < b_hi ? cnt[(b0 + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < 16; i++) run_q += c[i];
+    }
+    part[qt][e] = run_q;
+    __syncthreads();
+    const int run = part[0][e] + part[1][e] + part[2][e] + part[3][e];  // expert e's assignments
     int total;
-    const int off = block_exclusive_scan_256(run, smem, total);
-    for (int b = 0; b < nblk; b++) cnt[b * E + e] += off;
-    offs[e] = off;
-    if (e == E - 1) offs[E] = off + run;
-    const int nt = (run + bm - 1) / bm;
+    const int off_s = scan_256_of_1024(tid < 256 ? run : 0, smem, total);
+    if (tid < 256) {
+        s_run[e] = run;
+        s_off[e] = off_s;
+        offs[e] = off_s;
+        if (e == E - 1) offs[E] = off_s + run;
+    }
+    __syncthreads();
+    const int off = s_off[e];
+    int base_b = off;
+    for (int q = 0; q < qt; q++) base_b += part[q][e];
+    for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) c[i] = b0 + i < b_hi ? cnt[(b0 + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            if (b0 + i < b_hi) {
+                cnt[(b0 + i) * E + e] = base_b;
+                base_b += c[i];
+            }
+    }
+    // classes: live 32-row groups of each tile (4 for a full tile)
+    const int n_full = run / bm, part_rows = run - n_full * bm;
+    const int g_part = (part_rows + 31) >> 5;  // 0 when there is no partial tile
+    int cls[4];                                // tiles of this expert with 4, 3, 2, 1 live groups
+    cls[0] = n_full + (g_part == 4);
+#pragma unroll
+    for (int q = 1; q < 4; q++) cls[q] = (g_part == 4 - q);
+    int start[4], tot[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) start[q] = scan_256_of_1024(tid < 256 ? cls[q] : 0, smem, tot[q]);
     int ntot;
-    const int toff = block_exclusive_scan_256(nt, smem, ntot);
-    for (int j = 0; j < nt; j++)
-        *(int4*)&tiles[4 * (toff + j)] = make_int4(e, j * bm, off, min(bm, run - j * bm));
-    if (e == 0) tile_count[0] = ntot;
+    const int toff = scan_256_of_1024(tid < 256 ? n_full + (part_rows > 0) : 0, smem, ntot);
+    if (tid < 256) {
+        start4[e] = start[0];
+        starte[e] = toff;
+        if (e == E - 1) {
+            start4[E] = tot[0];
+            starte[E] = ntot;
+        }
+    }
+    __syncthreads();
+    // four-group class: tile p belongs to the expert whose range holds it
+    for (int p = tid; p < tot[0]; p += SCAN_THREADS) {
+        int lo = 0, hi = E - 1;  // largest x with start4[x] <= p (empty ranges share starts)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (start4[mid] <= p) lo = mid;
+            else hi = mid - 1;
+        }
+        const int j = p - start4[lo];
+        *(int4*)&tiles[4 * p] = make_int4(lo, j * bm, s_off[lo], min(bm, s_run[lo] - j * bm));
+    }
+    // the other classes: at most one (partial) tile per expert
+    if (tid < 256) {
+        int base = tot[0];
+#pragma unroll
+        for (int q = 1; q < 4; q++) {
+            if (cls[q]) *(int4*)&tiles[4 * (base + start[q])] = make_int4(e, n_full * bm, off, part_rows);
+            base += tot[q];
+        }
+        if (e == 0) tile_count[0] = base;
+    }
+    // the same records in expert order (each expert's tiles in row order)
+    for (int p = tid; p < ntot; p += SCAN_THREADS) {
+        int lo = 0, hi = E - 1;  // largest x with starte[x] <= p
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (starte[mid] <= p) lo = mid;
+            else hi = mid - 1;
+        }
+        const int j = p - starte[lo];
+        *(int4*)&tiles_e[4 * p] = make_int4(lo, j * bm, s_off[lo], min(bm, s_run[lo] - j * bm));
+    }
 }
 
 // Stable scatter: perm[pos] = a and pos_of[a] = pos.  Each block walks its
@@ -116,11 +205,12 @@ __global__ void __launch_bounds__(256) k_sort_scatter(const int32_t* __restrict_
     }
 }
 
-hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tile_count,
-                       int32_t* perm, int32_t* pos_of, int bm, hipStream_t s) {
+hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tiles_e,
+                       int32_t* tile_count, int32_t* perm, int32_t* pos_of, int bm, hipStream_t s) {
     const int nblk = (N + SORT_CH - 1) / SORT_CH;
     hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(256), 0, s, idx, cnt, N);
-    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(256), 0, s, cnt, nblk, offs, tiles, tile_count, bm);
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(SCAN_THREADS), 0, s, cnt, nblk, offs, tiles, tiles_e, tile_count,
+                       bm);
     hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(256), 0, s, idx, cnt, perm, pos_of, N);
     return hipGetLastError();
 }

@@ -21,8 +21,8 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 // Byte offsets of every workspace region for T tokens.
 struct Layout {
-    size_t wr2, er, shw, es, logits, idx, w, sgate, xh, ex, cnt, offs, tiles, tile_count, perm, pos_of, h, eh, hs, ehs,
-        partial, ep, total;
+    size_t wr2, er, shw, es, logits, idx, w, sgate, xh, ex, cnt, offs, tiles, tiles_e, tile_count, perm, pos_of, h, eh,
+        hs, ehs, partial, ep, total;
 };
 
 Layout layout(int64_t T) {
@@ -44,6 +44,7 @@ Layout layout(int64_t T) {
     L.cnt = o;        o += up((size_t)nblk * E * 4);
     L.offs = o;       o += up((E + 1) * 4);
     L.tiles = o;      o += up(max_tiles * 4 * 4);
+    L.tiles_e = o;    o += up(max_tiles * 4 * 4);
     L.tile_count = o; o += up(4);
     L.perm = o;       o += up(N * 4);
     L.pos_of = o;     o += up(N * 4);
@@ -175,12 +176,13 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
     chk(launch_prep_weights(router->weight, wr2, er, sh ? sh->gate : nullptr, sh ? sh->up : nullptr,
                             sh ? sh->down : nullptr, shw, es, s));
-    chk(launch_prep_x(x, xh, xe, T, s));
+    chk(launch_prep_x(x, xh, xe, sh ? sh->gate_inp : nullptr, sgate, T, s));
     chk(launch_router_gemm(xh, xe, wr2, er, router->bias, logits, shw, es, (uint16_t*)at(L.hs), (int32_t*)at(L.ehs), T,
                            tr, s));
-    chk(launch_topk(logits, x, sh ? sh->gate_inp : nullptr, idx, w, sgate, weights_scale(router), router->gating,
-                    router->tid2eid, router->token_ids, router->n_vocab, T, s));
-    chk(launch_sort(idx, N, cnt, offs, tiles, tile_count, perm, pos_of, gemm_bm(T), s));
+    chk(launch_topk(logits, idx, w, weights_scale(router), router->gating, router->tid2eid, router->token_ids,
+                    router->n_vocab, T, s));
+    int32_t* tiles_e = (int32_t*)at(L.tiles_e);
+    chk(launch_sort(idx, N, cnt, offs, tiles, tiles_e, tile_count, perm, pos_of, gemm_bm(T), s));
     PrefillGemmParams p{};
     p.xh = xh;
     p.ex = xe;
@@ -195,6 +197,7 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     p.pos_of = pos_of;
     p.offs = offs;
     p.tiles = tiles;
+    p.tiles_e = tiles_e;
     p.tile_count = tile_count;
     p.wflat = w;
     p.sgate = sgate;

@@ -31,14 +31,14 @@ hipError_t launch_prep_weights(const float* wr, uint16_t* wr2, int32_t* er, cons
                                const uint16_t* sd, uint16_t* shw, int32_t* es, hipStream_t s);
 // wscale multiplies every renormalised routing weight
 // tid2eid != nullptr: hash routing with token_ids [T] (n_vocab table columns)
-hipError_t launch_topk(const float* logits, const uint16_t* x, const uint16_t* gate_inp, int32_t* idx, float* w,
-                       float* sgate, float wscale, int gating, const int32_t* tid2eid, const int32_t* token_ids,
-                       int n_vocab, int T, hipStream_t s);
+hipError_t launch_topk(const float* logits, int32_t* idx, float* w, float wscale, int gating, const int32_t* tid2eid,
+                       const int32_t* token_ids, int n_vocab, int T, hipStream_t s);
 
 // ---- routing sort (k_sort.hip)
 int sort_blocks(int N);
-hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tile_count,
-                       int32_t* perm, int32_t* pos_of, int bm, hipStream_t s);
+// tiles: the tile records longest first; tiles_e: the same records in expert order
+hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tiles_e,
+                       int32_t* tile_count, int32_t* perm, int32_t* pos_of, int bm, hipStream_t s);
 
 // ---- grouped GEMMs (k_gemm.hip)
 struct PrefillGemmParams {
@@ -54,7 +54,8 @@ struct PrefillGemmParams {
     const int32_t* perm;
     const int32_t* pos_of;
     const int32_t* offs;
-    const int32_t* tiles;
+    const int32_t* tiles;     // tile records, longest first
+    const int32_t* tiles_e;   // the same records in expert order
     const int32_t* tile_count;
     const float* wflat;
     const float* sgate;
@@ -68,8 +69,10 @@ struct PrefillGemmParams {
     int T;
 };
 int gemm_bm(int T);  // rows per routed tile for a prefill pass of T tokens
-// x bf16 [T, D] -> fp16 xh (perm8) with row exponents ex [T]
-hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int32_t* ex, int T, hipStream_t s);
+// x bf16 [T, D] -> fp16 xh (perm8) with row exponents ex [T]; and the
+// shared-expert gate sgate [T] = sigmoid(gate_inp . x), 1 without gate_inp
+hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int32_t* ex, const uint16_t* gate_inp, float* sgate, int T,
+                         hipStream_t s);
 // router logits, and the shared expert's gate/up + SwiGLU into hs (ehs)
 // when shw != nullptr
 hipError_t launch_router_gemm(const uint16_t* xh, const int32_t* ex, const uint16_t* wr2, const int32_t* er,
