@@ -117,11 +117,12 @@ class Hip:
         return e.value
 
     def elapsed_ms(self, a, b):
-        """Elapsed ms between two events, NaN if they were never recorded."""
-        if self.L.hipEventSynchronize(b) != 0:
-            return float("nan")
+        """Elapsed ms between two events, NaN if they were never recorded
+        (the runtime's error state is cleared again, or the next HIP call
+        would report it)."""
         ms = ctypes.c_float()
-        if self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+        if self.L.hipEventSynchronize(b) != 0 or self.L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            self.L.hipGetLastError()
             return float("nan")
         return ms.value
 

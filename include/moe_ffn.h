@@ -168,6 +168,11 @@ typedef struct {
 
 /* Bytes of device workspace a call with T tokens needs (0 for T == 0; 0 for
  * invalid dims or T); the same for every T >= MOE_FFN_PREFILL_CHUNK_T.  The
+ * workspace holds the intermediates of the path's steps: routing results,
+ * the sort's histograms, offsets and tile map, the gate/up activations and
+ * the per-rank partials (the Lily engine page keeps routing on the GPU,
+ * section "Palikti ekspertu marsrutizavima GPU", and bounds this
+ * intermediate traffic, section "Sumazinti tarpini ir busenos srauta").  The
  * workspace needs no initialisation and carries no state from one call to
  * the next. */
 size_t moe_ffn_workspace_size(const moe_ffn_dims *dims, int64_t T);
@@ -284,7 +289,8 @@ int moe_ffn_forward_noalloc(const moe_ffn_dims *dims, int64_t T, const uint16_t 
                             const moe_ffn_experts *experts, const moe_ffn_shared *shared, uint16_t *y,
                             int32_t *topk_idx, float *topk_weight, void *stream);
 
-/* Static string for a status code. */
+/* Static string for a status code.  (The pages define no error reporting;
+ * these codes are this boundary's own.) */
 const char *moe_ffn_status_string(int status);
 
 #ifdef __cplusplus
