@@ -231,8 +231,12 @@ def main():
             torch.cuda.synchronize()
             wall = time.perf_counter() - t
         else:
-            # single layer: write 1 GiB between repetitions (outside the timed
-            # call) so no weights stay in the caches; time each call with events
+            # single layer: read (or write) 1 GiB between repetitions, outside
+            # the timed call, so no weights stay in the caches; time each call
+            # with events.  A bounded device-side sleep queued before the start
+            # event keeps the GPU busy while the host enqueues the event and
+            # the call (argument checks, ctypes), so the interval holds the
+            # call's GPU execution only.
             step_ms = []
             se, ee = hip.event(), hip.event()
             for s in range(nsteps):
@@ -241,6 +245,7 @@ def main():
                 else:
                     flush_sink.copy_(flush_words.amax(), non_blocking=True)
                 torch.cuda.synchronize()
+                torch.cuda._sleep(int(2.4e9 * 300e-6))  # ~300 us of GPU time
                 hip.record(se, stream)
                 call(0, moe.Trace(kernel, *ev[s]) if kernel is not None else None)
                 hip.record(ee, stream)
