@@ -83,32 +83,6 @@ __device__ inline void write_token_route(const DecodeArgs& a, int t, int lane, c
     }
 }
 
-// One wave: the shared-expert gate of token t, sgate = sigmoid(gate_inp . x)
-// (1 when the layer has no gate vector).
-__device__ inline void write_token_sgate(const DecodeArgs& a, int t, int lane) {
-    float z = 0.0f;
-    if (a.sgi) {
-        const u32x4* xq = (const u32x4*)(a.x + (size_t)t * D + 32 * lane);
-        const u32x4* gp = (const u32x4*)(a.sgi + 32 * lane);
-        u32x4 xv[4], gv[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            xv[q] = xq[q];
-            gv[q] = gp[q];
-        }
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const uint32_t xw = xv[q][j], gw = gv[q][j];
-                z += __uint_as_float(xw << 16) * __uint_as_float(gw << 16);
-                z += __uint_as_float(xw & 0xffff0000u) * __uint_as_float(gw & 0xffff0000u);
-            }
-        z = wave_sum(z);
-    }
-    if (lane == 0) a.sgate[t] = a.sgi ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
-}
-
 
 hipError_t launch_decode_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s);
 

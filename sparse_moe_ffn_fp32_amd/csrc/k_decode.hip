@@ -142,21 +142,44 @@ static_assert(N_ROUTER_GRP % 8 == 0 && N_SGU_GRP % 8 == 0, "a row group's blocks
 
 __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a, int nmt) {
     __shared__ float red[16][16][17];
+    __shared__ float zs[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
     const int b = blockIdx.x;
     const int nr = N_ROUTER_GRP * nmt, ns = N_SGU_GRP * nmt;
-    if (b >= nr + ns) {  // x -> perm8 copy: 4 tokens (1024 pieces of 16 bytes) per block
+    if (b >= nr + ns) {
+        // x -> perm8 copy: 4 tokens (1024 pieces of 16 bytes) per block, and
+        // their shared-expert gate sgate = sigmoid(gate_inp . x) (1 without
+        // a gate vector): thread tid holds piece tid % 256 of token tid / 256,
+        // the token's four waves summed in wave order
         const int i = 1024 * (b - nr - ns) + tid;
-        if (i < T * (D / 8)) {
-            const u32x4 d = ((const u32x4*)a.x)[i];
+        const bool live = i < T * (D / 8);
+        const u32x4 d = ((const u32x4*)a.x)[live ? i : 0];
+        u32x4 g = u32x4{0u, 0u, 0u, 0u};
+        if (a.sgi) g = ((const u32x4*)a.sgi)[tid & (D / 8 - 1)];
+        if (live) {
             u32x4 o;
             o[0] = (d[0] & 0xffffu) | (d[2] << 16);
             o[1] = (d[0] >> 16) | (d[2] & 0xffff0000u);
             o[2] = (d[1] & 0xffffu) | (d[3] << 16);
             o[3] = (d[1] >> 16) | (d[3] & 0xffff0000u);
             ((u32x4*)a.xp)[i] = o;
+        }
+        float z = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t xj = d[j], gj = g[j];
+            z += __uint_as_float(xj << 16) * __uint_as_float(gj << 16);
+            z += __uint_as_float(xj & 0xffff0000u) * __uint_as_float(gj & 0xffff0000u);
+        }
+        z = wave_sum(z);
+        if (lane == 0) zs[wave] = z;
+        __syncthreads();
+        const int t = 4 * (b - nr - ns) + tid;
+        if (tid < 4 && t < T) {
+            const float zt = ((zs[4 * tid] + zs[4 * tid + 1]) + zs[4 * tid + 2]) + zs[4 * tid + 3];
+            a.sgate[t] = a.sgi ? 1.0f / (1.0f + __expf(-zt)) : 1.0f;
         }
         return;
     }
@@ -233,9 +256,10 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a, int nmt) {
 }
 
 // ------------------------------------------------------------------ routing
-// One wave per token: DPP top-8 of the logits, renormalised weights and
-// sgate, with the token's logits, x and gate vector loaded together.  Many
-// small blocks, so the 8T arg-max rounds spread over the chip.
+// One wave per token: DPP top-8 of the logits (or the hash table's column)
+// and the renormalised weights.  Many small blocks, so the 8T arg-max rounds
+// spread over the chip (one block for all tokens made the rounds compete
+// for one compute unit's SIMDs: 11 us slower at 64 tokens).
 template <bool HASH>
 __global__ void __launch_bounds__(256) k_dec_topk(DecodeArgs a) {
     const int lane = threadIdx.x & 63, t = 4 * blockIdx.x + (threadIdx.x >> 6);
@@ -244,7 +268,6 @@ __global__ void __launch_bounds__(256) k_dec_topk(DecodeArgs a) {
     int sel_i[K];
     token_select<HASH>(a, t, lane, sel_v, sel_i);
     write_token_route<HASH>(a, t, lane, sel_v, sel_i, nullptr);
-    write_token_sgate(a, t, lane);
 }
 
 // One block lists the distinct experts in increasing id order, each with its

@@ -47,7 +47,11 @@ namespace moe {
 
 constexpr int TA_ROUTER_BLK = E / 4;  // 4 experts per block (8 waves)
 constexpr int TA_SHARED_BLK = FS / 4; // 4 features (8 rows) per block
-constexpr int TC_FEAT = 8;            // features per routed gate/up block
+// Features per routed gate/up block: 8 up to two tokens, 16 from three (the
+// launch then keeps all of its blocks resident at once and ranks each token
+// half as often); a block of chunk fc reads ahead the 4 * feat down rows
+// 4 feat * fc .. of its expert.
+__host__ __device__ constexpr int tc_feat(int nt) { return nt >= 3 ? 16 : 8; }
 constexpr int TC_SDOWN_BLK = D / 8;   // shared-down blocks, 8 rows each
 constexpr int TD_ROWS = 8;            // output rows per down block
 constexpr int TD_THREADS = 512;       // threads per down block (8 waves)
@@ -324,10 +328,11 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
             }
         return;
     }
-    // routed gate/up: pair p = (token t, rank r), features f0 .. f0 + 7
-    const int p = blockIdx.x / (F / TC_FEAT), fc = blockIdx.x % (F / TC_FEAT);
+    // routed gate/up: pair p = (token t, rank r), features f0 .. f0 + FEAT - 1
+    constexpr int FEAT = tc_feat(NT), FW = FEAT / 4, NR = 2 * FW;  // per wave: FW features, NR rows
+    const int p = blockIdx.x / (F / FEAT), fc = blockIdx.x % (F / FEAT);
     const int t = p >> 3, r = p & 7;
-    const int f0 = TC_FEAT * fc;
+    const int f0 = FEAT * fc;
     // x in the codes' K order and its piece sums do not depend on the routing
     u32x4 xv[4];
     const uint16_t* xrow = a.xp + (size_t)t * D + 32 * lane;
@@ -348,55 +353,66 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
     }
     __syncthreads();
     const int e = s_expert & (E - 1);
-    // wave w: features f0 + 2w, f0 + 2w + 1; rows gate f, gate f+1, up f, up f+1
-    const size_t row0 = (size_t)e * a.gu_rows + f0 + 2 * wave;
-    const uint32_t* rows[4] = {a.gq + row0 * (D / 8), a.gq + (row0 + 1) * (D / 8), a.uq + row0 * (D / 8),
-                               a.uq + (row0 + 1) * (D / 8)};
-    const uint16_t* srow[4] = {a.gs + row0 * (D / G), a.gs + (row0 + 1) * (D / G), a.us + row0 * (D / G),
-                               a.us + (row0 + 1) * (D / G)};
-    const uint16_t* brow[4] = {a.gb + row0 * (D / G), a.gb + (row0 + 1) * (D / G), a.ub + row0 * (D / G),
-                               a.ub + (row0 + 1) * (D / G)};
+    // wave w: features f0 + FW w .. f0 + FW w + FW - 1; rows q < FW: gate of
+    // feature q, q >= FW: up of feature q - FW
+    const size_t row0 = (size_t)e * a.gu_rows + f0 + FW * wave;
     // lane piece: 32 codes at K = 32 lane (4 u32), group lane / 2
-    u32x4 cv[4];
-    uint32_t sv[4], bv[4];
+    u32x4 cv[NR];
+    uint32_t sv[NR], bv[NR];
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-        cv[q] = *(const u32x4*)(rows[q] + 4 * lane);
-        sv[q] = *(const uint32_t*)(srow[q] + 2 * (lane >> 2));
-        bv[q] = *(const uint32_t*)(brow[q] + 2 * (lane >> 2));
+    for (int q = 0; q < NR; q++) {
+        const size_t row = row0 + (q % FW);
+        const uint32_t* qp = q < FW ? a.gq : a.uq;
+        const uint16_t* sp = q < FW ? a.gs : a.us;
+        const uint16_t* bp = q < FW ? a.gb : a.ub;
+        cv[q] = *(const u32x4*)(qp + row * (D / 8) + 4 * lane);
+        sv[q] = *(const uint32_t*)(sp + row * (D / G) + 2 * (lane >> 2));
+        bv[q] = *(const uint32_t*)(bp + row * (D / G) + 2 * (lane >> 2));
     }
-    // Down rows 32 fc .. 32 fc + 31 of this pair's expert, which stage D reads
-    // next: one dword per 64 bytes (8 KB of codes, 512 B each of scales and
-    // biases) pulls them into cache in this same round trip.  Stage D's
-    // blocks take these rows on this block's XCD (block id mod 8 = fc mod 8).
-    uint32_t pf = 0;
+    // Down rows 4 FEAT fc .. 4 FEAT fc + 4 FEAT - 1 of this pair's expert,
+    // which stage D reads next: one dword per 64 bytes (FEAT KB of codes,
+    // FEAT / 16 KB each of scales and biases) pulls them into cache in this
+    // same round trip.  Stage D's blocks take these rows on this block's XCD
+    // (block id mod 8 = fc mod 8).
+    constexpr int PF_ROWS = 4 * FEAT, PF_CODES = PF_ROWS * (F / 2) / 64, PF_SB = PF_ROWS * (F / G) * 2 / 64;
+    static_assert(PF_CODES <= 256 && 2 * PF_SB <= 256, "at most one code and one scale/bias dword per thread");
+    uint32_t pf = 0, pf2 = 0;
     {
-        const size_t drow0 = (size_t)e * D + 32 * fc;
-        if (tid < 128) pf = a.dq[drow0 * (F / 8) + 16 * tid];
-        else if (tid < 136) pf = *(const uint32_t*)(a.ds + drow0 * (F / G) + 32 * (tid - 128));
-        else if (tid < 144) pf = *(const uint32_t*)(a.db + drow0 * (F / G) + 32 * (tid - 136));
+        const size_t drow0 = (size_t)e * D + PF_ROWS * fc;
+        if (tid < PF_CODES) pf = a.dq[drow0 * (F / 8) + 16 * tid];
+        // the scale and bias dwords: threads from PF_CODES on, wrapping round
+        const int j = (tid + 256 - PF_CODES) & 255;
+        if (j < PF_SB) pf2 = *(const uint32_t*)(a.ds + drow0 * (F / G) + 32 * j);
+        else if (j < 2 * PF_SB) pf2 = *(const uint32_t*)(a.db + drow0 * (F / G) + 32 * (j - PF_SB));
     }
     __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
-    float out[4];
+    float out[NR];
     const int g = lane >> 1;
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
+    for (int q = 0; q < NR; q++) {
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++) acc = dot_codes_bf16(cv[q][i], xv[i], acc);
         const float s = group_param(sv[q], g), bb = group_param(bv[q], g);
         out[q] = wave_sum(s * acc + (bb - 128.0f * s) * xs);
     }
-    if (lane < 2) {
-        const int f = f0 + 2 * wave + lane;
-        const float hv = silu_f32(lane ? out[1] : out[0]) * (lane ? out[3] : out[2]);
+    if (lane < FW) {
+        float og = out[0], ou = out[FW];
+#pragma unroll
+        for (int i = 1; i < FW; i++)
+            if (lane == i) {
+                og = out[i];
+                ou = out[FW + i];
+            }
+        const int f = f0 + FW * wave + lane;
+        const float hv = silu_f32(og) * ou;
         const int pc = (f & ~7) | perm8_pos(f & 7);
         uint16_t hh, hlo;
         split_bf16(hv, hh, hlo);
         a.h[(size_t)p * F + pc] = hh;
         a.hl[(size_t)p * F + pc] = hlo;
     }
-    asm volatile("" ::"v"(pf));  // the prefetch completes before the wave ends
+    asm volatile("" ::"v"(pf), "v"(pf2));  // the prefetch completes before the wave ends
 }
 
 // ------------------------------------------------------------------ D
@@ -409,10 +425,11 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int T = NT, NP = T * K;
     // Row tile: block id b runs on XCD b % 8; stage C's block for feature
-    // chunk fc (rows 32 fc .. +31, row tiles 4 fc .. 4 fc + 3) ran on XCD
-    // fc % 8, so b takes a row tile of a chunk with fc % 8 = b % 8.
+    // chunk fc (rows 4 FEAT fc .., row tiles TPC fc .. TPC fc + TPC - 1) ran
+    // on XCD fc % 8, so b takes a row tile of a chunk with fc % 8 = b % 8.
+    constexpr int TPC = tc_feat(NT) * 4 / TD_ROWS;  // row tiles per chunk
     const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
-    const int o0 = TD_ROWS * (32 * (jb >> 2) + 4 * xcd + (jb & 3));
+    const int o0 = TD_ROWS * (TPC * (8 * (jb / TPC) + xcd) + jb % TPC);
     // Every load of the block is issued before any is waited for, in the
     // order of use: the expert ids, h, the codes, the combine's operands.
     // Loads sit under no lane-dependent branch (the compiler would wait for
@@ -518,7 +535,7 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
 
 template <int NT>
 hipError_t launch_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
-    const int n_gu = NT * K * (F / TC_FEAT);
+    const int n_gu = NT * K * (F / tc_feat(NT));
     const dim3 ga(TA_ROUTER_BLK + TA_SHARED_BLK + 1);
     if (a.nw)
         tr.launch(MOE_FFN_KERNEL_ROUTER, k_tiny_a<NT, true>, ga, dim3(512), 0, s, a);
