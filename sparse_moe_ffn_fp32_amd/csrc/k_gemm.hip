@@ -106,7 +106,17 @@ struct GemmCfg {
     static constexpr int R = Q4 ? 4 : 2;     // register ring stages (loads run R-1 steps ahead)
     static constexpr int NB = MODE == MODE_ROUTER ? E / 128
                             : GATED ? (MODE == MODE_GU ? F : FS) / 128 : D / GEMM_BN;  // column blocks
+    static constexpr int NB_XCD = MODE == MODE_SGU ? 2 : NB;  // column blocks per XCD (16-bit modes)
+    static_assert(NB % NB_XCD == 0 && 8 % (NB / NB_XCD) == 0, "column groups divide the XCDs");
 };
+
+// Blocks of a 16-bit-mode launch over n_tiles row tiles (the mapping of
+// gemm_block: every XCD gets slots for its rectangle).
+template <int MODE>
+__host__ __device__ constexpr int dense_grid(int n_tiles) {
+    constexpr int GRP = GemmCfg<MODE>::NB / GemmCfg<MODE>::NB_XCD, PARTS = 8 / GRP;
+    return 8 * ((n_tiles + PARTS - 1) / PARTS) * GemmCfg<MODE>::NB_XCD;
+}
 
 struct GemmArgs {
     // activations, fp16 rows each with its power-of-two exponent
@@ -167,40 +177,49 @@ struct GemmSmem {
 // One block's work; `bid` is the block's index within its mode's grid
 // (a multiple-of-8 offset from blockIdx.x, so bid % 8 is still the XCD).
 //
-// Wave w computes all 128 activation rows against LDS weight rows
-// [64w, 64w + 64): two 32-row tiles nt, acc[mt][nt] for activation rows
-// [32mt, 32mt + 32).  Paired modes map LDS row 64w + 32nt + j to gate
-// (nt = 0) or up (nt = 1) of feature 32w + j of the block (ROUTER: the hi
-// or lo plane of expert 32w + j), so one lane holds both values of a feature.
+// 8 waves, two per SIMD (GEMM_THREADS): wave w = (wm, wn) = (w / 4, w % 4)
+// computes activation rows [64wm, 64wm + 64) against LDS weight rows
+// [64wn, 64wn + 64): 32-row tiles acc[mt][nt] for activation rows
+// 64wm + 32mt and weight rows 64wn + 32nt.  Paired modes map LDS row
+// 64wn + 32nt + j to gate (nt = 0) or up (nt = 1) of feature 32wn + j of the
+// block (ROUTER: the hi or lo plane of expert 32wn + j), so one lane holds
+// both values of a feature.  (With four waves, one per SIMD, each wave
+// computing all 128 rows, every LDS wait and barrier left the matrix pipe
+// idle: about 48 us per block against 16 us of MFMAs.)
+constexpr int GEMM_THREADS = 512;
 template <int MODE>
 __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm, int bid) {
     using C = GemmCfg<MODE>;
     static_assert(!C::Q4, "the 4-bit modes run in gemm_block_gu_wide / gemm_block_down_wide");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
     const int l32 = lane & 31, kq = lane >> 5;
 
     // ---- which (row tile, column block) this block owns.  Workgroups are
-    // dealt to the 8 XCDs round-robin by id; id p is remapped so that XCD
-    // p%8 takes one contiguous run of the live (tile, column block) items,
-    // column block fastest: the blocks sharing a tile's activations, and the
-    // tiles sharing an expert's weights, then meet in the same L2.
+    // dealt to the 8 XCDs round-robin by id (XCD bid % 8).  Each XCD owns a
+    // rectangle of the (tile, column block) grid, small enough in columns
+    // that its weights stay in the XCD's 4 MB L2 (router 2 MB, shared down
+    // 2 MB: every column block; shared gate/up 4 MB: two of its four
+    // blocks), and runs it tile by tile, column block fastest, so the blocks
+    // sharing a tile's activations meet in that L2 too.
     constexpr int NB = C::NB;
+    constexpr int NGX = C::NB_XCD, GRP = NB / NGX, PARTS = 8 / GRP;
     const int n_tiles = (g.T + GEMM_BM - 1) / GEMM_BM;
-    const int live = n_tiles * NB, per_xcd = (live + 7) >> 3;
-    const int slot = bid >> 3, item = (bid & 7) * per_xcd + slot;
-    if (slot >= per_xcd || item >= live) return;
-    const int tile = item / NB, nblk = item % NB;
+    const int tpp = (n_tiles + PARTS - 1) / PARTS;  // tiles per XCD
+    const int x = bid & 7, slot = bid >> 3;
+    const int tile = (x / GRP) * tpp + slot / NGX, nblk = (x % GRP) * NGX + slot % NGX;
+    if (slot >= tpp * NGX || tile >= n_tiles) return;
     const int m0 = tile * GEMM_BM;
     const int rows = min(GEMM_BM, g.T - m0);  // >= 1 for tile < n_tiles
 
-    // ---- A: this thread loads 16 bytes (chunk ac) of rows ar0 + 32i, i < 4;
+    // ---- A: this thread loads 16 bytes (chunk ac) of rows ar0 + 64i, i < 2;
     // rows past the end repeat the last valid row (their results are dropped)
     const int ac = tid & 7, ar0 = tid >> 3;
-    const uint16_t* apt[4];
+    const uint16_t* apt[2];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int r = min(ar0 + 32 * i, rows - 1);
+    for (int i = 0; i < 2; i++) {
+        const int r = min(ar0 + 64 * i, rows - 1);
         const uint16_t* p;
         if constexpr (MODE == MODE_SGU || MODE == MODE_ROUTER) p = g.xh + (size_t)(m0 + r) * D;
         else p = g.hs + (size_t)(m0 + r) * FS;
@@ -208,7 +227,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     }
 
     // ---- B: this thread covers lane half bh (K [32bh, 32bh+32) of a step) of
-    // LDS weight rows br0 and br0 + 128, fp16 rows of the prepared arrays
+    // LDS weight row br0, an fp16 row of the prepared arrays
     const int bh = tid & 1, br0 = tid >> 1;
     auto wrow = [&](int n) -> const uint16_t* {  // global fp16 weight row of LDS row n
         if constexpr (C::PAIRED) {
@@ -220,9 +239,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
             return g.shw + 2 * (size_t)FS * D + (size_t)(nblk * GEMM_BN + n) * FS;           // shared down
         }
     };
-    const u32x4* bpt[2];
-#pragma unroll
-    for (int i = 0; i < 2; i++) bpt[i] = (const u32x4*)wrow(br0 + 128 * i) + 4 * bh;
+    const u32x4* bpt = (const u32x4*)wrow(br0) + 4 * bh;
 
     // ---- the activation rows' exponents; SDOWN: the shared h rows come in
     // four 128-feature pieces with exponents of their own, brought to the
@@ -248,8 +265,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     if constexpr (MODE == MODE_SDOWN) {
         const int pblk = (nblk * GEMM_BN) / 512;  // the partials' 512-column exponent block
 #pragma unroll
-        for (int i = 0; i < GEMM_BM * K / 256; i++) {
-            const int q = tid + 256 * i;
+        for (int i = 0; i < GEMM_BM * K / GEMM_THREADS; i++) {
+            const int q = tid + GEMM_THREADS * i;
             const int pos = g.pos_of[(size_t)(m0 + min(q / K, rows - 1)) * K + q % K];
             sm.pos[q] = pos;
             sm.epp[q] = g.ep[(size_t)pos * 4 + pblk];
@@ -257,74 +274,73 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     }
     __syncthreads();  // exponents and factors before the first A store
 
-    f32x16 acc[4][2];
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; mt++)
+    for (int mt = 0; mt < 2; mt++)
 #pragma unroll
         for (int nt = 0; nt < 2; nt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[mt][nt][v] = 0.0f;
 
-    // Eight MFMAs per 32-row group and sub-step kk against the activation
-    // tile in LDS buffer abuf.
+    // Four MFMAs per sub-step kk against the activation tile in LDS buffer
+    // abuf; the fragments of sub-step kk + 1 are read before the MFMAs of kk.
     auto mfma_step = [&](int abuf, const f16x8 (&bf)[2][4]) {
-        const f16* ab = &sm.a[abuf][l32 * LDSB + 32 * kq];
+        const f16* ab = &sm.a[abuf][(64 * wm + l32) * LDSB + 32 * kq];
+        f16x8 af[2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++) af[0][mt] = *(const f16x8*)(ab + mt * 32 * LDSB);
 #pragma unroll
         for (int kk = 0; kk < 4; kk++) {
-            f16x8 af[4];
+            if (kk < 3)
 #pragma unroll
-            for (int mt = 0; mt < 4; mt++) af[mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * kk);
+                for (int mt = 0; mt < 2; mt++) af[(kk + 1) & 1][mt] = *(const f16x8*)(ab + mt * 32 * LDSB + 8 * (kk + 1));
 #pragma unroll
-            for (int mt = 0; mt < 4; mt++)
+            for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                 for (int nt = 0; nt < 2; nt++)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt][kk], acc[mt][nt], 0, 0, 0);
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk & 1][mt], bf[nt][kk], acc[mt][nt], 0, 0, 0);
         }
     };
 
-    // ---- operands: global -> registers one step ahead -> LDS
+    // ---- operands: global -> registers R - 1 steps ahead -> LDS
     constexpr int R = 2;
     static_assert(C::NK % R == 0, "K steps must be a multiple of the ring size");
-    struct Stage { u32x4 a[4]; u32x4 b[2][4]; };
+    struct Stage { u32x4 a[2]; u32x4 b[4]; };
     auto load = [&](int k, Stage& st) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) st.a[i] = *(const u32x4*)(apt[i] + k * BK);
+        for (int i = 0; i < 2; i++) st.a[i] = *(const u32x4*)(apt[i] + k * BK);
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int w = 0; w < 4; w++) st.b[i][w] = bpt[i][8 * k + w];
+        for (int w = 0; w < 4; w++) st.b[w] = bpt[8 * k + w];
     };
     auto store = [&](const Stage& st, int k, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 2; i++) {
             u32x4 v = st.a[i];
             if constexpr (MODE == MODE_SDOWN) {  // this 128-feature piece to the row's exponent
-                const f16x2 f = __builtin_bit_cast(f16x2, sm.fac[ar0 + 32 * i][k >> 1]);
+                const f16x2 f = __builtin_bit_cast(f16x2, sm.fac[ar0 + 64 * i][k >> 1]);
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     const uint32_t vj = v[j];
                     v[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, vj) * f);
                 }
             }
-            *(u32x4*)&sm.a[buf][(ar0 + 32 * i) * LDSB + 8 * ac] = v;
+            *(u32x4*)&sm.a[buf][(ar0 + 64 * i) * LDSB + 8 * ac] = v;
         }
+        f16* dst = &sm.b[buf][br0 * LDSB + 32 * bh];
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            f16* dst = &sm.b[buf][(br0 + 128 * i) * LDSB + 32 * bh];
-#pragma unroll
-            for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = st.b[i][w];
-        }
+        for (int w = 0; w < 4; w++) *(u32x4*)(dst + 8 * w) = st.b[w];
     };
     auto read_b = [&](int buf, f16x8 (&bf)[2][4]) {
 #pragma unroll
         for (int nt = 0; nt < 2; nt++) {
-            const f16* bb = &sm.b[buf][(64 * wave + 32 * nt + l32) * LDSB + 32 * kq];
+            const f16* bb = &sm.b[buf][(64 * wn + 32 * nt + l32) * LDSB + 32 * kq];
 #pragma unroll
             for (int kk = 0; kk < 4; kk++) bf[nt][kk] = *(const f16x8*)(bb + 8 * kk);
         }
     };
     Stage ring[R];
-    load(0, ring[0]);
+#pragma unroll
+    for (int k = 0; k < R - 1; k++) load(k, ring[k]);
     store(ring[0], 0, 0);
     __syncthreads();
 #pragma unroll 1
@@ -332,7 +348,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
 #pragma unroll
         for (int j = 0; j < R; j++) {
             const int k = k0 + j;
-            load(min(k + 1, C::NK - 1), ring[(j + 1) % R]);
+            load(min(k + R - 1, C::NK - 1), ring[(j + R - 1) % R]);
             __builtin_amdgcn_sched_barrier(0);
             f16x8 bf[2][4];
             read_b(j & 1, bf);
@@ -345,13 +361,13 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
     // ---- epilogues (the loop ended with a barrier: the operand tiles are
     // free).  Accumulator element v of acc[mt][nt] is activation row
     // r = 32mt + 8(v/4) + 4kq + v%4 and LDS weight row 64w + 32nt + l32.
-    auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
+    auto acc_row = [&](int mt, int v) { return 64 * wm + mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
     if constexpr (MODE == MODE_ROUTER) {
-        const int ex = nblk * 128 + 32 * wave + l32;
+        const int ex = nblk * 128 + 32 * wn + l32;
         const float b = g.rbias ? g.rbias[ex] : 0.0f;
         const int ew = g.er[ex];
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++)
+        for (int mt = 0; mt < 2; mt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int r = acc_row(mt, v);
@@ -365,10 +381,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
         constexpr int HS = 128 + 4;
         static_assert(GEMM_BM * HS * sizeof(float) <= offsetof(GemmSmem<MODE>, ea), "h tile must fit a, b");
         float* hb = (float*)&sm.a[0][0];
-        const int f = 32 * wave + l32;  // feature inside the block
+        const int f = 32 * wn + l32;  // feature inside the block
         const int eg = g.es[nblk * 128 + f], eu = g.es[FS + nblk * 128 + f];
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++)
+        for (int mt = 0; mt < 2; mt++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int r = acc_row(mt, v);
@@ -379,11 +395,11 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
         uint16_t* const hs_out = pinned(g.hs_out);
         int32_t* const ehs = pinned(g.ehs);
         __syncthreads();
-        // 128 rows x 16 pieces: thread tid takes rows tid/16 + 16i, piece tid%16
+        // 128 rows x 16 pieces: thread tid takes rows tid/16 + 32i, piece tid%16
         const int c = tid & 15, rb = tid >> 4;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int r = rb + 16 * i;
+        for (int i = 0; i < GEMM_BM * 16 / GEMM_THREADS; i++) {
+            const int r = rb + 32 * i;
             const f32x4 p0 = *(const f32x4*)&hb[r * HS + 8 * c], p1 = *(const f32x4*)&hb[r * HS + 8 * c + 4];
             const float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
             float m = 0.0f;
@@ -404,13 +420,13 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
         float* yb = (float*)&sm.a[0][0];  // 128 x 132 fp32 = 67.6 KB
 #pragma unroll
         for (int pass = 0; pass < 2; pass++) {
-            if ((wave >> 1) == pass) {
+            if ((wn >> 1) == pass) {
 #pragma unroll
                 for (int nt = 0; nt < 2; nt++) {
-                    const int col = 64 * (wave & 1) + 32 * nt + l32;
+                    const int col = 64 * (wn & 1) + 32 * nt + l32;
                     const int ew = g.es[2 * FS + nblk * GEMM_BN + pass * 128 + col];
 #pragma unroll
-                    for (int mt = 0; mt < 4; mt++)
+                    for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                         for (int v = 0; v < 16; v++) {
                             const int r = acc_row(mt, v);
@@ -419,20 +435,21 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
                 }
             }
             __syncthreads();
-            // 128 rows x 16 pieces of 8 outputs, four rows at a time: every
-            // load of the four (8 partials, residual, gate each) is issued
+            // 128 rows x 16 pieces of 8 outputs, CB rows per thread at a time:
+            // every load of the CB (8 partials, residual, gate each) is issued
             // before any is used; rows past the end load the last valid row
             // and store nothing
+            constexpr int CB = 2;
             const uint16_t* const p_in = pinned(g.p_in);
             const uint16_t* const resid = pinned(g.resid);
             uint16_t* const yo = pinned(g.y);
 #pragma unroll 1
-            for (int i0 = 0; i0 < 8; i0 += 4) {
-                u32x4 pv[4][K], rv[4];
-                float sg[4];
+            for (int i0 = 0; i0 < GEMM_BM * 16 / GEMM_THREADS; i0 += CB) {
+                u32x4 pv[CB][K], rv[CB];
+                float sg[CB];
 #pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    const int pc = tid + 256 * (i0 + u), r = min(pc >> 4, rows - 1), c = pc & 15;
+                for (int u = 0; u < CB; u++) {
+                    const int pc = tid + GEMM_THREADS * (i0 + u), r = min(pc >> 4, rows - 1), c = pc & 15;
                     const int t = m0 + r, o = nblk * GEMM_BN + pass * 128 + 8 * c;
 #pragma unroll
                     for (int rr = 0; rr < K; rr++) pv[u][rr] = *(const u32x4*)&p_in[(size_t)sm.pos[r * K + rr] * D + o];
@@ -440,8 +457,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
                     sg[u] = g.sgate[t];
                 }
 #pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    const int pc = tid + 256 * (i0 + u), r = pc >> 4, c = pc & 15;
+                for (int u = 0; u < CB; u++) {
+                    const int pc = tid + GEMM_THREADS * (i0 + u), r = pc >> 4, c = pc & 15;
                     const int rl = min(r, rows - 1);
                     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -968,7 +985,7 @@ __global__ void __launch_bounds__(512) k_gemm_gu_wide(GemmArgs g) {
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
+__global__ void __launch_bounds__(GEMM_THREADS) k_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) GemmSmem<MODE> sm;
     gemm_block<MODE>(g, sm, blockIdx.x);
 }
@@ -978,7 +995,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
 // gate/up (either alone fills only part of the chip at a few thousand tokens).
 constexpr size_t ROUTER_SGU_SMEM = sizeof(GemmSmem<MODE_ROUTER>) > sizeof(GemmSmem<MODE_SGU>)
                                        ? sizeof(GemmSmem<MODE_ROUTER>) : sizeof(GemmSmem<MODE_SGU>);
-__global__ void __launch_bounds__(256) k_gemm_router_sgu(GemmArgs g, int n_router) {
+__global__ void __launch_bounds__(GEMM_THREADS) k_gemm_router_sgu(GemmArgs g, int n_router) {
     __shared__ __attribute__((aligned(16))) char sm[ROUTER_SGU_SMEM];
     if ((int)blockIdx.x < n_router)
         gemm_block<MODE_ROUTER>(g, *reinterpret_cast<GemmSmem<MODE_ROUTER>*>(sm), blockIdx.x);
@@ -1065,13 +1082,14 @@ hipError_t launch_router_gemm(const uint16_t* xh, const int32_t* ex, const uint1
     GemmArgs g = {};
     g.xh = xh; g.ex = ex; g.wr2 = wr2; g.er = er; g.rbias = bias; g.logits = logits; g.T = T;
     const int mt = (T + GEMM_BM - 1) / GEMM_BM;
-    const int n_router = 8 * ((mt * (E / 128) + 7) / 8);
+    const int n_router = dense_grid<MODE_ROUTER>(mt);
     if (shw) {
         g.shw = shw; g.es = es; g.hs_out = hs; g.ehs = ehs;
-        const int n_sgu = 8 * ((mt * (FS / 128) + 7) / 8);
-        tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm_router_sgu, dim3(n_router + n_sgu), dim3(256), 0, s, g, n_router);
+        const int n_sgu = dense_grid<MODE_SGU>(mt);
+        tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm_router_sgu, dim3(n_router + n_sgu), dim3(GEMM_THREADS), 0, s, g,
+                  n_router);
     } else {
-        tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm<MODE_ROUTER>, dim3(n_router), dim3(256), 0, s, g);
+        tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm<MODE_ROUTER>, dim3(n_router), dim3(GEMM_THREADS), 0, s, g);
     }
     return hipGetLastError();
 }
@@ -1109,7 +1127,8 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     // combine
     if (p.shw) {
         g.p_in = p.partial; g.y = p.y; g.resid = p.resid;
-        tr.launch(MOE_FFN_KERNEL_COMBINE, k_gemm<MODE_SDOWN>, grid(mt * (D / GEMM_BN)), dim3(256), 0, s, g);
+        tr.launch(MOE_FFN_KERNEL_COMBINE, k_gemm<MODE_SDOWN>, dim3(dense_grid<MODE_SDOWN>(mt)), dim3(GEMM_THREADS), 0,
+                  s, g);
     } else {
         tr.launch(MOE_FFN_KERNEL_COMBINE, k_combine_routed, dim3((p.T * D + 255) / 256), dim3(256), 0, s,
                   (const uint16_t*)p.partial, (const int32_t*)p.ep, (const int32_t*)p.pos_of, p.resid, p.y, p.T);
