@@ -31,18 +31,28 @@ __global__ void __launch_bounds__(256) k_sort_hist(const int32_t* __restrict__ i
     cnt[blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
 }
 
-// One block: per-(block, expert) bases, expert offsets offs[0..E], and the
-// tile map: record i is tiles[4i .. 4i+3] = {expert, first row of the tile
-// within the expert's segment, segment start, rows in the tile (1..bm)};
-// tile_count[0] = number of tiles.
+// One launch after the histograms (a one-block scan launch between them
+// and the scatter had cost 11 us at 4K tokens, all latency):
 //
+// Blocks 0 .. nblk-1 place the assignments of histogram block b: each forms
+// its own bases, base[e] = offs[e] + sum over blocks b' < b of cnt[b'][e],
+// with offs the exclusive scan of the expert totals, then walks its chunk in
+// assignment order (stable), 1024 at a time: perm[pos] = a, pos_of[a] = pos.
+// Ranks among equal experts inside a wave come from ballots on the 8 bits of
+// the expert id, across waves from per-wave counts.
+//
+// Block nblk writes offs[0..E] and the tile map: record i is tiles[4i ..
+// 4i+3] = {expert, first row of the tile within the expert's segment,
+// segment start, rows in the tile (1..bm)}; tile_count[0] = number of tiles.
 // The records are listed longest first: tiles with four live 32-row groups
 // (every full tile, and partial tiles of more than 96 rows), then three,
 // two, one; inside a class in expert order.  The grouped GEMMs take work
-// item = block id in this order, and blocks are started in id order as
-// compute units free up, so the longest items start first and the short
-// ones fill the tail (list scheduling, longest first).
-constexpr int SCAN_THREADS = 1024;  // four threads per expert for the count passes
+// items in this order, and blocks are started in id order as compute units
+// free up, so the longest items start first and the short ones fill the
+// tail (list scheduling, longest first).  tiles_e holds the same records in
+// expert order.
+constexpr int PLACE_THREADS = 1024;  // four threads per expert for the count passes
+constexpr int PLACE_WAVES = PLACE_THREADS / 64;
 
 // Exclusive scan of the 256 values held by threads 0..255 of a 1024-thread
 // block (every thread calls it; the others pass and get 0); returns the
@@ -63,52 +73,106 @@ __device__ int scan_256_of_1024(int v, int* smem, int& total) {
     return tid < 256 ? incl - v : 0;
 }
 
-__global__ void __launch_bounds__(SCAN_THREADS) k_sort_scan(int32_t* __restrict__ cnt, int nblk,
-                                                            int32_t* __restrict__ offs, int32_t* __restrict__ tiles,
-                                                            int32_t* __restrict__ tiles_e,
-                                                            int32_t* __restrict__ tile_count, int bm) {
+// Quarter qt of the histogram rows (thread tid = 256 qt + e): expert e's
+// count over all rows (into part_t[qt][e]) and over the rows before `upto`
+// (into part_p[qt][e]), sixteen independent loads at a time.
+__device__ __forceinline__ void count_quarter(const int32_t* __restrict__ cnt, int nblk, int upto, int (*part_t)[E],
+                                              int (*part_p)[E]) {
+    const int tid = threadIdx.x, e = tid & (E - 1), qt = tid >> 8;
+    const int nq = (nblk + 3) / 4, b_lo = qt * nq, b_hi = min(nblk, b_lo + nq);
+    int t = 0, p = 0;
+    for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) c[i] = b0 + i < b_hi ? cnt[(b0 + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            t += c[i];
+            p += b0 + i < upto ? c[i] : 0;
+        }
+    }
+    part_t[qt][e] = t;
+    if (part_p) part_p[qt][e] = p;
+}
+
+__device__ void place_chunk(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int nblk,
+                            int32_t* __restrict__ perm, int32_t* __restrict__ pos_of, int N) {
     __shared__ int smem[256];
-    __shared__ int part[4][E];     // each quarter's count of every expert
+    __shared__ int part_t[4][E], part_p[4][E];
+    __shared__ int base[E];
+    __shared__ int wcnt[PLACE_WAVES][E];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
+    // this chunk's expert ids, loaded with the counts
+    int eid[SORT_CH / PLACE_THREADS];
+#pragma unroll
+    for (int i = 0; i < SORT_CH / PLACE_THREADS; i++) {
+        const int a = b * SORT_CH + i * PLACE_THREADS + tid;
+        eid[i] = idx[min(a, N - 1)];  // past the end: a copy, never placed
+    }
+    count_quarter(cnt, nblk, b, part_t, part_p);
+    for (int i = tid; i < PLACE_WAVES * E; i += PLACE_THREADS) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const int e = tid & (E - 1);
+    const int total = part_t[0][e] + part_t[1][e] + part_t[2][e] + part_t[3][e];
+    const int before = part_p[0][e] + part_p[1][e] + part_p[2][e] + part_p[3][e];
+    int all;
+    const int off = scan_256_of_1024(tid < 256 ? total : 0, smem, all);
+    if (tid < 256) base[e] = off + before;
+    __syncthreads();
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int i = 0; i < SORT_CH / PLACE_THREADS; i++) {
+        const int a = b * SORT_CH + i * PLACE_THREADS + tid;
+        const bool valid = a < N;
+        const int ea = eid[i];
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; bit++) {
+            const uint64_t bb = __ballot((ea >> bit) & 1);
+            peers &= ((ea >> bit) & 1) ? bb : ~bb;
+        }
+        const int rank = __popcll(peers & lt);
+        if (valid && rank == 0) wcnt[wave][ea] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int pos = base[ea] + rank;
+            for (int w = 0; w < wave; w++) pos += wcnt[w][ea];
+            perm[pos] = a;
+            pos_of[a] = pos;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int add = 0;
+#pragma unroll
+            for (int w = 0; w < PLACE_WAVES; w++) {
+                add += wcnt[w][tid];
+                wcnt[w][tid] = 0;
+            }
+            base[tid] += add;
+        }
+        __syncthreads();
+    }
+}
+
+__device__ void tile_map(const int32_t* __restrict__ cnt, int nblk, int32_t* __restrict__ offs,
+                         int32_t* __restrict__ tiles, int32_t* __restrict__ tiles_e, int32_t* __restrict__ tile_count,
+                         int bm) {
+    __shared__ int smem[256];
+    __shared__ int part_t[4][E];
     __shared__ int start4[E + 1];  // exclusive start of each expert's tiles in the four-group class
     __shared__ int starte[E + 1];  // the same in expert order
     __shared__ int s_run[E], s_off[E];
-    const int tid = threadIdx.x, e = tid & (E - 1), qt = tid >> 8;
-    // counts: quarter qt of the block rows, sixteen independent loads at a
-    // time, in both passes
-    const int nq = (nblk + 3) / 4, b_lo = qt * nq, b_hi = min(nblk, b_lo + nq);
-    int run_q = 0;
-    for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
-        int c[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) c[i] = b0 + i < b_hi ? cnt[(b0 + i) * E + e] : 0;
-#pragma unroll
-        for (int i = 0; i < 16; i++) run_q += c[i];
-    }
-    part[qt][e] = run_q;
+    const int tid = threadIdx.x, e = tid & (E - 1);
+    count_quarter(cnt, nblk, 0, part_t, nullptr);
     __syncthreads();
-    const int run = part[0][e] + part[1][e] + part[2][e] + part[3][e];  // expert e's assignments
+    const int run = part_t[0][e] + part_t[1][e] + part_t[2][e] + part_t[3][e];  // expert e's assignments
     int total;
-    const int off_s = scan_256_of_1024(tid < 256 ? run : 0, smem, total);
+    const int off = scan_256_of_1024(tid < 256 ? run : 0, smem, total);
     if (tid < 256) {
         s_run[e] = run;
-        s_off[e] = off_s;
-        offs[e] = off_s;
-        if (e == E - 1) offs[E] = off_s + run;
-    }
-    __syncthreads();
-    const int off = s_off[e];
-    int base_b = off;
-    for (int q = 0; q < qt; q++) base_b += part[q][e];
-    for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
-        int c[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) c[i] = b0 + i < b_hi ? cnt[(b0 + i) * E + e] : 0;
-#pragma unroll
-        for (int i = 0; i < 16; i++)
-            if (b0 + i < b_hi) {
-                cnt[(b0 + i) * E + e] = base_b;
-                base_b += c[i];
-            }
+        s_off[e] = off;
+        offs[e] = off;
+        if (e == E - 1) offs[E] = off + run;
     }
     // classes: live 32-row groups of each tile (4 for a full tile)
     const int n_full = run / bm, part_rows = run - n_full * bm;
@@ -132,7 +196,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_sort_scan(int32_t* __restrict_
     }
     __syncthreads();
     // four-group class: tile p belongs to the expert whose range holds it
-    for (int p = tid; p < tot[0]; p += SCAN_THREADS) {
+    for (int p = tid; p < tot[0]; p += PLACE_THREADS) {
         int lo = 0, hi = E - 1;  // largest x with start4[x] <= p (empty ranges share starts)
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -153,7 +217,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_sort_scan(int32_t* __restrict_
         if (e == 0) tile_count[0] = base;
     }
     // the same records in expert order (each expert's tiles in row order)
-    for (int p = tid; p < ntot; p += SCAN_THREADS) {
+    for (int p = tid; p < ntot; p += PLACE_THREADS) {
         int lo = 0, hi = E - 1;  // largest x with starte[x] <= p
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -165,53 +229,23 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_sort_scan(int32_t* __restrict_
     }
 }
 
-// Stable scatter: perm[pos] = a and pos_of[a] = pos.  Each block walks its
-// chunk in assignment order, 256 at a time; ranks among equal experts inside
-// a wave come from ballots on the 8 bits of the expert id.
-__global__ void __launch_bounds__(256) k_sort_scatter(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
-                                                      int32_t* __restrict__ perm, int32_t* __restrict__ pos_of, int N) {
-    __shared__ int base[E];
-    __shared__ int wcnt[4][E];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    base[tid] = cnt[blockIdx.x * E + tid];
-#pragma unroll
-    for (int w = 0; w < 4; w++) wcnt[w][tid] = 0;
-    __syncthreads();
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int i = 0; i < SORT_CH / 256; i++) {
-        const int a = blockIdx.x * SORT_CH + i * 256 + tid;
-        const bool valid = a < N;
-        const int e = valid ? idx[a] : 0;
-        uint64_t peers = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < 8; bit++) {
-            uint64_t b = __ballot((e >> bit) & 1);
-            peers &= ((e >> bit) & 1) ? b : ~b;
-        }
-        const int rank = __popcll(peers & lt);
-        if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);
-        __syncthreads();
-        if (valid) {
-            int pos = base[e] + rank;
-            for (int w = 0; w < wave; w++) pos += wcnt[w][e];
-            perm[pos] = a;
-            pos_of[a] = pos;
-        }
-        __syncthreads();
-        base[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
-#pragma unroll
-        for (int w = 0; w < 4; w++) wcnt[w][tid] = 0;
-        __syncthreads();
-    }
+__global__ void __launch_bounds__(PLACE_THREADS) k_sort_place(const int32_t* __restrict__ idx,
+                                                              const int32_t* __restrict__ cnt, int nblk,
+                                                              int32_t* __restrict__ offs, int32_t* __restrict__ tiles,
+                                                              int32_t* __restrict__ tiles_e,
+                                                              int32_t* __restrict__ tile_count,
+                                                              int32_t* __restrict__ perm,
+                                                              int32_t* __restrict__ pos_of, int N, int bm) {
+    if ((int)blockIdx.x == nblk) tile_map(cnt, nblk, offs, tiles, tiles_e, tile_count, bm);
+    else place_chunk(idx, cnt, nblk, perm, pos_of, N);
 }
 
 hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tiles_e,
                        int32_t* tile_count, int32_t* perm, int32_t* pos_of, int bm, hipStream_t s) {
     const int nblk = (N + SORT_CH - 1) / SORT_CH;
     hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(256), 0, s, idx, cnt, N);
-    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(SCAN_THREADS), 0, s, cnt, nblk, offs, tiles, tiles_e, tile_count,
-                       bm);
-    hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(256), 0, s, idx, cnt, perm, pos_of, N);
+    hipLaunchKernelGGL(k_sort_place, dim3(nblk + 1), dim3(PLACE_THREADS), 0, s, idx, cnt, nblk, offs, tiles, tiles_e,
+                       tile_count, perm, pos_of, N, bm);
     return hipGetLastError();
 }
 
