@@ -38,7 +38,7 @@
 //     block's start), one step ahead of the MFMAs that use them (8-wave
 //     blocks: in the step itself, the other wave of the SIMD covering it);
 //   16-bit weights (shared expert, router planes): fp16 rows prepared per
-//     call (k_prep_weights), staged in LDS and read back as fragments.
+//     call (k_prep), staged in LDS and read back as fragments.
 // Global loads run ahead in a ring of register stages (three steps for 4-bit
 // weights, one otherwise); activation tiles are double-buffered, code tiles
 // quadruple-buffered; one barrier per step.  Epilogues stage the output tile
@@ -1021,59 +1021,6 @@ __global__ void __launch_bounds__(256) k_combine_routed(const uint16_t* __restri
     y[i] = f32_to_bf16_rne(sum);
 }
 
-// x bf16 [T, D] -> fp16 [T, D] in perm8 order, each row times 2^-ex[t] with
-// its exponent (row_exp of its largest |x|); exact where the scaled value is
-// an fp16 normal.  With the row at hand, also the shared-expert gate
-// (qwen35moe page, "Shared-expert MoE FFN"): sgate[t] = sigmoid(gate_inp . x)
-// (1 when the layer has no gate vector).  One wave per row, lane pieces
-// lane + 64 i.
-__global__ void __launch_bounds__(256) k_prep_x(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
-                                                int32_t* __restrict__ ex, const uint16_t* __restrict__ gate_inp,
-                                                float* __restrict__ sgate, int T) {
-    const int lane = threadIdx.x & 63, t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const u32x4* src = (const u32x4*)(x + (size_t)t * D);
-    u32x4 d[4], gv[4];
-    float m = 0.0f, z = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        d[i] = src[lane + 64 * i];
-        gv[i] = gate_inp ? ((const u32x4*)gate_inp)[lane + 64 * i] : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t w = d[i][j], gw = gv[i][j];
-            z += __uint_as_float(w << 16) * __uint_as_float(gw << 16);
-            z += __uint_as_float(w & 0xffff0000u) * __uint_as_float(gw & 0xffff0000u);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t w = d[i][j];
-            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w << 16)),
-                                                   __builtin_fabsf(__uint_as_float(w & 0xffff0000u))));
-        }
-    }
-    m = __builtin_bit_cast(float, wave_max(__builtin_bit_cast(int, m)));
-    z = wave_sum(z);
-    if (lane == 0) sgate[t] = gate_inp ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
-    const int e = row_exp(m);
-    u32x4* dst = (u32x4*)(xh + (size_t)t * D);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        float f[8];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t w = d[i][j];
-            f[2 * j] = __uint_as_float(w << 16);
-            f[2 * j + 1] = __uint_as_float(w & 0xffff0000u);
-        }
-        dst[lane + 64 * i] = f32x8_to_f16x8_perm_scaled(f, e);
-    }
-    if (lane == 0) ex[t] = e;
-}
-
 int gemm_bm(int) { return GEMM_BM; }  // the routed tiles the sort builds
 
 hipError_t launch_router_gemm(const uint16_t* xh, const int32_t* ex, const uint16_t* wr2, const int32_t* er,
@@ -1091,12 +1038,6 @@ hipError_t launch_router_gemm(const uint16_t* xh, const int32_t* ex, const uint1
     } else {
         tr.launch(MOE_FFN_KERNEL_ROUTER, k_gemm<MODE_ROUTER>, dim3(n_router), dim3(GEMM_THREADS), 0, s, g);
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int32_t* ex, const uint16_t* gate_inp, float* sgate, int T,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(k_prep_x, dim3((T + 3) / 4), dim3(256), 0, s, x, xh, ex, gate_inp, sgate, T);
     return hipGetLastError();
 }
 

@@ -33,13 +33,11 @@ namespace moe {
 //                 range) in shw = [gate FS x D | up FS x D | down D x FS];
 //                 es[row - E] = e.
 // K is in the perm8 order everywhere.
-__global__ void __launch_bounds__(256) k_prep_weights(const float* __restrict__ wr, uint16_t* __restrict__ wr2,
-                                                      int32_t* __restrict__ er, const uint16_t* __restrict__ sg,
-                                                      const uint16_t* __restrict__ su, const uint16_t* __restrict__ sd,
-                                                      uint16_t* __restrict__ shw, int32_t* __restrict__ es, int n_rows) {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= n_rows) return;
+__device__ __forceinline__ void prep_weight_row(const float* __restrict__ wr, uint16_t* __restrict__ wr2,
+                                                int32_t* __restrict__ er, const uint16_t* __restrict__ sg,
+                                                const uint16_t* __restrict__ su, const uint16_t* __restrict__ sd,
+                                                uint16_t* __restrict__ shw, int32_t* __restrict__ es, int row,
+                                                int lane) {
     if (row < E) {
         // 256 pieces of 8 weights: lane takes pieces lane + 64 i
         const f32x4* src = (const f32x4*)(wr + (size_t)row * D);
@@ -114,6 +112,77 @@ __global__ void __launch_bounds__(256) k_prep_weights(const float* __restrict__ 
     if (lane == 0) es[r] = e;
 }
 
+// x bf16 [T, D] -> fp16 [T, D] in perm8 order, each row times 2^-ex[t] with
+// its exponent (row_exp of its largest |x|); exact where the scaled value is
+// an fp16 normal.  With the row at hand, also the shared-expert gate
+// (qwen35moe page, "Shared-expert MoE FFN"): sgate[t] = sigmoid(gate_inp . x)
+// (1 when the layer has no gate vector).  One wave per row, lane pieces
+// lane + 64 i.
+__device__ __forceinline__ void prep_x_row(const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
+                                           int32_t* __restrict__ ex, const uint16_t* __restrict__ gate_inp,
+                                           float* __restrict__ sgate, int t, int lane) {
+    const u32x4* src = (const u32x4*)(x + (size_t)t * D);
+    u32x4 d[4], gv[4];
+    float m = 0.0f, z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        d[i] = src[lane + 64 * i];
+        gv[i] = gate_inp ? ((const u32x4*)gate_inp)[lane + 64 * i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t w = d[i][j], gw = gv[i][j];
+            z += __uint_as_float(w << 16) * __uint_as_float(gw << 16);
+            z += __uint_as_float(w & 0xffff0000u) * __uint_as_float(gw & 0xffff0000u);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t w = d[i][j];
+            m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w << 16)),
+                                                   __builtin_fabsf(__uint_as_float(w & 0xffff0000u))));
+        }
+    }
+    m = __builtin_bit_cast(float, wave_max(__builtin_bit_cast(int, m)));
+    z = wave_sum(z);
+    if (lane == 0) sgate[t] = gate_inp ? 1.0f / (1.0f + __expf(-z)) : 1.0f;
+    const int e = row_exp(m);
+    u32x4* dst = (u32x4*)(xh + (size_t)t * D);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t w = d[i][j];
+            f[2 * j] = __uint_as_float(w << 16);
+            f[2 * j + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+        dst[lane + 64 * i] = f32x8_to_f16x8_perm_scaled(f, e);
+    }
+    if (lane == 0) ex[t] = e;
+}
+
+
+// Both preparations in one launch, one wave per row: blocks [0, nb_w) take
+// the n_rows weight rows, the rest the T rows of x.
+__global__ void __launch_bounds__(256) k_prep(const float* __restrict__ wr, uint16_t* __restrict__ wr2,
+                                              int32_t* __restrict__ er, const uint16_t* __restrict__ sg,
+                                              const uint16_t* __restrict__ su, const uint16_t* __restrict__ sd,
+                                              uint16_t* __restrict__ shw, int32_t* __restrict__ es, int n_rows,
+                                              int nb_w, const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
+                                              int32_t* __restrict__ ex, const uint16_t* __restrict__ gate_inp,
+                                              float* __restrict__ sgate, int T) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if ((int)blockIdx.x < nb_w) {
+        const int row = blockIdx.x * 4 + wave;
+        if (row < n_rows) prep_weight_row(wr, wr2, er, sg, su, sd, shw, es, row, lane);
+    } else {
+        const int t = (blockIdx.x - nb_w) * 4 + wave;
+        if (t < T) prep_x_row(x, xh, ex, gate_inp, sgate, t, lane);
+    }
+}
+
 // One wave per token: top-8 of the 256 logits (or the hash table's
 // experts) and their renormalised weights.  Lane l holds experts l, l+64,
 // l+128, l+192.
@@ -152,10 +221,13 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
     }
 }
 
-hipError_t launch_prep_weights(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
-                               const uint16_t* sd, uint16_t* shw, int32_t* es, hipStream_t s) {
+hipError_t launch_prep(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
+                       const uint16_t* sd, uint16_t* shw, int32_t* es, const uint16_t* x, uint16_t* xh, int32_t* ex,
+                       const uint16_t* gate_inp, float* sgate, int T, hipStream_t s) {
     const int n_rows = E + (sg ? 2 * FS + D : 0);
-    hipLaunchKernelGGL(k_prep_weights, dim3((n_rows + 3) / 4), dim3(256), 0, s, wr, wr2, er, sg, su, sd, shw, es, n_rows);
+    const int nb_w = (n_rows + 3) / 4;
+    hipLaunchKernelGGL(k_prep, dim3(nb_w + (T + 3) / 4), dim3(256), 0, s, wr, wr2, er, sg, su, sd, shw, es, n_rows,
+                       nb_w, x, xh, ex, gate_inp, sgate, T);
     return hipGetLastError();
 }
 

@@ -174,9 +174,8 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
 
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-    chk(launch_prep_weights(router->weight, wr2, er, sh ? sh->gate : nullptr, sh ? sh->up : nullptr,
-                            sh ? sh->down : nullptr, shw, es, s));
-    chk(launch_prep_x(x, xh, xe, sh ? sh->gate_inp : nullptr, sgate, T, s));
+    chk(launch_prep(router->weight, wr2, er, sh ? sh->gate : nullptr, sh ? sh->up : nullptr, sh ? sh->down : nullptr,
+                    shw, es, x, xh, xe, sh ? sh->gate_inp : nullptr, sgate, T, s));
     chk(launch_router_gemm(xh, xe, wr2, er, router->bias, logits, shw, es, (uint16_t*)at(L.hs), (int32_t*)at(L.ehs), T,
                            tr, s));
     chk(launch_topk(logits, idx, w, weights_scale(router), router->gating, router->tid2eid, router->token_ids,

@@ -24,11 +24,14 @@ struct Tracer {
 
 
 // ---- router (k_router.hip)
-// router fp32 -> fp16 hi/lo planes wr2 [2, E, D] with row exponents er [E];
-// shared bf16 (when sg != nullptr) -> fp16 shw [gate | up | down] with row
-// exponents es [2 FS + D]
-hipError_t launch_prep_weights(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
-                               const uint16_t* sd, uint16_t* shw, int32_t* es, hipStream_t s);
+// one launch: router fp32 -> fp16 hi/lo planes wr2 [2, E, D] with row
+// exponents er [E]; shared bf16 (when sg != nullptr) -> fp16 shw [gate | up |
+// down] with row exponents es [2 FS + D]; x bf16 [T, D] -> fp16 xh (perm8)
+// with row exponents ex [T], and the shared-expert gate sgate [T] =
+// sigmoid(gate_inp . x), 1 without gate_inp
+hipError_t launch_prep(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
+                       const uint16_t* sd, uint16_t* shw, int32_t* es, const uint16_t* x, uint16_t* xh, int32_t* ex,
+                       const uint16_t* gate_inp, float* sgate, int T, hipStream_t s);
 // wscale multiplies every renormalised routing weight
 // tid2eid != nullptr: hash routing with token_ids [T] (n_vocab table columns)
 hipError_t launch_topk(const float* logits, int32_t* idx, float* w, float wscale, int gating, const int32_t* tid2eid,
@@ -69,10 +72,6 @@ struct PrefillGemmParams {
     int T;
 };
 int gemm_bm(int T);  // rows per routed tile for a prefill pass of T tokens
-// x bf16 [T, D] -> fp16 xh (perm8) with row exponents ex [T]; and the
-// shared-expert gate sgate [T] = sigmoid(gate_inp . x), 1 without gate_inp
-hipError_t launch_prep_x(const uint16_t* x, uint16_t* xh, int32_t* ex, const uint16_t* gate_inp, float* sgate, int T,
-                         hipStream_t s);
 // router logits, and the shared expert's gate/up + SwiGLU into hs (ehs)
 // when shw != nullptr
 hipError_t launch_router_gemm(const uint16_t* xh, const int32_t* ex, const uint16_t* wr2, const int32_t* er,
