@@ -47,11 +47,13 @@ struct DecodeArgs {
 };
 
 // The experts of token t (top 8 by logit, or looked up in the hash table)
-// with their logits (one wave, result wave-uniform).
+// with their logits (one wave, result wave-uniform); the top-8 form stops
+// after the first `ranks` of them.
 template <bool HASH>
-__device__ __forceinline__ void token_select(const DecodeArgs& a, int t, int lane, float* sel_v, int* sel_i) {
+__device__ __forceinline__ void token_select(const DecodeArgs& a, int t, int lane, float* sel_v, int* sel_i,
+                                             int ranks = K) {
     select_experts<HASH>(a.logits + (size_t)t * E, a.tid2eid, a.n_vocab, HASH ? a.token_ids[t] : 0, lane, sel_v,
-                         sel_i);
+                         sel_i, ranks);
 }
 
 // One wave: write token t's routing, the expert ids and renormalised weights

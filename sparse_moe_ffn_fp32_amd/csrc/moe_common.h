@@ -272,8 +272,9 @@ __device__ __forceinline__ int wave_max(int v) {
 // takes the wave maximum of the heads' order keys and a ballot of the heads
 // that equal it: one such head wins outright, and only equal scores in
 // several lanes need the (score, index) arg-max.  The winning lane advances its head.
-// The results are wave-uniform.
-__device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v, int* sel_i) {
+// The results are wave-uniform.  Only the first `rounds` ranks are formed
+// (wave-uniform, 1..8); later entries of sel_v / sel_i are left unset.
+__device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v, int* sel_i, int rounds = 8) {
     float a[4];
     int ai[4];
 #pragma unroll
@@ -300,6 +301,7 @@ __device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v
     int hi = ai[0], hk = order_key(hv);
 #pragma unroll
     for (int r = 0; r < 8; r++) {
+        if (r >= rounds) break;
         const int mk = wave_max(hk);
         const uint64_t at_max = __ballot(hk == mk);
         float bv;
@@ -329,12 +331,14 @@ __device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v
 // wave-uniform in sel_i / sel_v: the top K by logit (wave_top8), or with a
 // hash table (ds4.c study notes Part 3, MoE trace 3: experts looked up by
 // token id in a precomputed [K, n_vocab] table) column `tok` of the table in
-// table order.  The id and the entries are clamped into range.
+// table order.  The id and the entries are clamped into range.  A caller
+// that needs only the first `ranks` experts may say so: the top-K selection
+// then stops there (the table form sets all K regardless).
 // HASH is a compile-time choice so that the top-K path carries no trace of
 // the table path.
 template <bool HASH>
 __device__ __forceinline__ void select_experts(const float* lrow, const int32_t* tid2eid, int n_vocab, int tok,
-                                               int lane, float* sel_v, int* sel_i) {
+                                               int lane, float* sel_v, int* sel_i, int ranks = K) {
     if constexpr (HASH) {
         tok = min(max(tok, 0), n_vocab - 1);
         const int e = min(max(tid2eid[(size_t)min(lane, K - 1) * n_vocab + tok], 0), E - 1);
@@ -348,7 +352,7 @@ __device__ __forceinline__ void select_experts(const float* lrow, const int32_t*
         float v[4];
 #pragma unroll
         for (int c = 0; c < 4; c++) v[c] = lrow[lane + 64 * c];
-        wave_top8(v, lane, sel_v, sel_i);
+        wave_top8(v, lane, sel_v, sel_i, ranks);
     }
 }
 
