@@ -579,19 +579,24 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     }
 }
 
-// Blocks [0, n_sd) are the shared expert's down projection (first, so they
-// start at once), the routed blocks follow.
-__global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_sd) {
+// Blocks [0, GU_BLOCKS) are the routed workgroups, blocks from GU_BLOCKS on
+// the shared expert's down projection.  A workgroup of this kernel takes a
+// whole compute unit (its register count allows two waves per SIMD), so the
+// routed workgroups come first: all of them start at once, and the shared
+// blocks run on the compute units whose routed workgroup has no items (or
+// finished).  The other order delayed about a hundred routed workgroups by
+// a shared block's lifetime.
+__global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[sizeof(GuSmem)];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
-    if ((int)blockIdx.x < n_sd) {
+    if ((int)blockIdx.x >= GU_BLOCKS) {
         // ---- shared expert down: ys[t, o0+n] = sum_j Wsd[o0+n, j] hs[t, j],
         // hs split into bf16 hi + lo; wave w takes K in [64w, 64w+64)
         if (!a.sg) return;
         float(*sred)[16][16] = (float(*)[16][16])smem;  // [8][16][16]
-        const int o0 = 16 * blockIdx.x;
+        const int o0 = 16 * ((int)blockIdx.x - GU_BLOCKS);
         const int k0 = 64 * wave + 8 * kq;
         const uint16_t* wrow = a.sd + (size_t)(o0 + n) * FS + k0;
         const u32x4 b0 = *(const u32x4*)(wrow), b1 = *(const u32x4*)(wrow + 32);
@@ -630,7 +635,7 @@ __global__ void __launch_bounds__(512) k_dec_stage_c(DecodeArgs a, int n_sd) {
         }
         return;
     }
-    gu_stream(a, (int)blockIdx.x - n_sd, *reinterpret_cast<GuSmem*>(smem));
+    gu_stream(a, (int)blockIdx.x, *reinterpret_cast<GuSmem*>(smem));
 }
 
 // ------------------------------------------------------------------ stage D
@@ -892,7 +897,7 @@ static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s
         hipLaunchKernelGGL(k_dec_topk<false>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
     const int n_sd = a.sg ? N_SDOWN_BLK : 0;
-    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_sd + n_gu), dim3(512), 0, s, a, n_sd);
+    tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_gu + n_sd), dim3(512), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(DN_BLOCKS), dim3(512), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_COMBINE, k_dec_combine, dim3((a.T * D + 255) / 256), dim3(256), 0, s, a);
 }
