@@ -34,11 +34,6 @@ struct DecodeArgs {
     int32_t* idx;
     float* w;
     float* sgate;
-    int32_t* nuniq;  // [1]
-    int32_t* uexp;   // [E]
-    int32_t* ucnt;   // [E]
-    int32_t* uoff;   // [E]
-    int32_t* pairs;  // [8T] (t*8 + r), grouped by distinct expert, t ascending
     const uint16_t* resid;  // bf16 [T, D] added to y before its rounding, or nullptr
     const float* nw;        // T <= TINY_T: RMSNorm weights (x un-normalised), or nullptr
     float eps;

@@ -270,70 +270,88 @@ __global__ void __launch_bounds__(256) k_dec_topk(DecodeArgs a) {
     write_token_route<HASH>(a, t, lane, sel_v, sel_i, nullptr);
 }
 
-// One block lists the distinct experts in increasing id order, each with its
-// (token, rank) pairs in token order.  An assignment's place among equal
+// The distinct experts in increasing id order, each with its (token, rank)
+// pairs in token order, built in LDS by every workgroup of stages C and D
+// from the T*8 expert ids (2 KB): cheaper than a launch of its own between
+// top-k and stage C plus the dependent loads of its lists (expert count,
+// then the lists, then the pairs).  An assignment's place among equal
 // experts comes from ballots over the 8 bits of the expert id (within a
 // wave) plus per-wave counts (across waves).
-__global__ void __launch_bounds__(1024) k_dec_route(DecodeArgs a) {
-    __shared__ int sidx[64 * K];
-    __shared__ int wcnt[8][E];
-    __shared__ int scan_a[E], scan_b[E];
+struct RouteSmem {
+    int wcnt[8][E];     // per-wave counts of each expert, then per-wave offsets
+    int start[E];       // first pair slot of each expert
+    int uexp[E];        // distinct expert u: its id,
+    int ucnt[E];        //   its pair count,
+    int uoff[E];        //   its first pair slot
+    int pairs[64 * K];  // pair ids (t*8 + r) grouped by expert, t ascending
+    int wtot[8];
+    int nu;             // distinct experts
+};
+
+// v + the value lane CTRL names (0 where there is none or the row is masked)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add_from(int v) {
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, true);
+}
+// inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 within each
+// row of 16, then lane 15 into rows 1 and 3, lane 31 into rows 2 and 3
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v = dpp_add_from<0x111, 0xf>(v);
+    v = dpp_add_from<0x112, 0xf>(v);
+    v = dpp_add_from<0x114, 0xf>(v);
+    v = dpp_add_from<0x118, 0xf>(v);
+    v = dpp_add_from<0x142, 0xa>(v);
+    v = dpp_add_from<0x143, 0xc>(v);
+    return v;
+}
+
+// 512 threads, one assignment each (T*8 <= 512); every thread must call it.
+__device__ void build_route(const DecodeArgs& a, RouteSmem& rs) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int T = a.T, N = T * K;
-    if (tid < N) sidx[tid] = a.idx[tid];
-    for (int i = tid; i < 8 * E; i += 1024) (&wcnt[0][0])[i] = 0;
-    __syncthreads();
-    int e = 0, rank = 0;
+    const int N = a.T * K;
     const bool valid = tid < N;
-    if (tid < 64 * K) {  // waves 0..7 hold assignments 0..511
-        e = valid ? sidx[tid] & (E - 1) : 0;
-        uint64_t peers = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < 8; bit++) {
-            const uint64_t bb = __ballot((e >> bit) & 1);
-            peers &= ((e >> bit) & 1) ? bb : ~bb;
-        }
-        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-        rank = __popcll(peers & lt);
-        if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);
-    }
+    const int e = valid ? a.idx[tid] & (E - 1) : 0;
+    for (int i = tid; i < 8 * E; i += 512) (&rs.wcnt[0][0])[i] = 0;
     __syncthreads();
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; bit++) {
+        const uint64_t bb = __ballot((e >> bit) & 1);
+        peers &= ((e >> bit) & 1) ? bb : ~bb;
+    }
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(peers & lt);
+    if (valid && rank == 0) rs.wcnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    // experts tid < E (waves 0..3): per-wave counts -> per-wave offsets and
+    // the total; one scan of (total << 16 | distinct) gives both prefixes
     int cnt = 0;
-    if (tid < E) {  // per-wave counts -> per-wave prefixes, total per expert
+    if (tid < E) {
 #pragma unroll
         for (int w = 0; w < 8; w++) {
-            const int v = wcnt[w][tid];
-            wcnt[w][tid] = cnt;
+            const int v = rs.wcnt[w][tid];
+            rs.wcnt[w][tid] = cnt;
             cnt += v;
         }
-        scan_a[tid] = cnt > 0;
-        scan_b[tid] = cnt;
+    }
+    int incl = wave_incl_scan((cnt << 16) | (cnt > 0));
+    if (lane == 63) rs.wtot[wave] = incl;
+    __syncthreads();
+    if (tid < E) {
+        for (int w = 0; w < wave; w++) incl += rs.wtot[w];
+        const int first = (incl >> 16) - cnt;
+        rs.start[tid] = first;
+        if (cnt > 0) {
+            const int u = (incl & 0xffff) - 1;
+            rs.uexp[u] = tid;
+            rs.ucnt[u] = cnt;
+            rs.uoff[u] = first;
+        }
+        if (tid == E - 1) rs.nu = incl & 0xffff;
     }
     __syncthreads();
-    for (int off = 1; off < E; off <<= 1) {  // inclusive scans over experts
-        int va = 0, vb = 0;
-        if (tid < E && tid >= off) {
-            va = scan_a[tid - off];
-            vb = scan_b[tid - off];
-        }
-        __syncthreads();
-        if (tid < E) {
-            scan_a[tid] += va;
-            scan_b[tid] += vb;
-        }
-        __syncthreads();
-    }
-    if (tid < E && cnt > 0) {
-        const int u = scan_a[tid] - 1;
-        a.uexp[u] = tid;
-        a.ucnt[u] = cnt;
-        a.uoff[u] = scan_b[tid] - cnt;
-    }
-    if (valid) {
-        const int start = e > 0 ? scan_b[e - 1] : 0;
-        a.pairs[start + wcnt[wave][e] + rank] = tid;
-    }
-    if (tid == 0) a.nuniq[0] = scan_a[E - 1];
+    if (valid) rs.pairs[rs.start[e] + rs.wcnt[wave][e] + rank] = tid;
+    __syncthreads();
 }
 
 // ------------------------------------------------------------------ stage C
@@ -370,7 +388,11 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
     const int tk = T * K - 1;
-    const int nu = min(max(a.nuniq[0], 0), min(T * K, E));
+    // the routing lists, in the token tile's space (not yet in use)
+    static_assert(sizeof(RouteSmem) <= sizeof(sm.xs), "routing lists fit the token tile");
+    RouteSmem& rs = *reinterpret_cast<RouteSmem*>(&sm.xs[0][0]);
+    build_route(a, rs);
+    const int nu = min(max(rs.nu, 0), min(T * K, E));
     const int n_items = nu * GU_NCH;
     const int q = (n_items + GU_BLOCKS - 1) / GU_BLOCKS;  // <= GU_ITEMS
     const int i0 = bid * q, i1 = min(i0 + q, n_items);
@@ -381,10 +403,10 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     // ---- unit table: item descriptors in parallel, then units in order
     if (tid < i1 - i0) {
         const int u = (i0 + tid) / GU_NCH;
-        const int cnt = min(max(a.ucnt[u], 1), T);
-        sm.info[tid][0] = a.uexp[u] & (E - 1);
+        const int cnt = min(max(rs.ucnt[u], 1), T);
+        sm.info[tid][0] = rs.uexp[u] & (E - 1);
         sm.info[tid][1] = cnt;
-        sm.info[tid][2] = min(max(a.uoff[u], 0), T * K - cnt);
+        sm.info[tid][2] = min(max(rs.uoff[u], 0), T * K - cnt);
     }
     __syncthreads();
     if (tid == 0) {  // at most 4 items x 4 tiles, from LDS
@@ -411,7 +433,7 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     const int n_units = sm.n_units;
     if (tid < n_units * 16) {  // pair ids of every unit's token slots (slots >= tc repeat the last)
         const int k = tid >> 4, sl = tid & 15;
-        sm.pairs[k][sl] = min(max(a.pairs[sm.unit[k][4] + min(sl, sm.unit[k][2] - 1)], 0), tk);
+        sm.pairs[k][sl] = min(max(rs.pairs[sm.unit[k][4] + min(sl, sm.unit[k][2] - 1)], 0), tk);
     }
     __syncthreads();
 
@@ -670,7 +692,11 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
     const int tk = T * K - 1;
-    const int nu = min(max(a.nuniq[0], 0), min(T * K, E));
+    // the routing lists, in the h tiles' space (not yet in use)
+    static_assert(sizeof(RouteSmem) <= sizeof(sm.hs), "routing lists fit the h tiles");
+    RouteSmem& rs = *reinterpret_cast<RouteSmem*>(&sm.hs[0][0][0][0]);
+    build_route(a, rs);
+    const int nu = min(max(rs.nu, 0), min(T * K, E));
     const int n_items = nu * DN_NCH;
     const int q = (n_items + DN_BLOCKS - 1) / DN_BLOCKS;  // <= DN_ITEMS
     const int i0 = blockIdx.x * q, i1 = min(i0 + q, n_items);
@@ -679,10 +705,10 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
     // ---- unit table: item descriptors in parallel, then units in order
     if (tid < i1 - i0) {
         const int u = (i0 + tid) / DN_NCH;
-        const int cnt = min(max(a.ucnt[u], 1), T);
-        sm.info[tid][0] = a.uexp[u] & (E - 1);
+        const int cnt = min(max(rs.ucnt[u], 1), T);
+        sm.info[tid][0] = rs.uexp[u] & (E - 1);
         sm.info[tid][1] = cnt;
-        sm.info[tid][2] = min(max(a.uoff[u], 0), T * K - cnt);
+        sm.info[tid][2] = min(max(rs.uoff[u], 0), T * K - cnt);
     }
     __syncthreads();
     if (tid == 0) {  // at most 16 items x 4 tiles, from LDS
@@ -711,7 +737,7 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < DN_UNITS * 16 / 512; i++) {
         const int t = tid + 512 * i, k = t >> 4, sl = t & 15;
-        if (k < n_units) sm.pairs[k][sl] = min(max(a.pairs[sm.unit[k][4] + min(sl, sm.unit[k][2] - 1)], 0), tk);
+        if (k < n_units) sm.pairs[k][sl] = min(max(rs.pairs[sm.unit[k][4] + min(sl, sm.unit[k][2] - 1)], 0), tk);
     }
     __syncthreads();
 
@@ -875,11 +901,6 @@ size_t decode_workspace_bytes(int T, DecodeLayout* L) {
     l.idx = o;    o += up((size_t)T * K * 4);
     l.w = o;      o += up((size_t)T * K * 4);
     l.sgate = o;  o += up((size_t)T * 4);
-    l.nuniq = o;  o += up(4);
-    l.uexp = o;   o += up(E * 4);
-    l.ucnt = o;   o += up(E * 4);
-    l.uoff = o;   o += up(E * 4);
-    l.pairs = o;  o += up((size_t)T * K * 4);
     l.xsum = o;   o += up(T <= TINY_T ? (size_t)T * (D / 32) * 4 : 0);
     l.total = o;
     if (L) *L = l;
@@ -895,7 +916,6 @@ static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s
         hipLaunchKernelGGL(k_dec_topk<true>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(k_dec_topk<false>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_dec_route, dim3(1), dim3(1024), 0, s, a);
     const int n_sd = a.sg ? N_SDOWN_BLK : 0;
     tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_gu + n_sd), dim3(512), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(DN_BLOCKS), dim3(512), 0, s, a);
@@ -923,11 +943,6 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     a.idx = p.idx ? p.idx : (int32_t*)(ws + L.idx);
     a.w = p.w ? p.w : (float*)(ws + L.w);
     a.sgate = (float*)(ws + L.sgate);
-    a.nuniq = (int32_t*)(ws + L.nuniq);
-    a.uexp = (int32_t*)(ws + L.uexp);
-    a.ucnt = (int32_t*)(ws + L.ucnt);
-    a.uoff = (int32_t*)(ws + L.uoff);
-    a.pairs = (int32_t*)(ws + L.pairs);
     a.xsum = (float*)(ws + L.xsum);
     a.y = p.y;
     a.resid = p.resid;

@@ -83,7 +83,7 @@ hipError_t launch_rmsnorm(const uint16_t* h, const float* w, float eps, uint16_t
 
 // ---- decode path (k_decode.hip), T <= 64
 struct DecodeLayout {
-    size_t logits, xp, hs, ys, h, part, idx, w, sgate, nuniq, uexp, ucnt, uoff, pairs, xsum, total;
+    size_t logits, xp, hs, ys, h, part, idx, w, sgate, xsum, total;
 };
 struct DecodeParams {
     const uint16_t* x;
