@@ -31,6 +31,7 @@ struct DecodeArgs {
     uint16_t* h;     // bf16 [8T, F] (pair-major), perm8: h rounded to nearest
     uint16_t* hl;    // bf16 [8T, F]: the rounded remainder h - hi (hi + lo: 16 significant bits)
     float* part;     // [8T, D] routed down outputs per pair (T > 4)
+    float* pa;       // T > 4: stage A's K-slice partials [8][T][E + 2 FS] (in part's space)
     int32_t* idx;
     float* w;
     float* sgate;

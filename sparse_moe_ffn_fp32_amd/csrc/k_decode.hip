@@ -126,34 +126,43 @@ __device__ __forceinline__ float group_sum8(const u32x4& v) {
 }
 
 // ------------------------------------------------------------------ stage A
-// Block = (row group, token tile of 16): router groups of SA_ROWS experts,
-// shared groups of SA_ROWS features (their gate and up rows, 16 MFMA
-// columns); wave w takes K in [128w, 128w + 128) and the 16 K-slices are
-// summed in LDS in wave order.  A workgroup can keep only so many bytes in
-// flight, so the work is cut fine enough to spread over the chip (about
-// 64 KB of weights and 64 KB of activations per block at 64 tokens), with
-// the token-tile index in the high part of the block id: the blocks that
-// share a row group run on one XCD and read its weights from HBM once.
-// The last ceil(T / 4) blocks copy x into the K order of the codes.
-constexpr int SA_ROWS = 8;
-constexpr int N_ROUTER_GRP = E / SA_ROWS;
-constexpr int N_SGU_GRP = FS / SA_ROWS;
-static_assert(N_ROUTER_GRP % 8 == 0 && N_SGU_GRP % 8 == 0, "a row group's blocks share an XCD");
+// The router rows (fp32) and the shared expert's gate and up rows (bf16)
+// against every token, with K split over blocks: block = (group of 32 rows,
+// K slice of 256); 8 router groups, 16 gate and 16 up groups, 8 slices each,
+// 320 blocks of 512 threads (two fit a compute unit), each reading at most
+// 32 KB of weights and T x 512 bytes of x.  A compute unit moves only some
+// 20-odd GB/s of loads, so every compute unit has to stream a small share:
+// blocks of (8 rows, 16 tokens) over the whole K read 64 KB of weights and
+// 64 KB of x each, and at 8 tokens only 98 of them existed (8.3 us for
+// 6.3 MB).  Wave w takes the 16-row tile w & 1 and the K sub-slice w >> 1
+// (64 inputs) for every token tile; the four sub-slices are summed in LDS
+// in order and the block's sums leave as partials pa[slice][t][row] (rows:
+// 256 router, 512 gate, 512 up), which the routing launch adds in slice
+// order.  The last ceil(T / 2) blocks copy x into the K order of the codes
+// and form the shared-expert gate.
+constexpr int SA_ROWS = 32;                  // rows per group
+constexpr int SA_KS = 256;                   // K per slice
+constexpr int SA_NS = D / SA_KS;             // slices
+constexpr int SA_NROWS = E + 2 * FS;         // partial rows: router, gate, up
+constexpr int SA_NGRP = SA_NROWS / SA_ROWS;  // 40 groups, the 8 router groups first
+constexpr int SA_NGRP_R = E / SA_ROWS;
+constexpr int SA_BLOCKS = SA_NGRP * SA_NS;
+static_assert(E % SA_ROWS == 0 && FS % SA_ROWS == 0 && SA_KS == 4 * 64, "four 64-input sub-slices per slice");
 
-__global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a, int nmt) {
-    __shared__ float red[16][16][17];
-    __shared__ float zs[16];
+template <int NMT>  // token tiles of 16
+__global__ void __launch_bounds__(512) k_dec_stage_a(DecodeArgs a) {
+    __shared__ float red[4][16 * NMT][SA_ROWS + 1];  // [K sub-slice][token][row]
+    __shared__ float zs[8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int T = a.T;
     const int b = blockIdx.x;
-    const int nr = N_ROUTER_GRP * nmt, ns = N_SGU_GRP * nmt;
-    if (b >= nr + ns) {
-        // x -> perm8 copy: 4 tokens (1024 pieces of 16 bytes) per block, and
+    if (b >= SA_BLOCKS) {
+        // x -> perm8 copy: 2 tokens (512 pieces of 16 bytes) per block, and
         // their shared-expert gate sgate = sigmoid(gate_inp . x) (1 without
         // a gate vector): thread tid holds piece tid % 256 of token tid / 256,
         // the token's four waves summed in wave order
-        const int i = 1024 * (b - nr - ns) + tid;
+        const int i = 512 * (b - SA_BLOCKS) + tid;
         const bool live = i < T * (D / 8);
         const u32x4 d = ((const u32x4*)a.x)[live ? i : 0];
         u32x4 g = u32x4{0u, 0u, 0u, 0u};
@@ -176,82 +185,83 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a, int nmt) {
         z = wave_sum(z);
         if (lane == 0) zs[wave] = z;
         __syncthreads();
-        const int t = 4 * (b - nr - ns) + tid;
-        if (tid < 4 && t < T) {
+        const int t = 2 * (b - SA_BLOCKS) + tid;
+        if (tid < 2 && t < T) {
             const float zt = ((zs[4 * tid] + zs[4 * tid + 1]) + zs[4 * tid + 2]) + zs[4 * tid + 3];
             a.sgate[t] = a.sgi ? 1.0f / (1.0f + __expf(-zt)) : 1.0f;
         }
         return;
     }
-    const bool router = b < nr;
+    const int grp = b % SA_NGRP, sl = b / SA_NGRP;
+    const bool router = grp < SA_NGRP_R;
     if (!router && !a.sg) return;
-    const int bb = router ? b : b - nr;
-    const int ngrp = router ? N_ROUTER_GRP : N_SGU_GRP;
-    const int r0 = SA_ROWS * (bb % ngrp), m = bb / ngrp;
-    const int kb = 128 * wave + 8 * kq;
-    // router bias of output column tid % 8, loaded with the first round trip
-    const float bias = router && a.rbias ? a.rbias[r0 + (tid & (SA_ROWS - 1))] : 0.0f;
-
-    // A operand: token 16m + n (slots past T read token 0's row; dropped)
-    const int tA = 16 * m + n;
-    const uint16_t* xrow = a.x + (size_t)(tA < T ? tA : 0) * D + kb;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (router) {
-        // B column n: expert r0 + (n & 7) (columns 8..15 repeat 0..7)
-        const float* wrow = a.wr + (size_t)(r0 + (n & 7)) * D + kb;
-        u32x4 wv[4][2], xv[4];
+    const int nt = wave & 1, ks = wave >> 1;
+    const int k0 = SA_KS * sl + 64 * ks + 8 * kq;  // this lane's inputs: k0 .. k0 + 7 and k0 + 32 .. k0 + 39
+    const int prow = SA_ROWS * grp + 16 * nt + n;  // B column n: this partial row
+    // A rows: token 16 mt + n (slots past T read token 0's row; dropped)
+    u32x4 xv[NMT][2];
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            wv[ks][0] = *(const u32x4*)(wrow + 32 * ks);
-            wv[ks][1] = *(const u32x4*)(wrow + 32 * ks + 4);
-            xv[ks] = *(const u32x4*)(xrow + 32 * ks);
+    for (int mt = 0; mt < NMT; mt++) {
+        const int t = 16 * mt + n;
+        const uint16_t* xr = a.x + (size_t)(t < T ? t : 0) * D + k0;
+        xv[mt][0] = *(const u32x4*)xr;
+        xv[mt][1] = *(const u32x4*)(xr + 32);
+    }
+    f32x4 acc[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; mt++) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (router) {
+        const float* wrow = a.wr + (size_t)prow * D + k0;
+        u32x4 wv[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            wv[j][0] = *(const u32x4*)(wrow + 32 * j);
+            wv[j][1] = *(const u32x4*)(wrow + 32 * j + 4);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
+        for (int j = 0; j < 2; j++) {
             float v[8];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                v[j] = __uint_as_float(wv[ks][0][j]);
-                v[4 + j] = __uint_as_float(wv[ks][1][j]);
+            for (int q = 0; q < 4; q++) {
+                v[q] = __uint_as_float(wv[j][0][q]);
+                v[4 + q] = __uint_as_float(wv[j][1][q]);
             }
             u32x4 hi, mid, lo;
             split3(v, hi, mid, lo);
-            const bf16x8 av = as_bf16x8(xv[ks]);
-            acc = mfma16_bf16(av, as_bf16x8(lo), acc);
-            acc = mfma16_bf16(av, as_bf16x8(mid), acc);
-            acc = mfma16_bf16(av, as_bf16x8(hi), acc);
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++) {
+                const bf16x8 av = as_bf16x8(xv[mt][j]);
+                acc[mt] = mfma16_bf16(av, as_bf16x8(lo), acc[mt]);
+                acc[mt] = mfma16_bf16(av, as_bf16x8(mid), acc[mt]);
+                acc[mt] = mfma16_bf16(av, as_bf16x8(hi), acc[mt]);
+            }
         }
     } else {
-        // B column n: gate row r0 + n (n < 8), up row r0 + n - 8 (n >= 8)
-        const uint16_t* wrow = (n < 8 ? a.sg : a.su) + (size_t)(r0 + (n & 7)) * D + kb;
-        u32x4 wv[4], xv[4];
+        const int r = prow - E;  // gate rows 0 .. FS - 1, then up rows
+        const uint16_t* wrow = (r < FS ? a.sg + (size_t)r * D : a.su + (size_t)(r - FS) * D) + k0;
+        u32x4 wv[2];
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            wv[ks] = *(const u32x4*)(wrow + 32 * ks);
-            xv[ks] = *(const u32x4*)(xrow + 32 * ks);
-        }
+        for (int j = 0; j < 2; j++) wv[j] = *(const u32x4*)(wrow + 32 * j);
         __builtin_amdgcn_sched_barrier(0);  // keep every load above: one round trip, not one per use
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) acc = mfma16_bf16(as_bf16x8(xv[ks]), as_bf16x8(wv[ks]), acc);
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++) acc[mt] = mfma16_bf16(as_bf16x8(xv[mt][j]), as_bf16x8(wv[j]), acc[mt]);
     }
-    // lane (n, kq) holds tokens 4kq .. 4kq + 3 of column n; sum the 16
-    // K-slices in wave order
+    // lane (n, kq) holds tokens 16 mt + 4 kq .. + 3 of column n; the four K
+    // sub-slices summed in order, one partial per (token, row)
 #pragma unroll
-    for (int v = 0; v < 4; v++) red[wave][4 * kq + v][n] = acc[v];
+    for (int mt = 0; mt < NMT; mt++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) red[ks][16 * mt + 4 * kq + v][16 * nt + n] = acc[mt][v];
     __syncthreads();
-    if (tid < 16 * SA_ROWS) {
-        const int tt = tid / SA_ROWS, c = tid % SA_ROWS, t = 16 * m + tt;
-        float s0 = 0.f, s1 = 0.f;
+    float* const pa = a.pa + (size_t)sl * T * SA_NROWS + SA_ROWS * grp;
 #pragma unroll
-        for (int w = 0; w < 16; w++) {
-            s0 += red[w][tt][c];
-            s1 += red[w][tt][SA_ROWS + c];
-        }
-        if (t < T) {
-            if (router) a.logits[(size_t)t * E + r0 + c] = s0 + bias;
-            else a.hs[(size_t)t * FS + r0 + c] = silu_f32(s0) * s1;
-        }
+    for (int i = tid; i < 16 * NMT * SA_ROWS; i += 512) {
+        const int t = i / SA_ROWS, c = i % SA_ROWS;
+        const float v = ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
+        if (t < T) pa[(size_t)t * SA_NROWS + c] = v;
     }
 }
 
@@ -260,13 +270,61 @@ __global__ void __launch_bounds__(1024) k_dec_stage_a(DecodeArgs a, int nmt) {
 // and the renormalised weights.  Many small blocks, so the 8T arg-max rounds
 // spread over the chip (one block for all tokens made the rounds compete
 // for one compute unit's SIMDs: 11 us slower at 64 tokens).
+// The stage-A partials are finished here: a token's logits are the slice
+// partials added in slice order plus the router bias (in LDS, then the
+// top-8), and the blocks after the routing ones form the shared SwiGLU
+// hs = silu(gate) * up from the gate and up partials, four features per
+// thread.
 template <bool HASH>
 __global__ void __launch_bounds__(256) k_dec_topk(DecodeArgs a) {
-    const int lane = threadIdx.x & 63, t = 4 * blockIdx.x + (threadIdx.x >> 6);
-    if (t >= a.T) return;
+    __shared__ float lg[4][E];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = a.T;
+    const int nb = (T + 3) / 4;
+    if ((int)blockIdx.x >= nb) {
+        const int i = 256 * ((int)blockIdx.x - nb) + tid;
+        const int t = i / (FS / 4), f = 4 * (i % (FS / 4));
+        if (t >= T) return;
+        const float* pg = a.pa + (size_t)t * SA_NROWS + E + f;
+        f32x4 gp[SA_NS], up[SA_NS];
+#pragma unroll
+        for (int s = 0; s < SA_NS; s++) {
+            gp[s] = *(const f32x4*)(pg + (size_t)s * T * SA_NROWS);
+            up[s] = *(const f32x4*)(pg + (size_t)s * T * SA_NROWS + FS);
+        }
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            float g = 0.0f, u = 0.0f;
+#pragma unroll
+            for (int s = 0; s < SA_NS; s++) {
+                g += gp[s][j];
+                u += up[s][j];
+            }
+            o[j] = silu_f32(g) * u;
+        }
+        *(f32x4*)(a.hs + (size_t)t * FS + f) = o;
+        return;
+    }
+    const int t = 4 * blockIdx.x + wave;
+    if (t >= T) return;
+    float p[SA_NS][4], bias[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        bias[c] = a.rbias ? a.rbias[lane + 64 * c] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < SA_NS; s++) p[s][c] = a.pa[((size_t)s * T + t) * SA_NROWS + lane + 64 * c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        float v = 0.0f;
+#pragma unroll
+        for (int s = 0; s < SA_NS; s++) v += p[s][c];
+        lg[wave][lane + 64 * c] = v + bias[c];
+    }
     float sel_v[K];
     int sel_i[K];
-    token_select<HASH>(a, t, lane, sel_v, sel_i);
+    select_experts<HASH>(lg[wave], a.tid2eid, a.n_vocab, HASH ? a.token_ids[t] : 0, lane, sel_v, sel_i);
     write_token_route<HASH>(a, t, lane, sel_v, sel_i, nullptr);
 }
 
@@ -910,12 +968,18 @@ size_t decode_workspace_bytes(int T, DecodeLayout* L) {
 static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
     const int nmt = (a.T + 15) / 16;  // token tiles of 16
     const int n_gu = GU_BLOCKS;
-    tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a, dim3((N_ROUTER_GRP + N_SGU_GRP) * nmt + (a.T + 3) / 4), dim3(1024), 0,
-              s, a, nmt);
+    const dim3 ga(SA_BLOCKS + (a.T + 1) / 2);
+    switch (nmt) {
+        case 1: tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<1>, ga, dim3(512), 0, s, a); break;
+        case 2: tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<2>, ga, dim3(512), 0, s, a); break;
+        case 3: tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<3>, ga, dim3(512), 0, s, a); break;
+        default: tr.launch(MOE_FFN_KERNEL_ROUTER, k_dec_stage_a<4>, ga, dim3(512), 0, s, a); break;
+    }
+    const dim3 gt((a.T + 3) / 4 + (a.sg ? (a.T * FS / 4 + 255) / 256 : 0));
     if (a.tid2eid)
-        hipLaunchKernelGGL(k_dec_topk<true>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_dec_topk<true>, gt, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(k_dec_topk<false>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_dec_topk<false>, gt, dim3(256), 0, s, a);
     const int n_sd = a.sg ? N_SDOWN_BLK : 0;
     tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_gu + n_sd), dim3(512), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(DN_BLOCKS), dim3(512), 0, s, a);
@@ -940,6 +1004,7 @@ hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipS
     a.h = (uint16_t*)(ws + L.h);
     a.hl = a.h + (size_t)p.T * K * F;
     a.part = (float*)(ws + L.part);
+    a.pa = a.part;  // stage A's partials: read by the routing launch before stage D writes part
     a.idx = p.idx ? p.idx : (int32_t*)(ws + L.idx);
     a.w = p.w ? p.w : (float*)(ws + L.w);
     a.sgate = (float*)(ws + L.sgate);
