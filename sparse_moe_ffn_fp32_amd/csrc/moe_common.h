@@ -196,47 +196,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p) {
 // z -> -inf: exp overflows to inf and the reciprocal to 0, giving -0.
 __device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
-// (value desc, index asc): does (va, ia) rank before (vb, ib)?
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-    return (va > vb) | ((va == vb) & (ia < ib));
-}
-
-template <int CTRL>
-__device__ __forceinline__ void dpp_argmax_step(float& v, int& i) {
-    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-    const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xf, 0xf, false);
-    const bool take = ranks_before(ov, oi, v, i);
-    v = take ? ov : v;
-    i = take ? oi : i;
-}
-
-// Cross-row steps of a wave arg-max: rows 1 and 3 take the better of
-// themselves and lane 15 of the row below (row_bcast:15), then rows 2 and 3
-// take lane 31 (row_bcast:31); lane 63 ends with the wave's best.  Rows a
-// step does not write keep their own pair, which never ranks before itself.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ void dpp_argmax_bcast(float& v, int& i) {
-    const float ov = __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, false));
-    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false);
-    const bool take = ranks_before(ov, oi, v, i);
-    v = take ? ov : v;
-    i = take ? oi : i;
-}
-
-// Wave-wide best (score desc, index asc) of one candidate per lane; the
-// result is wave-uniform.
-__device__ __forceinline__ void wave_argmax(float cv, int ci, float& bv, int& bi) {
-    dpp_argmax_step<0xB1>(cv, ci);   // quad_perm [1,0,3,2]
-    dpp_argmax_step<0x4E>(cv, ci);   // quad_perm [2,3,0,1]
-    dpp_argmax_step<0x141>(cv, ci);  // row_half_mirror
-    dpp_argmax_step<0x140>(cv, ci);  // row_mirror: every lane holds its row's best
-    dpp_argmax_bcast<0x142, 0xa>(cv, ci);
-    dpp_argmax_bcast<0x143, 0xc>(cv, ci);
-    bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cv), 63));
-    bi = __builtin_amdgcn_readlane(ci, 63);
-}
-
 // Signed-integer key with the order of a float that is not NaN: the bits
 // as they are for v >= 0, the magnitude bits flipped for v < 0; -0 becomes
 // +0 first, so equal keys mean equal floats.
@@ -263,67 +222,82 @@ __device__ __forceinline__ int wave_max(int v) {
     return max((int)q[0], (int)q[1]);
 }
 
+// Wave-wide minimum of an int, the same value in every lane (as wave_max).
+template <int CTRL>
+__device__ __forceinline__ int dpp_min_step(int v) {
+    return min(v, __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ int wave_min(int v) {
+    v = dpp_min_step<0xB1>(v);
+    v = dpp_min_step<0x4E>(v);
+    v = dpp_min_step<0x141>(v);
+    v = dpp_min_step<0x140>(v);
+    const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = min((int)p[0], (int)p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    return min((int)q[0], (int)q[1]);
+}
+
+// The float an order key stands for (order_key inverted; -0 comes back +0).
+__device__ __forceinline__ float key_float(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7fffffff)); }
+
 // Top-8 of 256 scores held by one wave (lane l holds experts l, l+64,
 // l+128, l+192 in v[0..3]), ordered by (score desc, index asc); the scores
-// are finite or -inf, never NaN.  Each lane sorts its four candidates once;
-// in each of the eight rounds the winner is then the lowest index among the
-// lane heads equal to the wave maximum (a lane's other candidates equal to
-// it would sit behind a head of the same score and a lower index).  A round
-// takes the wave maximum of the heads' order keys and a ballot of the heads
-// that equal it: one such head wins outright, and only equal scores in
-// several lanes need the (score, index) arg-max.  The winning lane advances its head.
+// are finite or -inf, never NaN.  Each lane sorts its four candidates once,
+// as order keys; in each of the eight rounds the winner is then the lowest
+// index among the lane heads equal to the wave maximum (a lane's other
+// candidates equal to it would sit behind a head of the same score and a
+// lower index).  A round takes the wave maximum of the heads' keys and a
+// ballot of the heads that equal it: one such head wins outright, equal
+// maxima in several lanes go to the lowest index (a wave minimum).  The
+// winning lane, known by its lane number, shifts its list by selects, so a
+// round's chain is the maximum, one ballot and the selects.
 // The results are wave-uniform.  Only the first `rounds` ranks are formed
 // (wave-uniform, 1..8); later entries of sel_v / sel_i are left unset.
 __device__ __forceinline__ void wave_top8(const float* v, int lane, float* sel_v, int* sel_i, int rounds = 8) {
-    float a[4];
-    int ai[4];
+    int k[4], ai[4];
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-        a[c] = v[c];
+        k[c] = order_key(v[c]);
         ai[c] = lane + 64 * c;
     }
-    // sort the lane's four candidates (compare-exchange network)
+    // sort the lane's four candidates (compare-exchange network; equal keys
+    // keep index order)
     const int net[5][2] = {{0, 1}, {2, 3}, {0, 2}, {1, 3}, {1, 2}};
 #pragma unroll
     for (int s = 0; s < 5; s++) {
         const int p = net[s][0], q = net[s][1];
-        const bool sw = ranks_before(a[q], ai[q], a[p], ai[p]);
-        const float tv = a[p];
-        const int ti = ai[p];
-        a[p] = sw ? a[q] : a[p];
+        const bool sw = (k[q] > k[p]) | ((k[q] == k[p]) & (ai[q] < ai[p]));
+        const int tk = k[p], ti = ai[p];
+        k[p] = sw ? k[q] : k[p];
         ai[p] = sw ? ai[q] : ai[p];
-        a[q] = sw ? tv : a[q];
+        k[q] = sw ? tk : k[q];
         ai[q] = sw ? ti : ai[q];
     }
-    // the lane's head candidate and its order key; a lane that has given all
-    // four holds -inf
-    float hv = a[0];
-    int hi = ai[0], hk = order_key(hv);
+    // a lane that has given all four holds INT_MIN, below the key of -inf
 #pragma unroll
     for (int r = 0; r < 8; r++) {
         if (r >= rounds) break;
-        const int mk = wave_max(hk);
-        const uint64_t at_max = __ballot(hk == mk);
-        float bv;
-        int bi;
+        const int mk = wave_max(k[0]);
+        const uint64_t at_max = __ballot(k[0] == mk);
+        int wl;
         if (__popcll(at_max) == 1) {
-            const int wl = __ffsll((unsigned long long)at_max) - 1;
-            bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hv), wl));
-            bi = __builtin_amdgcn_readlane(hi, wl);
-        } else {
-            wave_argmax(hv, hi, bv, bi);  // equal maxima in several lanes
+            wl = __ffsll((unsigned long long)at_max) - 1;
+        } else {  // equal maxima in several lanes: the lowest index wins
+            const int mi = wave_min(k[0] == mk ? ai[0] : 0x7fffffff);
+            wl = __ffsll((unsigned long long)__ballot(ai[0] == mi)) - 1;
         }
-        sel_v[r] = bv;
-        sel_i[r] = bi;
-        if (bi == hi) {  // this lane gave the winner: shift its list
-            a[0] = a[1]; ai[0] = ai[1];
-            a[1] = a[2]; ai[1] = ai[2];
-            a[2] = a[3]; ai[2] = ai[3];
-            a[3] = -INFINITY; ai[3] = 0x7fffffff;
-            hv = a[0];
-            hi = ai[0];
-            hk = order_key(hv);
-        }
+        sel_v[r] = key_float(mk);
+        sel_i[r] = __builtin_amdgcn_readlane(ai[0], wl);
+        const bool win = lane == wl;  // this lane gave the winner: shift its list
+        k[0] = win ? k[1] : k[0];
+        ai[0] = win ? ai[1] : ai[0];
+        k[1] = win ? k[2] : k[1];
+        ai[1] = win ? ai[2] : ai[1];
+        k[2] = win ? k[3] : k[2];
+        ai[2] = win ? ai[3] : ai[2];
+        k[3] = win ? (int)0x80000000 : k[3];
+        ai[3] = win ? 0x7fffffff : ai[3];
     }
 }
 
