@@ -130,16 +130,16 @@ __device__ __forceinline__ float group_sum8(const u32x4& v) {
 // against every token, with K split over blocks: block = (group of 32 rows,
 // K slice of 256); 8 router groups, 16 gate and 16 up groups, 8 slices each,
 // 320 blocks of 512 threads (two fit a compute unit), each reading at most
-// 32 KB of weights and T x 512 bytes of x.  A compute unit moves only some
-// 20-odd GB/s of loads, so every compute unit has to stream a small share:
-// blocks of (8 rows, 16 tokens) over the whole K read 64 KB of weights and
-// 64 KB of x each, and at 8 tokens only 98 of them existed (8.3 us for
-// 6.3 MB).  Wave w takes the 16-row tile w & 1 and the K sub-slice w >> 1
-// (64 inputs) for every token tile; the four sub-slices are summed in LDS
-// in order and the block's sums leave as partials pa[slice][t][row] (rows:
-// 256 router, 512 gate, 512 up), which the routing launch adds in slice
-// order.  The last ceil(T / 2) blocks copy x into the K order of the codes
-// and form the shared-expert gate.
+// 32 KB of weights and T x 512 bytes of x, so the bytes and the router's
+// plane splitting spread over the whole chip: blocks of (8 rows, 16 tokens)
+// over the whole K read 64 KB of weights and 64 KB of x each, and at 8
+// tokens only 98 of them existed, 32 of them holding all the router work
+// (8.3 us for 6.3 MB).  Wave w takes the 16-row tile w & 1 and the K
+// sub-slice w >> 1 (64 inputs) for every token tile; the four sub-slices
+// are summed in LDS in order and the block's sums leave as partials
+// pa[slice][t][row] (rows: 256 router, 512 gate, 512 up), which the routing
+// launch adds in slice order.  The last ceil(T / 2) blocks copy x into the
+// K order of the codes and form the shared-expert gate.
 constexpr int SA_ROWS = 32;                  // rows per group
 constexpr int SA_KS = 256;                   // K per slice
 constexpr int SA_NS = D / SA_KS;             // slices

@@ -7,9 +7,10 @@
 // dequantised matrix never exists; accumulation is fp32.
 //
 // Block tile: 128 activation rows (tokens) x 256 weight rows (output
-// features); 4 waves, wave w computing all 128 rows against weight rows
-// [64w, 64w + 64) as 4 x 2 tiles of v_mfma_f32_32x32x16_f16.  The 4-bit
-// modes on 128-row tiles run 8 waves (two per SIMD) on 512 weight rows:
+// features); 8 waves (two per SIMD), wave (m, n) = (w / 4, w % 4) computing
+// activation rows [64m, 64m + 64) against weight rows [64n, 64n + 64) as
+// 2 x 2 tiles of v_mfma_f32_32x32x16_f16.  The 4-bit modes on 128-row tiles
+// run 8 waves on 512 weight rows, each wave all 128 rows against its 64:
 // gemm_block_gu_wide, gemm_block_down_wide.  MFMA layout:
 // lane l holds A[l%32][8*(l/32) .. +8] and B[8*(l/32) .. +8][l%32];
 // accumulator lane l holds C[i][l%32] for i = 8*(v/4) + 4*(l/32) + v%4,
