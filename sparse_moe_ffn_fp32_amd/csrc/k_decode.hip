@@ -524,6 +524,8 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
                (uint32_t)(16 * wave + n);
     };
     const __amdgpu_buffer_rsrc_t rgq = buffer_rsrc(a.gq), ruq = buffer_rsrc(a.uq);
+    const __amdgpu_buffer_rsrc_t rgq0 = empty_rsrc(a.gq), ruq0 = empty_rsrc(a.uq);
+    const int n_bodies = __builtin_amdgcn_readfirstlane(2 * n_units);
     // codes move as group pairs: lane (n, kq) loads words 4kq .. 4kq+3 of
     // the 16 words of pair p (groups 2p, 2p+1) of row n, so one instruction
     // reads 64 contiguous bytes of each of 16 rows (twice the run of one
@@ -560,12 +562,15 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     f32x4 og = {0.f, 0.f, 0.f, 0.f}, ou = {0.f, 0.f, 0.f, 0.f};
     u32x4 xn[8];
     // bodies of GU_RING groups, two per unit: ring slot q holds pair q of the
-    // body and is refilled with pair q of the next body (past the last unit:
-    // its copy); the scale vectors of the next body load at its start
+    // body and is refilled with pair q of the next body (past the last body:
+    // through an empty resource, so nothing is fetched); the scale vectors
+    // of the next body load at its start
 #pragma unroll 1
-    for (int bb = 0; bb < 2 * n_units; bb++) {
+    for (int bb = 0; bb < n_bodies; bb++) {
         const int k = bb >> 1, half = bb & 1;
         const uint32_t rn = row_of((bb + 1) >> 1);
+        const bool more = bb + 1 < n_bodies;  // wave-uniform
+        const __amdgpu_buffer_rsrc_t rg = more ? rgq : rgq0, ru = more ? ruq : ruq0;
         const int ghn = GU_RING * ((bb + 1) & 1);  // first group of the next body
         const u32x4 scn0 = ld_sc(rn, ghn / 8), scn1 = ld_sc(rn, ghn / 8 + 1);
         const bool next_tile = half == 1 && k + 1 < n_units && sm.unit[k + 1][3] != sm.unit[k][3];
@@ -597,8 +602,8 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
                 bu[0] = nibble_codes(u02[0], 0x43434343u); bu[1] = nibble_codes(u13[0], 0x43434343u);
                 bu[2] = nibble_codes(u02[1], 0x43434343u); bu[3] = nibble_codes(u13[1], 0x43434343u);
                 __builtin_amdgcn_sched_barrier(0);
-                gw[q] = ld_codes(rgq, rn, ghn / 2 + q);
-                uw[q] = ld_codes(ruq, rn, ghn / 2 + q);
+                gw[q] = ld_codes(rg, rn, ghn / 2 + q);
+                uw[q] = ld_codes(ru, rn, ghn / 2 + q);
             }
             const int h2 = 2 * (gi & 1);
             const bf16x8 a0 = as_bf16x8(*(const u32x4*)(xrow + 64 * g));
@@ -824,15 +829,16 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
         }
     };
     // code and scale offsets of this lane's output row in unit k
-    const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(a.dq);
+    const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(a.dq), rdq0 = empty_rsrc(a.dq);
+    const int n_units_s = __builtin_amdgcn_readfirstlane(n_units);
     auto row_of = [&](int k) {
         const int kk = min(k, n_units - 1);
         return (uint32_t)(__builtin_amdgcn_readfirstlane(sm.unit[kk][0]) * D + __builtin_amdgcn_readfirstlane(sm.unit[kk][1])) +
                (uint32_t)(16 * wave + n);
     };
     // lane (n, kq) loads words 4kq .. 4kq+3 of group pair p of row n
-    auto ld_codes = [&](uint32_t row, int p) {
-        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdq, (row * (F / 8) + 4 * kq) * 4, 64 * p, 0));
+    auto ld_codes = [&](__amdgpu_buffer_rsrc_t r, uint32_t row, int p) {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (row * (F / 8) + 4 * kq) * 4, 64 * p, 0));
     };
     auto ld_sc = [&](uint32_t row, u32x4& sv, u32x4& bv) {
         sv = *(const u32x4*)(a.ds + (size_t)row * (F / G));
@@ -852,16 +858,17 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
     {
         const uint32_t r0 = row_of(0), r1 = row_of(1);
 #pragma unroll
-        for (int q = 0; q < NPAIR; q++) ring[q] = ld_codes(r0, q);
+        for (int q = 0; q < NPAIR; q++) ring[q] = ld_codes(rdq, r0, q);
+        const __amdgpu_buffer_rsrc_t r = 1 < n_units_s ? rdq : rdq0;
 #pragma unroll
-        for (int q = 0; q < NPAIR; q++) ring[NPAIR + q] = ld_codes(r1, q);
+        for (int q = 0; q < NPAIR; q++) ring[NPAIR + q] = ld_codes(r, r1, q);
     }
     store_h(0, hv0);
     __syncthreads();
 
     static_assert(DN_RING == 2 * (F / G), "the ring holds two units");
     // bodies of two units: ring slot 4(k % 2) + q holds pair q of unit k and
-    // is refilled with pair q of unit k + 2 (past the last unit: its copy)
+    // is refilled with pair q of unit k + 2 (past the last unit: nothing)
 #pragma unroll 1
     for (int k0 = 0; k0 < n_units; k0 += 2) {
 #pragma unroll
@@ -875,6 +882,8 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
             u32x4 svn, bvn;
             ld_sc(row_of(k + 1), svn, bvn);
             const uint32_t rn = row_of(k + 2);
+            // past the last unit the refills go through an empty resource
+            const __amdgpu_buffer_rsrc_t rr = k + 2 < n_units_s ? rdq : rdq0;
             // A row: token slot n, at the K offset of the words this lane
             // holds after the regrouping (as in the gate/up stage)
             const int hb = sm.unit[kc][3], hslot = min(n, sm.unit[kc][2] - 1), hk = 32 * (kq & 1) + 16 * (kq >> 1);
@@ -894,7 +903,7 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
                     b[0] = nibble_codes(w02[0], 0x43434343u); b[1] = nibble_codes(w13[0], 0x43434343u);
                     b[2] = nibble_codes(w02[1], 0x43434343u); b[3] = nibble_codes(w13[1], 0x43434343u);
                     __builtin_amdgcn_sched_barrier(0);
-                    ring[rs] = ld_codes(rn, g >> 1);
+                    ring[rs] = ld_codes(rr, rn, g >> 1);
                 }
                 const int h2 = 2 * (g & 1);
                 const bf16x8 a0 = as_bf16x8(*(const u32x4*)(hrow + 64 * g));

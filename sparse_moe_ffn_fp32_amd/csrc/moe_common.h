@@ -189,6 +189,12 @@ __device__ __forceinline__ f16 pow2_f16(int d) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
 }
+// The same array with no bytes in range: a load through it returns zeros
+// and reaches no memory (the range check drops it), so a load ring can be
+// fed past its last unit without fetching anything.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t empty_rsrc(const void* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0, 0x00020000);
+}
 
 // silu(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (about
 // 1 ulp each): every caller rounds the result to fp16 or feeds an fp32 dot
