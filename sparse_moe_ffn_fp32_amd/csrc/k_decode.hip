@@ -412,6 +412,40 @@ __device__ void build_route(const DecodeArgs& a, RouteSmem& rs) {
     __syncthreads();
 }
 
+// The work units of items i0 .. i1 - 1 (at most 64; item = (distinct
+// expert, chunk of `step` rows), the chunks of an expert consecutive), one
+// per (item, token tile of up to 16), in order: expert, first row, tokens in
+// the tile, tile parity, first pair slot.  The parity flips with every new
+// token tile (consecutive items of one expert with one tile share it).  Wave
+// 0 only, lane j for item i0 + j: first units and parities from one prefix
+// sum of (tiles << 16 | flips) over the lanes.
+__device__ void build_units(const RouteSmem& rs, int i0, int i1, int nch, int step, int T, int (*unit)[8],
+                            int* n_units) {
+    const int lane = threadIdx.x & 63;
+    const int ni = i1 - i0;
+    const bool live = lane < ni;
+    const int it = i0 + min(lane, ni - 1);
+    const int u = it / nch, chunk = it % nch;
+    const int cnt = min(max(rs.ucnt[u], 1), T);
+    const int ex = rs.uexp[u] & (E - 1);
+    const int off = min(max(rs.uoff[u], 0), T * K - cnt);
+    const int u_prev = __shfl_up(u, 1);
+    const int first_flip = (lane > 0 && (u != u_prev || cnt > 16)) ? 1 : 0;
+    const int tiles = live ? (cnt + 15) >> 4 : 0;
+    const int flips = live ? first_flip + tiles - 1 : 0;  // parity flips at this item's units
+    const int incl = wave_incl_scan((tiles << 16) | flips);
+    const int u0 = (incl >> 16) - tiles, f0 = (incl & 0xffff) - flips;
+    for (int m = 0; m < tiles; m++) {
+        int* un = unit[u0 + m];
+        un[0] = ex;
+        un[1] = chunk * step;
+        un[2] = min(16, cnt - 16 * m);
+        un[3] = (f0 + first_flip + m) & 1;
+        un[4] = off + 16 * m;
+    }
+    if (lane == 63) *n_units = incl >> 16;
+}
+
 // ------------------------------------------------------------------ stage C
 // Routed gate/up, streamed.  The work units are (distinct expert, 128
 // features, token tile of up to 16 tokens); GU_BLOCKS persistent workgroups
@@ -431,11 +465,11 @@ constexpr int GU_RING = 16;                  // groups of codes in flight per wa
 constexpr int GU_BLOCKS = 256;               // persistent routed workgroups
 constexpr int GU_ITEMS = E * GU_NCH / GU_BLOCKS;  // at most this many items each
 constexpr int GU_UNITS = GU_ITEMS * 4;       // token tiles of 16: at most 64 tokens per expert
+static_assert(GU_ITEMS <= 64, "one wave builds the unit table");
 constexpr int XS_STRIDE = D + 8;             // bf16 per staged x row (16-byte pad)
 struct GuSmem {
     uint16_t xs[16][XS_STRIDE];              // token tile of x (bf16, perm8 K order)
     float xsum[D / G][16];                   // its sums over each quantisation group
-    int info[GU_ITEMS][4];                   // expert, token count, first pair of each item
     int unit[GU_UNITS][8];                   // expert, first feature, tokens in the tile, tile parity, first pair
     int pairs[GU_UNITS][16];                 // pair ids of each unit's token slots
     int n_units;
@@ -458,35 +492,8 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
     constexpr int NGRP = D / G;  // 32
     static_assert(NGRP == 2 * GU_RING && GU_RING % 8 == 0, "two ring bodies per unit, whole scale vectors");
 
-    // ---- unit table: item descriptors in parallel, then units in order
-    if (tid < i1 - i0) {
-        const int u = (i0 + tid) / GU_NCH;
-        const int cnt = min(max(rs.ucnt[u], 1), T);
-        sm.info[tid][0] = rs.uexp[u] & (E - 1);
-        sm.info[tid][1] = cnt;
-        sm.info[tid][2] = min(max(rs.uoff[u], 0), T * K - cnt);
-    }
-    __syncthreads();
-    if (tid == 0) {  // at most 4 items x 4 tiles, from LDS
-        int nun = 0, buf = 0, prev_u = -1;
-        for (int j = 0; j < i1 - i0; j++) {
-            const int u = (i0 + j) / GU_NCH, chunk = (i0 + j) % GU_NCH;
-            const int cnt = sm.info[j][1];
-            for (int m0 = 0; m0 < cnt && nun < GU_UNITS; m0 += 16) {
-                // the tile parity flips with every new token tile (consecutive
-                // items of one expert with one tile share it)
-                if (nun > 0 && (u != prev_u || m0 > 0 || cnt > 16)) buf ^= 1;
-                prev_u = u;
-                sm.unit[nun][0] = sm.info[j][0];
-                sm.unit[nun][1] = chunk * GU_FEAT;
-                sm.unit[nun][2] = min(16, cnt - m0);
-                sm.unit[nun][3] = buf;
-                sm.unit[nun][4] = sm.info[j][2] + m0;
-                nun++;
-            }
-        }
-        sm.n_units = nun;
-    }
+    // ---- unit table (at most 4 items x 4 tiles)
+    if (wave == 0) build_units(rs, i0, i1, GU_NCH, GU_FEAT, T, sm.unit, &sm.n_units);
     __syncthreads();
     const int n_units = sm.n_units;
     if (tid < n_units * 16) {  // pair ids of every unit's token slots (slots >= tc repeat the last)
@@ -738,12 +745,12 @@ constexpr int DN_NCH = D / DN_ROWS;                 // items per expert
 constexpr int DN_BLOCKS = 256;                      // persistent workgroups
 constexpr int DN_ITEMS = E * DN_NCH / DN_BLOCKS;    // at most this many items each
 constexpr int DN_UNITS = DN_ITEMS * 4;              // token tiles of 16: at most 64 tokens per expert
+static_assert(DN_ITEMS <= 64, "one wave builds the unit table");
 constexpr int DN_RING = 16;                         // groups of codes in flight per wave
 constexpr int HS_STRIDE = F + 8;                    // fp16 per staged h row (16-byte pad)
 struct DnSmem {
     uint16_t hs[2][2][16][HS_STRIDE];  // token tiles of h (bf16 hi, lo planes, perm8 order), two buffers
     float hsum[2][F / G][16];          // their sums over each quantisation group
-    int info[DN_ITEMS][4];          // expert, token count, first pair of each item
     int unit[DN_UNITS][8];          // expert, first output row, tokens in the tile, h buffer, first pair
     int pairs[DN_UNITS][16];        // pair ids of each unit's token slots
     int n_units;
@@ -765,35 +772,8 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
     const int i0 = blockIdx.x * q, i1 = min(i0 + q, n_items);
     if (i0 >= i1) return;
 
-    // ---- unit table: item descriptors in parallel, then units in order
-    if (tid < i1 - i0) {
-        const int u = (i0 + tid) / DN_NCH;
-        const int cnt = min(max(rs.ucnt[u], 1), T);
-        sm.info[tid][0] = rs.uexp[u] & (E - 1);
-        sm.info[tid][1] = cnt;
-        sm.info[tid][2] = min(max(rs.uoff[u], 0), T * K - cnt);
-    }
-    __syncthreads();
-    if (tid == 0) {  // at most 16 items x 4 tiles, from LDS
-        int nun = 0, buf = 0, prev_u = -1;
-        for (int j = 0; j < i1 - i0; j++) {
-            const int u = (i0 + j) / DN_NCH, chunk = (i0 + j) % DN_NCH;
-            const int cnt = sm.info[j][1];
-            for (int m0 = 0; m0 < cnt && nun < DN_UNITS; m0 += 16) {
-                // the tile parity flips with every new token tile (consecutive
-                // items of one expert with one tile share it)
-                if (nun > 0 && (u != prev_u || m0 > 0 || cnt > 16)) buf ^= 1;
-                prev_u = u;
-                sm.unit[nun][0] = sm.info[j][0];
-                sm.unit[nun][1] = chunk * DN_ROWS;
-                sm.unit[nun][2] = min(16, cnt - m0);
-                sm.unit[nun][3] = buf;
-                sm.unit[nun][4] = sm.info[j][2] + m0;
-                nun++;
-            }
-        }
-        sm.n_units = nun;
-    }
+    // ---- unit table (at most 16 items x 4 tiles)
+    if (wave == 0) build_units(rs, i0, i1, DN_NCH, DN_ROWS, T, sm.unit, &sm.n_units);
     __syncthreads();
     const int n_units = sm.n_units;
     // pair ids of every unit's token slots (slots >= tc repeat the last)
