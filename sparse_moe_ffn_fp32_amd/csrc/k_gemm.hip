@@ -781,16 +781,17 @@ __global__ void __launch_bounds__(512) k_gemm_down_wide(GemmArgs g) {
 
 // ---------------------------------------------------------------- wide gate/up
 // The routed gate/up on 128-row tiles with 256 features (512 gate and up
-// rows) per block: 8 waves, wave w computing all 128 rows against LDS weight
+// rows) per block: 8 waves, wave w computing all 128 rows against weight
 // rows [64w, 64w + 64) (gate and up of features 32w .. 32w + 31) over the
 // whole K.  Against two 128-feature blocks the tile's gathered x rows (512
-// KB per tile) are read once instead of twice.  Each step's codes are
-// expanded in the step itself (the other wave of the SIMD covers it), so
-// they need to land only one step ahead: two code buffers, which leaves room
-// for the scales and biases of all 32 groups.
+// KB per tile) are read once instead of twice.  Each wave loads the codes
+// of its own rows into its register ring and expands each step's codes in
+// the step itself (the other wave of the SIMD covers it); staging them in
+// LDS first had cost 4 % of the launch.  The LDS holds the x tiles, the
+// scales and biases of all 32 groups, and the epilogue's h tile.
 struct WideGuSmem {
     f16 a[2][GEMM_BM * LDSB];
-    uint32_t bq[2][WBN * BQS];
+    uint32_t pad[2][WBN * BQS];      // unused in the loop: with a and sb, room for the epilogue's h tile
     uint32_t sb[WBN * (D / G + 4)];  // (bias' << 16) | scale', fp16 bits (row-scaled)
     int32_t ea[GEMM_BM];             // the gathered x rows' exponents
     int32_t ew[WBN];                 // the gate/up rows' exponents
@@ -815,20 +816,22 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
 #pragma unroll
     for (int i = 0; i < 2; i++)
         apt[i] = g.xh + (size_t)(g.perm[seg + m0 + min(ar0 + 64 * i, rows - 1)] / K) * D + 8 * ac;
-    // ---- B: LDS row n is gate (n & 32 == 0) or up row of feature
-    // nblk * 256 + 32 (n >> 6) + (n & 31); thread covers lane half bh of rows
-    // br0 and br0 + 256
+    // ---- B: block row n is gate (n & 32 == 0) or up row of feature
+    // nblk * 256 + 32 (n >> 6) + (n & 31).  Each wave loads the codes of its
+    // own rows 64 w + 32 nt + l32 straight into registers in the layout its
+    // MFMAs take (lane half kq: 16 bytes = 32 weights of the step), the same
+    // 32 bytes per row per instruction a staged copy would load, with no LDS
+    // round trip
     auto wrow = [&](int n, int& mat) -> size_t {
         mat = (n >> 5) & 1;
         return (size_t)e * g.gu_rows + nblk * (WBN / 2) + 32 * (n >> 6) + (n & 31);
     };
-    const int bh = tid & 1, br0 = tid >> 1;
     const u32x4* bpt[2];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+    for (int nt = 0; nt < 2; nt++) {
         int mat;
-        const size_t row = wrow(br0 + 256 * i, mat);
-        bpt[i] = (const u32x4*)(g.q[mat] + row * (D / 8)) + bh;
+        const size_t row = wrow(64 * wave + 32 * nt + l32, mat);
+        bpt[nt] = (const u32x4*)(g.q[mat] + row * (D / 8)) + kq;
     }
     // ---- scales and biases of every group of LDS row n = tid, scaled by
     // the row's exponent; the gathered x rows' exponents
@@ -878,11 +881,11 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt][kk], acc[mt][nt], 0, 0, 0);
         }
     };
-    auto dequant = [&](int k, int qbuf, f16x8 (&bf)[2][4]) {
+    auto dequant = [&](int k, const u32x4 (&cb)[2], f16x8 (&bf)[2][4]) {
 #pragma unroll
         for (int nt = 0; nt < 2; nt++) {
             const int n = 64 * wave + 32 * nt + l32;
-            const u32x4 codes = *(const u32x4*)&sm.bq[qbuf][n * BQS + 4 * kq];
+            const u32x4 codes = cb[nt];
             f16x2 s2, b2;
             group_sb(sm.sb[n * SROW + k], s2, b2);
 #pragma unroll
@@ -893,7 +896,8 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
         }
     };
     // ring stage j holds A(j) and the codes of step j; loads run three steps
-    // ahead; A(j) and codes(j) sit in LDS buffer j % 2 during step j
+    // ahead; A(j) sits in LDS buffer j % 2 during step j, the codes stay in
+    // the ring
     constexpr int R = 4;
     static_assert(C::NK % R == 0, "K steps must be a multiple of the ring size");
     struct Stage { u32x4 a[2]; u32x4 b[2]; };
@@ -906,8 +910,6 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
     auto store = [&](const Stage& st, int buf) {
 #pragma unroll
         for (int i = 0; i < 2; i++) *(u32x4*)&sm.a[buf][(ar0 + 64 * i) * LDSB + 8 * ac] = st.a[i];
-#pragma unroll
-        for (int i = 0; i < 2; i++) *(u32x4*)&sm.bq[buf][(br0 + 256 * i) * BQS + 4 * bh] = st.b[i];
     };
     auto main_loop = [&](auto nmt_c) {
         Stage ring[R];
@@ -923,7 +925,7 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
                 load(min(k + R - 1, C::NK - 1), ring[(j + R - 1) % R]);
                 __builtin_amdgcn_sched_barrier(0);
                 f16x8 bfr[2][4];
-                dequant(k, j & 1, bfr);
+                dequant(k, ring[j].b, bfr);
                 mfma_step(nmt_c, j & 1, bfr);
                 store(ring[(j + 1) % R], (j + 1) & 1);
                 __syncthreads();
