@@ -27,23 +27,22 @@
 // (ldexp).  Inside a K step, MFMA sub-step kk and lane half kq = l/32 use K
 // in [32kq + 8kk, +8) for both operands.
 //
-// Per K step every operand goes global -> registers -> LDS in coalesced
-// pieces:
+// Per K step the operands go global -> registers in coalesced pieces:
 //   A (activations): eight lanes per row, 16 bytes each, so one load
-//     instruction covers eight whole 128-byte rows of the step; the MFMAs
-//     read their fragments from LDS;
-//   4-bit weights: two lanes per weight row, 16 bytes of codes (32 weights)
-//     each, stored raw (a quarter of the fp16 bytes); each wave expands the
-//     codes of its own 64 rows straight into MFMA operand registers, fp16
-//     s*q + b with the group's scale and bias (staged in LDS once at the
-//     block's start), one step ahead of the MFMAs that use them (8-wave
-//     blocks: in the step itself, the other wave of the SIMD covering it);
+//     instruction covers eight whole 128-byte rows of the step, then LDS;
+//     the MFMAs read their fragments from LDS;
+//   4-bit weights: each wave loads the raw codes of its own 64 rows (two
+//     lanes per row, 16 bytes = 32 weights each, a quarter of the fp16
+//     bytes) straight into registers in the MFMA operand layout and expands
+//     them there, fp16 s*q + b with the group's scale and bias (staged in
+//     LDS once at the block's start), in the step that uses them (the other
+//     wave of the SIMD covering it);
 //   16-bit weights (shared expert, router planes): fp16 rows prepared per
 //     call (k_prep), staged in LDS and read back as fragments.
 // Global loads run ahead in a ring of register stages (three steps for 4-bit
-// weights, one otherwise); activation tiles are double-buffered, code tiles
-// quadruple-buffered; one barrier per step.  Epilogues stage the output tile
-// in LDS so global stores are 16-byte row pieces.
+// weights, one otherwise); activation tiles are double-buffered; one barrier
+// per step.  Epilogues stage the output tile in LDS so global stores are
+// 16-byte row pieces.
 //
 // Modes:
 //   GU     routed gate/up over the expert-sorted rows; epilogue SwiGLU
@@ -158,13 +157,14 @@ struct GemmArgs {
     int T;
 };
 
-constexpr int BQS = 12;  // u32 per LDS raw-code row: 32 bytes of codes + 16 bytes pad
-constexpr int QBUF = 4;  // raw-code LDS buffers (codes are stored two steps ahead of their MFMAs)
+// LDS room the 4-bit kernels keep beside their tiles for the epilogues'
+// output staging (sized as four 512-row code buffers of 48-byte rows)
+constexpr int BQS = 12;
+constexpr int QBUF = 4;
 
-// LDS of one block: double-buffered activation tiles; the 4-bit modes keep the
-// raw codes of four steps plus the staged scales and biases (and DOWN the
-// rows' routing weights), the other modes a double-buffered fp16 weight
-// tile.  The epilogues reuse the operand tiles (a, then b or bq).
+// LDS of one block of the 16-bit modes: double-buffered activation tiles and
+// a double-buffered fp16 weight tile.  The epilogues reuse the operand tiles
+// (a, then b).
 template <int MODE>
 struct GemmSmem {
     f16 a[2][GEMM_BM * LDSB];
@@ -527,7 +527,7 @@ __host__ __device__ constexpr int routed_grid(int max_tiles) {
 constexpr int WBN = 512;  // output columns per wide block
 struct WideSmem {
     f16 a[2][GEMM_BM * LDSB];
-    uint32_t bq[QBUF][WBN * BQS];
+    uint32_t pad[QBUF][WBN * BQS];   // unused in the loop: with a, room for the epilogue's partial tile
     uint32_t sb[WBN * (F / G + 4)];  // (bias' << 16) | scale', fp16 bits (row-scaled)
     float rw[GEMM_BM];               // routing weight * 2^-(E_w + PART_BOUND) per row
     int32_t eprow[GEMM_BM];          // eh_max + E_w + PART_BOUND per row
@@ -591,12 +591,13 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
     const uint16_t* apt[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) apt[i] = g.h + (size_t)(seg + m0 + min(ar0 + 64 * i, rows - 1)) * F + 8 * ac;
-    // ---- B: thread covers lane half bh of LDS weight rows br0, br0 + 256
-    const int bh = tid & 1, br0 = tid >> 1;
+    // ---- B: each wave loads the codes of its own rows 64 w + 32 nt + l32
+    // straight into registers in the layout its MFMAs take (lane half kq:
+    // 16 bytes = 32 weights of the step)
     const u32x4* bpt[2];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-        bpt[i] = (const u32x4*)(g.q[0] + ((size_t)e * D + nblk * WBN + br0 + 256 * i) * (F / 8)) + bh;
+    for (int nt = 0; nt < 2; nt++)
+        bpt[nt] = (const u32x4*)(g.q[0] + ((size_t)e * D + nblk * WBN + 64 * wave + 32 * nt + l32) * (F / 8)) + kq;
     // ---- scales and biases of LDS row n = tid, scaled by the row's exponent
     // ew (and the block's largest, ew_max); per tile row: the h exponents of
     // its two 256-feature halves (the staged A rows are brought to the larger
@@ -673,15 +674,11 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
 #pragma unroll
         for (int i = 0; i < 2; i++) bv[i] = bpt[i][2 * k];
     };
-    auto store_b = [&](const u32x4 (&bv)[2], int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; i++) *(u32x4*)&sm.bq[buf][(br0 + 256 * i) * BQS + 4 * bh] = bv[i];
-    };
-    auto dequant = [&](int k, int qbuf, f16x8 (&bf)[2][4]) {
+    auto dequant = [&](int k, const u32x4 (&cb)[2], f16x8 (&bf)[2][4]) {
 #pragma unroll
         for (int nt = 0; nt < 2; nt++) {
             const int n = 64 * wave + 32 * nt + l32;
-            const u32x4 codes = *(const u32x4*)&sm.bq[qbuf][n * BQS + 4 * kq];
+            const u32x4 codes = cb[nt];
             f16x2 s2, b2;
             group_sb(sm.sb[n * SROW + k], s2, b2);
 #pragma unroll
@@ -691,23 +688,21 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
             }
         }
     };
-    // ring stage j holds A(j) and the codes of step j + 1 (as in gemm_block)
+    // ring stage j holds A(j) and the codes of step j; loads run three steps
+    // ahead; A(j) sits in LDS buffer j % 2 during step j, the codes stay in
+    // the ring
     constexpr int R = 4;
-    static_assert(C::NK % R == 0 && QBUF == R, "K steps must be a multiple of the ring size");
+    static_assert(C::NK % R == 0, "K steps must be a multiple of the ring size");
     struct Stage { u32x4 a[2]; u32x4 b[2]; };
     auto main_loop = [&](auto nmt_c) {
         Stage ring[R];
-        u32x4 c0[2];
-        load_b(0, c0);
 #pragma unroll
         for (int j = 0; j < R - 1; j++) {
             load_a(j, ring[j].a);
-            load_b(min(j + 1, C::NK - 1), ring[j].b);
+            load_b(j, ring[j].b);
         }
-        store_b(c0, 0);
-        __syncthreads();  // staged scales, biases, exponents, routing weights; codes of step 0
+        __syncthreads();  // staged scales, biases, exponents, routing weights
         store_a(ring[0].a, 0, 0);
-        store_b(ring[0].b, 1);
         __syncthreads();
 #pragma unroll 1
         for (int k0 = 0; k0 < C::NK; k0 += R) {
@@ -716,13 +711,12 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
                 const int k = k0 + j;
                 Stage& nx = ring[(j + R - 1) % R];
                 load_a(min(k + R - 1, C::NK - 1), nx.a);
-                load_b(min(k + R, C::NK - 1), nx.b);
+                load_b(min(k + R - 1, C::NK - 1), nx.b);
                 __builtin_amdgcn_sched_barrier(0);
                 f16x8 bfr[2][4];
-                dequant(k, j % QBUF, bfr);
+                dequant(k, ring[j].b, bfr);
                 mfma_step(nmt_c, j & 1, bfr);
                 store_a(ring[(j + 1) % R].a, min(k + 1, C::NK - 1), (j + 1) & 1);
-                store_b(ring[(j + 1) % R].b, (j + 2) % QBUF);
                 __syncthreads();
             }
         }
@@ -734,10 +728,10 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
     else main_loop(std::integral_constant<int, 1>{});
 
     // ---- epilogue: partial tile [128 rows][512 outputs] fp16 (routing
-    // weight, exponents as PART_BOUND states) in LDS (a and bq), then 16-byte
+    // weight, exponents as PART_BOUND states) in LDS (a and pad), then 16-byte
     // row pieces; the rows' exponents
     constexpr int PS = WBN + 8;
-    static_assert(GEMM_BM * PS * sizeof(f16) <= offsetof(WideSmem, sb), "partial tile must fit a, bq");
+    static_assert(GEMM_BM * PS * sizeof(f16) <= offsetof(WideSmem, sb), "partial tile must fit a, pad");
     f16* pb = &sm.a[0][0];
     auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
     int ewmax = sm.red[0];
@@ -938,13 +932,13 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
     else if (nmt == 2) main_loop(std::integral_constant<int, 2>{});
     else main_loop(std::integral_constant<int, 1>{});
 
-    // ---- epilogue: h tile [128 rows][256 features] fp32 in LDS (a, bq,
+    // ---- epilogue: h tile [128 rows][256 features] fp32 in LDS (a, pad,
     // sb): SwiGLU of the lane's gate and up values with their exponents
     // applied; then per row piece of 8 features: the row's largest |h| over
     // the block's 256 features (32 lanes), its exponent, fp16 in perm8
     // order, 16-byte stores
     constexpr int HS = WBN / 2 + 4;
-    static_assert(GEMM_BM * HS * sizeof(float) <= offsetof(WideGuSmem, ea), "h tile must fit a, bq, sb");
+    static_assert(GEMM_BM * HS * sizeof(float) <= offsetof(WideGuSmem, ea), "h tile must fit a, pad, sb");
     float* hb = (float*)&sm.a[0][0];
     auto acc_row = [&](int mt, int v) { return mt * 32 + 8 * (v >> 2) + 4 * kq + (v & 3); };
     const int f = 32 * wave + l32;  // feature inside the block
