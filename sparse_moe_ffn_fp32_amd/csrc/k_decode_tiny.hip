@@ -370,7 +370,9 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
         const uint32_t* qp = q < FW ? a.gq : a.uq;
         const uint16_t* sp = q < FW ? a.gs : a.us;
         const uint16_t* bp = q < FW ? a.gb : a.ub;
-        cv[q] = *(const u32x4*)(qp + row * (D / 8) + 4 * lane);
+        // read once: non-temporal, so they do not push the down rows read
+        // ahead below (for stage D) out of the cache
+        cv[q] = __builtin_nontemporal_load((const u32x4*)(qp + row * (D / 8) + 4 * lane));
         sv[q] = *(const uint32_t*)(sp + row * (D / G) + 2 * (lane >> 2));
         bv[q] = *(const uint32_t*)(bp + row * (D / G) + 2 * (lane >> 2));
     }
