@@ -146,22 +146,36 @@ __device__ __forceinline__ void norm_rows_to_lds(const u32x2 (&hx)[NT], const f3
     __syncthreads();
 }
 
+// The rows of x as they are, staged in LDS by the block (elements
+// 4 tid .. 4 tid + 3 of every token per thread).
+template <int NT>
+__device__ __forceinline__ void copy_rows_to_lds(const u32x2 (&hx)[NT], uint32_t* xs, int tid) {
+#pragma unroll
+    for (int t = 0; t < NT; t++) *(u32x2*)(xs + t * (D / 2) + 2 * tid) = hx[t];
+    __syncthreads();
+}
+
 // NT = T tokens (compiled per token count: every loop bound is a constant);
 // NORM: x is the residual stream, normalised here first (a.nw, a.eps).
+// From two tokens on (and always with NORM) the router and shared blocks
+// read x from a copy in LDS: every wave needs all of x over its K range,
+// and at four tokens the waves of one block had re-read 64-128 KB of x from
+// the cache.
 template <int NT, bool NORM>
 __global__ void __launch_bounds__(512) k_tiny_a(DecodeArgs a) {
+    constexpr bool XS = NORM || NT >= 2;  // x from LDS
     __shared__ float red[8][2 * NT];
     __shared__ double red64[8][NT];
-    __shared__ uint32_t xs[NORM ? NT * (D / 2) : 1];
+    __shared__ uint32_t xs[XS ? NT * (D / 2) : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x;
     u32x2 hx[NT];
     f32x4 nw;
-    if (NORM) {
+    if (XS) {
 #pragma unroll
         for (int t = 0; t < NT; t++) hx[t] = *(const u32x2*)(a.x + (size_t)t * D + 4 * tid);
-        nw = *(const f32x4*)(a.nw + 4 * tid);
     }
+    if (NORM) nw = *(const f32x4*)(a.nw + 4 * tid);
     if (b == TA_ROUTER_BLK + TA_SHARED_BLK) {
         // x -> perm8 copy (pairs j, j+4 of every 8-block), its 32-element
         // piece sums and the shared-expert gate, from one round trip: thread
@@ -221,13 +235,14 @@ __global__ void __launch_bounds__(512) k_tiny_a(DecodeArgs a) {
         for (int i = 0; i < 4; i++) {
             const int c = lane + 64 * (2 * i + kh);
             wv[i] = __builtin_nontemporal_load((const f32x4*)(wrow + 4 * c));
-            if (!NORM)
+            if (!XS)
 #pragma unroll
                 for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x2*)(a.x + (size_t)t * D + 4 * c);
         }
         __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
-        if (NORM) {
-            norm_rows_to_lds<NT>(hx, nw, a.eps, red64, xs, tid);
+        if (XS) {
+            if (NORM) norm_rows_to_lds<NT>(hx, nw, a.eps, red64, xs, tid);
+            else copy_rows_to_lds<NT>(hx, xs, tid);
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -268,13 +283,14 @@ __global__ void __launch_bounds__(512) k_tiny_a(DecodeArgs a) {
     for (int i = 0; i < 4; i++) {
         const int c = lane + 64 * i;
         wv[i] = __builtin_nontemporal_load((const u32x4*)(wrow + 8 * c));
-        if (!NORM)
+        if (!XS)
 #pragma unroll
             for (int t = 0; t < NT; t++) xv[t][i] = *(const u32x4*)(a.x + (size_t)t * D + 8 * c);
     }
     __builtin_amdgcn_sched_barrier(0);  // every load above first: one round trip
-    if (NORM) {
-        norm_rows_to_lds<NT>(hx, nw, a.eps, red64, xs, tid);
+    if (XS) {
+        if (NORM) norm_rows_to_lds<NT>(hx, nw, a.eps, red64, xs, tid);
+        else copy_rows_to_lds<NT>(hx, xs, tid);
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
