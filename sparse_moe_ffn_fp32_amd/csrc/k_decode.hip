@@ -30,17 +30,19 @@
 //
 // Launches (all on the caller's stream):
 //   A      router logits (fp32 weights split exactly into three bf16 terms)
-//          and the shared expert's gate/up + SwiGLU, per (row group, token
-//          tile) block with K split over its 16 waves and reduced in LDS in
-//          fixed order; x copied into the K order of the codes.
-//   route  one block: softmax/top-8/renormalise per token, sgate, the
-//          distinct experts with their (token, rank) pairs.
-//   C      routed gate/up + SwiGLU: 256 persistent workgroups stream the
+//          and the shared expert's gate/up rows against every token, K
+//          split over blocks of (32 rows, 256 inputs), each block's four
+//          64-input sub-slices summed in LDS in fixed order, the sums left
+//          as slice partials; x copied into the K order of the codes, sgate.
+//   top-k  the slice partials added in fixed order: per token the logits
+//          (+ bias), top-8 and renormalised weights; the shared SwiGLU.
+//   C      routed gate/up + SwiGLU: 256 persistent workgroups build the
+//          distinct-expert and pair lists in LDS and stream their
 //          (distinct expert, 128 features) items, each wave a full K sweep
 //          of 16 gate and 16 up rows with a deep load ring; extra blocks:
 //          the shared expert's down projection.
-//   D      routed down projection of 16 output rows per block over 8 distinct
-//          experts (one per wave), fp32 partials per pair.
+//   D      routed down, streamed the same way over (distinct expert, 128
+//          output rows) items, fp32 partials per pair.
 //   combine  y = sum_{r=0..7} w_r * partial_r + sgate * shexp  in fixed order
 //          with one bf16 rounding (no float atomics).
 //
