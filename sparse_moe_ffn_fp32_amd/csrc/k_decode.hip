@@ -665,8 +665,12 @@ __device__ __forceinline__ void gu_stream(const DecodeArgs& a, int bid, GuSmem& 
             og = f32x4{0.f, 0.f, 0.f, 0.f};
             ou = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (half == 1) __syncthreads();
-        if (next_tile) {  // every wave has left the old tile: store and publish the new one
+        // the tile is the only LDS the loop writes: the waves meet only where
+        // it changes (every wave has left the old tile, then the new one is
+        // stored and published); at 64 tokens a workgroup keeps one tile and
+        // its waves never wait for each other
+        if (next_tile) {
+            __syncthreads();
             store_x(xn);
             __syncthreads();
         }
@@ -914,10 +918,14 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
             }
             sv = svn;
             bv = bvn;
-            // the other buffer's last reader finished before the barrier that
-            // ended the previous unit; the barrier below publishes the tile
-            if (next_tile) store_h(k + 1, hv);
-            __syncthreads();
+            // the tile buffers are the only LDS the loop writes: the other
+            // buffer's last reader finished before the barrier that published
+            // the current tile, and the barrier below publishes the next one;
+            // units that keep their tile need no barrier
+            if (next_tile) {
+                store_h(k + 1, hv);
+                __syncthreads();
+            }
         }
     }
 }
