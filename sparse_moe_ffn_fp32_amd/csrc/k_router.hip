@@ -165,21 +165,28 @@ __device__ __forceinline__ void prep_x_row(const uint16_t* __restrict__ x, uint1
 
 
 // Both preparations in one launch, one wave per row: blocks [0, nb_w) take
-// the n_rows weight rows, the rest the T rows of x.
+// the n_rows weight rows, the next nb_x blocks the T rows of x, and the last
+// ones zero the sort's per-chunk expert counts (n_cnt ints), which the top-k
+// launch then accumulates (a fill kernel of its own would be one more
+// launch; no memset node either, so the sequence can be captured in a graph).
 __global__ void __launch_bounds__(256) k_prep(const float* __restrict__ wr, uint16_t* __restrict__ wr2,
                                               int32_t* __restrict__ er, const uint16_t* __restrict__ sg,
                                               const uint16_t* __restrict__ su, const uint16_t* __restrict__ sd,
                                               uint16_t* __restrict__ shw, int32_t* __restrict__ es, int n_rows,
                                               int nb_w, const uint16_t* __restrict__ x, uint16_t* __restrict__ xh,
                                               int32_t* __restrict__ ex, const uint16_t* __restrict__ gate_inp,
-                                              float* __restrict__ sgate, int T) {
+                                              float* __restrict__ sgate, int T, int nb_x, int32_t* __restrict__ cnt,
+                                              int n_cnt) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if ((int)blockIdx.x < nb_w) {
         const int row = blockIdx.x * 4 + wave;
         if (row < n_rows) prep_weight_row(wr, wr2, er, sg, su, sd, shw, es, row, lane);
-    } else {
+    } else if ((int)blockIdx.x < nb_w + nb_x) {
         const int t = (blockIdx.x - nb_w) * 4 + wave;
         if (t < T) prep_x_row(x, xh, ex, gate_inp, sgate, t, lane);
+    } else {
+        const int i = ((int)blockIdx.x - nb_w - nb_x) * 256 + threadIdx.x;
+        if (i < n_cnt) cnt[i] = 0;
     }
 }
 
@@ -190,7 +197,8 @@ template <bool HASH>
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int32_t* __restrict__ idx_out,
                                               float* __restrict__ w_out, float wscale,
                                               int gating, const int32_t* __restrict__ tid2eid,
-                                              const int32_t* __restrict__ token_ids, int n_vocab, int T) {
+                                              const int32_t* __restrict__ token_ids, int n_vocab, int T,
+                                              int32_t* __restrict__ cnt, int chunk) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -218,27 +226,30 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
             }
         idx_out[(size_t)t * K + lane] = iv;
         w_out[(size_t)t * K + lane] = wv;
+        // the sort's expert counts of this assignment's chunk (integer
+        // atomics: the totals do not depend on their order)
+        atomicAdd(&cnt[(size_t)((t * K + lane) / chunk) * E + (iv & (E - 1))], 1);
     }
 }
 
 hipError_t launch_prep(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
                        const uint16_t* sd, uint16_t* shw, int32_t* es, const uint16_t* x, uint16_t* xh, int32_t* ex,
-                       const uint16_t* gate_inp, float* sgate, int T, hipStream_t s) {
+                       const uint16_t* gate_inp, float* sgate, int T, int32_t* cnt, int n_cnt, hipStream_t s) {
     const int n_rows = E + (sg ? 2 * FS + D : 0);
-    const int nb_w = (n_rows + 3) / 4;
-    hipLaunchKernelGGL(k_prep, dim3(nb_w + (T + 3) / 4), dim3(256), 0, s, wr, wr2, er, sg, su, sd, shw, es, n_rows,
-                       nb_w, x, xh, ex, gate_inp, sgate, T);
+    const int nb_w = (n_rows + 3) / 4, nb_x = (T + 3) / 4;
+    hipLaunchKernelGGL(k_prep, dim3(nb_w + nb_x + (n_cnt + 255) / 256), dim3(256), 0, s, wr, wr2, er, sg, su, sd,
+                       shw, es, n_rows, nb_w, x, xh, ex, gate_inp, sgate, T, nb_x, cnt, n_cnt);
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int32_t* idx, float* w, float wscale, int gating, const int32_t* tid2eid,
-                       const int32_t* token_ids, int n_vocab, int T, hipStream_t s) {
+                       const int32_t* token_ids, int n_vocab, int T, int32_t* cnt, int chunk, hipStream_t s) {
     if (tid2eid)
         hipLaunchKernelGGL(k_topk<true>, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx, w, wscale, gating, tid2eid,
-                           token_ids, n_vocab, T);
+                           token_ids, n_vocab, T, cnt, chunk);
     else
         hipLaunchKernelGGL(k_topk<false>, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx, w, wscale, gating, tid2eid,
-                           token_ids, n_vocab, T);
+                           token_ids, n_vocab, T, cnt, chunk);
     return hipGetLastError();
 }
 

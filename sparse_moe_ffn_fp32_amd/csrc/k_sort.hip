@@ -5,7 +5,9 @@
 // expert routing on the GPU), a histogram counts the assignments per expert,
 // a prefix scan turns counts into start offsets, a scatter writes every
 // assignment into its expert's segment, and a tile map lists the fixed-size
-// row tiles the GEMMs process.  Nothing returns to the host.
+// row tiles the GEMMs process.  Nothing returns to the host.  The histogram
+// of every SORT_CH-assignment chunk is counted by the top-k launch as it
+// selects (k_router.hip); this file holds the rest in one launch.
 //
 // Assignment a = t*8 + r is token t's r-th selected expert.  The scatter is
 // stable: inside an expert's segment assignments keep increasing a (i.e.
@@ -16,20 +18,6 @@
 namespace moe {
 
 constexpr int SORT_CH = 2048;  // assignments per histogram/scatter block
-
-__global__ void __launch_bounds__(256) k_sort_hist(const int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int N) {
-    __shared__ int h[E];
-    h[threadIdx.x] = 0;
-    __syncthreads();
-    const int base = blockIdx.x * SORT_CH;
-#pragma unroll
-    for (int i = 0; i < SORT_CH / 256; i++) {
-        int a = base + i * 256 + threadIdx.x;
-        if (a < N) atomicAdd(&h[idx[a]], 1);
-    }
-    __syncthreads();
-    cnt[blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
-}
 
 // One launch after the histograms (a one-block scan launch between them
 // and the scatter had cost 11 us at 4K tokens, all latency):
@@ -242,13 +230,13 @@ __global__ void __launch_bounds__(PLACE_THREADS) k_sort_place(const int32_t* __r
 
 hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tiles_e,
                        int32_t* tile_count, int32_t* perm, int32_t* pos_of, int bm, hipStream_t s) {
-    const int nblk = (N + SORT_CH - 1) / SORT_CH;
-    hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(256), 0, s, idx, cnt, N);
+    const int nblk = (N + SORT_CH - 1) / SORT_CH;  // the histograms come from the top-k launch
     hipLaunchKernelGGL(k_sort_place, dim3(nblk + 1), dim3(PLACE_THREADS), 0, s, idx, cnt, nblk, offs, tiles, tiles_e,
                        tile_count, perm, pos_of, N, bm);
     return hipGetLastError();
 }
 
 int sort_blocks(int N) { return (N + SORT_CH - 1) / SORT_CH; }
+int sort_chunk() { return SORT_CH; }
 
 }  // namespace moe

@@ -174,12 +174,13 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
 
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    const int n_cnt = sort_blocks(N) * E;
     chk(launch_prep(router->weight, wr2, er, sh ? sh->gate : nullptr, sh ? sh->up : nullptr, sh ? sh->down : nullptr,
-                    shw, es, x, xh, xe, sh ? sh->gate_inp : nullptr, sgate, T, s));
+                    shw, es, x, xh, xe, sh ? sh->gate_inp : nullptr, sgate, T, cnt, n_cnt, s));
     chk(launch_router_gemm(xh, xe, wr2, er, router->bias, logits, shw, es, (uint16_t*)at(L.hs), (int32_t*)at(L.ehs), T,
                            tr, s));
     chk(launch_topk(logits, idx, w, weights_scale(router), router->gating, router->tid2eid, router->token_ids,
-                    router->n_vocab, T, s));
+                    router->n_vocab, T, cnt, sort_chunk(), s));
     int32_t* tiles_e = (int32_t*)at(L.tiles_e);
     chk(launch_sort(idx, N, cnt, offs, tiles, tiles_e, tile_count, perm, pos_of, gemm_bm(T), s));
     PrefillGemmParams p{};

@@ -28,18 +28,22 @@ struct Tracer {
 // exponents er [E]; shared bf16 (when sg != nullptr) -> fp16 shw [gate | up |
 // down] with row exponents es [2 FS + D]; x bf16 [T, D] -> fp16 xh (perm8)
 // with row exponents ex [T], and the shared-expert gate sgate [T] =
-// sigmoid(gate_inp . x), 1 without gate_inp
+// sigmoid(gate_inp . x), 1 without gate_inp; cnt [n_cnt] zeroed
 hipError_t launch_prep(const float* wr, uint16_t* wr2, int32_t* er, const uint16_t* sg, const uint16_t* su,
                        const uint16_t* sd, uint16_t* shw, int32_t* es, const uint16_t* x, uint16_t* xh, int32_t* ex,
-                       const uint16_t* gate_inp, float* sgate, int T, hipStream_t s);
+                       const uint16_t* gate_inp, float* sgate, int T, int32_t* cnt, int n_cnt, hipStream_t s);
 // wscale multiplies every renormalised routing weight
 // tid2eid != nullptr: hash routing with token_ids [T] (n_vocab table columns)
+// cnt [N / chunk, E] (zeroed before): the assignments a of each chunk a / chunk
+// counted per expert (the sort's histograms)
 hipError_t launch_topk(const float* logits, int32_t* idx, float* w, float wscale, int gating, const int32_t* tid2eid,
-                       const int32_t* token_ids, int n_vocab, int T, hipStream_t s);
+                       const int32_t* token_ids, int n_vocab, int T, int32_t* cnt, int chunk, hipStream_t s);
 
 // ---- routing sort (k_sort.hip)
 int sort_blocks(int N);
-// tiles: the tile records longest first; tiles_e: the same records in expert order
+int sort_chunk();  // assignments per histogram chunk
+// cnt: the per-chunk expert counts (launch_topk); tiles: the tile records
+// longest first; tiles_e: the same records in expert order
 hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tiles_e,
                        int32_t* tile_count, int32_t* perm, int32_t* pos_of, int bm, hipStream_t s);
 
