@@ -507,8 +507,11 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
         const int q = tid + TD_THREADS * i;
         const int pp = q / (F / 8), k8 = q % (F / 8);
         const u32x4 v = hv[i], vl = hw[i];
-        *(u32x4*)&hl[0][pp][8 * k8] = v;
-        *(u32x4*)&hl[1][pp][8 * k8] = vl;
+        // piece 4c + w (lane c's w-th) at 4c + (w ^ (c >> 2)): the 16 lanes
+        // reading one w then hit 16 distinct 16-byte bank slots
+        const int ks = (k8 & ~3) | ((k8 & 3) ^ ((k8 >> 4) & 3));
+        *(u32x4*)&hl[0][pp][8 * ks] = v;
+        *(u32x4*)&hl[1][pp][8 * ks] = vl;
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -521,34 +524,30 @@ __global__ void __launch_bounds__(TD_THREADS) k_tiny_d(DecodeArgs a) {
     }
     __syncthreads();
     const int g = c >> 1;
-    // two units at a time: every LDS read of both (h hi and lo planes, the
-    // piece sums) is issued before the first dot product waits for one
+    // two units at a time: units j0 and j0 + 1 (j0 even) are rows sub and
+    // 4 + sub of one pair, so they share one read of its h piece (both
+    // planes and the piece sum) from LDS
+    static_assert(nj % 2 == 0, "unit pairs");
 #pragma unroll
     for (int j0 = 0; j0 < nj; j0 += 2) {
-        u32x4 hh[2][4], hw[2][4];
-        float hs[2];
+        const int pp = ((wave * nj + j0) * 4 + sub) >> 3;
+        u32x4 hh[4], hw[4];
 #pragma unroll
-        for (int jj = 0; jj < 2; jj++) {
-            const int pp = ((wave * nj + j0 + jj) * 4 + sub) >> 3;
-#pragma unroll
-            for (int w = 0; w < 4; w++) {
-                hh[jj][w] = *(const u32x4*)&hl[0][pp][32 * c + 8 * w];
-                hw[jj][w] = *(const u32x4*)&hl[1][pp][32 * c + 8 * w];
-            }
-            hs[jj] = hsum[pp][c];
+        for (int w = 0; w < 4; w++) {
+            const int ws = w ^ ((c >> 2) & 3);
+            hh[w] = *(const u32x4*)&hl[0][pp][32 * c + 8 * ws];
+            hw[w] = *(const u32x4*)&hl[1][pp][32 * c + 8 * ws];
         }
-        __builtin_amdgcn_sched_barrier(0);
+        const float hs = hsum[pp][c];
 #pragma unroll
         for (int jj = 0; jj < 2; jj++) {
             const int j = j0 + jj;
-            const int u = (wave * nj + j) * 4 + sub;
-            const int pp = u >> 3, i = u & 7;
             float acc = 0.0f;
 #pragma unroll
-            for (int w = 0; w < 4; w++) acc = dot_codes_bf16_2(cv[j][w], hh[jj][w], hw[jj][w], acc);
+            for (int w = 0; w < 4; w++) acc = dot_codes_bf16_2(cv[j][w], hh[w], hw[w], acc);
             const float s = group_param(sv[j], g), bb = group_param(bv[j], g);
-            const float v = row16_sum(s * acc + (bb - 128.0f * s) * hs[jj]);
-            if (c == 0) dv[pp][i] = v;
+            const float v = row16_sum(s * acc + (bb - 128.0f * s) * hs);
+            if (c == 0) dv[pp][4 * jj + sub] = v;
         }
     }
     __syncthreads();
