@@ -348,23 +348,6 @@ struct RouteSmem {
     int nu;             // distinct experts
 };
 
-// v + the value lane CTRL names (0 where there is none or the row is masked)
-template <int CTRL, int ROWS>
-__device__ __forceinline__ int dpp_add_from(int v) {
-    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, true);
-}
-// inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 within each
-// row of 16, then lane 15 into rows 1 and 3, lane 31 into rows 2 and 3
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    v = dpp_add_from<0x111, 0xf>(v);
-    v = dpp_add_from<0x112, 0xf>(v);
-    v = dpp_add_from<0x114, 0xf>(v);
-    v = dpp_add_from<0x118, 0xf>(v);
-    v = dpp_add_from<0x142, 0xa>(v);
-    v = dpp_add_from<0x143, 0xc>(v);
-    return v;
-}
-
 // 512 threads, one assignment each (T*8 <= 512); every thread must call it.
 __device__ void build_route(const DecodeArgs& a, RouteSmem& rs) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -42,23 +42,33 @@ constexpr int SORT_CH = 2048;  // assignments per histogram/scatter block
 constexpr int PLACE_THREADS = 1024;  // four threads per expert for the count passes
 constexpr int PLACE_WAVES = PLACE_THREADS / 64;
 
-// Exclusive scan of the 256 values held by threads 0..255 of a 1024-thread
-// block (every thread calls it; the others pass and get 0); returns the
-// total to every thread.
-__device__ int scan_256_of_1024(int v, int* smem, int& total) {
-    const int tid = threadIdx.x;
-    if (tid < 256) smem[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const int t = (tid < 256 && tid >= off) ? smem[tid - off] : 0;
-        __syncthreads();
-        if (tid < 256) smem[tid] += t;
-        __syncthreads();
+// Exclusive scans of NS sets of 256 values, value e of set j held by thread
+// e < 256 (waves 0..3; every thread calls it, the others pass 0 and get 0):
+// one DPP scan per wave and set, then the wave totals through LDS, with one
+// barrier for all the sets.  tot[j] = set j's total, in every thread.
+// wtot: LDS of 4 * NS ints, not used by the caller until its next barrier.
+template <int NS>
+__device__ __forceinline__ void scan_256(const int (&v)[NS], int (&excl)[NS], int (&tot)[NS], int* wtot) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int incl[NS];
+#pragma unroll
+    for (int j = 0; j < NS; j++) {
+        incl[j] = wave_incl_scan(tid < 256 ? v[j] : 0);
+        if (wave < 4 && lane == 63) wtot[4 * j + wave] = incl[j];
     }
-    const int incl = tid < 256 ? smem[tid] : 0;
-    total = smem[255];
     __syncthreads();
-    return tid < 256 ? incl - v : 0;
+#pragma unroll
+    for (int j = 0; j < NS; j++) {
+        int before = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            const int t = wtot[4 * j + w];
+            before += w < wave ? t : 0;
+            all += t;
+        }
+        tot[j] = all;
+        excl[j] = tid < 256 ? before + incl[j] - v[j] : 0;
+    }
 }
 
 // Quarter qt of the histogram rows (thread tid = 256 qt + e): expert e's
@@ -85,7 +95,7 @@ __device__ __forceinline__ void count_quarter(const int32_t* __restrict__ cnt, i
 
 __device__ void place_chunk(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int nblk,
                             int32_t* __restrict__ perm, int32_t* __restrict__ pos_of, int N) {
-    __shared__ int smem[256];
+    __shared__ int wtot[4];
     __shared__ int part_t[4][E], part_p[4][E];
     __shared__ int base[E];
     __shared__ int wcnt[PLACE_WAVES][E];
@@ -103,9 +113,10 @@ __device__ void place_chunk(const int32_t* __restrict__ idx, const int32_t* __re
     const int e = tid & (E - 1);
     const int total = part_t[0][e] + part_t[1][e] + part_t[2][e] + part_t[3][e];
     const int before = part_p[0][e] + part_p[1][e] + part_p[2][e] + part_p[3][e];
-    int all;
-    const int off = scan_256_of_1024(tid < 256 ? total : 0, smem, all);
-    if (tid < 256) base[e] = off + before;
+    const int tv[1] = {total};
+    int off[1], all[1];
+    scan_256<1>(tv, off, all, wtot);
+    if (tid < 256) base[e] = off[0] + before;
     __syncthreads();
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
@@ -145,7 +156,7 @@ __device__ void place_chunk(const int32_t* __restrict__ idx, const int32_t* __re
 __device__ void tile_map(const int32_t* __restrict__ cnt, int nblk, int32_t* __restrict__ offs,
                          int32_t* __restrict__ tiles, int32_t* __restrict__ tiles_e, int32_t* __restrict__ tile_count,
                          int bm) {
-    __shared__ int smem[256];
+    __shared__ int wtot[4 * 6];
     __shared__ int part_t[4][E];
     __shared__ int start4[E + 1];  // exclusive start of each expert's tiles in the four-group class
     __shared__ int starte[E + 1];  // the same in expert order
@@ -154,26 +165,33 @@ __device__ void tile_map(const int32_t* __restrict__ cnt, int nblk, int32_t* __r
     count_quarter(cnt, nblk, 0, part_t, nullptr);
     __syncthreads();
     const int run = part_t[0][e] + part_t[1][e] + part_t[2][e] + part_t[3][e];  // expert e's assignments
-    int total;
-    const int off = scan_256_of_1024(tid < 256 ? run : 0, smem, total);
+    // classes: live 32-row groups of each tile (4 for a full tile)
+    const int n_full = run / bm, part_rows = run - n_full * bm;
+    const int g_part = (part_rows + 31) >> 5;  // 0 when there is no partial tile
+    // the scanned sets: the expert's assignments, its tiles with 4, 3, 2, 1
+    // live groups, and all its tiles
+    int sv[6];
+    sv[0] = run;
+    sv[1] = n_full + (g_part == 4);
+#pragma unroll
+    for (int q = 1; q < 4; q++) sv[1 + q] = (g_part == 4 - q);
+    sv[5] = n_full + (part_rows > 0);
+    int sx[6], st[6];
+    scan_256<6>(sv, sx, st, wtot);
+    const int off = sx[0], toff = sx[5], ntot = st[5];
+    int cls[4], start[4], tot[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        cls[q] = sv[1 + q];
+        start[q] = sx[1 + q];
+        tot[q] = st[1 + q];
+    }
     if (tid < 256) {
         s_run[e] = run;
         s_off[e] = off;
         offs[e] = off;
         if (e == E - 1) offs[E] = off + run;
     }
-    // classes: live 32-row groups of each tile (4 for a full tile)
-    const int n_full = run / bm, part_rows = run - n_full * bm;
-    const int g_part = (part_rows + 31) >> 5;  // 0 when there is no partial tile
-    int cls[4];                                // tiles of this expert with 4, 3, 2, 1 live groups
-    cls[0] = n_full + (g_part == 4);
-#pragma unroll
-    for (int q = 1; q < 4; q++) cls[q] = (g_part == 4 - q);
-    int start[4], tot[4];
-#pragma unroll
-    for (int q = 0; q < 4; q++) start[q] = scan_256_of_1024(tid < 256 ? cls[q] : 0, smem, tot[q]);
-    int ntot;
-    const int toff = scan_256_of_1024(tid < 256 ? n_full + (part_rows > 0) : 0, smem, ntot);
     if (tid < 256) {
         start4[e] = start[0];
         starte[e] = toff;

@@ -245,6 +245,23 @@ __device__ __forceinline__ int wave_min(int v) {
 }
 
 // The float an order key stands for (order_key inverted; -0 comes back +0).
+// v + the value lane CTRL names (0 where there is none or the row is masked)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add_from(int v) {
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, true);
+}
+// inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 within each
+// row of 16, then lane 15 into rows 1 and 3, lane 31 into rows 2 and 3
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v = dpp_add_from<0x111, 0xf>(v);
+    v = dpp_add_from<0x112, 0xf>(v);
+    v = dpp_add_from<0x114, 0xf>(v);
+    v = dpp_add_from<0x118, 0xf>(v);
+    v = dpp_add_from<0x142, 0xa>(v);
+    v = dpp_add_from<0x143, 0xc>(v);
+    return v;
+}
+
 __device__ __forceinline__ float key_float(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7fffffff)); }
 
 // Top-8 of 256 scores held by one wave (lane l holds experts l, l+64,
