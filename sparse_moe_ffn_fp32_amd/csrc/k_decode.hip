@@ -1,5 +1,5 @@
-// Decode path for 4 < T <= 64 tokens: bandwidth-bound expert GEMVs on skinny
-// MFMA tiles (T <= 4 runs k_decode_tiny.hip).
+// Decode path for 8 < T <= 64 tokens: bandwidth-bound expert GEMVs on skinny
+// MFMA tiles (T <= 8 runs k_decode_tiny.hip).
 //
 // Lily engine page: batch-1 decode is a GEMV bound by the bytes moved per
 // token ("Dekodavimas: sumazinti perkeliamu baitu kieki vienam tokenui"), and
@@ -914,7 +914,7 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
 }
 
 // y = sum_{r=0..7} w_r * partial_r + sgate * shexp (+ the residual), fixed
-// order, one bf16 rounding (T > 4).
+// order, one bf16 rounding (T > 8).
 __global__ void __launch_bounds__(256) k_dec_combine(DecodeArgs a) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= a.T * D) return;

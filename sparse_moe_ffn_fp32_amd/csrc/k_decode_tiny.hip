@@ -1,10 +1,10 @@
-// Decode path for T <= 4 tokens: weight streaming on the vector ALUs.
+// Decode path for T <= 8 tokens: weight streaming on the vector ALUs.
 //
 // Lily engine page, "Dekodavimas: sumazinti perkeliamu baitu kieki vienam
 // tokenui": batch-1 decode is a GEMV bound by the bytes moved per token, and
 // a group of lanes cooperates on one output while reading different parts of
-// its weight row.  With at most four tokens a matrix-core tile would be 3/4
-// or more padding, so here every weight row is read by one wave: lane l takes
+// its weight row.  With at most eight tokens a matrix-core tile would be
+// half or more padding, so here every weight row is read by one wave: lane l takes
 // the l-th 16-byte piece of the row (64 lanes = 1 KB, whole cache lines per
 // load instruction), forms dot products with v_dot2 on pairs, and the wave
 // sums the 64 partials in a fixed order (DPP and lane swaps).  Each launch is spread
@@ -19,7 +19,7 @@
 // x come from the first launch, those of h from the down launch's own
 // staging.
 //
-// Every kernel is compiled per token count (T = 1 .. 4), so that all loop
+// Every kernel is compiled per token count (T = 1 .. 8), so that all loop
 // bounds are constants: a load in a loop with a run-time trip count or under
 // a run-time guard makes the compiler copy registers and wait for it at once.
 //
@@ -54,10 +54,10 @@ namespace moe {
 
 constexpr int TA_ROUTER_BLK = E / 4;  // 4 experts per block (8 waves)
 constexpr int TA_SHARED_BLK = FS / 4; // 4 features (8 rows) per block
-// Features per routed gate/up block: 8 up to two tokens, 16 from three (the
-// launch then keeps all of its blocks resident at once and ranks each token
-// half as often); a block of chunk fc reads ahead the 4 * feat down rows
-// 4 feat * fc .. of its expert.
+// Features per routed gate/up block: 8 up to two tokens, 16 from three (at
+// three and four tokens the launch then keeps all of its blocks resident at
+// once, and each token is ranked half as often); a block of chunk fc reads
+// ahead the 4 * feat down rows 4 feat * fc .. of its expert.
 __host__ __device__ constexpr int tc_feat(int nt) { return nt >= 3 ? 16 : 8; }
 constexpr int TC_SDOWN_BLK = D / 8;   // shared-down blocks, 8 rows each
 constexpr int TD_ROWS = 8;            // output rows per down block
@@ -580,11 +580,16 @@ hipError_t launch_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
 }
 
 hipError_t launch_decode_tiny(const DecodeArgs& a, const Tracer& tr, hipStream_t s) {
+    static_assert(TINY_T == 8, "one case per token count");
     switch (a.T) {
         case 1: return launch_tiny<1>(a, tr, s);
         case 2: return launch_tiny<2>(a, tr, s);
         case 3: return launch_tiny<3>(a, tr, s);
         case 4: return launch_tiny<4>(a, tr, s);
+        case 5: return launch_tiny<5>(a, tr, s);
+        case 6: return launch_tiny<6>(a, tr, s);
+        case 7: return launch_tiny<7>(a, tr, s);
+        case 8: return launch_tiny<8>(a, tr, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -48,7 +48,7 @@ def fused0(gpu, layer0):
     return moe.DeviceLayer.from_host(layer0, fused=True)
 
 
-@pytest.mark.parametrize("T,path", [(1, "auto"), (3, "auto"), (4, "auto"), (37, "decode"), (64, "auto"),
+@pytest.mark.parametrize("T,path", [(1, "auto"), (3, "auto"), (4, "auto"), (6, "auto"), (37, "decode"), (64, "auto"),
                                     (37, "prefill"), (300, "auto")])
 def test_fused_gate_up_equals_separate(gpu, layer0, fused0, T, path):
     x, _, _ = workloads.enforce_margin(layer0, T, 900 + T)
@@ -162,7 +162,8 @@ def _hash_layer(base, n_vocab, seed, dup):
     return lay
 
 
-@pytest.mark.parametrize("T,path,gating,dup", [(1, "auto", 0, False), (4, "auto", 1, True), (37, "decode", 0, False),
+@pytest.mark.parametrize("T,path,gating,dup", [(1, "auto", 0, False), (4, "auto", 1, True), (8, "auto", 0, False),
+                                               (37, "decode", 0, False),
                                                (37, "prefill", 1, False), (300, "auto", 0, True),
                                                (300, "auto", 1, False)])
 def test_hash_routing(gpu, layer0, T, path, gating, dup):

@@ -47,7 +47,7 @@ def test_config0_T4(gpu, layer0):
     _say(routing_check(layer0, x, idx, w), output_check(layer0, x, y))
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 5, 17, 33, 63, 64, 65, 100, 257])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 17, 33, 63, 64, 65, 100, 257])
 @pytest.mark.parametrize("path", ["auto", "decode", "prefill"])
 def test_ragged_T(gpu, layer0, T, path):
     if path == "decode" and T > 64:
@@ -94,7 +94,7 @@ def test_config4_T32768_skewed_ties(gpu):
 @pytest.mark.parametrize("variant", ["no_shared", "no_gate_inp", "router_bias"])
 def test_layer_variants(gpu, variant, T):
     """Layers without a shared expert, without its gate vector, or with router
-    offsets, on the T <= 4 and T <= 64 decode paths and the prefill path (its
+    offsets, on the T <= 8 and T <= 64 decode paths and the prefill path (its
     routed-only combine, the router-only launch and sgate = 1)."""
     kw = dict(no_shared=dict(shared=False), no_gate_inp=dict(gate_inp=False), router_bias=dict(zipf_s=1.0))[variant]
     layer = workloads.layer_for(7, **kw)

@@ -132,9 +132,9 @@ def routing_check_rel(layer, x, idx, w):
 
 
 CASES = ["x_outliers", "x_tiny", "big_routed", "tiny_routed", "big_shared", "big_router"]
-# (T, path): the T <= 4 decode kernels, the 4 < T <= 64 decode kernels, the
+# (T, path): the T <= 8 decode kernels (3 and 7 tokens), the 8 < T <= 64 decode kernels, the
 # prefill path on a ragged tile and on several tiles
-RUNS = [(3, 0), (37, 0), (37, 2), (300, 0)]
+RUNS = [(3, 0), (7, 0), (37, 0), (37, 2), (300, 0)]
 
 
 @pytest.fixture(scope="module")
