@@ -362,25 +362,24 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
 #pragma unroll
     for (int i = 0; i < 4; i++) xv[i] = *(const u32x4*)(xrow + 8 * i);
     const float xs = a.xsum[t * XPIECES + lane];
-    // wave 0 ranks the token's experts once for the block, only as far as
-    // rank r (a rank-r block is done after r + 1 rounds, so most blocks
-    // issue their code loads earlier); the rank-7 blocks form all eight and
-    // one of them writes the token's routing
-    __shared__ int s_expert;
-    if (wave == 0) {
+    // every wave ranks the token's experts itself (no LDS hand-off and no
+    // barrier before the code loads), only as far as rank r (a rank-r block
+    // is done after r + 1 rounds, so most blocks issue their code loads
+    // earlier); the rank-7 blocks form all eight and one wave of one of them
+    // writes the token's routing
+    int e;
+    {
         float sel_v[K];
         int sel_i[K];
 #pragma unroll
         for (int k = 0; k < K; k++) sel_i[k] = 0;
         token_select<HASH>(a, t, lane, sel_v, sel_i, r + 1);
-        if (r == K - 1 && fc == 0) write_token_route<HASH>(a, t, lane, sel_v, sel_i, nullptr);  // sgate: stage A
+        if (wave == 0 && r == K - 1 && fc == 0) write_token_route<HASH>(a, t, lane, sel_v, sel_i, nullptr);  // sgate: stage A
         int er = sel_i[0];
 #pragma unroll
         for (int k = 1; k < K; k++) er = (k == r) ? sel_i[k] : er;
-        if (lane == 0) s_expert = er;
+        e = __builtin_amdgcn_readfirstlane(er) & (E - 1);
     }
-    __syncthreads();
-    const int e = s_expert & (E - 1);
     // wave w: features f0 + FW w .. f0 + FW w + FW - 1; rows q < FW: gate of
     // feature q, q >= FW: up of feature q - FW
     const size_t row0 = (size_t)e * a.gu_rows + f0 + FW * wave;
