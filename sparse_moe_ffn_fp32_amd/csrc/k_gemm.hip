@@ -170,6 +170,8 @@ template <int MODE>
 struct GemmSmem {
     f16 a[2][GEMM_BM * LDSB];
     f16 b[2][GEMM_BN * LDSB];
+    // SDOWN: with a and b, room for the combine's fp32 shared tile [128][260]
+    float yx[MODE == MODE_SDOWN ? GEMM_BM * (GEMM_BN + 4) - (2 * (GEMM_BM + GEMM_BN) * LDSB) / 2 : 1];
     int32_t ea[GEMM_BM];                                // the activation rows' exponents
     uint32_t fac[MODE == MODE_SDOWN ? GEMM_BM : 1][4];  // SDOWN: fp16 2^(ehs - ehs_max) per 128 features, both halves
     int32_t pos[MODE == MODE_SDOWN ? GEMM_BM * K : 4];  // SDOWN: each row's partial positions
@@ -263,6 +265,14 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
         } else {
             sm.ea[tid] = g.ex[t];
         }
+    }
+    // SDOWN: the exponents of this lane's two shared-down weight rows, loaded
+    // here so the epilogue's staging waits for no global load (the partial
+    // loads issued before it would be drained with it)
+    int ew_sd[2] = {0, 0};
+    if constexpr (MODE == MODE_SDOWN) {
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) ew_sd[nt] = g.es[2 * FS + nblk * GEMM_BN + 64 * wn + 32 * nt + l32];
     }
     if constexpr (MODE == MODE_SDOWN) {
         const int pblk = (nblk * GEMM_BN) / 512;  // the partials' 512-column exponent block
@@ -415,81 +425,92 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
             }
         }
     } else {
-        // combine: y = sum_r partial_r * 2^ep_r + sgate * shexp, in two passes
-        // of 128 columns (the fp32 shared tile of waves 2p, 2p + 1 in pass p)
-        constexpr int YS = 128 + 4;
-        static_assert(GEMM_BM * YS * sizeof(float) <= offsetof(GemmSmem<MODE>, ea), "shared tile must fit a, b");
-        float* yb = (float*)&sm.a[0][0];  // 128 x 132 fp32 = 67.6 KB
+        // combine: y = sum_r partial_r * 2^ep_r + sgate * shexp.  The fp32
+        // shared tile of all 256 columns goes to LDS once; then 128 rows x 32
+        // pieces of 8 outputs, thread tid taking pieces tid + 512 i (row
+        // (tid + 512 i) / 32, piece tid % 32), CB at a time, the loads of the
+        // next CB pieces (8 partials, residual, gate each) issued before the
+        // current ones are summed; the first are issued before the tile is
+        // staged.  Rows past the end load the last valid row and store nothing.
+        constexpr int YS = GEMM_BN + 4;
+        static_assert(GEMM_BM * YS * sizeof(float) <= offsetof(GemmSmem<MODE>, ea), "shared tile must fit a, b, y");
+        float* yb = (float*)&sm.a[0][0];  // 128 x 260 fp32 = 133 KB
+        constexpr int CB = 2, NPIECE = GEMM_BM * (GEMM_BN / 8) / GEMM_THREADS, NBATCH = NPIECE / CB;
+        static_assert(NPIECE % CB == 0, "whole batches");
+        // buffer loads and stores: vector-memory only (a flat access also
+        // counts as an LDS access, so every LDS read of the next batch's
+        // positions would wait for the partials in flight); without a
+        // residual its resource has no records and reads as zeros
+        const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(g.p_in), ry = buffer_rsrc(g.y);
+        const __amdgpu_buffer_rsrc_t rres = g.resid ? buffer_rsrc(g.resid) : empty_rsrc(g.y);
+        const int c = tid & 31;
+        const int o = nblk * GEMM_BN + 8 * c;  // this thread's first output column
+        u32x4 pv[2][CB][K], rv[2][CB];
+        float sg[2][CB];
+        auto issue = [&](int bi, int buf) {
 #pragma unroll
-        for (int pass = 0; pass < 2; pass++) {
-            if ((wn >> 1) == pass) {
+            for (int u = 0; u < CB; u++) {
+                const int r = min((tid + GEMM_THREADS * (CB * bi + u)) >> 5, rows - 1);
+                const int t = m0 + r;
 #pragma unroll
-                for (int nt = 0; nt < 2; nt++) {
-                    const int col = 64 * (wn & 1) + 32 * nt + l32;
-                    const int ew = g.es[2 * FS + nblk * GEMM_BN + pass * 128 + col];
-#pragma unroll
-                    for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                        for (int v = 0; v < 16; v++) {
-                            const int r = acc_row(mt, v);
-                            yb[r * YS + col] = __builtin_ldexpf(acc[mt][nt][v], sm.ea[r] + ew);
-                        }
-                }
+                for (int rr = 0; rr < K; rr++)
+                    pv[buf][u][rr] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, ((uint32_t)sm.pos[r * K + rr] * D + o) * 2, 0, 0));
+                rv[buf][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rres, ((uint32_t)t * D + o) * 2, 0, 0));
+                sg[buf][u] = g.sgate[t];
             }
-            __syncthreads();
-            // 128 rows x 16 pieces of 8 outputs, CB rows per thread at a time:
-            // every load of the CB (8 partials, residual, gate each) is issued
-            // before any is used; rows past the end load the last valid row
-            // and store nothing
-            constexpr int CB = 2;
-            const uint16_t* const p_in = pinned(g.p_in);
-            const uint16_t* const resid = pinned(g.resid);
-            uint16_t* const yo = pinned(g.y);
-#pragma unroll 1
-            for (int i0 = 0; i0 < GEMM_BM * 16 / GEMM_THREADS; i0 += CB) {
-                u32x4 pv[CB][K], rv[CB];
-                float sg[CB];
+        };
+        auto finish = [&](int bi, int buf) {
 #pragma unroll
-                for (int u = 0; u < CB; u++) {
-                    const int pc = tid + GEMM_THREADS * (i0 + u), r = min(pc >> 4, rows - 1), c = pc & 15;
-                    const int t = m0 + r, o = nblk * GEMM_BN + pass * 128 + 8 * c;
+            for (int u = 0; u < CB; u++) {
+                const int r = (tid + GEMM_THREADS * (CB * bi + u)) >> 5;
+                const int rl = min(r, rows - 1);
+                float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int rr = 0; rr < K; rr++) pv[u][rr] = *(const u32x4*)&p_in[(size_t)sm.pos[r * K + rr] * D + o];
-                    rv[u] = resid ? *(const u32x4*)&resid[(size_t)t * D + o] : u32x4{0u, 0u, 0u, 0u};
-                    sg[u] = g.sgate[t];
-                }
-#pragma unroll
-                for (int u = 0; u < CB; u++) {
-                    const int pc = tid + GEMM_THREADS * (i0 + u), r = pc >> 4, c = pc & 15;
-                    const int rl = min(r, rows - 1);
-                    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int rr = 0; rr < K; rr++) {
-                        const int ep = sm.epp[rl * K + rr];
-#pragma unroll
-                        for (int j = 0; j < 4; j++) {
-                            // copy the element to a scalar first: a bit cast of the
-                            // vector-element expression itself is miscompiled by
-                            // clang 22 (it reads element 0 for every j)
-                            const uint32_t pw = pv[u][rr][j];
-                            const f16x2 h2 = __builtin_bit_cast(f16x2, pw);
-                            sum[2 * j] += __builtin_ldexpf((float)h2[0], ep);
-                            sum[2 * j + 1] += __builtin_ldexpf((float)h2[1], ep);
-                        }
-                    }
-                    // the residual (added last, before the one rounding)
-                    u32x4 out;
+                for (int rr = 0; rr < K; rr++) {
+                    const int ep = sm.epp[rl * K + rr];
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
-                        const uint32_t rj = rv[u][j];
-                        const float y0 = sum[2 * j] + sg[u] * yb[rl * YS + 8 * c + 2 * j] + bf16_to_f32(rj & 0xffffu);
-                        const float y1 = sum[2 * j + 1] + sg[u] * yb[rl * YS + 8 * c + 2 * j + 1] + bf16_to_f32(rj >> 16);
-                        out[j] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+                        // copy the element to a scalar first: a bit cast of the
+                        // vector-element expression itself is miscompiled by
+                        // clang 22 (it reads element 0 for every j)
+                        const uint32_t pw = pv[buf][u][rr][j];
+                        const f16x2 h2 = __builtin_bit_cast(f16x2, pw);
+                        sum[2 * j] += __builtin_ldexpf((float)h2[0], ep);
+                        sum[2 * j + 1] += __builtin_ldexpf((float)h2[1], ep);
                     }
-                    if (r < rows) *(u32x4*)&yo[(size_t)(m0 + r) * D + nblk * GEMM_BN + pass * 128 + 8 * c] = out;
                 }
+                // the residual (added last, before the one rounding)
+                u32x4 out;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t rj = rv[buf][u][j];
+                    const float y0 = sum[2 * j] + sg[buf][u] * yb[rl * YS + 8 * c + 2 * j] + bf16_to_f32(rj & 0xffffu);
+                    const float y1 =
+                        sum[2 * j + 1] + sg[buf][u] * yb[rl * YS + 8 * c + 2 * j + 1] + bf16_to_f32(rj >> 16);
+                    out[j] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+                }
+                if (r < rows) __builtin_amdgcn_raw_buffer_store_b128(out, ry, ((uint32_t)(m0 + r) * D + o) * 2, 0, 0);
             }
-            __syncthreads();
+        };
+        issue(0, 0);
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) {
+            const int col = 64 * wn + 32 * nt + l32;
+            const int ew = ew_sd[nt];
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int r = acc_row(mt, v);
+                    yb[r * YS + col] = __builtin_ldexpf(acc[mt][nt][v], sm.ea[r] + ew);
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int bi = 0; bi < NBATCH; bi++) {
+            if (bi + 1 < NBATCH) issue(bi + 1, (bi + 1) & 1);
+            finish(bi, bi & 1);
         }
     }
 }
