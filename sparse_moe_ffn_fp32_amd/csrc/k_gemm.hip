@@ -404,8 +404,9 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
                 const float uv = __builtin_ldexpf(acc[mt][1][v], sm.ea[r] + eu);
                 hb[r * HS + f] = silu_f32(gv) * uv;
             }
-        uint16_t* const hs_out = pinned(g.hs_out);
-        int32_t* const ehs = pinned(g.ehs);
+        // buffer stores: a flat store also counts as an LDS access, so the
+        // LDS reads of the next rows would wait for it
+        const __amdgpu_buffer_rsrc_t rhs = buffer_rsrc(g.hs_out), rehs = buffer_rsrc(g.ehs);
         __syncthreads();
         // 128 rows x 16 pieces: thread tid takes rows tid/16 + 32i, piece tid%16
         const int c = tid & 15, rb = tid >> 4;
@@ -420,8 +421,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& g, GemmSmem<MODE>& sm
             const int e = row_exp(row16_max(m));
             const u32x4 o = f32x8_to_f16x8_perm_scaled(v, e);
             if (r < rows) {
-                *(u32x4*)&hs_out[(size_t)(m0 + r) * FS + nblk * 128 + 8 * c] = o;
-                if (c == 0) ehs[(size_t)(m0 + r) * 4 + nblk] = e;
+                __builtin_amdgcn_raw_buffer_store_b128(o, rhs, ((uint32_t)(m0 + r) * FS + nblk * 128 + 8 * c) * 2, 0, 0);
+                if (c == 0) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)e, rehs, ((uint32_t)(m0 + r) * 4 + nblk) * 4, 0, 0);
             }
         }
     } else {
@@ -983,9 +984,9 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
             const float uv = __builtin_ldexpf(acc[mt][1][v], sm.ea[r] + eu);
             hb[r * HS + f] = silu_f32(gv) * uv;
         }
-    uint16_t* const h_out = pinned(g.h_out);
-    const __amdgpu_buffer_rsrc_t rh_out = buffer_rsrc(h_out);
-    int32_t* const eh = pinned(g.eh);
+    // buffer stores (a flat store also counts as an LDS access, so the LDS
+    // reads of the next rows would wait for it)
+    const __amdgpu_buffer_rsrc_t rh_out = buffer_rsrc(g.h_out), reh = buffer_rsrc(g.eh);
     __syncthreads();
     // 128 rows x 32 pieces of 8 features: thread tid takes rows tid/32 + 16i,
     // piece tid%32 (a half-wave per row)
@@ -1007,7 +1008,7 @@ __device__ __forceinline__ void gemm_block_gu_wide(const GemmArgs& g, WideGuSmem
             const int off = (int)(((size_t)(seg + m0 + r) * F + fo) * sizeof(uint16_t));
             if (g.stream_nt) __builtin_amdgcn_raw_buffer_store_b128(o, rh_out, off, 0, 2);
             else __builtin_amdgcn_raw_buffer_store_b128(o, rh_out, off, 0, 0);
-            if (c == 0) eh[(size_t)(seg + m0 + r) * 2 + nblk] = e;
+            if (c == 0) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)e, reh, (uint32_t)((seg + m0 + r) * 2 + nblk) * 4, 0, 0);
         }
     }
 }
