@@ -134,7 +134,7 @@ struct GemmArgs {
     const int32_t* tiles;    // [4i..4i+3] expert, first row, segment start, rows; longest first
     const int32_t* tiles_e;  // the same records in expert order
     const int32_t* tile_count;
-    const float* wflat;      // [T*K] routing weights by assignment
+    const float* wsort;      // [T*K] routing weights by expert-sorted position
     const float* sgate;      // [T]
     int gu_rows;             // GU: rows per expert in the gate/up arrays (F, or 2F fused)
     // weights
@@ -643,7 +643,7 @@ __device__ __forceinline__ void gemm_block_down_wide(const GemmArgs& g, WideSmem
         const int2 e2 = *(const int2*)&g.eh[(size_t)sr * 2];
         const int em = max(e2.x, e2.y);
         sm.fac[tid] = __builtin_bit_cast(uint32_t, f16x2{pow2_f16(e2.x - em), pow2_f16(e2.y - em)});
-        const float w = g.wflat[g.perm[sr]];
+        const float w = g.wsort[sr];  // sorted by the routing sort: no dependent load
         int ewt;
         __builtin_frexpf(w, &ewt);  // w < 2^ewt
         sm.rw[tid] = __builtin_ldexpf(w, -ewt - PART_BOUND);
@@ -1081,7 +1081,7 @@ hipError_t launch_prefill_gemms(const PrefillGemmParams& p, const Tracer& tr, hi
     g.shw = p.shw; g.es = p.es;
     g.perm = p.perm; g.pos_of = p.pos_of; g.offs = p.offs; g.tiles = p.tiles; g.tiles_e = p.tiles_e;
     g.tile_count = p.tile_count;
-    g.wflat = p.wflat; g.sgate = p.sgate;
+    g.wsort = p.wsort; g.sgate = p.sgate;
     g.gu_rows = p.gu_rows;
     g.T = p.T;
     const int bm = gemm_bm(p.T);

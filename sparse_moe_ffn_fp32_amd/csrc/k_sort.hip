@@ -25,7 +25,8 @@ constexpr int SORT_CH = 2048;  // assignments per histogram/scatter block
 // Blocks 0 .. nblk-1 place the assignments of histogram block b: each forms
 // its own bases, base[e] = offs[e] + sum over blocks b' < b of cnt[b'][e],
 // with offs the exclusive scan of the expert totals, then walks its chunk in
-// assignment order (stable), 1024 at a time: perm[pos] = a, pos_of[a] = pos.
+// assignment order (stable), 1024 at a time: perm[pos] = a, pos_of[a] = pos,
+// and the routing weight in sorted order, wsort[pos] = w[a].
 // Ranks among equal experts inside a wave come from ballots on the 8 bits of
 // the expert id, across waves from per-wave counts.
 //
@@ -94,18 +95,21 @@ __device__ __forceinline__ void count_quarter(const int32_t* __restrict__ cnt, i
 }
 
 __device__ void place_chunk(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int nblk,
-                            int32_t* __restrict__ perm, int32_t* __restrict__ pos_of, int N) {
+                            int32_t* __restrict__ perm, int32_t* __restrict__ pos_of, const float* __restrict__ wt,
+                            float* __restrict__ wsort, int N) {
     __shared__ int wtot[4];
     __shared__ int part_t[4][E], part_p[4][E];
     __shared__ int base[E];
     __shared__ int wcnt[PLACE_WAVES][E];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
-    // this chunk's expert ids, loaded with the counts
+    // this chunk's expert ids and routing weights, loaded with the counts
     int eid[SORT_CH / PLACE_THREADS];
+    float wa[SORT_CH / PLACE_THREADS];
 #pragma unroll
     for (int i = 0; i < SORT_CH / PLACE_THREADS; i++) {
         const int a = b * SORT_CH + i * PLACE_THREADS + tid;
         eid[i] = idx[min(a, N - 1)];  // past the end: a copy, never placed
+        wa[i] = wt[min(a, N - 1)];
     }
     count_quarter(cnt, nblk, b, part_t, part_p);
     for (int i = tid; i < PLACE_WAVES * E; i += PLACE_THREADS) (&wcnt[0][0])[i] = 0;
@@ -138,6 +142,7 @@ __device__ void place_chunk(const int32_t* __restrict__ idx, const int32_t* __re
             for (int w = 0; w < wave; w++) pos += wcnt[w][ea];
             perm[pos] = a;
             pos_of[a] = pos;
+            wsort[pos] = wa[i];
         }
         __syncthreads();
         if (tid < E) {
@@ -241,16 +246,19 @@ __global__ void __launch_bounds__(PLACE_THREADS) k_sort_place(const int32_t* __r
                                                               int32_t* __restrict__ tiles_e,
                                                               int32_t* __restrict__ tile_count,
                                                               int32_t* __restrict__ perm,
-                                                              int32_t* __restrict__ pos_of, int N, int bm) {
+                                                              int32_t* __restrict__ pos_of,
+                                                              const float* __restrict__ w,
+                                                              float* __restrict__ wsort, int N, int bm) {
     if ((int)blockIdx.x == nblk) tile_map(cnt, nblk, offs, tiles, tiles_e, tile_count, bm);
-    else place_chunk(idx, cnt, nblk, perm, pos_of, N);
+    else place_chunk(idx, cnt, nblk, perm, pos_of, w, wsort, N);
 }
 
 hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tiles_e,
-                       int32_t* tile_count, int32_t* perm, int32_t* pos_of, int bm, hipStream_t s) {
+                       int32_t* tile_count, int32_t* perm, int32_t* pos_of, const float* w, float* wsort, int bm,
+                       hipStream_t s) {
     const int nblk = (N + SORT_CH - 1) / SORT_CH;  // the histograms come from the top-k launch
     hipLaunchKernelGGL(k_sort_place, dim3(nblk + 1), dim3(PLACE_THREADS), 0, s, idx, cnt, nblk, offs, tiles, tiles_e,
-                       tile_count, perm, pos_of, N, bm);
+                       tile_count, perm, pos_of, w, wsort, N, bm);
     return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 // Byte offsets of every workspace region for T tokens.
 struct Layout {
-    size_t wr2, er, shw, es, logits, idx, w, sgate, xh, ex, cnt, offs, tiles, tiles_e, tile_count, perm, pos_of, h, eh,
+    size_t wr2, er, shw, es, logits, idx, w, sgate, xh, ex, cnt, offs, tiles, tiles_e, tile_count, perm, pos_of, wsort, h, eh,
         hs, ehs, partial, ep, total;
 };
 
@@ -48,6 +48,7 @@ Layout layout(int64_t T) {
     L.tile_count = o; o += up(4);
     L.perm = o;       o += up(N * 4);
     L.pos_of = o;     o += up(N * 4);
+    L.wsort = o;      o += up(N * 4);
     L.h = o;          o += up(N * F * 2);
     L.eh = o;         o += up(N * 2 * 4);
     L.hs = o;         o += up((size_t)T * FS * 2);
@@ -182,7 +183,8 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     chk(launch_topk(logits, idx, w, weights_scale(router), router->gating, router->tid2eid, router->token_ids,
                     router->n_vocab, T, cnt, sort_chunk(), s));
     int32_t* tiles_e = (int32_t*)at(L.tiles_e);
-    chk(launch_sort(idx, N, cnt, offs, tiles, tiles_e, tile_count, perm, pos_of, gemm_bm(T), s));
+    float* wsort = (float*)at(L.wsort);
+    chk(launch_sort(idx, N, cnt, offs, tiles, tiles_e, tile_count, perm, pos_of, w, wsort, gemm_bm(T), s));
     PrefillGemmParams p{};
     p.xh = xh;
     p.ex = xe;
@@ -199,7 +201,7 @@ int run_prefill(int T, const uint16_t* x, const moe_ffn_router* router, const mo
     p.tiles = tiles;
     p.tiles_e = tiles_e;
     p.tile_count = tile_count;
-    p.wflat = w;
+    p.wsort = wsort;
     p.sgate = sgate;
     const GateUp gu = resolve_gate_up(ex);
     p.gate_q = gu.gq; p.gate_s = gu.gs; p.gate_b = gu.gb;

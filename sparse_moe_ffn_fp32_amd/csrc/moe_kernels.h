@@ -45,7 +45,8 @@ int sort_chunk();  // assignments per histogram chunk
 // cnt: the per-chunk expert counts (launch_topk); tiles: the tile records
 // longest first; tiles_e: the same records in expert order
 hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tiles_e,
-                       int32_t* tile_count, int32_t* perm, int32_t* pos_of, int bm, hipStream_t s);
+                       int32_t* tile_count, int32_t* perm, int32_t* pos_of, const float* w, float* wsort, int bm,
+                       hipStream_t s);
 
 // ---- grouped GEMMs (k_gemm.hip)
 struct PrefillGemmParams {
@@ -64,7 +65,7 @@ struct PrefillGemmParams {
     const int32_t* tiles;     // tile records, longest first
     const int32_t* tiles_e;   // the same records in expert order
     const int32_t* tile_count;
-    const float* wflat;
+    const float* wsort;  // [N_assign] routing weight of each expert-sorted position
     const float* sgate;
     const uint32_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_s, *up_s, *down_s;
