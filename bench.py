@@ -351,10 +351,9 @@ def main():
         # the gate/up launch also runs the shared expert's down projection:
         # routed gate/up weights of the distinct experts, the shared down
         # weights, x and the shared h in; routed h and the shared output out.
-        # For T <= 8 (the vector-ALU decode kernels) it also streams the
-        # selected experts' down rows from HBM (the down launch then reads
-        # them from cache), so they count here.
-        down_here = DOWN_BYTES if T <= 8 else 0
+        # For T <= 4 it also streams the selected experts' down rows from HBM
+        # (the down launch then reads them from cache), so they count here.
+        down_here = DOWN_BYTES if T <= 4 else 0
         gu_bytes = [d * (GU_BYTES + down_here) + SHARED_DOWN_BYTES + T * 2048 * 2 + T * 512 * 4 + T * 8 * 512 * 2
                     + T * 2048 * 4 for d in distinct]
         per_launch = float(np.mean(gu_bytes))

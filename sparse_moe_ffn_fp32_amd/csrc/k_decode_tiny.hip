@@ -402,11 +402,14 @@ __global__ void __launch_bounds__(256) k_tiny_c(DecodeArgs a, int n_gu_blocks) {
     // which stage D reads next: one dword per 64 bytes (FEAT KB of codes,
     // FEAT / 16 KB each of scales and biases) pulls them into cache in this
     // same round trip.  Stage D's blocks take these rows on this block's XCD
-    // (block id mod 8 = fc mod 8).
+    // (block id mod 8 = fc mod 8).  Up to four tokens only: from five on this
+    // launch is bandwidth-bound and the read-ahead lengthens it by more than
+    // it saves D (T=6 33.5 -> 33.0 us, T=8 41.6 -> 40.6 us without it; T=3
+    // 22.1 -> 22.4 us without it).
     constexpr int PF_ROWS = 4 * FEAT, PF_CODES = PF_ROWS * (F / 2) / 64, PF_SB = PF_ROWS * (F / G) * 2 / 64;
     static_assert(PF_CODES <= 256 && 2 * PF_SB <= 256, "at most one code and one scale/bias dword per thread");
     uint32_t pf = 0, pf2 = 0;
-    {
+    if constexpr (NT <= 4) {
         const size_t drow0 = (size_t)e * D + PF_ROWS * fc;
         if (tid < PF_CODES) pf = a.dq[drow0 * (F / 8) + 16 * tid];
         // the scale and bias dwords: threads from PF_CODES on, wrapping round
