@@ -38,11 +38,11 @@
 //      For the block entry point every block of A first RMS-normalises the
 //      rows itself (no launch of its own), and the copy block also writes
 //      the normalised rows out.
-//   C  routed gate/up + SwiGLU: block = one (token, rank) pair x 8 features;
-//      the block's first wave derives the pair's expert from the token's
-//      logits (DPP top-8) so no routing launch is needed; each block also
-//      pulls the down rows stage D will read into cache; shared down (8 rows
-//      per block).
+//   C  routed gate/up + SwiGLU: block = one (token, rank) pair x 8 features
+//      (16 from three tokens on); each wave derives the pair's expert from
+//      the token's logits (DPP top-8) so no routing launch is needed; up to
+//      four tokens each block also pulls the down rows stage D will read
+//      into cache; shared down (8 rows per block).
 //   D  routed down: block = 8 output rows x every pair; h staged in LDS;
 //      then the combine  y = sum_{r=0..7} w_r * down_r + sgate * shexp (+ the
 //      residual of the block entry point)  in fixed order with one bf16
