@@ -43,7 +43,8 @@ hipError_t launch_topk(const float* logits, int32_t* idx, float* w, float wscale
 int sort_blocks(int N);
 int sort_chunk();  // assignments per histogram chunk
 // cnt: the per-chunk expert counts (launch_topk); tiles: the tile records
-// longest first; tiles_e: the same records in expert order
+// longest first; tiles_e: the same records in expert order; w: the routing
+// weights by assignment, wsort: the same by sorted position
 hipError_t launch_sort(const int32_t* idx, int N, int32_t* cnt, int32_t* offs, int32_t* tiles, int32_t* tiles_e,
                        int32_t* tile_count, int32_t* perm, int32_t* pos_of, const float* w, float* wsort, int bm,
                        hipStream_t s);
