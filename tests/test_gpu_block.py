@@ -101,7 +101,7 @@ def check(layer, h, w, y, idx, wt, xn, O=None):
     return float(err.max())
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 37, 64, 300])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 9, 37, 64, 300])
 def test_block_forward(gpu, layer0, norm_w, T):
     h = block_inputs(layer0, norm_w, T, 400 + T)
     _say(f"block T={T}")

@@ -33,7 +33,7 @@ def test_noalloc_matches_workspace_entry_point():
 
     layer = workloads.layer_for(0)
     dl = moe.DeviceLayer.from_host(layer)
-    sizes = (64, 37, 3)
+    sizes = (64, 37, 8, 3)
     xs, refs = {}, {}
 
     def outputs(T):
