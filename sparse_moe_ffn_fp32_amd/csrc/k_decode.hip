@@ -916,15 +916,35 @@ __global__ void __launch_bounds__(512) k_dec_stage_d(DecodeArgs a) {
 // y = sum_{r=0..7} w_r * partial_r + sgate * shexp (+ the residual), fixed
 // order, one bf16 rounding (T > 8).
 __global__ void __launch_bounds__(256) k_dec_combine(DecodeArgs a) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
+    // four consecutive outputs per thread (16-byte partial loads)
+    const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
     if (i >= a.T * D) return;
     const int t = i / D, o = i % D;
-    float sum = 0.0f;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < K; r++) sum += a.w[t * K + r] * a.part[(size_t)(t * K + r) * D + o];
-    if (a.sg) sum += a.sgate[t] * a.ys[i];
-    if (a.resid) sum += bf16_to_f32(a.resid[i]);
-    a.y[i] = f32_to_bf16_rne(sum);
+    for (int r = 0; r < K; r++) {
+        const float w = a.w[t * K + r];
+        const f32x4 p = *(const f32x4*)&a.part[(size_t)(t * K + r) * D + o];
+#pragma unroll
+        for (int j = 0; j < 4; j++) sum[j] += w * p[j];
+    }
+    if (a.sg) {
+        const float g = a.sgate[t];
+        const f32x4 ys = *(const f32x4*)&a.ys[i];
+#pragma unroll
+        for (int j = 0; j < 4; j++) sum[j] += g * ys[j];
+    }
+    if (a.resid) {
+        const u32x2 rv = *(const u32x2*)&a.resid[i];
+        sum[0] += bf16_to_f32(rv[0] & 0xffffu);
+        sum[1] += bf16_to_f32(rv[0] >> 16);
+        sum[2] += bf16_to_f32(rv[1] & 0xffffu);
+        sum[3] += bf16_to_f32(rv[1] >> 16);
+    }
+    u32x2 out;
+    out[0] = (uint32_t)f32_to_bf16_rne(sum[0]) | ((uint32_t)f32_to_bf16_rne(sum[1]) << 16);
+    out[1] = (uint32_t)f32_to_bf16_rne(sum[2]) | ((uint32_t)f32_to_bf16_rne(sum[3]) << 16);
+    *(u32x2*)&a.y[i] = out;
 }
 
 // ------------------------------------------------------------------ host
@@ -965,7 +985,7 @@ static void launch_decode_t(const DecodeArgs& a, const Tracer& tr, hipStream_t s
     const int n_sd = a.sg ? N_SDOWN_BLK : 0;
     tr.launch(MOE_FFN_KERNEL_EXPERT_GU, k_dec_stage_c, dim3(n_gu + n_sd), dim3(512), 0, s, a);
     tr.launch(MOE_FFN_KERNEL_EXPERT_DOWN, k_dec_stage_d, dim3(DN_BLOCKS), dim3(512), 0, s, a);
-    tr.launch(MOE_FFN_KERNEL_COMBINE, k_dec_combine, dim3((a.T * D + 255) / 256), dim3(256), 0, s, a);
+    tr.launch(MOE_FFN_KERNEL_COMBINE, k_dec_combine, dim3((a.T * D / 4 + 255) / 256), dim3(256), 0, s, a);
 }
 
 hipError_t launch_decode(const DecodeParams& p, char* ws, const Tracer& tr, hipStream_t s) {
