@@ -147,12 +147,20 @@ def main():
                     help="time the FFN sub-block (RMSNorm in, residual out) instead of the bare FFN")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (calibrates PMC byte counters)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="the default workload also times the other four workloads (one child process each, "
+                         "before its own measurement) and lists them under other_workloads; this turns that off")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
+    # the other workloads first, each in a child process, while this one has
+    # not touched the GPU yet
+    others = None
+    if args.workload == ap.get_default("workload") and not args.no_sweep and not args.block:
+        others = sweep()
 
     import torch
 
@@ -454,7 +462,39 @@ def main():
                           "n": len(step_ms),
                           "how": "one-step graph replays between events" if nlayers > 1 else
                                  "per call between events, caches evicted before each"}
+    if others is not None:
+        out["other_workloads"] = others
     print(json.dumps(out), flush=True)
+
+
+def sweep(steps=10, warmup=3):
+    """The other workloads, each timed by a child run of this script (its
+    own process, started before this one uses the GPU), reduced to their
+    headline fields; a child that fails is recorded as such."""
+    import subprocess
+
+    res = {}
+    for name in WORKLOADS:
+        if name == "decode_T1_40layers":
+            continue
+        log(f"sweep: {name}")
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--steps", str(steps),
+               "--warmup", str(warmup), "--no-cpu-baseline", "--no-sweep"]
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+            line = [ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1] if r.returncode == 0 else None
+        except (subprocess.TimeoutExpired, IndexError):
+            r, line = None, None
+        if line is None:
+            res[name] = {"error": f"child exit {None if r is None else r.returncode}"}
+            continue
+        d = json.loads(line)
+        roof = d["roofline"]
+        res[name] = {"value": d["value"], "unit": d["unit"], "ms_per_step": d["ms_per_step"], "steps": d["steps"],
+                     "dtype": d["dtype"], "step_us_p50": d.get("step_us", {}).get("p50"),
+                     "roofline": {k: roof.get(k) for k in ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                                           "kernel", "avg_launch_us")}}
+    return res
 
 
 if __name__ == "__main__":
