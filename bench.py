@@ -135,7 +135,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_T1_40layers", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
+                    help="one workload (default: decode_T1_40layers, plus the sweep of the others)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 decode, 2 prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every traced kernel (stderr)")
@@ -148,8 +149,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (calibrates PMC byte counters)")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="the default workload also times the other four workloads (one child process each, "
-                         "before its own measurement) and lists them under other_workloads; this turns that off")
+                    help="with no --workload the run also times the other four workloads (one child process "
+                         "each, before its own measurement) and lists them under other_workloads; this turns "
+                         "that off")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -158,9 +160,13 @@ def main():
         sys.exit(2)
     # the other workloads first, each in a child process, while this one has
     # not touched the GPU yet
+    # (only when no workload was named: the profiling runs name theirs, and
+    # a run under a profiler must not start other programs)
     others = None
-    if args.workload == ap.get_default("workload") and not args.no_sweep and not args.block:
-        others = sweep()
+    if args.workload is None:
+        args.workload = "decode_T1_40layers"
+        if not args.no_sweep and not args.block:
+            others = sweep()
 
     import torch
 
